@@ -1,0 +1,215 @@
+"""CPU oracle for the gated linear-attention forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
+with the GPU library (``mlstm_sequence_amd``) and never imports it.
+
+Three independent evaluations of one function live here:
+
+* :func:`recurrent_fwd` -- the step-by-step recurrence in double, in plain C
+  (``oracle.c``, OpenMP over heads).  This is *the* oracle: the recurrent
+  ("FusedRecurrent", O(T)) form listed among the computation forms of the
+  flash-linear-attention README.
+* :func:`closed_form_fwd` -- the quadratic closed form, brute force in numpy
+  float64 (the "Parallel", O(T^2) form of the same README):
+      h_t = sum_{s<=t} (prod_{r=s+1..t} f_r) i_s (q_t . k_s) v_s / sqrt(d_qk)
+  with the product taken per key channel inside q.k for the per-channel gate.
+* :func:`chunkwise_fwd` -- the chunkwise-parallel form ("ParallelChunk" in the
+  README; the chunkwise formulation that Tiled Flash Linear Attention tiles,
+  TFLA abstract) in numpy float64 for any chunk size, ragged last chunk
+  included: an inter-chunk state recurrence plus a masked intra-chunk product.
+
+The two numpy forms exist to pin the C oracle; they are slower and limited to
+tiny inputs.  Gate variants (``kind``):
+
+* 0 ``MLSTM_SIG``: i = sigmoid(igate_pre[t]), f = sigmoid(fgate_pre[t])
+  (mLSTMsig: sigmoid input gate, no normaliser, no max state -- TFLA
+  research-map summary, Approach).
+* 1 ``SCALAR``: i = 1, f = sigmoid(fgate_pre[h]) per head (RetNet-style fixed
+  decay, README model table).
+* 2 ``GLA``: i = 1, f_{t,c} = exp(logsigmoid(x_{t,c}) / 16) per key channel
+  (data-dependent gates, GLA abstract).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+MLSTM_SIG, SCALAR, GLA = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run oracle.build.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_fwd.argtypes = [dp] * 7 + [ctypes.c_int] * 7
+        lib.oracle_fwd.restype = ctypes.c_int
+        lib.oracle_log_gates.argtypes = [dp] * 5 + [ctypes.c_int] * 6
+        lib.oracle_log_gates.restype = ctypes.c_int
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = ctypes.c_int
+        lib.oracle_sigmoid.argtypes = [ctypes.c_double]
+        lib.oracle_sigmoid.restype = ctypes.c_double
+        lib.oracle_log_sigmoid.argtypes = [ctypes.c_double]
+        lib.oracle_log_sigmoid.restype = ctypes.c_double
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def threads() -> int:
+    """OpenMP threads the C oracle runs with."""
+    return _load().oracle_threads()
+
+
+def sigmoid(x: float) -> float:
+    return _load().oracle_sigmoid(float(x))
+
+
+def log_sigmoid(x: float) -> float:
+    return _load().oracle_log_sigmoid(float(x))
+
+
+def recurrent_fwd(q, k, v, igate_pre, fgate_pre, kind, L=None):
+    """Recurrent oracle.  Arrays: q,k [B,H,T,dqk], v [B,H,T,dhv] (any real
+    dtype; converted exactly to float64).  Returns h [B,H,T,dhv] float64, and
+    with ``L`` also the states after every full block of L steps
+    [B,H,T//L,dqk,dhv]."""
+    q, k, v, ig, fg = map(_f64, (q, k, v, igate_pre, fgate_pre))
+    B, H, T, dqk = q.shape
+    dhv = v.shape[-1]
+    h = np.empty((B, H, T, dhv), dtype=np.float64)
+    states = None
+    if L is not None:
+        states = np.empty((B, H, T // L, dqk, dhv), dtype=np.float64)
+    rc = _load().oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(ig), _ptr(fg), _ptr(h),
+                            _ptr(states), B, H, T, dqk, dhv, L or 0, kind)
+    if rc != 0:
+        raise ValueError("oracle_fwd rejected its arguments")
+    return (h, states) if L is not None else h
+
+
+def log_gates(igate_pre, fgate_pre, kind, B, H, T, dqk, L):
+    """Chunk-local log-gate sums a, li, g (see oracle.c)."""
+    ig, fg = _f64(igate_pre), _f64(fgate_pre)
+    nc = -(-T // L)
+    w = dqk if kind == GLA else 1
+    a = np.empty((B, H, T, w), dtype=np.float64)
+    li = np.empty((B, H, T), dtype=np.float64)
+    g = np.empty((B, H, nc, w), dtype=np.float64)
+    rc = _load().oracle_log_gates(_ptr(ig), _ptr(fg), _ptr(a), _ptr(li), _ptr(g),
+                                  B, H, T, dqk, L, kind)
+    if rc != 0:
+        raise ValueError("oracle_log_gates rejected its arguments")
+    if kind != GLA:
+        a, g = a[..., 0], g[..., 0]
+    return a, li, g
+
+
+# ----------------------------------------------------------------------------
+# numpy float64 forms (tiny inputs only)
+# ----------------------------------------------------------------------------
+
+def _np_sigmoid(x):
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    e = np.exp(x[~pos])
+    out[~pos] = e / (1.0 + e)
+    return out
+
+
+def gates_np(igate_pre, fgate_pre, kind, B, H, T, dqk):
+    """Per-step gates in float64: i [B,H,T], f [B,H,T,dqk] (channel-constant
+    unless kind == GLA)."""
+    if kind == MLSTM_SIG:
+        i = _np_sigmoid(igate_pre)
+        f = np.repeat(_np_sigmoid(fgate_pre)[..., None], dqk, axis=-1)
+    elif kind == SCALAR:
+        i = np.ones((B, H, T))
+        gam = _np_sigmoid(np.asarray(fgate_pre, dtype=np.float64))  # [H]
+        f = np.broadcast_to(gam[None, :, None, None], (B, H, T, dqk)).copy()
+    elif kind == GLA:
+        x = np.asarray(fgate_pre, dtype=np.float64)
+        ls = np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))
+        i = np.ones((B, H, T))
+        f = np.exp(ls / 16.0)
+    else:
+        raise ValueError(kind)
+    return i, f
+
+
+def closed_form_fwd(q, k, v, igate_pre, fgate_pre, kind):
+    """Quadratic closed form by brute force: every decay product is formed
+    explicitly as a product of forget gates."""
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    B, H, T, dqk = q.shape
+    dhv = v.shape[-1]
+    i, f = gates_np(igate_pre, fgate_pre, kind, B, H, T, dqk)
+    h = np.zeros((B, H, T, dhv))
+    for b in range(B):
+        for hh in range(H):
+            for t in range(T):
+                acc = np.zeros(dhv)
+                for s in range(t + 1):
+                    decay = np.prod(f[b, hh, s + 1:t + 1, :], axis=0)  # per channel
+                    w = np.sum(q[b, hh, t] * k[b, hh, s] * decay) * i[b, hh, s]
+                    acc += w * v[b, hh, s]
+                h[b, hh, t] = acc / np.sqrt(dqk)
+    return h
+
+
+def chunkwise_fwd(q, k, v, igate_pre, fgate_pre, kind, L):
+    """Chunkwise form: states at chunk boundaries plus masked intra-chunk
+    products, all in float64.  Any L >= 1; the last chunk may be partial.
+    Returns (h, states after every full chunk [B,H,T//L,dqk,dhv])."""
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    B, H, T, dqk = q.shape
+    dhv = v.shape[-1]
+    i, f = gates_np(igate_pre, fgate_pre, kind, B, H, T, dqk)
+    h = np.zeros((B, H, T, dhv))
+    states = np.zeros((B, H, T // L, dqk, dhv))
+    for b in range(B):
+        for hh in range(H):
+            C = np.zeros((dqk, dhv))
+            for kc, t0 in enumerate(range(0, T, L)):
+                t1 = min(t0 + L, T)
+                n = t1 - t0
+                Q, K, V = q[b, hh, t0:t1], k[b, hh, t0:t1], v[b, hh, t0:t1]
+                fc, ic = f[b, hh, t0:t1], i[b, hh, t0:t1]
+                # F[t] = prod_{r=t0..t} f_r  (decay from the chunk start)
+                F = np.cumprod(fc, axis=0)
+                # D[t,s,c] = prod_{r=s+1..t} f_{r,c} for s <= t, 0 above the diagonal
+                D = np.zeros((n, n, dqk))
+                for s in range(n):
+                    D[s, s] = 1.0
+                    if s + 1 < n:
+                        D[s + 1:, s] = np.cumprod(fc[s + 1:], axis=0)
+                W = np.einsum("tc,sc,tsc->ts", Q, K, D) * ic[None, :]
+                inter = (Q * F) @ C
+                h[b, hh, t0:t1] = (inter + W @ V) / np.sqrt(dqk)
+                # state after the chunk: decay to its last step, then add the chunk
+                w_s = D[n - 1] * ic[:, None]          # [s, c] = prod_{r=s+1..end} f * i_s
+                C = F[n - 1][:, None] * C + (K * w_s).T @ V
+                if n == L:
+                    states[b, hh, kc] = C
+    return h, states

@@ -1,0 +1,28 @@
+"""Builds liboracle.so from oracle.c with the host C compiler (gcc, OpenMP).
+
+Generic x86-64 code (no -march=native): the library is built in one
+container and may run on another machine's host cores.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def build(verbose: bool = False) -> str:
+    src = os.path.join(_HERE, "oracle.c")
+    out = os.path.join(_HERE, "liboracle.so")
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra",
+           src, "-o", tmp, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,256 @@
+"""Pins of the CPU oracle against what the mathematics fixes (no GPU).
+
+The recurrent oracle (plain C, double) is checked against independent
+evaluations of the same function: the quadratic closed form by brute force,
+causal linear attention (all gates one), the RetNet parallel form (fixed
+per-head decay), hand-worked examples, the chunkwise form at every chunk
+size, and invariants.  A mistake in the oracle -- a dropped term, a wrong
+sign, a shifted time index, a transposed operand -- fails at least one.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import GLA, MLSTM_SIG, SCALAR
+
+REL = 1e-12
+
+
+def rel_err(x, ref):
+    x, ref = np.asarray(x), np.asarray(ref)
+    m = np.max(np.abs(ref))
+    return np.max(np.abs(x - ref)) / (m if m > 0 else 1.0)
+
+
+def rand_case(kind, B, H, T, dqk, dhv, seed, gate_scale=1.0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, T, dqk))
+    k = rng.standard_normal((B, H, T, dqk))
+    v = rng.standard_normal((B, H, T, dhv))
+    if kind == MLSTM_SIG:
+        ig = rng.standard_normal((B, H, T)) * 2.0 * gate_scale
+        fg = rng.uniform(-2.0, 4.0, (B, H, T)) * gate_scale
+    elif kind == SCALAR:
+        ig = None
+        fg = rng.uniform(-1.0, 5.0, (H,))
+    else:
+        ig = None
+        fg = rng.standard_normal((B, H, T, dqk)) * 3.0 * gate_scale
+    return q, k, v, ig, fg
+
+
+SHAPES = [(2, 2, 1, 1, 1), (2, 2, 2, 3, 4), (2, 2, 7, 8, 1), (2, 2, 33, 3, 8), (2, 2, 48, 8, 4),
+          (1, 3, 17, 1, 8)]
+
+
+@pytest.mark.parametrize("kind", [MLSTM_SIG, SCALAR, GLA])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_recurrence_equals_closed_form(kind, shape):
+    B, H, T, dqk, dhv = shape
+    q, k, v, ig, fg = rand_case(kind, B, H, T, dqk, dhv, seed=hash((kind,) + shape) % 2**32)
+    h = oracle.recurrent_fwd(q, k, v, ig, fg, kind)
+    ref = oracle.closed_form_fwd(q, k, v, ig, fg, kind)
+    assert rel_err(h, ref) <= REL
+
+
+@pytest.mark.parametrize("kind", [MLSTM_SIG, SCALAR, GLA])
+def test_unit_gates_give_causal_linear_attention(kind):
+    """i = f = 1 reduces the method to causal linear attention:
+    h = tril(Q K^T) V / sqrt(d_qk) ("Transformers are RNNs", on the TFLA
+    index page's builds-on list)."""
+    B, H, T, dqk, dhv = 2, 3, 29, 8, 5
+    rng = np.random.default_rng(7)
+    q, k, v = (rng.standard_normal((B, H, T, d)) for d in (dqk, dqk, dhv))
+    if kind == MLSTM_SIG:
+        ig, fg = np.full((B, H, T), np.inf), np.full((B, H, T), np.inf)
+    elif kind == SCALAR:
+        ig, fg = None, np.full((H,), np.inf)
+    else:
+        ig, fg = None, np.full((B, H, T, dqk), np.inf)
+    h = oracle.recurrent_fwd(q, k, v, ig, fg, kind)
+    ref = np.tril(q @ np.swapaxes(k, -1, -2)) @ v / math.sqrt(dqk)
+    assert rel_err(h, ref) <= REL
+
+
+def test_scalar_decay_equals_retnet_parallel_form():
+    """Fixed decay gamma_h: h = ((Q K^T) * D) V / sqrt(d), D_ts = gamma^(t-s)
+    for s <= t (the parallel retention form)."""
+    B, H, T, dqk, dhv = 2, 4, 40, 6, 3
+    rng = np.random.default_rng(11)
+    q, k, v = (rng.standard_normal((B, H, T, d)) for d in (dqk, dqk, dhv))
+    logits = np.array([math.log(2.0 ** (5 + hh / 4) - 1) for hh in range(H)])
+    h = oracle.recurrent_fwd(q, k, v, None, logits, SCALAR)
+    gam = 1.0 - 2.0 ** -(5 + np.arange(H) / 4)
+    t = np.arange(T)
+    expo = t[:, None] - t[None, :]
+    D = np.where(expo >= 0, np.power(gam[:, None, None], np.maximum(expo, 0)), 0.0)
+    ref = (q @ np.swapaxes(k, -1, -2) * D[None]) @ v / math.sqrt(dqk)
+    assert rel_err(h, ref) <= REL
+
+
+@pytest.mark.parametrize("kind", [MLSTM_SIG, SCALAR, GLA])
+@pytest.mark.parametrize("T", [24, 37])
+def test_chunkwise_equals_recurrence_for_every_chunk_size(kind, T):
+    """The chunkwise form gives the same function for every chunk size; L = 1
+    is the recurrence and L >= T the closed form.  Ragged last chunks
+    (L not dividing T) included.  The states at chunk ends match too."""
+    B, H, dqk, dhv = 1, 2, 4, 3
+    q, k, v, ig, fg = rand_case(kind, B, H, T, dqk, dhv, seed=5 + T + kind)
+    for L in range(1, T + 2):
+        h_rec, st_rec = oracle.recurrent_fwd(q, k, v, ig, fg, kind, L=L)
+        h_ch, st_ch = oracle.chunkwise_fwd(q, k, v, ig, fg, kind, L)
+        assert rel_err(h_ch, h_rec) <= REL, L
+        if st_rec.size:
+            assert rel_err(st_ch, st_rec) <= REL, L
+
+
+def test_hand_worked_scalar_example():
+    """d_qk = d_hv = 1, mLSTMsig with pre-activations 0 (i = f = 1/2):
+        C1 = 1/2*k1*v1          = 1/2*1*2 = 1      h1 = C1*q1 = 1
+        C2 = 1/2*C1 + 1/2*k2*v2 = 1/2 + 1/2 = 1    h2 = C2*q2 = 2
+        C3 = 1/2*C2 + 1/2*k3*v3 = 1/2 + 4   = 4.5  h3 = C3*q3 = 4.5
+    The first forget gate multiplies C0 = 0 and has no effect."""
+    q = np.array([1.0, 2.0, 1.0]).reshape(1, 1, 3, 1)
+    k = np.array([1.0, 1.0, 2.0]).reshape(1, 1, 3, 1)
+    v = np.array([2.0, 1.0, 4.0]).reshape(1, 1, 3, 1)
+    ig = np.zeros((1, 1, 3))
+    fg = np.zeros((1, 1, 3))
+    h = oracle.recurrent_fwd(q, k, v, ig, fg, MLSTM_SIG)
+    assert np.array_equal(h.ravel(), [1.0, 2.0, 4.5])
+
+
+def test_hand_worked_matrix_example():
+    """d_qk = 2, d_hv = 3, i = 1 (pre-activation +inf), f = 1/2:
+        C1 = k1 v1^T = [[1,2,3],[2,4,6]]             h1 = C1^T q1 / sqrt2 = (2,4,6)/sqrt2
+        C2 = C1/2 + k2 v2^T = [[1/2,2,3/2],[1,2,3]]  h2 = C2^T q2 / sqrt2 = (1/2,2,3/2)/sqrt2
+    with q1 = (0,1), k1 = (1,2), v1 = (1,2,3), q2 = (1,0), k2 = (1,0), v2 = (0,1,0).
+    A transposed state or a swapped q/k would give different numbers."""
+    q = np.array([[0.0, 1.0], [1.0, 0.0]]).reshape(1, 1, 2, 2)
+    k = np.array([[1.0, 2.0], [1.0, 0.0]]).reshape(1, 1, 2, 2)
+    v = np.array([[1.0, 2.0, 3.0], [0.0, 1.0, 0.0]]).reshape(1, 1, 2, 3)
+    ig = np.full((1, 1, 2), np.inf)
+    fg = np.zeros((1, 1, 2))
+    h = oracle.recurrent_fwd(q, k, v, ig, fg, MLSTM_SIG)
+    r2 = math.sqrt(2.0)
+    expect = np.array([[2.0, 4.0, 6.0], [0.5, 2.0, 1.5]]) / r2
+    assert np.allclose(h[0, 0], expect, rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("kind", [MLSTM_SIG, GLA])
+def test_single_step(kind):
+    """T = 1: h1 = i1 (q1 . k1) v1 / sqrt(d) whatever the forget gate."""
+    q, k, v, ig, fg = rand_case(kind, 2, 2, 1, 5, 3, seed=3)
+    h = oracle.recurrent_fwd(q, k, v, ig, fg, kind)
+    i = 1.0 / (1.0 + np.exp(-ig)) if kind == MLSTM_SIG else np.ones((2, 2, 1))
+    ref = i[..., None] * np.sum(q * k, axis=-1, keepdims=True) * v / math.sqrt(5)
+    assert rel_err(h, ref) <= REL
+
+
+def test_zero_forget_gate_forgets_everything():
+    """f = 0 (pre-activation -inf) everywhere: h_t = i_t (q_t . k_t) v_t / sqrt(d)."""
+    q, k, v, ig, _ = rand_case(MLSTM_SIG, 2, 2, 9, 4, 3, seed=4)
+    fg = np.full((2, 2, 9), -np.inf)
+    h = oracle.recurrent_fwd(q, k, v, ig, fg, MLSTM_SIG)
+    i = 1.0 / (1.0 + np.exp(-ig))
+    ref = i[..., None] * np.sum(q * k, axis=-1, keepdims=True) * v / math.sqrt(4)
+    assert rel_err(h, ref) <= REL
+    # the same through a per-channel gate
+    x = np.full((2, 2, 9, 4), -np.inf)
+    h2 = oracle.recurrent_fwd(q, k, v, None, x, GLA)
+    ref2 = np.sum(q * k, axis=-1, keepdims=True) * v / math.sqrt(4)
+    assert rel_err(h2, ref2) <= REL
+
+
+def test_zero_input_gate_gives_zero():
+    q, k, v, _, fg = rand_case(MLSTM_SIG, 1, 2, 8, 3, 3, seed=9)
+    ig = np.full((1, 2, 8), -np.inf)
+    h = oracle.recurrent_fwd(q, k, v, ig, fg, MLSTM_SIG)
+    assert np.all(h == 0.0)
+
+
+@pytest.mark.parametrize("kind", [MLSTM_SIG, SCALAR, GLA])
+def test_invariants(kind):
+    B, H, T, dqk, dhv = 2, 3, 21, 4, 5
+    q, k, v, ig, fg = rand_case(kind, B, H, T, dqk, dhv, seed=21 + kind)
+    h = oracle.recurrent_fwd(q, k, v, ig, fg, kind)
+    # the first forget gate multiplies C0 = 0
+    if kind != SCALAR:
+        fg2 = fg.copy()
+        fg2[:, :, 0] = -fg2[:, :, 0] + 1.3
+        assert np.array_equal(oracle.recurrent_fwd(q, k, v, ig, fg2, kind), h)
+    # causality: changing step >= t0 leaves h_{<t0} bit-identical
+    t0 = 11
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    q2[:, :, t0:] += 1.0
+    k2[:, :, t0:] -= 2.0
+    v2[:, :, t0:] *= 3.0
+    h2 = oracle.recurrent_fwd(q2, k2, v2, ig, fg, kind)
+    assert np.array_equal(h2[:, :, :t0], h[:, :, :t0])
+    assert not np.array_equal(h2[:, :, t0:], h[:, :, t0:])
+    # linear in v, homogeneous of degree one in q and in k
+    v3 = np.random.default_rng(1).standard_normal(v.shape)
+    hv = oracle.recurrent_fwd(q, k, v + 2.5 * v3, ig, fg, kind)
+    hv3 = oracle.recurrent_fwd(q, k, v3, ig, fg, kind)
+    assert rel_err(hv, h + 2.5 * hv3) <= REL
+    assert rel_err(oracle.recurrent_fwd(-3.0 * q, k, v, ig, fg, kind), -3.0 * h) <= REL
+    assert rel_err(oracle.recurrent_fwd(q, 0.5 * k, v, ig, fg, kind), 0.5 * h) <= REL
+    # heads are independent: permuting (b, h) permutes outputs
+    if kind != SCALAR:
+        perm = np.random.default_rng(2).permutation(B * H)
+
+        def p(a):
+            if a is None:
+                return None
+            s = a.shape
+            return a.reshape((B * H,) + s[2:])[perm].reshape(s)
+
+        hp = oracle.recurrent_fwd(p(q), p(k), p(v), p(ig), p(fg), kind)
+        assert np.array_equal(hp, p(h))
+
+
+def test_channel_constant_gla_equals_scalar_gate_core():
+    """A per-channel gate that is the same on every channel is a per-step
+    scalar gate: GLA with x[t, c] = x[t] equals mLSTMsig with i = 1 and
+    f = exp(logsigmoid(x)/16)."""
+    B, H, T, dqk, dhv = 1, 2, 19, 4, 3
+    rng = np.random.default_rng(33)
+    q, k, v = (rng.standard_normal((B, H, T, d)) for d in (dqk, dqk, dhv))
+    x = rng.standard_normal((B, H, T)) * 2.0
+    h_gla = oracle.recurrent_fwd(q, k, v, None, np.repeat(x[..., None], dqk, axis=-1), GLA)
+    f = np.exp((np.minimum(x, 0) - np.log1p(np.exp(-np.abs(x)))) / 16.0)
+    fpre = np.log(f) - np.log1p(-f)           # logit(f)
+    h_sig = oracle.recurrent_fwd(q, k, v, np.full((B, H, T), np.inf), fpre, MLSTM_SIG)
+    assert rel_err(h_sig, h_gla) <= 1e-11
+
+
+def test_gate_functions():
+    for x in [-30.0, -5.0, -0.5, 0.0, 0.25, 3.0, 17.0]:
+        assert oracle.log_sigmoid(x) == pytest.approx(-math.log1p(math.exp(-x)), rel=1e-14, abs=1e-300)
+        assert oracle.sigmoid(x) == pytest.approx(1.0 / (1.0 + math.exp(-x)), rel=1e-14)
+    for x in [-80.0, 80.0, -700.0, 700.0]:
+        assert math.isfinite(oracle.log_sigmoid(x))
+    assert oracle.log_sigmoid(-80.0) == pytest.approx(-80.0, rel=1e-15)
+    assert oracle.sigmoid(math.inf) == 1.0 and oracle.sigmoid(-math.inf) == 0.0
+    assert oracle.log_sigmoid(math.inf) == 0.0 and oracle.log_sigmoid(-math.inf) == -math.inf
+
+
+@pytest.mark.parametrize("kind", [MLSTM_SIG, SCALAR, GLA])
+def test_log_gate_sums_are_log_decay_products(kind):
+    """exp(a_t - a_s) is the product of the forget gates strictly after s up
+    to t inside a chunk, exp(a_t) the product from the chunk start, exp(li)
+    the input gate, g the value at the chunk's last step."""
+    B, H, T, dqk, L = 1, 2, 23, 3, 8
+    q, k, v, ig, fg = rand_case(kind, B, H, T, dqk, 2, seed=44 + kind)
+    a, li, g = oracle.log_gates(ig, fg, kind, B, H, T, dqk, L)
+    i, f = oracle.gates_np(ig, fg, kind, B, H, T, dqk)
+    if kind != GLA:
+        a, g = a[..., None], g[..., None]
+    for t0 in range(0, T, L):
+        t1 = min(t0 + L, T)
+        for t in range(t0, t1):
+            assert np.allclose(np.exp(a[:, :, t]), np.prod(f[:, :, t0:t + 1], axis=2)[..., :a.shape[-1]],
+                               rtol=1e-12, atol=0)
+        assert np.array_equal(g[:, :, t0 // L], a[:, :, t1 - 1])
+    assert np.allclose(np.exp(li), i, rtol=1e-13, atol=0)
