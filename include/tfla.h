@@ -1,0 +1,141 @@
+/*
+ * tfla.h -- C ABI of libtfla: the chunkwise-parallel forward pass of gated
+ * linear attention (mLSTMsig and two gate variants) on AMD gfx950.
+ *
+ * The operation.  Per batch b and head h, with matrix memory C in
+ * R^{d_qk x d_hv} starting at C_0 = 0:
+ *
+ *     C_t = diag(f_t) C_{t-1} + i_t k_t v_t^T,     h_t = C_t^T q_t / sqrt(d_qk)
+ *
+ * mLSTMsig (the mLSTM with a sigmoid input gate and neither normaliser nor
+ * max state) is defined in words in "Tiled Flash Linear Attention: More
+ * Efficient Linear RNN and xLSTM Kernels" (research-map summary, sections
+ * Approach and Surprising findings); the fixed per-head decay is the RetNet
+ * row and the per-key-channel gate the GLA row of the flash-linear-attention
+ * README's model table; the data-dependent gate is from "Gated Linear
+ * Attention Transformers with Hardware-Efficient Training" (Abstract).
+ *
+ * The library evaluates it chunkwise (TFLA abstract: chunkwise-parallel
+ * formulation with a second level of sequence tiling inside each chunk, so
+ * the chunk size L is not bounded by on-chip memory): a gate prefix-sum
+ * kernel, an inter-chunk state kernel that materialises the fp32 state at
+ * every chunk boundary (the "ParallelChunk" form of the README), and an
+ * intra-chunk kernel on bf16 matrix cores.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
+ *     aligned, contiguous row-major.  The library keeps no pointer after a
+ *     call returns.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *     the null stream) and the call returns without waiting.  Device faults
+ *     surface at the caller's next synchronisation.
+ *   - Arguments are validated before any HIP call; a rejected call has no
+ *     side effect.  Every call returns a tfla_status; tfla_last_error()
+ *     returns a thread-local message describing the last failure.
+ *   - Calls are reentrant; the only mutable global state is that message.
+ */
+#ifndef TFLA_H
+#define TFLA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* `variant` = gate kind (low byte) | I/O element type flag. */
+enum tfla_variant {
+    TFLA_MLSTM_SIG = 0,     /* i = sigmoid(igate_pre[t]), f = sigmoid(fgate_pre[t])       */
+    TFLA_SCALAR_DECAY = 1,  /* i = 1, f = sigmoid(fgate_pre[h]) fixed per head            */
+    TFLA_GLA_KEY = 2,       /* i = 1, f_{t,c} = exp(logsigmoid(fgate_pre[t,c]) / 16)      */
+    TFLA_IO_BF16 = 0x100    /* q, k, v, h are bf16; without the flag they are fp32        */
+};
+
+enum tfla_status {
+    TFLA_OK = 0,
+    TFLA_ERR_INVALID_ARG = 1,   /* NULL/misaligned pointer, bad size, unknown variant   */
+    TFLA_ERR_UNSUPPORTED = 2,   /* valid but not built: head dims or chunk size          */
+    TFLA_ERR_HIP = 3,           /* a HIP launch or runtime call failed                   */
+    TFLA_ERR_OUT_OF_MEMORY = 4  /* workspace allocation failed, or the caller's is small */
+};
+
+/*
+ * tfla_fwd -- the forward pass.
+ *
+ *   q          [B,H,T,d_qk]  bf16 or fp32 (see TFLA_IO_BF16)
+ *   k          [B,H,T,d_qk]
+ *   v          [B,H,T,d_hv]
+ *   igate_pre  fp32 [B,H,T] input-gate pre-activations for TFLA_MLSTM_SIG;
+ *              must be NULL for the other variants (their input gate is 1).
+ *   fgate_pre  fp32 forget-gate pre-activations:
+ *                TFLA_MLSTM_SIG    [B,H,T]
+ *                TFLA_SCALAR_DECAY [H]      (logit of the per-head decay;
+ *                                            +inf means no decay)
+ *                TFLA_GLA_KEY      [B,H,T,d_qk]
+ *   h          [B,H,T,d_hv] output, same element type as q; fully
+ *              overwritten; must not overlap any input.
+ *   B, H, T    >= 1.  T need not be a multiple of L (the last chunk may be
+ *              partial).
+ *   d_qk       64, 128 or 256          (fp32 I/O: 64 or 128)
+ *   d_hv       a multiple of 64, <= 512 (fp32 I/O: <= 256)
+ *   L          chunk size: 64, 128, 256, 512 or 1024
+ *
+ * Gate pre-activations may be +-inf (a gate of exactly 1 or 0).  The log
+ * forget gate is floored at -100 (a forget gate below e^-100 acts as
+ * e^-100), which keeps log-decay differences finite.
+ *
+ * Scratch: allocates its workspace (tfla_workspace_bytes) stream-ordered
+ * with hipMallocAsync and frees it with hipFreeAsync on `stream`.
+ */
+int tfla_fwd(const void* q, const void* k, const void* v,
+             const float* igate_pre, const float* fgate_pre, void* h,
+             int B, int H, int T, int d_qk, int d_hv, int L, int variant, void* stream);
+
+/* Bytes of device workspace tfla_fwd_ws needs for these arguments (0 when
+ * the arguments are invalid or unsupported). */
+size_t tfla_workspace_bytes(int B, int H, int T, int d_qk, int d_hv, int L, int variant);
+
+/* tfla_fwd with a caller-owned device workspace of at least
+ * tfla_workspace_bytes(...) bytes, 256-byte aligned; no allocation.  The
+ * workspace must not be used by other work while this call's kernels run. */
+int tfla_fwd_ws(const void* q, const void* k, const void* v,
+                const float* igate_pre, const float* fgate_pre, void* h,
+                int B, int H, int T, int d_qk, int d_hv, int L, int variant,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Test hooks: run part of the path and copy its intermediate out.
+ *
+ * tfla_dbg_gates -- the gate prefix-sum kernel alone.  Outputs (device, fp32):
+ *   a_out   chunk-local inclusive sums of the log forget gate:
+ *           [B,H,T] (TFLA_GLA_KEY: [B,H,T,d_qk])
+ *   li_out  log input gate [B,H,T]
+ *   g_out   a at the last step of each chunk: [B,H,ceil(T/L)]
+ *           (TFLA_GLA_KEY: [B,H,ceil(T/L),d_qk])
+ * For TFLA_SCALAR_DECAY the path computes these in closed form inside the
+ * other kernels; this hook evaluates the same closed form.
+ *
+ * tfla_dbg_states -- gates plus the inter-chunk state kernel.  states_out
+ * (device, fp32) receives the state after chunks 1..N_c-1 (N_c = ceil(T/L)),
+ * each stored TRANSPOSED as [d_hv][d_qk]: layout [B,H,N_c-1,d_hv,d_qk].
+ * q is not needed; h is untouched.
+ */
+int tfla_dbg_gates(const float* igate_pre, const float* fgate_pre,
+                   float* a_out, float* li_out, float* g_out,
+                   int B, int H, int T, int d_qk, int L, int variant, void* stream);
+int tfla_dbg_states(const void* k, const void* v,
+                    const float* igate_pre, const float* fgate_pre, float* states_out,
+                    int B, int H, int T, int d_qk, int d_hv, int L, int variant, void* stream);
+
+/* Static description of a status code. */
+const char* tfla_error_string(int code);
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* tfla_last_error(void);
+/* Library version as major*10000 + minor*100 + patch. */
+int tfla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TFLA_H */

@@ -1,0 +1,122 @@
+// gates.hip -- log-sigmoid gate prefix sums (first kernel of the path).
+//
+// For step t of chunk [t0, t0+L) the chunkwise form needs the log of the
+// forget-gate product since the chunk start and the log input gate:
+//   a_t  = sum_{r=t0..t} log f_r,   li_t = log i_t,   g = a at the chunk end
+// (for the per-key-channel gate, a and g are vectors over key channels).
+// Sums are chunk-local: the decay between two steps of one chunk is
+// exp(a_t - a_s), and exponent arguments stay small even for long sequences.
+// The mLSTMsig gates are sigmoids of the pre-activations (TFLA research-map
+// summary, Approach); the per-channel gate is logsigmoid(x)/16.
+#include "gfx950.hpp"
+#include "kernels.hpp"
+
+namespace tfla {
+namespace {
+
+// One wavefront per (chunk, head).  Lane j owns E = L/64 consecutive steps:
+// a serial prefix over its steps, then an exclusive scan of the lane totals
+// across the wavefront.
+__global__ __launch_bounds__(64) void gates_sig_kernel(const float* __restrict__ ig,
+                                                       const float* __restrict__ fg,
+                                                       float* __restrict__ a, float* __restrict__ li,
+                                                       float* __restrict__ g, int T, int L, int nc)
+{
+    const int kc = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    const int lane = threadIdx.x;
+    const int t0 = kc * L;
+    const int n = min(L, T - t0);
+    const int E = L >> 6;                     // L is a multiple of 64, <= 1024
+    const size_t base = bh * (size_t)T + t0;
+
+    float vals[16];
+    float run = 0.0f;
+    for (int e = 0; e < E; ++e) {
+        const int p = lane * E + e;
+        float lf = 0.0f;
+        if (p < n) lf = fmaxf(log_sigmoid(fg[base + p]), kLogForgetFloor);
+        run += lf;
+        vals[e] = run;
+    }
+    // exclusive scan of lane totals
+    float incl = run;
+    for (int off = 1; off < 64; off <<= 1) {
+        float o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    const float excl = incl - run;
+    for (int e = 0; e < E; ++e) {
+        const int p = lane * E + e;
+        if (p < n) {
+            a[base + p] = vals[e] + excl;
+            li[base + p] = log_sigmoid(ig[base + p]);
+        }
+    }
+    const float total = __shfl(incl, 63, 64);
+    if (lane == 0) g[bh * nc + kc] = total;
+}
+
+// Per-key-channel gate: one thread per (chunk, head, channel), serial over
+// the chunk's steps; consecutive threads read consecutive channels.
+__global__ __launch_bounds__(256) void gates_gla_kernel(const float* __restrict__ x,
+                                                        float* __restrict__ a, float* __restrict__ g,
+                                                        int T, int dqk, int L, int nc)
+{
+    const int kc = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    const int c = threadIdx.x;
+    if (c >= dqk) return;
+    const int t0 = kc * L;
+    const int n = min(L, T - t0);
+    size_t idx = (bh * (size_t)T + t0) * dqk + c;
+    float run = 0.0f;
+    for (int p = 0; p < n; ++p, idx += dqk) {
+        run += fmaxf(log_sigmoid(x[idx]) * (1.0f / 16.0f), kLogForgetFloor);
+        a[idx] = run;
+    }
+    g[(bh * nc + kc) * dqk + c] = run;
+}
+
+// Fixed per-head decay: a_t = (t - t0 + 1) log(gamma_h) in closed form.
+// Only the test hook materialises it; the other kernels evaluate the same
+// expression inline.
+__global__ void gates_scalar_kernel(const float* __restrict__ fg, float* __restrict__ a,
+                                    float* __restrict__ li, float* __restrict__ g, int H, int T,
+                                    int L, int nc)
+{
+    const size_t bh = blockIdx.y;
+    const float lgam = fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor);
+    for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < T; t += gridDim.x * blockDim.x) {
+        const int p = t % L;
+        a[bh * T + t] = (float)(p + 1) * lgam;
+        li[bh * T + t] = 0.0f;
+        if (p == L - 1 || t == T - 1) g[bh * nc + t / L] = (float)(p + 1) * lgam;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gates(const Problem& p, const float* igate_pre, const float* fgate_pre,
+                        const Workspace& ws, hipStream_t stream)
+{
+    const dim3 grid(p.nc, p.B * p.H);
+    if (p.gate == kSig) {
+        gates_sig_kernel<<<grid, 64, 0, stream>>>(igate_pre, fgate_pre, ws.a, ws.li, ws.g, p.T, p.L, p.nc);
+    } else if (p.gate == kGla) {
+        gates_gla_kernel<<<grid, 256, 0, stream>>>(fgate_pre, ws.a, ws.g, p.T, p.dqk, p.L, p.nc);
+    } else {
+        return hipSuccess;   // closed form, evaluated inside the consumers
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gates_closed_form(const Problem& p, const float* fgate_pre, float* a, float* li,
+                                    float* g, hipStream_t stream)
+{
+    const dim3 grid((p.T + 255) / 256, p.B * p.H);
+    gates_scalar_kernel<<<grid, 256, 0, stream>>>(fgate_pre, a, li, g, p.H, p.T, p.L, p.nc);
+    return hipGetLastError();
+}
+
+}  // namespace tfla

@@ -1,0 +1,39 @@
+// kernels.hpp -- host-side launchers of the libtfla kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace tfla {
+
+enum GateKind { kSig = 0, kScalar = 1, kGla = 2 };
+
+// Problem description shared by the launchers.  Sizes in elements.
+struct Problem {
+    int B, H, T, dqk, dhv, L;
+    int nc;          // number of chunks, ceil(T / L)
+    int gate;        // GateKind
+    bool bf16;       // element type of q, k, v, h
+};
+
+// Workspace carve-up (device pointers into one allocation).
+struct Workspace {
+    float* a;        // [B,H,T] (GLA: [B,H,T,dqk]) chunk-local log-forget sums; NULL for kScalar
+    float* li;       // [B,H,T] log input gate; kSig only
+    float* g;        // [B,H,nc] (GLA: [B,H,nc,dqk]); NULL for kScalar
+    float* states;   // [B,H,nc-1,dhv,dqk] fp32, transposed states
+};
+
+// Lays the workspace out from `base` (NULL: sizes only); returns its byte size.
+size_t workspace_layout(const Problem& p, Workspace* ws, char* base, bool with_states = true);
+
+hipError_t launch_gates(const Problem& p, const float* igate_pre, const float* fgate_pre,
+                        const Workspace& ws, hipStream_t stream);
+hipError_t launch_gates_closed_form(const Problem& p, const float* fgate_pre, float* a, float* li,
+                                    float* g, hipStream_t stream);
+hipError_t launch_state(const Problem& p, const void* k, const void* v, const float* fgate_pre,
+                        const Workspace& ws, hipStream_t stream);
+hipError_t launch_intra(const Problem& p, const void* q, const void* k, const void* v,
+                        const float* fgate_pre, const Workspace& ws, void* h, hipStream_t stream);
+
+}  // namespace tfla

@@ -1,0 +1,298 @@
+// tfla_api.cpp -- the C ABI declared in include/tfla.h: argument validation
+// (no HIP call before it passes), workspace sizing and carve-up, and the
+// three launches of the forward path on the caller's stream.
+#include "tfla.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg)
+{
+    g_last_error = msg;
+    return code;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+Range range_of(const void* p, size_t bytes)
+{
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + bytes};
+}
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Shape and variant checks shared by every entry point.  Fills *p.
+int check_problem(int B, int H, int T, int d_qk, int d_hv, int L, int variant, tfla::Problem* p)
+{
+    const int gate = variant & 0xff;
+    if ((variant & ~(0xff | TFLA_IO_BF16)) != 0 || gate > TFLA_GLA_KEY || gate < 0)
+        return fail(TFLA_ERR_INVALID_ARG, "unknown variant " + std::to_string(variant));
+    if (B < 1 || H < 1 || T < 1 || d_qk < 1 || d_hv < 1 || L < 1)
+        return fail(TFLA_ERR_INVALID_ARG, "B, H, T, d_qk, d_hv and L must be >= 1");
+    const bool bf16 = (variant & TFLA_IO_BF16) != 0;
+    if (!(d_qk == 64 || d_qk == 128 || (d_qk == 256 && bf16)))
+        return fail(TFLA_ERR_UNSUPPORTED, "d_qk must be 64, 128 or 256 (fp32 I/O: 64 or 128), got " +
+                                              std::to_string(d_qk));
+    if (d_hv % 64 != 0 || d_hv > (bf16 ? 512 : 256))
+        return fail(TFLA_ERR_UNSUPPORTED, "d_hv must be a multiple of 64 up to 512 (fp32 I/O: 256), got " +
+                                              std::to_string(d_hv));
+    if (!(L == 64 || L == 128 || L == 256 || L == 512 || L == 1024))
+        return fail(TFLA_ERR_UNSUPPORTED, "chunk size L must be 64, 128, 256, 512 or 1024, got " +
+                                              std::to_string(L));
+    const long long bh = (long long)B * H;
+    if (bh > 65535) return fail(TFLA_ERR_UNSUPPORTED, "B*H must be <= 65535");
+    const long long nqt = (T + 63) / 64;
+    if (bh * nqt * (d_hv / 64) > 0x7fffffffLL)
+        return fail(TFLA_ERR_UNSUPPORTED, "problem too large for one launch grid");
+    p->B = B;
+    p->H = H;
+    p->T = T;
+    p->dqk = d_qk;
+    p->dhv = d_hv;
+    p->L = L;
+    p->nc = (T + L - 1) / L;
+    p->gate = gate;
+    p->bf16 = bf16;
+    return TFLA_OK;
+}
+
+int check_gates(const tfla::Problem& p, const float* igate_pre, const float* fgate_pre)
+{
+    if (!fgate_pre) return fail(TFLA_ERR_INVALID_ARG, "fgate_pre is NULL");
+    if (!aligned(fgate_pre, 4)) return fail(TFLA_ERR_INVALID_ARG, "fgate_pre is not 4-byte aligned");
+    if (p.gate == tfla::kSig) {
+        if (!igate_pre) return fail(TFLA_ERR_INVALID_ARG, "igate_pre is NULL but the variant is mLSTMsig");
+        if (!aligned(igate_pre, 4)) return fail(TFLA_ERR_INVALID_ARG, "igate_pre is not 4-byte aligned");
+    } else if (igate_pre) {
+        return fail(TFLA_ERR_INVALID_ARG, "igate_pre must be NULL for this variant (input gate is 1)");
+    }
+    return TFLA_OK;
+}
+
+size_t gate_bytes(const tfla::Problem& p)
+{
+    const size_t bh = (size_t)p.B * p.H;
+    if (p.gate == tfla::kSig) return bh * p.T * 4;
+    if (p.gate == tfla::kScalar) return (size_t)p.H * 4;
+    return bh * p.T * p.dqk * 4;
+}
+
+int check_fwd(const void* q, const void* k, const void* v, const float* igate_pre, const float* fgate_pre,
+              const void* h, int B, int H, int T, int d_qk, int d_hv, int L, int variant, tfla::Problem* p)
+{
+    int rc = check_problem(B, H, T, d_qk, d_hv, L, variant, p);
+    if (rc) return rc;
+    if (!q || !k || !v || !h) return fail(TFLA_ERR_INVALID_ARG, "q, k, v and h must not be NULL");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(h, 16))
+        return fail(TFLA_ERR_INVALID_ARG, "q, k, v and h must be 16-byte aligned");
+    rc = check_gates(*p, igate_pre, fgate_pre);
+    if (rc) return rc;
+    const size_t esz = p->bf16 ? 2 : 4;
+    const size_t bht = (size_t)B * H * T;
+    const Range hr = range_of(h, bht * d_hv * esz);
+    if (overlaps(hr, range_of(q, bht * d_qk * esz)) || overlaps(hr, range_of(k, bht * d_qk * esz)) ||
+        overlaps(hr, range_of(v, bht * d_hv * esz)) || overlaps(hr, range_of(fgate_pre, gate_bytes(*p))) ||
+        (igate_pre && overlaps(hr, range_of(igate_pre, bht * 4))))
+        return fail(TFLA_ERR_INVALID_ARG, "h overlaps an input");
+    return TFLA_OK;
+}
+
+// Failure injection for tests of the error paths: TFLA_FAULT=alloc makes the
+// library's own workspace allocation fail before any launch.
+bool inject_alloc_fault()
+{
+    const char* f = std::getenv("TFLA_FAULT");
+    return f && std::strcmp(f, "alloc") == 0;
+}
+
+int hip_fail(hipError_t e, const char* what)
+{
+    return fail(TFLA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int run_path(const tfla::Problem& p, const void* q, const void* k, const void* v, const float* igate_pre,
+             const float* fgate_pre, void* h, const tfla::Workspace& ws, hipStream_t stream)
+{
+    hipError_t e = tfla::launch_gates(p, igate_pre, fgate_pre, ws, stream);
+    if (e != hipSuccess) return hip_fail(e, "gate kernel launch");
+    e = tfla::launch_state(p, k, v, fgate_pre, ws, stream);
+    if (e != hipSuccess) return hip_fail(e, "state kernel launch");
+    e = tfla::launch_intra(p, q, k, v, fgate_pre, ws, h, stream);
+    if (e != hipSuccess) return hip_fail(e, "intra-chunk kernel launch");
+    return TFLA_OK;
+}
+
+}  // namespace
+
+namespace tfla {
+
+size_t workspace_layout(const Problem& p, Workspace* ws, char* base, bool with_states)
+{
+    const size_t bh = (size_t)p.B * p.H;
+    const size_t w = p.gate == kGla ? p.dqk : 1;
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> float* {
+        float* ptr = base ? reinterpret_cast<float*>(base + off) : nullptr;
+        off += align256(bytes);
+        return ptr;
+    };
+    ws->a = p.gate == kScalar ? nullptr : take(bh * p.T * w * 4);
+    ws->li = p.gate == kSig ? take(bh * p.T * 4) : nullptr;
+    ws->g = p.gate == kScalar ? nullptr : take(bh * p.nc * w * 4);
+    ws->states = (with_states && p.nc > 1) ? take(bh * (size_t)(p.nc - 1) * p.dhv * p.dqk * 4) : nullptr;
+    return off;
+}
+
+}  // namespace tfla
+
+extern "C" {
+
+size_t tfla_workspace_bytes(int B, int H, int T, int d_qk, int d_hv, int L, int variant)
+{
+    tfla::Problem p;
+    if (check_problem(B, H, T, d_qk, d_hv, L, variant, &p) != TFLA_OK) return 0;
+    tfla::Workspace ws;
+    return tfla::workspace_layout(p, &ws, nullptr);
+}
+
+int tfla_fwd_ws(const void* q, const void* k, const void* v, const float* igate_pre, const float* fgate_pre,
+                void* h, int B, int H, int T, int d_qk, int d_hv, int L, int variant, void* workspace,
+                size_t workspace_bytes, void* stream)
+{
+    tfla::Problem p;
+    int rc = check_fwd(q, k, v, igate_pre, fgate_pre, h, B, H, T, d_qk, d_hv, L, variant, &p);
+    if (rc) return rc;
+    tfla::Workspace ws;
+    const size_t need = tfla::workspace_layout(p, &ws, nullptr);
+    if (need > 0 && (!workspace || !aligned(workspace, 256)))
+        return fail(TFLA_ERR_INVALID_ARG, "workspace is NULL or not 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(TFLA_ERR_OUT_OF_MEMORY, "workspace of " + std::to_string(workspace_bytes) +
+                                                " bytes is smaller than the " + std::to_string(need) + " needed");
+    tfla::workspace_layout(p, &ws, static_cast<char*>(workspace));
+    return run_path(p, q, k, v, igate_pre, fgate_pre, h, ws, static_cast<hipStream_t>(stream));
+}
+
+int tfla_fwd(const void* q, const void* k, const void* v, const float* igate_pre, const float* fgate_pre,
+             void* h, int B, int H, int T, int d_qk, int d_hv, int L, int variant, void* stream)
+{
+    tfla::Problem p;
+    int rc = check_fwd(q, k, v, igate_pre, fgate_pre, h, B, H, T, d_qk, d_hv, L, variant, &p);
+    if (rc) return rc;
+    tfla::Workspace ws;
+    const size_t need = tfla::workspace_layout(p, &ws, nullptr);
+    if (inject_alloc_fault()) return fail(TFLA_ERR_OUT_OF_MEMORY, "injected allocation failure (TFLA_FAULT=alloc)");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* base = nullptr;
+    if (need > 0) {
+        hipError_t e = hipMallocAsync(&base, need, s);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(TFLA_ERR_OUT_OF_MEMORY, std::string("workspace allocation of ") + std::to_string(need) +
+                                                    " bytes failed: " + hipGetErrorString(e));
+        }
+    }
+    tfla::workspace_layout(p, &ws, static_cast<char*>(base));
+    rc = run_path(p, q, k, v, igate_pre, fgate_pre, h, ws, s);
+    if (base) {
+        hipError_t e = hipFreeAsync(base, s);
+        if (e != hipSuccess && rc == TFLA_OK) rc = hip_fail(e, "workspace free");
+    }
+    return rc;
+}
+
+int tfla_dbg_gates(const float* igate_pre, const float* fgate_pre, float* a_out, float* li_out, float* g_out,
+                   int B, int H, int T, int d_qk, int L, int variant, void* stream)
+{
+    tfla::Problem p;
+    int rc = check_problem(B, H, T, d_qk, 64, L, variant, &p);
+    if (rc) return rc;
+    rc = check_gates(p, igate_pre, fgate_pre);
+    if (rc) return rc;
+    if (!a_out || !li_out || !g_out) return fail(TFLA_ERR_INVALID_ARG, "a_out, li_out and g_out must not be NULL");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (p.gate == tfla::kScalar) {
+        e = tfla::launch_gates_closed_form(p, fgate_pre, a_out, li_out, g_out, s);
+    } else {
+        tfla::Workspace ws{a_out, li_out, g_out, nullptr};
+        if (p.gate == tfla::kGla) {
+            e = hipMemsetAsync(li_out, 0, (size_t)B * H * T * 4, s);
+            if (e != hipSuccess) return hip_fail(e, "li_out clear");
+        }
+        e = tfla::launch_gates(p, igate_pre, fgate_pre, ws, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "gate kernel launch");
+    return TFLA_OK;
+}
+
+int tfla_dbg_states(const void* k, const void* v, const float* igate_pre, const float* fgate_pre, float* states_out,
+                    int B, int H, int T, int d_qk, int d_hv, int L, int variant, void* stream)
+{
+    tfla::Problem p;
+    int rc = check_problem(B, H, T, d_qk, d_hv, L, variant, &p);
+    if (rc) return rc;
+    rc = check_gates(p, igate_pre, fgate_pre);
+    if (rc) return rc;
+    if (!k || !v || !aligned(k, 16) || !aligned(v, 16))
+        return fail(TFLA_ERR_INVALID_ARG, "k and v must be non-NULL and 16-byte aligned");
+    if (p.nc > 1 && (!states_out || !aligned(states_out, 16)))
+        return fail(TFLA_ERR_INVALID_ARG, "states_out must be non-NULL and 16-byte aligned");
+    // gate sums in a private allocation; the states go straight to states_out
+    tfla::Workspace ws;
+    const size_t need = tfla::workspace_layout(p, &ws, nullptr, false);
+    if (inject_alloc_fault()) return fail(TFLA_ERR_OUT_OF_MEMORY, "injected allocation failure (TFLA_FAULT=alloc)");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* base = nullptr;
+    hipError_t e = hipSuccess;
+    if (need > 0) {
+        e = hipMallocAsync(&base, need, s);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(TFLA_ERR_OUT_OF_MEMORY, "workspace allocation failed");
+        }
+    }
+    tfla::workspace_layout(p, &ws, static_cast<char*>(base), false);
+    ws.states = states_out;
+    e = tfla::launch_gates(p, igate_pre, fgate_pre, ws, s);
+    if (e == hipSuccess) e = tfla::launch_state(p, k, v, fgate_pre, ws, s);
+    rc = e == hipSuccess ? TFLA_OK : hip_fail(e, "gate/state kernel launch");
+    if (base) {
+        e = hipFreeAsync(base, s);
+        if (e != hipSuccess && rc == TFLA_OK) rc = hip_fail(e, "workspace free");
+    }
+    return rc;
+}
+
+const char* tfla_error_string(int code)
+{
+    switch (code) {
+    case TFLA_OK: return "success";
+    case TFLA_ERR_INVALID_ARG: return "invalid argument";
+    case TFLA_ERR_UNSUPPORTED: return "unsupported shape or chunk size";
+    case TFLA_ERR_HIP: return "HIP runtime error";
+    case TFLA_ERR_OUT_OF_MEMORY: return "out of memory";
+    default: return "unknown status code";
+    }
+}
+
+const char* tfla_last_error(void) { return g_last_error.c_str(); }
+
+int tfla_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+"""The C-ABI boundary without a GPU: the library loads, exports every entry
+point include/tfla.h declares, and rejects bad arguments before any HIP call
+(so these run on a machine with no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tfla.h")
+
+tfla = pytest.importorskip("mlstm_sequence_amd.tfla")
+
+BF16 = 0x100
+SIG, SCALAR, GLA = 0, 1, 2
+INVALID, UNSUPPORTED, OOM = 1, 2, 4
+
+# 16-byte aligned fake device addresses: validation never dereferences them
+Q, K, V, H_, IG, FG, WS = (0x10000000 * (n + 1) for n in range(7))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tfla_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(tfla.LIB_PATH):
+        pytest.skip("libtfla.so not built")
+    return tfla.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert {"tfla_fwd", "tfla_fwd_ws", "tfla_workspace_bytes", "tfla_dbg_gates", "tfla_dbg_states",
+            "tfla_error_string", "tfla_last_error", "tfla_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_strings(L):
+    assert tfla.tfla_version() == 100
+    for code in range(5):
+        assert tfla.error_string(code)
+    assert tfla.error_string(99) == "unknown status code"
+
+
+def fwd(q=Q, k=K, v=V, ig=IG, fg=FG, h=H_, B=2, H=3, T=300, dqk=128, dhv=256, Lc=64, variant=SIG | BF16):
+    return tfla.lib().tfla_fwd(q, k, v, ig, fg, h, B, H, T, dqk, dhv, Lc, variant, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(variant=3), INVALID), (dict(variant=0x200), INVALID), (dict(variant=-1), INVALID),
+    (dict(B=0), INVALID), (dict(T=0), INVALID), (dict(H=-2), INVALID),
+    (dict(q=None), INVALID), (dict(h=None), INVALID), (dict(fg=None), INVALID),
+    (dict(q=Q + 8), INVALID), (dict(h=H_ + 2), INVALID), (dict(fg=FG + 2), INVALID),
+    (dict(ig=None), INVALID),                                   # mLSTMsig needs an input gate
+    (dict(variant=SCALAR | BF16), INVALID),                     # ... the others must not have one
+    (dict(h=Q + 64), INVALID), (dict(h=V - 32), INVALID),       # output overlaps an input
+    (dict(dqk=96), UNSUPPORTED), (dict(dqk=512), UNSUPPORTED), (dict(dhv=100), UNSUPPORTED),
+    (dict(dhv=576), UNSUPPORTED), (dict(Lc=32), UNSUPPORTED), (dict(Lc=96), UNSUPPORTED),
+    (dict(Lc=2048), UNSUPPORTED), (dict(variant=SIG, dqk=256), UNSUPPORTED),
+    (dict(variant=SIG, dhv=320), UNSUPPORTED), (dict(B=300, H=300), UNSUPPORTED),
+])
+def test_rejects_bad_arguments(L, kw, code):
+    assert fwd(**kw) == code
+    assert tfla.tfla_last_error()
+
+
+def test_injected_allocation_failure(L, monkeypatch):
+    monkeypatch.setenv("TFLA_FAULT", "alloc")
+    assert fwd() == OOM
+    assert "injected" in tfla.tfla_last_error()
+    assert L.tfla_dbg_states(K, V, IG, FG, WS, 2, 3, 300, 128, 256, 64, SIG | BF16, None) == OOM
+
+
+def test_workspace_bytes(L):
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    B, H, T, dqk, dhv, Lc = 2, 3, 300, 128, 256, 64
+    nc = -(-T // Lc)
+    sig = a256(B * H * T * 4) * 2 + a256(B * H * nc * 4) + a256(B * H * (nc - 1) * dhv * dqk * 4)
+    assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16) == sig
+    scal = a256(B * H * (nc - 1) * dhv * dqk * 4)
+    assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SCALAR | BF16) == scal
+    gla = a256(B * H * T * dqk * 4) + a256(B * H * nc * dqk * 4) + scal
+    assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, GLA | BF16) == gla
+    assert tfla.tfla_workspace_bytes(B, H, 64, dqk, dhv, Lc, SCALAR | BF16) == 0   # one chunk, no state
+    assert tfla.tfla_workspace_bytes(B, H, T, 96, dhv, Lc, SIG) == 0
+
+
+def test_fwd_ws_checks_workspace(L):
+    need = tfla.tfla_workspace_bytes(2, 3, 300, 128, 256, 64, SIG | BF16)
+    rc = L.tfla_fwd_ws(Q, K, V, IG, FG, H_, 2, 3, 300, 128, 256, 64, SIG | BF16, WS, need - 1, None)
+    assert rc == OOM
+    rc = L.tfla_fwd_ws(Q, K, V, IG, FG, H_, 2, 3, 300, 128, 256, 64, SIG | BF16, None, need, None)
+    assert rc == INVALID
+    rc = L.tfla_fwd_ws(Q, K, V, IG, FG, H_, 2, 3, 300, 128, 256, 64, SIG | BF16, WS + 16, need, None)
+    assert rc == INVALID
+
+
+def test_python_binding_raises(L):
+    with pytest.raises(tfla.TflaError) as ei:
+        tfla.tfla_fwd(Q, K, V, IG, FG, H_, 2, 3, 300, 96, 256, 64, SIG | BF16, stream=0)
+    assert ei.value.code == UNSUPPORTED
