@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Throughput of the chunkwise mLSTMsig forward pass on one GPU.
+
+One step = one tfla_fwd_ws call (gate prefix sums, inter-chunk states,
+intra-chunk outputs) over the whole workload, inputs and workspace already
+resident in HBM.  Default workload: mLSTMsig, B=4, H=8, T=8192, d_qk=256,
+d_hv=512, bf16 I/O, at the best of the chunk sizes 64/128/256 (all chunk
+sizes are swept and reported).  Prints one JSON line on stdout; progress
+goes to stderr.
+
+Roofline accounting (per launch, algorithmic = what the chunkwise method
+must move or compute, not what the kernels happen to execute):
+  flops  state kernel : 2 d_qk d_hv per step of chunks 1..N_c-1
+         intra kernel : 2 d_qk d_hv per step of chunks 2..N_c  (q C_{k-1})
+                        + n(n+1)(d_qk + d_hv) per chunk of n steps (causal QK^T and PV)
+  bytes  gate kernel  : gate pre-activations in, a and li out (16 B per step) + g
+         state kernel : k, v of chunks 1..N_c-1 in, a and li in, fp32 states out
+         intra kernel : q, k, v in, h out, fp32 states in, a and li in
+The dominant kernel (longest average duration, measured with HIP events
+recorded around each launch on the stream it runs on) is reported against
+the HBM peak (8 TB/s) when its arithmetic intensity is below the bf16
+matrix-core ridge (2.5 PFLOP/s / 8 TB/s), else against the matrix-core peak.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "mLSTMsig chunkwise fwd tokens/s at T=8192; % of bf16 MFMA peak, 1 MI355X"
+PEAK_BF16 = 2.5e15      # dense bf16 matrix-core FLOP/s, MI355X
+PEAK_FP32 = 157.3e12    # dense fp32 matrix-core FLOP/s
+PEAK_HBM = 8.0e12       # HBM3E bytes/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------- model
+def chunk_lengths(T, L):
+    nc = -(-T // L)
+    return [min(L, T - k * L) for k in range(nc)]
+
+
+def kernel_model(wl, L):
+    """Algorithmic flops and bytes per launch of each kernel (whole workload)."""
+    e = 2 if wl.dtype_name == "bf16" else 4
+    bh = wl.B * wl.H
+    n = chunk_lengths(wl.T, L)
+    T, dqk, dhv = wl.T, wl.dqk, wl.dhv
+    steps_state = sum(n[:-1])           # steps whose chunk feeds a materialised state
+    steps_inter = sum(n[1:])            # steps that read a state
+    st_bytes = 4 * dqk * dhv * (len(n) - 1)
+    # per-step gate sums read by the consumers: a and li (mLSTMsig), a per
+    # key channel (GLA), none for the closed-form fixed decay
+    gstep = {0: 8, 1: 0, 2: 4 * dqk}[wl.variant]
+    gchunk = {0: 4, 1: 0, 2: 4 * dqk}[wl.variant] * len(n)
+    gin = {0: 8, 1: 0, 2: 4 * dqk}[wl.variant] * T
+    gates = {"flops": 0, "bytes": bh * (gin + gstep * T + gchunk)}
+    state = {"flops": bh * 2 * dqk * dhv * steps_state,
+             "bytes": bh * ((dqk + dhv) * e * steps_state + gstep * steps_state + gchunk + st_bytes)}
+    intra_f = 2 * dqk * dhv * steps_inter + sum(m * (m + 1) * (dqk + dhv) for m in n)
+    intra = {"flops": bh * intra_f,
+             "bytes": bh * ((2 * dqk + dhv) * e * T + dhv * e * T + st_bytes + gstep * T)}
+    return {"gates": gates, "state": state, "intra": intra}
+
+
+def total_flops(wl, L):
+    m = kernel_model(wl, L)
+    return sum(v["flops"] for v in m.values())
+
+
+# --------------------------------------------------------------------------- GPU timing
+def run_gpu(wl, L, steps, warmup, inputs_dev):
+    import torch
+    from mlstm_sequence_amd import tfla
+
+    q, k, v = inputs_dev["q"], inputs_dev["k"], inputs_dev["v"]
+    ig, fg = inputs_dev["igate_pre"], inputs_dev["fgate_pre"]
+    gate = {0: tfla.MLSTM_SIG, 1: tfla.SCALAR_DECAY, 2: tfla.GLA_KEY}[wl.variant]
+    var = tfla.variant_of(gate, q.dtype)
+    h = torch.empty((wl.B, wl.H, wl.T, wl.dhv), dtype=q.dtype, device=q.device)
+    ws = tfla.workspace_for(q, v, gate, L)
+    nbytes = ws.numel()
+    stream = torch.cuda.current_stream()
+    args = (q, k, v, ig, fg, h, wl.B, wl.H, wl.T, wl.dqk, wl.dhv, L, var, ws, nbytes)
+
+    for _ in range(warmup):
+        tfla.tfla_fwd_ws(*args)
+    torch.cuda.synchronize()
+
+    marks = []
+    for _ in range(steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for ev in evs:
+            ev.record(stream)          # creates the event; the library re-records it
+        marks.append(evs)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        tfla.tfla_fwd_ws_marked(*args, [ev.cuda_event for ev in marks[i]])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms = start.elapsed_time(end) / steps
+    per = {"gates": 0.0, "state": 0.0, "intra": 0.0}
+    for evs in marks:
+        per["gates"] += evs[0].elapsed_time(evs[1])
+        per["state"] += evs[1].elapsed_time(evs[2])
+        per["intra"] += evs[2].elapsed_time(evs[3])
+    per = {kname: t / steps for kname, t in per.items()}
+    del ws, h
+    return ms, wall / steps * 1e3, per
+
+
+# --------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(wl, target_s=15.0):
+    """The oracle (plain C recurrence in double, OpenMP over heads) on all
+    heads of the workload for its first T' steps; its cost is linear in T', so
+    tokens/s over T' is its throughput on the whole sequence."""
+    import oracle
+    import workloads as W
+
+    def run(Tp):
+        sub = wl.with_(T=Tp)
+        inp = W.make_inputs(sub)
+        arrs = [W.as_f64(inp[n]) for n in ("q", "k", "v", "igate_pre", "fgate_pre")]
+        t0 = time.perf_counter()
+        oracle.recurrent_fwd(*arrs, wl.variant)
+        return time.perf_counter() - t0
+
+    t_cal = run(256)
+    Tp = int(min(wl.T, max(256, 256 * round(target_s / max(t_cal, 1e-3)))))
+    Tp = min(wl.T, (Tp // 256) * 256 or 256)
+    dt = run(Tp) if Tp != 256 else t_cal
+    threads = oracle.threads()
+    return {"value": wl.B * Tp / dt, "unit": "tokens/s", "cores": min(threads, wl.B * wl.H),
+            "kind": "oracle", "seconds": round(dt, 3), "host_threads": threads,
+            "sample": f"all {wl.B * wl.H} (b,h) heads of the workload, first {Tp} of {wl.T} steps "
+                      f"(seed-identical inputs); OpenMP over heads, {min(threads, wl.B * wl.H)} threads busy"}
+
+
+def traffic_for(kernel, wl, L):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, only
+    when they were taken on the current source of that kernel."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    key = f"{kernel}:{wl.name}:L{L}"
+    r = rec.get(key)
+    if not r or r.get("src_sha") != source_sha(kernel):
+        return None
+    return r.get("bytes_per_launch")
+
+
+def source_sha(kernel):
+    files = {"gates": ["gates.hip"], "state": ["state.hip"], "intra": ["intra.hip"]}[kernel]
+    hs = hashlib.sha256()
+    for f in files + ["gfx950.hpp"]:
+        with open(os.path.join(ROOT, "mlstm_sequence_amd", "csrc", f), "rb") as fh:
+            hs.update(fh.read())
+    return hs.hexdigest()[:16]
+
+
+# --------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload index (1..5)")
+    ap.add_argument("--L", type=int, default=None, help="headline chunk size (default: best listed)")
+    ap.add_argument("--sweep", type=str, default=None, help="comma-separated chunk sizes to sweep")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); every head "
+              "is independent, so the per-GPU shard of a multi-GPU run is this same kernel at fewer heads",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+
+    wl = W.WORKLOADS[args.config]
+
+    listed = list(wl.chunk_sizes)
+    sweep = [int(x) for x in args.sweep.split(",")] if args.sweep else sorted(
+        set(listed + ([512, 1024] if args.config == 3 else [])))
+    if args.L is not None and args.L not in sweep:
+        sweep.append(args.L)
+
+    log(f"workload {wl.name}: B={wl.B} H={wl.H} T={wl.T} d_qk={wl.dqk} d_hv={wl.dhv} {wl.dtype_name}; "
+        f"chunk sizes {sweep}")
+    inputs = W.make_inputs(wl)
+    dev = {n: (None if t is None else t.cuda()) for n, t in inputs.items()}
+    torch.cuda.synchronize()
+
+    results = {}
+    for L in sweep:
+        ms, wall_ms, per = run_gpu(wl, L, args.steps, args.warmup, dev)
+        tps = wl.B * wl.T / (ms * 1e-3)
+        fl = total_flops(wl, L)
+        results[L] = {"ms": ms, "wall_ms": wall_ms, "per": per, "tokens_per_s": tps,
+                      "mfma_frac": fl / (ms * 1e-3) / PEAK_BF16}
+        log(f"L={L}: {ms:.3f} ms/step, {tps:.4g} tokens/s, {results[L]['mfma_frac'] * 100:.2f}% of bf16 peak "
+            f"(gates {per['gates']:.3f} ms, state {per['state']:.3f} ms, intra {per['intra']:.3f} ms)")
+
+    if args.L is not None:
+        Lh = args.L
+    else:
+        Lh = max((L for L in listed if L in results), key=lambda L: results[L]["tokens_per_s"])
+    r = results[Lh]
+    model = kernel_model(wl, Lh)
+    dom = max(("gates", "state", "intra"), key=lambda k: r["per"][k])
+    dm = model[dom]
+    dt = r["per"][dom] * 1e-3
+    peak_f = PEAK_BF16 if wl.dtype_name == "bf16" else PEAK_FP32
+    mfma_bound = dm["flops"] / peak_f > dm["bytes"] / PEAK_HBM
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": dm["flops"] / dt / 1e12, "peak": peak_f / 1e12, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": dm["bytes"] / dt / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    tr = traffic_for(dom, wl, Lh)
+    roof["traffic"] = tr
+    roof.update({"kernel": dom, "ms_per_launch": r["per"][dom], "algorithmic_bytes": dm["bytes"],
+                 "algorithmic_flops": dm["flops"]})
+
+    out = {
+        "metric": METRIC,
+        "value": r["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype_name,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "d_qk": wl.dqk, "d_hv": wl.dhv,
+                   "L": Lh, "variant": W.VARIANT_NAMES[wl.variant], "io": wl.dtype_name},
+        "mfma_frac": r["mfma_frac"],
+        "roofline": roof,
+        "kernels_ms": r["per"],
+        "sweep": {str(L): {"tokens_per_s": x["tokens_per_s"], "ms_per_step": x["ms"],
+                           "mfma_frac": x["mfma_frac"], "kernels_ms": x["per"]} for L, x in results.items()},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(wl)
+        log(f"oracle: {out['cpu_baseline']['value']:.4g} tokens/s ({out['cpu_baseline']['sample']})")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

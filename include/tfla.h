@@ -103,6 +103,16 @@ int tfla_fwd_ws(const void* q, const void* k, const void* v,
                 int B, int H, int T, int d_qk, int d_hv, int L, int variant,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* tfla_fwd_ws with timing marks for profiling: `marks` points to four
+ * hipEvent_t (created by the caller) that are recorded on `stream` before
+ * the gate kernel, after it, after the state kernel and after the
+ * intra-chunk kernel, so the caller can time each kernel on the stream it
+ * runs on.  marks == NULL behaves exactly like tfla_fwd_ws. */
+int tfla_fwd_ws_marked(const void* q, const void* k, const void* v,
+                       const float* igate_pre, const float* fgate_pre, void* h,
+                       int B, int H, int T, int d_qk, int d_hv, int L, int variant,
+                       void* workspace, size_t workspace_bytes, void* const* marks, void* stream);
+
 /*
  * Test hooks: run part of the path and copy its intermediate out.
  *

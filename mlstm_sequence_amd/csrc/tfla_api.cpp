@@ -125,16 +125,28 @@ int hip_fail(hipError_t e, const char* what)
     return fail(TFLA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-int run_path(const tfla::Problem& p, const void* q, const void* k, const void* v, const float* igate_pre,
-             const float* fgate_pre, void* h, const tfla::Workspace& ws, hipStream_t stream)
+int mark(void* const* marks, int i, hipStream_t stream)
 {
+    if (!marks) return TFLA_OK;
+    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(marks[i]), stream);
+    return e == hipSuccess ? TFLA_OK : hip_fail(e, "timing mark");
+}
+
+int run_path(const tfla::Problem& p, const void* q, const void* k, const void* v, const float* igate_pre,
+             const float* fgate_pre, void* h, const tfla::Workspace& ws, hipStream_t stream,
+             void* const* marks = nullptr)
+{
+    int rc = mark(marks, 0, stream);
+    if (rc) return rc;
     hipError_t e = tfla::launch_gates(p, igate_pre, fgate_pre, ws, stream);
     if (e != hipSuccess) return hip_fail(e, "gate kernel launch");
+    if ((rc = mark(marks, 1, stream))) return rc;
     e = tfla::launch_state(p, k, v, fgate_pre, ws, stream);
     if (e != hipSuccess) return hip_fail(e, "state kernel launch");
+    if ((rc = mark(marks, 2, stream))) return rc;
     e = tfla::launch_intra(p, q, k, v, fgate_pre, ws, h, stream);
     if (e != hipSuccess) return hip_fail(e, "intra-chunk kernel launch");
-    return TFLA_OK;
+    return mark(marks, 3, stream);
 }
 
 }  // namespace
@@ -174,6 +186,14 @@ int tfla_fwd_ws(const void* q, const void* k, const void* v, const float* igate_
                 void* h, int B, int H, int T, int d_qk, int d_hv, int L, int variant, void* workspace,
                 size_t workspace_bytes, void* stream)
 {
+    return tfla_fwd_ws_marked(q, k, v, igate_pre, fgate_pre, h, B, H, T, d_qk, d_hv, L, variant, workspace,
+                              workspace_bytes, nullptr, stream);
+}
+
+int tfla_fwd_ws_marked(const void* q, const void* k, const void* v, const float* igate_pre,
+                       const float* fgate_pre, void* h, int B, int H, int T, int d_qk, int d_hv, int L,
+                       int variant, void* workspace, size_t workspace_bytes, void* const* marks, void* stream)
+{
     tfla::Problem p;
     int rc = check_fwd(q, k, v, igate_pre, fgate_pre, h, B, H, T, d_qk, d_hv, L, variant, &p);
     if (rc) return rc;
@@ -185,7 +205,7 @@ int tfla_fwd_ws(const void* q, const void* k, const void* v, const float* igate_
         return fail(TFLA_ERR_OUT_OF_MEMORY, "workspace of " + std::to_string(workspace_bytes) +
                                                 " bytes is smaller than the " + std::to_string(need) + " needed");
     tfla::workspace_layout(p, &ws, static_cast<char*>(workspace));
-    return run_path(p, q, k, v, igate_pre, fgate_pre, h, ws, static_cast<hipStream_t>(stream));
+    return run_path(p, q, k, v, igate_pre, fgate_pre, h, ws, static_cast<hipStream_t>(stream), marks);
 }
 
 int tfla_fwd(const void* q, const void* k, const void* v, const float* igate_pre, const float* fgate_pre,

@@ -42,6 +42,8 @@ def lib():
         L.tfla_fwd.restype = i
         L.tfla_fwd_ws.argtypes = [vp, vp, vp, fp, fp, vp] + [i] * 7 + [vp, sz, vp]
         L.tfla_fwd_ws.restype = i
+        L.tfla_fwd_ws_marked.argtypes = [vp, vp, vp, fp, fp, vp] + [i] * 7 + [vp, sz, vp, vp]
+        L.tfla_fwd_ws_marked.restype = i
         L.tfla_workspace_bytes.argtypes = [i] * 7
         L.tfla_workspace_bytes.restype = sz
         L.tfla_dbg_gates.argtypes = [fp, fp, fp, fp, fp] + [i] * 6 + [vp]
@@ -116,6 +118,18 @@ def tfla_fwd_ws(q, k, v, igate_pre, fgate_pre, h, B, H, T, d_qk, d_hv, L, varian
                            B, H, T, d_qk, d_hv, L, variant, _ptr(workspace), workspace_bytes,
                            _stream(stream))
     _check(rc, "tfla_fwd_ws")
+
+
+def tfla_fwd_ws_marked(q, k, v, igate_pre, fgate_pre, h, B, H, T, d_qk, d_hv, L, variant, workspace,
+                       workspace_bytes, marks, stream=None):
+    """``marks``: four raw hipEvent_t handles (ints), or None."""
+    arr = None
+    if marks is not None:
+        arr = (ctypes.c_void_p * 4)(*marks)
+    rc = lib().tfla_fwd_ws_marked(_ptr(q), _ptr(k), _ptr(v), _ptr(igate_pre), _ptr(fgate_pre), _ptr(h),
+                                  B, H, T, d_qk, d_hv, L, variant, _ptr(workspace), workspace_bytes, arr,
+                                  _stream(stream))
+    _check(rc, "tfla_fwd_ws_marked")
 
 
 def tfla_dbg_gates(igate_pre, fgate_pre, a_out, li_out, g_out, B, H, T, d_qk, L, variant, stream=None):

@@ -49,6 +49,10 @@ class Workload:
     def tokens(self) -> int:
         return self.B * self.T
 
+    @property
+    def dtype_name(self) -> str:
+        return "bf16" if self.dtype == torch.bfloat16 else "fp32"
+
 
 # The five workloads.  Seeds are 1000 + index.
 WORKLOADS = {
