@@ -10,8 +10,12 @@
 // and loops over the 64-step key/value tiles at or before its own, so the
 // chunk size L is bounded by nothing on chip.
 //
+// Every stage (a block of C^T, or a K/V tile) is software-pipelined: its
+// global loads are issued into registers right after the previous stage was
+// written to LDS, so they are in flight while the matrix cores work.
+//
 // Per workgroup (4 wavefronts, wave w owns query rows 16w..16w+15):
-//   inter: acc = Q C_{k-1}[:, v-tile]  (C^T staged in LDS per 64-channel
+//   inter: acc = Q C_{k-1}[:, v-tile]  (C^T staged in LDS per 32-channel
 //          block, rounded fp32 -> operand type), rows scaled by e^{a_t};
 //   intra: for each key tile j <= own tile: stage K_j (row-major) and V_j^T
 //          in LDS; S^T = K_j Q^T on matrix cores (Q fragments stay in
@@ -26,6 +30,8 @@
 // scale q by e^{a_t - a_ref} and k by e^{a_ref - a_s} with a_ref at the step
 // before the query tile (both factors <= 1); the diagonal tile uses the
 // tile's middle step.
+#include <cstdlib>
+
 #include "gfx950.hpp"
 #include "kernels.hpp"
 
@@ -39,21 +45,35 @@ template <typename T, int DQK, int BV> struct IntraLds {
             T ks[64][DQK + pad];   // K tile, row-major [step][channel]
             T vt[BV][64 + pad];    // V tile transposed [value][step]
         } kv;
-        T cs[BV][64 + pad];        // 64-channel block of C^T [value][channel]
+        T cs[BV][32 + pad];        // 32-channel block of C^T [value][channel]
     };
     float bcol[64];                // mLSTMsig: (li_s - a_s) log2(e) per key step
 };
 
+// Registers holding one stage's global loads while the previous stage computes.
+template <typename T, int DQK, int BV> struct Prefetch {
+    static constexpr int VEC = Elem<T>::vec;
+    static constexpr int NC = BV / 64;                     // C^T block: 8 floats per item
+    static constexpr int NK = 64 * DQK / VEC / 256;        // K tile: 16 bytes per item
+    static constexpr int NV = 32 * (BV / VEC) / 256;       // V tile: two rows x 16 bytes per item
+    static_assert(NC >= 1 && NK >= 1 && NV >= 1, "tile too small for 256 threads");
+    f32x4 c[NC][2];
+    Vec16<T> k[NK];
+    Vec16<T> v[NV][2];
+    float li, a;
+};
+
 template <typename T, int GATE, int DQK, int BV>
-__global__ __launch_bounds__(256) void intra_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                                                    const T* __restrict__ v, const float* __restrict__ a,
-                                                    const float* __restrict__ li,
-                                                    const float* __restrict__ fg,
-                                                    const float* __restrict__ states, T* __restrict__ h,
-                                                    int H, int T_, int dhv, int L, int nc, float scale)
+__global__ __launch_bounds__(256, (BV >= 256 ? 1 : 2)) void intra_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                       const T* __restrict__ v, const float* __restrict__ a,
+                                                       const float* __restrict__ li,
+                                                       const float* __restrict__ fg,
+                                                       const float* __restrict__ states, T* __restrict__ h,
+                                                       int H, int T_, int dhv, int L, int nc, float scale)
 {
     __shared__ IntraLds<T, DQK, BV> sm;
     typedef typename Elem<T>::frag Frag;
+    typedef Prefetch<T, DQK, BV> PF;
     constexpr int VEC = Elem<T>::vec;
     constexpr int KQ = DQK / 32;   // contraction steps over key channels
     constexpr int NT = BV / 16;    // 16-wide output column tiles
@@ -77,8 +97,11 @@ __global__ __launch_bounds__(256) void intra_kernel(const T* __restrict__ q, con
     const T* kb = k + bh * (size_t)T_ * DQK;
     const T* vb = v + bh * (size_t)T_ * dhv;
     const float* ab = (GATE == kGla) ? a + bh * (size_t)T_ * DQK : a + bh * (size_t)T_;
+    const float* lb = (GATE == kSig) ? li + bh * (size_t)T_ : nullptr;
     float lg2 = 0.0f;   // log2 of the fixed decay
     if (GATE == kScalar) lg2 = fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor) * kLog2e;
+
+    PF pf;
 
     // Q fragments; per-channel gate: q * e^{a_t - a_ref} (ref_row < 0: chunk start, a = 0)
     Frag qf[KQ];
@@ -102,33 +125,95 @@ __global__ __launch_bounds__(256) void intra_kernel(const T* __restrict__ q, con
         }
     };
 
+    // ---- stage loaders (global -> registers) and writers (registers -> LDS)
+    auto fetch_c = [&](const float* st, int cb) {
+#pragma unroll
+        for (int u = 0; u < PF::NC; ++u) {
+            const int idx = tid + 256 * u, vr = idx >> 2, c8 = (idx & 3) * 8;
+            const float* src = st + (size_t)vr * DQK + cb + c8;
+            pf.c[u][0] = *reinterpret_cast<const f32x4*>(src);
+            pf.c[u][1] = *reinterpret_cast<const f32x4*>(src + 4);
+        }
+    };
+    auto store_c = [&]() {
+#pragma unroll
+        for (int u = 0; u < PF::NC; ++u) {
+            const int idx = tid + 256 * u, vr = idx >> 2, c8 = (idx & 3) * 8;
+            if constexpr (sizeof(T) == 2) {
+                Vec16<T> x;
+                for (int e = 0; e < 4; ++e) {
+                    x.set(e, pf.c[u][0][e]);
+                    x.set(4 + e, pf.c[u][1][e]);
+                }
+                x.store(&sm.cs[vr][c8]);
+            } else {
+                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(&sm.cs[vr][c8])) = pf.c[u][0];
+                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(&sm.cs[vr][c8 + 4])) = pf.c[u][1];
+            }
+        }
+    };
+    auto fetch_kv = [&](int s0) {
+#pragma unroll
+        for (int u = 0; u < PF::NK; ++u) {
+            const int idx = tid + 256 * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
+            const int s = s0 + r;
+            if (s < T_) pf.k[u].load(kb + (size_t)s * DQK + c); else pf.k[u].zero();
+        }
+#pragma unroll
+        for (int u = 0; u < PF::NV; ++u) {
+            const int idx = tid + 256 * u, sp = idx & 31, cg = (idx >> 5) * VEC;
+            const int s = s0 + 2 * sp;
+            if (s < T_) pf.v[u][0].load(vb + (size_t)s * dhv + v0 + cg); else pf.v[u][0].zero();
+            if (s + 1 < T_) pf.v[u][1].load(vb + (size_t)(s + 1) * dhv + v0 + cg); else pf.v[u][1].zero();
+        }
+        if (GATE == kSig && tid < 64) {
+            const int s = s0 + tid;
+            pf.li = (s < T_) ? lb[s] : 0.0f;
+            pf.a = (s < T_) ? ab[s] : 0.0f;
+        }
+    };
+    auto store_kv = [&](int s0, int ref_row) {
+#pragma unroll
+        for (int u = 0; u < PF::NK; ++u) {
+            const int idx = tid + 256 * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
+            if (GATE == kGla) {
+                const int s = s0 + r;
+                if (s < T_) {
+                    for (int e = 0; e < VEC; ++e) {
+                        const float ex = ab[(size_t)ref_row * DQK + c + e] - ab[(size_t)s * DQK + c + e];
+                        pf.k[u].set(e, pf.k[u].get(e) * exp2_fast(ex * kLog2e));
+                    }
+                }
+            }
+            pf.k[u].store(&sm.kv.ks[r][c]);
+        }
+#pragma unroll
+        for (int u = 0; u < PF::NV; ++u) {
+            const int idx = tid + 256 * u, sp = idx & 31, cg = (idx >> 5) * VEC;
+            for (int e = 0; e < VEC; ++e)
+                store2(&sm.kv.vt[cg + e][2 * sp], pf.v[u][0].get(e), pf.v[u][1].get(e));
+        }
+        if (GATE == kSig && tid < 64) sm.bcol[tid] = (pf.li - pf.a) * kLog2e;
+    };
+
     f32x4 acc[NT];
     for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // ---------------- inter-chunk term: e^{a_t} q_t^T C_{k-1}
     if (kc > 0) {
-        load_q(-1);
         const float* st = states + ((bh * (nc - 1) + kc - 1) * (size_t)dhv + v0) * DQK;
-        for (int cb = 0; cb < DQK; cb += 64) {
+        fetch_c(st, 0);
+        load_q(-1);
+        for (int kq = 0; kq < KQ; ++kq) {
             __syncthreads();
-            for (int it = tid; it < BV * 8; it += 256) {
-                const int vr = it >> 3, c8 = (it & 7) * 8;
-                const float* src = st + (size_t)vr * DQK + cb + c8;
-                const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-                const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
-                T* dst = &sm.cs[vr][c8];
-                for (int e = 0; e < 4; ++e) {
-                    dst[e] = from_float<T>(x0[e]);
-                    dst[4 + e] = from_float<T>(x1[e]);
-                }
-            }
+            store_c();
             __syncthreads();
-            for (int kk = 0; kk < 2; ++kk) {
-                const int kq = cb / 32 + kk;
-                for (int nt = 0; nt < NT; ++nt) {
-                    const Frag bf = load8(&sm.cs[16 * nt + l16][32 * kk + 8 * gq]);
-                    acc[nt] = mma(qf[kq], bf, acc[nt]);
-                }
+            // the next stage's loads fly while this block is multiplied
+            if (kq + 1 < KQ) fetch_c(st, 32 * (kq + 1));
+            else fetch_kv(cs);
+            for (int nt = 0; nt < NT; ++nt) {
+                const Frag bf = load8(&sm.cs[16 * nt + l16][8 * gq]);
+                acc[nt] = mma(qf[kq], bf, acc[nt]);
             }
         }
         if (GATE != kGla) {
@@ -142,10 +227,14 @@ __global__ __launch_bounds__(256) void intra_kernel(const T* __restrict__ q, con
                 for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= e;
             }
         }
+    } else {
+        fetch_kv(cs);
     }
 
     // ---------------- intra-chunk term, tiled along the chunk
-    if (GATE != kGla) load_q(-1);
+    if (GATE != kGla) {
+        if (kc == 0) load_q(-1);
+    }
     const float at2 = (GATE == kSig && tq_ok) ? ab[tq] * kLog2e : 0.0f;
     const int tl = 16 * w + l16;            // query row inside the tile
 
@@ -158,38 +247,9 @@ __global__ __launch_bounds__(256) void intra_kernel(const T* __restrict__ q, con
             if (j == 0 || diag) load_q(ref_row);
         }
         __syncthreads();
-        // K tile, row-major; per-channel gate: k * e^{a_ref - a_s}
-        for (int it = tid; it < 64 * (DQK / VEC); it += 256) {
-            const int r = it / (DQK / VEC), c = (it % (DQK / VEC)) * VEC;
-            const int s = s0 + r;
-            Vec16<T> x;
-            if (s < T_) {
-                x.load(kb + (size_t)s * DQK + c);
-                if (GATE == kGla) {
-                    for (int e = 0; e < VEC; ++e) {
-                        const float ex = ab[(size_t)ref_row * DQK + c + e] - ab[(size_t)s * DQK + c + e];
-                        x.set(e, x.get(e) * exp2_fast(ex * kLog2e));
-                    }
-                }
-            } else {
-                x.zero();
-            }
-            x.store(&sm.kv.ks[r][c]);
-        }
-        // V tile, transposed; step pairs fastest
-        for (int it = tid; it < 32 * (BV / VEC); it += 256) {
-            const int sp = it & 31, cg = (it >> 5) * VEC;
-            const int s = s0 + 2 * sp;
-            Vec16<T> x0, x1;
-            if (s < T_) x0.load(vb + (size_t)s * dhv + v0 + cg); else x0.zero();
-            if (s + 1 < T_) x1.load(vb + (size_t)(s + 1) * dhv + v0 + cg); else x1.zero();
-            for (int e = 0; e < VEC; ++e) store2(&sm.kv.vt[cg + e][2 * sp], x0.get(e), x1.get(e));
-        }
-        if (GATE == kSig && tid < 64) {
-            const int s = s0 + tid;
-            sm.bcol[tid] = (s < T_) ? (li[bh * (size_t)T_ + s] - ab[s]) * kLog2e : 0.0f;
-        }
+        store_kv(s0, ref_row);
         __syncthreads();
+        if (!diag) fetch_kv(s0 + 64);
 
         // S^T (64 key steps x 16 query rows of this wave)
         f32x4 st[4];
@@ -215,15 +275,15 @@ __global__ __launch_bounds__(256) void intra_kernel(const T* __restrict__ q, con
         }
         // acc += P V_j, step index contracted in accumulator order
         for (int kk = 0; kk < 2; ++kk) {
-            Frag pf;
+            Frag pfr;
             for (int e = 0; e < 4; ++e) {
-                frag_set(pf, e, st[2 * kk][e]);
-                frag_set(pf, 4 + e, st[2 * kk + 1][e]);
+                frag_set(pfr, e, st[2 * kk][e]);
+                frag_set(pfr, 4 + e, st[2 * kk + 1][e]);
             }
             for (int nt = 0; nt < NT; ++nt) {
                 const T* row = sm.kv.vt[16 * nt + l16];
                 const Frag vf = load4x2(row + 32 * kk + 4 * gq, row + 32 * kk + 16 + 4 * gq);
-                acc[nt] = mma(pf, vf, acc[nt]);
+                acc[nt] = mma(pfr, vf, acc[nt]);
             }
         }
     }
@@ -250,13 +310,31 @@ hipError_t launch_intra_t(const Problem& p, const void* q, const void* k, const 
     return hipGetLastError();
 }
 
+// Value-tile width: the widest of 128 / 64 dividing d_hv.  128 keeps two
+// workgroups per CU; 256 (one workgroup per CU, no recomputed S across value
+// tiles) measured slower.  TFLA_INTRA_BV=64|128|256 overrides (bf16 I/O only
+// for 256) for tuning sweeps.
+inline int intra_bv(const Problem& p)
+{
+    int cap = 128;
+    if (const char* e = std::getenv("TFLA_INTRA_BV")) {
+        const int want = std::atoi(e);
+        if (want == 64 || want == 128 || want == 256) cap = (want == 256 && !p.bf16) ? 128 : want;
+    }
+    for (int bv = cap; bv >= 64; bv /= 2)
+        if (p.dhv % bv == 0) return bv;
+    return 64;
+}
+
 template <typename T, int GATE, int DQK>
 hipError_t dispatch_bv(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
                        const Workspace& ws, void* h, hipStream_t stream)
 {
-    constexpr int kMaxBV = sizeof(T) == 2 ? 256 : 128;
-    if (kMaxBV >= 256 && p.dhv % 256 == 0) return launch_intra_t<T, GATE, DQK, (kMaxBV >= 256 ? 256 : 128)>(p, q, k, v, fg, ws, h, stream);
-    if (p.dhv % 128 == 0) return launch_intra_t<T, GATE, DQK, 128>(p, q, k, v, fg, ws, h, stream);
+    const int bv = intra_bv(p);
+    if constexpr (sizeof(T) == 2) {
+        if (bv == 256) return launch_intra_t<T, GATE, DQK, 256>(p, q, k, v, fg, ws, h, stream);
+    }
+    if (bv >= 128) return launch_intra_t<T, GATE, DQK, 128>(p, q, k, v, fg, ws, h, stream);
     return launch_intra_t<T, GATE, DQK, 64>(p, q, k, v, fg, ws, h, stream);
 }
 

@@ -16,6 +16,8 @@
 // tile in accumulator registers.  Per 64-step block of a chunk it stages V^T
 // and (w.K)^T in LDS, transposing on the way (K is scaled in fp32 and then
 // rounded, once, to the operand type).  Wave w owns value rows 16w..16w+15.
+// The block loop is software-pipelined: the next block's global loads are
+// issued right after the current block reaches LDS.
 #include "gfx950.hpp"
 #include "kernels.hpp"
 
@@ -32,6 +34,19 @@ template <typename T> struct StateLds {
     T kt[kTile][row];   // (w.K)^T block: [key channel][step]
 };
 
+// One 64-step block's global loads, held in registers while the previous
+// block is multiplied.  Item = two consecutive steps x VEC columns.
+template <typename T, int GATE> struct StatePrefetch {
+    static constexpr int VEC = Elem<T>::vec;
+    static constexpr int NI = (kSB / 2) * (kTile / VEC) / 256;
+    static_assert(NI >= 1, "block too small for 256 threads");
+    Vec16<T> v[NI][2], k[NI][2];
+    float a[NI][2], li[NI][2];                 // mLSTMsig step gates
+    f32x4 ga[NI][2][VEC / 4];                  // per-channel gate: a of the item's columns
+    f32x4 gg[NI][VEC / 4];                     // per-channel gate: g of the item's columns
+    float g;                                   // mLSTMsig: g of the block's chunk
+};
+
 template <typename T, int GATE>
 __global__ __launch_bounds__(256) void state_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                     const float* __restrict__ a,
@@ -42,6 +57,7 @@ __global__ __launch_bounds__(256) void state_kernel(const T* __restrict__ k, con
                                                     int dqk, int dhv, int L, int nc)
 {
     __shared__ StateLds<T> sm;
+    typedef StatePrefetch<T, GATE> PF;
     constexpr int VEC = Elem<T>::vec;
 
     const int ntv = dhv / kTile, ntk = dqk / kTile;
@@ -53,82 +69,125 @@ __global__ __launch_bounds__(256) void state_kernel(const T* __restrict__ k, con
     const int c0 = (tile % ntk) * kTile;
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, gq = lane >> 4, li16 = lane & 15;
+    const int w = tid >> 6, lane = tid & 63, gq = lane >> 4, l16 = lane & 15;
 
     const T* kb = k + bh * (size_t)T_ * dqk;
     const T* vb = v + bh * (size_t)T_ * dhv;
-    float lgam = 0.0f;
-    if (GATE == kScalar) lgam = fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor);
+    float lg2 = 0.0f;
+    if (GATE == kScalar) lg2 = fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor) * kLog2e;
+
+    const int bpc = L / kSB;                 // blocks per chunk
+    const int nblocks = (nc - 1) * bpc;      // chunks 0..nc-2 are full and feed a state
+
+    PF pf;
+    auto item = [&](int u, int& sp, int& cg) {
+        const int idx = tid + 256 * u;
+        sp = idx % (kSB / 2);                // step pair fastest: transposed LDS writes spread over banks
+        cg = (idx / (kSB / 2)) * VEC;
+    };
+    auto fetch = [&](int b) {
+        const int kc = b / bpc;
+        const int s0 = b * kSB;              // block start (chunks are full, so = kc*L + (b%bpc)*kSB)
+        if (GATE == kSig) pf.g = g[bh * nc + kc];
+#pragma unroll
+        for (int u = 0; u < PF::NI; ++u) {
+            int sp, cg;
+            item(u, sp, cg);
+            const int s = s0 + 2 * sp;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                pf.v[u][r].load(vb + (size_t)(s + r) * dhv + v0 + cg);
+                pf.k[u][r].load(kb + (size_t)(s + r) * dqk + c0 + cg);
+                if (GATE == kSig) {
+                    pf.a[u][r] = a[bh * T_ + s + r];
+                    pf.li[u][r] = li[bh * T_ + s + r];
+                }
+                if (GATE == kGla) {
+                    const float* ar = a + (bh * T_ + s + r) * (size_t)dqk + c0 + cg;
+                    for (int e4 = 0; e4 < VEC / 4; ++e4) pf.ga[u][r][e4] = *reinterpret_cast<const f32x4*>(ar + 4 * e4);
+                }
+            }
+            if (GATE == kGla) {
+                const float* gr = g + (bh * nc + kc) * (size_t)dqk + c0 + cg;
+                for (int e4 = 0; e4 < VEC / 4; ++e4) pf.gg[u][e4] = *reinterpret_cast<const f32x4*>(gr + 4 * e4);
+            }
+        }
+    };
+    auto store = [&](int b) {
+        const int kc = b / bpc;
+        const int cs = kc * L;
+#pragma unroll
+        for (int u = 0; u < PF::NI; ++u) {
+            int sp, cg;
+            item(u, sp, cg);
+            const int s = b * kSB + 2 * sp;
+            float w0 = 1.0f, w1 = 1.0f;
+            if (GATE == kSig) {
+                w0 = exp2_fast((pf.g - pf.a[u][0] + pf.li[u][0]) * kLog2e);
+                w1 = exp2_fast((pf.g - pf.a[u][1] + pf.li[u][1]) * kLog2e);
+            } else if (GATE == kScalar) {
+                const int p0 = s - cs;
+                w0 = exp2_fast((float)(L - 1 - p0) * lg2);
+                w1 = exp2_fast((float)(L - 2 - p0) * lg2);
+            }
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                const int col = cg + e;
+                store2(&sm.vt[col][2 * sp], pf.v[u][0].get(e), pf.v[u][1].get(e));
+                float kw0, kw1;
+                if (GATE == kGla) {
+                    const float gc = pf.gg[u][e / 4][e % 4];
+                    kw0 = pf.k[u][0].get(e) * exp2_fast((gc - pf.ga[u][0][e / 4][e % 4]) * kLog2e);
+                    kw1 = pf.k[u][1].get(e) * exp2_fast((gc - pf.ga[u][1][e / 4][e % 4]) * kLog2e);
+                } else {
+                    kw0 = pf.k[u][0].get(e) * w0;
+                    kw1 = pf.k[u][1].get(e) * w1;
+                }
+                store2(&sm.kt[col][2 * sp], kw0, kw1);
+            }
+        }
+    };
 
     f32x4 acc[4];
     for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int kc = 0; kc + 1 < nc; ++kc) {
-        const int cs = kc * L;
-        // decay of the carried state across chunk kc
-        if (GATE == kSig) {
-            const float e = exp2_fast(g[bh * nc + kc] * kLog2e);
-            for (int nt = 0; nt < 4; ++nt) acc[nt] *= e;
-        } else if (GATE == kScalar) {
-            const float e = exp2_fast((float)L * lgam * kLog2e);
-            for (int nt = 0; nt < 4; ++nt) acc[nt] *= e;
-        } else {
-            for (int nt = 0; nt < 4; ++nt) {
-                const int c = c0 + nt * 16 + li16;
-                acc[nt] *= exp2_fast(g[(bh * nc + kc) * dqk + c] * kLog2e);
-            }
-        }
-        const float gk = (GATE == kSig) ? g[bh * nc + kc] : 0.0f;
-
-        for (int sb = 0; sb < L; sb += kSB) {
-            __syncthreads();
-            // stage: items = (kSB/2 step pairs) x (kTile/VEC column groups),
-            // step pair fastest so the transposed LDS writes spread over banks
-            constexpr int CG = kTile / VEC;
-            for (int it = tid; it < (kSB / 2) * CG; it += 256) {
-                const int sp = it % (kSB / 2), cg = it / (kSB / 2);
-                const int s = cs + sb + 2 * sp;        // always < T: chunk kc is full
-                Vec16<T> v0r, v1r, k0r, k1r;
-                v0r.load(vb + (size_t)s * dhv + v0 + cg * VEC);
-                v1r.load(vb + (size_t)(s + 1) * dhv + v0 + cg * VEC);
-                k0r.load(kb + (size_t)s * dqk + c0 + cg * VEC);
-                k1r.load(kb + (size_t)(s + 1) * dqk + c0 + cg * VEC);
-                float w0 = 1.0f, w1 = 1.0f;
-                if (GATE == kSig) {
-                    w0 = exp2_fast((gk - a[bh * T_ + s] + li[bh * T_ + s]) * kLog2e);
-                    w1 = exp2_fast((gk - a[bh * T_ + s + 1] + li[bh * T_ + s + 1]) * kLog2e);
-                } else if (GATE == kScalar) {
-                    const int p0 = s - cs;
-                    w0 = exp2_fast((float)(L - 1 - p0) * lgam * kLog2e);
-                    w1 = exp2_fast((float)(L - 2 - p0) * lgam * kLog2e);
-                }
-                for (int e = 0; e < VEC; ++e) {
-                    const int col = cg * VEC + e;
-                    store2(&sm.vt[col][2 * sp], v0r.get(e), v1r.get(e));
-                    float kw0 = k0r.get(e) * w0, kw1 = k1r.get(e) * w1;
-                    if (GATE == kGla) {
-                        const size_t gi = (bh * nc + kc) * dqk + c0 + col;
-                        const float gc = g[gi];
-                        kw0 = k0r.get(e) * exp2_fast((gc - a[(bh * T_ + s) * dqk + c0 + col]) * kLog2e);
-                        kw1 = k1r.get(e) * exp2_fast((gc - a[(bh * T_ + s + 1) * dqk + c0 + col]) * kLog2e);
-                    }
-                    store2(&sm.kt[col][2 * sp], kw0, kw1);
-                }
-            }
-            __syncthreads();
-            // acc[nt] (value rows 16w.., key cols 16nt..) += V^T (w.K)
-            for (int ks = 0; ks < kSB; ks += 32) {
-                const auto af = load8(&sm.vt[16 * w + li16][ks + 8 * gq]);
+    if (nblocks > 0) fetch(0);
+    for (int b = 0; b < nblocks; ++b) {
+        const int kc = b / bpc;
+        const bool first = (b % bpc) == 0, last = (b % bpc) == bpc - 1;
+        __syncthreads();
+        store(b);
+        __syncthreads();
+        if (b + 1 < nblocks) fetch(b + 1);
+        if (first) {
+            // decay of the carried state across chunk kc
+            if (GATE == kSig) {
+                const float e = exp2_fast(g[bh * nc + kc] * kLog2e);
+                for (int nt = 0; nt < 4; ++nt) acc[nt] *= e;
+            } else if (GATE == kScalar) {
+                const float e = exp2_fast((float)L * lg2);
+                for (int nt = 0; nt < 4; ++nt) acc[nt] *= e;
+            } else {
                 for (int nt = 0; nt < 4; ++nt) {
-                    const auto bf = load8(&sm.kt[16 * nt + li16][ks + 8 * gq]);
-                    acc[nt] = mma(af, bf, acc[nt]);
+                    const int c = c0 + nt * 16 + l16;
+                    acc[nt] *= exp2_fast(g[(bh * nc + kc) * dqk + c] * kLog2e);
                 }
             }
         }
-        // write C^T tile of the state after chunk kc
-        float* dst = states + ((bh * (nc - 1) + kc) * (size_t)dhv + v0 + 16 * w + 4 * gq) * dqk + c0 + li16;
-        for (int nt = 0; nt < 4; ++nt)
-            for (int r = 0; r < 4; ++r) dst[(size_t)r * dqk + 16 * nt] = acc[nt][r];
+        // acc[nt] (value rows 16w.., key cols 16nt..) += V^T (w.K)
+        for (int ks = 0; ks < kSB; ks += 32) {
+            const auto af = load8(&sm.vt[16 * w + l16][ks + 8 * gq]);
+            for (int nt = 0; nt < 4; ++nt) {
+                const auto bf = load8(&sm.kt[16 * nt + l16][ks + 8 * gq]);
+                acc[nt] = mma(af, bf, acc[nt]);
+            }
+        }
+        if (last) {
+            // C^T tile of the state after chunk kc
+            float* dst = states + ((bh * (nc - 1) + kc) * (size_t)dhv + v0 + 16 * w + 4 * gq) * dqk + c0 + l16;
+            for (int nt = 0; nt < 4; ++nt)
+                for (int r = 0; r < 4; ++r) dst[(size_t)r * dqk + 16 * nt] = acc[nt][r];
+        }
     }
 }
 
