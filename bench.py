@@ -188,7 +188,20 @@ def main():
     ap.add_argument("--L", type=int, default=None, help="headline chunk size (default: best listed)")
     ap.add_argument("--sweep", type=str, default=None, help="comma-separated chunk sizes to sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (scales HBM byte counters)")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "dispatches": 3}), flush=True)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

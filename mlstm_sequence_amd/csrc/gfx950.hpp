@@ -1,7 +1,7 @@
 // gfx950.hpp -- device-side building blocks for the libtfla kernels (CDNA4,
 // 64-lane wavefronts, matrix-core instructions with fp32 accumulation).
 //
-// Fragment convention used by every kernel.  A 16x16 output tile is produced
+// Fragment conventions.  A 16x16 output tile is produced
 // by v_mfma_f32_16x16x32_bf16 from:
 //   A (16 x 32, M x K): lane l holds A[l%16][8*(l/16) + e], e = 0..7
 //   B (32 x 16, K x N): lane l holds B[8*(l/16) + e][l%16], e = 0..7
@@ -10,6 +10,17 @@
 // issues eight v_mfma_f32_16x16x4_f32, the e-th one contracting the K
 // indices {e, 8+e, 16+e, 24+e}; the sum over e is the same contraction, so a
 // kernel written once serves both element types.
+//
+// 32x32 tiles (v_mfma_f32_32x32x16_bf16; fp32: eight v_mfma_f32_32x32x2_f32):
+//   A (32 x 16): lane l holds A[l%32][8*(l/32) + e], e = 0..7
+//   B (16 x 32): lane l holds B[8*(l/32) + e][l%32]
+//   D (32 x 32): lane l holds D[8*(r/4) + 4*(l/32) + r%4][l%32], r = 0..15
+//
+// LDS transpose read (ds_read_b64_tr_b16): within each 16-lane group, output
+// lane j element r is element j%4 of the 8 bytes addressed by lane 4r + j/4.
+// With lane i of a group pointing at row (base + i/4), column (c0 + 4*(i%4))
+// of a row-major 16-bit tile, lane j receives column c0 + j, rows base..base+3:
+// a matrix-core operand fragment read straight from a row-major tile.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,6 +34,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 // Floor of the log forget gate: a gate below e^-100 acts as e^-100, which
@@ -65,6 +78,66 @@ __device__ __forceinline__ f32x4 mma(const Elem<float>::frag& a, const Elem<floa
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[2], b.hi[2], c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[3], b.hi[3], c, 0, 0, 0);
     return c;
+}
+
+// ---- matrix-core step on a 32x32 tile: acc += A * B over K = 16 ----------
+__device__ __forceinline__ f32x16 mma32(const bf16x8& a, const bf16x8& b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma32(const Elem<float>::frag& a, const Elem<float>::frag& b, f32x16 c)
+{
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[0], b.lo[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[1], b.lo[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[2], b.lo[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[3], b.lo[3], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[0], b.hi[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[1], b.hi[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[2], b.hi[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[3], b.hi[3], c, 0, 0, 0);
+    return c;
+}
+
+// ---- LDS transpose read ------------------------------------------------------
+// Four 16-bit elements of a row-major LDS tile, transposed across the lane's
+// 16-lane group (see the convention above).  `p` must point into LDS.
+__device__ __forceinline__ bf16x4 tr_read4(const bf16* p)
+{
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+// Operand fragment of a 32x32x16 product read from a row-major LDS tile
+// whose rows run along the contraction index (e.g. V[step][value] as the B
+// operand of P V, or both operands of V^T K): the 16-row block at `row0`,
+// the 32 columns at `col0`.  Element e of lane l holds row
+// row0 + 4h + e (e < 4) or row0 + 8 + 4h + (e - 4) (e >= 4), h = l/32, and
+// column col0 + l%32 -- the order in which a 32x32 accumulator holds its
+// rows, so an accumulator reused as the other operand contracts consistently.
+template <int LD>
+__device__ __forceinline__ bf16x8 frag_tr(const bf16 (*t)[LD], int row0, int col0, int lane)
+{
+    const int G = lane >> 4, i = lane & 15, h = G >> 1;
+    const int col = col0 + 16 * (G & 1) + 4 * (i & 3);
+    const int r = row0 + 4 * h + (i >> 2);
+    const bf16x4 lo = tr_read4(&t[r][col]);
+    const bf16x4 hi = tr_read4(&t[r + 8][col]);
+    bf16x8 f;
+    f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
+    f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
+    return f;
+}
+template <int LD>
+__device__ __forceinline__ Elem<float>::frag frag_tr(const float (*t)[LD], int row0, int col0, int lane)
+{
+    const int h = lane >> 5, col = col0 + (lane & 31);
+    Elem<float>::frag f;
+    for (int e = 0; e < 4; ++e) {
+        f.lo[e] = t[row0 + 4 * h + e][col];
+        f.hi[e] = t[row0 + 8 + 4 * h + e][col];
+    }
+    return f;
 }
 
 // ---- fragment element access ----------------------------------------------

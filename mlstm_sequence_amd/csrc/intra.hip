@@ -6,30 +6,30 @@
 // (GLA gate: the decay enters per key channel inside q.k, and the inter term
 // is (q_t o e^{a_t}) C_{k-1}).  TFLA's second level of sequence parallelism
 // (TFLA abstract; research-map summary, Approach) tiles this along the
-// sequence: a workgroup owns 64 query steps x BV value columns of one chunk
-// and loops over the 64-step key/value tiles at or before its own, so the
+// sequence: a workgroup owns BQ query steps x BV value columns of one chunk
+// and loops over the 64-step key/value tiles up to its own rows, so the
 // chunk size L is bounded by nothing on chip.
 //
-// Every stage (a block of C^T, or a K/V tile) is software-pipelined: its
-// global loads are issued into registers right after the previous stage was
-// written to LDS, so they are in flight while the matrix cores work.
-//
-// Per workgroup (4 wavefronts, wave w owns query rows 16w..16w+15):
-//   inter: acc = Q C_{k-1}[:, v-tile]  (C^T staged in LDS per 32-channel
-//          block, rounded fp32 -> operand type), rows scaled by e^{a_t};
-//   intra: for each key tile j <= own tile: stage K_j (row-major) and V_j^T
-//          in LDS; S^T = K_j Q^T on matrix cores (Q fragments stay in
-//          registers, they are the B operand here and the A operand of the
-//          inter product); decay and causal mask applied in fp32 (a select,
-//          never a multiply by 0); the S^T accumulators are reused directly
-//          as the A operand of acc += P V_j, by contracting the step index in
-//          the order the accumulator layout holds it (V_j^T is read in the
-//          same order);
+// Workgroup = NW wavefronts, wave w owning query rows 32w..32w+31 (BQ = 32 NW);
+// all products are 32x32x16 matrix-core tiles:
+//   inter: acc = Q C_{k-1}[:, v-tile]; C^T is staged in LDS per CW-channel
+//          block (fp32 -> operand type, RNE); Q fragments stay in registers
+//          (A operand here, B operand of S^T below); rows scaled by e^{a_t}.
+//   intra: per key tile j: K_j and V_j staged row-major in LDS; per 32-step
+//          half: S^T = K Q^T, decay and causal mask in fp32 (a select, never
+//          a multiply by 0), and the S^T accumulators reused in place as the A
+//          operand of acc += P V_j -- the step index is contracted in the
+//          order the accumulator holds it, and V_j is read in that order with
+//          LDS transpose reads.  Halves entirely above the diagonal are
+//          skipped per wave.
 //   out:   h = acc * scale, rounded to the I/O type.
-// Per-channel gates use a reference-point factorisation: off-diagonal tiles
-// scale q by e^{a_t - a_ref} and k by e^{a_ref - a_s} with a_ref at the step
-// before the query tile (both factors <= 1); the diagonal tile uses the
-// tile's middle step.
+// Every stage (a block of C^T, a K/V tile) is software-pipelined: its global
+// loads are issued into registers right after the previous stage reached
+// LDS, with consecutive lanes on consecutive 16-byte pieces of a row.
+// Per-channel gates use a reference-point factorisation: tiles wholly before
+// the query tile scale q by e^{a_t - a_ref} and k by e^{a_ref - a_s} with
+// a_ref at the step before the query tile (both factors <= 1); tiles that
+// overlap it use the tile's middle step.
 #include <cstdlib>
 
 #include "gfx950.hpp"
@@ -38,59 +38,65 @@
 namespace tfla {
 namespace {
 
-template <typename T, int DQK, int BV> struct IntraLds {
-    static constexpr int pad = 16 / sizeof(T);
+template <typename T, int DQK, int BV, int CW> struct IntraLds {
+    static constexpr int kpad = 16 / sizeof(T);   // K / C^T rows: stride = 4 banks mod 32
+    static constexpr int vpad = 32 / sizeof(T);   // V rows: stride = 8 banks mod 32 (transpose reads)
     union {
         struct {
-            T ks[64][DQK + pad];   // K tile, row-major [step][channel]
-            T vt[BV][64 + pad];    // V tile transposed [value][step]
+            T ks[64][DQK + kpad];   // K tile [step][channel]
+            T vs[64][BV + vpad];    // V tile [step][value]
         } kv;
-        T cs[BV][32 + pad];        // 32-channel block of C^T [value][channel]
+        T cs[BV][CW + kpad];        // CW-channel block of C^T [value][channel]
     };
-    float bcol[64];                // mLSTMsig: (li_s - a_s) log2(e) per key step
+    float bcol[64];                 // mLSTMsig: (li_s - a_s) log2(e) per key step
 };
 
-// Registers holding one stage's global loads while the previous stage computes.
-template <typename T, int DQK, int BV> struct Prefetch {
+// One stage's global loads, held in registers while the previous stage computes.
+template <typename T, int DQK, int BV, int CW, int NTH> struct Prefetch {
     static constexpr int VEC = Elem<T>::vec;
-    static constexpr int NC = BV / 64;                     // C^T block: 8 floats per item
-    static constexpr int NK = 64 * DQK / VEC / 256;        // K tile: 16 bytes per item
-    static constexpr int NV = 32 * (BV / VEC) / 256;       // V tile: two rows x 16 bytes per item
-    static_assert(NC >= 1 && NK >= 1 && NV >= 1, "tile too small for 256 threads");
+    static constexpr int NC = BV * CW / 8 / NTH;          // C^T block: 8 floats per item
+    static constexpr int NK = 64 * DQK / VEC / NTH;       // K tile: 16 bytes per item
+    static constexpr int NV = 64 * BV / VEC / NTH;        // V tile: 16 bytes per item
+    static_assert(NC >= 1 && NK >= 1 && NV >= 1, "tile too small for the workgroup");
     f32x4 c[NC][2];
     Vec16<T> k[NK];
-    Vec16<T> v[NV][2];
+    Vec16<T> v[NV];
     float li, a;
 };
 
-template <typename T, int GATE, int DQK, int BV>
-__global__ __launch_bounds__(256, (BV >= 256 ? 1 : 2)) void intra_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                                                       const T* __restrict__ v, const float* __restrict__ a,
-                                                       const float* __restrict__ li,
-                                                       const float* __restrict__ fg,
-                                                       const float* __restrict__ states, T* __restrict__ h,
-                                                       int H, int T_, int dhv, int L, int nc, float scale)
+template <typename T, int GATE, int DQK, int BV, int NW>
+__global__ __launch_bounds__(64 * NW, NW >= 4 ? 2 : 1) void intra_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                           const T* __restrict__ v, const float* __restrict__ a,
+                                                           const float* __restrict__ li,
+                                                           const float* __restrict__ fg,
+                                                           const float* __restrict__ states,
+                                                           T* __restrict__ h, int H, int T_, int dhv, int L,
+                                                           int nc, float scale)
 {
-    __shared__ IntraLds<T, DQK, BV> sm;
-    typedef typename Elem<T>::frag Frag;
-    typedef Prefetch<T, DQK, BV> PF;
+    constexpr int NTH = 64 * NW;
+    constexpr int BQ = 32 * NW;           // query rows per workgroup
+    constexpr int CW = NW >= 4 ? 64 : 32; // C^T channels per stage
+    constexpr int KQ = DQK / 16;          // 16-channel contraction steps
+    constexpr int NT = BV / 32;           // 32-wide output column tiles
     constexpr int VEC = Elem<T>::vec;
-    constexpr int KQ = DQK / 32;   // contraction steps over key channels
-    constexpr int NT = BV / 16;    // 16-wide output column tiles
+    typedef typename Elem<T>::frag Frag;
+    typedef IntraLds<T, DQK, BV, CW> Lds;
+    typedef Prefetch<T, DQK, BV, CW, NTH> PF;
+    __shared__ Lds sm;
 
-    const int nqt = (T_ + 63) >> 6;
+    const int nqt = (T_ + BQ - 1) / BQ;
     const int nvt = dhv / BV;
     const int blk = xcd_remap(blockIdx.x, gridDim.x);
     const size_t bh = blk / (nqt * nvt);
     const int rem = blk % (nqt * nvt);
     const int qt = rem / nvt;
     const int v0 = (rem % nvt) * BV;
-    const int t0 = qt * 64;
-    const int kc = t0 / L, cs = kc * L, qi = (t0 - cs) >> 6;
+    const int t0 = qt * BQ;
+    const int kc = t0 / L, cs = kc * L;
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, gq = lane >> 4, l16 = lane & 15;
-    const int tq = t0 + 16 * w + l16;       // query step of this lane's fragment row
+    const int w = tid >> 6, lane = tid & 63, hh = lane >> 5, i32 = lane & 31;
+    const int tq = t0 + 32 * w + i32;      // query step of this lane's fragment row
     const bool tq_ok = tq < T_;
 
     const T* qb = q + bh * (size_t)T_ * DQK;
@@ -103,11 +109,13 @@ __global__ __launch_bounds__(256, (BV >= 256 ? 1 : 2)) void intra_kernel(const T
 
     PF pf;
 
-    // Q fragments; per-channel gate: q * e^{a_t - a_ref} (ref_row < 0: chunk start, a = 0)
+    // Q fragments (lane row tq, channels 16 kq + 8 hh ..); per-channel gate:
+    // q * e^{a_t - a_ref} (ref_row < 0: the chunk start, where a = 0)
     Frag qf[KQ];
     auto load_q = [&](int ref_row) {
+#pragma unroll
         for (int kq = 0; kq < KQ; ++kq) {
-            const int c = 32 * kq + 8 * gq;
+            const int c = 16 * kq + 8 * hh;
             if (!tq_ok) {
                 for (int e = 0; e < 8; ++e) frag_set(qf[kq], e, 0.0f);
                 continue;
@@ -129,7 +137,7 @@ __global__ __launch_bounds__(256, (BV >= 256 ? 1 : 2)) void intra_kernel(const T
     auto fetch_c = [&](const float* st, int cb) {
 #pragma unroll
         for (int u = 0; u < PF::NC; ++u) {
-            const int idx = tid + 256 * u, vr = idx >> 2, c8 = (idx & 3) * 8;
+            const int idx = tid + NTH * u, vr = idx / (CW / 8), c8 = (idx % (CW / 8)) * 8;
             const float* src = st + (size_t)vr * DQK + cb + c8;
             pf.c[u][0] = *reinterpret_cast<const f32x4*>(src);
             pf.c[u][1] = *reinterpret_cast<const f32x4*>(src + 4);
@@ -138,7 +146,7 @@ __global__ __launch_bounds__(256, (BV >= 256 ? 1 : 2)) void intra_kernel(const T
     auto store_c = [&]() {
 #pragma unroll
         for (int u = 0; u < PF::NC; ++u) {
-            const int idx = tid + 256 * u, vr = idx >> 2, c8 = (idx & 3) * 8;
+            const int idx = tid + NTH * u, vr = idx / (CW / 8), c8 = (idx % (CW / 8)) * 8;
             if constexpr (sizeof(T) == 2) {
                 Vec16<T> x;
                 for (int e = 0; e < 4; ++e) {
@@ -155,16 +163,15 @@ __global__ __launch_bounds__(256, (BV >= 256 ? 1 : 2)) void intra_kernel(const T
     auto fetch_kv = [&](int s0) {
 #pragma unroll
         for (int u = 0; u < PF::NK; ++u) {
-            const int idx = tid + 256 * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
+            const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
             const int s = s0 + r;
             if (s < T_) pf.k[u].load(kb + (size_t)s * DQK + c); else pf.k[u].zero();
         }
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
-            const int idx = tid + 256 * u, sp = idx & 31, cg = (idx >> 5) * VEC;
-            const int s = s0 + 2 * sp;
-            if (s < T_) pf.v[u][0].load(vb + (size_t)s * dhv + v0 + cg); else pf.v[u][0].zero();
-            if (s + 1 < T_) pf.v[u][1].load(vb + (size_t)(s + 1) * dhv + v0 + cg); else pf.v[u][1].zero();
+            const int idx = tid + NTH * u, r = idx / (BV / VEC), c = (idx % (BV / VEC)) * VEC;
+            const int s = s0 + r;
+            if (s < T_) pf.v[u].load(vb + (size_t)s * dhv + v0 + c); else pf.v[u].zero();
         }
         if (GATE == kSig && tid < 64) {
             const int s = s0 + tid;
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(256, (BV >= 256 ? 1 : 2)) void intra_kernel(const T
     auto store_kv = [&](int s0, int ref_row) {
 #pragma unroll
         for (int u = 0; u < PF::NK; ++u) {
-            const int idx = tid + 256 * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
+            const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
             if (GATE == kGla) {
                 const int s = s0 + r;
                 if (s < T_) {
@@ -189,41 +196,48 @@ __global__ __launch_bounds__(256, (BV >= 256 ? 1 : 2)) void intra_kernel(const T
         }
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
-            const int idx = tid + 256 * u, sp = idx & 31, cg = (idx >> 5) * VEC;
-            for (int e = 0; e < VEC; ++e)
-                store2(&sm.kv.vt[cg + e][2 * sp], pf.v[u][0].get(e), pf.v[u][1].get(e));
+            const int idx = tid + NTH * u, r = idx / (BV / VEC), c = (idx % (BV / VEC)) * VEC;
+            pf.v[u].store(&sm.kv.vs[r][c]);
         }
         if (GATE == kSig && tid < 64) sm.bcol[tid] = (pf.li - pf.a) * kLog2e;
     };
 
-    f32x4 acc[NT];
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x16 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+        for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
 
     // ---------------- inter-chunk term: e^{a_t} q_t^T C_{k-1}
     if (kc > 0) {
         const float* st = states + ((bh * (nc - 1) + kc - 1) * (size_t)dhv + v0) * DQK;
         fetch_c(st, 0);
         load_q(-1);
-        for (int kq = 0; kq < KQ; ++kq) {
+        for (int cb = 0; cb < DQK; cb += CW) {
             __syncthreads();
             store_c();
             __syncthreads();
             // the next stage's loads fly while this block is multiplied
-            if (kq + 1 < KQ) fetch_c(st, 32 * (kq + 1));
+            if (cb + CW < DQK) fetch_c(st, cb + CW);
             else fetch_kv(cs);
-            for (int nt = 0; nt < NT; ++nt) {
-                const Frag bf = load8(&sm.cs[16 * nt + l16][8 * gq]);
-                acc[nt] = mma(qf[kq], bf, acc[nt]);
+#pragma unroll
+            for (int kk = 0; kk < CW / 16; ++kk) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const Frag bf = load8(&sm.cs[32 * nt + i32][16 * kk + 8 * hh]);
+                    acc[nt] = mma32(qf[cb / 16 + kk], bf, acc[nt]);
+                }
             }
         }
         if (GATE != kGla) {
-            for (int r = 0; r < 4; ++r) {
-                const int t = t0 + 16 * w + 4 * gq + r;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int t = t0 + 32 * w + 8 * (r >> 2) + 4 * hh + (r & 3);
                 float e = 0.0f;
                 if (t < T_) {
                     e = (GATE == kSig) ? exp2_fast(ab[t] * kLog2e)
                                        : exp2_fast((float)(t - cs + 1) * lg2);
                 }
+#pragma unroll
                 for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= e;
             }
         }
@@ -232,110 +246,118 @@ __global__ __launch_bounds__(256, (BV >= 256 ? 1 : 2)) void intra_kernel(const T
     }
 
     // ---------------- intra-chunk term, tiled along the chunk
-    if (GATE != kGla) {
-        if (kc == 0) load_q(-1);
-    }
+    if (GATE != kGla && kc == 0) load_q(-1);
     const float at2 = (GATE == kSig && tq_ok) ? ab[tq] * kLog2e : 0.0f;
-    const int tl = 16 * w + l16;            // query row inside the tile
+    const int tlo = t0 + 32 * w;                  // first query row of this wave
+    const int nkv = (t0 - cs) / 64 + BQ / 64;     // key tiles up to the end of the query tile
+    int q_ref = -2;                               // reference row the Q fragments are scaled for
 
-    for (int j = 0; j <= qi; ++j) {
-        const bool diag = (j == qi);
+    for (int j = 0; j < nkv; ++j) {
         const int s0 = cs + 64 * j;
         int ref_row = -1;
         if (GATE == kGla) {
-            ref_row = diag ? min(t0 + 31, T_ - 1) : t0 - 1;
-            if (j == 0 || diag) load_q(ref_row);
+            ref_row = (s0 + 63 < t0) ? t0 - 1 : min(s0 + 31, T_ - 1);
+            if (ref_row != q_ref) {
+                load_q(ref_row);
+                q_ref = ref_row;
+            }
         }
         __syncthreads();
         store_kv(s0, ref_row);
         __syncthreads();
-        if (!diag) fetch_kv(s0 + 64);
+        if (j + 1 < nkv) fetch_kv(s0 + 64);
 
-        // S^T (64 key steps x 16 query rows of this wave)
-        f32x4 st[4];
-        for (int mt = 0; mt < 4; ++mt) st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int kq = 0; kq < KQ; ++kq) {
-            for (int mt = 0; mt < 4; ++mt) {
-                const Frag af = load8(&sm.kv.ks[16 * mt + l16][32 * kq + 8 * gq]);
-                st[mt] = mma(af, qf[kq], st[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int slo = s0 + 32 * mt;
+            if (slo > tlo + 31 || slo >= T_) continue;   // wholly above the diagonal, or past the end
+            const bool diag = slo == tlo;
+            // S^T (32 key steps x 32 query rows of this wave)
+            f32x16 st;
+            for (int r = 0; r < 16; ++r) st[r] = 0.0f;
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) {
+                const Frag af = load8(&sm.kv.ks[32 * mt + i32][16 * kq + 8 * hh]);
+                st = mma32(af, qf[kq], st);
             }
-        }
-        // decay and causal mask: element (mt, r) is key step sl = 16mt + 4gq + r, query row tl
-        for (int mt = 0; mt < 4; ++mt) {
-            for (int r = 0; r < 4; ++r) {
-                const int sl = 16 * mt + 4 * gq + r;
-                float p = st[mt][r];
+            // decay and causal mask: element r is key step slo + sr, query row tlo + i32
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int sr = 8 * (r >> 2) + 4 * hh + (r & 3);
+                float p = st[r];
                 if (GATE == kSig) {
-                    p *= exp2_fast(at2 + sm.bcol[sl]);
+                    p *= exp2_fast(at2 + sm.bcol[32 * mt + sr]);
                 } else if (GATE == kScalar) {
-                    p *= exp2_fast((float)(64 * (qi - j) + tl - sl) * lg2);
+                    p *= exp2_fast((float)(tlo + i32 - slo - sr) * lg2);
                 }
-                st[mt][r] = (diag && sl > tl) ? 0.0f : p;
+                st[r] = (diag && sr > i32) ? 0.0f : p;
             }
-        }
-        // acc += P V_j, step index contracted in accumulator order
-        for (int kk = 0; kk < 2; ++kk) {
-            Frag pfr;
-            for (int e = 0; e < 4; ++e) {
-                frag_set(pfr, e, st[2 * kk][e]);
-                frag_set(pfr, 4 + e, st[2 * kk + 1][e]);
-            }
-            for (int nt = 0; nt < NT; ++nt) {
-                const T* row = sm.kv.vt[16 * nt + l16];
-                const Frag vf = load4x2(row + 32 * kk + 4 * gq, row + 32 * kk + 16 + 4 * gq);
-                acc[nt] = mma(pfr, vf, acc[nt]);
+            // acc += P V: 16-step halves, in accumulator order
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                Frag pfr;
+                for (int e = 0; e < 8; ++e) frag_set(pfr, e, st[8 * half + e]);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const Frag vf = frag_tr(sm.kv.vs, 32 * mt + 16 * half, 32 * nt, lane);
+                    acc[nt] = mma32(pfr, vf, acc[nt]);
+                }
             }
         }
     }
 
     // ---------------- output
-    for (int r = 0; r < 4; ++r) {
-        const int t = t0 + 16 * w + 4 * gq + r;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int t = t0 + 32 * w + 8 * (r >> 2) + 4 * hh + (r & 3);
         if (t >= T_) continue;
-        T* dst = h + (bh * (size_t)T_ + t) * dhv + v0 + l16;
-        for (int nt = 0; nt < NT; ++nt) dst[16 * nt] = from_float<T>(acc[nt][r] * scale);
+        T* dst = h + (bh * (size_t)T_ + t) * dhv + v0 + i32;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) dst[32 * nt] = from_float<T>(acc[nt][r] * scale);
     }
 }
 
-template <typename T, int GATE, int DQK, int BV>
+template <typename T, int GATE, int DQK, int BV, int NW>
 hipError_t launch_intra_t(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
                           const Workspace& ws, void* h, hipStream_t stream)
 {
-    const int nqt = (p.T + 63) / 64;
+    constexpr int BQ = 32 * NW;
+    const int nqt = (p.T + BQ - 1) / BQ;
     const int blocks = p.B * p.H * nqt * (p.dhv / BV);
     const float scale = 1.0f / sqrtf((float)DQK);
-    intra_kernel<T, GATE, DQK, BV><<<blocks, 256, 0, stream>>>(
+    intra_kernel<T, GATE, DQK, BV, NW><<<blocks, 64 * NW, 0, stream>>>(
         static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), ws.a, ws.li, fg,
         ws.states, static_cast<T*>(h), p.H, p.T, p.dhv, p.L, p.nc, scale);
     return hipGetLastError();
 }
 
-// Value-tile width: the widest of 128 / 64 dividing d_hv.  128 keeps two
-// workgroups per CU; 256 (one workgroup per CU, no recomputed S across value
-// tiles) measured slower.  TFLA_INTRA_BV=64|128|256 overrides (bf16 I/O only
-// for 256) for tuning sweeps.
+// Value-tile width: 128 when it divides d_hv (bf16 I/O), else 64 (fp32 I/O
+// always: its doubled fragments would not fit the register budget).
+// TFLA_INTRA_BV=64 forces 64 (tuning sweeps).
 inline int intra_bv(const Problem& p)
 {
-    int cap = 128;
-    if (const char* e = std::getenv("TFLA_INTRA_BV")) {
-        const int want = std::atoi(e);
-        if (want == 64 || want == 128 || want == 256) cap = (want == 256 && !p.bf16) ? 128 : want;
-    }
-    for (int bv = cap; bv >= 64; bv /= 2)
-        if (p.dhv % bv == 0) return bv;
-    return 64;
+    if (const char* e = std::getenv("TFLA_INTRA_BV"))
+        if (std::atoi(e) == 64) return 64;
+    return (p.bf16 && p.dhv % 128 == 0) ? 128 : 64;
+}
+
+template <typename T, int GATE, int DQK, int BV>
+hipError_t dispatch_nw(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
+                       const Workspace& ws, void* h, hipStream_t stream)
+{
+    // a workgroup's query rows never straddle a chunk: 128 rows when L >= 128
+    if (p.L >= 128) return launch_intra_t<T, GATE, DQK, BV, 4>(p, q, k, v, fg, ws, h, stream);
+    return launch_intra_t<T, GATE, DQK, BV, 2>(p, q, k, v, fg, ws, h, stream);
 }
 
 template <typename T, int GATE, int DQK>
 hipError_t dispatch_bv(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
                        const Workspace& ws, void* h, hipStream_t stream)
 {
-    const int bv = intra_bv(p);
     if constexpr (sizeof(T) == 2) {
-        if (bv == 256) return launch_intra_t<T, GATE, DQK, 256>(p, q, k, v, fg, ws, h, stream);
+        if (intra_bv(p) == 128) return dispatch_nw<T, GATE, DQK, 128>(p, q, k, v, fg, ws, h, stream);
     }
-    if (bv >= 128) return launch_intra_t<T, GATE, DQK, 128>(p, q, k, v, fg, ws, h, stream);
-    return launch_intra_t<T, GATE, DQK, 64>(p, q, k, v, fg, ws, h, stream);
+    return dispatch_nw<T, GATE, DQK, 64>(p, q, k, v, fg, ws, h, stream);
 }
 
 template <typename T, int GATE>
