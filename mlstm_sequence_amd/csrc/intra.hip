@@ -51,16 +51,22 @@ template <typename T, int DQK, int BV, int CW> struct IntraLds {
     float bcol[64];                 // mLSTMsig: (li_s - a_s) log2(e) per key step
 };
 
-// One stage's global loads, held in registers while the previous stage computes.
+// One stage's global loads, held in registers while the previous stage
+// computes.  A C^T block and a K/V tile are never in flight together, so they
+// share the registers.
 template <typename T, int DQK, int BV, int CW, int NTH> struct Prefetch {
     static constexpr int VEC = Elem<T>::vec;
     static constexpr int NC = BV * CW / 8 / NTH;          // C^T block: 8 floats per item
     static constexpr int NK = 64 * DQK / VEC / NTH;       // K tile: 16 bytes per item
     static constexpr int NV = 64 * BV / VEC / NTH;        // V tile: 16 bytes per item
     static_assert(NC >= 1 && NK >= 1 && NV >= 1, "tile too small for the workgroup");
-    f32x4 c[NC][2];
-    Vec16<T> k[NK];
-    Vec16<T> v[NV];
+    union {
+        f32x4 c[NC][2];
+        struct {
+            Vec16<T> k[NK];
+            Vec16<T> v[NV];
+        } kv;
+    };
     float li, a;
 };
 
@@ -75,7 +81,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 2 : 1) void intra_kernel(const T
 {
     constexpr int NTH = 64 * NW;
     constexpr int BQ = 32 * NW;           // query rows per workgroup
-    constexpr int CW = NW >= 4 ? 64 : 32; // C^T channels per stage
+    // C^T channels per stage: 128 (two stages at d_qk = 256) when the
+    // registers allow, fewer for fp32 and two-wave workgroups
+    constexpr int CW = NW >= 4 ? ((sizeof(T) == 2 && DQK >= 128) ? 128 : 64) : 32;
     constexpr int KQ = DQK / 16;          // 16-channel contraction steps
     constexpr int NT = BV / 32;           // 32-wide output column tiles
     constexpr int VEC = Elem<T>::vec;
@@ -165,13 +173,13 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 2 : 1) void intra_kernel(const T
         for (int u = 0; u < PF::NK; ++u) {
             const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
             const int s = s0 + r;
-            if (s < T_) pf.k[u].load(kb + (size_t)s * DQK + c); else pf.k[u].zero();
+            if (s < T_) pf.kv.k[u].load(kb + (size_t)s * DQK + c); else pf.kv.k[u].zero();
         }
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
             const int idx = tid + NTH * u, r = idx / (BV / VEC), c = (idx % (BV / VEC)) * VEC;
             const int s = s0 + r;
-            if (s < T_) pf.v[u].load(vb + (size_t)s * dhv + v0 + c); else pf.v[u].zero();
+            if (s < T_) pf.kv.v[u].load(vb + (size_t)s * dhv + v0 + c); else pf.kv.v[u].zero();
         }
         if (GATE == kSig && tid < 64) {
             const int s = s0 + tid;
@@ -188,16 +196,16 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 2 : 1) void intra_kernel(const T
                 if (s < T_) {
                     for (int e = 0; e < VEC; ++e) {
                         const float ex = ab[(size_t)ref_row * DQK + c + e] - ab[(size_t)s * DQK + c + e];
-                        pf.k[u].set(e, pf.k[u].get(e) * exp2_fast(ex * kLog2e));
+                        pf.kv.k[u].set(e, pf.kv.k[u].get(e) * exp2_fast(ex * kLog2e));
                     }
                 }
             }
-            pf.k[u].store(&sm.kv.ks[r][c]);
+            pf.kv.k[u].store(&sm.kv.ks[r][c]);
         }
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
             const int idx = tid + NTH * u, r = idx / (BV / VEC), c = (idx % (BV / VEC)) * VEC;
-            pf.v[u].store(&sm.kv.vs[r][c]);
+            pf.kv.v[u].store(&sm.kv.vs[r][c]);
         }
         if (GATE == kSig && tid < 64) sm.bcol[tid] = (pf.li - pf.a) * kLog2e;
     };

@@ -11,43 +11,44 @@
 // transposed ([d_hv][d_qk]) so the intra-chunk kernel reads them as
 // contiguous matrix-core B operands.
 //
-// One workgroup (4 wavefronts) owns a 64x64 tile of C^T (64 value rows x 64
-// key columns) for one head and walks the chunks serially, keeping the fp32
-// tile in accumulator registers; wave w owns the 32x32 quarter
-// (value rows 32(w/2).., key columns 32(w%2)..).  Per SB-step block it stages
-// V and w.K row-major in LDS (K scaled in fp32, rounded once to the operand
-// type) -- consecutive lanes load consecutive 16-byte pieces of a row -- and
-// reads both operands of acc += V^T (w.K) with LDS transpose reads.  The
-// block loop is software-pipelined: the next block's global loads are issued
-// right after the current block reaches LDS.  States leave as 128-byte rows.
+// One workgroup (4 wavefronts) owns a TV x TC tile of C^T (value rows x key
+// columns; 128x128 when the problem is large enough to give every CU one,
+// else 64x64) for one head and walks the chunks serially, keeping the fp32
+// tile in accumulator registers; wave w owns a quarter.  Per 64-step block
+// it stages V and w.K row-major in LDS (K scaled in fp32, rounded once to the
+// operand type) -- consecutive lanes load consecutive 16-byte pieces of a
+// row -- and reads both operands of acc += V^T (w.K) with LDS transpose
+// reads.  The block loop is software-pipelined two blocks deep (two register
+// sets).  States leave as 128-byte rows.
 #include "gfx950.hpp"
 #include "kernels.hpp"
 
 namespace tfla {
 namespace {
 
-constexpr int kTile = 64;   // C^T tile: 64 value rows x 64 key columns
-
-template <typename T, int SB> struct StateLds {
+// Tile of C^T per workgroup: TV value rows x TC key columns, 4 wavefronts in
+// a 2 x 2 grid, each owning a (TV/2) x (TC/2) quarter as 32x32 accumulators.
+template <typename T, int SB, int TV, int TC> struct StateLds {
     static constexpr int pad = 32 / sizeof(T);   // row stride = 8 banks mod 32 (transpose reads)
-    T vs[SB][kTile + pad];   // V block [step][value]
-    T ks[SB][kTile + pad];   // w.K block [step][key channel]
+    T vs[SB][TV + pad];   // V block [step][value]
+    T ks[SB][TC + pad];   // w.K block [step][key channel]
 };
 
-// One block's global loads, held in registers while the previous block is
-// multiplied.  Item u covers step row r(u) and VEC columns at c(u).
-template <typename T, int SB> struct StatePrefetch {
+// One block's global loads, held in registers while earlier blocks are
+// multiplied.  V item u: step row r, VEC value columns; K item u likewise.
+template <typename T, int SB, int TV, int TC> struct StatePrefetch {
     static constexpr int VEC = Elem<T>::vec;
-    static constexpr int NI = SB * (kTile / VEC) / 256;
-    static_assert(NI >= 1, "block too small for 256 threads");
-    Vec16<T> v[NI], k[NI];
-    float a[NI], li[NI];          // mLSTMsig step gates of the item's row
-    f32x4 ga[NI][VEC / 4];        // per-channel gate: a of the item's columns
-    f32x4 gg[NI][VEC / 4];        // per-channel gate: g of the item's columns
+    static constexpr int NV = SB * (TV / VEC) / 256;
+    static constexpr int NK = SB * (TC / VEC) / 256;
+    static_assert(NV >= 1 && NK >= 1, "block too small for 256 threads");
+    Vec16<T> v[NV], k[NK];
+    float a[NK], li[NK];          // mLSTMsig step gates of each K item's row
+    f32x4 ga[NK][VEC / 4];        // per-channel gate: a of the K item's columns
+    f32x4 gg[NK][VEC / 4];        // per-channel gate: g of the K item's columns
     float g;                      // mLSTMsig: g of the block's chunk
 };
 
-template <typename T, int GATE, int SB>
+template <typename T, int GATE, int SB, int TV, int TC>
 __global__ __launch_bounds__(256) void state_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                     const float* __restrict__ a,
                                                     const float* __restrict__ li,
@@ -56,22 +57,22 @@ __global__ __launch_bounds__(256) void state_kernel(const T* __restrict__ k, con
                                                     float* __restrict__ states, int H, int T_,
                                                     int dqk, int dhv, int L, int nc)
 {
-    __shared__ StateLds<T, SB> sm;
-    typedef StatePrefetch<T, SB> PF;
+    typedef StatePrefetch<T, SB, TV, TC> PF;
+    __shared__ StateLds<T, SB, TV, TC> sm;
     constexpr int VEC = Elem<T>::vec;
-    constexpr int CG = kTile / VEC;          // column groups per row
+    constexpr int MV = TV / 64, MC = TC / 64;   // 32x32 accumulators per wave along value / key
 
-    const int ntv = dhv / kTile, ntk = dqk / kTile;
+    const int ntv = dhv / TV, ntk = dqk / TC;
     const int blk = xcd_remap(blockIdx.x, gridDim.x);
     const int tiles = ntv * ntk;
     const size_t bh = blk / tiles;
     const int tile = blk % tiles;
-    const int v0 = (tile / ntk) * kTile;
-    const int c0 = (tile % ntk) * kTile;
+    const int v0 = (tile / ntk) * TV;
+    const int c0 = (tile % ntk) * TC;
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, hh = lane >> 5, i32 = lane & 31;
-    const int vw = 32 * (w >> 1), cw = 32 * (w & 1);   // this wave's quarter of the tile
+    const int vw = (TV / 2) * (w >> 1), cw = (TC / 2) * (w & 1);   // this wave's quarter
 
     const T* kb = k + bh * (size_t)T_ * dqk;
     const T* vb = v + bh * (size_t)T_ * dhv;
@@ -81,24 +82,27 @@ __global__ __launch_bounds__(256) void state_kernel(const T* __restrict__ k, con
     const int bpc = L / SB;                  // blocks per chunk
     const int nblocks = (nc - 1) * bpc;      // chunks 0..nc-2 are full and feed a state
 
-    PF pf;
-    auto fetch = [&](int b) {
+    auto fetch = [&](PF& pf, int b) {
         const int kc = b / bpc;
         const int s0 = b * SB;               // chunks are full: = kc*L + (b%bpc)*SB
         if (GATE == kSig) pf.g = g[bh * nc + kc];
 #pragma unroll
-        for (int u = 0; u < PF::NI; ++u) {
-            const int idx = tid + 256 * u, r = idx / CG, cg = (idx % CG) * VEC;
+        for (int u = 0; u < PF::NV; ++u) {
+            const int idx = tid + 256 * u, r = idx / (TV / VEC), c = (idx % (TV / VEC)) * VEC;
+            pf.v[u].load(vb + (size_t)(s0 + r) * dhv + v0 + c);
+        }
+#pragma unroll
+        for (int u = 0; u < PF::NK; ++u) {
+            const int idx = tid + 256 * u, r = idx / (TC / VEC), c = (idx % (TC / VEC)) * VEC;
             const int s = s0 + r;
-            pf.v[u].load(vb + (size_t)s * dhv + v0 + cg);
-            pf.k[u].load(kb + (size_t)s * dqk + c0 + cg);
+            pf.k[u].load(kb + (size_t)s * dqk + c0 + c);
             if (GATE == kSig) {
                 pf.a[u] = a[bh * T_ + s];
                 pf.li[u] = li[bh * T_ + s];
             }
             if (GATE == kGla) {
-                const float* ar = a + (bh * T_ + s) * (size_t)dqk + c0 + cg;
-                const float* gr = g + (bh * nc + kc) * (size_t)dqk + c0 + cg;
+                const float* ar = a + (bh * T_ + s) * (size_t)dqk + c0 + c;
+                const float* gr = g + (bh * nc + kc) * (size_t)dqk + c0 + c;
                 for (int e4 = 0; e4 < VEC / 4; ++e4) {
                     pf.ga[u][e4] = *reinterpret_cast<const f32x4*>(ar + 4 * e4);
                     pf.gg[u][e4] = *reinterpret_cast<const f32x4*>(gr + 4 * e4);
@@ -106,11 +110,16 @@ __global__ __launch_bounds__(256) void state_kernel(const T* __restrict__ k, con
             }
         }
     };
-    auto store = [&](int b) {
+    auto store = [&](PF& pf, int b) {
         const int cs = (b / bpc) * L;
 #pragma unroll
-        for (int u = 0; u < PF::NI; ++u) {
-            const int idx = tid + 256 * u, r = idx / CG, cg = (idx % CG) * VEC;
+        for (int u = 0; u < PF::NV; ++u) {
+            const int idx = tid + 256 * u, r = idx / (TV / VEC), c = (idx % (TV / VEC)) * VEC;
+            pf.v[u].store(&sm.vs[r][c]);
+        }
+#pragma unroll
+        for (int u = 0; u < PF::NK; ++u) {
+            const int idx = tid + 256 * u, r = idx / (TC / VEC), c = (idx % (TC / VEC)) * VEC;
             const int s = b * SB + r;
             float ws = 1.0f;
             if (GATE == kSig) ws = exp2_fast((pf.g - pf.a[u] + pf.li[u]) * kLog2e);
@@ -123,62 +132,90 @@ __global__ __launch_bounds__(256) void state_kernel(const T* __restrict__ k, con
                 else x *= ws;
                 kw.set(e, x);
             }
-            pf.v[u].store(&sm.vs[r][cg]);
-            kw.store(&sm.ks[r][cg]);
+            kw.store(&sm.ks[r][c]);
         }
     };
 
-    f32x16 acc;
-    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    f32x16 acc[MV][MC];
+#pragma unroll
+    for (int mv = 0; mv < MV; ++mv)
+        for (int mc = 0; mc < MC; ++mc)
+            for (int r = 0; r < 16; ++r) acc[mv][mc][r] = 0.0f;
 
-    if (nblocks > 0) fetch(0);
-    for (int b = 0; b < nblocks; ++b) {
+    // one block: stage it, launch the loads of block b + 2 into the same
+    // registers, multiply, and write the state at a chunk end
+    auto step = [&](PF& pf, int b) {
         const int kc = b / bpc;
         const bool first = (b % bpc) == 0, last = (b % bpc) == bpc - 1;
         __syncthreads();
-        store(b);
+        store(pf, b);
         __syncthreads();
-        if (b + 1 < nblocks) fetch(b + 1);
+        if (b + 2 < nblocks) fetch(pf, b + 2);
         if (first) {
             // decay of the carried state across chunk kc (column c of C^T = row c of C)
-            float e;
-            if (GATE == kSig) e = exp2_fast(g[bh * nc + kc] * kLog2e);
-            else if (GATE == kScalar) e = exp2_fast((float)L * lg2);
-            else e = exp2_fast(g[(bh * nc + kc) * dqk + c0 + cw + i32] * kLog2e);
-            acc *= e;
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc) {
+                float e;
+                if (GATE == kSig) e = exp2_fast(g[bh * nc + kc] * kLog2e);
+                else if (GATE == kScalar) e = exp2_fast((float)L * lg2);
+                else e = exp2_fast(g[(bh * nc + kc) * dqk + c0 + cw + 32 * mc + i32] * kLog2e);
+#pragma unroll
+                for (int mv = 0; mv < MV; ++mv) acc[mv][mc] *= e;
+            }
         }
         // acc (value rows vw.., key columns cw..) += V^T (w.K) over this block
 #pragma unroll
         for (int kb16 = 0; kb16 < SB; kb16 += 16) {
-            const auto af = frag_tr(sm.vs, kb16, vw, lane);
-            const auto bf = frag_tr(sm.ks, kb16, cw, lane);
-            acc = mma32(af, bf, acc);
+            typename Elem<T>::frag af[MV], bf[MC];
+#pragma unroll
+            for (int mv = 0; mv < MV; ++mv) af[mv] = frag_tr(sm.vs, kb16, vw + 32 * mv, lane);
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc) bf[mc] = frag_tr(sm.ks, kb16, cw + 32 * mc, lane);
+#pragma unroll
+            for (int mv = 0; mv < MV; ++mv)
+#pragma unroll
+                for (int mc = 0; mc < MC; ++mc) acc[mv][mc] = mma32(af[mv], bf[mc], acc[mv][mc]);
         }
         if (last) {
-            float* dst = states + ((bh * (nc - 1) + kc) * (size_t)dhv + v0 + vw) * dqk + c0 + cw + i32;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) dst[(size_t)(8 * (r >> 2) + 4 * hh + (r & 3)) * dqk] = acc[r];
+            for (int mv = 0; mv < MV; ++mv) {
+                float* dst = states + ((bh * (nc - 1) + kc) * (size_t)dhv + v0 + vw + 32 * mv) * dqk + c0 + cw + i32;
+#pragma unroll
+                for (int mc = 0; mc < MC; ++mc)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        dst[(size_t)(8 * (r >> 2) + 4 * hh + (r & 3)) * dqk + 32 * mc] = acc[mv][mc][r];
+            }
         }
+    };
+
+    // two register sets in flight: blocks b and b + 1 load while b - 1 is multiplied
+    PF p0, p1;
+    if (nblocks > 0) fetch(p0, 0);
+    if (nblocks > 1) fetch(p1, 1);
+    for (int b = 0; b < nblocks; b += 2) {
+        step(p0, b);
+        if (b + 1 < nblocks) step(p1, b + 1);
     }
 }
 
-template <typename T, int SB>
-hipError_t launch_state_sb(const Problem& p, const T* k, const T* v, const float* fg, const Workspace& ws,
-                           hipStream_t stream)
+template <typename T, int SB, int TV, int TC>
+hipError_t launch_state_cfg(const Problem& p, const T* k, const T* v, const float* fg, const Workspace& ws,
+                            hipStream_t stream)
 {
-    const int blocks = p.B * p.H * (p.dhv / kTile) * (p.dqk / kTile);
+    const int blocks = p.B * p.H * (p.dhv / TV) * (p.dqk / TC);
     switch (p.gate) {
     case kSig:
-        state_kernel<T, kSig, SB><<<blocks, 256, 0, stream>>>(k, v, ws.a, ws.li, ws.g, fg, ws.states, p.H,
-                                                               p.T, p.dqk, p.dhv, p.L, p.nc);
+        state_kernel<T, kSig, SB, TV, TC><<<blocks, 256, 0, stream>>>(k, v, ws.a, ws.li, ws.g, fg, ws.states,
+                                                                       p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
         break;
     case kScalar:
-        state_kernel<T, kScalar, SB><<<blocks, 256, 0, stream>>>(k, v, ws.a, ws.li, ws.g, fg, ws.states, p.H,
-                                                                  p.T, p.dqk, p.dhv, p.L, p.nc);
+        state_kernel<T, kScalar, SB, TV, TC><<<blocks, 256, 0, stream>>>(k, v, ws.a, ws.li, ws.g, fg, ws.states,
+                                                                          p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
         break;
     default:
-        state_kernel<T, kGla, SB><<<blocks, 256, 0, stream>>>(k, v, ws.a, ws.li, ws.g, fg, ws.states, p.H,
-                                                               p.T, p.dqk, p.dhv, p.L, p.nc);
+        state_kernel<T, kGla, SB, TV, TC><<<blocks, 256, 0, stream>>>(k, v, ws.a, ws.li, ws.g, fg, ws.states,
+                                                                       p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
         break;
     }
     return hipGetLastError();
@@ -189,9 +226,13 @@ hipError_t launch_state_t(const Problem& p, const T* k, const T* v, const float*
                           hipStream_t stream)
 {
     if (p.nc < 2) return hipSuccess;
-    // 128-step blocks (two latencies fewer per chunk) whenever the chunk holds them
-    if (p.L >= 128) return launch_state_sb<T, 128>(p, k, v, fg, ws, stream);
-    return launch_state_sb<T, 64>(p, k, v, fg, ws, stream);
+    // 128x128 tiles halve the LDS bytes per flop and the L2 re-reads of K and
+    // V; use them when they still give every CU a workgroup (bf16 I/O only:
+    // fp32 blocks would not fit LDS), else 64x64 tiles for parallelism.
+    const long big = (long)p.B * p.H * (p.dhv / 128) * (p.dqk / 128);
+    if (sizeof(T) == 2 && p.dhv % 128 == 0 && p.dqk % 128 == 0 && big >= 256)
+        return launch_state_cfg<T, 64, 128, 128>(p, k, v, fg, ws, stream);
+    return launch_state_cfg<T, 64, 64, 64>(p, k, v, fg, ws, stream);
 }
 
 }  // namespace
