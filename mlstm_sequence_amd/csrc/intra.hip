@@ -10,7 +10,8 @@
 // and loops over the 64-step key/value tiles up to its own rows, so the
 // chunk size L is bounded by nothing on chip.
 //
-// Workgroup = NW wavefronts, wave w owning query rows 32w..32w+31 (BQ = 32 NW);
+// Workgroup = NW wavefronts (2, 4 or 8), wave w owning query rows
+// 32w..32w+31 (BQ = 32 NW, at most the chunk size);
 // all products are 32x32x16 matrix-core tiles:
 //   inter: acc = Q C_{k-1}[:, v-tile]; C^T is staged in LDS per CW-channel
 //          block (fp32 -> operand type, RNE); Q fragments stay in registers
@@ -105,7 +106,11 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 2 : 1) void intra_kernel(const T
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, hh = lane >> 5, i32 = lane & 31;
     const int tq = t0 + 32 * w + i32;      // query step of this lane's fragment row
-    const bool tq_ok = tq < T_;
+    // Rows at or past T are read clamped to row T-1 (branch-free loads): a
+    // query row past the end only feeds its own output row, which is never
+    // stored, and a key/value row past the end only meets query rows before
+    // it through the causal select (P = 0, times finite data).
+    const int tqc = min(tq, T_ - 1);
 
     const T* qb = q + bh * (size_t)T_ * DQK;
     const T* kb = k + bh * (size_t)T_ * DQK;
@@ -124,16 +129,12 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 2 : 1) void intra_kernel(const T
 #pragma unroll
         for (int kq = 0; kq < KQ; ++kq) {
             const int c = 16 * kq + 8 * hh;
-            if (!tq_ok) {
-                for (int e = 0; e < 8; ++e) frag_set(qf[kq], e, 0.0f);
-                continue;
-            }
             if (GATE != kGla) {
-                qf[kq] = load8(qb + (size_t)tq * DQK + c);
+                qf[kq] = load8(qb + (size_t)tqc * DQK + c);
             } else {
-                const Frag raw = load8(qb + (size_t)tq * DQK + c);
+                const Frag raw = load8(qb + (size_t)tqc * DQK + c);
                 for (int e = 0; e < 8; ++e) {
-                    float ex = ab[(size_t)tq * DQK + c + e];
+                    float ex = ab[(size_t)tqc * DQK + c + e];
                     if (ref_row >= 0) ex -= ab[(size_t)ref_row * DQK + c + e];
                     frag_set(qf[kq], e, frag_get(raw, e) * exp2_fast(ex * kLog2e));
                 }
@@ -172,19 +173,19 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 2 : 1) void intra_kernel(const T
 #pragma unroll
         for (int u = 0; u < PF::NK; ++u) {
             const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
-            const int s = s0 + r;
-            if (s < T_) pf.kv.k[u].load(kb + (size_t)s * DQK + c); else pf.kv.k[u].zero();
+            const int s = min(s0 + r, T_ - 1);
+            pf.kv.k[u].load(kb + (size_t)s * DQK + c);
         }
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
             const int idx = tid + NTH * u, r = idx / (BV / VEC), c = (idx % (BV / VEC)) * VEC;
-            const int s = s0 + r;
-            if (s < T_) pf.kv.v[u].load(vb + (size_t)s * dhv + v0 + c); else pf.kv.v[u].zero();
+            const int s = min(s0 + r, T_ - 1);
+            pf.kv.v[u].load(vb + (size_t)s * dhv + v0 + c);
         }
         if (GATE == kSig && tid < 64) {
-            const int s = s0 + tid;
-            pf.li = (s < T_) ? lb[s] : 0.0f;
-            pf.a = (s < T_) ? ab[s] : 0.0f;
+            const int s = min(s0 + tid, T_ - 1);
+            pf.li = lb[s];
+            pf.a = ab[s];
         }
     };
     auto store_kv = [&](int s0, int ref_row) {
@@ -192,12 +193,10 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 2 : 1) void intra_kernel(const T
         for (int u = 0; u < PF::NK; ++u) {
             const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
             if (GATE == kGla) {
-                const int s = s0 + r;
-                if (s < T_) {
-                    for (int e = 0; e < VEC; ++e) {
-                        const float ex = ab[(size_t)ref_row * DQK + c + e] - ab[(size_t)s * DQK + c + e];
-                        pf.kv.k[u].set(e, pf.kv.k[u].get(e) * exp2_fast(ex * kLog2e));
-                    }
+                const int s = min(s0 + r, T_ - 1);
+                for (int e = 0; e < VEC; ++e) {
+                    const float ex = ab[(size_t)ref_row * DQK + c + e] - ab[(size_t)s * DQK + c + e];
+                    pf.kv.k[u].set(e, pf.kv.k[u].get(e) * exp2_fast(ex * kLog2e));
                 }
             }
             pf.kv.k[u].store(&sm.kv.ks[r][c]);
@@ -239,12 +238,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 2 : 1) void intra_kernel(const T
         if (GATE != kGla) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int t = t0 + 32 * w + 8 * (r >> 2) + 4 * hh + (r & 3);
-                float e = 0.0f;
-                if (t < T_) {
-                    e = (GATE == kSig) ? exp2_fast(ab[t] * kLog2e)
-                                       : exp2_fast((float)(t - cs + 1) * lg2);
-                }
+                const int t = min(t0 + 32 * w + 8 * (r >> 2) + 4 * hh + (r & 3), T_ - 1);
+                const float e = (GATE == kSig) ? exp2_fast(ab[t] * kLog2e)
+                                               : exp2_fast((float)(t - cs + 1) * lg2);
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= e;
             }
@@ -255,7 +251,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 2 : 1) void intra_kernel(const T
 
     // ---------------- intra-chunk term, tiled along the chunk
     if (GATE != kGla && kc == 0) load_q(-1);
-    const float at2 = (GATE == kSig && tq_ok) ? ab[tq] * kLog2e : 0.0f;
+    const float at2 = (GATE == kSig) ? ab[tqc] * kLog2e : 0.0f;
     const int tlo = t0 + 32 * w;                  // first query row of this wave
     const int nkv = (t0 - cs) / 64 + BQ / 64;     // key tiles up to the end of the query tile
     int q_ref = -2;                               // reference row the Q fragments are scaled for
@@ -349,12 +345,31 @@ inline int intra_bv(const Problem& p)
     return (p.bf16 && p.dhv % 128 == 0) ? 128 : 64;
 }
 
+// Query rows per workgroup (32 per wave): as many as the chunk allows, up to
+// 256 (bf16) -- every staged C^T block and K/V tile then serves more rows.
+// TFLA_INTRA_ROWS=64|128|256 caps it (tuning sweeps).
+inline int intra_rows(const Problem& p)
+{
+    int cap = p.bf16 ? 256 : 128;
+    if (const char* e = std::getenv("TFLA_INTRA_ROWS")) {
+        const int want = std::atoi(e);
+        if (want == 64 || want == 128 || want == 256) cap = want < cap ? want : cap;
+    }
+    int rows = 64;
+    while (rows * 2 <= cap && p.L % (rows * 2) == 0) rows *= 2;
+    return rows;
+}
+
 template <typename T, int GATE, int DQK, int BV>
 hipError_t dispatch_nw(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
                        const Workspace& ws, void* h, hipStream_t stream)
 {
-    // a workgroup's query rows never straddle a chunk: 128 rows when L >= 128
-    if (p.L >= 128) return launch_intra_t<T, GATE, DQK, BV, 4>(p, q, k, v, fg, ws, h, stream);
+    // a workgroup's query rows never straddle a chunk
+    const int rows = intra_rows(p);
+    if constexpr (sizeof(T) == 2) {
+        if (rows == 256) return launch_intra_t<T, GATE, DQK, BV, 8>(p, q, k, v, fg, ws, h, stream);
+    }
+    if (rows >= 128) return launch_intra_t<T, GATE, DQK, BV, 4>(p, q, k, v, fg, ws, h, stream);
     return launch_intra_t<T, GATE, DQK, BV, 2>(p, q, k, v, fg, ws, h, stream);
 }
 

@@ -14,12 +14,13 @@
 // One workgroup (4 wavefronts) owns a TV x TC tile of C^T (value rows x key
 // columns; 128x128 when the problem is large enough to give every CU one,
 // else 64x64) for one head and walks the chunks serially, keeping the fp32
-// tile in accumulator registers; wave w owns a quarter.  Per 64-step block
+// tile in accumulator registers; wave w owns a quarter.  Per block
 // it stages V and w.K row-major in LDS (K scaled in fp32, rounded once to the
 // operand type) -- consecutive lanes load consecutive 16-byte pieces of a
 // row -- and reads both operands of acc += V^T (w.K) with LDS transpose
-// reads.  The block loop is software-pipelined two blocks deep (two register
-// sets).  States leave as 128-byte rows.
+// reads.  The block loop is software-pipelined: the next block's loads are
+// issued into registers right after the current block reached LDS.  Blocks
+// are 128 steps when the chunk holds them.  States leave as 128-byte rows.
 #include "gfx950.hpp"
 #include "kernels.hpp"
 
@@ -142,21 +143,24 @@ __global__ __launch_bounds__(256) void state_kernel(const T* __restrict__ k, con
         for (int mc = 0; mc < MC; ++mc)
             for (int r = 0; r < 16; ++r) acc[mv][mc][r] = 0.0f;
 
-    // one block: stage it, launch the loads of block b + 2 into the same
+    // one block: stage it, launch the next block's loads into the freed
     // registers, multiply, and write the state at a chunk end
-    auto step = [&](PF& pf, int b) {
+    PF pf;
+    if (nblocks > 0) fetch(pf, 0);
+    for (int b = 0; b < nblocks; ++b) {
         const int kc = b / bpc;
         const bool first = (b % bpc) == 0, last = (b % bpc) == bpc - 1;
         __syncthreads();
         store(pf, b);
+        const float gk = pf.g;                // g of this block's chunk, before the next fetch overwrites it
         __syncthreads();
-        if (b + 2 < nblocks) fetch(pf, b + 2);
+        if (b + 1 < nblocks) fetch(pf, b + 1);
         if (first) {
             // decay of the carried state across chunk kc (column c of C^T = row c of C)
 #pragma unroll
             for (int mc = 0; mc < MC; ++mc) {
                 float e;
-                if (GATE == kSig) e = exp2_fast(g[bh * nc + kc] * kLog2e);
+                if (GATE == kSig) e = exp2_fast(gk * kLog2e);
                 else if (GATE == kScalar) e = exp2_fast((float)L * lg2);
                 else e = exp2_fast(g[(bh * nc + kc) * dqk + c0 + cw + 32 * mc + i32] * kLog2e);
 #pragma unroll
@@ -187,15 +191,6 @@ __global__ __launch_bounds__(256) void state_kernel(const T* __restrict__ k, con
                         dst[(size_t)(8 * (r >> 2) + 4 * hh + (r & 3)) * dqk + 32 * mc] = acc[mv][mc][r];
             }
         }
-    };
-
-    // two register sets in flight: blocks b and b + 1 load while b - 1 is multiplied
-    PF p0, p1;
-    if (nblocks > 0) fetch(p0, 0);
-    if (nblocks > 1) fetch(p1, 1);
-    for (int b = 0; b < nblocks; b += 2) {
-        step(p0, b);
-        if (b + 1 < nblocks) step(p1, b + 1);
     }
 }
 
@@ -230,8 +225,11 @@ hipError_t launch_state_t(const Problem& p, const T* k, const T* v, const float*
     // V; use them when they still give every CU a workgroup (bf16 I/O only:
     // fp32 blocks would not fit LDS), else 64x64 tiles for parallelism.
     const long big = (long)p.B * p.H * (p.dhv / 128) * (p.dqk / 128);
-    if (sizeof(T) == 2 && p.dhv % 128 == 0 && p.dqk % 128 == 0 && big >= 256)
+    if (sizeof(T) == 2 && p.dhv % 128 == 0 && p.dqk % 128 == 0 && big >= 256) {
+        if (p.L >= 128) return launch_state_cfg<T, 128, 128, 128>(p, k, v, fg, ws, stream);
         return launch_state_cfg<T, 64, 128, 128>(p, k, v, fg, ws, stream);
+    }
+    if (p.L >= 128) return launch_state_cfg<T, 128, 64, 64>(p, k, v, fg, ws, stream);
     return launch_state_cfg<T, 64, 64, 64>(p, k, v, fg, ws, stream);
 }
 
