@@ -11,24 +11,28 @@
 // transposed ([d_hv][d_qk]) so the intra-chunk kernel reads them as
 // contiguous matrix-core B operands.
 //
-// One workgroup (4 wavefronts) owns a TV x TC tile of C^T (value rows x key
-// columns; 128x128 when the problem is large enough to give every CU one,
-// else 64x64) for one head and walks the chunks serially, keeping the fp32
-// tile in accumulator registers; wave w owns a quarter.  Per block
+// One workgroup owns a TV x TC tile of C^T (value rows x key columns; 128x128
+// with 8 wavefronts when the problem is large enough to give every CU one,
+// else 64x64 with 4) for one head and walks the chunks serially, keeping the
+// fp32 tile in accumulator registers spread over its waves.  Per block
 // it stages V and w.K row-major in LDS (K scaled in fp32, rounded once to the
 // operand type) -- consecutive lanes load consecutive 16-byte pieces of a
 // row -- and reads both operands of acc += V^T (w.K) with LDS transpose
 // reads.  The block loop is software-pipelined: the next block's loads are
 // issued into registers right after the current block reached LDS.  Blocks
-// are 128 steps when the chunk holds them.  States leave as 128-byte rows.
+// are as long as the chunk allows (up to 256 steps on 128x128 tiles).
+// States leave as 128-byte rows.
+#include <cstdlib>
+
 #include "gfx950.hpp"
 #include "kernels.hpp"
 
 namespace tfla {
 namespace {
 
-// Tile of C^T per workgroup: TV value rows x TC key columns, 4 wavefronts in
-// a 2 x 2 grid, each owning a (TV/2) x (TC/2) quarter as 32x32 accumulators.
+// Tile of C^T per workgroup: TV value rows x TC key columns; NWS wavefronts
+// in a 2 x (NWS/2) grid, each owning a (TV/2) x (2 TC/NWS) piece as 32x32
+// accumulators.
 template <typename T, int SB, int TV, int TC> struct StateLds {
     static constexpr int pad = 32 / sizeof(T);   // row stride = 8 banks mod 32 (transpose reads)
     T vs[SB][TV + pad];   // V block [step][value]
@@ -37,11 +41,11 @@ template <typename T, int SB, int TV, int TC> struct StateLds {
 
 // One block's global loads, held in registers while earlier blocks are
 // multiplied.  V item u: step row r, VEC value columns; K item u likewise.
-template <typename T, int SB, int TV, int TC> struct StatePrefetch {
+template <typename T, int SB, int TV, int TC, int NTH> struct StatePrefetch {
     static constexpr int VEC = Elem<T>::vec;
-    static constexpr int NV = SB * (TV / VEC) / 256;
-    static constexpr int NK = SB * (TC / VEC) / 256;
-    static_assert(NV >= 1 && NK >= 1, "block too small for 256 threads");
+    static constexpr int NV = SB * (TV / VEC) / NTH;
+    static constexpr int NK = SB * (TC / VEC) / NTH;
+    static_assert(NV >= 1 && NK >= 1, "block too small for the workgroup");
     Vec16<T> v[NV], k[NK];
     float a[NK], li[NK];          // mLSTMsig step gates of each K item's row
     f32x4 ga[NK][VEC / 4];        // per-channel gate: a of the K item's columns
@@ -49,8 +53,8 @@ template <typename T, int SB, int TV, int TC> struct StatePrefetch {
     float g;                      // mLSTMsig: g of the block's chunk
 };
 
-template <typename T, int GATE, int SB, int TV, int TC>
-__global__ __launch_bounds__(256) void state_kernel(const T* __restrict__ k, const T* __restrict__ v,
+template <typename T, int GATE, int SB, int TV, int TC, int NWS>
+__global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                     const float* __restrict__ a,
                                                     const float* __restrict__ li,
                                                     const float* __restrict__ g,
@@ -58,10 +62,13 @@ __global__ __launch_bounds__(256) void state_kernel(const T* __restrict__ k, con
                                                     float* __restrict__ states, int H, int T_,
                                                     int dqk, int dhv, int L, int nc)
 {
-    typedef StatePrefetch<T, SB, TV, TC> PF;
+    constexpr int NTH = 64 * NWS;
+    typedef StatePrefetch<T, SB, TV, TC, NTH> PF;
     __shared__ StateLds<T, SB, TV, TC> sm;
     constexpr int VEC = Elem<T>::vec;
-    constexpr int MV = TV / 64, MC = TC / 64;   // 32x32 accumulators per wave along value / key
+    constexpr int WC = NWS / 2;                        // waves along the key columns
+    constexpr int MV = TV / 64, MC = TC / WC / 32;     // 32x32 accumulators per wave along value / key
+    static_assert(MC >= 1, "tile too narrow for the waves");
 
     const int ntv = dhv / TV, ntk = dqk / TC;
     const int blk = xcd_remap(blockIdx.x, gridDim.x);
@@ -73,7 +80,7 @@ __global__ __launch_bounds__(256) void state_kernel(const T* __restrict__ k, con
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, hh = lane >> 5, i32 = lane & 31;
-    const int vw = (TV / 2) * (w >> 1), cw = (TC / 2) * (w & 1);   // this wave's quarter
+    const int vw = (TV / 2) * (w / WC), cw = (TC / WC) * (w % WC);   // this wave's piece
 
     const T* kb = k + bh * (size_t)T_ * dqk;
     const T* vb = v + bh * (size_t)T_ * dhv;
@@ -89,12 +96,12 @@ __global__ __launch_bounds__(256) void state_kernel(const T* __restrict__ k, con
         if (GATE == kSig) pf.g = g[bh * nc + kc];
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
-            const int idx = tid + 256 * u, r = idx / (TV / VEC), c = (idx % (TV / VEC)) * VEC;
+            const int idx = tid + NTH * u, r = idx / (TV / VEC), c = (idx % (TV / VEC)) * VEC;
             pf.v[u].load(vb + (size_t)(s0 + r) * dhv + v0 + c);
         }
 #pragma unroll
         for (int u = 0; u < PF::NK; ++u) {
-            const int idx = tid + 256 * u, r = idx / (TC / VEC), c = (idx % (TC / VEC)) * VEC;
+            const int idx = tid + NTH * u, r = idx / (TC / VEC), c = (idx % (TC / VEC)) * VEC;
             const int s = s0 + r;
             pf.k[u].load(kb + (size_t)s * dqk + c0 + c);
             if (GATE == kSig) {
@@ -115,12 +122,12 @@ __global__ __launch_bounds__(256) void state_kernel(const T* __restrict__ k, con
         const int cs = (b / bpc) * L;
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
-            const int idx = tid + 256 * u, r = idx / (TV / VEC), c = (idx % (TV / VEC)) * VEC;
+            const int idx = tid + NTH * u, r = idx / (TV / VEC), c = (idx % (TV / VEC)) * VEC;
             pf.v[u].store(&sm.vs[r][c]);
         }
 #pragma unroll
         for (int u = 0; u < PF::NK; ++u) {
-            const int idx = tid + 256 * u, r = idx / (TC / VEC), c = (idx % (TC / VEC)) * VEC;
+            const int idx = tid + NTH * u, r = idx / (TC / VEC), c = (idx % (TC / VEC)) * VEC;
             const int s = b * SB + r;
             float ws = 1.0f;
             if (GATE == kSig) ws = exp2_fast((pf.g - pf.a[u] + pf.li[u]) * kLog2e);
@@ -194,23 +201,24 @@ __global__ __launch_bounds__(256) void state_kernel(const T* __restrict__ k, con
     }
 }
 
-template <typename T, int SB, int TV, int TC>
+template <typename T, int SB, int TV, int TC, int NWS>
 hipError_t launch_state_cfg(const Problem& p, const T* k, const T* v, const float* fg, const Workspace& ws,
                             hipStream_t stream)
 {
     const int blocks = p.B * p.H * (p.dhv / TV) * (p.dqk / TC);
+    const int threads = 64 * NWS;
     switch (p.gate) {
     case kSig:
-        state_kernel<T, kSig, SB, TV, TC><<<blocks, 256, 0, stream>>>(k, v, ws.a, ws.li, ws.g, fg, ws.states,
-                                                                       p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
+        state_kernel<T, kSig, SB, TV, TC, NWS><<<blocks, threads, 0, stream>>>(
+            k, v, ws.a, ws.li, ws.g, fg, ws.states, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
         break;
     case kScalar:
-        state_kernel<T, kScalar, SB, TV, TC><<<blocks, 256, 0, stream>>>(k, v, ws.a, ws.li, ws.g, fg, ws.states,
-                                                                          p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
+        state_kernel<T, kScalar, SB, TV, TC, NWS><<<blocks, threads, 0, stream>>>(
+            k, v, ws.a, ws.li, ws.g, fg, ws.states, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
         break;
     default:
-        state_kernel<T, kGla, SB, TV, TC><<<blocks, 256, 0, stream>>>(k, v, ws.a, ws.li, ws.g, fg, ws.states,
-                                                                       p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
+        state_kernel<T, kGla, SB, TV, TC, NWS><<<blocks, threads, 0, stream>>>(
+            k, v, ws.a, ws.li, ws.g, fg, ws.states, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
         break;
     }
     return hipGetLastError();
@@ -223,14 +231,21 @@ hipError_t launch_state_t(const Problem& p, const T* k, const T* v, const float*
     if (p.nc < 2) return hipSuccess;
     // 128x128 tiles halve the LDS bytes per flop and the L2 re-reads of K and
     // V; use them when they still give every CU a workgroup (bf16 I/O only:
-    // fp32 blocks would not fit LDS), else 64x64 tiles for parallelism.
+    // fp32 blocks would not fit LDS), else 64x64 tiles for parallelism.  The
+    // big tiles run 8 waves over blocks of up to 256 steps (128 KB of loads in
+    // flight per workgroup).
     const long big = (long)p.B * p.H * (p.dhv / 128) * (p.dqk / 128);
-    if (sizeof(T) == 2 && p.dhv % 128 == 0 && p.dqk % 128 == 0 && big >= 256) {
-        if (p.L >= 128) return launch_state_cfg<T, 128, 128, 128>(p, k, v, fg, ws, stream);
-        return launch_state_cfg<T, 64, 128, 128>(p, k, v, fg, ws, stream);
+    int sb_cap = 256;   // TFLA_STATE_SB=64|128 caps the block (tuning sweeps)
+    if (const char* e = std::getenv("TFLA_STATE_SB")) sb_cap = std::atoi(e);
+    if constexpr (sizeof(T) == 2) {
+        if (p.dhv % 128 == 0 && p.dqk % 128 == 0 && big >= 256) {
+            if (p.L >= 256 && sb_cap >= 256) return launch_state_cfg<T, 256, 128, 128, 8>(p, k, v, fg, ws, stream);
+            if (p.L >= 128 && sb_cap >= 128) return launch_state_cfg<T, 128, 128, 128, 8>(p, k, v, fg, ws, stream);
+            return launch_state_cfg<T, 64, 128, 128, 8>(p, k, v, fg, ws, stream);
+        }
     }
-    if (p.L >= 128) return launch_state_cfg<T, 128, 64, 64>(p, k, v, fg, ws, stream);
-    return launch_state_cfg<T, 64, 64, 64>(p, k, v, fg, ws, stream);
+    if (p.L >= 128) return launch_state_cfg<T, 128, 64, 64, 4>(p, k, v, fg, ws, stream);
+    return launch_state_cfg<T, 64, 64, 64, 4>(p, k, v, fg, ws, stream);
 }
 
 }  // namespace
