@@ -53,6 +53,8 @@ def _load():
         dp = ctypes.POINTER(ctypes.c_double)
         lib.oracle_fwd.argtypes = [dp] * 7 + [ctypes.c_int] * 7
         lib.oracle_fwd.restype = ctypes.c_int
+        lib.oracle_fwd_state.argtypes = [dp] * 9 + [ctypes.c_int] * 7
+        lib.oracle_fwd_state.restype = ctypes.c_int
         lib.oracle_log_gates.argtypes = [dp] * 5 + [ctypes.c_int] * 6
         lib.oracle_log_gates.restype = ctypes.c_int
         lib.oracle_threads.argtypes = []
@@ -105,6 +107,21 @@ def recurrent_fwd(q, k, v, igate_pre, fgate_pre, kind, L=None):
     if rc != 0:
         raise ValueError("oracle_fwd rejected its arguments")
     return (h, states) if L is not None else h
+
+
+def recurrent_fwd_state(q, k, v, igate_pre, fgate_pre, kind, c0=None):
+    """Recurrent oracle from an initial state C_0 = c0 ([B,H,dqk,dhv]; None
+    means zero).  Returns (h [B,H,T,dhv], C_T [B,H,dqk,dhv])."""
+    q, k, v, ig, fg, c0 = map(_f64, (q, k, v, igate_pre, fgate_pre, c0))
+    B, H, T, dqk = q.shape
+    dhv = v.shape[-1]
+    h = np.empty((B, H, T, dhv), dtype=np.float64)
+    cT = np.empty((B, H, dqk, dhv), dtype=np.float64)
+    rc = _load().oracle_fwd_state(_ptr(q), _ptr(k), _ptr(v), _ptr(ig), _ptr(fg), _ptr(c0), _ptr(h), None,
+                                  _ptr(cT), B, H, T, dqk, dhv, 0, kind)
+    if rc != 0:
+        raise ValueError("oracle_fwd_state rejected its arguments")
+    return h, cT
 
 
 def log_gates(igate_pre, fgate_pre, kind, B, H, T, dqk, L):

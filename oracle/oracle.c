@@ -6,7 +6,7 @@
  *
  * What it computes (per batch b and head h, everything in double):
  *
- *   C_0 = 0                                        (d_qk x d_hv matrix memory)
+ *   C_0 = 0, or a given initial state              (d_qk x d_hv matrix memory)
  *   C_t = diag(f_t) C_{t-1} + i_t k_t v_t^T         t = 1..T
  *   h_t = C_t^T q_t / sqrt(d_qk)
  *
@@ -36,6 +36,8 @@
  *   fgate_pre [B,H,T] (kind 0), [H] (kind 1), [B,H,T,d_qk] (kind 2)
  *   states    optional; when non-NULL receives C after every full block of
  *             L steps: [B,H,T/L (floor),d_qk,d_hv]
+ *   c0        optional initial state C_0 [B,H,d_qk,d_hv] (NULL: zero)
+ *   c_final   optional; receives C_T [B,H,d_qk,d_hv]
  */
 #include <math.h>
 #include <stdlib.h>
@@ -86,11 +88,12 @@ int oracle_threads(void)
 #endif
 }
 
-/* Recurrent forward.  Returns 0, or -1 on an invalid argument. */
-int oracle_fwd(const double* q, const double* k, const double* v,
-               const double* igate_pre, const double* fgate_pre,
-               double* h, double* states,
-               int B, int H, int T, int dqk, int dhv, int L, int kind)
+/* Recurrent forward from an initial state.  Returns 0, or -1 on an invalid
+ * argument. */
+int oracle_fwd_state(const double* q, const double* k, const double* v,
+                     const double* igate_pre, const double* fgate_pre,
+                     const double* c0, double* h, double* states, double* c_final,
+                     int B, int H, int T, int dqk, int dhv, int L, int kind)
 {
     if (!q || !k || !v || !fgate_pre || !h) return -1;
     if (B < 0 || H < 0 || T < 0 || dqk < 1 || dhv < 1) return -1;
@@ -114,6 +117,7 @@ int oracle_fwd(const double* q, const double* k, const double* v,
             bad = 1;
             continue;
         }
+        if (c0) memcpy(C, c0 + (size_t)bh * dqk * dhv, (size_t)dqk * dhv * sizeof(double));
         for (int t = 0; t < T; ++t) {
             const double* qt = q + ((size_t)bh * T + t) * dqk;
             const double* kt = k + ((size_t)bh * T + t) * dqk;
@@ -141,10 +145,21 @@ int oracle_fwd(const double* q, const double* k, const double* v,
                        (size_t)dqk * dhv * sizeof(double));
             }
         }
+        if (c_final) memcpy(c_final + (size_t)bh * dqk * dhv, C, (size_t)dqk * dhv * sizeof(double));
         free(C);
         free(f);
     }
     return bad ? -1 : 0;
+}
+
+/* Recurrent forward from C_0 = 0. */
+int oracle_fwd(const double* q, const double* k, const double* v,
+               const double* igate_pre, const double* fgate_pre,
+               double* h, double* states,
+               int B, int H, int T, int dqk, int dhv, int L, int kind)
+{
+    return oracle_fwd_state(q, k, v, igate_pre, fgate_pre, NULL, h, states, NULL, B, H, T, dqk, dhv, L,
+                            kind);
 }
 
 /*

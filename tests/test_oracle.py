@@ -254,3 +254,38 @@ def test_log_gate_sums_are_log_decay_products(kind):
                                rtol=1e-12, atol=0)
         assert np.array_equal(g[:, :, t0 // L], a[:, :, t1 - 1])
     assert np.allclose(np.exp(li), i, rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("kind", [MLSTM_SIG, SCALAR, GLA])
+def test_initial_state_splits_a_sequence(kind):
+    """Running steps [0, t1) and then [t1, T) from the first part's final
+    state reproduces the whole sequence: outputs and final state."""
+    B, H, T, dqk, dhv = 2, 2, 31, 5, 4
+    q, k, v, ig, fg = rand_case(kind, B, H, T, dqk, dhv, seed=70 + kind)
+    h_all, c_all = oracle.recurrent_fwd_state(q, k, v, ig, fg, kind)
+    for t1 in (1, 13, 30):
+        def part(a, lo, hi):
+            if a is None or kind == SCALAR and a is fg:
+                return a
+            return a[:, :, lo:hi]
+        h1, c1 = oracle.recurrent_fwd_state(part(q, 0, t1), part(k, 0, t1), part(v, 0, t1), part(ig, 0, t1),
+                                            part(fg, 0, t1), kind)
+        h2, c2 = oracle.recurrent_fwd_state(part(q, t1, T), part(k, t1, T), part(v, t1, T), part(ig, t1, T),
+                                            part(fg, t1, T), kind, c0=c1)
+        assert rel_err(np.concatenate([h1, h2], axis=2), h_all) <= REL
+        assert rel_err(c2, c_all) <= REL
+
+
+def test_initial_state_closed_form():
+    """With an initial state, h_t gains (prod_{r<=t} f_r) C_0^T q_t / sqrt(d)
+    on top of the zero-start result; the final state gains prod_{r<=T} f_r C_0."""
+    B, H, T, dqk, dhv = 1, 2, 17, 4, 3
+    q, k, v, ig, fg = rand_case(MLSTM_SIG, B, H, T, dqk, dhv, seed=81)
+    c0 = np.random.default_rng(82).standard_normal((B, H, dqk, dhv))
+    h0, cT0 = oracle.recurrent_fwd_state(q, k, v, ig, fg, MLSTM_SIG)
+    h1, cT1 = oracle.recurrent_fwd_state(q, k, v, ig, fg, MLSTM_SIG, c0=c0)
+    f = 1.0 / (1.0 + np.exp(-fg))                       # [B,H,T]
+    F = np.cumprod(f, axis=2)
+    extra = F[..., None] * np.einsum("bhtc,bhcj->bhtj", q, c0) / math.sqrt(dqk)
+    assert rel_err(h1, h0 + extra) <= REL
+    assert rel_err(cT1, cT0 + F[:, :, -1, None, None] * c0) <= REL
