@@ -3,7 +3,7 @@
  * linear attention (mLSTMsig and two gate variants) on AMD gfx950.
  *
  * The operation.  Per batch b and head h, with matrix memory C in
- * R^{d_qk x d_hv} starting at C_0 = 0:
+ * R^{d_qk x d_hv} starting at C_0 = 0 (or a given state: tfla_fwd_state):
  *
  *     C_t = diag(f_t) C_{t-1} + i_t k_t v_t^T,     h_t = C_t^T q_t / sqrt(d_qk)
  *
@@ -112,6 +112,53 @@ int tfla_fwd_ws_marked(const void* q, const void* k, const void* v,
                        const float* igate_pre, const float* fgate_pre, void* h,
                        int B, int H, int T, int d_qk, int d_hv, int L, int variant,
                        void* workspace, size_t workspace_bytes, void* const* marks, void* stream);
+
+/*
+ * tfla_fwd_state -- the forward pass from a given initial state, returning
+ * the final state (chunked prefill; splitting a long sequence into calls;
+ * the sequence-sharded evaluation of several devices).  The recurrence is
+ * the one above with C_0 taken from c0: the carried state of the
+ * step-by-step form (the "FusedRecurrent" row of the flash-linear-attention
+ * README's list of computation forms) made explicit.
+ *
+ *   c0        fp32 [B,H,d_qk,d_hv] initial state C_0 (row c = key channel,
+ *             column j = value channel), or NULL for C_0 = 0.
+ *   c_final   fp32 [B,H,d_qk,d_hv] receives C_T, or NULL.  May be the same
+ *             pointer as c0 (the state is then updated in place); must not
+ *             otherwise overlap c0, an input or h.
+ *   workspace caller-owned device workspace of at least
+ *             tfla_state_workspace_bytes(...) bytes, 256-byte aligned, or
+ *             NULL to let the call allocate it stream-ordered
+ *             (hipMallocAsync / hipFreeAsync on `stream`).
+ * Every other argument, layout and rule is that of tfla_fwd.  With c0 and
+ * c_final both NULL the result equals tfla_fwd's.
+ */
+int tfla_fwd_state(const void* q, const void* k, const void* v,
+                   const float* igate_pre, const float* fgate_pre, const float* c0,
+                   void* h, float* c_final,
+                   int B, int H, int T, int d_qk, int d_hv, int L, int variant,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace tfla_fwd_state needs (it includes a slot for
+ * the initial state); 0 when the arguments are invalid or unsupported. */
+size_t tfla_state_workspace_bytes(int B, int H, int T, int d_qk, int d_hv, int L, int variant);
+
+/*
+ * tfla_fwd_recurrent -- the same recurrence evaluated step by step in one
+ * fused kernel (the O(T) "FusedRecurrent" form of the
+ * flash-linear-attention README): for decoding one or a few steps from a
+ * carried state.  Work per call is O(T d_qk d_hv), serial in T, so long
+ * sequences belong to tfla_fwd / tfla_fwd_state.
+ *
+ *   state     fp32 [B,H,d_qk,d_hv], read as C_0 and overwritten with C_T
+ *             (the layout of tfla_fwd_state's c0 / c_final, so the two
+ *             calls chain); must not overlap an input or h.
+ * q, k, v, igate_pre, fgate_pre, h, B, H, T, d_qk, d_hv and variant are as
+ * for tfla_fwd (there is no chunk size).  No workspace; no allocation.
+ */
+int tfla_fwd_recurrent(const void* q, const void* k, const void* v,
+                       const float* igate_pre, const float* fgate_pre, float* state, void* h,
+                       int B, int H, int T, int d_qk, int d_hv, int variant, void* stream);
 
 /*
  * Test hooks: run part of the path and copy its intermediate out.

@@ -1,7 +1,7 @@
 // intra.hip -- intra-chunk kernel (third kernel of the path).
 //
 // For step t of chunk k (steps [cs, cs+L)):
-//   h_t = scale * ( e^{a_t} q_t^T C_{k-1}
+//   h_t = scale * ( e^{a_t} q_t^T C_{k-1}           (C_{-1}: the initial state, or 0)
 //                   + sum_{cs <= s <= t} e^{a_t - a_s + li_s} (q_t . k_s) v_s )
 // (GLA gate: the decay enters per key channel inside q.k, and the inter term
 // is (q_t o e^{a_t}) C_{k-1}).  TFLA's second level of sequence parallelism
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 2 : 1) void intra_kernel(const T
                                                            const float* __restrict__ fg,
                                                            const float* __restrict__ states,
                                                            T* __restrict__ h, int H, int T_, int dhv, int L,
-                                                           int nc, float scale)
+                                                           int nc, int c0, float scale)
 {
     constexpr int NTH = 64 * NW;
     constexpr int BQ = 32 * NW;           // query rows per workgroup
@@ -215,8 +215,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 2 : 1) void intra_kernel(const T
         for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
 
     // ---------------- inter-chunk term: e^{a_t} q_t^T C_{k-1}
-    if (kc > 0) {
-        const float* st = states + ((bh * (nc - 1) + kc - 1) * (size_t)dhv + v0) * DQK;
+    // states hold C before chunks 1..nc-1, preceded by C_0 when one is given (c0 = 1)
+    if (kc > 0 || c0) {
+        const float* st = states + ((bh * (nc - 1 + c0) + kc - 1 + c0) * (size_t)dhv + v0) * DQK;
         fetch_c(st, 0);
         load_q(-1);
         for (int cb = 0; cb < DQK; cb += CW) {
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 ? 2 : 1) void intra_kernel(const T
     }
 
     // ---------------- intra-chunk term, tiled along the chunk
-    if (GATE != kGla && kc == 0) load_q(-1);
+    if (GATE != kGla && kc == 0 && !c0) load_q(-1);
     const float at2 = (GATE == kSig) ? ab[tqc] * kLog2e : 0.0f;
     const int tlo = t0 + 32 * w;                  // first query row of this wave
     const int nkv = (t0 - cs) / 64 + BQ / 64;     // key tiles up to the end of the query tile
@@ -331,7 +332,7 @@ hipError_t launch_intra_t(const Problem& p, const void* q, const void* k, const 
     const float scale = 1.0f / sqrtf((float)DQK);
     intra_kernel<T, GATE, DQK, BV, NW><<<blocks, 64 * NW, 0, stream>>>(
         static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), ws.a, ws.li, fg,
-        ws.states, static_cast<T*>(h), p.H, p.T, p.dhv, p.L, p.nc, scale);
+        ws.states, static_cast<T*>(h), p.H, p.T, p.dhv, p.L, p.nc, ws.c0 != nullptr, scale);
     return hipGetLastError();
 }
 

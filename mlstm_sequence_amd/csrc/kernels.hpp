@@ -21,11 +21,16 @@ struct Workspace {
     float* a;        // [B,H,T] (GLA: [B,H,T,dqk]) chunk-local log-forget sums; NULL for kScalar
     float* li;       // [B,H,T] log input gate; kSig only
     float* g;        // [B,H,nc] (GLA: [B,H,nc,dqk]); NULL for kScalar
-    float* states;   // [B,H,nc-1,dhv,dqk] fp32, transposed states
+    float* states;   // [B,H,ns,dhv,dqk] fp32, transposed states before chunks
+                     // 1..nc-1 (ns = nc-1), or 0..nc-1 with an initial state (ns = nc)
+    const float* c0 = nullptr;   // caller's initial state [B,H,dqk,dhv] (NULL: zero)
+    float* c_final = nullptr;    // caller's final-state output [B,H,dqk,dhv] (NULL: none)
 };
 
 // Lays the workspace out from `base` (NULL: sizes only); returns its byte size.
-size_t workspace_layout(const Problem& p, Workspace* ws, char* base, bool with_states = true);
+// with_c0 reserves the extra state slot an initial state needs.
+size_t workspace_layout(const Problem& p, Workspace* ws, char* base, bool with_states = true,
+                        bool with_c0 = false);
 
 hipError_t launch_gates(const Problem& p, const float* igate_pre, const float* fgate_pre,
                         const Workspace& ws, hipStream_t stream);
@@ -33,6 +38,9 @@ hipError_t launch_gates_closed_form(const Problem& p, const float* fgate_pre, fl
                                     float* g, hipStream_t stream);
 hipError_t launch_state(const Problem& p, const void* k, const void* v, const float* fgate_pre,
                         const Workspace& ws, hipStream_t stream);
+hipError_t launch_recurrent(const Problem& p, const void* q, const void* k, const void* v,
+                            const float* igate_pre, const float* fgate_pre, float* state, void* h,
+                            hipStream_t stream);
 hipError_t launch_intra(const Problem& p, const void* q, const void* k, const void* v,
                         const float* fgate_pre, const Workspace& ws, void* h, hipStream_t stream);
 

@@ -7,9 +7,12 @@
 //   C_k = diag(e^{g_k}) C_{k-1} + sum_{s in chunk k} w_s k_s v_s^T,
 //   w_s = e^{g_k - a_s + li_s}    (per key channel c for the GLA gate:
 //                                  e^{g_{k,c} - a_{s,c}})
-// with C_0 = 0.  States after chunks 1..N_c-1 are written in fp32,
-// transposed ([d_hv][d_qk]) so the intra-chunk kernel reads them as
-// contiguous matrix-core B operands.
+// from C_0 = 0 or a given initial state.  The state before chunk k (k >= 1,
+// and k = 0 when an initial state is given) is written in fp32, transposed
+// ([d_hv][d_qk]) so the intra-chunk kernel reads it as contiguous
+// matrix-core B operands.  On request the walk continues through the last
+// (possibly partial) chunk and writes the final state C_T in the caller's
+// [d_qk][d_hv] layout.
 //
 // One workgroup owns a TV x TC tile of C^T (value rows x key columns; 128x128
 // with 8 wavefronts when the problem is large enough to give every CU one,
@@ -59,7 +62,9 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
                                                     const float* __restrict__ li,
                                                     const float* __restrict__ g,
                                                     const float* __restrict__ fg,
-                                                    float* __restrict__ states, int H, int T_,
+                                                    float* __restrict__ states,
+                                                    const float* __restrict__ c_init,
+                                                    float* __restrict__ c_final, int H, int T_,
                                                     int dqk, int dhv, int L, int nc)
 {
     constexpr int NTH = 64 * NWS;
@@ -88,21 +93,26 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
     if (GATE == kScalar) lg2 = fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor) * kLog2e;
 
     const int bpc = L / SB;                  // blocks per chunk
-    const int nblocks = (nc - 1) * bpc;      // chunks 0..nc-2 are full and feed a state
+    // chunks 0..nc-2 are full and feed a state; the last one (steps
+    // [(nc-1)L, T)) only feeds the final state
+    const int ns = nc - 1 + (c_init != nullptr);   // stored states per head
+    const int soff = c_init != nullptr;            // slot of the state after chunk kc: kc + soff
+    const int nblocks = (nc - 1) * bpc + (c_final ? (T_ - (nc - 1) * L + SB - 1) / SB : 0);
 
     auto fetch = [&](PF& pf, int b) {
         const int kc = b / bpc;
-        const int s0 = b * SB;               // chunks are full: = kc*L + (b%bpc)*SB
+        const int s0 = b * SB;               // = kc*L + (b%bpc)*SB
         if (GATE == kSig) pf.g = g[bh * nc + kc];
+        // rows past the end (partial last chunk) are read clamped and weighted 0
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
             const int idx = tid + NTH * u, r = idx / (TV / VEC), c = (idx % (TV / VEC)) * VEC;
-            pf.v[u].load(vb + (size_t)(s0 + r) * dhv + v0 + c);
+            pf.v[u].load(vb + (size_t)min(s0 + r, T_ - 1) * dhv + v0 + c);
         }
 #pragma unroll
         for (int u = 0; u < PF::NK; ++u) {
             const int idx = tid + NTH * u, r = idx / (TC / VEC), c = (idx % (TC / VEC)) * VEC;
-            const int s = s0 + r;
+            const int s = min(s0 + r, T_ - 1);
             pf.k[u].load(kb + (size_t)s * dqk + c0 + c);
             if (GATE == kSig) {
                 pf.a[u] = a[bh * T_ + s];
@@ -120,6 +130,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
     };
     auto store = [&](PF& pf, int b) {
         const int cs = (b / bpc) * L;
+        const int len = min(L, T_ - cs);     // steps in this chunk
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
             const int idx = tid + NTH * u, r = idx / (TV / VEC), c = (idx % (TV / VEC)) * VEC;
@@ -129,26 +140,53 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
         for (int u = 0; u < PF::NK; ++u) {
             const int idx = tid + NTH * u, r = idx / (TC / VEC), c = (idx % (TC / VEC)) * VEC;
             const int s = b * SB + r;
+            const bool live = s < T_;
             float ws = 1.0f;
             if (GATE == kSig) ws = exp2_fast((pf.g - pf.a[u] + pf.li[u]) * kLog2e);
-            else if (GATE == kScalar) ws = exp2_fast((float)(L - 1 - (s - cs)) * lg2);
+            else if (GATE == kScalar) ws = exp2_fast((float)(len - 1 - (s - cs)) * lg2);
             Vec16<T> kw;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 float x = pf.k[u].get(e);
                 if (GATE == kGla) x *= exp2_fast((pf.gg[u][e / 4][e % 4] - pf.ga[u][e / 4][e % 4]) * kLog2e);
                 else x *= ws;
-                kw.set(e, x);
+                kw.set(e, live ? x : 0.0f);
             }
             kw.store(&sm.ks[r][c]);
         }
     };
 
-    f32x16 acc[MV][MC];
+    // accumulator element r of lane (hh, i32) in tile (mv, mc): value row
+    // vw + 32 mv + arow(r), key column cw + 32 mc + i32
+    auto arow = [&](int r) { return 8 * (r >> 2) + 4 * hh + (r & 3); };
+    auto put_state = [&](const f32x16 (&acc)[MV][MC], int slot) {
 #pragma unroll
-    for (int mv = 0; mv < MV; ++mv)
-        for (int mc = 0; mc < MC; ++mc)
-            for (int r = 0; r < 16; ++r) acc[mv][mc][r] = 0.0f;
+        for (int mv = 0; mv < MV; ++mv) {
+            float* dst = states + ((bh * ns + slot) * (size_t)dhv + v0 + vw + 32 * mv) * dqk + c0 + cw + i32;
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dst[(size_t)arow(r) * dqk + 32 * mc] = acc[mv][mc][r];
+        }
+    };
+
+    f32x16 acc[MV][MC];
+    if (c_init) {
+        // C_0 in [d_qk][d_hv]: read once, and stored transposed as the state
+        // before chunk 0
+        const float* src = c_init + bh * (size_t)dqk * dhv;
+#pragma unroll
+        for (int mv = 0; mv < MV; ++mv)
+            for (int mc = 0; mc < MC; ++mc)
+                for (int r = 0; r < 16; ++r)
+                    acc[mv][mc][r] = src[(size_t)(c0 + cw + 32 * mc + i32) * dhv + v0 + vw + 32 * mv + arow(r)];
+        put_state(acc, 0);
+    } else {
+#pragma unroll
+        for (int mv = 0; mv < MV; ++mv)
+            for (int mc = 0; mc < MC; ++mc)
+                for (int r = 0; r < 16; ++r) acc[mv][mc][r] = 0.0f;
+    }
 
     // one block: stage it, launch the next block's loads into the freed
     // registers, multiply, and write the state at a chunk end
@@ -156,7 +194,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
     if (nblocks > 0) fetch(pf, 0);
     for (int b = 0; b < nblocks; ++b) {
         const int kc = b / bpc;
-        const bool first = (b % bpc) == 0, last = (b % bpc) == bpc - 1;
+        const bool first = (b % bpc) == 0, last = (b % bpc) == bpc - 1 || b == nblocks - 1;
         __syncthreads();
         store(pf, b);
         const float gk = pf.g;                // g of this block's chunk, before the next fetch overwrites it
@@ -168,7 +206,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
             for (int mc = 0; mc < MC; ++mc) {
                 float e;
                 if (GATE == kSig) e = exp2_fast(gk * kLog2e);
-                else if (GATE == kScalar) e = exp2_fast((float)L * lg2);
+                else if (GATE == kScalar) e = exp2_fast((float)min(L, T_ - kc * L) * lg2);
                 else e = exp2_fast(g[(bh * nc + kc) * dqk + c0 + cw + 32 * mc + i32] * kLog2e);
 #pragma unroll
                 for (int mv = 0; mv < MV; ++mv) acc[mv][mc] *= e;
@@ -188,14 +226,17 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
                 for (int mc = 0; mc < MC; ++mc) acc[mv][mc] = mma32(af[mv], bf[mc], acc[mv][mc]);
         }
         if (last) {
+            if (kc < nc - 1) {
+                put_state(acc, kc + soff);
+            } else {
+                // C_T in [d_qk][d_hv]; each workgroup writes only the tile it read
+                // from C_0, so the two may be the same buffer
+                float* dst = c_final + bh * (size_t)dqk * dhv;
 #pragma unroll
-            for (int mv = 0; mv < MV; ++mv) {
-                float* dst = states + ((bh * (nc - 1) + kc) * (size_t)dhv + v0 + vw + 32 * mv) * dqk + c0 + cw + i32;
-#pragma unroll
-                for (int mc = 0; mc < MC; ++mc)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        dst[(size_t)(8 * (r >> 2) + 4 * hh + (r & 3)) * dqk + 32 * mc] = acc[mv][mc][r];
+                for (int mv = 0; mv < MV; ++mv)
+                    for (int mc = 0; mc < MC; ++mc)
+                        for (int r = 0; r < 16; ++r)
+                            dst[(size_t)(c0 + cw + 32 * mc + i32) * dhv + v0 + vw + 32 * mv + arow(r)] = acc[mv][mc][r];
             }
         }
     }
@@ -210,15 +251,15 @@ hipError_t launch_state_cfg(const Problem& p, const T* k, const T* v, const floa
     switch (p.gate) {
     case kSig:
         state_kernel<T, kSig, SB, TV, TC, NWS><<<blocks, threads, 0, stream>>>(
-            k, v, ws.a, ws.li, ws.g, fg, ws.states, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
+            k, v, ws.a, ws.li, ws.g, fg, ws.states, ws.c0, ws.c_final, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
         break;
     case kScalar:
         state_kernel<T, kScalar, SB, TV, TC, NWS><<<blocks, threads, 0, stream>>>(
-            k, v, ws.a, ws.li, ws.g, fg, ws.states, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
+            k, v, ws.a, ws.li, ws.g, fg, ws.states, ws.c0, ws.c_final, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
         break;
     default:
         state_kernel<T, kGla, SB, TV, TC, NWS><<<blocks, threads, 0, stream>>>(
-            k, v, ws.a, ws.li, ws.g, fg, ws.states, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
+            k, v, ws.a, ws.li, ws.g, fg, ws.states, ws.c0, ws.c_final, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
         break;
     }
     return hipGetLastError();
@@ -228,7 +269,7 @@ template <typename T>
 hipError_t launch_state_t(const Problem& p, const T* k, const T* v, const float* fg, const Workspace& ws,
                           hipStream_t stream)
 {
-    if (p.nc < 2) return hipSuccess;
+    if (p.nc < 2 && !ws.c0 && !ws.c_final) return hipSuccess;
     // 128x128 tiles halve the LDS bytes per flop and the L2 re-reads of K and
     // V; use them when they still give every CU a workgroup (bf16 I/O only:
     // fp32 blocks would not fit LDS), else 64x64 tiles for parallelism.  The

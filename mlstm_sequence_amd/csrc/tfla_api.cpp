@@ -112,6 +112,32 @@ int check_fwd(const void* q, const void* k, const void* v, const float* igate_pr
     return TFLA_OK;
 }
 
+// Initial / final state buffers: fp32 [B,H,d_qk,d_hv], 16-byte aligned.
+// c_final may be c0 itself (in-place update); otherwise neither overlaps an
+// input or h.
+int check_state_io(const tfla::Problem& p, const void* q, const void* k, const void* v, const float* igate_pre,
+                   const float* fgate_pre, const void* h, const float* c0, const float* c_final)
+{
+    if ((c0 && !aligned(c0, 16)) || (c_final && !aligned(c_final, 16)))
+        return fail(TFLA_ERR_INVALID_ARG, "c0 and c_final must be 16-byte aligned");
+    const size_t esz = p.bf16 ? 2 : 4;
+    const size_t bht = (size_t)p.B * p.H * p.T;
+    const size_t sbytes = (size_t)p.B * p.H * p.dqk * p.dhv * 4;
+    const Range ins[] = {range_of(q, bht * p.dqk * esz), range_of(k, bht * p.dqk * esz),
+                         range_of(v, bht * p.dhv * esz), range_of(h, bht * p.dhv * esz),
+                         range_of(fgate_pre, gate_bytes(p)),
+                         igate_pre ? range_of(igate_pre, bht * 4) : Range{0, 0}};
+    for (const float* st : {c0, c_final}) {
+        if (!st) continue;
+        const Range r = range_of(st, sbytes);
+        for (const Range& x : ins)
+            if (overlaps(r, x)) return fail(TFLA_ERR_INVALID_ARG, "c0 / c_final overlaps q, k, v, h or a gate");
+    }
+    if (c0 && c_final && c0 != c_final && overlaps(range_of(c0, sbytes), range_of(c_final, sbytes)))
+        return fail(TFLA_ERR_INVALID_ARG, "c_final overlaps c0 without being the same buffer");
+    return TFLA_OK;
+}
+
 // Failure injection for tests of the error paths: TFLA_FAULT=alloc makes the
 // library's own workspace allocation fail before any launch.
 bool inject_alloc_fault()
@@ -153,7 +179,7 @@ int run_path(const tfla::Problem& p, const void* q, const void* k, const void* v
 
 namespace tfla {
 
-size_t workspace_layout(const Problem& p, Workspace* ws, char* base, bool with_states)
+size_t workspace_layout(const Problem& p, Workspace* ws, char* base, bool with_states, bool with_c0)
 {
     const size_t bh = (size_t)p.B * p.H;
     const size_t w = p.gate == kGla ? p.dqk : 1;
@@ -166,7 +192,8 @@ size_t workspace_layout(const Problem& p, Workspace* ws, char* base, bool with_s
     ws->a = p.gate == kScalar ? nullptr : take(bh * p.T * w * 4);
     ws->li = p.gate == kSig ? take(bh * p.T * 4) : nullptr;
     ws->g = p.gate == kScalar ? nullptr : take(bh * p.nc * w * 4);
-    ws->states = (with_states && p.nc > 1) ? take(bh * (size_t)(p.nc - 1) * p.dhv * p.dqk * 4) : nullptr;
+    const size_t slots = p.nc - 1 + (with_c0 ? 1 : 0);
+    ws->states = (with_states && slots > 0) ? take(bh * slots * p.dhv * p.dqk * 4) : nullptr;
     return off;
 }
 
@@ -234,6 +261,66 @@ int tfla_fwd(const void* q, const void* k, const void* v, const float* igate_pre
         if (e != hipSuccess && rc == TFLA_OK) rc = hip_fail(e, "workspace free");
     }
     return rc;
+}
+
+size_t tfla_state_workspace_bytes(int B, int H, int T, int d_qk, int d_hv, int L, int variant)
+{
+    tfla::Problem p;
+    if (check_problem(B, H, T, d_qk, d_hv, L, variant, &p) != TFLA_OK) return 0;
+    tfla::Workspace ws;
+    return tfla::workspace_layout(p, &ws, nullptr, true, true);
+}
+
+int tfla_fwd_state(const void* q, const void* k, const void* v, const float* igate_pre, const float* fgate_pre,
+                   const float* c0, void* h, float* c_final, int B, int H, int T, int d_qk, int d_hv, int L,
+                   int variant, void* workspace, size_t workspace_bytes, void* stream)
+{
+    tfla::Problem p;
+    int rc = check_fwd(q, k, v, igate_pre, fgate_pre, h, B, H, T, d_qk, d_hv, L, variant, &p);
+    if (rc) return rc;
+    if ((rc = check_state_io(p, q, k, v, igate_pre, fgate_pre, h, c0, c_final))) return rc;
+    tfla::Workspace ws;
+    const bool with_c0 = c0 != nullptr;
+    const size_t need = tfla::workspace_layout(p, &ws, nullptr, true, with_c0);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* base = workspace;
+    if (workspace) {
+        if (!aligned(workspace, 256)) return fail(TFLA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+        if (workspace_bytes < need)
+            return fail(TFLA_ERR_OUT_OF_MEMORY, "workspace of " + std::to_string(workspace_bytes) +
+                                                    " bytes is smaller than the " + std::to_string(need) + " needed");
+    } else if (need > 0) {
+        if (inject_alloc_fault())
+            return fail(TFLA_ERR_OUT_OF_MEMORY, "injected allocation failure (TFLA_FAULT=alloc)");
+        hipError_t e = hipMallocAsync(&base, need, s);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(TFLA_ERR_OUT_OF_MEMORY, std::string("workspace allocation of ") + std::to_string(need) +
+                                                    " bytes failed: " + hipGetErrorString(e));
+        }
+    }
+    tfla::workspace_layout(p, &ws, static_cast<char*>(base), true, with_c0);
+    ws.c0 = c0;
+    ws.c_final = c_final;
+    rc = run_path(p, q, k, v, igate_pre, fgate_pre, h, ws, s);
+    if (!workspace && base) {
+        hipError_t e = hipFreeAsync(base, s);
+        if (e != hipSuccess && rc == TFLA_OK) rc = hip_fail(e, "workspace free");
+    }
+    return rc;
+}
+
+int tfla_fwd_recurrent(const void* q, const void* k, const void* v, const float* igate_pre, const float* fgate_pre,
+                       float* state, void* h, int B, int H, int T, int d_qk, int d_hv, int variant, void* stream)
+{
+    tfla::Problem p;
+    // the chunk size plays no part here; any valid one passes the shared checks
+    int rc = check_fwd(q, k, v, igate_pre, fgate_pre, h, B, H, T, d_qk, d_hv, 64, variant, &p);
+    if (rc) return rc;
+    if (!state) return fail(TFLA_ERR_INVALID_ARG, "state must not be NULL");
+    if ((rc = check_state_io(p, q, k, v, igate_pre, fgate_pre, h, state, nullptr))) return rc;
+    hipError_t e = tfla::launch_recurrent(p, q, k, v, igate_pre, fgate_pre, state, h, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TFLA_OK : hip_fail(e, "recurrent kernel launch");
 }
 
 int tfla_dbg_gates(const float* igate_pre, const float* fgate_pre, float* a_out, float* li_out, float* g_out,
@@ -313,6 +400,6 @@ const char* tfla_error_string(int code)
 
 const char* tfla_last_error(void) { return g_last_error.c_str(); }
 
-int tfla_version(void) { return 100; }
+int tfla_version(void) { return 200; }
 
 }  // extern "C"

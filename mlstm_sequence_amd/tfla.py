@@ -46,6 +46,12 @@ def lib():
         L.tfla_fwd_ws_marked.restype = i
         L.tfla_workspace_bytes.argtypes = [i] * 7
         L.tfla_workspace_bytes.restype = sz
+        L.tfla_fwd_state.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp] + [i] * 7 + [vp, sz, vp]
+        L.tfla_fwd_state.restype = i
+        L.tfla_state_workspace_bytes.argtypes = [i] * 7
+        L.tfla_state_workspace_bytes.restype = sz
+        L.tfla_fwd_recurrent.argtypes = [vp, vp, vp, fp, fp, fp, vp] + [i] * 6 + [vp]
+        L.tfla_fwd_recurrent.restype = i
         L.tfla_dbg_gates.argtypes = [fp, fp, fp, fp, fp] + [i] * 6 + [vp]
         L.tfla_dbg_gates.restype = i
         L.tfla_dbg_states.argtypes = [vp, vp, fp, fp, fp] + [i] * 7 + [vp]
@@ -130,6 +136,27 @@ def tfla_fwd_ws_marked(q, k, v, igate_pre, fgate_pre, h, B, H, T, d_qk, d_hv, L,
                                   B, H, T, d_qk, d_hv, L, variant, _ptr(workspace), workspace_bytes, arr,
                                   _stream(stream))
     _check(rc, "tfla_fwd_ws_marked")
+
+
+def tfla_state_workspace_bytes(B, H, T, d_qk, d_hv, L, variant) -> int:
+    return lib().tfla_state_workspace_bytes(B, H, T, d_qk, d_hv, L, variant)
+
+
+def tfla_fwd_state(q, k, v, igate_pre, fgate_pre, c0, h, c_final, B, H, T, d_qk, d_hv, L, variant,
+                   workspace=None, workspace_bytes=0, stream=None):
+    """tfla_fwd_state(...): c0 / c_final fp32 [B,H,d_qk,d_hv] or None;
+    workspace None lets the library allocate it."""
+    rc = lib().tfla_fwd_state(_ptr(q), _ptr(k), _ptr(v), _ptr(igate_pre), _ptr(fgate_pre), _ptr(c0), _ptr(h),
+                              _ptr(c_final), B, H, T, d_qk, d_hv, L, variant, _ptr(workspace),
+                              workspace_bytes, _stream(stream))
+    _check(rc, "tfla_fwd_state")
+
+
+def tfla_fwd_recurrent(q, k, v, igate_pre, fgate_pre, state, h, B, H, T, d_qk, d_hv, variant, stream=None):
+    """tfla_fwd_recurrent(...): ``state`` fp32 [B,H,d_qk,d_hv] is updated in place."""
+    rc = lib().tfla_fwd_recurrent(_ptr(q), _ptr(k), _ptr(v), _ptr(igate_pre), _ptr(fgate_pre), _ptr(state),
+                                  _ptr(h), B, H, T, d_qk, d_hv, variant, _stream(stream))
+    _check(rc, "tfla_fwd_recurrent")
 
 
 def tfla_dbg_gates(igate_pre, fgate_pre, a_out, li_out, g_out, B, H, T, d_qk, L, variant, stream=None):

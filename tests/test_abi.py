@@ -17,7 +17,7 @@ SIG, SCALAR, GLA = 0, 1, 2
 INVALID, UNSUPPORTED, OOM = 1, 2, 4
 
 # 16-byte aligned fake device addresses: validation never dereferences them
-Q, K, V, H_, IG, FG, WS = (0x10000000 * (n + 1) for n in range(7))
+Q, K, V, H_, IG, FG, WS, C0, CF = (0x10000000 * (n + 1) for n in range(9))
 
 
 def declared_functions():
@@ -36,13 +36,14 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert {"tfla_fwd", "tfla_fwd_ws", "tfla_workspace_bytes", "tfla_dbg_gates", "tfla_dbg_states",
+            "tfla_fwd_state", "tfla_state_workspace_bytes", "tfla_fwd_recurrent",
             "tfla_error_string", "tfla_last_error", "tfla_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_strings(L):
-    assert tfla.tfla_version() == 100
+    assert tfla.tfla_version() == 200
     for code in range(5):
         assert tfla.error_string(code)
     assert tfla.error_string(99) == "unknown status code"
@@ -107,3 +108,63 @@ def test_python_binding_raises(L):
     with pytest.raises(tfla.TflaError) as ei:
         tfla.tfla_fwd(Q, K, V, IG, FG, H_, 2, 3, 300, 96, 256, 64, SIG | BF16, stream=0)
     assert ei.value.code == UNSUPPORTED
+
+
+def fwd_state(c0=C0, cf=CF, ws=WS, nws=1 << 30, **kw):
+    a = dict(q=Q, k=K, v=V, ig=IG, fg=FG, h=H_, B=2, H=3, T=300, dqk=128, dhv=256, Lc=64, variant=SIG | BF16)
+    a.update(kw)
+    return tfla.lib().tfla_fwd_state(a["q"], a["k"], a["v"], a["ig"], a["fg"], c0, a["h"], cf, a["B"], a["H"],
+                                     a["T"], a["dqk"], a["dhv"], a["Lc"], a["variant"], ws, nws, None)
+
+
+SBYTES = 2 * 3 * 128 * 256 * 4   # one state per head at the shapes above
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(c0=C0 + 4), INVALID), (dict(cf=CF + 8), INVALID),          # misaligned
+    (dict(cf=H_ + 64), INVALID), (dict(c0=Q), INVALID),              # overlaps an input / h
+    (dict(c0=K + 4096), INVALID), (dict(cf=FG), INVALID),
+    (dict(cf=C0 + 256), INVALID),                                    # partial overlap of c0 and c_final
+    (dict(nws=1000), OOM), (dict(ws=WS + 16), INVALID),               # workspace too small / misaligned
+    (dict(dqk=96), UNSUPPORTED), (dict(q=None), INVALID), (dict(variant=7), INVALID),
+])
+def test_fwd_state_rejects_bad_arguments(L, kw, code):
+    assert fwd_state(**kw) == code
+    assert tfla.tfla_last_error()
+
+
+def test_fwd_state_allocation_failure(L, monkeypatch):
+    monkeypatch.setenv("TFLA_FAULT", "alloc")
+    assert fwd_state(ws=None, nws=0) == OOM
+    assert "injected" in tfla.tfla_last_error()
+
+
+def test_state_workspace_bytes(L):
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    B, H, T, dqk, dhv, Lc = 2, 3, 300, 128, 256, 64
+    nc = -(-T // Lc)
+    base = tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16)
+    sig = a256(B * H * T * 4) * 2 + a256(B * H * nc * 4) + a256(B * H * nc * dhv * dqk * 4)
+    assert tfla.tfla_state_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16) == sig > base
+    # one chunk: the only state slot is the initial state's
+    assert tfla.tfla_state_workspace_bytes(B, H, 64, dqk, dhv, Lc, SCALAR | BF16) == a256(B * H * dhv * dqk * 4)
+    assert tfla.tfla_state_workspace_bytes(B, H, T, 96, dhv, Lc, SIG) == 0
+
+
+def rec(state=C0, **kw):
+    a = dict(q=Q, k=K, v=V, ig=IG, fg=FG, h=H_, B=2, H=3, T=5, dqk=128, dhv=256, variant=SIG | BF16)
+    a.update(kw)
+    return tfla.lib().tfla_fwd_recurrent(a["q"], a["k"], a["v"], a["ig"], a["fg"], state, a["h"], a["B"], a["H"],
+                                         a["T"], a["dqk"], a["dhv"], a["variant"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(state=None), INVALID), (dict(state=C0 + 4), INVALID), (dict(state=H_), INVALID),
+    (dict(state=V + 256), INVALID), (dict(T=0), INVALID), (dict(ig=None), INVALID),
+    (dict(dhv=100), UNSUPPORTED), (dict(dqk=256, variant=SIG), UNSUPPORTED),
+])
+def test_recurrent_rejects_bad_arguments(L, kw, code):
+    assert rec(**kw) == code
+    assert tfla.tfla_last_error()

@@ -119,6 +119,12 @@ def as_f64(t) -> np.ndarray | None:
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
+def initial_state(B: int, H: int, dqk: int, dhv: int, seed: int, std: float = 1.0) -> torch.Tensor:
+    """A seeded fp32 initial state C_0 [B,H,d_qk,d_hv] ~ N(0, std^2)."""
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn((B, H, dqk, dhv), generator=g, dtype=torch.float32) * std
+
+
 def head_slice(inputs: dict, variant: int, heads: list) -> dict:
     """Inputs restricted to a list of (b, h) pairs, as a batch of one with
     len(heads) heads -- used to run the oracle on sampled heads of a large
