@@ -279,6 +279,17 @@ def main():
         "sweep": {str(L): {"tokens_per_s": x["tokens_per_s"], "ms_per_step": x["ms"],
                            "mfma_frac": x["mfma_frac"], "kernels_ms": x["per"]} for L, x in results.items()},
     }
+    # Chunk-size ablation (limit_chunk vs xl_chunk, TFLA abstract and summary):
+    # at L = 64 every chunk is a single 64-step key/value tile, i.e. the chunk
+    # is bounded by what one workgroup stages on chip; larger L tile the
+    # chunk along the sequence.  Reported when L = 64 was swept.
+    if 64 in results and len(results) > 1:
+        xl = max((L for L in results if L != 64), key=lambda L: results[L]["tokens_per_s"])
+        out["chunking_ablation"] = {
+            "limit_chunk": {"L": 64, "ms_per_step": results[64]["ms"], "tokens_per_s": results[64]["tokens_per_s"]},
+            "xl_chunk": {"L": xl, "ms_per_step": results[xl]["ms"], "tokens_per_s": results[xl]["tokens_per_s"]},
+            "xl_speedup": results[xl]["tokens_per_s"] / results[64]["tokens_per_s"],
+        }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(wl)

@@ -25,7 +25,17 @@ struct Workspace {
                      // 1..nc-1 (ns = nc-1), or 0..nc-1 with an initial state (ns = nc)
     const float* c0 = nullptr;   // caller's initial state [B,H,dqk,dhv] (NULL: zero)
     float* c_final = nullptr;    // caller's final-state output [B,H,dqk,dhv] (NULL: none)
+    float* seg_end = nullptr;    // segmented state walk: end states [B*H][P][dqk][dhv]
+    float* seg_start = nullptr;  //                       start states [B*H][P][dqk][dhv]
 };
+
+// Segmented state walk (few heads, long sequences): number of segments P
+// (1: unsegmented), chunks per segment, and whether 128x128 state tiles
+// are used.  Functions of the problem shape only.
+int state_segments(const Problem& p);
+int state_segments_for(const Problem& p, long heads_tiles);
+int state_chunks_per_segment(const Problem& p, int P);
+bool state_big_tiles(const Problem& p);
 
 // Lays the workspace out from `base` (NULL: sizes only); returns its byte size.
 // with_c0 reserves the extra state slot an initial state needs.

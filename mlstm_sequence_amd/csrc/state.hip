@@ -25,6 +25,19 @@
 // issued into registers right after the current block reached LDS.  Blocks
 // are as long as the chunk allows (up to 256 steps on 128x128 tiles).
 // States leave as 128-byte rows.
+//
+// Few heads and long sequences leave most CUs idle on that serial walk.
+// Then the chunk chain is cut into P segments (sequence parallelism on one
+// device, the same decomposition that shards a sequence over devices):
+//   pass 1: every segment but the last walks its chunks from zero and
+//           writes its end state E_p;
+//   combine: S_0 = C_0, S_{p+1} = diag(e^{G_p}) S_p + E_p, G_p the segment's
+//           summed log forget gate (per key channel for the GLA gate);
+//   pass 2: every segment walks its chunks again from its true start S_p
+//           and writes the states (and C_T).
+// It costs one more read of k and v; the serial part left is P steps of a
+// d_qk x d_hv elementwise update.
+#include <algorithm>
 #include <cstdlib>
 
 #include "gfx950.hpp"
@@ -32,6 +45,22 @@
 
 namespace tfla {
 namespace {
+
+// What one launch of the state kernel walks and writes.  Grid =
+// tiles x heads x nseg, segment slowest.
+struct StateWalk {
+    const float* init;   // initial states [B*H][nseg_buf][d_qk][d_hv]; NULL: zero
+    float* end;          // end states: [B*H][nseg_buf][d_qk][d_hv] (end_all), else
+                         // [B*H][d_qk][d_hv] written by the last segment; NULL: none
+    int nseg_buf;        // segments per head in the init / end buffers
+    int nseg;            // segments in the grid
+    int cps;             // chunks per segment
+    int nwalk;           // chunks walked in all (nc-1, or nc to reach C_T)
+    int put_c0;          // segment 0 stores its initial state as the state before chunk 0
+    int end_all;         // every segment writes its end state
+    int write_states;    // store the state after every chunk kc < nc-1
+    int soff;            // 1 when the stored states start with C_0
+};
 
 // Tile of C^T per workgroup: TV value rows x TC key columns; NWS wavefronts
 // in a 2 x (NWS/2) grid, each owning a (TV/2) x (2 TC/NWS) piece as 32x32
@@ -62,10 +91,8 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
                                                     const float* __restrict__ li,
                                                     const float* __restrict__ g,
                                                     const float* __restrict__ fg,
-                                                    float* __restrict__ states,
-                                                    const float* __restrict__ c_init,
-                                                    float* __restrict__ c_final, int H, int T_,
-                                                    int dqk, int dhv, int L, int nc)
+                                                    float* __restrict__ states, StateWalk wk, int H,
+                                                    int T_, int dqk, int dhv, int L, int nc)
 {
     constexpr int NTH = 64 * NWS;
     typedef StatePrefetch<T, SB, TV, TC, NTH> PF;
@@ -78,8 +105,10 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
     const int ntv = dhv / TV, ntk = dqk / TC;
     const int blk = xcd_remap(blockIdx.x, gridDim.x);
     const int tiles = ntv * ntk;
-    const size_t bh = blk / tiles;
+    const int nbh = gridDim.x / (tiles * wk.nseg);
     const int tile = blk % tiles;
+    const size_t bh = (blk / tiles) % nbh;
+    const int seg = blk / (tiles * nbh);
     const int v0 = (tile / ntk) * TV;
     const int c0 = (tile % ntk) * TC;
 
@@ -94,10 +123,14 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
 
     const int bpc = L / SB;                  // blocks per chunk
     // chunks 0..nc-2 are full and feed a state; the last one (steps
-    // [(nc-1)L, T)) only feeds the final state
-    const int ns = nc - 1 + (c_init != nullptr);   // stored states per head
-    const int soff = c_init != nullptr;            // slot of the state after chunk kc: kc + soff
-    const int nblocks = (nc - 1) * bpc + (c_final ? (T_ - (nc - 1) * L + SB - 1) / SB : 0);
+    // [(nc-1)L, T)) only feeds the final state.  This workgroup walks the
+    // chunks [kbeg, kend) of its segment: blocks [b0, bend).
+    const int ns = nc - 1 + wk.soff;                // stored states per head
+    // (the buffer's last segment also takes any chunks past P * cps)
+    const int kbeg = seg * wk.cps;
+    const int kend = seg == wk.nseg_buf - 1 ? wk.nwalk : min(kbeg + wk.cps, wk.nwalk);
+    const int b0 = kbeg * bpc;
+    const int bend = kend <= nc - 1 ? kend * bpc : (nc - 1) * bpc + (T_ - (nc - 1) * L + SB - 1) / SB;
 
     auto fetch = [&](PF& pf, int b) {
         const int kc = b / bpc;
@@ -170,17 +203,20 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
         }
     };
 
+    // tile element (acc layout) <-> index in a [d_qk][d_hv] state
+    auto nat = [&](int mv, int mc, int r) {
+        return (size_t)(c0 + cw + 32 * mc + i32) * dhv + v0 + vw + 32 * mv + arow(r);
+    };
     f32x16 acc[MV][MC];
-    if (c_init) {
-        // C_0 in [d_qk][d_hv]: read once, and stored transposed as the state
-        // before chunk 0
-        const float* src = c_init + bh * (size_t)dqk * dhv;
+    if (wk.init) {
+        // the segment's initial state in [d_qk][d_hv]: read once; segment 0
+        // stores the caller's C_0 transposed as the state before chunk 0
+        const float* src = wk.init + (bh * wk.nseg_buf + seg) * (size_t)dqk * dhv;
 #pragma unroll
         for (int mv = 0; mv < MV; ++mv)
             for (int mc = 0; mc < MC; ++mc)
-                for (int r = 0; r < 16; ++r)
-                    acc[mv][mc][r] = src[(size_t)(c0 + cw + 32 * mc + i32) * dhv + v0 + vw + 32 * mv + arow(r)];
-        put_state(acc, 0);
+                for (int r = 0; r < 16; ++r) acc[mv][mc][r] = src[nat(mv, mc, r)];
+        if (seg == 0 && wk.put_c0) put_state(acc, 0);
     } else {
 #pragma unroll
         for (int mv = 0; mv < MV; ++mv)
@@ -191,15 +227,15 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
     // one block: stage it, launch the next block's loads into the freed
     // registers, multiply, and write the state at a chunk end
     PF pf;
-    if (nblocks > 0) fetch(pf, 0);
-    for (int b = 0; b < nblocks; ++b) {
+    if (b0 < bend) fetch(pf, b0);
+    for (int b = b0; b < bend; ++b) {
         const int kc = b / bpc;
-        const bool first = (b % bpc) == 0, last = (b % bpc) == bpc - 1 || b == nblocks - 1;
+        const bool first = (b % bpc) == 0, last = (b % bpc) == bpc - 1 || b == bend - 1;
         __syncthreads();
         store(pf, b);
         const float gk = pf.g;                // g of this block's chunk, before the next fetch overwrites it
         __syncthreads();
-        if (b + 1 < nblocks) fetch(pf, b + 1);
+        if (b + 1 < bend) fetch(pf, b + 1);
         if (first) {
             // decay of the carried state across chunk kc (column c of C^T = row c of C)
 #pragma unroll
@@ -225,44 +261,123 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
 #pragma unroll
                 for (int mc = 0; mc < MC; ++mc) acc[mv][mc] = mma32(af[mv], bf[mc], acc[mv][mc]);
         }
-        if (last) {
-            if (kc < nc - 1) {
-                put_state(acc, kc + soff);
-            } else {
-                // C_T in [d_qk][d_hv]; each workgroup writes only the tile it read
-                // from C_0, so the two may be the same buffer
-                float* dst = c_final + bh * (size_t)dqk * dhv;
+        if (last && wk.write_states && kc < nc - 1) put_state(acc, kc + wk.soff);
+        if (b == bend - 1 && wk.end && (wk.end_all || seg == wk.nseg - 1)) {
+            // the state after the walk, in [d_qk][d_hv]; each workgroup writes
+            // only the tile it read from its initial state, so the caller's C_0
+            // and C_T may be the same buffer
+            float* dst = wk.end + (bh * (wk.end_all ? wk.nseg_buf : 1) + (wk.end_all ? seg : 0)) * (size_t)dqk * dhv;
 #pragma unroll
-                for (int mv = 0; mv < MV; ++mv)
-                    for (int mc = 0; mc < MC; ++mc)
-                        for (int r = 0; r < 16; ++r)
-                            dst[(size_t)(c0 + cw + 32 * mc + i32) * dhv + v0 + vw + 32 * mv + arow(r)] = acc[mv][mc][r];
+            for (int mv = 0; mv < MV; ++mv)
+                for (int mc = 0; mc < MC; ++mc)
+                    for (int r = 0; r < 16; ++r) dst[nat(mv, mc, r)] = acc[mv][mc][r];
+        }
+    }
+}
+
+// combine pass: start states of the segments from their end states
+template <int GATE>
+__global__ __launch_bounds__(256) void state_combine_kernel(const float* __restrict__ E, float* __restrict__ S,
+                                                            const float* __restrict__ c0,
+                                                            const float* __restrict__ g,
+                                                            const float* __restrict__ fg, int H, int dqk,
+                                                            int dhv, int L, int nc, int P, int cps)
+{
+    const size_t n = (size_t)dqk * dhv;
+    const size_t bh = blockIdx.y;
+    const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= n) return;
+    const int c = (int)(e / dhv);
+    float lgam = 0.0f;
+    if (GATE == kScalar) lgam = fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor);
+    float st = c0 ? c0[bh * n + e] : 0.0f;
+    S[(bh * P) * n + e] = st;
+    constexpr int U = 8;   // segments whose loads are issued together
+    for (int p0 = 0; p0 + 1 < P; p0 += U) {
+        float ev[U], gv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = p0 + u;
+            ev[u] = 0.0f;
+            gv[u] = 0.0f;
+            if (p + 1 < P) {
+                ev[u] = E[(bh * P + p) * n + e];
+                if (GATE == kScalar) {
+                    gv[u] = (float)(cps * L) * lgam;
+                } else {
+                    for (int kc = p * cps; kc < (p + 1) * cps; ++kc)
+                        gv[u] += GATE == kSig ? g[bh * nc + kc] : g[(bh * nc + kc) * dqk + c];
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = p0 + u;
+            if (p + 1 < P) {
+                st = exp2_fast(gv[u] * kLog2e) * st + ev[u];
+                S[(bh * P + p + 1) * n + e] = st;
             }
         }
     }
 }
 
 template <typename T, int SB, int TV, int TC, int NWS>
-hipError_t launch_state_cfg(const Problem& p, const T* k, const T* v, const float* fg, const Workspace& ws,
-                            hipStream_t stream)
+hipError_t launch_walk(const Problem& p, const T* k, const T* v, const float* fg, const Workspace& ws,
+                       const StateWalk& wk, hipStream_t stream)
 {
-    const int blocks = p.B * p.H * (p.dhv / TV) * (p.dqk / TC);
+    const int blocks = p.B * p.H * (p.dhv / TV) * (p.dqk / TC) * wk.nseg;
     const int threads = 64 * NWS;
     switch (p.gate) {
     case kSig:
         state_kernel<T, kSig, SB, TV, TC, NWS><<<blocks, threads, 0, stream>>>(
-            k, v, ws.a, ws.li, ws.g, fg, ws.states, ws.c0, ws.c_final, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
+            k, v, ws.a, ws.li, ws.g, fg, ws.states, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
         break;
     case kScalar:
         state_kernel<T, kScalar, SB, TV, TC, NWS><<<blocks, threads, 0, stream>>>(
-            k, v, ws.a, ws.li, ws.g, fg, ws.states, ws.c0, ws.c_final, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
+            k, v, ws.a, ws.li, ws.g, fg, ws.states, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
         break;
     default:
         state_kernel<T, kGla, SB, TV, TC, NWS><<<blocks, threads, 0, stream>>>(
-            k, v, ws.a, ws.li, ws.g, fg, ws.states, ws.c0, ws.c_final, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
+            k, v, ws.a, ws.li, ws.g, fg, ws.states, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
         break;
     }
     return hipGetLastError();
+}
+
+// One configuration: unsegmented walk, or pass 1 + combine + pass 2.
+template <typename T, int SB, int TV, int TC, int NWS>
+hipError_t launch_state_cfg(const Problem& p, const T* k, const T* v, const float* fg, const Workspace& ws,
+                            hipStream_t stream)
+{
+    const int P = state_segments(p);
+    const int soff = ws.c0 != nullptr;
+    const int nwalk = p.nc - 1 + (ws.c_final != nullptr);
+    if (P <= 1) {
+        const StateWalk wk{ws.c0, ws.c_final, 1, 1, nwalk > 0 ? nwalk : 1, nwalk, soff, 0, 1, soff};
+        return launch_walk<T, SB, TV, TC, NWS>(p, k, v, fg, ws, wk, stream);
+    }
+    const int cps = state_chunks_per_segment(p, P);
+    const StateWalk pass1{nullptr, ws.seg_end, P, P - 1, cps, p.nc - 1, 0, 1, 0, soff};
+    hipError_t e = launch_walk<T, SB, TV, TC, NWS>(p, k, v, fg, ws, pass1, stream);
+    if (e != hipSuccess) return e;
+    const dim3 cgrid((unsigned)((p.dqk * p.dhv + 255) / 256), (unsigned)(p.B * p.H));
+    switch (p.gate) {
+    case kSig:
+        state_combine_kernel<kSig><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, ws.c0, ws.g, fg, p.H, p.dqk,
+                                                              p.dhv, p.L, p.nc, P, cps);
+        break;
+    case kScalar:
+        state_combine_kernel<kScalar><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, ws.c0, ws.g, fg, p.H,
+                                                                 p.dqk, p.dhv, p.L, p.nc, P, cps);
+        break;
+    default:
+        state_combine_kernel<kGla><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, ws.c0, ws.g, fg, p.H, p.dqk,
+                                                              p.dhv, p.L, p.nc, P, cps);
+        break;
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const StateWalk pass2{ws.seg_start, ws.c_final, P, P, cps, nwalk, soff, 0, 1, soff};
+    return launch_walk<T, SB, TV, TC, NWS>(p, k, v, fg, ws, pass2, stream);
 }
 
 template <typename T>
@@ -270,16 +385,10 @@ hipError_t launch_state_t(const Problem& p, const T* k, const T* v, const float*
                           hipStream_t stream)
 {
     if (p.nc < 2 && !ws.c0 && !ws.c_final) return hipSuccess;
-    // 128x128 tiles halve the LDS bytes per flop and the L2 re-reads of K and
-    // V; use them when they still give every CU a workgroup (bf16 I/O only:
-    // fp32 blocks would not fit LDS), else 64x64 tiles for parallelism.  The
-    // big tiles run 8 waves over blocks of up to 256 steps (128 KB of loads in
-    // flight per workgroup).
-    const long big = (long)p.B * p.H * (p.dhv / 128) * (p.dqk / 128);
     int sb_cap = 256;   // TFLA_STATE_SB=64|128 caps the block (tuning sweeps)
     if (const char* e = std::getenv("TFLA_STATE_SB")) sb_cap = std::atoi(e);
     if constexpr (sizeof(T) == 2) {
-        if (p.dhv % 128 == 0 && p.dqk % 128 == 0 && big >= 256) {
+        if (state_big_tiles(p)) {
             if (p.L >= 256 && sb_cap >= 256) return launch_state_cfg<T, 256, 128, 128, 8>(p, k, v, fg, ws, stream);
             if (p.L >= 128 && sb_cap >= 128) return launch_state_cfg<T, 128, 128, 128, 8>(p, k, v, fg, ws, stream);
             return launch_state_cfg<T, 64, 128, 128, 8>(p, k, v, fg, ws, stream);
@@ -290,6 +399,48 @@ hipError_t launch_state_t(const Problem& p, const T* k, const T* v, const float*
 }
 
 }  // namespace
+
+// 128x128 tiles halve the LDS bytes per flop and the L2 re-reads of k and v;
+// they are used (bf16 I/O only: fp32 blocks would not fit LDS) when they give
+// every CU a workgroup -- counting the segments of a segmented walk -- else
+// 64x64 tiles.  The big tiles run 8 waves over blocks of up to 256 steps.
+bool state_big_tiles(const Problem& p)
+{
+    if (!p.bf16 || p.dhv % 128 != 0 || p.dqk % 128 != 0) return false;
+    const long heads_tiles = (long)p.B * p.H * (p.dhv / 128) * (p.dqk / 128);
+    return heads_tiles >= 256 || state_segments_for(p, heads_tiles) > 1;
+}
+
+// Segments of the chunk chain: enough workgroups for about two per CU of
+// a 256-CU device (512), each segment at least two chunks long; 1 when the
+// heads and tiles alone fill the device.  TFLA_STATE_SEGMENTS=n overrides
+// (tuning).
+int state_segments_for(const Problem& p, long heads_tiles)
+{
+    const int nfeed = p.nc - 1;   // chunks that feed a stored state
+    if (nfeed < 4) return 1;
+    long P = 1;
+    if (const char* e = std::getenv("TFLA_STATE_SEGMENTS")) P = std::atol(e);
+    else if (heads_tiles < 256) P = (512 + heads_tiles - 1) / heads_tiles;
+    P = std::min<long>(P, nfeed / 2);
+    if (P < 2) return 1;
+    const int cps = (int)((nfeed + P - 1) / P);
+    return (nfeed + cps - 1) / cps;   // no empty segment
+}
+
+int state_segments(const Problem& p)
+{
+    const bool big128 = p.bf16 && p.dhv % 128 == 0 && p.dqk % 128 == 0;
+    long tiles128 = (long)p.B * p.H * (p.dhv / 128) * (p.dqk / 128);
+    if (big128 && (tiles128 >= 256 || state_segments_for(p, tiles128) > 1)) return state_segments_for(p, tiles128);
+    return state_segments_for(p, (long)p.B * p.H * (p.dhv / 64) * (p.dqk / 64));
+}
+
+int state_chunks_per_segment(const Problem& p, int P)
+{
+    const int nfeed = p.nc - 1;
+    return (nfeed + P - 1) / P;
+}
 
 hipError_t launch_state(const Problem& p, const void* k, const void* v, const float* fgate_pre,
                         const Workspace& ws, hipStream_t stream)

@@ -194,6 +194,9 @@ size_t workspace_layout(const Problem& p, Workspace* ws, char* base, bool with_s
     ws->g = p.gate == kScalar ? nullptr : take(bh * p.nc * w * 4);
     const size_t slots = p.nc - 1 + (with_c0 ? 1 : 0);
     ws->states = (with_states && slots > 0) ? take(bh * slots * p.dhv * p.dqk * 4) : nullptr;
+    const int P = state_segments(p);
+    ws->seg_end = P > 1 ? take(bh * P * p.dhv * p.dqk * 4) : nullptr;
+    ws->seg_start = P > 1 ? take(bh * P * p.dhv * p.dqk * 4) : nullptr;
     return off;
 }
 

@@ -82,7 +82,8 @@ def test_workspace_bytes(L):
     def a256(x):
         return (x + 255) // 256 * 256
 
-    B, H, T, dqk, dhv, Lc = 2, 3, 300, 128, 256, 64
+    # T = 250, L = 64: four chunks, too few to split the state walk into segments
+    B, H, T, dqk, dhv, Lc = 2, 3, 250, 128, 256, 64
     nc = -(-T // Lc)
     sig = a256(B * H * T * 4) * 2 + a256(B * H * nc * 4) + a256(B * H * (nc - 1) * dhv * dqk * 4)
     assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16) == sig
@@ -92,6 +93,19 @@ def test_workspace_bytes(L):
     assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, GLA | BF16) == gla
     assert tfla.tfla_workspace_bytes(B, H, 64, dqk, dhv, Lc, SCALAR | BF16) == 0   # one chunk, no state
     assert tfla.tfla_workspace_bytes(B, H, T, 96, dhv, Lc, SIG) == 0
+
+
+def test_segmented_state_walk_workspace(L):
+    """A long chunk chain over few heads splits the state walk into P >= 2
+    segments, whose start and end states ([B*H, P, d_qk, d_hv] fp32 each)
+    join the workspace."""
+    B, H, dqk, dhv, Lc = 1, 2, 128, 128, 64
+    base = tfla.tfla_workspace_bytes(B, H, 250, dqk, dhv, Lc, SIG | BF16)        # 4 chunks: no segments
+    T = 64 * 40
+    nc = 40
+    plain = (T * 4 * 2 + 256) + (nc * 4 + 256) + (nc - 1) * dhv * dqk * 4 * B * H
+    seg = tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16)
+    assert base > 0 and seg >= plain + 2 * B * H * 2 * dqk * dhv * 4
 
 
 def test_fwd_ws_checks_workspace(L):
@@ -143,7 +157,7 @@ def test_state_workspace_bytes(L):
     def a256(x):
         return (x + 255) // 256 * 256
 
-    B, H, T, dqk, dhv, Lc = 2, 3, 300, 128, 256, 64
+    B, H, T, dqk, dhv, Lc = 2, 3, 250, 128, 256, 64   # four chunks: no segmented state walk
     nc = -(-T // Lc)
     base = tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16)
     sig = a256(B * H * T * 4) * 2 + a256(B * H * nc * 4) + a256(B * H * nc * dhv * dqk * 4)

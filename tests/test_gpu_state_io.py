@@ -195,3 +195,36 @@ def test_long_context_split_in_two():
     assert err <= TOL[BF]
     got_c = np.stack([st[b, hh].cpu().double().numpy() for b, hh in heads])[None]
     assert rel_err(got_c, c_ref) <= STOL[BF]
+
+
+# ---------------------------------------------------------------- segmented state walk
+@pytest.mark.parametrize("segments", ["1", "2", "3", "7"])
+@pytest.mark.parametrize("variant,dtype,B,H,T,dqk,dhv,L,with_c0", [
+    (SIG, BF, 1, 2, 1500, 128, 128, 64, True),     # 24 chunks, partial last chunk
+    (SIG, BF, 1, 1, 2048, 256, 512, 128, False),
+    (SCAL, BF, 2, 1, 1000, 128, 256, 64, True),
+    (GLA, BF, 1, 2, 900, 128, 128, 64, True),
+    (SIG, F32, 1, 2, 1111, 64, 128, 64, True),
+])
+def test_segmented_state_walk(monkeypatch, segments, variant, dtype, B, H, T, dqk, dhv, L, with_c0):
+    """The chunk chain cut into segments (end states from zero, a combine
+    pass, a second walk from the true start states) gives the oracle's
+    outputs, final state and chunk-boundary states."""
+    monkeypatch.setenv("TFLA_STATE_SEGMENTS", segments)
+    wl, inp = case(variant, B, H, T, dqk, dhv, dtype, seed=int(segments) * 100 + T)
+    c0 = W.initial_state(B, H, dqk, dhv, seed=int(segments), std=1.5) if with_c0 else None
+    print(f"segments {segments}: {variant} {dtype} B{B} H{H} T{T} {dqk}x{dhv} L{L} c0={with_c0}", flush=True)
+    h, cf = run_state(to_dev(inp), variant, L, c0=c0)
+    h_ref, c_ref = oracle_state(inp, variant, c0)
+    assert rel_err(h_f64(h), h_ref) <= TOL[dtype]
+    assert rel_err(cf.cpu().double().numpy(), c_ref) <= STOL[dtype]
+    if not with_c0:
+        _, st_ref = oracle.recurrent_fwd(W.as_f64(inp["q"]), W.as_f64(inp["k"]), W.as_f64(inp["v"]),
+                                         W.as_f64(inp["igate_pre"]), W.as_f64(inp["fgate_pre"]), variant, L=L)
+        nc = -(-T // L)
+        st = torch.full((B, H, nc - 1, dhv, dqk), float("nan"), device="cuda")
+        d = to_dev(inp)
+        tfla.tfla_dbg_states(d["k"], d["v"], d["igate_pre"], d["fgate_pre"], st, B, H, T, dqk, dhv, L,
+                             tfla.variant_of(GATE[variant], dtype))
+        torch.cuda.synchronize()
+        assert rel_err(st.cpu().double().numpy().swapaxes(-1, -2), st_ref[:, :, :nc - 1]) <= STOL[dtype]
