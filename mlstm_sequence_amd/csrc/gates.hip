@@ -58,22 +58,33 @@ __global__ __launch_bounds__(64) void gates_sig_kernel(const float* __restrict__
 }
 
 // Per-key-channel gate: one thread per (chunk, head, channel), serial over
-// the chunk's steps; consecutive threads read consecutive channels.
+// the chunk's steps; consecutive threads read consecutive channels.  The
+// loads of 16 steps are issued together (the running sum is the only serial
+// dependence), so the loop is not one memory latency per step.
 __global__ __launch_bounds__(256) void gates_gla_kernel(const float* __restrict__ x,
                                                         float* __restrict__ a, float* __restrict__ g,
                                                         int T, int dqk, int L, int nc)
 {
+    constexpr int U = 16;
     const int kc = blockIdx.x;
     const size_t bh = blockIdx.y;
     const int c = threadIdx.x;
     if (c >= dqk) return;
     const int t0 = kc * L;
     const int n = min(L, T - t0);
-    size_t idx = (bh * (size_t)T + t0) * dqk + c;
+    const size_t base = (bh * (size_t)T + t0) * dqk + c;
     float run = 0.0f;
-    for (int p = 0; p < n; ++p, idx += dqk) {
-        run += fmaxf(log_sigmoid(x[idx]) * (1.0f / 16.0f), kLogForgetFloor);
-        a[idx] = run;
+    for (int p0 = 0; p0 < n; p0 += U) {
+        float xv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) xv[u] = x[base + (size_t)min(p0 + u, n - 1) * dqk];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (p0 + u < n) {
+                run += fmaxf(log_sigmoid(xv[u]) * (1.0f / 16.0f), kLogForgetFloor);
+                a[base + (size_t)(p0 + u) * dqk] = run;
+            }
+        }
     }
     g[(bh * nc + kc) * dqk + c] = run;
 }
