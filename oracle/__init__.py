@@ -55,6 +55,8 @@ def _load():
         lib.oracle_fwd.restype = ctypes.c_int
         lib.oracle_fwd_state.argtypes = [dp] * 9 + [ctypes.c_int] * 7
         lib.oracle_fwd_state.restype = ctypes.c_int
+        lib.oracle_bwd.argtypes = [dp] * 11 + [ctypes.c_int] * 6
+        lib.oracle_bwd.restype = ctypes.c_int
         lib.oracle_log_gates.argtypes = [dp] * 5 + [ctypes.c_int] * 6
         lib.oracle_log_gates.restype = ctypes.c_int
         lib.oracle_threads.argtypes = []
@@ -122,6 +124,23 @@ def recurrent_fwd_state(q, k, v, igate_pre, fgate_pre, kind, c0=None):
     if rc != 0:
         raise ValueError("oracle_fwd_state rejected its arguments")
     return h, cT
+
+
+def recurrent_bwd(q, k, v, igate_pre, fgate_pre, dh, kind):
+    """Reverse-mode derivative of the recurrence for the upstream gradient
+    dh [B,H,T,dhv].  Returns (dq, dk, dv, dig, dfg): dig like igate_pre
+    (None unless mLSTMsig), dfg like fgate_pre."""
+    q, k, v, ig, fg, dh = map(_f64, (q, k, v, igate_pre, fgate_pre, dh))
+    B, H, T, dqk = q.shape
+    dhv = v.shape[-1]
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    dig = np.empty_like(ig) if kind == MLSTM_SIG else None
+    dfg = np.empty_like(fg)
+    rc = _load().oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(ig), _ptr(fg), _ptr(dh), _ptr(dq), _ptr(dk), _ptr(dv),
+                            _ptr(dig), _ptr(dfg), B, H, T, dqk, dhv, kind)
+    if rc != 0:
+        raise ValueError("oracle_bwd rejected its arguments")
+    return dq, dk, dv, dig, dfg
 
 
 def log_gates(igate_pre, fgate_pre, kind, B, H, T, dqk, L):

@@ -206,6 +206,169 @@ int oracle_log_gates(const double* igate_pre, const double* fgate_pre,
     return 0;
 }
 
+/*
+ * Backward pass of the recurrence (reverse-mode derivative, in double).
+ * Given dh_t = dL/dh_t, returns dL/dq, dL/dk, dL/dv and the gradients of
+ * the gate pre-activations, straight from the recurrence (s = 1/sqrt(d_qk)):
+ *
+ *   dq_t      = s C_t dh_t
+ *   dC_t      = s q_t dh_t^T + diag(f_{t+1}) dC_{t+1}        (dC after the last step: 0)
+ *   dk_t      = i_t dC_t v_t          dv_t = i_t dC_t^T k_t      di_t = k_t^T dC_t v_t
+ *   df_{t,c}  = sum_j dC_t[c][j] C_{t-1}[c][j]
+ *
+ * and through the gate functions:
+ *   kind 0:  dL/digate_pre_t = di_t i_t (1 - i_t),
+ *            dL/dfgate_pre_t = (sum_c df_{t,c}) f_t (1 - f_t)
+ *   kind 1:  dL/dfgate_pre[h] = sum over b, t, c of df_{t,c} f_h (1 - f_h)
+ *   kind 2:  dL/dx_{t,c} = df_{t,c} f_{t,c} (1 - sigmoid(x_{t,c})) / 16
+ * where a floored log forget gate (below -100) passes no gradient.  C_0 = 0.
+ * The forward sweep yields C_t and dq_t; the reverse sweep recomputes the
+ * states of each 64-step block from a checkpoint taken in the forward sweep.
+ *
+ * Layouts as oracle_fwd; dh like h; dq, dk, dv like q, k, v; dig like
+ * igate_pre (kind 0; may be NULL otherwise); dfg like fgate_pre.
+ */
+static int forget_floored(int kind, const double* fgate_pre, size_t bh, int head, int T, int dqk, int t, int c)
+{
+    double x;
+    switch (kind) {
+    case KIND_MLSTM_SIG: x = log_sigmoid(fgate_pre[bh * (size_t)T + t]); break;
+    case KIND_SCALAR: x = log_sigmoid(fgate_pre[head]); break;
+    default: x = log_sigmoid(fgate_pre[(bh * (size_t)T + t) * dqk + c]) / 16.0; break;
+    }
+    return x < -100.0;
+}
+
+int oracle_bwd(const double* q, const double* k, const double* v,
+               const double* igate_pre, const double* fgate_pre, const double* dh,
+               double* dq, double* dk, double* dv, double* dig, double* dfg,
+               int B, int H, int T, int dqk, int dhv, int kind)
+{
+    if (!q || !k || !v || !fgate_pre || !dh || !dq || !dk || !dv || !dfg) return -1;
+    if (B < 0 || H < 0 || T < 0 || dqk < 1 || dhv < 1) return -1;
+    if (kind < KIND_MLSTM_SIG || kind > KIND_GLA) return -1;
+    if (kind == KIND_MLSTM_SIG && (!igate_pre || !dig)) return -1;
+    const long nbh = (long)B * H;
+    const double scale = 1.0 / sqrt((double)dqk);
+    const int BLK = 64;
+    const int nck = (T + BLK - 1) / BLK;
+    const size_t csz = (size_t)dqk * dhv;
+    double* dscal = (double*)calloc((size_t)(nbh > 0 ? nbh : 1), sizeof(double));   /* kind 1: per (b,h) */
+    if (!dscal) return -1;
+    int bad = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < nbh; ++bh) {
+        const int head = (int)(bh % H);
+        double* C = (double*)calloc(csz, sizeof(double));
+        double* dC = (double*)calloc(csz, sizeof(double));
+        double* ck = (double*)malloc((size_t)(nck > 0 ? nck : 1) * csz * sizeof(double));
+        double* Cb = (double*)malloc((size_t)BLK * csz * sizeof(double));
+        double* f = (double*)malloc((size_t)dqk * sizeof(double));
+        double* df = (double*)malloc((size_t)dqk * sizeof(double));
+        if (!C || !dC || !ck || !Cb || !f || !df) {
+            free(C); free(dC); free(ck); free(Cb); free(f); free(df);
+#pragma omp atomic write
+            bad = 1;
+            continue;
+        }
+        /* forward sweep: C_t, dq_t, and the state before every 64-step block */
+        for (int t = 0; t < T; ++t) {
+            if (t % BLK == 0) memcpy(ck + (size_t)(t / BLK) * csz, C, csz * sizeof(double));
+            const double* kt = k + ((size_t)bh * T + t) * dqk;
+            const double* vt = v + ((size_t)bh * T + t) * dhv;
+            const double it = input_gate(kind, igate_pre, (size_t)bh, T, t);
+            for (int c = 0; c < dqk; ++c) f[c] = forget_gate(kind, fgate_pre, (size_t)bh, head, T, dqk, t, c);
+            for (int c = 0; c < dqk; ++c)
+                for (int j = 0; j < dhv; ++j) C[(size_t)c * dhv + j] = f[c] * C[(size_t)c * dhv + j] + it * kt[c] * vt[j];
+            const double* dht = dh + ((size_t)bh * T + t) * dhv;
+            double* dqt = dq + ((size_t)bh * T + t) * dqk;
+            for (int c = 0; c < dqk; ++c) {
+                double acc = 0.0;
+                for (int j = 0; j < dhv; ++j) acc += C[(size_t)c * dhv + j] * dht[j];
+                dqt[c] = scale * acc;
+            }
+        }
+        /* reverse sweep, one block at a time */
+        for (int n = nck - 1; n >= 0; --n) {
+            const int t0 = n * BLK, t1 = t0 + BLK < T ? t0 + BLK : T;
+            /* states after steps t0..t1-1 of this block */
+            memcpy(C, ck + (size_t)n * csz, csz * sizeof(double));
+            for (int t = t0; t < t1; ++t) {
+                const double* kt = k + ((size_t)bh * T + t) * dqk;
+                const double* vt = v + ((size_t)bh * T + t) * dhv;
+                const double it = input_gate(kind, igate_pre, (size_t)bh, T, t);
+                for (int c = 0; c < dqk; ++c) f[c] = forget_gate(kind, fgate_pre, (size_t)bh, head, T, dqk, t, c);
+                for (int c = 0; c < dqk; ++c)
+                    for (int j = 0; j < dhv; ++j)
+                        C[(size_t)c * dhv + j] = f[c] * C[(size_t)c * dhv + j] + it * kt[c] * vt[j];
+                memcpy(Cb + (size_t)(t - t0) * csz, C, csz * sizeof(double));
+            }
+            for (int t = t1 - 1; t >= t0; --t) {
+                const double* qt = q + ((size_t)bh * T + t) * dqk;
+                const double* kt = k + ((size_t)bh * T + t) * dqk;
+                const double* vt = v + ((size_t)bh * T + t) * dhv;
+                const double* dht = dh + ((size_t)bh * T + t) * dhv;
+                /* dC_t = diag(f_{t+1}) dC_{t+1} + s q_t dh_t^T */
+                if (t + 1 < T)
+                    for (int c = 0; c < dqk; ++c) f[c] = forget_gate(kind, fgate_pre, (size_t)bh, head, T, dqk, t + 1, c);
+                for (int c = 0; c < dqk; ++c)
+                    for (int j = 0; j < dhv; ++j) {
+                        double* e = &dC[(size_t)c * dhv + j];
+                        *e = (t + 1 < T ? f[c] * *e : 0.0) + scale * qt[c] * dht[j];
+                    }
+                const double it = input_gate(kind, igate_pre, (size_t)bh, T, t);
+                double* dkt = dk + ((size_t)bh * T + t) * dqk;
+                double* dvt = dv + ((size_t)bh * T + t) * dhv;
+                double di = 0.0;
+                for (int c = 0; c < dqk; ++c) {
+                    double acc = 0.0;
+                    for (int j = 0; j < dhv; ++j) acc += dC[(size_t)c * dhv + j] * vt[j];
+                    dkt[c] = it * acc;
+                    di += kt[c] * acc;
+                }
+                for (int j = 0; j < dhv; ++j) {
+                    double acc = 0.0;
+                    for (int c = 0; c < dqk; ++c) acc += dC[(size_t)c * dhv + j] * kt[c];
+                    dvt[j] = it * acc;
+                }
+                /* df_{t,c} against the state before step t */
+                const double* Cprev = t > t0 ? Cb + (size_t)(t - t0 - 1) * csz : ck + (size_t)n * csz;
+                for (int c = 0; c < dqk; ++c) {
+                    double acc = 0.0;
+                    for (int j = 0; j < dhv; ++j) acc += dC[(size_t)c * dhv + j] * Cprev[(size_t)c * dhv + j];
+                    df[c] = acc;
+                }
+                for (int c = 0; c < dqk; ++c) f[c] = forget_gate(kind, fgate_pre, (size_t)bh, head, T, dqk, t, c);
+                if (kind == KIND_MLSTM_SIG) {
+                    dig[(size_t)bh * T + t] = di * it * (1.0 - it);
+                    double sdf = 0.0;
+                    for (int c = 0; c < dqk; ++c) sdf += df[c];
+                    dfg[(size_t)bh * T + t] =
+                        forget_floored(kind, fgate_pre, (size_t)bh, head, T, dqk, t, 0) ? 0.0 : sdf * f[0] * (1.0 - f[0]);
+                } else if (kind == KIND_SCALAR) {
+                    if (!forget_floored(kind, fgate_pre, (size_t)bh, head, T, dqk, t, 0))
+                        for (int c = 0; c < dqk; ++c) dscal[bh] += df[c] * f[c] * (1.0 - f[c]);
+                } else {
+                    for (int c = 0; c < dqk; ++c) {
+                        const double x = fgate_pre[((size_t)bh * T + t) * dqk + c];
+                        dfg[((size_t)bh * T + t) * dqk + c] =
+                            forget_floored(kind, fgate_pre, (size_t)bh, head, T, dqk, t, c)
+                                ? 0.0 : df[c] * f[c] * (1.0 - sigmoid(x)) / 16.0;
+                    }
+                }
+            }
+        }
+        free(C); free(dC); free(ck); free(Cb); free(f); free(df);
+    }
+    if (kind == KIND_SCALAR) {
+        for (int hh = 0; hh < H; ++hh) dfg[hh] = 0.0;
+        for (long bh = 0; bh < nbh; ++bh) dfg[bh % H] += dscal[bh];
+    }
+    free(dscal);
+    return bad ? -1 : 0;
+}
+
 /* the scalar gate functions, exported so tests can pin them */
 double oracle_sigmoid(double x) { return sigmoid(x); }
 double oracle_log_sigmoid(double x) { return log_sigmoid(x); }

@@ -289,3 +289,106 @@ def test_initial_state_closed_form():
     extra = F[..., None] * np.einsum("bhtc,bhcj->bhtj", q, c0) / math.sqrt(dqk)
     assert rel_err(h1, h0 + extra) <= REL
     assert rel_err(cT1, cT0 + F[:, :, -1, None, None] * c0) <= REL
+
+
+# ---------------------------------------------------------------- backward pass
+def _all_inputs(kind, B, H, T, dqk, dhv, seed):
+    q, k, v, ig, fg = rand_case(kind, B, H, T, dqk, dhv, seed=seed)
+    dh = np.random.default_rng(seed + 1).standard_normal((B, H, T, dhv))
+    return q, k, v, ig, fg, dh
+
+
+@pytest.mark.parametrize("kind", [MLSTM_SIG, SCALAR, GLA])
+def test_backward_matches_finite_differences(kind):
+    """Every gradient of L = sum(dh * h) against central differences of the
+    forward recurrence, element by element."""
+    B, H, T, dqk, dhv = 1, 2, 6, 3, 2
+    q, k, v, ig, fg, dh = _all_inputs(kind, B, H, T, dqk, dhv, seed=40 + kind)
+    grads = oracle.recurrent_bwd(q, k, v, ig, fg, dh, kind)
+    names = ["q", "k", "v", "ig", "fg"]
+    arrs = {"q": q, "k": k, "v": v, "ig": ig, "fg": fg}
+
+    def loss(a):
+        return float(np.sum(dh * oracle.recurrent_fwd(a["q"], a["k"], a["v"], a["ig"], a["fg"], kind)))
+
+    eps = 1e-6
+    for name, g in zip(names, [grads[0], grads[1], grads[2], grads[3], grads[4]]):
+        if arrs[name] is None:
+            assert g is None
+            continue
+        num = np.empty_like(arrs[name])
+        for idx in np.ndindex(arrs[name].shape):
+            plus = {n: (a.copy() if a is not None else None) for n, a in arrs.items()}
+            minus = {n: (a.copy() if a is not None else None) for n, a in arrs.items()}
+            plus[name][idx] += eps
+            minus[name][idx] -= eps
+            num[idx] = (loss(plus) - loss(minus)) / (2 * eps)
+        assert rel_err(g, num) <= 1e-6, name
+
+
+def _closed_form_torch(q, k, v, ig, fg, kind):
+    """The quadratic closed form in float64 torch ops (cumulative log forget
+    gates, explicit decay matrix), differentiated by autograd."""
+    import torch
+    B, H, T, dqk = q.shape
+    if kind == MLSTM_SIG:
+        lf = torch.clamp(torch.nn.functional.logsigmoid(fg), min=-100.0)        # [B,H,T]
+        li = torch.nn.functional.logsigmoid(ig)
+        cum = torch.cumsum(lf, dim=-1)
+        logd = cum[..., :, None] - cum[..., None, :] + li[..., None, :]          # [B,H,t,s]
+        s = q @ k.transpose(-1, -2)
+    elif kind == SCALAR:
+        lf = torch.clamp(torch.nn.functional.logsigmoid(fg), min=-100.0)        # [H]
+        t = torch.arange(T, dtype=torch.float64)
+        logd = (t[:, None] - t[None, :])[None, None] * lf[None, :, None, None]
+        s = q @ k.transpose(-1, -2)
+    else:
+        lf = torch.clamp(torch.nn.functional.logsigmoid(fg) / 16.0, min=-100.0)  # [B,H,T,c]
+        cum = torch.cumsum(lf, dim=2)
+        # per channel decay inside q.k; mask before exponentiating (no inf * 0)
+        diff = cum[:, :, :, None, :] - cum[:, :, None, :, :]                     # [B,H,t,s,c]
+        mask = torch.tril(torch.ones(T, T, dtype=torch.bool))[None, None, :, :, None]
+        diff = torch.where(mask, diff, torch.full_like(diff, -1e9))
+        s = torch.einsum("bhtc,bhsc,bhtsc->bhts", q, k, torch.exp(diff))
+        logd = torch.zeros_like(s)
+    causal = torch.tril(torch.ones(T, T, dtype=torch.bool))
+    logd = torch.where(causal, logd, torch.full_like(logd, -1e9))
+    return (s * torch.exp(logd)) @ v / math.sqrt(dqk)
+
+
+@pytest.mark.parametrize("kind", [MLSTM_SIG, SCALAR, GLA])
+def test_backward_matches_autograd_of_closed_form(kind):
+    import torch
+    B, H, T, dqk, dhv = 2, 2, 21, 4, 5
+    q, k, v, ig, fg, dh = _all_inputs(kind, B, H, T, dqk, dhv, seed=50 + kind)
+    tt = {n: (None if a is None else torch.tensor(a, dtype=torch.float64, requires_grad=True))
+          for n, a in zip(["q", "k", "v", "ig", "fg"], [q, k, v, ig, fg])}
+    h = _closed_form_torch(tt["q"], tt["k"], tt["v"], tt["ig"], tt["fg"], kind)
+    (h * torch.tensor(dh)).sum().backward()
+    got = oracle.recurrent_bwd(q, k, v, ig, fg, dh, kind)
+    for name, g in zip(["q", "k", "v", "ig", "fg"], got):
+        if tt[name] is None:
+            continue
+        assert rel_err(g, tt[name].grad.numpy()) <= 1e-10, name
+
+
+@pytest.mark.parametrize("kind", [MLSTM_SIG, GLA])
+def test_forget_gradient_is_reverse_sum_of_q_dq_minus_k_dk(kind):
+    """dL/dlog f_t = sum over t' >= t of (q_t' . dq_t' - k_t' . dk_t'),
+    per key channel for the per-channel gate (the form the GPU backward
+    evaluates), against the oracle's direct df."""
+    B, H, T, dqk, dhv = 2, 1, 40, 6, 3
+    q, k, v, ig, fg, dh = _all_inputs(kind, B, H, T, dqk, dhv, seed=60 + kind)
+    dq, dk, dv, dig, dfg = oracle.recurrent_bwd(q, k, v, ig, fg, dh, kind)
+    if kind == MLSTM_SIG:
+        r = np.sum(q * dq - k * dk, axis=-1)                      # [B,H,T]
+        dlogf = np.flip(np.cumsum(np.flip(r, -1), -1), -1)
+        f = 1.0 / (1.0 + np.exp(-fg))
+        assert rel_err(dlogf * (1.0 - f), dfg) <= 1e-10
+        i = 1.0 / (1.0 + np.exp(-ig))
+        assert rel_err(np.sum(k * dk, axis=-1) * (1.0 - i), dig) <= 1e-10
+    else:
+        r = q * dq - k * dk                                        # [B,H,T,c]
+        dlogf = np.flip(np.cumsum(np.flip(r, 2), 2), 2)
+        sx = 1.0 / (1.0 + np.exp(-fg))
+        assert rel_err(dlogf * (1.0 - sx) / 16.0, dfg) <= 1e-10
