@@ -161,6 +161,53 @@ int tfla_fwd_recurrent(const void* q, const void* k, const void* v,
                        int B, int H, int T, int d_qk, int d_hv, int variant, void* stream);
 
 /*
+ * tfla_bwd -- the backward pass: given dh = dL/dh for the forward pass of
+ * tfla_fwd (C_0 = 0), the gradients of L with respect to every input.  The
+ * pages list forward-and-backward timings for each computation form (the
+ * "fwdbwd" columns of the flash-linear-attention README's timing table) and
+ * TFLA's training kernels; this is the chunkwise form of the same
+ * recurrence run backwards:
+ *
+ *     dC_t = q_t dh_t^T / sqrt(d_qk) + diag(f_{t+1}) dC_{t+1},   dC_T from dh_T only
+ *     dq_t = C_t dh_t / sqrt(d_qk),   dk_t = i_t dC_t v_t,   dv_t = i_t dC_t^T k_t
+ *     dL/dlog i_t = k_t . dk_t,       dL/dlog f_t = sum_{t'>=t} (q_t'.dq_t' - k_t'.dk_t')
+ *
+ * and the gate pre-activations through their sigmoids (a log forget gate at
+ * its floor of -100 passes no gradient).  The states C_k are recomputed
+ * (nothing is kept from the forward call); the gradient into the state at
+ * each chunk boundary is walked backwards over the chunks and materialised
+ * in fp32 like C_k; dq, dk and dv are intra-chunk matrix-core products over
+ * 64-step tiles as in the forward pass.
+ *
+ *   q, k, v, igate_pre, fgate_pre: as for tfla_fwd.
+ *   dh        [B,H,T,d_hv], the element type of q.
+ *   dq, dk    [B,H,T,d_qk] outputs, the element type of q.
+ *   dv        [B,H,T,d_hv] output, the element type of q.
+ *   dig       fp32 [B,H,T] output for TFLA_MLSTM_SIG; NULL otherwise.
+ *   dfg       fp32 output shaped like fgate_pre: [B,H,T] (TFLA_MLSTM_SIG),
+ *             [H] (TFLA_SCALAR_DECAY: summed over batches and steps).
+ *   Outputs are fully overwritten and must not overlap each other or an
+ *   input.
+ *   variant   TFLA_MLSTM_SIG or TFLA_SCALAR_DECAY (| TFLA_IO_BF16);
+ *             TFLA_GLA_KEY returns TFLA_ERR_UNSUPPORTED.
+ *   d_qk      as for tfla_fwd; d_hv 64, 128, 256 or 512 (fp32 I/O: 64 or
+ *             128), since the dq and dk products contract over it.
+ *   workspace caller-owned device workspace of at least
+ *             tfla_bwd_workspace_bytes(...) bytes, 256-byte aligned, or NULL
+ *             to let the call allocate it stream-ordered (hipMallocAsync /
+ *             hipFreeAsync on `stream`).
+ */
+int tfla_bwd(const void* q, const void* k, const void* v,
+             const float* igate_pre, const float* fgate_pre, const void* dh,
+             void* dq, void* dk, void* dv, float* dig, float* dfg,
+             int B, int H, int T, int d_qk, int d_hv, int L, int variant,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace tfla_bwd needs; 0 when the arguments are
+ * invalid or unsupported. */
+size_t tfla_bwd_workspace_bytes(int B, int H, int T, int d_qk, int d_hv, int L, int variant);
+
+/*
  * Test hooks: run part of the path and copy its intermediate out.
  *
  * tfla_dbg_gates -- the gate prefix-sum kernel alone.  Outputs (device, fp32):

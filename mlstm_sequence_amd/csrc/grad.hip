@@ -1,0 +1,199 @@
+// grad.hip -- the gate work of the backward pass.
+//
+// Gradients of the loss L through h_t = C_t^T q_t / sqrt(d_qk) with
+// C_t = f_t C_{t-1} + i_t k_t v_t^T (the recurrence of the mLSTMsig and
+// scalar-decay variants).  The matrix products (dq, dk, dv) run in the
+// intra-chunk kernel's gradient modes; this file holds what is left:
+//
+//   mirrored gates:  for chunk rows visited in reverse (logical row cs + r
+//                    is step p = cs + len - 1 - r), the query-side exponent
+//                    a'_t = g - a_p + li_p and the key-side exponent
+//                    li'_t - a'_t = a_p - g (stored pre-combined, so an input
+//                    gate of 0 never meets -inf - -inf).
+//   gate gradients:  log f_t enters every state from C_t on, and a direct
+//                    calculation gives
+//                       dL/dlog f_t = sum_{t' >= t} (q_t' . dq_t' - k_t' . dk_t'),
+//                       dL/dlog i_t = k_t . dk_t.
+//                    r_t = q_t.dq_t - k_t.dk_t and k_t.dk_t come from the dq
+//                    and dk kernels' fp32 row partials (one per value tile).
+//                    The suffix sum is split at the chunk end: the part of it
+//                    past chunk k's last step equals the coupling carried
+//                    across that boundary,
+//                       X_k = <D_k, C_k> / sqrt(d_qk)   (X_{nc-1} = 0),
+//                    the Frobenius product of the two fp32 states the path
+//                    materialises (every pair s <= end of chunk k < t
+//                    contributes once to it), so
+//                       dL/dlog f_t = sum_{t <= t' in chunk k} r_t' + X_k
+//                    and no error accumulates over the sequence.  The fixed
+//                    per-head decay shares one log f over every step; with
+//                    sum_t r_t = 0 (scaling q by e^e and k by e^-e leaves h
+//                    unchanged) the same split gives
+//                       dL/dlog f = sum_t (t - cs_t - (L-1)/2) r_t + L sum_k X_k
+//                    summed over batches: chunk-centred weights of at most L/2
+//                    instead of weights up to T on two sums that nearly
+//                    cancel.  Through the sigmoids: dig = (k.dk)(1 - i),
+//                    dfg = dL/dlog f (1 - f), 0 where the log forget gate
+//                    sits at its floor.
+#include "gfx950.hpp"
+#include "kernels.hpp"
+
+namespace tfla {
+namespace {
+
+constexpr int kScanThreads = 256;
+
+__global__ __launch_bounds__(256) void gates_mirror_kernel(const float* __restrict__ a, const float* __restrict__ li,
+                                                          const float* __restrict__ g, float* __restrict__ ar,
+                                                          float* __restrict__ lr, int T_, int L, int nc)
+{
+    const size_t bh = blockIdx.y;
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= T_) return;
+    const int kc = t / L, cs = kc * L, len = min(L, T_ - cs);
+    const int p = 2 * cs + len - 1 - t;
+    const float gk = g[bh * nc + kc];
+    const float ap = a[bh * T_ + p];
+    ar[bh * T_ + t] = gk - ap + li[bh * T_ + p];
+    lr[bh * T_ + t] = ap - gk;
+}
+
+// r_t and k_t.dk_t from the per-tile partial dots of step t
+__device__ __forceinline__ void step_dots(const float* dq_dots, const float* dk_dots, size_t t, int np, double& r,
+                                          double& kd)
+{
+    double a = 0.0, b = 0.0;
+    for (int j = 0; j < np; ++j) {
+        a += dq_dots[t * np + j];
+        b += dk_dots[t * np + j];
+    }
+    r = a - b;
+    kd = b;
+}
+
+// X_k = scale <D_k, C_k>: one workgroup per (batch-head, boundary); both
+// states in the same layout, n = d_qk d_hv elements each.
+__global__ __launch_bounds__(256) void state_dot_kernel(const float* __restrict__ C, const float* __restrict__ D,
+                                                       float* __restrict__ X, int n, float scale)
+{
+    __shared__ double part[256];
+    const size_t base = (size_t)blockIdx.x * n;
+    const f32x4* c4 = reinterpret_cast<const f32x4*>(C + base);
+    const f32x4* d4 = reinterpret_cast<const f32x4*>(D + base);
+    float s = 0.0f;
+    for (int i = threadIdx.x; i < n / 4; i += 256) {
+        const f32x4 a = c4[i], b = d4[i];
+        s += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
+    }
+    part[threadIdx.x] = s;
+    __syncthreads();
+    for (int d = 128; d >= 1; d >>= 1) {
+        if (threadIdx.x < d) part[threadIdx.x] += part[threadIdx.x + d];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) X[blockIdx.x] = (float)(part[0] * scale);
+}
+
+// mLSTMsig: one workgroup per (batch-head, chunk); thread i owns steps
+// [cs + i n, cs + (i+1) n) of the chunk.  Sums are kept in double.
+__global__ __launch_bounds__(kScanThreads) void grad_scan_sig_kernel(const float* __restrict__ dq_dots,
+                                                                    const float* __restrict__ dk_dots, int np,
+                                                                    const float* __restrict__ X,
+                                                                    const float* __restrict__ ig,
+                                                                    const float* __restrict__ fg,
+                                                                    float* __restrict__ dig, float* __restrict__ dfg,
+                                                                    int T_, int L, int nc)
+{
+    __shared__ double part[2][kScanThreads];
+    const int kc = blockIdx.x % nc;
+    const size_t bh = blockIdx.x / nc;
+    const size_t base = bh * T_;
+    const int cs = kc * L, ce = min(cs + L, T_);
+    const int tid = threadIdx.x;
+    const int n = (L + kScanThreads - 1) / kScanThreads;
+    const int t0 = min(cs + tid * n, ce), t1 = min(t0 + n, ce);
+    double s = 0.0, r, kd;
+    for (int t = t0; t < t1; ++t) {
+        step_dots(dq_dots, dk_dots, base + t, np, r, kd);
+        s += r;
+    }
+    // suffix sums over the threads after this one (Hillis-Steele, reversed)
+    int cur = 0;
+    part[cur][tid] = s;
+    __syncthreads();
+    for (int d = 1; d < kScanThreads; d <<= 1) {
+        const double x = part[cur][tid] + (tid + d < kScanThreads ? part[cur][tid + d] : 0.0);
+        part[cur ^ 1][tid] = x;
+        cur ^= 1;
+        __syncthreads();
+    }
+    // sum over the steps of the chunk after t1, plus the coupling past it
+    double acc = part[cur][tid] - s + (kc < nc - 1 ? (double)X[bh * (nc - 1) + kc] : 0.0);
+    for (int t = t1 - 1; t >= t0; --t) {
+        step_dots(dq_dots, dk_dots, base + t, np, r, kd);
+        acc += r;
+        const float x = fg[base + t];
+        const bool floored = log_sigmoid(x) < kLogForgetFloor;
+        dfg[base + t] = floored ? 0.0f : (float)(acc / (1.0 + exp((double)x)));
+        dig[base + t] = (float)(kd / (1.0 + exp((double)ig[base + t])));
+    }
+}
+
+// Fixed per-head decay: one workgroup per head, over every batch.
+__global__ __launch_bounds__(kScanThreads) void grad_scalar_kernel(const float* __restrict__ dq_dots,
+                                                                  const float* __restrict__ dk_dots, int np,
+                                                                  const float* __restrict__ X,
+                                                                  const float* __restrict__ fg,
+                                                                  float* __restrict__ dfg, int B, int H, int T_,
+                                                                  int L, int nc)
+{
+    __shared__ double part[kScanThreads];
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const double centre = 0.5 * (L - 1);
+    double s = 0.0, r, kd;
+    for (int b = 0; b < B; ++b) {
+        const size_t bh = (size_t)b * H + h;
+        for (int t = tid; t < T_; t += kScanThreads) {
+            step_dots(dq_dots, dk_dots, bh * T_ + t, np, r, kd);
+            s += ((double)(t % L) - centre) * r;
+        }
+        for (int k = tid; k < nc - 1; k += kScanThreads) s += (double)L * X[bh * (nc - 1) + k];
+    }
+    part[tid] = s;
+    __syncthreads();
+    for (int d = kScanThreads / 2; d >= 1; d >>= 1) {
+        if (tid < d) part[tid] += part[tid + d];
+        __syncthreads();
+    }
+    if (tid == 0) {
+        const float x = fg[h];
+        const bool floored = log_sigmoid(x) < kLogForgetFloor;
+        dfg[h] = floored ? 0.0f : (float)(part[0] / (1.0 + exp((double)x)));
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gates_mirror(const Problem& p, const Workspace& ws, float* ar, float* lr, hipStream_t stream)
+{
+    const dim3 grid((unsigned)((p.T + 255) / 256), (unsigned)(p.B * p.H));
+    gates_mirror_kernel<<<grid, 256, 0, stream>>>(ws.a, ws.li, ws.g, ar, lr, p.T, p.L, p.nc);
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_grads(const Problem& p, const float* states, const float* dstates, float* X,
+                             const float* dq_dots, const float* dk_dots, int np, const float* igate_pre,
+                             const float* fgate_pre, float* dig, float* dfg, hipStream_t stream)
+{
+    if (p.nc > 1)
+        state_dot_kernel<<<p.B * p.H * (p.nc - 1), 256, 0, stream>>>(states, dstates, X, p.dqk * p.dhv,
+                                                                     1.0f / sqrtf((float)p.dqk));
+    if (p.gate == kSig)
+        grad_scan_sig_kernel<<<p.B * p.H * p.nc, kScanThreads, 0, stream>>>(dq_dots, dk_dots, np, X, igate_pre,
+                                                                            fgate_pre, dig, dfg, p.T, p.L, p.nc);
+    else
+        grad_scalar_kernel<<<p.H, kScanThreads, 0, stream>>>(dq_dots, dk_dots, np, X, fgate_pre, dfg, p.B, p.H,
+                                                             p.T, p.L, p.nc);
+    return hipGetLastError();
+}
+
+}  // namespace tfla

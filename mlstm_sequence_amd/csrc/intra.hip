@@ -1,420 +1,14 @@
-// intra.hip -- intra-chunk kernel (third kernel of the path).
-//
-// For step t of chunk k (steps [cs, cs+L)):
-//   h_t = scale * ( e^{a_t} q_t^T C_{k-1}           (C_{-1}: the initial state, or 0)
-//                   + sum_{cs <= s <= t} e^{a_t - a_s + li_s} (q_t . k_s) v_s )
-// (GLA gate: the decay enters per key channel inside q.k, and the inter term
-// is (q_t o e^{a_t}) C_{k-1}).  TFLA's second level of sequence parallelism
-// (TFLA abstract; research-map summary, Approach) tiles this along the
-// sequence: a workgroup owns BQ query steps x BV value columns of one chunk
-// and loops over the 64-step key/value tiles up to its own rows, so the
-// chunk size L is bounded by nothing on chip.
-//
-// Workgroup = NW wavefronts (2, 4 or 8), wave w owning query rows
-// 32w..32w+31 (BQ = 32 NW, at most the chunk size);
-// all products are 32x32x16 matrix-core tiles:
-//   inter: acc = Q C_{k-1}[:, v-tile]; C^T is staged in LDS per CW-channel
-//          block (fp32 -> operand type, RNE); Q fragments stay in registers
-//          (A operand here, B operand of S^T below); rows scaled by e^{a_t}.
-//   intra: per key tile j: K_j and V_j staged row-major in LDS; per 32-step
-//          half: S^T = K Q^T, decay and causal mask in fp32 (a select, never
-//          a multiply by 0), and the S^T accumulators reused in place as the A
-//          operand of acc += P V_j -- the step index is contracted in the
-//          order the accumulator holds it, and V_j is read in that order with
-//          LDS transpose reads.  Halves entirely above the diagonal are
-//          skipped per wave.
-//   out:   h = acc * scale, rounded to the I/O type.
-// Every stage (a block of C^T, a K/V tile) is software-pipelined: its global
-// loads are issued into registers right after the previous stage reached
-// LDS, with consecutive lanes on consecutive 16-byte pieces of a row.
-// Per-channel gates use a reference-point factorisation: tiles wholly before
-// the query tile scale q by e^{a_t - a_ref} and k by e^{a_ref - a_s} with
-// a_ref at the step before the query tile (both factors <= 1); tiles that
-// overlap it use the tile's middle step.
-#include <cstdlib>
-
-#include "gfx950.hpp"
-#include "kernels.hpp"
+// intra.hip -- the intra-chunk kernel of the forward pass.
+#include "intra_impl.hpp"
 
 namespace tfla {
-namespace {
-
-template <typename T, int DQK, int BV, int CW> struct IntraLds {
-    static constexpr int kpad = 16 / sizeof(T);   // K / C^T rows: stride = 4 banks mod 32
-    static constexpr int vpad = 32 / sizeof(T);   // V rows: stride = 8 banks mod 32 (transpose reads)
-    union {
-        struct {
-            T ks[64][DQK + kpad];   // K tile [step][channel]
-            T vs[64][BV + vpad];    // V tile [step][value]
-        } kv;
-        T cs[BV][CW + kpad];        // CW-channel block of C^T [value][channel]
-    };
-    float bcol[64];                 // mLSTMsig: (li_s - a_s) log2(e) per key step
-};
-
-// One stage's global loads, held in registers while the previous stage
-// computes.  A C^T block and a K/V tile are never in flight together, so they
-// share the registers.
-template <typename T, int DQK, int BV, int CW, int NTH> struct Prefetch {
-    static constexpr int VEC = Elem<T>::vec;
-    static constexpr int NC = BV * CW / 8 / NTH;          // C^T block: 8 floats per item
-    static constexpr int NK = 64 * DQK / VEC / NTH;       // K tile: 16 bytes per item
-    static constexpr int NV = 64 * BV / VEC / NTH;        // V tile: 16 bytes per item
-    static_assert(NC >= 1 && NK >= 1 && NV >= 1, "tile too small for the workgroup");
-    union {
-        f32x4 c[NC][2];
-        struct {
-            Vec16<T> k[NK];
-            Vec16<T> v[NV];
-        } kv;
-    };
-    float li, a;
-};
-
-template <typename T, int GATE, int DQK, int BV, int NW>
-__global__ __launch_bounds__(64 * NW, NW >= 4 ? 2 : 1) void intra_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                                                           const T* __restrict__ v, const float* __restrict__ a,
-                                                           const float* __restrict__ li,
-                                                           const float* __restrict__ fg,
-                                                           const float* __restrict__ states,
-                                                           T* __restrict__ h, int H, int T_, int dhv, int L,
-                                                           int nc, int c0, float scale)
-{
-    constexpr int NTH = 64 * NW;
-    constexpr int BQ = 32 * NW;           // query rows per workgroup
-    // C^T channels per stage: 128 (two stages at d_qk = 256) when the
-    // registers allow, fewer for fp32 and two-wave workgroups
-    constexpr int CW = NW >= 4 ? ((sizeof(T) == 2 && DQK >= 128) ? 128 : 64) : 32;
-    constexpr int KQ = DQK / 16;          // 16-channel contraction steps
-    constexpr int NT = BV / 32;           // 32-wide output column tiles
-    constexpr int VEC = Elem<T>::vec;
-    typedef typename Elem<T>::frag Frag;
-    typedef IntraLds<T, DQK, BV, CW> Lds;
-    typedef Prefetch<T, DQK, BV, CW, NTH> PF;
-    __shared__ Lds sm;
-
-    const int nqt = (T_ + BQ - 1) / BQ;
-    const int nvt = dhv / BV;
-    const int blk = xcd_remap(blockIdx.x, gridDim.x);
-    const size_t bh = blk / (nqt * nvt);
-    const int rem = blk % (nqt * nvt);
-    const int qt = rem / nvt;
-    const int v0 = (rem % nvt) * BV;
-    const int t0 = qt * BQ;
-    const int kc = t0 / L, cs = kc * L;
-
-    const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63, hh = lane >> 5, i32 = lane & 31;
-    const int tq = t0 + 32 * w + i32;      // query step of this lane's fragment row
-    // Rows at or past T are read clamped to row T-1 (branch-free loads): a
-    // query row past the end only feeds its own output row, which is never
-    // stored, and a key/value row past the end only meets query rows before
-    // it through the causal select (P = 0, times finite data).
-    const int tqc = min(tq, T_ - 1);
-
-    const T* qb = q + bh * (size_t)T_ * DQK;
-    const T* kb = k + bh * (size_t)T_ * DQK;
-    const T* vb = v + bh * (size_t)T_ * dhv;
-    const float* ab = (GATE == kGla) ? a + bh * (size_t)T_ * DQK : a + bh * (size_t)T_;
-    const float* lb = (GATE == kSig) ? li + bh * (size_t)T_ : nullptr;
-    float lg2 = 0.0f;   // log2 of the fixed decay
-    if (GATE == kScalar) lg2 = fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor) * kLog2e;
-
-    PF pf;
-
-    // Q fragments (lane row tq, channels 16 kq + 8 hh ..); per-channel gate:
-    // q * e^{a_t - a_ref} (ref_row < 0: the chunk start, where a = 0)
-    Frag qf[KQ];
-    auto load_q = [&](int ref_row) {
-#pragma unroll
-        for (int kq = 0; kq < KQ; ++kq) {
-            const int c = 16 * kq + 8 * hh;
-            if (GATE != kGla) {
-                qf[kq] = load8(qb + (size_t)tqc * DQK + c);
-            } else {
-                const Frag raw = load8(qb + (size_t)tqc * DQK + c);
-                for (int e = 0; e < 8; ++e) {
-                    float ex = ab[(size_t)tqc * DQK + c + e];
-                    if (ref_row >= 0) ex -= ab[(size_t)ref_row * DQK + c + e];
-                    frag_set(qf[kq], e, frag_get(raw, e) * exp2_fast(ex * kLog2e));
-                }
-            }
-        }
-    };
-
-    // ---- stage loaders (global -> registers) and writers (registers -> LDS)
-    auto fetch_c = [&](const float* st, int cb) {
-#pragma unroll
-        for (int u = 0; u < PF::NC; ++u) {
-            const int idx = tid + NTH * u, vr = idx / (CW / 8), c8 = (idx % (CW / 8)) * 8;
-            const float* src = st + (size_t)vr * DQK + cb + c8;
-            pf.c[u][0] = *reinterpret_cast<const f32x4*>(src);
-            pf.c[u][1] = *reinterpret_cast<const f32x4*>(src + 4);
-        }
-    };
-    auto store_c = [&]() {
-#pragma unroll
-        for (int u = 0; u < PF::NC; ++u) {
-            const int idx = tid + NTH * u, vr = idx / (CW / 8), c8 = (idx % (CW / 8)) * 8;
-            if constexpr (sizeof(T) == 2) {
-                Vec16<T> x;
-                for (int e = 0; e < 4; ++e) {
-                    x.set(e, pf.c[u][0][e]);
-                    x.set(4 + e, pf.c[u][1][e]);
-                }
-                x.store(&sm.cs[vr][c8]);
-            } else {
-                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(&sm.cs[vr][c8])) = pf.c[u][0];
-                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(&sm.cs[vr][c8 + 4])) = pf.c[u][1];
-            }
-        }
-    };
-    auto fetch_kv = [&](int s0) {
-#pragma unroll
-        for (int u = 0; u < PF::NK; ++u) {
-            const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
-            const int s = min(s0 + r, T_ - 1);
-            pf.kv.k[u].load(kb + (size_t)s * DQK + c);
-        }
-#pragma unroll
-        for (int u = 0; u < PF::NV; ++u) {
-            const int idx = tid + NTH * u, r = idx / (BV / VEC), c = (idx % (BV / VEC)) * VEC;
-            const int s = min(s0 + r, T_ - 1);
-            pf.kv.v[u].load(vb + (size_t)s * dhv + v0 + c);
-        }
-        if (GATE == kSig && tid < 64) {
-            const int s = min(s0 + tid, T_ - 1);
-            pf.li = lb[s];
-            pf.a = ab[s];
-        }
-    };
-    auto store_kv = [&](int s0, int ref_row) {
-#pragma unroll
-        for (int u = 0; u < PF::NK; ++u) {
-            const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
-            if (GATE == kGla) {
-                const int s = min(s0 + r, T_ - 1);
-                for (int e = 0; e < VEC; ++e) {
-                    const float ex = ab[(size_t)ref_row * DQK + c + e] - ab[(size_t)s * DQK + c + e];
-                    pf.kv.k[u].set(e, pf.kv.k[u].get(e) * exp2_fast(ex * kLog2e));
-                }
-            }
-            pf.kv.k[u].store(&sm.kv.ks[r][c]);
-        }
-#pragma unroll
-        for (int u = 0; u < PF::NV; ++u) {
-            const int idx = tid + NTH * u, r = idx / (BV / VEC), c = (idx % (BV / VEC)) * VEC;
-            pf.kv.v[u].store(&sm.kv.vs[r][c]);
-        }
-        if (GATE == kSig && tid < 64) sm.bcol[tid] = (pf.li - pf.a) * kLog2e;
-    };
-
-    f32x16 acc[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-        for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
-
-    // ---------------- inter-chunk term: e^{a_t} q_t^T C_{k-1}
-    // states hold C before chunks 1..nc-1, preceded by C_0 when one is given (c0 = 1)
-    if (kc > 0 || c0) {
-        const float* st = states + ((bh * (nc - 1 + c0) + kc - 1 + c0) * (size_t)dhv + v0) * DQK;
-        fetch_c(st, 0);
-        load_q(-1);
-        for (int cb = 0; cb < DQK; cb += CW) {
-            __syncthreads();
-            store_c();
-            __syncthreads();
-            // the next stage's loads fly while this block is multiplied
-            if (cb + CW < DQK) fetch_c(st, cb + CW);
-            else fetch_kv(cs);
-#pragma unroll
-            for (int kk = 0; kk < CW / 16; ++kk) {
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const Frag bf = load8(&sm.cs[32 * nt + i32][16 * kk + 8 * hh]);
-                    acc[nt] = mma32(qf[cb / 16 + kk], bf, acc[nt]);
-                }
-            }
-        }
-        if (GATE != kGla) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int t = min(t0 + 32 * w + 8 * (r >> 2) + 4 * hh + (r & 3), T_ - 1);
-                const float e = (GATE == kSig) ? exp2_fast(ab[t] * kLog2e)
-                                               : exp2_fast((float)(t - cs + 1) * lg2);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= e;
-            }
-        }
-    } else {
-        fetch_kv(cs);
-    }
-
-    // ---------------- intra-chunk term, tiled along the chunk
-    if (GATE != kGla && kc == 0 && !c0) load_q(-1);
-    const float at2 = (GATE == kSig) ? ab[tqc] * kLog2e : 0.0f;
-    const int tlo = t0 + 32 * w;                  // first query row of this wave
-    const int nkv = (t0 - cs) / 64 + BQ / 64;     // key tiles up to the end of the query tile
-    int q_ref = -2;                               // reference row the Q fragments are scaled for
-
-    for (int j = 0; j < nkv; ++j) {
-        const int s0 = cs + 64 * j;
-        int ref_row = -1;
-        if (GATE == kGla) {
-            ref_row = (s0 + 63 < t0) ? t0 - 1 : min(s0 + 31, T_ - 1);
-            if (ref_row != q_ref) {
-                load_q(ref_row);
-                q_ref = ref_row;
-            }
-        }
-        __syncthreads();
-        store_kv(s0, ref_row);
-        __syncthreads();
-        if (j + 1 < nkv) fetch_kv(s0 + 64);
-
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int slo = s0 + 32 * mt;
-            if (slo > tlo + 31 || slo >= T_) continue;   // wholly above the diagonal, or past the end
-            const bool diag = slo == tlo;
-            // S^T (32 key steps x 32 query rows of this wave)
-            f32x16 st;
-            for (int r = 0; r < 16; ++r) st[r] = 0.0f;
-#pragma unroll
-            for (int kq = 0; kq < KQ; ++kq) {
-                const Frag af = load8(&sm.kv.ks[32 * mt + i32][16 * kq + 8 * hh]);
-                st = mma32(af, qf[kq], st);
-            }
-            // decay and causal mask: element r is key step slo + sr, query row tlo + i32
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int sr = 8 * (r >> 2) + 4 * hh + (r & 3);
-                float p = st[r];
-                if (GATE == kSig) {
-                    p *= exp2_fast(at2 + sm.bcol[32 * mt + sr]);
-                } else if (GATE == kScalar) {
-                    p *= exp2_fast((float)(tlo + i32 - slo - sr) * lg2);
-                }
-                st[r] = (diag && sr > i32) ? 0.0f : p;
-            }
-            // acc += P V: 16-step halves, in accumulator order
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                Frag pfr;
-                for (int e = 0; e < 8; ++e) frag_set(pfr, e, st[8 * half + e]);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const Frag vf = frag_tr(sm.kv.vs, 32 * mt + 16 * half, 32 * nt, lane);
-                    acc[nt] = mma32(pfr, vf, acc[nt]);
-                }
-            }
-        }
-    }
-
-    // ---------------- output
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int t = t0 + 32 * w + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (t >= T_) continue;
-        T* dst = h + (bh * (size_t)T_ + t) * dhv + v0 + i32;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) dst[32 * nt] = from_float<T>(acc[nt][r] * scale);
-    }
-}
-
-template <typename T, int GATE, int DQK, int BV, int NW>
-hipError_t launch_intra_t(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
-                          const Workspace& ws, void* h, hipStream_t stream)
-{
-    constexpr int BQ = 32 * NW;
-    const int nqt = (p.T + BQ - 1) / BQ;
-    const int blocks = p.B * p.H * nqt * (p.dhv / BV);
-    const float scale = 1.0f / sqrtf((float)DQK);
-    intra_kernel<T, GATE, DQK, BV, NW><<<blocks, 64 * NW, 0, stream>>>(
-        static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), ws.a, ws.li, fg,
-        ws.states, static_cast<T*>(h), p.H, p.T, p.dhv, p.L, p.nc, ws.c0 != nullptr, scale);
-    return hipGetLastError();
-}
-
-// Value-tile width: 128 when it divides d_hv (bf16 I/O), else 64 (fp32 I/O
-// always: its doubled fragments would not fit the register budget).
-// TFLA_INTRA_BV=64 forces 64 (tuning sweeps).
-inline int intra_bv(const Problem& p)
-{
-    if (const char* e = std::getenv("TFLA_INTRA_BV"))
-        if (std::atoi(e) == 64) return 64;
-    return (p.bf16 && p.dhv % 128 == 0) ? 128 : 64;
-}
-
-// Query rows per workgroup (32 per wave): as many as the chunk allows, up to
-// 256 (bf16) -- every staged C^T block and K/V tile then serves more rows.
-// TFLA_INTRA_ROWS=64|128|256 caps it (tuning sweeps).
-inline int intra_rows(const Problem& p)
-{
-    int cap = p.bf16 ? 256 : 128;
-    if (const char* e = std::getenv("TFLA_INTRA_ROWS")) {
-        const int want = std::atoi(e);
-        if (want == 64 || want == 128 || want == 256) cap = want < cap ? want : cap;
-    }
-    int rows = 64;
-    while (rows * 2 <= cap && p.L % (rows * 2) == 0) rows *= 2;
-    return rows;
-}
-
-template <typename T, int GATE, int DQK, int BV>
-hipError_t dispatch_nw(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
-                       const Workspace& ws, void* h, hipStream_t stream)
-{
-    // a workgroup's query rows never straddle a chunk
-    const int rows = intra_rows(p);
-    if constexpr (sizeof(T) == 2) {
-        if (rows == 256) return launch_intra_t<T, GATE, DQK, BV, 8>(p, q, k, v, fg, ws, h, stream);
-    }
-    if (rows >= 128) return launch_intra_t<T, GATE, DQK, BV, 4>(p, q, k, v, fg, ws, h, stream);
-    return launch_intra_t<T, GATE, DQK, BV, 2>(p, q, k, v, fg, ws, h, stream);
-}
-
-template <typename T, int GATE, int DQK>
-hipError_t dispatch_bv(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
-                       const Workspace& ws, void* h, hipStream_t stream)
-{
-    if constexpr (sizeof(T) == 2) {
-        if (intra_bv(p) == 128) return dispatch_nw<T, GATE, DQK, 128>(p, q, k, v, fg, ws, h, stream);
-    }
-    return dispatch_nw<T, GATE, DQK, 64>(p, q, k, v, fg, ws, h, stream);
-}
-
-template <typename T, int GATE>
-hipError_t dispatch_dqk(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
-                        const Workspace& ws, void* h, hipStream_t stream)
-{
-    switch (p.dqk) {
-    case 64: return dispatch_bv<T, GATE, 64>(p, q, k, v, fg, ws, h, stream);
-    case 128: return dispatch_bv<T, GATE, 128>(p, q, k, v, fg, ws, h, stream);
-    default:
-        if constexpr (sizeof(T) == 2) return dispatch_bv<T, GATE, 256>(p, q, k, v, fg, ws, h, stream);
-        return hipErrorInvalidValue;
-    }
-}
-
-template <typename T>
-hipError_t dispatch_gate(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
-                         const Workspace& ws, void* h, hipStream_t stream)
-{
-    switch (p.gate) {
-    case kSig: return dispatch_dqk<T, kSig>(p, q, k, v, fg, ws, h, stream);
-    case kScalar: return dispatch_dqk<T, kScalar>(p, q, k, v, fg, ws, h, stream);
-    default: return dispatch_dqk<T, kGla>(p, q, k, v, fg, ws, h, stream);
-    }
-}
-
-}  // namespace
 
 hipError_t launch_intra(const Problem& p, const void* q, const void* k, const void* v, const float* fgate_pre,
                         const Workspace& ws, void* h, hipStream_t stream)
 {
-    if (p.bf16) return dispatch_gate<bf16>(p, q, k, v, fgate_pre, ws, h, stream);
-    return dispatch_gate<float>(p, q, k, v, fgate_pre, ws, h, stream);
+    return dispatch_type<0>(p, q, k, v, fgate_pre, ws, h, 1.0f / sqrtf((float)p.dqk), stream);
 }
+
+int intra_value_tile(const Problem& p) { return intra_bv(p); }
 
 }  // namespace tfla

@@ -8,6 +8,9 @@ namespace tfla {
 
 enum GateKind { kSig = 0, kScalar = 1, kGla = 2 };
 
+// Operand modes of the intra-chunk kernel (bit set) for the gradient products.
+enum IntraMode { kNatState = 1, kMirror = 2, kRowDots = 4 };
+
 // Problem description shared by the launchers.  Sizes in elements.
 struct Problem {
     int B, H, T, dqk, dhv, L;
@@ -27,6 +30,11 @@ struct Workspace {
     float* c_final = nullptr;    // caller's final-state output [B,H,dqk,dhv] (NULL: none)
     float* seg_end = nullptr;    // segmented state walk: end states [B*H][P][dqk][dhv]
     float* seg_start = nullptr;  //                       start states [B*H][P][dqk][dhv]
+    // intra-chunk gradient modes with kRowDots: per output row and value
+    // tile, the dot product of the fp32 output row with the same row of
+    // `dot_partner` (an I/O-typed [B,H,T,out] tensor), into dots [B,H,T][out/BV]
+    const void* dot_partner = nullptr;
+    float* dots = nullptr;
 };
 
 // Segmented state walk (few heads, long sequences): number of segments P
@@ -35,6 +43,9 @@ struct Workspace {
 int state_segments(const Problem& p);
 int state_segments_for(const Problem& p, long heads_tiles);
 int state_chunks_per_segment(const Problem& p, int P);
+// Value-tile width of the intra-chunk kernel for an output width p.dhv
+// contracted over p.dqk (the number of row-dot partials is p.dhv / BV).
+int intra_value_tile(const Problem& p);
 bool state_big_tiles(const Problem& p);
 
 // Lays the workspace out from `base` (NULL: sizes only); returns its byte size.
@@ -48,10 +59,36 @@ hipError_t launch_gates_closed_form(const Problem& p, const float* fgate_pre, fl
                                     float* g, hipStream_t stream);
 hipError_t launch_state(const Problem& p, const void* k, const void* v, const float* fgate_pre,
                         const Workspace& ws, hipStream_t stream);
+// The reverse state walk of the backward pass: ws.states receives
+// D_0..D_{nc-2} (D_j: gradient into the state from the chunks after chunk
+// j, without the 1/sqrt(d_qk) factor), transposed [d_hv][d_qk]; ws.c0 and
+// ws.c_final must be NULL.
+hipError_t launch_state_rev(const Problem& p, const void* q, const void* dh, const float* fgate_pre,
+                            const Workspace& ws, hipStream_t stream);
 hipError_t launch_recurrent(const Problem& p, const void* q, const void* k, const void* v,
                             const float* igate_pre, const float* fgate_pre, float* state, void* h,
                             hipStream_t stream);
 hipError_t launch_intra(const Problem& p, const void* q, const void* k, const void* v,
                         const float* fgate_pre, const Workspace& ws, void* h, hipStream_t stream);
+// The intra-chunk kernel in its gradient modes (dq: kNatState | kRowDots;
+// dk: kNatState | kMirror | kRowDots; dv: kMirror): p.dqk is the contracted width (64..512),
+// p.dhv the output width; ws.a / ws.li / ws.states as the mode reads them;
+// every output row scaled by `scale`.
+hipError_t launch_intra_dq(const Problem& p, const void* q, const void* k, const void* v, const float* fgate_pre,
+                           const Workspace& ws, void* out, float scale, hipStream_t stream);
+hipError_t launch_intra_dk(const Problem& p, const void* q, const void* k, const void* v, const float* fgate_pre,
+                           const Workspace& ws, void* out, float scale, hipStream_t stream);
+hipError_t launch_intra_dv(const Problem& p, const void* q, const void* k, const void* v, const float* fgate_pre,
+                           const Workspace& ws, void* out, float scale, hipStream_t stream);
+
+// Backward-pass gate work: mirrored gate exponents for the mirrored intra
+// mode (mLSTMsig), and the input / forget gate gradients from the dq and dk
+// kernels' row partials (q_t.dq_t and k_t.dk_t, np per step, [B,H,T][np])
+// and the boundary couplings X [B,H,nc-1] (scratch) of the forward states
+// and the reverse-walk states (both [B,H,nc-1,d_hv,d_qk]).
+hipError_t launch_gates_mirror(const Problem& p, const Workspace& ws, float* ar, float* lr, hipStream_t stream);
+hipError_t launch_gate_grads(const Problem& p, const float* states, const float* dstates, float* X,
+                             const float* dq_dots, const float* dk_dots, int np, const float* igate_pre,
+                             const float* fgate_pre, float* dig, float* dfg, hipStream_t stream);
 
 }  // namespace tfla

@@ -37,6 +37,14 @@
 //           and writes the states (and C_T).
 // It costs one more read of k and v; the serial part left is P steps of a
 // d_qk x d_hv elementwise update.
+//
+// Reverse walk (REV, for the backward pass): the gradient that flows into
+// the state from the chunks after chunk j,
+//   D_{j-1} = diag(e^{g_j}) D_j + sum_{t in chunk j} e^{a_t} q_t dh_t^T,
+// D_{nc-1} = 0, is the same walk over the chunks in reverse order with
+// k := q, v := dh and weights e^{a_t}; D_{j-1} is stored in slot j-1 (the
+// intra-chunk kernel's mirrored mode reads slot kc for chunk kc).  Logical
+// chunk kl of the walk is chunk nc-1-kl; the partial last chunk comes first.
 #include <algorithm>
 #include <cstdlib>
 
@@ -85,7 +93,7 @@ template <typename T, int SB, int TV, int TC, int NTH> struct StatePrefetch {
     float g;                      // mLSTMsig: g of the block's chunk
 };
 
-template <typename T, int GATE, int SB, int TV, int TC, int NWS>
+template <typename T, int GATE, int SB, int TV, int TC, int NWS, bool REV>
 __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                     const float* __restrict__ a,
                                                     const float* __restrict__ li,
@@ -101,6 +109,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
     constexpr int WC = NWS / 2;                        // waves along the key columns
     constexpr int MV = TV / 64, MC = TC / WC / 32;     // 32x32 accumulators per wave along value / key
     static_assert(MC >= 1, "tile too narrow for the waves");
+    static_assert(!REV || GATE != kGla, "the reverse walk covers the per-step gates only");
 
     const int ntv = dhv / TV, ntk = dqk / TC;
     const int blk = xcd_remap(blockIdx.x, gridDim.x);
@@ -130,11 +139,14 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
     const int kbeg = seg * wk.cps;
     const int kend = seg == wk.nseg_buf - 1 ? wk.nwalk : min(kbeg + wk.cps, wk.nwalk);
     const int b0 = kbeg * bpc;
-    const int bend = kend <= nc - 1 ? kend * bpc : (nc - 1) * bpc + (T_ - (nc - 1) * L + SB - 1) / SB;
+    const int bend = (REV || kend <= nc - 1) ? kend * bpc
+                                             : (nc - 1) * bpc + (T_ - (nc - 1) * L + SB - 1) / SB;
+    // chunk of walk position kc
+    auto chunk = [&](int kc) { return REV ? nc - 1 - kc : kc; };
 
     auto fetch = [&](PF& pf, int b) {
-        const int kc = b / bpc;
-        const int s0 = b * SB;               // = kc*L + (b%bpc)*SB
+        const int kc = chunk(b / bpc);
+        const int s0 = kc * L + (b % bpc) * SB;
         if (GATE == kSig) pf.g = g[bh * nc + kc];
         // rows past the end (partial last chunk) are read clamped and weighted 0
 #pragma unroll
@@ -149,7 +161,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
             pf.k[u].load(kb + (size_t)s * dqk + c0 + c);
             if (GATE == kSig) {
                 pf.a[u] = a[bh * T_ + s];
-                pf.li[u] = li[bh * T_ + s];
+                if (!REV) pf.li[u] = li[bh * T_ + s];
             }
             if (GATE == kGla) {
                 const float* ar = a + (bh * T_ + s) * (size_t)dqk + c0 + c;
@@ -162,7 +174,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
         }
     };
     auto store = [&](PF& pf, int b) {
-        const int cs = (b / bpc) * L;
+        const int cs = chunk(b / bpc) * L;
         const int len = min(L, T_ - cs);     // steps in this chunk
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
@@ -172,11 +184,16 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
 #pragma unroll
         for (int u = 0; u < PF::NK; ++u) {
             const int idx = tid + NTH * u, r = idx / (TC / VEC), c = (idx % (TC / VEC)) * VEC;
-            const int s = b * SB + r;
+            const int s = cs + (b % bpc) * SB + r;
             const bool live = s < T_;
             float ws = 1.0f;
-            if (GATE == kSig) ws = exp2_fast((pf.g - pf.a[u] + pf.li[u]) * kLog2e);
-            else if (GATE == kScalar) ws = exp2_fast((float)(len - 1 - (s - cs)) * lg2);
+            if (REV) {
+                ws = GATE == kSig ? exp2_fast(pf.a[u] * kLog2e) : exp2_fast((float)(s - cs + 1) * lg2);
+            } else if (GATE == kSig) {
+                ws = exp2_fast((pf.g - pf.a[u] + pf.li[u]) * kLog2e);
+            } else if (GATE == kScalar) {
+                ws = exp2_fast((float)(len - 1 - (s - cs)) * lg2);
+            }
             Vec16<T> kw;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
@@ -229,7 +246,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
     PF pf;
     if (b0 < bend) fetch(pf, b0);
     for (int b = b0; b < bend; ++b) {
-        const int kc = b / bpc;
+        const int kc = b / bpc;               // walk position; chunk(kc) is the chunk
         const bool first = (b % bpc) == 0, last = (b % bpc) == bpc - 1 || b == bend - 1;
         __syncthreads();
         store(pf, b);
@@ -242,7 +259,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
             for (int mc = 0; mc < MC; ++mc) {
                 float e;
                 if (GATE == kSig) e = exp2_fast(gk * kLog2e);
-                else if (GATE == kScalar) e = exp2_fast((float)min(L, T_ - kc * L) * lg2);
+                else if (GATE == kScalar) e = exp2_fast((float)min(L, T_ - chunk(kc) * L) * lg2);
                 else e = exp2_fast(g[(bh * nc + kc) * dqk + c0 + cw + 32 * mc + i32] * kLog2e);
 #pragma unroll
                 for (int mv = 0; mv < MV; ++mv) acc[mv][mc] *= e;
@@ -261,7 +278,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
 #pragma unroll
                 for (int mc = 0; mc < MC; ++mc) acc[mv][mc] = mma32(af[mv], bf[mc], acc[mv][mc]);
         }
-        if (last && wk.write_states && kc < nc - 1) put_state(acc, kc + wk.soff);
+        if (last && wk.write_states && kc < nc - 1) put_state(acc, REV ? nc - 2 - kc : kc + wk.soff);
         if (b == bend - 1 && wk.end && (wk.end_all || seg == wk.nseg - 1)) {
             // the state after the walk, in [d_qk][d_hv]; each workgroup writes
             // only the tile it read from its initial state, so the caller's C_0
@@ -276,11 +293,11 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
 }
 
 // combine pass: start states of the segments from their end states
-template <int GATE>
+template <int GATE, bool REV>
 __global__ __launch_bounds__(256) void state_combine_kernel(const float* __restrict__ E, float* __restrict__ S,
                                                             const float* __restrict__ c0,
                                                             const float* __restrict__ g,
-                                                            const float* __restrict__ fg, int H, int dqk,
+                                                            const float* __restrict__ fg, int H, int T_, int dqk,
                                                             int dhv, int L, int nc, int P, int cps)
 {
     const size_t n = (size_t)dqk * dhv;
@@ -303,10 +320,14 @@ __global__ __launch_bounds__(256) void state_combine_kernel(const float* __restr
             if (p + 1 < P) {
                 ev[u] = E[(bh * P + p) * n + e];
                 if (GATE == kScalar) {
-                    gv[u] = (float)(cps * L) * lgam;
+                    // the reverse walk's first segment holds the partial last chunk
+                    const int steps = REV && p == 0 ? (cps - 1) * L + (T_ - (nc - 1) * L) : cps * L;
+                    gv[u] = (float)steps * lgam;
                 } else {
-                    for (int kc = p * cps; kc < (p + 1) * cps; ++kc)
+                    for (int kw = p * cps; kw < (p + 1) * cps; ++kw) {
+                        const int kc = REV ? nc - 1 - kw : kw;
                         gv[u] += GATE == kSig ? g[bh * nc + kc] : g[(bh * nc + kc) * dqk + c];
+                    }
                 }
             }
         }
@@ -321,7 +342,7 @@ __global__ __launch_bounds__(256) void state_combine_kernel(const float* __restr
     }
 }
 
-template <typename T, int SB, int TV, int TC, int NWS>
+template <typename T, int SB, int TV, int TC, int NWS, bool REV>
 hipError_t launch_walk(const Problem& p, const T* k, const T* v, const float* fg, const Workspace& ws,
                        const StateWalk& wk, hipStream_t stream)
 {
@@ -329,23 +350,47 @@ hipError_t launch_walk(const Problem& p, const T* k, const T* v, const float* fg
     const int threads = 64 * NWS;
     switch (p.gate) {
     case kSig:
-        state_kernel<T, kSig, SB, TV, TC, NWS><<<blocks, threads, 0, stream>>>(
+        state_kernel<T, kSig, SB, TV, TC, NWS, REV><<<blocks, threads, 0, stream>>>(
             k, v, ws.a, ws.li, ws.g, fg, ws.states, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
         break;
     case kScalar:
-        state_kernel<T, kScalar, SB, TV, TC, NWS><<<blocks, threads, 0, stream>>>(
+        state_kernel<T, kScalar, SB, TV, TC, NWS, REV><<<blocks, threads, 0, stream>>>(
             k, v, ws.a, ws.li, ws.g, fg, ws.states, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
         break;
     default:
-        state_kernel<T, kGla, SB, TV, TC, NWS><<<blocks, threads, 0, stream>>>(
+        if constexpr (REV) return hipErrorInvalidValue;
+        state_kernel<T, kGla, SB, TV, TC, NWS, false><<<blocks, threads, 0, stream>>>(
             k, v, ws.a, ws.li, ws.g, fg, ws.states, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
         break;
     }
     return hipGetLastError();
 }
 
+template <bool REV>
+hipError_t launch_combine(const Problem& p, const float* fg, const Workspace& ws, int P, int cps,
+                          hipStream_t stream)
+{
+    const dim3 cgrid((unsigned)((p.dqk * p.dhv + 255) / 256), (unsigned)(p.B * p.H));
+    switch (p.gate) {
+    case kSig:
+        state_combine_kernel<kSig, REV><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, ws.c0, ws.g, fg, p.H,
+                                                                   p.T, p.dqk, p.dhv, p.L, p.nc, P, cps);
+        break;
+    case kScalar:
+        state_combine_kernel<kScalar, REV><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, ws.c0, ws.g, fg,
+                                                                      p.H, p.T, p.dqk, p.dhv, p.L, p.nc, P, cps);
+        break;
+    default:
+        if constexpr (REV) return hipErrorInvalidValue;
+        state_combine_kernel<kGla, false><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, ws.c0, ws.g, fg,
+                                                                     p.H, p.T, p.dqk, p.dhv, p.L, p.nc, P, cps);
+        break;
+    }
+    return hipGetLastError();
+}
+
 // One configuration: unsegmented walk, or pass 1 + combine + pass 2.
-template <typename T, int SB, int TV, int TC, int NWS>
+template <typename T, int SB, int TV, int TC, int NWS, bool REV>
 hipError_t launch_state_cfg(const Problem& p, const T* k, const T* v, const float* fg, const Workspace& ws,
                             hipStream_t stream)
 {
@@ -354,33 +399,18 @@ hipError_t launch_state_cfg(const Problem& p, const T* k, const T* v, const floa
     const int nwalk = p.nc - 1 + (ws.c_final != nullptr);
     if (P <= 1) {
         const StateWalk wk{ws.c0, ws.c_final, 1, 1, nwalk > 0 ? nwalk : 1, nwalk, soff, 0, 1, soff};
-        return launch_walk<T, SB, TV, TC, NWS>(p, k, v, fg, ws, wk, stream);
+        return launch_walk<T, SB, TV, TC, NWS, REV>(p, k, v, fg, ws, wk, stream);
     }
     const int cps = state_chunks_per_segment(p, P);
     const StateWalk pass1{nullptr, ws.seg_end, P, P - 1, cps, p.nc - 1, 0, 1, 0, soff};
-    hipError_t e = launch_walk<T, SB, TV, TC, NWS>(p, k, v, fg, ws, pass1, stream);
+    hipError_t e = launch_walk<T, SB, TV, TC, NWS, REV>(p, k, v, fg, ws, pass1, stream);
     if (e != hipSuccess) return e;
-    const dim3 cgrid((unsigned)((p.dqk * p.dhv + 255) / 256), (unsigned)(p.B * p.H));
-    switch (p.gate) {
-    case kSig:
-        state_combine_kernel<kSig><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, ws.c0, ws.g, fg, p.H, p.dqk,
-                                                              p.dhv, p.L, p.nc, P, cps);
-        break;
-    case kScalar:
-        state_combine_kernel<kScalar><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, ws.c0, ws.g, fg, p.H,
-                                                                 p.dqk, p.dhv, p.L, p.nc, P, cps);
-        break;
-    default:
-        state_combine_kernel<kGla><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, ws.c0, ws.g, fg, p.H, p.dqk,
-                                                              p.dhv, p.L, p.nc, P, cps);
-        break;
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_combine<REV>(p, fg, ws, P, cps, stream)) != hipSuccess) return e;
     const StateWalk pass2{ws.seg_start, ws.c_final, P, P, cps, nwalk, soff, 0, 1, soff};
-    return launch_walk<T, SB, TV, TC, NWS>(p, k, v, fg, ws, pass2, stream);
+    return launch_walk<T, SB, TV, TC, NWS, REV>(p, k, v, fg, ws, pass2, stream);
 }
 
-template <typename T>
+template <typename T, bool REV>
 hipError_t launch_state_t(const Problem& p, const T* k, const T* v, const float* fg, const Workspace& ws,
                           hipStream_t stream)
 {
@@ -389,13 +419,15 @@ hipError_t launch_state_t(const Problem& p, const T* k, const T* v, const float*
     if (const char* e = std::getenv("TFLA_STATE_SB")) sb_cap = std::atoi(e);
     if constexpr (sizeof(T) == 2) {
         if (state_big_tiles(p)) {
-            if (p.L >= 256 && sb_cap >= 256) return launch_state_cfg<T, 256, 128, 128, 8>(p, k, v, fg, ws, stream);
-            if (p.L >= 128 && sb_cap >= 128) return launch_state_cfg<T, 128, 128, 128, 8>(p, k, v, fg, ws, stream);
-            return launch_state_cfg<T, 64, 128, 128, 8>(p, k, v, fg, ws, stream);
+            if (p.L >= 256 && sb_cap >= 256)
+                return launch_state_cfg<T, 256, 128, 128, 8, REV>(p, k, v, fg, ws, stream);
+            if (p.L >= 128 && sb_cap >= 128)
+                return launch_state_cfg<T, 128, 128, 128, 8, REV>(p, k, v, fg, ws, stream);
+            return launch_state_cfg<T, 64, 128, 128, 8, REV>(p, k, v, fg, ws, stream);
         }
     }
-    if (p.L >= 128) return launch_state_cfg<T, 128, 64, 64, 4>(p, k, v, fg, ws, stream);
-    return launch_state_cfg<T, 64, 64, 64, 4>(p, k, v, fg, ws, stream);
+    if (p.L >= 128) return launch_state_cfg<T, 128, 64, 64, 4, REV>(p, k, v, fg, ws, stream);
+    return launch_state_cfg<T, 64, 64, 64, 4, REV>(p, k, v, fg, ws, stream);
 }
 
 }  // namespace
@@ -446,10 +478,20 @@ hipError_t launch_state(const Problem& p, const void* k, const void* v, const fl
                         const Workspace& ws, hipStream_t stream)
 {
     if (p.bf16)
-        return launch_state_t<bf16>(p, static_cast<const bf16*>(k), static_cast<const bf16*>(v), fgate_pre, ws,
-                                    stream);
-    return launch_state_t<float>(p, static_cast<const float*>(k), static_cast<const float*>(v), fgate_pre, ws,
-                                 stream);
+        return launch_state_t<bf16, false>(p, static_cast<const bf16*>(k), static_cast<const bf16*>(v), fgate_pre,
+                                           ws, stream);
+    return launch_state_t<float, false>(p, static_cast<const float*>(k), static_cast<const float*>(v), fgate_pre,
+                                        ws, stream);
+}
+
+hipError_t launch_state_rev(const Problem& p, const void* q, const void* dh, const float* fgate_pre,
+                            const Workspace& ws, hipStream_t stream)
+{
+    if (p.bf16)
+        return launch_state_t<bf16, true>(p, static_cast<const bf16*>(q), static_cast<const bf16*>(dh), fgate_pre,
+                                          ws, stream);
+    return launch_state_t<float, true>(p, static_cast<const float*>(q), static_cast<const float*>(dh), fgate_pre,
+                                       ws, stream);
 }
 
 }  // namespace tfla

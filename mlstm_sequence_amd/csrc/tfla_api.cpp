@@ -1,10 +1,11 @@
 // tfla_api.cpp -- the C ABI declared in include/tfla.h: argument validation
 // (no HIP call before it passes), workspace sizing and carve-up, and the
-// three launches of the forward path on the caller's stream.
+// launches of the forward and backward paths on the caller's stream.
 #include "tfla.h"
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -173,6 +174,144 @@ int run_path(const tfla::Problem& p, const void* q, const void* k, const void* v
     e = tfla::launch_intra(p, q, k, v, fgate_pre, ws, h, stream);
     if (e != hipSuccess) return hip_fail(e, "intra-chunk kernel launch");
     return mark(marks, 3, stream);
+}
+
+// Backward pass: the forward workspace, then the reverse-walk states, the
+// mirrored gate exponents (mLSTMsig) and the per-step gate-gradient sums.
+struct BwdWorkspace {
+    tfla::Workspace fwd;
+    float* dstates;   // [B,H,nc-1,d_hv,d_qk]
+    float* ar;        // [B,H,T] mLSTMsig
+    float* lr;        // [B,H,T] mLSTMsig
+    float* dq_dots;   // [B,H,T][np]: q_t . dq_t per value tile of the dq kernel
+    float* dk_dots;   // [B,H,T][np]: k_t . dk_t likewise
+    float* X;         // [B,H,nc-1]: coupling <D_k, C_k> / sqrt(d_qk) across each chunk boundary
+    int np;
+};
+
+// the dq and dk products: contract d_hv, emit d_qk
+tfla::Problem grad_qk_problem(const tfla::Problem& p)
+{
+    tfla::Problem pc = p;
+    pc.dqk = p.dhv;
+    pc.dhv = p.dqk;
+    return pc;
+}
+
+size_t bwd_layout(const tfla::Problem& p, BwdWorkspace* ws, char* base)
+{
+    size_t off = tfla::workspace_layout(p, &ws->fwd, base);
+    const size_t bh = (size_t)p.B * p.H;
+    auto take = [&](size_t bytes) -> float* {
+        float* ptr = base ? reinterpret_cast<float*>(base + off) : nullptr;
+        off += align256(bytes);
+        return ptr;
+    };
+    ws->dstates = p.nc > 1 ? take(bh * (p.nc - 1) * p.dhv * p.dqk * 4) : nullptr;
+    const bool sig = p.gate == tfla::kSig;
+    ws->ar = sig ? take(bh * p.T * 4) : nullptr;
+    ws->lr = sig ? take(bh * p.T * 4) : nullptr;
+    ws->np = p.dqk / tfla::intra_value_tile(grad_qk_problem(p));
+    ws->dq_dots = take(bh * p.T * ws->np * 4);
+    ws->dk_dots = take(bh * p.T * ws->np * 4);
+    ws->X = p.nc > 1 ? take(bh * (p.nc - 1) * 4) : nullptr;
+    return off;
+}
+
+// Shapes the backward pass is built for: per-step gates, and d_hv (the
+// width the dq and dk products contract) a power of two the intra kernel
+// is instantiated for.
+int check_bwd_problem(int B, int H, int T, int d_qk, int d_hv, int L, int variant, tfla::Problem* p)
+{
+    int rc = check_problem(B, H, T, d_qk, d_hv, L, variant, p);
+    if (rc) return rc;
+    if (p->gate == tfla::kGla)
+        return fail(TFLA_ERR_UNSUPPORTED, "the backward pass covers TFLA_MLSTM_SIG and TFLA_SCALAR_DECAY");
+    if (!(d_hv == 64 || d_hv == 128 || (p->bf16 && (d_hv == 256 || d_hv == 512))))
+        return fail(TFLA_ERR_UNSUPPORTED, "backward: d_hv must be 64, 128, 256 or 512 (fp32 I/O: 64 or 128), got " +
+                                              std::to_string(d_hv));
+    return TFLA_OK;
+}
+
+int run_bwd(const tfla::Problem& p, const void* q, const void* k, const void* v, const float* igate_pre,
+            const float* fgate_pre, const void* dh, void* dq, void* dk, void* dv, float* dig, float* dfg,
+            const BwdWorkspace& ws, hipStream_t stream)
+{
+    const float scale = 1.0f / sqrtf((float)p.dqk);
+    hipError_t e = tfla::launch_gates(p, igate_pre, fgate_pre, ws.fwd, stream);
+    if (e != hipSuccess) return hip_fail(e, "gate kernel launch");
+    // forward states C_1..C_{nc-1}, [d_hv][d_qk] each
+    if ((e = tfla::launch_state(p, k, v, fgate_pre, ws.fwd, stream)) != hipSuccess)
+        return hip_fail(e, "state kernel launch");
+    tfla::Workspace mirrored = ws.fwd;   // gate exponents of the mirrored chunks
+    if (p.gate == tfla::kSig) {
+        if ((e = tfla::launch_gates_mirror(p, ws.fwd, ws.ar, ws.lr, stream)) != hipSuccess)
+            return hip_fail(e, "mirrored gate kernel launch");
+        mirrored.a = ws.ar;
+        mirrored.li = ws.lr;
+    }
+    // reverse walk: D_0..D_{nc-2}, [d_hv][d_qk] each
+    tfla::Workspace rev = ws.fwd;
+    rev.states = ws.dstates;
+    if ((e = tfla::launch_state_rev(p, q, dh, fgate_pre, rev, stream)) != hipSuccess)
+        return hip_fail(e, "reverse state kernel launch");
+    mirrored.states = ws.dstates;
+    // dq = scale (e^{a_t} C_{k-1} dh_t + sum_{s<=t} w_ts (dh_t . v_s) k_s): contract d_hv, emit d_qk
+    const tfla::Problem pc = grad_qk_problem(p);
+    tfla::Workspace wq = ws.fwd;
+    wq.dot_partner = q;
+    wq.dots = ws.dq_dots;
+    if ((e = tfla::launch_intra_dq(pc, dh, v, k, fgate_pre, wq, dq, scale, stream)) != hipSuccess)
+        return hip_fail(e, "dq kernel launch");
+    // dk = scale (e^{a'_t} D_k v_t + sum_{s>=t} w_st (v_t . dh_s) q_s): mirrored, contract d_hv
+    tfla::Workspace wk = mirrored;
+    wk.dot_partner = k;
+    wk.dots = ws.dk_dots;
+    if ((e = tfla::launch_intra_dk(pc, v, dh, q, fgate_pre, wk, dk, scale, stream)) != hipSuccess)
+        return hip_fail(e, "dk kernel launch");
+    // dv = scale (e^{a'_t} D_k^T k_t + sum_{s>=t} w_st (k_t . q_s) dh_s): mirrored, contract d_qk
+    if ((e = tfla::launch_intra_dv(p, k, q, dh, fgate_pre, mirrored, dv, scale, stream)) != hipSuccess)
+        return hip_fail(e, "dv kernel launch");
+    if ((e = tfla::launch_gate_grads(p, ws.fwd.states, ws.dstates, ws.X, ws.dq_dots, ws.dk_dots, ws.np, igate_pre,
+                                     fgate_pre, dig, dfg, stream)) != hipSuccess)
+        return hip_fail(e, "gate gradient kernel launch");
+    return TFLA_OK;
+}
+
+int check_bwd(const void* q, const void* k, const void* v, const float* igate_pre, const float* fgate_pre,
+              const void* dh, const void* dq, const void* dk, const void* dv, const float* dig, const float* dfg,
+              int B, int H, int T, int d_qk, int d_hv, int L, int variant, tfla::Problem* p)
+{
+    int rc = check_bwd_problem(B, H, T, d_qk, d_hv, L, variant, p);
+    if (rc) return rc;
+    if (!q || !k || !v || !dh || !dq || !dk || !dv)
+        return fail(TFLA_ERR_INVALID_ARG, "q, k, v, dh, dq, dk and dv must not be NULL");
+    for (const void* x : {q, k, v, dh, dq, dk, dv})
+        if (!aligned(x, 16)) return fail(TFLA_ERR_INVALID_ARG, "q, k, v, dh, dq, dk and dv must be 16-byte aligned");
+    if ((rc = check_gates(*p, igate_pre, fgate_pre))) return rc;
+    if (!dfg || !aligned(dfg, 4)) return fail(TFLA_ERR_INVALID_ARG, "dfg must be non-NULL and 4-byte aligned");
+    if (p->gate == tfla::kSig) {
+        if (!dig || !aligned(dig, 4))
+            return fail(TFLA_ERR_INVALID_ARG, "dig must be non-NULL and 4-byte aligned for mLSTMsig");
+    } else if (dig) {
+        return fail(TFLA_ERR_INVALID_ARG, "dig must be NULL for this variant (input gate is 1)");
+    }
+    const size_t esz = p->bf16 ? 2 : 4;
+    const size_t bht = (size_t)B * H * T;
+    const Range ins[] = {range_of(q, bht * d_qk * esz), range_of(k, bht * d_qk * esz),
+                         range_of(v, bht * d_hv * esz), range_of(dh, bht * d_hv * esz),
+                         range_of(fgate_pre, gate_bytes(*p)),
+                         igate_pre ? range_of(igate_pre, bht * 4) : Range{0, 0}};
+    const Range outs[] = {range_of(dq, bht * d_qk * esz), range_of(dk, bht * d_qk * esz),
+                          range_of(dv, bht * d_hv * esz), range_of(dfg, gate_bytes(*p)),
+                          dig ? range_of(dig, bht * 4) : Range{0, 0}};
+    for (size_t i = 0; i < 5; ++i) {
+        for (const Range& x : ins)
+            if (overlaps(outs[i], x)) return fail(TFLA_ERR_INVALID_ARG, "a gradient output overlaps an input");
+        for (size_t j = i + 1; j < 5; ++j)
+            if (overlaps(outs[i], outs[j])) return fail(TFLA_ERR_INVALID_ARG, "gradient outputs overlap");
+    }
+    return TFLA_OK;
 }
 
 }  // namespace
@@ -389,6 +528,49 @@ int tfla_dbg_states(const void* k, const void* v, const float* igate_pre, const 
     return rc;
 }
 
+size_t tfla_bwd_workspace_bytes(int B, int H, int T, int d_qk, int d_hv, int L, int variant)
+{
+    tfla::Problem p;
+    if (check_bwd_problem(B, H, T, d_qk, d_hv, L, variant, &p) != TFLA_OK) return 0;
+    BwdWorkspace ws;
+    return bwd_layout(p, &ws, nullptr);
+}
+
+int tfla_bwd(const void* q, const void* k, const void* v, const float* igate_pre, const float* fgate_pre,
+             const void* dh, void* dq, void* dk, void* dv, float* dig, float* dfg, int B, int H, int T, int d_qk,
+             int d_hv, int L, int variant, void* workspace, size_t workspace_bytes, void* stream)
+{
+    tfla::Problem p;
+    int rc = check_bwd(q, k, v, igate_pre, fgate_pre, dh, dq, dk, dv, dig, dfg, B, H, T, d_qk, d_hv, L, variant, &p);
+    if (rc) return rc;
+    BwdWorkspace ws;
+    const size_t need = bwd_layout(p, &ws, nullptr);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* base = workspace;
+    if (workspace) {
+        if (!aligned(workspace, 256)) return fail(TFLA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+        if (workspace_bytes < need)
+            return fail(TFLA_ERR_OUT_OF_MEMORY, "workspace of " + std::to_string(workspace_bytes) +
+                                                    " bytes is smaller than the " + std::to_string(need) + " needed");
+    } else {
+        if (inject_alloc_fault())
+            return fail(TFLA_ERR_OUT_OF_MEMORY, "injected allocation failure (TFLA_FAULT=alloc)");
+        hipError_t e = hipMallocAsync(&base, need, s);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(TFLA_ERR_OUT_OF_MEMORY, std::string("workspace allocation of ") + std::to_string(need) +
+                                                    " bytes failed: " + hipGetErrorString(e));
+        }
+    }
+    bwd_layout(p, &ws, static_cast<char*>(base));
+    rc = run_bwd(p, q, k, v, igate_pre, fgate_pre, dh, dq, dk, dv, dig, dfg, ws, s);
+    if (!workspace && base) {
+        hipError_t e = hipFreeAsync(base, s);
+        if (e != hipSuccess && rc == TFLA_OK) rc = hip_fail(e, "workspace free");
+    }
+    return rc;
+}
+
 const char* tfla_error_string(int code)
 {
     switch (code) {
@@ -403,6 +585,6 @@ const char* tfla_error_string(int code)
 
 const char* tfla_last_error(void) { return g_last_error.c_str(); }
 
-int tfla_version(void) { return 200; }
+int tfla_version(void) { return 300; }
 
 }  // extern "C"

@@ -52,6 +52,10 @@ def lib():
         L.tfla_state_workspace_bytes.restype = sz
         L.tfla_fwd_recurrent.argtypes = [vp, vp, vp, fp, fp, fp, vp] + [i] * 6 + [vp]
         L.tfla_fwd_recurrent.restype = i
+        L.tfla_bwd.argtypes = [vp, vp, vp, fp, fp, vp, vp, vp, vp, fp, fp] + [i] * 7 + [vp, sz, vp]
+        L.tfla_bwd.restype = i
+        L.tfla_bwd_workspace_bytes.argtypes = [i] * 7
+        L.tfla_bwd_workspace_bytes.restype = sz
         L.tfla_dbg_gates.argtypes = [fp, fp, fp, fp, fp] + [i] * 6 + [vp]
         L.tfla_dbg_gates.restype = i
         L.tfla_dbg_states.argtypes = [vp, vp, fp, fp, fp] + [i] * 7 + [vp]
@@ -159,6 +163,20 @@ def tfla_fwd_recurrent(q, k, v, igate_pre, fgate_pre, state, h, B, H, T, d_qk, d
     _check(rc, "tfla_fwd_recurrent")
 
 
+def tfla_bwd_workspace_bytes(B, H, T, d_qk, d_hv, L, variant) -> int:
+    return lib().tfla_bwd_workspace_bytes(B, H, T, d_qk, d_hv, L, variant)
+
+
+def tfla_bwd(q, k, v, igate_pre, fgate_pre, dh, dq, dk, dv, dig, dfg, B, H, T, d_qk, d_hv, L, variant,
+             workspace=None, workspace_bytes=0, stream=None):
+    """tfla_bwd(...): dq, dk, dv in the element type of q; dig (mLSTMsig,
+    else None) and dfg fp32; workspace None lets the library allocate it."""
+    rc = lib().tfla_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(igate_pre), _ptr(fgate_pre), _ptr(dh), _ptr(dq),
+                        _ptr(dk), _ptr(dv), _ptr(dig), _ptr(dfg), B, H, T, d_qk, d_hv, L, variant,
+                        _ptr(workspace), workspace_bytes, _stream(stream))
+    _check(rc, "tfla_bwd")
+
+
 def tfla_dbg_gates(igate_pre, fgate_pre, a_out, li_out, g_out, B, H, T, d_qk, L, variant, stream=None):
     rc = lib().tfla_dbg_gates(_ptr(igate_pre), _ptr(fgate_pre), _ptr(a_out), _ptr(li_out), _ptr(g_out),
                               B, H, T, d_qk, L, variant, _stream(stream))
@@ -192,6 +210,20 @@ def forward(q, k, v, igate_pre, fgate_pre, gate: int, L: int, h=None, workspace=
         tfla_fwd_ws(q, k, v, igate_pre, fgate_pre, h, B, H, T, d_qk, d_hv, L, var, workspace,
                     workspace.numel() * workspace.element_size(), stream)
     return h
+
+
+def backward(q, k, v, igate_pre, fgate_pre, dh, gate: int, L: int, workspace=None, stream=None):
+    """Allocates the gradients and runs the backward path on device tensors;
+    returns (dq, dk, dv, dig, dfg), dig None unless mLSTMsig."""
+    B, H, T, d_qk, d_hv = _dims(q, v)
+    var = variant_of(gate, q.dtype)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dig = torch.empty_like(igate_pre) if igate_pre is not None else None
+    dfg = torch.empty_like(fgate_pre)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    tfla_bwd(q, k, v, igate_pre, fgate_pre, dh, dq, dk, dv, dig, dfg, B, H, T, d_qk, d_hv, L, var,
+             workspace, nbytes, stream)
+    return dq, dk, dv, dig, dfg
 
 
 def workspace_for(q, v, gate: int, L: int) -> torch.Tensor:

@@ -37,13 +37,14 @@ def test_exports_every_declared_symbol(L):
     names = declared_functions()
     assert {"tfla_fwd", "tfla_fwd_ws", "tfla_workspace_bytes", "tfla_dbg_gates", "tfla_dbg_states",
             "tfla_fwd_state", "tfla_state_workspace_bytes", "tfla_fwd_recurrent",
+            "tfla_bwd", "tfla_bwd_workspace_bytes",
             "tfla_error_string", "tfla_last_error", "tfla_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
 
 def test_version_and_strings(L):
-    assert tfla.tfla_version() == 200
+    assert tfla.tfla_version() == 300
     for code in range(5):
         assert tfla.error_string(code)
     assert tfla.error_string(99) == "unknown status code"
@@ -182,3 +183,57 @@ def rec(state=C0, **kw):
 def test_recurrent_rejects_bad_arguments(L, kw, code):
     assert rec(**kw) == code
     assert tfla.tfla_last_error()
+
+
+# ---- backward entry point
+DH, DQ, DK, DV, DIG, DFG = (0x10000000 * (n + 10) for n in range(6))
+
+
+def bwd(q=Q, k=K, v=V, ig=IG, fg=FG, dh=DH, dq=DQ, dk=DK, dv=DV, dig=DIG, dfg=DFG, B=2, H=3, T=300, dqk=128,
+        dhv=256, Lc=64, variant=SIG | BF16, ws=None, nws=0):
+    return tfla.lib().tfla_bwd(q, k, v, ig, fg, dh, dq, dk, dv, dig, dfg, B, H, T, dqk, dhv, Lc, variant, ws, nws,
+                               None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(variant=GLA | BF16, ig=None, dig=None), UNSUPPORTED),   # per-channel gate: forward only
+    (dict(dhv=192), UNSUPPORTED), (dict(dhv=320), UNSUPPORTED),   # d_hv is contracted: powers of two
+    (dict(variant=SIG, dhv=256), UNSUPPORTED),                    # fp32 I/O: d_hv <= 128
+    (dict(dqk=96), UNSUPPORTED), (dict(Lc=32), UNSUPPORTED),
+    (dict(B=0), INVALID), (dict(variant=7), INVALID),
+    (dict(dh=None), INVALID), (dict(dq=None), INVALID), (dict(dv=None), INVALID),
+    (dict(dk=DK + 8), INVALID), (dict(dfg=None), INVALID), (dict(dfg=DFG + 2), INVALID),
+    (dict(dig=None), INVALID),                                    # mLSTMsig needs dig
+    (dict(variant=SCALAR | BF16, ig=None), INVALID),              # ... the others must not have one
+    (dict(dq=Q + 64), INVALID), (dict(dv=DH), INVALID),           # an output overlaps an input
+    (dict(dk=DQ + 16), INVALID), (dict(dig=DFG), INVALID),        # outputs overlap each other
+    (dict(ws=WS + 16, nws=1 << 30), INVALID), (dict(ws=WS, nws=16), OOM),
+])
+def test_bwd_rejects_bad_arguments(L, kw, code):
+    assert bwd(**kw) == code
+    assert tfla.tfla_last_error()
+
+
+def test_bwd_injected_allocation_failure(L, monkeypatch):
+    monkeypatch.setenv("TFLA_FAULT", "alloc")
+    assert bwd() == OOM
+
+
+def test_bwd_workspace_bytes(L):
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    B, H, T, dqk, dhv, Lc = 2, 3, 250, 128, 256, 64
+    nc = -(-T // Lc)
+    states = a256(B * H * (nc - 1) * dhv * dqk * 4)
+    steps = a256(B * H * T * 4)
+    # forward workspace, reverse-walk states, mirrored gates (2), the row
+    # partials of q.dq and k.dk (one per 128-wide tile of d_qk here), and
+    # the coupling across each chunk boundary
+    X = a256(B * H * (nc - 1) * 4)
+    sig = tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16) + states + 4 * steps + X
+    assert tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16) == sig
+    scal = tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SCALAR | BF16) + states + 2 * steps + X
+    assert tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, dhv, Lc, SCALAR | BF16) == scal
+    assert tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, dhv, Lc, GLA | BF16) == 0
+    assert tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, 192, Lc, SIG | BF16) == 0

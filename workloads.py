@@ -125,6 +125,13 @@ def initial_state(B: int, H: int, dqk: int, dhv: int, seed: int, std: float = 1.
     return torch.randn((B, H, dqk, dhv), generator=g, dtype=torch.float32) * std
 
 
+def upstream_grad(B: int, H: int, T: int, dhv: int, dtype: torch.dtype, seed: int) -> torch.Tensor:
+    """A seeded gradient dL/dh [B,H,T,d_hv] ~ N(0, 1), cast to ``dtype``
+    (the input of the backward pass)."""
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn((B, H, T, dhv), generator=g, dtype=torch.float32).to(dtype).contiguous()
+
+
 def head_slice(inputs: dict, variant: int, heads: list) -> dict:
     """Inputs restricted to a list of (b, h) pairs, as a batch of one with
     len(heads) heads -- used to run the oracle on sampled heads of a large
