@@ -77,6 +77,18 @@ def total_flops(wl, L):
     return sum(v["flops"] for v in m.values())
 
 
+def backward_flops(wl, L):
+    """Algorithmic flops of one backward pass (tfla_bwd): the forward states
+    recomputed and the reverse state walk (2 d_qk d_hv per step of the chunks
+    that feed a state, each), the three inter-chunk products of dq, dk and dv
+    (2 d_qk d_hv per step that reads a state, each) and their three causal
+    intra-chunk products (n(n+1)(d_qk + d_hv) per chunk of n steps, each)."""
+    n = chunk_lengths(wl.T, L)
+    per_head = (2 * 2 * wl.dqk * wl.dhv * sum(n[:-1]) + 3 * 2 * wl.dqk * wl.dhv * sum(n[1:])
+                + 3 * sum(m * (m + 1) * (wl.dqk + wl.dhv) for m in n))
+    return wl.B * wl.H * per_head
+
+
 # --------------------------------------------------------------------------- GPU timing
 def run_gpu(wl, L, steps, warmup, inputs_dev):
     import torch
@@ -123,6 +135,38 @@ def run_gpu(wl, L, steps, warmup, inputs_dev):
     per = {kname: t / steps for kname, t in per.items()}
     del ws, h
     return ms, wall / steps * 1e3, per
+
+
+def run_gpu_bwd(wl, L, steps, warmup, inputs_dev, dh):
+    """Milliseconds per tfla_bwd call (caller-owned workspace), timed with
+    events on the stream the library launches on."""
+    import torch
+    from mlstm_sequence_amd import tfla
+
+    q, k, v = inputs_dev["q"], inputs_dev["k"], inputs_dev["v"]
+    ig, fg = inputs_dev["igate_pre"], inputs_dev["fgate_pre"]
+    gate = {0: tfla.MLSTM_SIG, 1: tfla.SCALAR_DECAY}[wl.variant]
+    var = tfla.variant_of(gate, q.dtype)
+    nws = tfla.tfla_bwd_workspace_bytes(wl.B, wl.H, wl.T, wl.dqk, wl.dhv, L, var)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dig = None if ig is None else torch.empty_like(ig)
+    dfg = torch.empty_like(fg)
+    args = (q, k, v, ig, fg, dh, dq, dk, dv, dig, dfg, wl.B, wl.H, wl.T, wl.dqk, wl.dhv, L, var, ws, nws)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        tfla.tfla_bwd(*args)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        tfla.tfla_bwd(*args)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    del ws, dq, dk, dv, dig, dfg
+    return ms
 
 
 # --------------------------------------------------------------------------- CPU baseline
@@ -188,6 +232,7 @@ def main():
     ap.add_argument("--L", type=int, default=None, help="headline chunk size (default: best listed)")
     ap.add_argument("--sweep", type=str, default=None, help="comma-separated chunk sizes to sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (scales HBM byte counters)")
     args = ap.parse_args()
@@ -290,6 +335,21 @@ def main():
             "xl_chunk": {"L": xl, "ms_per_step": results[xl]["ms"], "tokens_per_s": results[xl]["tokens_per_s"]},
             "xl_speedup": results[xl]["tokens_per_s"] / results[64]["tokens_per_s"],
         }
+    # The backward pass (tfla_bwd) on the same workload, every swept chunk
+    # size: context beside the forward metric, not part of `value`.
+    if not args.no_backward and wl.variant != W.GLA:
+        dh = W.upstream_grad(wl.B, wl.H, wl.T, wl.dhv, wl.dtype, seed=wl.seed + 1).cuda()
+        bwd = {}
+        for L in sweep:
+            ms = run_gpu_bwd(wl, L, max(1, args.steps // 2), max(1, args.warmup // 2), dev, dh)
+            fl = backward_flops(wl, L)
+            bwd[L] = {"ms_per_step": ms, "tokens_per_s": wl.B * wl.T / (ms * 1e-3),
+                      "mfma_frac": fl / (ms * 1e-3) / PEAK_BF16, "algorithmic_flops": fl}
+            log(f"backward L={L}: {ms:.3f} ms/step, {bwd[L]['tokens_per_s']:.4g} tokens/s, "
+                f"{bwd[L]['mfma_frac'] * 100:.2f}% of bf16 peak")
+        Lb = min(bwd, key=lambda L: bwd[L]["ms_per_step"])
+        out["backward"] = dict(bwd[Lb], L=Lb, sweep={str(L): x for L, x in bwd.items()})
+        del dh
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(wl)
