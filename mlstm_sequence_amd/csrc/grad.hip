@@ -22,7 +22,8 @@
 //                       X_k = <D_k, C_k> / sqrt(d_qk)   (X_{nc-1} = 0),
 //                    the Frobenius product of the two fp32 states the path
 //                    materialises (every pair s <= end of chunk k < t
-//                    contributes once to it), so
+//                    contributes once to it; the reverse state walk forms it
+//                    in partials where it stores D_k), so
 //                       dL/dlog f_t = sum_{t <= t' in chunk k} r_t' + X_k
 //                    and no error accumulates over the sequence.  The fixed
 //                    per-head decay shares one log f over every step; with
@@ -70,35 +71,20 @@ __device__ __forceinline__ void step_dots(const float* dq_dots, const float* dk_
     kd = b;
 }
 
-// X_k = scale <D_k, C_k>: one workgroup per (batch-head, boundary); both
-// states in the same layout, n = d_qk d_hv elements each.
-__global__ __launch_bounds__(256) void state_dot_kernel(const float* __restrict__ C, const float* __restrict__ D,
-                                                       float* __restrict__ X, int n, float scale)
+// X_k = scale <D_k, C_k> from the reverse walk's nx partials of boundary k
+__device__ __forceinline__ double coupling(const float* xpart, size_t k, int nx, float scale)
 {
-    __shared__ double part[256];
-    const size_t base = (size_t)blockIdx.x * n;
-    const f32x4* c4 = reinterpret_cast<const f32x4*>(C + base);
-    const f32x4* d4 = reinterpret_cast<const f32x4*>(D + base);
-    float s = 0.0f;
-    for (int i = threadIdx.x; i < n / 4; i += 256) {
-        const f32x4 a = c4[i], b = d4[i];
-        s += a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
-    }
-    part[threadIdx.x] = s;
-    __syncthreads();
-    for (int d = 128; d >= 1; d >>= 1) {
-        if (threadIdx.x < d) part[threadIdx.x] += part[threadIdx.x + d];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) X[blockIdx.x] = (float)(part[0] * scale);
+    double x = 0.0;
+    for (int j = 0; j < nx; ++j) x += xpart[k * nx + j];
+    return x * scale;
 }
 
 // mLSTMsig: one workgroup per (batch-head, chunk); thread i owns steps
 // [cs + i n, cs + (i+1) n) of the chunk.  Sums are kept in double.
 __global__ __launch_bounds__(kScanThreads) void grad_scan_sig_kernel(const float* __restrict__ dq_dots,
                                                                     const float* __restrict__ dk_dots, int np,
-                                                                    const float* __restrict__ X,
-                                                                    const float* __restrict__ ig,
+                                                                    const float* __restrict__ xpart, int nx,
+                                                                    float scale, const float* __restrict__ ig,
                                                                     const float* __restrict__ fg,
                                                                     float* __restrict__ dig, float* __restrict__ dfg,
                                                                     int T_, int L, int nc)
@@ -127,7 +113,7 @@ __global__ __launch_bounds__(kScanThreads) void grad_scan_sig_kernel(const float
         __syncthreads();
     }
     // sum over the steps of the chunk after t1, plus the coupling past it
-    double acc = part[cur][tid] - s + (kc < nc - 1 ? (double)X[bh * (nc - 1) + kc] : 0.0);
+    double acc = part[cur][tid] - s + (kc < nc - 1 ? coupling(xpart, bh * (nc - 1) + kc, nx, scale) : 0.0);
     for (int t = t1 - 1; t >= t0; --t) {
         step_dots(dq_dots, dk_dots, base + t, np, r, kd);
         acc += r;
@@ -141,8 +127,8 @@ __global__ __launch_bounds__(kScanThreads) void grad_scan_sig_kernel(const float
 // Fixed per-head decay: one workgroup per head, over every batch.
 __global__ __launch_bounds__(kScanThreads) void grad_scalar_kernel(const float* __restrict__ dq_dots,
                                                                   const float* __restrict__ dk_dots, int np,
-                                                                  const float* __restrict__ X,
-                                                                  const float* __restrict__ fg,
+                                                                  const float* __restrict__ xpart, int nx,
+                                                                  float scale, const float* __restrict__ fg,
                                                                   float* __restrict__ dfg, int B, int H, int T_,
                                                                   int L, int nc)
 {
@@ -156,7 +142,7 @@ __global__ __launch_bounds__(kScanThreads) void grad_scalar_kernel(const float* 
             step_dots(dq_dots, dk_dots, bh * T_ + t, np, r, kd);
             s += ((double)(t % L) - centre) * r;
         }
-        for (int k = tid; k < nc - 1; k += kScanThreads) s += (double)L * X[bh * (nc - 1) + k];
+        for (int k = tid; k < nc - 1; k += kScanThreads) s += (double)L * coupling(xpart, bh * (nc - 1) + k, nx, scale);
     }
     part[tid] = s;
     __syncthreads();
@@ -180,19 +166,17 @@ hipError_t launch_gates_mirror(const Problem& p, const Workspace& ws, float* ar,
     return hipGetLastError();
 }
 
-hipError_t launch_gate_grads(const Problem& p, const float* states, const float* dstates, float* X,
-                             const float* dq_dots, const float* dk_dots, int np, const float* igate_pre,
-                             const float* fgate_pre, float* dig, float* dfg, hipStream_t stream)
+hipError_t launch_gate_grads(const Problem& p, const float* xpart, int nx, const float* dq_dots,
+                             const float* dk_dots, int np, const float* igate_pre, const float* fgate_pre,
+                             float* dig, float* dfg, hipStream_t stream)
 {
-    if (p.nc > 1)
-        state_dot_kernel<<<p.B * p.H * (p.nc - 1), 256, 0, stream>>>(states, dstates, X, p.dqk * p.dhv,
-                                                                     1.0f / sqrtf((float)p.dqk));
+    const float scale = 1.0f / sqrtf((float)p.dqk);
     if (p.gate == kSig)
-        grad_scan_sig_kernel<<<p.B * p.H * p.nc, kScanThreads, 0, stream>>>(dq_dots, dk_dots, np, X, igate_pre,
-                                                                            fgate_pre, dig, dfg, p.T, p.L, p.nc);
+        grad_scan_sig_kernel<<<p.B * p.H * p.nc, kScanThreads, 0, stream>>>(
+            dq_dots, dk_dots, np, xpart, nx, scale, igate_pre, fgate_pre, dig, dfg, p.T, p.L, p.nc);
     else
-        grad_scalar_kernel<<<p.H, kScanThreads, 0, stream>>>(dq_dots, dk_dots, np, X, fgate_pre, dfg, p.B, p.H,
-                                                             p.T, p.L, p.nc);
+        grad_scalar_kernel<<<p.H, kScanThreads, 0, stream>>>(dq_dots, dk_dots, np, xpart, nx, scale, fgate_pre, dfg,
+                                                             p.B, p.H, p.T, p.L, p.nc);
     return hipGetLastError();
 }
 

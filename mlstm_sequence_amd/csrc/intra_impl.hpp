@@ -408,21 +408,27 @@ hipError_t launch_intra_t(const Problem& p, const void* q, const void* k, const 
 
 // Value-tile width: 128 when it divides d_hv (bf16 I/O), else 64 (fp32 I/O
 // always: its doubled fragments would not fit the register budget; nor
-// would a 512-channel contraction's).  TFLA_INTRA_BV=64 forces 64 (tuning
-// sweeps).
+// would a 512-wide contraction's at two waves, i.e. L = 64).
+// TFLA_INTRA_BV=64 forces 64 (tuning sweeps).
 inline int intra_bv(const Problem& p)
 {
     if (const char* e = std::getenv("TFLA_INTRA_BV"))
         if (std::atoi(e) == 64) return 64;
-    return (p.bf16 && p.dhv % 128 == 0 && p.dqk <= 256) ? 128 : 64;
+    if (p.dqk > 256 && p.L < 128) return 64;
+    return (p.bf16 && p.dhv % 128 == 0) ? 128 : 64;
 }
 
 // Query rows per workgroup (32 per wave): as many as the chunk allows, up to
 // 256 (bf16) -- every staged C^T block and K/V tile then serves more rows.
-// TFLA_INTRA_ROWS=64|128|256 caps it (tuning sweeps).
+// A 512-wide contraction (the dq and dk products of the backward pass)
+// keeps 128: its 32 Q fragments need the whole register file, i.e. four
+// waves at one wave per SIMD (measured 14% faster over the backward pass
+// than eight spilling waves, and than 64-wide value tiles, which recompute
+// S = K Q^T for twice as many tiles).  TFLA_INTRA_ROWS=64|128|256 caps it
+// (tuning sweeps).
 inline int intra_rows(const Problem& p)
 {
-    int cap = p.bf16 ? 256 : 128;
+    int cap = p.bf16 ? (p.dqk > 256 ? 128 : 256) : 128;
     if (const char* e = std::getenv("TFLA_INTRA_ROWS")) {
         const int want = std::atoi(e);
         if (want == 64 || want == 128 || want == 256) cap = want < cap ? want : cap;
@@ -438,7 +444,7 @@ hipError_t dispatch_nw(const Problem& p, const void* q, const void* k, const voi
 {
     // a workgroup's query rows never straddle a chunk
     const int rows = intra_rows(p);
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (sizeof(T) == 2 && DQK <= 256) {
         if (rows == 256) return launch_intra_t<T, GATE, DQK, BV, 8, MODE>(p, q, k, v, fg, ws, h, scale, stream);
     }
     if (rows >= 128) return launch_intra_t<T, GATE, DQK, BV, 4, MODE>(p, q, k, v, fg, ws, h, scale, stream);
@@ -449,7 +455,7 @@ template <typename T, int GATE, int DQK, int MODE>
 hipError_t dispatch_bv(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
                        const Workspace& ws, void* h, float scale, hipStream_t stream)
 {
-    if constexpr (sizeof(T) == 2 && DQK <= 256) {
+    if constexpr (sizeof(T) == 2) {
         if (intra_bv(p) == 128) return dispatch_nw<T, GATE, DQK, 128, MODE>(p, q, k, v, fg, ws, h, scale, stream);
     }
     return dispatch_nw<T, GATE, DQK, 64, MODE>(p, q, k, v, fg, ws, h, scale, stream);

@@ -32,7 +32,10 @@ struct Workspace {
     float* seg_start = nullptr;  //                       start states [B*H][P][dqk][dhv]
     // intra-chunk gradient modes with kRowDots: per output row and value
     // tile, the dot product of the fp32 output row with the same row of
-    // `dot_partner` (an I/O-typed [B,H,T,out] tensor), into dots [B,H,T][out/BV]
+    // `dot_partner` (an I/O-typed [B,H,T,out] tensor), into dots [B,H,T][out/BV].
+    // Reverse state walk: `dot_partner` = the forward states (fp32, the
+    // layout of `states`), dots = per-wave partials of <D_m, C_m>
+    // [B,H,nc-1][state_dot_parts(p)].
     const void* dot_partner = nullptr;
     float* dots = nullptr;
 };
@@ -47,6 +50,8 @@ int state_chunks_per_segment(const Problem& p, int P);
 // contracted over p.dqk (the number of row-dot partials is p.dhv / BV).
 int intra_value_tile(const Problem& p);
 bool state_big_tiles(const Problem& p);
+// Partials per chunk boundary of the reverse walk's state product (tiles x waves).
+int state_dot_parts(const Problem& p);
 
 // Lays the workspace out from `base` (NULL: sizes only); returns its byte size.
 // with_c0 reserves the extra state slot an initial state needs.
@@ -84,11 +89,11 @@ hipError_t launch_intra_dv(const Problem& p, const void* q, const void* k, const
 // Backward-pass gate work: mirrored gate exponents for the mirrored intra
 // mode (mLSTMsig), and the input / forget gate gradients from the dq and dk
 // kernels' row partials (q_t.dq_t and k_t.dk_t, np per step, [B,H,T][np])
-// and the boundary couplings X [B,H,nc-1] (scratch) of the forward states
-// and the reverse-walk states (both [B,H,nc-1,d_hv,d_qk]).
+// and the reverse walk's partials of <D_m, C_m> (nx per boundary,
+// [B,H,nc-1][nx]).
 hipError_t launch_gates_mirror(const Problem& p, const Workspace& ws, float* ar, float* lr, hipStream_t stream);
-hipError_t launch_gate_grads(const Problem& p, const float* states, const float* dstates, float* X,
-                             const float* dq_dots, const float* dk_dots, int np, const float* igate_pre,
-                             const float* fgate_pre, float* dig, float* dfg, hipStream_t stream);
+hipError_t launch_gate_grads(const Problem& p, const float* xpart, int nx, const float* dq_dots,
+                             const float* dk_dots, int np, const float* igate_pre, const float* fgate_pre,
+                             float* dig, float* dfg, hipStream_t stream);
 
 }  // namespace tfla

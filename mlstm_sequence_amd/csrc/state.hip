@@ -45,6 +45,9 @@
 // k := q, v := dh and weights e^{a_t}; D_{j-1} is stored in slot j-1 (the
 // intra-chunk kernel's mirrored mode reads slot kc for chunk kc).  Logical
 // chunk kl of the walk is chunk nc-1-kl; the partial last chunk comes first.
+// Where it stores D_m it also forms the Frobenius product with the forward
+// state C_m of the same slot (the gate gradients' boundary coupling), as one
+// partial per wavefront: [B*H][nc-1][tiles][waves].
 #include <algorithm>
 #include <cstdlib>
 
@@ -100,7 +103,9 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
                                                     const float* __restrict__ g,
                                                     const float* __restrict__ fg,
                                                     float* __restrict__ states, StateWalk wk, int H,
-                                                    int T_, int dqk, int dhv, int L, int nc)
+                                                    int T_, int dqk, int dhv, int L, int nc,
+                                                    const float* __restrict__ cstates,
+                                                    float* __restrict__ xpart)
 {
     constexpr int NTH = 64 * NWS;
     typedef StatePrefetch<T, SB, TV, TC, NTH> PF;
@@ -278,7 +283,28 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
 #pragma unroll
                 for (int mc = 0; mc < MC; ++mc) acc[mv][mc] = mma32(af[mv], bf[mc], acc[mv][mc]);
         }
-        if (last && wk.write_states && kc < nc - 1) put_state(acc, REV ? nc - 2 - kc : kc + wk.soff);
+        if (last && wk.write_states && kc < nc - 1) {
+            put_state(acc, REV ? nc - 2 - kc : kc + wk.soff);
+            if (REV && xpart) {
+                // the coupling <D_m, C_m> across this chunk boundary: this
+                // wave's share, against the forward state stored in the
+                // same slot and layout
+                const int slot = nc - 2 - kc;
+                float x = 0.0f;
+#pragma unroll
+                for (int mv = 0; mv < MV; ++mv) {
+                    const float* src =
+                        cstates + ((bh * ns + slot) * (size_t)dhv + v0 + vw + 32 * mv) * dqk + c0 + cw + i32;
+#pragma unroll
+                    for (int mc = 0; mc < MC; ++mc)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) x += acc[mv][mc][r] * src[(size_t)arow(r) * dqk + 32 * mc];
+                }
+#pragma unroll
+                for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+                if (lane == 0) xpart[((bh * (nc - 1) + slot) * tiles + tile) * NWS + w] = x;
+            }
+        }
         if (b == bend - 1 && wk.end && (wk.end_all || seg == wk.nseg - 1)) {
             // the state after the walk, in [d_qk][d_hv]; each workgroup writes
             // only the tile it read from its initial state, so the caller's C_0
@@ -351,16 +377,19 @@ hipError_t launch_walk(const Problem& p, const T* k, const T* v, const float* fg
     switch (p.gate) {
     case kSig:
         state_kernel<T, kSig, SB, TV, TC, NWS, REV><<<blocks, threads, 0, stream>>>(
-            k, v, ws.a, ws.li, ws.g, fg, ws.states, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
+            k, v, ws.a, ws.li, ws.g, fg, ws.states, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc,
+            static_cast<const float*>(ws.dot_partner), ws.dots);
         break;
     case kScalar:
         state_kernel<T, kScalar, SB, TV, TC, NWS, REV><<<blocks, threads, 0, stream>>>(
-            k, v, ws.a, ws.li, ws.g, fg, ws.states, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
+            k, v, ws.a, ws.li, ws.g, fg, ws.states, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc,
+            static_cast<const float*>(ws.dot_partner), ws.dots);
         break;
     default:
         if constexpr (REV) return hipErrorInvalidValue;
         state_kernel<T, kGla, SB, TV, TC, NWS, false><<<blocks, threads, 0, stream>>>(
-            k, v, ws.a, ws.li, ws.g, fg, ws.states, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc);
+            k, v, ws.a, ws.li, ws.g, fg, ws.states, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc,
+            static_cast<const float*>(ws.dot_partner), ws.dots);
         break;
     }
     return hipGetLastError();
@@ -458,6 +487,12 @@ int state_segments_for(const Problem& p, long heads_tiles)
     if (P < 2) return 1;
     const int cps = (int)((nfeed + P - 1) / P);
     return (nfeed + cps - 1) / cps;   // no empty segment
+}
+
+int state_dot_parts(const Problem& p)
+{
+    if (p.bf16 && state_big_tiles(p)) return (p.dhv / 128) * (p.dqk / 128) * 8;
+    return (p.dhv / 64) * (p.dqk / 64) * 4;
 }
 
 int state_segments(const Problem& p)

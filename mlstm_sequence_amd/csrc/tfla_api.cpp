@@ -185,8 +185,8 @@ struct BwdWorkspace {
     float* lr;        // [B,H,T] mLSTMsig
     float* dq_dots;   // [B,H,T][np]: q_t . dq_t per value tile of the dq kernel
     float* dk_dots;   // [B,H,T][np]: k_t . dk_t likewise
-    float* X;         // [B,H,nc-1]: coupling <D_k, C_k> / sqrt(d_qk) across each chunk boundary
-    int np;
+    float* xpart;     // [B,H,nc-1][nx]: partials of <D_k, C_k> across each chunk boundary
+    int np, nx;
 };
 
 // the dq and dk products: contract d_hv, emit d_qk
@@ -214,7 +214,8 @@ size_t bwd_layout(const tfla::Problem& p, BwdWorkspace* ws, char* base)
     ws->np = p.dqk / tfla::intra_value_tile(grad_qk_problem(p));
     ws->dq_dots = take(bh * p.T * ws->np * 4);
     ws->dk_dots = take(bh * p.T * ws->np * 4);
-    ws->X = p.nc > 1 ? take(bh * (p.nc - 1) * 4) : nullptr;
+    ws->nx = tfla::state_dot_parts(p);
+    ws->xpart = p.nc > 1 ? take(bh * (p.nc - 1) * ws->nx * 4) : nullptr;
     return off;
 }
 
@@ -253,6 +254,8 @@ int run_bwd(const tfla::Problem& p, const void* q, const void* k, const void* v,
     // reverse walk: D_0..D_{nc-2}, [d_hv][d_qk] each
     tfla::Workspace rev = ws.fwd;
     rev.states = ws.dstates;
+    rev.dot_partner = ws.fwd.states;
+    rev.dots = ws.xpart;
     if ((e = tfla::launch_state_rev(p, q, dh, fgate_pre, rev, stream)) != hipSuccess)
         return hip_fail(e, "reverse state kernel launch");
     mirrored.states = ws.dstates;
@@ -272,8 +275,8 @@ int run_bwd(const tfla::Problem& p, const void* q, const void* k, const void* v,
     // dv = scale (e^{a'_t} D_k^T k_t + sum_{s>=t} w_st (k_t . q_s) dh_s): mirrored, contract d_qk
     if ((e = tfla::launch_intra_dv(p, k, q, dh, fgate_pre, mirrored, dv, scale, stream)) != hipSuccess)
         return hip_fail(e, "dv kernel launch");
-    if ((e = tfla::launch_gate_grads(p, ws.fwd.states, ws.dstates, ws.X, ws.dq_dots, ws.dk_dots, ws.np, igate_pre,
-                                     fgate_pre, dig, dfg, stream)) != hipSuccess)
+    if ((e = tfla::launch_gate_grads(p, ws.xpart, ws.nx, ws.dq_dots, ws.dk_dots, ws.np, igate_pre, fgate_pre, dig,
+                                     dfg, stream)) != hipSuccess)
         return hip_fail(e, "gate gradient kernel launch");
     return TFLA_OK;
 }

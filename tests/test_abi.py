@@ -229,8 +229,9 @@ def test_bwd_workspace_bytes(L):
     steps = a256(B * H * T * 4)
     # forward workspace, reverse-walk states, mirrored gates (2), the row
     # partials of q.dq and k.dk (one per 128-wide tile of d_qk here), and
-    # the coupling across each chunk boundary
-    X = a256(B * H * (nc - 1) * 4)
+    # the partials of the coupling across each chunk boundary (64x64 state
+    # tiles at this size, four waves each)
+    X = a256(B * H * (nc - 1) * (dhv // 64) * (dqk // 64) * 4 * 4)
     sig = tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16) + states + 4 * steps + X
     assert tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16) == sig
     scal = tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SCALAR | BF16) + states + 2 * steps + X
