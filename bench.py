@@ -214,7 +214,7 @@ def traffic_for(kernel, wl, L):
 
 
 def source_sha(kernel):
-    files = {"gates": ["gates.hip"], "state": ["state.hip"], "intra": ["intra.hip"]}[kernel]
+    files = {"gates": ["gates.hip"], "state": ["state.hip"], "intra": ["intra.hip", "intra_impl.hpp"]}[kernel]
     hs = hashlib.sha256()
     for f in files + ["gfx950.hpp"]:
         with open(os.path.join(ROOT, "mlstm_sequence_amd", "csrc", f), "rb") as fh:
