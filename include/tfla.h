@@ -172,8 +172,10 @@ int tfla_fwd_recurrent(const void* q, const void* k, const void* v,
  *     dq_t = C_t dh_t / sqrt(d_qk),   dk_t = i_t dC_t v_t,   dv_t = i_t dC_t^T k_t
  *     dL/dlog i_t = k_t . dk_t,       dL/dlog f_t = sum_{t'>=t} (q_t'.dq_t' - k_t'.dk_t')
  *
- * and the gate pre-activations through their sigmoids (a log forget gate at
- * its floor of -100 passes no gradient).  The states C_k are recomputed
+ * (for the per-key-channel gate diag(f) acts per channel and the last sum is
+ * taken per channel c: q_t',c dq_t',c - k_t',c dk_t',c), and the gate
+ * pre-activations through their sigmoids (a log forget gate at its floor of
+ * -100 passes no gradient).  The states C_k are recomputed
  * (nothing is kept from the forward call); the gradient into the state at
  * each chunk boundary is walked backwards over the chunks and materialised
  * in fp32 like C_k; dq, dk and dv are intra-chunk matrix-core products over
@@ -185,11 +187,11 @@ int tfla_fwd_recurrent(const void* q, const void* k, const void* v,
  *   dv        [B,H,T,d_hv] output, the element type of q.
  *   dig       fp32 [B,H,T] output for TFLA_MLSTM_SIG; NULL otherwise.
  *   dfg       fp32 output shaped like fgate_pre: [B,H,T] (TFLA_MLSTM_SIG),
- *             [H] (TFLA_SCALAR_DECAY: summed over batches and steps).
+ *             [H] (TFLA_SCALAR_DECAY: summed over batches and steps),
+ *             [B,H,T,d_qk] (TFLA_GLA_KEY).
  *   Outputs are fully overwritten and must not overlap each other or an
  *   input.
- *   variant   TFLA_MLSTM_SIG or TFLA_SCALAR_DECAY (| TFLA_IO_BF16);
- *             TFLA_GLA_KEY returns TFLA_ERR_UNSUPPORTED.
+ *   variant   any gate kind | TFLA_IO_BF16, as for tfla_fwd.
  *   d_qk      as for tfla_fwd; d_hv 64, 128, 256 or 512 (fp32 I/O: 64 or
  *             128), since the dq and dk products contract over it.
  *   workspace caller-owned device workspace of at least

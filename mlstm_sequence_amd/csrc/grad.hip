@@ -35,6 +35,10 @@
 //                    cancel.  Through the sigmoids: dig = (k.dk)(1 - i),
 //                    dfg = dL/dlog f (1 - f), 0 where the log forget gate
 //                    sits at its floor.
+//                    Per-channel gate: every quantity above per key channel c,
+//                    r_{t,c} = q_{t,c} dq_{t,c} - k_{t,c} dk_{t,c} (from the dq and dk
+//                    kernels' fp32 per-element products), X_{k,c} the row dot
+//                    of D_k and C_k in channel c, and d log f / dx = (1 - sigmoid(x))/16.
 #include "gfx950.hpp"
 #include "kernels.hpp"
 
@@ -56,6 +60,20 @@ __global__ __launch_bounds__(256) void gates_mirror_kernel(const float* __restri
     const float ap = a[bh * T_ + p];
     ar[bh * T_ + t] = gk - ap + li[bh * T_ + p];
     lr[bh * T_ + t] = ap - gk;
+}
+
+// per-channel gate, mirrored chunks: a'_{t,c} = g_{k,c} - a_{p,c}
+__global__ __launch_bounds__(256) void gates_mirror_gla_kernel(const float* __restrict__ a,
+                                                              const float* __restrict__ g, float* __restrict__ ar,
+                                                              int T_, int L, int nc, int dqk)
+{
+    const size_t bh = blockIdx.y;
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const int t = (int)(idx / dqk), c = (int)(idx % dqk);
+    if (t >= T_) return;
+    const int kc = t / L, cs = kc * L, len = min(L, T_ - cs);
+    const int p = 2 * cs + len - 1 - t;
+    ar[(bh * T_ + t) * dqk + c] = g[(bh * nc + kc) * dqk + c] - a[(bh * T_ + p) * dqk + c];
 }
 
 // r_t and k_t.dk_t from the per-tile partial dots of step t
@@ -124,6 +142,34 @@ __global__ __launch_bounds__(kScanThreads) void grad_scan_sig_kernel(const float
     }
 }
 
+// Per-channel gate: one workgroup per (batch-head, chunk), one thread per key
+// channel walking the chunk backwards from its boundary coupling.
+__global__ __launch_bounds__(256) void grad_gla_kernel(const float* __restrict__ dq_prod,
+                                                      const float* __restrict__ dk_prod,
+                                                      const float* __restrict__ xpart, int nx, float scale,
+                                                      const float* __restrict__ fg, float* __restrict__ dfg,
+                                                      int T_, int L, int nc, int dqk)
+{
+    const int kc = blockIdx.x % nc;
+    const size_t bh = blockIdx.x / nc;
+    const int c = threadIdx.x;
+    if (c >= dqk) return;
+    const int cs = kc * L, ce = min(cs + L, T_);
+    double acc = 0.0;
+    if (kc < nc - 1) {
+        const float* xp = xpart + ((bh * (nc - 1) + kc) * dqk + c) * nx;
+        for (int j = 0; j < nx; ++j) acc += xp[j];
+        acc *= scale;
+    }
+    for (int t = ce - 1; t >= cs; --t) {
+        const size_t o = (bh * T_ + t) * dqk + c;
+        acc += (double)dq_prod[o] - (double)dk_prod[o];
+        const float x = fg[o];
+        const bool floored = log_sigmoid(x) * (1.0f / 16.0f) < kLogForgetFloor;
+        dfg[o] = floored ? 0.0f : (float)(acc / (16.0 * (1.0 + exp((double)x))));
+    }
+}
+
 // Fixed per-head decay: one workgroup per head, over every batch.
 __global__ __launch_bounds__(kScanThreads) void grad_scalar_kernel(const float* __restrict__ dq_dots,
                                                                   const float* __restrict__ dk_dots, int np,
@@ -161,8 +207,13 @@ __global__ __launch_bounds__(kScanThreads) void grad_scalar_kernel(const float* 
 
 hipError_t launch_gates_mirror(const Problem& p, const Workspace& ws, float* ar, float* lr, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((p.T + 255) / 256), (unsigned)(p.B * p.H));
-    gates_mirror_kernel<<<grid, 256, 0, stream>>>(ws.a, ws.li, ws.g, ar, lr, p.T, p.L, p.nc);
+    if (p.gate == kGla) {
+        const dim3 grid((unsigned)(((size_t)p.T * p.dqk + 255) / 256), (unsigned)(p.B * p.H));
+        gates_mirror_gla_kernel<<<grid, 256, 0, stream>>>(ws.a, ws.g, ar, p.T, p.L, p.nc, p.dqk);
+    } else {
+        const dim3 grid((unsigned)((p.T + 255) / 256), (unsigned)(p.B * p.H));
+        gates_mirror_kernel<<<grid, 256, 0, stream>>>(ws.a, ws.li, ws.g, ar, lr, p.T, p.L, p.nc);
+    }
     return hipGetLastError();
 }
 
@@ -171,7 +222,10 @@ hipError_t launch_gate_grads(const Problem& p, const float* xpart, int nx, const
                              float* dig, float* dfg, hipStream_t stream)
 {
     const float scale = 1.0f / sqrtf((float)p.dqk);
-    if (p.gate == kSig)
+    if (p.gate == kGla)
+        grad_gla_kernel<<<p.B * p.H * p.nc, 256, 0, stream>>>(dq_dots, dk_dots, xpart, nx, scale, fgate_pre, dfg, p.T,
+                                                              p.L, p.nc, p.dqk);
+    else if (p.gate == kSig)
         grad_scan_sig_kernel<<<p.B * p.H * p.nc, kScanThreads, 0, stream>>>(
             dq_dots, dk_dots, np, xpart, nx, scale, igate_pre, fgate_pre, dig, dfg, p.T, p.L, p.nc);
     else

@@ -100,7 +100,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
                                                            float* __restrict__ dots)
 {
     constexpr bool NAT = (MODE & kNatState) != 0, REV = (MODE & kMirror) != 0, DOTS = (MODE & kRowDots) != 0;
-    static_assert(MODE == 0 || GATE != kGla, "gradient modes cover the per-step gates only");
+    // per-channel gate: decay inside the contraction (forward, dv), or on the
+    // output columns (dq, dk: the contracted index is the value channel)
+    constexpr bool OUTDECAY = GATE == kGla && NAT, INDECAY = GATE == kGla && !NAT;
     constexpr int NTH = 64 * NW;
     constexpr int BQ = 32 * NW;           // query rows per workgroup
     // C^T channels per stage: 128 (two stages at d_qk = 256) when the
@@ -139,7 +141,8 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     const T* qb = q + bh * (size_t)T_ * DQK;
     const T* kb = k + bh * (size_t)T_ * DQK;
     const T* vb = v + bh * (size_t)T_ * dhv;
-    const float* ab = (GATE == kGla) ? a + bh * (size_t)T_ * DQK : a + bh * (size_t)T_;
+    const int gw = OUTDECAY ? dhv : DQK;   // per-channel gate row width
+    const float* ab = (GATE == kGla) ? a + bh * (size_t)T_ * gw : a + bh * (size_t)T_;
     const float* lb = (GATE == kSig) ? li + bh * (size_t)T_ : nullptr;
     float lg2 = 0.0f;   // log2 of the fixed decay
     if (GATE == kScalar) lg2 = fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor) * kLog2e;
@@ -153,10 +156,10 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
 #pragma unroll
         for (int kq = 0; kq < KQ; ++kq) {
             const int c = 16 * kq + 8 * hh;
-            if (GATE != kGla) {
+            if (!INDECAY) {
                 qf[kq] = load8(qb + (size_t)row(tqc) * DQK + c);
             } else {
-                const Frag raw = load8(qb + (size_t)tqc * DQK + c);
+                const Frag raw = load8(qb + (size_t)row(tqc) * DQK + c);
                 for (int e = 0; e < 8; ++e) {
                     float ex = ab[(size_t)tqc * DQK + c + e];
                     if (ref_row >= 0) ex -= ab[(size_t)ref_row * DQK + c + e];
@@ -231,7 +234,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
 #pragma unroll
         for (int u = 0; u < PF::NK; ++u) {
             const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
-            if (GATE == kGla) {
+            if (INDECAY) {
                 const int s = min(s0 + r, T_ - 1);
                 for (int e = 0; e < VEC; ++e) {
                     const float ex = ab[(size_t)ref_row * DQK + c + e] - ab[(size_t)s * DQK + c + e];
@@ -243,6 +246,16 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
             const int idx = tid + NTH * u, r = idx / (BV / VEC), c = (idx % (BV / VEC)) * VEC;
+            if (OUTDECAY) {
+                // output-side decay: value row s scaled by e^{a_R - a_s} per
+                // column, R the last step of its 32-step half (factor <= 1)
+                const int s = min(s0 + r, T_ - 1);
+                const int R = min(s0 + 32 * (r >> 5) + 31, T_ - 1);
+                for (int e = 0; e < VEC; ++e) {
+                    const float ex = ab[(size_t)R * gw + v0 + c + e] - ab[(size_t)s * gw + v0 + c + e];
+                    pf.kv.v[u].set(e, pf.kv.v[u].get(e) * exp2_fast(ex * kLog2e));
+                }
+            }
             pf.kv.v[u].store(&sm.kv.vs[r][c]);
         }
         if (GATE == kSig && tid < 64) sm.bcol[tid] = (REV ? pf.li : pf.li - pf.a) * kLog2e;
@@ -294,7 +307,23 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     }
 
     // ---------------- intra-chunk term, tiled along the chunk
-    if (GATE != kGla && !inter) load_q(-1);
+    if (!INDECAY && !inter) load_q(-1);
+    // output-side decay: acc holds its partial sums in the frame of step
+    // fref (true value = acc e^{a_t - a_fref}; fref < 0: the chunk start,
+    // a = 0); the frame moves forward half by half, each move a factor <= 1
+    int fref = -1;
+    auto move_frame = [&](int R) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int col = v0 + 32 * nt + i32;
+            float ex = ab[(size_t)R * gw + col];
+            if (fref >= 0) ex -= ab[(size_t)fref * gw + col];
+            const float e = exp2_fast(ex * kLog2e);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[nt][r] *= e;
+        }
+        fref = R;
+    };
     const float at2 = (GATE == kSig) ? ab[tqc] * kLog2e : 0.0f;
     const int tlo = t0 + 32 * w;                  // first query row of this wave
     const int nkv = (t0 - cs) / 64 + BQ / 64;     // key tiles up to the end of the query tile
@@ -303,7 +332,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     for (int j = 0; j < nkv; ++j) {
         const int s0 = cs + 64 * j;
         int ref_row = -1;
-        if (GATE == kGla) {
+        if (INDECAY) {
             ref_row = (s0 + 63 < t0) ? t0 - 1 : min(s0 + 31, T_ - 1);
             if (ref_row != q_ref) {
                 load_q(ref_row);
@@ -320,6 +349,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
             const int slo = s0 + 32 * mt;
             if (slo > tlo + 31 || slo >= T_) continue;   // wholly above the diagonal, or past the end
             const bool diag = slo == tlo;
+            if (OUTDECAY) move_frame(min(slo + 31, T_ - 1));
             // S^T (32 key steps x 32 query rows of this wave)
             f32x16 st;
             for (int r = 0; r < 16; ++r) st[r] = 0.0f;
@@ -355,6 +385,20 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     }
 
     // ---------------- output
+    if (OUTDECAY) {
+        // out of the frame: e^{a_t - a_fref}, t within 31 steps before fref
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int t = min(t0 + 32 * w + 8 * (r >> 2) + 4 * hh + (r & 3), T_ - 1);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int col = v0 + 32 * nt + i32;
+                float ex = ab[(size_t)t * gw + col];
+                if (fref >= 0) ex -= ab[(size_t)fref * gw + col];
+                acc[nt][r] *= exp2_fast(ex * kLog2e);
+            }
+        }
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int t = t0 + 32 * w + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -363,7 +407,20 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) dst[32 * nt] = from_float<T>(acc[nt][r] * scale);
     }
-    if constexpr (DOTS) {
+    if constexpr (DOTS && GATE == kGla) {
+        // per-element products of the fp32 output with the partner, before
+        // rounding (the per-channel gate gradient sums them per channel)
+        const T* pb = partner + bh * (size_t)T_ * dhv + v0 + i32;
+        float* db = dots + bh * (size_t)T_ * dhv + v0 + i32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int t = t0 + 32 * w + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (t >= T_) continue;
+            const size_t o = (size_t)row(t) * dhv;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) db[o + 32 * nt] = acc[nt][r] * scale * to_float(pb[o + 32 * nt]);
+        }
+    } else if constexpr (DOTS) {
         // row dot products of the fp32 output with the partner rows, before
         // rounding: the gate gradients sum them over the sequence, where
         // rounding first would not cancel
@@ -488,9 +545,7 @@ hipError_t dispatch_gate(const Problem& p, const void* q, const void* k, const v
     switch (p.gate) {
     case kSig: return dispatch_dqk<T, kSig, MODE>(p, q, k, v, fg, ws, h, scale, stream);
     case kScalar: return dispatch_dqk<T, kScalar, MODE>(p, q, k, v, fg, ws, h, scale, stream);
-    default:
-        if constexpr (MODE == 0) return dispatch_dqk<T, kGla, 0>(p, q, k, v, fg, ws, h, scale, stream);
-        return hipErrorInvalidValue;
+    default: return dispatch_dqk<T, kGla, MODE>(p, q, k, v, fg, ws, h, scale, stream);
     }
 }
 

@@ -50,7 +50,8 @@ int state_chunks_per_segment(const Problem& p, int P);
 // contracted over p.dqk (the number of row-dot partials is p.dhv / BV).
 int intra_value_tile(const Problem& p);
 bool state_big_tiles(const Problem& p);
-// Partials per chunk boundary of the reverse walk's state product (tiles x waves).
+// Partials per chunk boundary of the reverse walk's state product (tiles x
+// waves; per-channel gate: per key channel, value tiles x 2).
 int state_dot_parts(const Problem& p);
 
 // Lays the workspace out from `base` (NULL: sizes only); returns its byte size.

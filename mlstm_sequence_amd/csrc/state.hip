@@ -47,7 +47,9 @@
 // chunk kl of the walk is chunk nc-1-kl; the partial last chunk comes first.
 // Where it stores D_m it also forms the Frobenius product with the forward
 // state C_m of the same slot (the gate gradients' boundary coupling), as one
-// partial per wavefront: [B*H][nc-1][tiles][waves].
+// partial per wavefront: [B*H][nc-1][tiles][waves]; for the per-channel gate
+// one per key channel (the row dot of D_m and C_m in that channel),
+// [B*H][nc-1][d_qk][value tiles x 2].
 #include <algorithm>
 #include <cstdlib>
 
@@ -114,7 +116,6 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
     constexpr int WC = NWS / 2;                        // waves along the key columns
     constexpr int MV = TV / 64, MC = TC / WC / 32;     // 32x32 accumulators per wave along value / key
     static_assert(MC >= 1, "tile too narrow for the waves");
-    static_assert(!REV || GATE != kGla, "the reverse walk covers the per-step gates only");
 
     const int ntv = dhv / TV, ntk = dqk / TC;
     const int blk = xcd_remap(blockIdx.x, gridDim.x);
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
                 const float* gr = g + (bh * nc + kc) * (size_t)dqk + c0 + c;
                 for (int e4 = 0; e4 < VEC / 4; ++e4) {
                     pf.ga[u][e4] = *reinterpret_cast<const f32x4*>(ar + 4 * e4);
-                    pf.gg[u][e4] = *reinterpret_cast<const f32x4*>(gr + 4 * e4);
+                    if (!REV) pf.gg[u][e4] = *reinterpret_cast<const f32x4*>(gr + 4 * e4);
                 }
             }
         }
@@ -203,7 +204,8 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
                 float x = pf.k[u].get(e);
-                if (GATE == kGla) x *= exp2_fast((pf.gg[u][e / 4][e % 4] - pf.ga[u][e / 4][e % 4]) * kLog2e);
+                if (GATE == kGla && REV) x *= exp2_fast(pf.ga[u][e / 4][e % 4] * kLog2e);
+                else if (GATE == kGla) x *= exp2_fast((pf.gg[u][e / 4][e % 4] - pf.ga[u][e / 4][e % 4]) * kLog2e);
                 else x *= ws;
                 kw.set(e, live ? x : 0.0f);
             }
@@ -265,9 +267,24 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
                 float e;
                 if (GATE == kSig) e = exp2_fast(gk * kLog2e);
                 else if (GATE == kScalar) e = exp2_fast((float)min(L, T_ - chunk(kc) * L) * lg2);
-                else e = exp2_fast(g[(bh * nc + kc) * dqk + c0 + cw + 32 * mc + i32] * kLog2e);
+                else e = exp2_fast(g[(bh * nc + chunk(kc)) * dqk + c0 + cw + 32 * mc + i32] * kLog2e);
 #pragma unroll
                 for (int mv = 0; mv < MV; ++mv) acc[mv][mc] *= e;
+            }
+        }
+        // the forward state of the boundary this block ends (reverse walk):
+        // loaded now, used after the block's products
+        const bool dot_now = REV && xpart && last && wk.write_states && kc < nc - 1;
+        float cpre[MV][MC][16];
+        if (dot_now) {
+#pragma unroll
+            for (int mv = 0; mv < MV; ++mv) {
+                const float* src =
+                    cstates + ((bh * ns + (nc - 2 - kc)) * (size_t)dhv + v0 + vw + 32 * mv) * dqk + c0 + cw + i32;
+#pragma unroll
+                for (int mc = 0; mc < MC; ++mc)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) cpre[mv][mc][r] = src[(size_t)arow(r) * dqk + 32 * mc];
             }
         }
         // acc (value rows vw.., key columns cw..) += V^T (w.K) over this block
@@ -285,24 +302,37 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
         }
         if (last && wk.write_states && kc < nc - 1) {
             put_state(acc, REV ? nc - 2 - kc : kc + wk.soff);
-            if (REV && xpart) {
+            if (dot_now) {
                 // the coupling <D_m, C_m> across this chunk boundary: this
                 // wave's share, against the forward state stored in the
                 // same slot and layout
                 const int slot = nc - 2 - kc;
-                float x = 0.0f;
+                if constexpr (GATE == kGla) {
+                    // per key channel: [B*H][nc-1][d_qk][value tiles x 2 row groups]
+                    const int nvp = (dhv / TV) * 2, part = (tile / ntk) * 2 + w / WC;
 #pragma unroll
-                for (int mv = 0; mv < MV; ++mv) {
-                    const float* src =
-                        cstates + ((bh * ns + slot) * (size_t)dhv + v0 + vw + 32 * mv) * dqk + c0 + cw + i32;
+                    for (int mc = 0; mc < MC; ++mc) {
+                        float x = 0.0f;
 #pragma unroll
-                    for (int mc = 0; mc < MC; ++mc)
+                        for (int mv = 0; mv < MV; ++mv)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) x += acc[mv][mc][r] * src[(size_t)arow(r) * dqk + 32 * mc];
+                            for (int r = 0; r < 16; ++r) x += acc[mv][mc][r] * cpre[mv][mc][r];
+                        x += __shfl_xor(x, 32, 64);
+                        if (hh == 0)
+                            xpart[((bh * (nc - 1) + slot) * dqk + c0 + cw + 32 * mc + i32) * nvp + part] = x;
+                    }
+                } else {
+                    float x = 0.0f;
+#pragma unroll
+                    for (int mv = 0; mv < MV; ++mv)
+#pragma unroll
+                        for (int mc = 0; mc < MC; ++mc)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) x += acc[mv][mc][r] * cpre[mv][mc][r];
+#pragma unroll
+                    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+                    if (lane == 0) xpart[((bh * (nc - 1) + slot) * tiles + tile) * NWS + w] = x;
                 }
-#pragma unroll
-                for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-                if (lane == 0) xpart[((bh * (nc - 1) + slot) * tiles + tile) * NWS + w] = x;
             }
         }
         if (b == bend - 1 && wk.end && (wk.end_all || seg == wk.nseg - 1)) {
@@ -386,8 +416,7 @@ hipError_t launch_walk(const Problem& p, const T* k, const T* v, const float* fg
             static_cast<const float*>(ws.dot_partner), ws.dots);
         break;
     default:
-        if constexpr (REV) return hipErrorInvalidValue;
-        state_kernel<T, kGla, SB, TV, TC, NWS, false><<<blocks, threads, 0, stream>>>(
+        state_kernel<T, kGla, SB, TV, TC, NWS, REV><<<blocks, threads, 0, stream>>>(
             k, v, ws.a, ws.li, ws.g, fg, ws.states, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc,
             static_cast<const float*>(ws.dot_partner), ws.dots);
         break;
@@ -410,8 +439,7 @@ hipError_t launch_combine(const Problem& p, const float* fg, const Workspace& ws
                                                                       p.H, p.T, p.dqk, p.dhv, p.L, p.nc, P, cps);
         break;
     default:
-        if constexpr (REV) return hipErrorInvalidValue;
-        state_combine_kernel<kGla, false><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, ws.c0, ws.g, fg,
+        state_combine_kernel<kGla, REV><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, ws.c0, ws.g, fg,
                                                                      p.H, p.T, p.dqk, p.dhv, p.L, p.nc, P, cps);
         break;
     }
@@ -491,7 +519,9 @@ int state_segments_for(const Problem& p, long heads_tiles)
 
 int state_dot_parts(const Problem& p)
 {
-    if (p.bf16 && state_big_tiles(p)) return (p.dhv / 128) * (p.dqk / 128) * 8;
+    const bool big = p.bf16 && state_big_tiles(p);
+    if (p.gate == kGla) return (p.dhv / (big ? 128 : 64)) * 2;
+    if (big) return (p.dhv / 128) * (p.dqk / 128) * 8;
     return (p.dhv / 64) * (p.dqk / 64) * 4;
 }
 

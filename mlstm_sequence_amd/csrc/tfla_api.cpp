@@ -181,11 +181,13 @@ int run_path(const tfla::Problem& p, const void* q, const void* k, const void* v
 struct BwdWorkspace {
     tfla::Workspace fwd;
     float* dstates;   // [B,H,nc-1,d_hv,d_qk]
-    float* ar;        // [B,H,T] mLSTMsig
+    float* ar;        // [B,H,T] mLSTMsig, [B,H,T,d_qk] per-channel gate
     float* lr;        // [B,H,T] mLSTMsig
     float* dq_dots;   // [B,H,T][np]: q_t . dq_t per value tile of the dq kernel
+                      // (per-channel gate: np = d_qk per-element products)
     float* dk_dots;   // [B,H,T][np]: k_t . dk_t likewise
     float* xpart;     // [B,H,nc-1][nx]: partials of <D_k, C_k> across each chunk boundary
+                      // (per-channel gate: [B,H,nc-1,d_qk][nx])
     int np, nx;
 };
 
@@ -208,26 +210,24 @@ size_t bwd_layout(const tfla::Problem& p, BwdWorkspace* ws, char* base)
         return ptr;
     };
     ws->dstates = p.nc > 1 ? take(bh * (p.nc - 1) * p.dhv * p.dqk * 4) : nullptr;
-    const bool sig = p.gate == tfla::kSig;
-    ws->ar = sig ? take(bh * p.T * 4) : nullptr;
+    const bool sig = p.gate == tfla::kSig, gla = p.gate == tfla::kGla;
+    ws->ar = sig ? take(bh * p.T * 4) : gla ? take(bh * p.T * p.dqk * 4) : nullptr;
     ws->lr = sig ? take(bh * p.T * 4) : nullptr;
-    ws->np = p.dqk / tfla::intra_value_tile(grad_qk_problem(p));
+    ws->np = gla ? p.dqk : p.dqk / tfla::intra_value_tile(grad_qk_problem(p));
     ws->dq_dots = take(bh * p.T * ws->np * 4);
     ws->dk_dots = take(bh * p.T * ws->np * 4);
     ws->nx = tfla::state_dot_parts(p);
-    ws->xpart = p.nc > 1 ? take(bh * (p.nc - 1) * ws->nx * 4) : nullptr;
+    const size_t per_boundary = (size_t)ws->nx * (p.gate == tfla::kGla ? p.dqk : 1);
+    ws->xpart = p.nc > 1 ? take(bh * (p.nc - 1) * per_boundary * 4) : nullptr;
     return off;
 }
 
-// Shapes the backward pass is built for: per-step gates, and d_hv (the
-// width the dq and dk products contract) a power of two the intra kernel
-// is instantiated for.
+// Shapes the backward pass is built for: d_hv (the width the dq and dk
+// products contract) a power of two the intra kernel is instantiated for.
 int check_bwd_problem(int B, int H, int T, int d_qk, int d_hv, int L, int variant, tfla::Problem* p)
 {
     int rc = check_problem(B, H, T, d_qk, d_hv, L, variant, p);
     if (rc) return rc;
-    if (p->gate == tfla::kGla)
-        return fail(TFLA_ERR_UNSUPPORTED, "the backward pass covers TFLA_MLSTM_SIG and TFLA_SCALAR_DECAY");
     if (!(d_hv == 64 || d_hv == 128 || (p->bf16 && (d_hv == 256 || d_hv == 512))))
         return fail(TFLA_ERR_UNSUPPORTED, "backward: d_hv must be 64, 128, 256 or 512 (fp32 I/O: 64 or 128), got " +
                                               std::to_string(d_hv));
@@ -245,7 +245,7 @@ int run_bwd(const tfla::Problem& p, const void* q, const void* k, const void* v,
     if ((e = tfla::launch_state(p, k, v, fgate_pre, ws.fwd, stream)) != hipSuccess)
         return hip_fail(e, "state kernel launch");
     tfla::Workspace mirrored = ws.fwd;   // gate exponents of the mirrored chunks
-    if (p.gate == tfla::kSig) {
+    if (p.gate != tfla::kScalar) {
         if ((e = tfla::launch_gates_mirror(p, ws.fwd, ws.ar, ws.lr, stream)) != hipSuccess)
             return hip_fail(e, "mirrored gate kernel launch");
         mirrored.a = ws.ar;

@@ -196,7 +196,7 @@ def bwd(q=Q, k=K, v=V, ig=IG, fg=FG, dh=DH, dq=DQ, dk=DK, dv=DV, dig=DIG, dfg=DF
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(variant=GLA | BF16, ig=None, dig=None), UNSUPPORTED),   # per-channel gate: forward only
+    (dict(variant=GLA | BF16), INVALID),                          # per-channel gate: no input gate
     (dict(dhv=192), UNSUPPORTED), (dict(dhv=320), UNSUPPORTED),   # d_hv is contracted: powers of two
     (dict(variant=SIG, dhv=256), UNSUPPORTED),                    # fp32 I/O: d_hv <= 128
     (dict(dqk=96), UNSUPPORTED), (dict(Lc=32), UNSUPPORTED),
@@ -236,5 +236,10 @@ def test_bwd_workspace_bytes(L):
     assert tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16) == sig
     scal = tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SCALAR | BF16) + states + 2 * steps + X
     assert tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, dhv, Lc, SCALAR | BF16) == scal
-    assert tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, dhv, Lc, GLA | BF16) == 0
+    # per-channel gate: mirrored gate exponents and per-element products per key channel,
+    # coupling partials per key channel (value tiles x 2 row groups of 64x64 state tiles)
+    Xg = a256(B * H * (nc - 1) * dqk * (dhv // 64) * 2 * 4)
+    gla = (tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, GLA | BF16) + states + 3 * a256(B * H * T * dqk * 4)
+           + Xg)
+    assert tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, dhv, Lc, GLA | BF16) == gla
     assert tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, 192, Lc, SIG | BF16) == 0

@@ -19,7 +19,7 @@ from mlstm_sequence_amd import tfla
 
 pytestmark = pytest.mark.gpu
 
-SIG, SCAL = W.MLSTM_SIG, W.SCALAR
+SIG, SCAL, GLA = W.MLSTM_SIG, W.SCALAR, W.GLA
 F32, BF = torch.float32, torch.bfloat16
 NAMES = ["dq", "dk", "dv", "dig", "dfg"]
 
@@ -83,6 +83,10 @@ BWD_CASES = [
     (SCAL, BF, 1, 3, 333, 128, 128, 64),
     (SCAL, F32, 1, 2, 129, 64, 128, 128),
     (SCAL, BF, 2, 2, 600, 256, 512, 128),
+    (GLA, BF, 1, 2, 450, 256, 256, 64),        # per-channel gate: output-side decay in dq, dk
+    (GLA, F32, 1, 2, 200, 64, 128, 128),
+    (GLA, BF, 2, 1, 700, 128, 512, 256),       # 512-wide contraction, long chunks
+    (GLA, BF, 1, 1, 40, 64, 64, 64),           # one partial chunk
 ]
 
 
@@ -96,7 +100,7 @@ def test_backward_matches_oracle(variant, dtype, B, H, T, dqk, dhv, L):
 
 
 @pytest.mark.parametrize("segments", ["1", "2", "5"])
-@pytest.mark.parametrize("variant", [SIG, SCAL])
+@pytest.mark.parametrize("variant", [SIG, SCAL, GLA])
 def test_backward_segmented_walk(variant, segments, monkeypatch):
     """Forced segment counts of both state walks (the reverse walk's first
     segment holds the partial last chunk)."""
@@ -149,12 +153,13 @@ def test_backward_workspace_entry_matches_allocating_entry():
         assert torch.equal(x, y)
 
 
-def test_backward_rejects_gla_and_odd_widths():
-    wl, inp = case(W.GLA, 1, 1, 64, 64, 64, BF, seed=1)
+def test_backward_rejects_odd_widths():
+    wl, inp = case(SIG, 1, 1, 64, 64, 192, BF, seed=1)
     d = to_dev(inp)
     dh = torch.zeros_like(d["v"])
     out = [torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"])]
-    with pytest.raises(RuntimeError, match="unsupported|UNSUPPORTED|covers"):
-        tfla.tfla_bwd(d["q"], d["k"], d["v"], None, d["fgate_pre"], dh, *out, None, torch.empty_like(d["fgate_pre"]),
-                      1, 1, 64, 64, 64, 64, tfla.variant_of(tfla.GLA_KEY, BF))
+    with pytest.raises(RuntimeError, match="unsupported"):
+        tfla.tfla_bwd(d["q"], d["k"], d["v"], d["igate_pre"], d["fgate_pre"], dh, *out,
+                      torch.empty_like(d["igate_pre"]), torch.empty_like(d["fgate_pre"]),
+                      1, 1, 64, 64, 192, 64, tfla.variant_of(tfla.MLSTM_SIG, BF))
     assert tfla.tfla_bwd_workspace_bytes(1, 1, 64, 64, 192, 64, tfla.variant_of(tfla.MLSTM_SIG, BF)) == 0

@@ -3,7 +3,7 @@ the GPU runs the whole workload, the oracle's backward recurrence recomputes
 a sample of heads over their whole sequences, and those heads are compared
 element by element (tolerances of the forward pass).  The per-head
 scalar-decay gradient sums over batches, so its sample takes every batch of
-the sampled heads.  The per-channel gate has no backward pass."""
+the sampled heads."""
 import numpy as np
 import pytest
 import torch
@@ -20,6 +20,7 @@ CASES = {
     1: (64, [(0, 0)]),
     2: (64, [(b, 17) for b in range(8)]),
     3: (256, [(0, 0), (3, 7)]),
+    4: (64, [(0, 0), (7, 3)]),
     5: (256, [(0, 5)]),
 }
 
