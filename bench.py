@@ -145,7 +145,7 @@ def run_gpu_bwd(wl, L, steps, warmup, inputs_dev, dh):
 
     q, k, v = inputs_dev["q"], inputs_dev["k"], inputs_dev["v"]
     ig, fg = inputs_dev["igate_pre"], inputs_dev["fgate_pre"]
-    gate = {0: tfla.MLSTM_SIG, 1: tfla.SCALAR_DECAY}[wl.variant]
+    gate = {0: tfla.MLSTM_SIG, 1: tfla.SCALAR_DECAY, 2: tfla.GLA_KEY}[wl.variant]
     var = tfla.variant_of(gate, q.dtype)
     nws = tfla.tfla_bwd_workspace_bytes(wl.B, wl.H, wl.T, wl.dqk, wl.dhv, L, var)
     ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=q.device)
@@ -337,7 +337,7 @@ def main():
         }
     # The backward pass (tfla_bwd) on the same workload, every swept chunk
     # size: context beside the forward metric, not part of `value`.
-    if not args.no_backward and wl.variant != W.GLA:
+    if not args.no_backward:
         dh = W.upstream_grad(wl.B, wl.H, wl.T, wl.dhv, wl.dtype, seed=wl.seed + 1).cuda()
         bwd = {}
         for L in sweep:

@@ -170,37 +170,45 @@ __global__ __launch_bounds__(256) void grad_gla_kernel(const float* __restrict__
     }
 }
 
-// Fixed per-head decay: one workgroup per head, over every batch.
+// Fixed per-head decay: one workgroup per (batch, head) sums its part of
+// dL/dlog gamma in double; a second kernel adds the batches of each head in
+// a fixed order.
 __global__ __launch_bounds__(kScanThreads) void grad_scalar_kernel(const float* __restrict__ dq_dots,
                                                                   const float* __restrict__ dk_dots, int np,
                                                                   const float* __restrict__ xpart, int nx,
-                                                                  float scale, const float* __restrict__ fg,
-                                                                  float* __restrict__ dfg, int B, int H, int T_,
-                                                                  int L, int nc)
+                                                                  float scale, double* __restrict__ part_out,
+                                                                  int T_, int L, int nc)
 {
     __shared__ double part[kScanThreads];
-    const int h = blockIdx.x, tid = threadIdx.x;
+    const size_t bh = blockIdx.x;
+    const int tid = threadIdx.x;
     const double centre = 0.5 * (L - 1);
     double s = 0.0, r, kd;
-    for (int b = 0; b < B; ++b) {
-        const size_t bh = (size_t)b * H + h;
-        for (int t = tid; t < T_; t += kScanThreads) {
-            step_dots(dq_dots, dk_dots, bh * T_ + t, np, r, kd);
-            s += ((double)(t % L) - centre) * r;
-        }
-        for (int k = tid; k < nc - 1; k += kScanThreads) s += (double)L * coupling(xpart, bh * (nc - 1) + k, nx, scale);
+    for (int t = tid; t < T_; t += kScanThreads) {
+        step_dots(dq_dots, dk_dots, bh * T_ + t, np, r, kd);
+        s += ((double)(t % L) - centre) * r;
     }
+    for (int k = tid; k < nc - 1; k += kScanThreads) s += (double)L * coupling(xpart, bh * (nc - 1) + k, nx, scale);
     part[tid] = s;
     __syncthreads();
     for (int d = kScanThreads / 2; d >= 1; d >>= 1) {
         if (tid < d) part[tid] += part[tid + d];
         __syncthreads();
     }
-    if (tid == 0) {
-        const float x = fg[h];
-        const bool floored = log_sigmoid(x) < kLogForgetFloor;
-        dfg[h] = floored ? 0.0f : (float)(part[0] / (1.0 + exp((double)x)));
-    }
+    if (tid == 0) part_out[bh] = part[0];
+}
+
+__global__ __launch_bounds__(64) void grad_scalar_final_kernel(const double* __restrict__ part,
+                                                              const float* __restrict__ fg,
+                                                              float* __restrict__ dfg, int B, int H)
+{
+    const int h = blockIdx.x * 64 + threadIdx.x;
+    if (h >= H) return;
+    double s = 0.0;
+    for (int b = 0; b < B; ++b) s += part[(size_t)b * H + h];
+    const float x = fg[h];
+    const bool floored = log_sigmoid(x) < kLogForgetFloor;
+    dfg[h] = floored ? 0.0f : (float)(s / (1.0 + exp((double)x)));
 }
 
 }  // namespace
@@ -219,7 +227,7 @@ hipError_t launch_gates_mirror(const Problem& p, const Workspace& ws, float* ar,
 
 hipError_t launch_gate_grads(const Problem& p, const float* xpart, int nx, const float* dq_dots,
                              const float* dk_dots, int np, const float* igate_pre, const float* fgate_pre,
-                             float* dig, float* dfg, hipStream_t stream)
+                             float* dig, float* dfg, double* head_part, hipStream_t stream)
 {
     const float scale = 1.0f / sqrtf((float)p.dqk);
     if (p.gate == kGla)
@@ -228,9 +236,11 @@ hipError_t launch_gate_grads(const Problem& p, const float* xpart, int nx, const
     else if (p.gate == kSig)
         grad_scan_sig_kernel<<<p.B * p.H * p.nc, kScanThreads, 0, stream>>>(
             dq_dots, dk_dots, np, xpart, nx, scale, igate_pre, fgate_pre, dig, dfg, p.T, p.L, p.nc);
-    else
-        grad_scalar_kernel<<<p.H, kScanThreads, 0, stream>>>(dq_dots, dk_dots, np, xpart, nx, scale, fgate_pre, dfg,
-                                                             p.B, p.H, p.T, p.L, p.nc);
+    else {
+        grad_scalar_kernel<<<p.B * p.H, kScanThreads, 0, stream>>>(dq_dots, dk_dots, np, xpart, nx, scale,
+                                                                   head_part, p.T, p.L, p.nc);
+        grad_scalar_final_kernel<<<(p.H + 63) / 64, 64, 0, stream>>>(head_part, fgate_pre, dfg, p.B, p.H);
+    }
     return hipGetLastError();
 }
 

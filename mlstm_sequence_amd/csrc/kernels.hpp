@@ -91,10 +91,10 @@ hipError_t launch_intra_dv(const Problem& p, const void* q, const void* k, const
 // mode (mLSTMsig), and the input / forget gate gradients from the dq and dk
 // kernels' row partials (q_t.dq_t and k_t.dk_t, np per step, [B,H,T][np])
 // and the reverse walk's partials of <D_m, C_m> (nx per boundary,
-// [B,H,nc-1][nx]).
+// [B,H,nc-1][nx]); head_part: [B,H] double scratch of the fixed decay.
 hipError_t launch_gates_mirror(const Problem& p, const Workspace& ws, float* ar, float* lr, hipStream_t stream);
 hipError_t launch_gate_grads(const Problem& p, const float* xpart, int nx, const float* dq_dots,
                              const float* dk_dots, int np, const float* igate_pre, const float* fgate_pre,
-                             float* dig, float* dfg, hipStream_t stream);
+                             float* dig, float* dfg, double* head_part, hipStream_t stream);
 
 }  // namespace tfla

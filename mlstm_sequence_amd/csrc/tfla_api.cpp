@@ -188,6 +188,7 @@ struct BwdWorkspace {
     float* dk_dots;   // [B,H,T][np]: k_t . dk_t likewise
     float* xpart;     // [B,H,nc-1][nx]: partials of <D_k, C_k> across each chunk boundary
                       // (per-channel gate: [B,H,nc-1,d_qk][nx])
+    double* head_part;  // [B,H]: per-(batch, head) part of the fixed decay's gradient
     int np, nx;
 };
 
@@ -219,6 +220,7 @@ size_t bwd_layout(const tfla::Problem& p, BwdWorkspace* ws, char* base)
     ws->nx = tfla::state_dot_parts(p);
     const size_t per_boundary = (size_t)ws->nx * (p.gate == tfla::kGla ? p.dqk : 1);
     ws->xpart = p.nc > 1 ? take(bh * (p.nc - 1) * per_boundary * 4) : nullptr;
+    ws->head_part = p.gate == tfla::kScalar ? reinterpret_cast<double*>(take(bh * 8)) : nullptr;
     return off;
 }
 
@@ -276,7 +278,7 @@ int run_bwd(const tfla::Problem& p, const void* q, const void* k, const void* v,
     if ((e = tfla::launch_intra_dv(p, k, q, dh, fgate_pre, mirrored, dv, scale, stream)) != hipSuccess)
         return hip_fail(e, "dv kernel launch");
     if ((e = tfla::launch_gate_grads(p, ws.xpart, ws.nx, ws.dq_dots, ws.dk_dots, ws.np, igate_pre, fgate_pre, dig,
-                                     dfg, stream)) != hipSuccess)
+                                     dfg, ws.head_part, stream)) != hipSuccess)
         return hip_fail(e, "gate gradient kernel launch");
     return TFLA_OK;
 }

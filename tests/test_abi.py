@@ -234,7 +234,7 @@ def test_bwd_workspace_bytes(L):
     X = a256(B * H * (nc - 1) * (dhv // 64) * (dqk // 64) * 4 * 4)
     sig = tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16) + states + 4 * steps + X
     assert tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16) == sig
-    scal = tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SCALAR | BF16) + states + 2 * steps + X
+    scal = tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SCALAR | BF16) + states + 2 * steps + X + a256(B * H * 8)
     assert tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, dhv, Lc, SCALAR | BF16) == scal
     # per-channel gate: mirrored gate exponents and per-element products per key channel,
     # coupling partials per key channel (value tiles x 2 row groups of 64x64 state tiles)
