@@ -154,19 +154,29 @@ def run_gpu_bwd(wl, L, steps, warmup, inputs_dev, dh):
     dfg = torch.empty_like(fg)
     args = (q, k, v, ig, fg, dh, dq, dk, dv, dig, dfg, wl.B, wl.H, wl.T, wl.dqk, wl.dhv, L, var, ws, nws)
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        tfla.tfla_bwd(*args)
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(steps):
-        tfla.tfla_bwd(*args)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
-    del ws, dq, dk, dv, dig, dfg
-    return ms
+
+    def timed(call):
+        for _ in range(warmup):
+            call()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(steps):
+            call()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    ms = timed(lambda: tfla.tfla_bwd(*args))
+    # training use: the forward pass ran on this workspace, and the backward
+    # reuses its gate sums and states (TFLA_BWD_REUSE_FWD)
+    h = torch.empty_like(v)
+    tfla.tfla_fwd_ws(q, k, v, ig, fg, h, wl.B, wl.H, wl.T, wl.dqk, wl.dhv, L, var, ws, nws)
+    reuse = args[:17] + (var | tfla.BWD_REUSE_FWD, ws, nws)
+    ms_reuse = timed(lambda: tfla.tfla_bwd(*reuse))
+    del ws, dq, dk, dv, dig, dfg, h
+    return ms, ms_reuse
 
 
 # --------------------------------------------------------------------------- CPU baseline
@@ -341,12 +351,13 @@ def main():
         dh = W.upstream_grad(wl.B, wl.H, wl.T, wl.dhv, wl.dtype, seed=wl.seed + 1).cuda()
         bwd = {}
         for L in sweep:
-            ms = run_gpu_bwd(wl, L, max(1, args.steps // 2), max(1, args.warmup // 2), dev, dh)
+            ms, ms_reuse = run_gpu_bwd(wl, L, max(1, args.steps // 2), max(1, args.warmup // 2), dev, dh)
             fl = backward_flops(wl, L)
             bwd[L] = {"ms_per_step": ms, "tokens_per_s": wl.B * wl.T / (ms * 1e-3),
-                      "mfma_frac": fl / (ms * 1e-3) / PEAK_BF16, "algorithmic_flops": fl}
+                      "mfma_frac": fl / (ms * 1e-3) / PEAK_BF16, "algorithmic_flops": fl,
+                      "ms_per_step_reusing_forward_states": ms_reuse}
             log(f"backward L={L}: {ms:.3f} ms/step, {bwd[L]['tokens_per_s']:.4g} tokens/s, "
-                f"{bwd[L]['mfma_frac'] * 100:.2f}% of bf16 peak")
+                f"{bwd[L]['mfma_frac'] * 100:.2f}% of bf16 peak; {ms_reuse:.3f} ms reusing the forward's states")
         Lb = min(bwd, key=lambda L: bwd[L]["ms_per_step"])
         out["backward"] = dict(bwd[Lb], L=Lb, sweep={str(L): x for L, x in bwd.items()})
         del dh

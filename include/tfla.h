@@ -48,7 +48,9 @@ enum tfla_variant {
     TFLA_MLSTM_SIG = 0,     /* i = sigmoid(igate_pre[t]), f = sigmoid(fgate_pre[t])       */
     TFLA_SCALAR_DECAY = 1,  /* i = 1, f = sigmoid(fgate_pre[h]) fixed per head            */
     TFLA_GLA_KEY = 2,       /* i = 1, f_{t,c} = exp(logsigmoid(fgate_pre[t,c]) / 16)      */
-    TFLA_IO_BF16 = 0x100    /* q, k, v, h are bf16; without the flag they are fp32        */
+    TFLA_IO_BF16 = 0x100,   /* q, k, v, h are bf16; without the flag they are fp32        */
+    TFLA_BWD_REUSE_FWD = 0x200  /* tfla_bwd only: reuse the forward pass's gate sums and
+                                   states left in the workspace (see tfla_bwd)              */
 };
 
 enum tfla_status {
@@ -191,7 +193,14 @@ int tfla_fwd_recurrent(const void* q, const void* k, const void* v,
  *             [B,H,T,d_qk] (TFLA_GLA_KEY).
  *   Outputs are fully overwritten and must not overlap each other or an
  *   input.
- *   variant   any gate kind | TFLA_IO_BF16, as for tfla_fwd.
+ *   variant   any gate kind | TFLA_IO_BF16, as for tfla_fwd, optionally
+ *             | TFLA_BWD_REUSE_FWD: the caller asserts that `workspace` (which
+ *             must then be given) was last used by a completed tfla_fwd_ws
+ *             call with the same inputs, shape, chunk size and variant, and
+ *             nothing has written its first tfla_workspace_bytes(...) bytes
+ *             since; the gate prefix sums and the states C_k found there are
+ *             used as they are, skipping their recomputation.  Results are
+ *             then bitwise those without the flag.
  *   d_qk      as for tfla_fwd; d_hv 64, 128, 256 or 512 (fp32 I/O: 64 or
  *             128), since the dq and dk products contract over it.
  *   workspace caller-owned device workspace of at least

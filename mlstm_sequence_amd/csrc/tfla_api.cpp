@@ -228,7 +228,7 @@ size_t bwd_layout(const tfla::Problem& p, BwdWorkspace* ws, char* base)
 // products contract) a power of two the intra kernel is instantiated for.
 int check_bwd_problem(int B, int H, int T, int d_qk, int d_hv, int L, int variant, tfla::Problem* p)
 {
-    int rc = check_problem(B, H, T, d_qk, d_hv, L, variant, p);
+    int rc = check_problem(B, H, T, d_qk, d_hv, L, variant & ~TFLA_BWD_REUSE_FWD, p);
     if (rc) return rc;
     if (!(d_hv == 64 || d_hv == 128 || (p->bf16 && (d_hv == 256 || d_hv == 512))))
         return fail(TFLA_ERR_UNSUPPORTED, "backward: d_hv must be 64, 128, 256 or 512 (fp32 I/O: 64 or 128), got " +
@@ -238,14 +238,17 @@ int check_bwd_problem(int B, int H, int T, int d_qk, int d_hv, int L, int varian
 
 int run_bwd(const tfla::Problem& p, const void* q, const void* k, const void* v, const float* igate_pre,
             const float* fgate_pre, const void* dh, void* dq, void* dk, void* dv, float* dig, float* dfg,
-            const BwdWorkspace& ws, hipStream_t stream)
+            const BwdWorkspace& ws, bool reuse_fwd, hipStream_t stream)
 {
     const float scale = 1.0f / sqrtf((float)p.dqk);
-    hipError_t e = tfla::launch_gates(p, igate_pre, fgate_pre, ws.fwd, stream);
-    if (e != hipSuccess) return hip_fail(e, "gate kernel launch");
-    // forward states C_1..C_{nc-1}, [d_hv][d_qk] each
-    if ((e = tfla::launch_state(p, k, v, fgate_pre, ws.fwd, stream)) != hipSuccess)
-        return hip_fail(e, "state kernel launch");
+    hipError_t e;
+    if (!reuse_fwd) {
+        if ((e = tfla::launch_gates(p, igate_pre, fgate_pre, ws.fwd, stream)) != hipSuccess)
+            return hip_fail(e, "gate kernel launch");
+        // forward states C_1..C_{nc-1}, [d_hv][d_qk] each
+        if ((e = tfla::launch_state(p, k, v, fgate_pre, ws.fwd, stream)) != hipSuccess)
+            return hip_fail(e, "state kernel launch");
+    }
     tfla::Workspace mirrored = ws.fwd;   // gate exponents of the mirrored chunks
     if (p.gate != tfla::kScalar) {
         if ((e = tfla::launch_gates_mirror(p, ws.fwd, ws.ar, ws.lr, stream)) != hipSuccess)
@@ -552,6 +555,9 @@ int tfla_bwd(const void* q, const void* k, const void* v, const float* igate_pre
     const size_t need = bwd_layout(p, &ws, nullptr);
     hipStream_t s = static_cast<hipStream_t>(stream);
     void* base = workspace;
+    const bool reuse_fwd = (variant & TFLA_BWD_REUSE_FWD) != 0;
+    if (reuse_fwd && !workspace)
+        return fail(TFLA_ERR_INVALID_ARG, "TFLA_BWD_REUSE_FWD needs the forward pass's workspace");
     if (workspace) {
         if (!aligned(workspace, 256)) return fail(TFLA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
         if (workspace_bytes < need)
@@ -568,7 +574,7 @@ int tfla_bwd(const void* q, const void* k, const void* v, const float* igate_pre
         }
     }
     bwd_layout(p, &ws, static_cast<char*>(base));
-    rc = run_bwd(p, q, k, v, igate_pre, fgate_pre, dh, dq, dk, dv, dig, dfg, ws, s);
+    rc = run_bwd(p, q, k, v, igate_pre, fgate_pre, dh, dq, dk, dv, dig, dfg, ws, reuse_fwd, s);
     if (!workspace && base) {
         hipError_t e = hipFreeAsync(base, s);
         if (e != hipSuccess && rc == TFLA_OK) rc = hip_fail(e, "workspace free");

@@ -214,6 +214,14 @@ def test_bwd_rejects_bad_arguments(L, kw, code):
     assert tfla.tfla_last_error()
 
 
+def test_bwd_reuse_needs_the_forward_workspace(L):
+    assert bwd(variant=SIG | BF16 | 0x200) == INVALID
+    assert "workspace" in tfla.tfla_last_error()
+    assert bwd(variant=SIG | BF16 | 0x400) == INVALID          # unknown flag
+    n = tfla.tfla_bwd_workspace_bytes(2, 3, 300, 128, 256, 64, SIG | BF16)
+    assert n > 0 and tfla.tfla_bwd_workspace_bytes(2, 3, 300, 128, 256, 64, SIG | BF16 | 0x200) == n
+
+
 def test_bwd_injected_allocation_failure(L, monkeypatch):
     monkeypatch.setenv("TFLA_FAULT", "alloc")
     assert bwd() == OOM

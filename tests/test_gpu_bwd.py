@@ -163,3 +163,36 @@ def test_backward_rejects_odd_widths():
                       torch.empty_like(d["igate_pre"]), torch.empty_like(d["fgate_pre"]),
                       1, 1, 64, 64, 192, 64, tfla.variant_of(tfla.MLSTM_SIG, BF))
     assert tfla.tfla_bwd_workspace_bytes(1, 1, 64, 64, 192, 64, tfla.variant_of(tfla.MLSTM_SIG, BF)) == 0
+
+
+@pytest.mark.parametrize("variant,dtype,T,L,segments", [
+    (SIG, BF, 1100, 128, None), (SCAL, F32, 333, 64, None), (GLA, BF, 530, 64, None), (SIG, BF, 64 * 11 + 29, 64, "3"),
+])
+def test_backward_reusing_forward_workspace(variant, dtype, T, L, segments, monkeypatch):
+    """tfla_fwd_ws leaves its gate sums and states in the workspace; tfla_bwd
+    with TFLA_BWD_REUSE_FWD on that workspace skips recomputing them and
+    returns bitwise the gradients of the recomputing call."""
+    if segments:
+        monkeypatch.setenv("TFLA_STATE_SEGMENTS", segments)
+    B, H, dqk, dhv = 1, 2, 64, 128
+    wl, inp = case(variant, B, H, T, dqk, dhv, dtype, seed=T + variant)
+    dh = W.upstream_grad(B, H, T, dhv, dtype, seed=T + 1)
+    ref = gpu_bwd(inp, dh, variant, L, workspace=True)
+    d = to_dev(inp)
+    var = tfla.variant_of(GATE[variant], dtype)
+    nws = tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, dhv, L, var)
+    assert nws >= tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, L, var)
+    ws = torch.full((nws,), 0xFF, dtype=torch.uint8, device="cuda")   # NaN bit patterns until written
+    h = torch.empty_like(d["v"])
+    tfla.tfla_fwd_ws(d["q"], d["k"], d["v"], d["igate_pre"], d["fgate_pre"], h, B, H, T, dqk, dhv, L, var, ws, nws)
+    out = [torch.full_like(d["q"], float("nan")), torch.full_like(d["k"], float("nan")),
+           torch.full_like(d["v"], float("nan")),
+           None if d["igate_pre"] is None else torch.full_like(d["igate_pre"], float("nan")),
+           torch.full_like(d["fgate_pre"], float("nan"))]
+    for _ in range(2):   # the backward leaves the forward's part of the workspace intact
+        tfla.tfla_bwd(d["q"], d["k"], d["v"], d["igate_pre"], d["fgate_pre"], dh.cuda(), *out, B, H, T, dqk, dhv, L,
+                      var | tfla.BWD_REUSE_FWD, ws, nws)
+        torch.cuda.synchronize()
+        for name, x, y in zip(NAMES, out, ref):
+            if y is not None:
+                assert torch.equal(x, y), name
