@@ -90,7 +90,7 @@ def backward_flops(wl, L):
 
 
 # --------------------------------------------------------------------------- GPU timing
-def run_gpu(wl, L, steps, warmup, inputs_dev):
+def run_gpu(wl, L, steps, warmup, inputs_dev, cold_calls=0):
     import torch
     from mlstm_sequence_amd import tfla
 
@@ -127,6 +127,23 @@ def run_gpu(wl, L, steps, warmup, inputs_dev):
     wall = time.perf_counter() - t0
 
     ms = start.elapsed_time(end) / steps
+    cold = None
+    if cold_calls:
+        # cold caches: a 1 GiB write between calls evicts the 8 x 4 MB L2 and
+        # the 256 MB last-level cache; each call timed alone
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=q.device)
+        times = []
+        for _ in range(cold_calls):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            tfla.tfla_fwd_ws(*args)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        times.sort()
+        cold = {"median_ms": times[len(times) // 2], "min_ms": times[0], "calls": cold_calls, "flush_bytes": 1 << 30}
+        del flush
     per = {"gates": 0.0, "state": 0.0, "intra": 0.0}
     for evs in marks:
         per["gates"] += evs[0].elapsed_time(evs[1])
@@ -134,7 +151,7 @@ def run_gpu(wl, L, steps, warmup, inputs_dev):
         per["intra"] += evs[2].elapsed_time(evs[3])
     per = {kname: t / steps for kname, t in per.items()}
     del ws, h
-    return ms, wall / steps * 1e3, per
+    return ms, wall / steps * 1e3, per, cold
 
 
 def run_gpu_bwd(wl, L, steps, warmup, inputs_dev, dh):
@@ -200,8 +217,14 @@ def cpu_baseline(wl, target_s=15.0):
     Tp = min(wl.T, (Tp // 256) * 256 or 256)
     dt = run(Tp) if Tp != 256 else t_cal
     threads = oracle.threads()
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": wl.B * Tp / dt, "unit": "tokens/s", "cores": min(threads, wl.B * wl.H),
-            "kind": "oracle", "seconds": round(dt, 3), "host_threads": threads,
+            "kind": "oracle", "seconds": round(dt, 3), "host_threads": threads, "cpu_model": model,
             "sample": f"all {wl.B * wl.H} (b,h) heads of the workload, first {Tp} of {wl.T} steps "
                       f"(seed-identical inputs); OpenMP over heads, {min(threads, wl.B * wl.H)} threads busy"}
 
@@ -284,11 +307,11 @@ def main():
 
     results = {}
     for L in sweep:
-        ms, wall_ms, per = run_gpu(wl, L, args.steps, args.warmup, dev)
+        ms, wall_ms, per, cold = run_gpu(wl, L, args.steps, args.warmup, dev, cold_calls=10)
         tps = wl.B * wl.T / (ms * 1e-3)
         fl = total_flops(wl, L)
         results[L] = {"ms": ms, "wall_ms": wall_ms, "per": per, "tokens_per_s": tps,
-                      "mfma_frac": fl / (ms * 1e-3) / PEAK_BF16}
+                      "mfma_frac": fl / (ms * 1e-3) / PEAK_BF16, "cold": cold}
         log(f"L={L}: {ms:.3f} ms/step, {tps:.4g} tokens/s, {results[L]['mfma_frac'] * 100:.2f}% of bf16 peak "
             f"(gates {per['gates']:.3f} ms, state {per['state']:.3f} ms, intra {per['intra']:.3f} ms)")
 
@@ -332,7 +355,9 @@ def main():
         "roofline": roof,
         "kernels_ms": r["per"],
         "sweep": {str(L): {"tokens_per_s": x["tokens_per_s"], "ms_per_step": x["ms"],
-                           "mfma_frac": x["mfma_frac"], "kernels_ms": x["per"]} for L, x in results.items()},
+                           "mfma_frac": x["mfma_frac"], "kernels_ms": x["per"], "cold_cache": x["cold"]}
+                  for L, x in results.items()},
+        "cold_cache": r["cold"],
     }
     # Chunk-size ablation (limit_chunk vs xl_chunk, TFLA abstract and summary):
     # at L = 64 every chunk is a single 64-step key/value tile, i.e. the chunk

@@ -58,7 +58,7 @@ namespace {
 
 template <typename T, int DQK, int BV, int CW> struct IntraLds {
     static constexpr int kpad = 16 / sizeof(T);   // K / C^T rows: stride = 4 banks mod 32
-    static constexpr int vpad = 32 / sizeof(T);   // V rows: stride = 8 banks mod 32 (transpose reads)
+    static constexpr int vpad = 64 / sizeof(T);   // V rows: stride = 16 banks mod 64 (transpose reads)
     union {
         struct {
             T ks[64][DQK + kpad];   // K tile [step][channel]

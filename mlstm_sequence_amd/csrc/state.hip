@@ -79,7 +79,10 @@ struct StateWalk {
 // in a 2 x (NWS/2) grid, each owning a (TV/2) x (2 TC/NWS) piece as 32x32
 // accumulators.
 template <typename T, int SB, int TV, int TC> struct StateLds {
-    static constexpr int pad = 32 / sizeof(T);   // row stride = 8 banks mod 32 (transpose reads)
+    // row stride = 16 banks mod 64: the 32 lanes of one transpose-read phase
+    // (4 rows x 64 B) land on distinct banks (LDS bank conflicts 37.5% -> 0%
+    // by counter; 256-step blocks then fill the 160 KB exactly)
+    static constexpr int pad = 64 / sizeof(T);
     T vs[SB][TV + pad];   // V block [step][value]
     T ks[SB][TC + pad];   // w.K block [step][key channel]
 };
