@@ -1,0 +1,49 @@
+"""The benchmark's algorithmic work model against the closed form it
+implements (host logic, no GPU)."""
+import pytest
+
+import bench
+import workloads as W
+
+
+def f_alg(B, H, T, L, dqk, dhv):
+    """Chunkwise algorithmic flops when L divides T: the state update and the
+    inter term (2 d_qk d_hv each per step of the T - L steps that feed or read
+    a materialised state) and the causal QK^T and PV (L(L+1)/2 pairs per
+    chunk, 2 (d_qk + d_hv) flops per pair)."""
+    return B * H * (4 * (T - L) * dqk * dhv + T * (L + 1) * (dqk + dhv))
+
+
+@pytest.mark.parametrize("c", sorted(W.WORKLOADS))
+def test_forward_flops_match_closed_form(c):
+    wl = W.WORKLOADS[c]
+    for L in wl.chunk_sizes:
+        assert bench.total_flops(wl, L) == f_alg(wl.B, wl.H, wl.T, L, wl.dqk, wl.dhv)
+
+
+def test_forward_flops_ragged_tail():
+    wl = W.WORKLOADS[3].with_(T=1000)
+    n = [256, 256, 256, 232]
+    want = wl.B * wl.H * (2 * wl.dqk * wl.dhv * (sum(n[:-1]) + sum(n[1:]))
+                          + sum(m * (m + 1) * (wl.dqk + wl.dhv) for m in n))
+    assert bench.total_flops(wl, 256) == want
+
+
+def test_backward_flops():
+    wl = W.WORKLOADS[3]
+    L = 256
+    # two state walks + three inter products (2 d_qk d_hv per step each) and three causal products
+    want = wl.B * wl.H * (5 * 2 * (wl.T - L) * wl.dqk * wl.dhv + 3 * wl.T * (L + 1) * (wl.dqk + wl.dhv))
+    assert bench.backward_flops(wl, L) == want
+
+
+def test_intra_bytes_are_compulsory_io_plus_states():
+    wl = W.WORKLOADS[3]
+    L = 256
+    m = bench.kernel_model(wl, L)
+    bh = wl.B * wl.H
+    nc = wl.T // L
+    io = bh * wl.T * (2 * wl.dqk + 2 * wl.dhv) * 2          # q, k, v in, h out (bf16)
+    states = bh * (nc - 1) * wl.dqk * wl.dhv * 4            # fp32 states read once
+    gates = bh * wl.T * 8                                   # a and li
+    assert m["intra"]["bytes"] == io + states + gates

@@ -196,3 +196,26 @@ def test_backward_reusing_forward_workspace(variant, dtype, T, L, segments, monk
         for name, x, y in zip(NAMES, out, ref):
             if y is not None:
                 assert torch.equal(x, y), name
+
+
+@pytest.mark.parametrize("variant", [SIG, SCAL, GLA])
+@pytest.mark.parametrize("T,L", [(1, 64), (64, 64), (65, 64), (257, 128), (1024, 1024)])
+def test_backward_sequence_edges(variant, T, L):
+    """One step, exactly one chunk, one step into a second chunk, a one-row
+    tail past several chunks, one whole 1024-step chunk."""
+    B, H, dqk, dhv = 1, 1, 64, 64
+    wl, inp = case(variant, B, H, T, dqk, dhv, F32, seed=T * 3 + variant)
+    dh = W.upstream_grad(B, H, T, dhv, F32, seed=T + 2)
+    print(f"bwd edge variant={variant} T={T} L={L}", flush=True)
+    check(gpu_bwd(inp, dh, variant, L), oracle_bwd(inp, dh, variant), F32, f"T={T}")
+
+
+def test_backward_is_deterministic():
+    """No atomics: two calls give bitwise the same gradients."""
+    B, H, T, dqk, dhv, L = 2, 2, 700, 128, 256, 128
+    wl, inp = case(SIG, B, H, T, dqk, dhv, BF, seed=21)
+    dh = W.upstream_grad(B, H, T, dhv, BF, seed=22)
+    a = gpu_bwd(inp, dh, SIG, L)
+    b = gpu_bwd(inp, dh, SIG, L)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
