@@ -99,7 +99,8 @@ size_t tfla_workspace_bytes(int B, int H, int T, int d_qk, int d_hv, int L, int 
 
 /* tfla_fwd with a caller-owned device workspace of at least
  * tfla_workspace_bytes(...) bytes, 256-byte aligned; no allocation.  The
- * workspace must not be used by other work while this call's kernels run. */
+ * workspace must not be used by other work while this call's kernels run,
+ * and must not overlap a tensor argument (checked: TFLA_ERR_INVALID_ARG). */
 int tfla_fwd_ws(const void* q, const void* k, const void* v,
                 const float* igate_pre, const float* fgate_pre, void* h,
                 int B, int H, int T, int d_qk, int d_hv, int L, int variant,
@@ -129,9 +130,10 @@ int tfla_fwd_ws_marked(const void* q, const void* k, const void* v,
  *             pointer as c0 (the state is then updated in place); must not
  *             otherwise overlap c0, an input or h.
  *   workspace caller-owned device workspace of at least
- *             tfla_state_workspace_bytes(...) bytes, 256-byte aligned, or
- *             NULL to let the call allocate it stream-ordered
- *             (hipMallocAsync / hipFreeAsync on `stream`).
+ *             tfla_state_workspace_bytes(...) bytes, 256-byte aligned and
+ *             disjoint from every tensor argument, or NULL to let the call
+ *             allocate it stream-ordered (hipMallocAsync / hipFreeAsync on
+ *             `stream`).
  * Every other argument, layout and rule is that of tfla_fwd.  With c0 and
  * c_final both NULL the result equals tfla_fwd's.
  */
@@ -204,9 +206,10 @@ int tfla_fwd_recurrent(const void* q, const void* k, const void* v,
  *   d_qk      as for tfla_fwd; d_hv 64, 128, 256 or 512 (fp32 I/O: 64 or
  *             128), since the dq and dk products contract over it.
  *   workspace caller-owned device workspace of at least
- *             tfla_bwd_workspace_bytes(...) bytes, 256-byte aligned, or NULL
- *             to let the call allocate it stream-ordered (hipMallocAsync /
- *             hipFreeAsync on `stream`).
+ *             tfla_bwd_workspace_bytes(...) bytes, 256-byte aligned and
+ *             disjoint from every tensor argument, or NULL to let the call
+ *             allocate it stream-ordered (hipMallocAsync / hipFreeAsync on
+ *             `stream`).
  */
 int tfla_bwd(const void* q, const void* k, const void* v,
              const float* igate_pre, const float* fgate_pre, const void* dh,

@@ -37,6 +37,7 @@ Range range_of(const void* p, size_t bytes)
 }
 bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
+
 // Shape and variant checks shared by every entry point.  Fills *p.
 int check_problem(int B, int H, int T, int d_qk, int d_hv, int L, int variant, tfla::Problem* p)
 {
@@ -91,6 +92,29 @@ size_t gate_bytes(const tfla::Problem& p)
     if (p.gate == tfla::kSig) return bh * p.T * 4;
     if (p.gate == tfla::kScalar) return (size_t)p.H * 4;
     return bh * p.T * p.dqk * 4;
+}
+
+// Byte ranges of the tensors of a forward call: q, k, v, h, fgate_pre, igate_pre.
+void fwd_ranges(const tfla::Problem& p, const void* q, const void* k, const void* v, const float* igate_pre,
+                const float* fgate_pre, const void* h, Range out[6])
+{
+    const size_t esz = p.bf16 ? 2 : 4;
+    const size_t bht = (size_t)p.B * p.H * p.T;
+    out[0] = range_of(q, bht * p.dqk * esz);
+    out[1] = range_of(k, bht * p.dqk * esz);
+    out[2] = range_of(v, bht * p.dhv * esz);
+    out[3] = range_of(h, bht * p.dhv * esz);
+    out[4] = range_of(fgate_pre, gate_bytes(p));
+    out[5] = igate_pre ? range_of(igate_pre, bht * 4) : Range{0, 0};
+}
+
+// The caller's workspace must not share a byte with any tensor of the call.
+int check_workspace_disjoint(const void* workspace, size_t bytes, const Range* tensors, size_t n)
+{
+    const Range w = range_of(workspace, bytes);
+    for (size_t i = 0; i < n; ++i)
+        if (overlaps(w, tensors[i])) return fail(TFLA_ERR_INVALID_ARG, "workspace overlaps an input or output");
+    return TFLA_OK;
 }
 
 int check_fwd(const void* q, const void* k, const void* v, const float* igate_pre, const float* fgate_pre,
@@ -381,6 +405,9 @@ int tfla_fwd_ws_marked(const void* q, const void* k, const void* v, const float*
     if (workspace_bytes < need)
         return fail(TFLA_ERR_OUT_OF_MEMORY, "workspace of " + std::to_string(workspace_bytes) +
                                                 " bytes is smaller than the " + std::to_string(need) + " needed");
+    Range tensors[6];
+    fwd_ranges(p, q, k, v, igate_pre, fgate_pre, h, tensors);
+    if ((rc = check_workspace_disjoint(workspace, need, tensors, 6))) return rc;
     tfla::workspace_layout(p, &ws, static_cast<char*>(workspace));
     return run_path(p, q, k, v, igate_pre, fgate_pre, h, ws, static_cast<hipStream_t>(stream), marks);
 }
@@ -439,6 +466,12 @@ int tfla_fwd_state(const void* q, const void* k, const void* v, const float* iga
         if (workspace_bytes < need)
             return fail(TFLA_ERR_OUT_OF_MEMORY, "workspace of " + std::to_string(workspace_bytes) +
                                                     " bytes is smaller than the " + std::to_string(need) + " needed");
+        const size_t sbytes = (size_t)p.B * p.H * p.dqk * p.dhv * 4;
+        Range tensors[8];
+        fwd_ranges(p, q, k, v, igate_pre, fgate_pre, h, tensors);
+        tensors[6] = c0 ? range_of(c0, sbytes) : Range{0, 0};
+        tensors[7] = c_final ? range_of(c_final, sbytes) : Range{0, 0};
+        if ((rc = check_workspace_disjoint(workspace, need, tensors, 8))) return rc;
     } else if (need > 0) {
         if (inject_alloc_fault())
             return fail(TFLA_ERR_OUT_OF_MEMORY, "injected allocation failure (TFLA_FAULT=alloc)");
@@ -563,6 +596,16 @@ int tfla_bwd(const void* q, const void* k, const void* v, const float* igate_pre
         if (workspace_bytes < need)
             return fail(TFLA_ERR_OUT_OF_MEMORY, "workspace of " + std::to_string(workspace_bytes) +
                                                     " bytes is smaller than the " + std::to_string(need) + " needed");
+        const size_t esz = p.bf16 ? 2 : 4;
+        const size_t bht = (size_t)B * H * T;
+        Range tensors[11];
+        fwd_ranges(p, q, k, v, igate_pre, fgate_pre, dh, tensors);   // slot 3: dh, shaped like h
+        tensors[6] = range_of(dq, bht * d_qk * esz);
+        tensors[7] = range_of(dk, bht * d_qk * esz);
+        tensors[8] = range_of(dv, bht * d_hv * esz);
+        tensors[9] = range_of(dfg, gate_bytes(p));
+        tensors[10] = dig ? range_of(dig, bht * 4) : Range{0, 0};
+        if ((rc = check_workspace_disjoint(workspace, need, tensors, 11))) return rc;
     } else {
         if (inject_alloc_fault())
             return fail(TFLA_ERR_OUT_OF_MEMORY, "injected allocation failure (TFLA_FAULT=alloc)");

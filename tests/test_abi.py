@@ -251,3 +251,19 @@ def test_bwd_workspace_bytes(L):
            + Xg)
     assert tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, dhv, Lc, GLA | BF16) == gla
     assert tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, 192, Lc, SIG | BF16) == 0
+
+
+def test_workspace_must_not_overlap_a_tensor(L):
+    """Each workspace-taking entry point rejects a workspace that shares
+    bytes with one of its tensors, before any HIP call."""
+    B, H, T, dqk, dhv, Lc, var = 2, 3, 300, 128, 256, 64, SIG | BF16
+    need = tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, var)
+    assert L.tfla_fwd_ws(Q, K, V, IG, FG, H_, B, H, T, dqk, dhv, Lc, var, Q - 256, need, None) == INVALID
+    assert "overlaps" in tfla.tfla_last_error()
+    assert L.tfla_fwd_ws(Q, K, V, IG, FG, H_, B, H, T, dqk, dhv, Lc, var, H_ + 4096, need, None) == INVALID
+    sneed = tfla.tfla_state_workspace_bytes(B, H, T, dqk, dhv, Lc, var)
+    assert L.tfla_fwd_state(Q, K, V, IG, FG, C0, H_, CF, B, H, T, dqk, dhv, Lc, var, C0, sneed, None) == INVALID
+    bneed = tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, dhv, Lc, var)
+    assert bwd(ws=DQ, nws=bneed) == INVALID
+    assert bwd(ws=DIG, nws=bneed) == INVALID
+    assert bwd(ws=FG - 256 * 256, nws=bneed) == INVALID
