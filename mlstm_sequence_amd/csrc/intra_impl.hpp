@@ -88,6 +88,13 @@ template <typename T, int DQK, int BV, int CW, int NTH> struct Prefetch {
     float li, a;
 };
 
+// 8 consecutive fp32 gate values (16-byte aligned) as two vector loads
+__device__ __forceinline__ void load_gates8(const float* p, f32x4 (&x)[2])
+{
+    x[0] = *reinterpret_cast<const f32x4*>(p);
+    x[1] = *reinterpret_cast<const f32x4*>(p + 4);
+}
+
 template <typename T, int GATE, int DQK, int BV, int NW, int MODE>
 __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                            const T* __restrict__ v, const float* __restrict__ a,
@@ -160,11 +167,17 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
                 qf[kq] = load8(qb + (size_t)row(tqc) * DQK + c);
             } else {
                 const Frag raw = load8(qb + (size_t)row(tqc) * DQK + c);
-                for (int e = 0; e < 8; ++e) {
-                    float ex = ab[(size_t)tqc * DQK + c + e];
-                    if (ref_row >= 0) ex -= ab[(size_t)ref_row * DQK + c + e];
-                    frag_set(qf[kq], e, frag_get(raw, e) * exp2_fast(ex * kLog2e));
+                // 8 consecutive channels of the gate row: two 16-byte loads
+                f32x4 ex[2];
+                load_gates8(ab + (size_t)tqc * DQK + c, ex);
+                if (ref_row >= 0) {
+                    f32x4 er[2];
+                    load_gates8(ab + (size_t)ref_row * DQK + c, er);
+                    ex[0] -= er[0];
+                    ex[1] -= er[1];
                 }
+                for (int e = 0; e < 8; ++e)
+                    frag_set(qf[kq], e, frag_get(raw, e) * exp2_fast(ex[e >> 2][e & 3] * kLog2e));
             }
         }
     };
@@ -236,10 +249,13 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
             const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
             if (INDECAY) {
                 const int s = min(s0 + r, T_ - 1);
-                for (int e = 0; e < VEC; ++e) {
-                    const float ex = ab[(size_t)ref_row * DQK + c + e] - ab[(size_t)s * DQK + c + e];
-                    pf.kv.k[u].set(e, pf.kv.k[u].get(e) * exp2_fast(ex * kLog2e));
+                f32x4 er[VEC / 4], es[VEC / 4];
+                for (int e4 = 0; e4 < VEC / 4; ++e4) {
+                    er[e4] = *reinterpret_cast<const f32x4*>(ab + (size_t)ref_row * DQK + c + 4 * e4);
+                    es[e4] = *reinterpret_cast<const f32x4*>(ab + (size_t)s * DQK + c + 4 * e4);
                 }
+                for (int e = 0; e < VEC; ++e)
+                    pf.kv.k[u].set(e, pf.kv.k[u].get(e) * exp2_fast((er[e >> 2][e & 3] - es[e >> 2][e & 3]) * kLog2e));
             }
             pf.kv.k[u].store(&sm.kv.ks[r][c]);
         }
@@ -251,10 +267,13 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
                 // column, R the last step of its 32-step half (factor <= 1)
                 const int s = min(s0 + r, T_ - 1);
                 const int R = min(s0 + 32 * (r >> 5) + 31, T_ - 1);
-                for (int e = 0; e < VEC; ++e) {
-                    const float ex = ab[(size_t)R * gw + v0 + c + e] - ab[(size_t)s * gw + v0 + c + e];
-                    pf.kv.v[u].set(e, pf.kv.v[u].get(e) * exp2_fast(ex * kLog2e));
+                f32x4 er[VEC / 4], es[VEC / 4];
+                for (int e4 = 0; e4 < VEC / 4; ++e4) {
+                    er[e4] = *reinterpret_cast<const f32x4*>(ab + (size_t)R * gw + v0 + c + 4 * e4);
+                    es[e4] = *reinterpret_cast<const f32x4*>(ab + (size_t)s * gw + v0 + c + 4 * e4);
                 }
+                for (int e = 0; e < VEC; ++e)
+                    pf.kv.v[u].set(e, pf.kv.v[u].get(e) * exp2_fast((er[e >> 2][e & 3] - es[e >> 2][e & 3]) * kLog2e));
             }
             pf.kv.v[u].store(&sm.kv.vs[r][c]);
         }
