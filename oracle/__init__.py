@@ -57,6 +57,8 @@ def _load():
         lib.oracle_fwd_state.restype = ctypes.c_int
         lib.oracle_bwd.argtypes = [dp] * 11 + [ctypes.c_int] * 6
         lib.oracle_bwd.restype = ctypes.c_int
+        lib.oracle_bwd_state.argtypes = [dp] * 14 + [ctypes.c_int] * 6
+        lib.oracle_bwd_state.restype = ctypes.c_int
         lib.oracle_log_gates.argtypes = [dp] * 5 + [ctypes.c_int] * 6
         lib.oracle_log_gates.restype = ctypes.c_int
         lib.oracle_threads.argtypes = []
@@ -141,6 +143,26 @@ def recurrent_bwd(q, k, v, igate_pre, fgate_pre, dh, kind):
     if rc != 0:
         raise ValueError("oracle_bwd rejected its arguments")
     return dq, dk, dv, dig, dfg
+
+
+def recurrent_bwd_state(q, k, v, igate_pre, fgate_pre, dh, kind, c0=None, dcT=None):
+    """The backward pass with an initial state C_0 = c0 [B,H,dqk,dhv] (None:
+    0) and the gradient dcT of the loss with respect to the final state C_T
+    (None: 0), i.e. for L = sum(dh * h) + sum(dcT * C_T).  Returns (dq, dk, dv,
+    dig, dfg, dc0), dc0 = dL/dC_0."""
+    q, k, v, ig, fg, dh, c0, dcT = map(_f64, (q, k, v, igate_pre, fgate_pre, dh, c0, dcT))
+    B, H, T, dqk = q.shape
+    dhv = v.shape[-1]
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    dig = np.empty_like(ig) if kind == MLSTM_SIG else None
+    dfg = np.empty_like(fg)
+    dc0 = np.empty((B, H, dqk, dhv), dtype=np.float64)
+    rc = _load().oracle_bwd_state(_ptr(q), _ptr(k), _ptr(v), _ptr(ig), _ptr(fg), _ptr(c0), _ptr(dh), _ptr(dcT),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dig), _ptr(dfg), _ptr(dc0),
+                                  B, H, T, dqk, dhv, kind)
+    if rc != 0:
+        raise ValueError("oracle_bwd_state rejected its arguments")
+    return dq, dk, dv, dig, dfg, dc0
 
 
 def log_gates(igate_pre, fgate_pre, kind, B, H, T, dqk, L):

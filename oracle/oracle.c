@@ -239,10 +239,11 @@ static int forget_floored(int kind, const double* fgate_pre, size_t bh, int head
     return x < -100.0;
 }
 
-int oracle_bwd(const double* q, const double* k, const double* v,
-               const double* igate_pre, const double* fgate_pre, const double* dh,
-               double* dq, double* dk, double* dv, double* dig, double* dfg,
-               int B, int H, int T, int dqk, int dhv, int kind)
+int oracle_bwd_state(const double* q, const double* k, const double* v,
+                     const double* igate_pre, const double* fgate_pre, const double* c0,
+                     const double* dh, const double* dcT,
+                     double* dq, double* dk, double* dv, double* dig, double* dfg, double* dc0,
+                     int B, int H, int T, int dqk, int dhv, int kind)
 {
     if (!q || !k || !v || !fgate_pre || !dh || !dq || !dk || !dv || !dfg) return -1;
     if (B < 0 || H < 0 || T < 0 || dqk < 1 || dhv < 1) return -1;
@@ -272,7 +273,9 @@ int oracle_bwd(const double* q, const double* k, const double* v,
             bad = 1;
             continue;
         }
-        /* forward sweep: C_t, dq_t, and the state before every 64-step block */
+        /* forward sweep from C_0: C_t, dq_t, and the state before every 64-step block */
+        if (c0) memcpy(C, c0 + (size_t)bh * csz, csz * sizeof(double));
+        if (dcT) memcpy(dC, dcT + (size_t)bh * csz, csz * sizeof(double));
         for (int t = 0; t < T; ++t) {
             if (t % BLK == 0) memcpy(ck + (size_t)(t / BLK) * csz, C, csz * sizeof(double));
             const double* kt = k + ((size_t)bh * T + t) * dqk;
@@ -309,13 +312,14 @@ int oracle_bwd(const double* q, const double* k, const double* v,
                 const double* kt = k + ((size_t)bh * T + t) * dqk;
                 const double* vt = v + ((size_t)bh * T + t) * dhv;
                 const double* dht = dh + ((size_t)bh * T + t) * dhv;
-                /* dC_t = diag(f_{t+1}) dC_{t+1} + s q_t dh_t^T */
+                /* dC_t = diag(f_{t+1}) dC_{t+1} + s q_t dh_t^T; for the last step the
+                   first term is the gradient dcT of the final state (or 0) */
                 if (t + 1 < T)
                     for (int c = 0; c < dqk; ++c) f[c] = forget_gate(kind, fgate_pre, (size_t)bh, head, T, dqk, t + 1, c);
                 for (int c = 0; c < dqk; ++c)
                     for (int j = 0; j < dhv; ++j) {
                         double* e = &dC[(size_t)c * dhv + j];
-                        *e = (t + 1 < T ? f[c] * *e : 0.0) + scale * qt[c] * dht[j];
+                        *e = (t + 1 < T ? f[c] * *e : *e) + scale * qt[c] * dht[j];
                     }
                 const double it = input_gate(kind, igate_pre, (size_t)bh, T, t);
                 double* dkt = dk + ((size_t)bh * T + t) * dqk;
@@ -359,6 +363,15 @@ int oracle_bwd(const double* q, const double* k, const double* v,
                 }
             }
         }
+        /* the initial state enters C_1 through the first step's forget gate:
+           dL/dC_0 = diag(f_1) dC_1 (dcT itself when T = 0) */
+        if (dc0) {
+            double* out = dc0 + (size_t)bh * csz;
+            if (T > 0)
+                for (int c = 0; c < dqk; ++c) f[c] = forget_gate(kind, fgate_pre, (size_t)bh, head, T, dqk, 0, c);
+            for (int c = 0; c < dqk; ++c)
+                for (int j = 0; j < dhv; ++j) out[(size_t)c * dhv + j] = (T > 0 ? f[c] : 1.0) * dC[(size_t)c * dhv + j];
+        }
         free(C); free(dC); free(ck); free(Cb); free(f); free(df);
     }
     if (kind == KIND_SCALAR) {
@@ -367,6 +380,15 @@ int oracle_bwd(const double* q, const double* k, const double* v,
     }
     free(dscal);
     return bad ? -1 : 0;
+}
+
+int oracle_bwd(const double* q, const double* k, const double* v,
+               const double* igate_pre, const double* fgate_pre, const double* dh,
+               double* dq, double* dk, double* dv, double* dig, double* dfg,
+               int B, int H, int T, int dqk, int dhv, int kind)
+{
+    return oracle_bwd_state(q, k, v, igate_pre, fgate_pre, NULL, dh, NULL, dq, dk, dv, dig, dfg, NULL,
+                            B, H, T, dqk, dhv, kind);
 }
 
 /* the scalar gate functions, exported so tests can pin them */

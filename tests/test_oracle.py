@@ -392,3 +392,67 @@ def test_forget_gradient_is_reverse_sum_of_q_dq_minus_k_dk(kind):
         dlogf = np.flip(np.cumsum(np.flip(r, 2), 2), 2)
         sx = 1.0 / (1.0 + np.exp(-fg))
         assert rel_err(dlogf * (1.0 - sx) / 16.0, dfg) <= 1e-10
+
+
+# ------------------------------------------------ backward with state in and out
+@pytest.mark.parametrize("kind", [MLSTM_SIG, SCALAR, GLA])
+def test_state_backward_matches_finite_differences(kind):
+    """L = sum(dh * h) + sum(dcT * C_T) from the initial state c0: every
+    gradient, dL/dc0 included, against central differences of the forward
+    recurrence from that state."""
+    B, H, T, dqk, dhv = 1, 2, 5, 3, 2
+    q, k, v, ig, fg, dh = _all_inputs(kind, B, H, T, dqk, dhv, seed=70 + kind)
+    rng = np.random.default_rng(80 + kind)
+    c0 = rng.standard_normal((B, H, dqk, dhv))
+    dcT = rng.standard_normal((B, H, dqk, dhv))
+    got = oracle.recurrent_bwd_state(q, k, v, ig, fg, dh, kind, c0=c0, dcT=dcT)
+    arrs = {"q": q, "k": k, "v": v, "ig": ig, "fg": fg, "c0": c0}
+
+    def loss(a):
+        h, cT = oracle.recurrent_fwd_state(a["q"], a["k"], a["v"], a["ig"], a["fg"], kind, c0=a["c0"])
+        return float(np.sum(dh * h) + np.sum(dcT * cT))
+
+    eps = 1e-6
+    for name, g in zip(["q", "k", "v", "ig", "fg", "c0"], got):
+        if arrs[name] is None:
+            assert g is None
+            continue
+        num = np.empty_like(arrs[name])
+        for idx in np.ndindex(arrs[name].shape):
+            plus = {n: (x.copy() if x is not None else None) for n, x in arrs.items()}
+            minus = {n: (x.copy() if x is not None else None) for n, x in arrs.items()}
+            plus[name][idx] += eps
+            minus[name][idx] -= eps
+            num[idx] = (loss(plus) - loss(minus)) / (2 * eps)
+        assert rel_err(g, num) <= 1e-6, name
+
+
+@pytest.mark.parametrize("kind", [MLSTM_SIG, GLA])
+def test_state_backward_chains_over_a_split_sequence(kind):
+    """The backward of a sequence equals that of its two halves chained: the
+    second half starts from the first half's final state, and its dL/dC_0 is
+    the first half's final-state gradient."""
+    B, H, T, dqk, dhv = 2, 1, 37, 4, 3
+    q, k, v, ig, fg, dh = _all_inputs(kind, B, H, T, dqk, dhv, seed=90 + kind)
+    whole = oracle.recurrent_bwd(q, k, v, ig, fg, dh, kind)
+    m = 16
+    cut = lambda x, a, b: None if x is None else x[:, :, a:b]
+    _, c_mid = oracle.recurrent_fwd_state(cut(q, 0, m), cut(k, 0, m), cut(v, 0, m), cut(ig, 0, m), cut(fg, 0, m), kind)
+    second = oracle.recurrent_bwd_state(cut(q, m, T), cut(k, m, T), cut(v, m, T), cut(ig, m, T), cut(fg, m, T),
+                                        cut(dh, m, T), kind, c0=c_mid)
+    first = oracle.recurrent_bwd_state(cut(q, 0, m), cut(k, 0, m), cut(v, 0, m), cut(ig, 0, m), cut(fg, 0, m),
+                                       cut(dh, 0, m), kind, dcT=second[5])
+    for i in range(5):
+        if whole[i] is None:
+            continue
+        joined = np.concatenate([first[i], second[i]], axis=2)
+        assert rel_err(joined, whole[i]) <= 1e-12, i
+    assert np.abs(first[5]).max() > 0      # a gradient reaches the zero initial state
+
+
+def test_state_backward_without_states_is_the_plain_backward():
+    q, k, v, ig, fg, dh = _all_inputs(MLSTM_SIG, 1, 2, 30, 4, 5, seed=99)
+    a = oracle.recurrent_bwd(q, k, v, ig, fg, dh, MLSTM_SIG)
+    b = oracle.recurrent_bwd_state(q, k, v, ig, fg, dh, MLSTM_SIG)
+    for x, y in zip(a, b[:5]):
+        assert np.array_equal(x, y)
