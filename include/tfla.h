@@ -222,6 +222,39 @@ int tfla_bwd(const void* q, const void* k, const void* v,
 size_t tfla_bwd_workspace_bytes(int B, int H, int T, int d_qk, int d_hv, int L, int variant);
 
 /*
+ * tfla_bwd_state -- the backward pass of tfla_fwd_state: the forward pass
+ * ran from the initial state c0 (NULL: 0), and the loss also depends on the
+ * final state C_T through dc_final = dL/dC_T (NULL: it does not), so
+ *
+ *     dC_T = q_T dh_T^T / sqrt(d_qk) + dc_final,   dL/dC_0 = diag(f_1) dC_1.
+ *
+ * This is what chains the backward passes of consecutive segments of one
+ * sequence (a long sequence trained in pieces, or split over devices): a
+ * segment's dc0 is the dc_final of the segment before it, whose c0 chain
+ * is the forward pass's.  The forget-gate gradient includes the paths
+ * through C_0 and into C_T.
+ *
+ *   c0        fp32 [B,H,d_qk,d_hv] or NULL, as for tfla_fwd_state.
+ *   dc_final  fp32 [B,H,d_qk,d_hv] or NULL.
+ *   dc0       fp32 [B,H,d_qk,d_hv] output dL/dC_0, or NULL.  May be the
+ *             same pointer as c0 or as dc_final (updated in place).
+ *   workspace at least tfla_bwd_state_workspace_bytes(...) bytes, or NULL;
+ *             TFLA_BWD_REUSE_FWD is not accepted here.
+ * Every other argument and rule is that of tfla_bwd; with c0, dc_final and
+ * dc0 all NULL the gradients equal tfla_bwd's.
+ */
+int tfla_bwd_state(const void* q, const void* k, const void* v,
+                   const float* igate_pre, const float* fgate_pre, const float* c0,
+                   const void* dh, const float* dc_final,
+                   void* dq, void* dk, void* dv, float* dig, float* dfg, float* dc0,
+                   int B, int H, int T, int d_qk, int d_hv, int L, int variant,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace tfla_bwd_state needs (whatever of c0, dc_final
+ * and dc0 are given); 0 when the arguments are invalid or unsupported. */
+size_t tfla_bwd_state_workspace_bytes(int B, int H, int T, int d_qk, int d_hv, int L, int variant);
+
+/*
  * Test hooks: run part of the path and copy its intermediate out.
  *
  * tfla_dbg_gates -- the gate prefix-sum kernel alone.  Outputs (device, fp32):

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kScanThreads) void grad_scan_sig_kernel(const float
                                                                     float scale, const float* __restrict__ ig,
                                                                     const float* __restrict__ fg,
                                                                     float* __restrict__ dig, float* __restrict__ dfg,
-                                                                    int T_, int L, int nc)
+                                                                    int T_, int L, int nc, int nbound)
 {
     __shared__ double part[2][kScanThreads];
     const int kc = blockIdx.x % nc;
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kScanThreads) void grad_scan_sig_kernel(const float
         __syncthreads();
     }
     // sum over the steps of the chunk after t1, plus the coupling past it
-    double acc = part[cur][tid] - s + (kc < nc - 1 ? coupling(xpart, bh * (nc - 1) + kc, nx, scale) : 0.0);
+    double acc = part[cur][tid] - s + (kc < nbound ? coupling(xpart, bh * nbound + kc, nx, scale) : 0.0);
     for (int t = t1 - 1; t >= t0; --t) {
         step_dots(dq_dots, dk_dots, base + t, np, r, kd);
         acc += r;
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256) void grad_gla_kernel(const float* __restrict__
                                                       const float* __restrict__ dk_prod,
                                                       const float* __restrict__ xpart, int nx, float scale,
                                                       const float* __restrict__ fg, float* __restrict__ dfg,
-                                                      int T_, int L, int nc, int dqk)
+                                                      int T_, int L, int nc, int dqk, int nbound)
 {
     const int kc = blockIdx.x % nc;
     const size_t bh = blockIdx.x / nc;
@@ -156,8 +156,8 @@ __global__ __launch_bounds__(256) void grad_gla_kernel(const float* __restrict__
     if (c >= dqk) return;
     const int cs = kc * L, ce = min(cs + L, T_);
     double acc = 0.0;
-    if (kc < nc - 1) {
-        const float* xp = xpart + ((bh * (nc - 1) + kc) * dqk + c) * nx;
+    if (kc < nbound) {
+        const float* xp = xpart + ((bh * nbound + kc) * dqk + c) * nx;
         for (int j = 0; j < nx; ++j) acc += xp[j];
         acc *= scale;
     }
@@ -172,23 +172,27 @@ __global__ __launch_bounds__(256) void grad_gla_kernel(const float* __restrict__
 
 // Fixed per-head decay: one workgroup per (batch, head) sums its part of
 // dL/dlog gamma in double; a second kernel adds the batches of each head in
-// a fixed order.
+// a fixed order.  Every step of chunk k adds sum_{t <= t' in k} r_t' + X_k,
+// i.e. sum_t (t - cs_t + 1) r_t + sum_k len_k X_k; without an initial state
+// or a final-state gradient sum_t r_t = 0 and the weights are centred on
+// the chunk (centred = 1).
 __global__ __launch_bounds__(kScanThreads) void grad_scalar_kernel(const float* __restrict__ dq_dots,
                                                                   const float* __restrict__ dk_dots, int np,
                                                                   const float* __restrict__ xpart, int nx,
                                                                   float scale, double* __restrict__ part_out,
-                                                                  int T_, int L, int nc)
+                                                                  int T_, int L, int nc, int nbound, int centred)
 {
     __shared__ double part[kScanThreads];
     const size_t bh = blockIdx.x;
     const int tid = threadIdx.x;
-    const double centre = 0.5 * (L - 1);
+    const double centre = centred ? 0.5 * (L - 1) : -1.0;
     double s = 0.0, r, kd;
     for (int t = tid; t < T_; t += kScanThreads) {
         step_dots(dq_dots, dk_dots, bh * T_ + t, np, r, kd);
         s += ((double)(t % L) - centre) * r;
     }
-    for (int k = tid; k < nc - 1; k += kScanThreads) s += (double)L * coupling(xpart, bh * (nc - 1) + k, nx, scale);
+    for (int k = tid; k < nbound; k += kScanThreads)
+        s += (double)min(L, T_ - k * L) * coupling(xpart, bh * nbound + k, nx, scale);
     part[tid] = s;
     __syncthreads();
     for (int d = kScanThreads / 2; d >= 1; d >>= 1) {
@@ -211,6 +215,42 @@ __global__ __launch_bounds__(64) void grad_scalar_final_kernel(const double* __r
     dfg[h] = floored ? 0.0f : (float)(s / (1.0 + exp((double)x)));
 }
 
+// y = a x over n floats
+__global__ __launch_bounds__(256) void scale_copy_kernel(const float* __restrict__ x, float* __restrict__ y, size_t n,
+                                                         float a)
+{
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) y[i] = a * x[i];
+}
+
+// Coupling across the end of the sequence: the Frobenius product of the
+// final-state gradient (given as dC_T sqrt(d_qk), the reverse walk's
+// scaling) and C_T, both [d_qk][d_hv], over the whole state (per head) or
+// over one key channel's row (per-channel gate: one workgroup per row).  It
+// is stored as partial 0 of boundary nbound-1, the other partials zero.
+__global__ __launch_bounds__(256) void final_coupling_kernel(const float* __restrict__ g, const float* __restrict__ c,
+                                                            float* __restrict__ xpart, int nx, int nbound, int dqk,
+                                                            int dhv, int per_channel)
+{
+    __shared__ double part[256];
+    const int rows = per_channel ? 1 : dqk;   // rows of the state per workgroup
+    const size_t bh = per_channel ? blockIdx.x / dqk : blockIdx.x;
+    const int ch = per_channel ? blockIdx.x % dqk : 0;
+    const size_t base = (bh * dqk + ch) * (size_t)dhv;
+    const size_t n = (size_t)rows * dhv;
+    double s = 0.0;
+    for (size_t i = threadIdx.x; i < n; i += 256) s += (double)g[base + i] * c[base + i];
+    part[threadIdx.x] = s;
+    __syncthreads();
+    for (int d = 128; d >= 1; d >>= 1) {
+        if (threadIdx.x < d) part[threadIdx.x] += part[threadIdx.x + d];
+        __syncthreads();
+    }
+    float* dst = per_channel ? xpart + ((bh * nbound + nbound - 1) * dqk + ch) * nx
+                             : xpart + (bh * nbound + nbound - 1) * nx;
+    for (int j = threadIdx.x; j < nx; j += 256) dst[j] = j == 0 ? (float)part[0] : 0.0f;
+}
+
 }  // namespace
 
 hipError_t launch_gates_mirror(const Problem& p, const Workspace& ws, float* ar, float* lr, hipStream_t stream)
@@ -225,20 +265,35 @@ hipError_t launch_gates_mirror(const Problem& p, const Workspace& ws, float* ar,
     return hipGetLastError();
 }
 
-hipError_t launch_gate_grads(const Problem& p, const float* xpart, int nx, const float* dq_dots,
-                             const float* dk_dots, int np, const float* igate_pre, const float* fgate_pre,
-                             float* dig, float* dfg, double* head_part, hipStream_t stream)
+hipError_t launch_scale_copy(const float* x, float* y, size_t n, float a, hipStream_t stream)
+{
+    scale_copy_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(x, y, n, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_final_coupling(const Problem& p, const float* g_scaled, const float* c_final, float* xpart, int nx,
+                                 int nbound, hipStream_t stream)
+{
+    const bool per_channel = p.gate == kGla;
+    const unsigned blocks = (unsigned)(p.B * p.H * (per_channel ? p.dqk : 1));
+    final_coupling_kernel<<<blocks, 256, 0, stream>>>(g_scaled, c_final, xpart, nx, nbound, p.dqk, p.dhv, per_channel);
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_grads(const Problem& p, const float* xpart, int nx, int nbound, bool with_states,
+                             const float* dq_dots, const float* dk_dots, int np, const float* igate_pre,
+                             const float* fgate_pre, float* dig, float* dfg, double* head_part, hipStream_t stream)
 {
     const float scale = 1.0f / sqrtf((float)p.dqk);
     if (p.gate == kGla)
         grad_gla_kernel<<<p.B * p.H * p.nc, 256, 0, stream>>>(dq_dots, dk_dots, xpart, nx, scale, fgate_pre, dfg, p.T,
-                                                              p.L, p.nc, p.dqk);
+                                                              p.L, p.nc, p.dqk, nbound);
     else if (p.gate == kSig)
         grad_scan_sig_kernel<<<p.B * p.H * p.nc, kScanThreads, 0, stream>>>(
-            dq_dots, dk_dots, np, xpart, nx, scale, igate_pre, fgate_pre, dig, dfg, p.T, p.L, p.nc);
+            dq_dots, dk_dots, np, xpart, nx, scale, igate_pre, fgate_pre, dig, dfg, p.T, p.L, p.nc, nbound);
     else {
         grad_scalar_kernel<<<p.B * p.H, kScanThreads, 0, stream>>>(dq_dots, dk_dots, np, xpart, nx, scale,
-                                                                   head_part, p.T, p.L, p.nc);
+                                                                   head_part, p.T, p.L, p.nc, nbound, !with_states);
         grad_scalar_final_kernel<<<(p.H + 63) / 64, 64, 0, stream>>>(head_part, fgate_pre, dfg, p.B, p.H);
     }
     return hipGetLastError();

@@ -287,8 +287,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
 
     // ---------------- inter-chunk term: e^{a_t} q_t^T C_{k-1}
     // states hold C before chunks 1..nc-1, preceded by C_0 when one is given
-    // (c0 = 1); mirrored: the state of chunks kc+1.. in slot kc
-    const bool inter = REV ? kc < nc - 1 : (kc > 0 || c0);
+    // (c0 = 1); mirrored: the state of chunks kc+1.. in slot kc, the last
+    // chunk's (a final-state gradient) in slot nc-1 when one is given (c0 = 1)
+    const bool inter = REV ? kc < nc - 1 + c0 : (kc > 0 || c0);
     if (inter) {
         const size_t slot = bh * (nc - 1 + c0) + (REV ? kc : kc - 1 + c0);
         const float* st = NAT ? states + slot * DQK * (size_t)dhv + v0

@@ -38,6 +38,11 @@ struct Workspace {
     // [B,H,nc-1][state_dot_parts(p)].
     const void* dot_partner = nullptr;
     float* dots = nullptr;
+    // reverse walk: slots per head of the forward states in dot_partner and
+    // the slot of the state after chunk 0 (1 when they begin with C_0);
+    // boundaries per head in dots; factor on the end state written to c_final
+    int dot_slots = 0, dot_off = 0, dot_bound = 0;
+    float end_scale = 1.0f;
 };
 
 // Segmented state walk (few heads, long sequences): number of segments P
@@ -67,8 +72,9 @@ hipError_t launch_state(const Problem& p, const void* k, const void* v, const fl
                         const Workspace& ws, hipStream_t stream);
 // The reverse state walk of the backward pass: ws.states receives
 // D_0..D_{nc-2} (D_j: gradient into the state from the chunks after chunk
-// j, without the 1/sqrt(d_qk) factor), transposed [d_hv][d_qk]; ws.c0 and
-// ws.c_final must be NULL.
+// j, without the 1/sqrt(d_qk) factor), transposed [d_hv][d_qk], followed by
+// D_{nc-1} when ws.c0 holds one (the final-state gradient, same factor,
+// [d_qk][d_hv]); ws.c_final receives D_{-1} * ws.end_scale when given.
 hipError_t launch_state_rev(const Problem& p, const void* q, const void* dh, const float* fgate_pre,
                             const Workspace& ws, hipStream_t stream);
 hipError_t launch_recurrent(const Problem& p, const void* q, const void* k, const void* v,
@@ -91,10 +97,18 @@ hipError_t launch_intra_dv(const Problem& p, const void* q, const void* k, const
 // mode (mLSTMsig), and the input / forget gate gradients from the dq and dk
 // kernels' row partials (q_t.dq_t and k_t.dk_t, np per step, [B,H,T][np])
 // and the reverse walk's partials of <D_m, C_m> (nx per boundary,
-// [B,H,nc-1][nx]); head_part: [B,H] double scratch of the fixed decay.
+// [B,H,nbound][nx], nbound = nc-1, or nc with a final-state gradient);
+// with_states: an initial state or a final-state gradient is present;
+// head_part: [B,H] double scratch of the fixed decay.
 hipError_t launch_gates_mirror(const Problem& p, const Workspace& ws, float* ar, float* lr, hipStream_t stream);
-hipError_t launch_gate_grads(const Problem& p, const float* xpart, int nx, const float* dq_dots,
-                             const float* dk_dots, int np, const float* igate_pre, const float* fgate_pre,
-                             float* dig, float* dfg, double* head_part, hipStream_t stream);
+hipError_t launch_gate_grads(const Problem& p, const float* xpart, int nx, int nbound, bool with_states,
+                             const float* dq_dots, const float* dk_dots, int np, const float* igate_pre,
+                             const float* fgate_pre, float* dig, float* dfg, double* head_part, hipStream_t stream);
+// y = a x (n floats)
+hipError_t launch_scale_copy(const float* x, float* y, size_t n, float a, hipStream_t stream);
+// the coupling across the end of the sequence, <dC_T sqrt(d_qk), C_T>, into
+// boundary nbound-1 of xpart (per key channel for the per-channel gate)
+hipError_t launch_final_coupling(const Problem& p, const float* g_scaled, const float* c_final, float* xpart, int nx,
+                                 int nbound, hipStream_t stream);
 
 }  // namespace tfla

@@ -73,6 +73,11 @@ struct StateWalk {
     int end_all;         // every segment writes its end state
     int write_states;    // store the state after every chunk kc < nc-1
     int soff;            // 1 when the stored states start with C_0
+    // reverse walk: the forward states its couplings read (slots per head,
+    // slot of the state after chunk 0), boundaries per head in xpart, and
+    // the factor on the end state it writes
+    int cp_slots = 0, cp_off = 0, nbound = 0;
+    float end_scale = 1.0f;
 };
 
 // Tile of C^T per workgroup: TV value rows x TC key columns; NWS wavefronts
@@ -243,7 +248,9 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
         for (int mv = 0; mv < MV; ++mv)
             for (int mc = 0; mc < MC; ++mc)
                 for (int r = 0; r < 16; ++r) acc[mv][mc][r] = src[nat(mv, mc, r)];
-        if (seg == 0 && wk.put_c0) put_state(acc, 0);
+        // (reverse walk: the final-state gradient, the state of the chunks
+        // after the last one, in slot nc-1)
+        if (seg == 0 && wk.put_c0) put_state(acc, REV ? nc - 1 : 0);
     } else {
 #pragma unroll
         for (int mv = 0; mv < MV; ++mv)
@@ -283,7 +290,8 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
 #pragma unroll
             for (int mv = 0; mv < MV; ++mv) {
                 const float* src =
-                    cstates + ((bh * ns + (nc - 2 - kc)) * (size_t)dhv + v0 + vw + 32 * mv) * dqk + c0 + cw + i32;
+                    cstates + ((bh * wk.cp_slots + (nc - 2 - kc) + wk.cp_off) * (size_t)dhv + v0 + vw + 32 * mv) * dqk +
+                    c0 + cw + i32;
 #pragma unroll
                 for (int mc = 0; mc < MC; ++mc)
 #pragma unroll
@@ -322,7 +330,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
                             for (int r = 0; r < 16; ++r) x += acc[mv][mc][r] * cpre[mv][mc][r];
                         x += __shfl_xor(x, 32, 64);
                         if (hh == 0)
-                            xpart[((bh * (nc - 1) + slot) * dqk + c0 + cw + 32 * mc + i32) * nvp + part] = x;
+                            xpart[((bh * wk.nbound + slot) * dqk + c0 + cw + 32 * mc + i32) * nvp + part] = x;
                     }
                 } else {
                     float x = 0.0f;
@@ -334,7 +342,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
                             for (int r = 0; r < 16; ++r) x += acc[mv][mc][r] * cpre[mv][mc][r];
 #pragma unroll
                     for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-                    if (lane == 0) xpart[((bh * (nc - 1) + slot) * tiles + tile) * NWS + w] = x;
+                    if (lane == 0) xpart[((bh * wk.nbound + slot) * tiles + tile) * NWS + w] = x;
                 }
             }
         }
@@ -346,7 +354,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
 #pragma unroll
             for (int mv = 0; mv < MV; ++mv)
                 for (int mc = 0; mc < MC; ++mc)
-                    for (int r = 0; r < 16; ++r) dst[nat(mv, mc, r)] = acc[mv][mc][r];
+                    for (int r = 0; r < 16; ++r) dst[nat(mv, mc, r)] = acc[mv][mc][r] * wk.end_scale;
         }
     }
 }
@@ -449,6 +457,15 @@ hipError_t launch_combine(const Problem& p, const float* fg, const Workspace& ws
     return hipGetLastError();
 }
 
+// the reverse walk's coupling partner and end-state factor, from the workspace
+inline void set_rev_fields(StateWalk& wk, const Workspace& ws)
+{
+    wk.cp_slots = ws.dot_slots;
+    wk.cp_off = ws.dot_off;
+    wk.nbound = ws.dot_bound;
+    wk.end_scale = ws.end_scale;
+}
+
 // One configuration: unsegmented walk, or pass 1 + combine + pass 2.
 template <typename T, int SB, int TV, int TC, int NWS, bool REV>
 hipError_t launch_state_cfg(const Problem& p, const T* k, const T* v, const float* fg, const Workspace& ws,
@@ -458,7 +475,8 @@ hipError_t launch_state_cfg(const Problem& p, const T* k, const T* v, const floa
     const int soff = ws.c0 != nullptr;
     const int nwalk = p.nc - 1 + (ws.c_final != nullptr);
     if (P <= 1) {
-        const StateWalk wk{ws.c0, ws.c_final, 1, 1, nwalk > 0 ? nwalk : 1, nwalk, soff, 0, 1, soff};
+        StateWalk wk{ws.c0, ws.c_final, 1, 1, nwalk > 0 ? nwalk : 1, nwalk, soff, 0, 1, soff};
+        set_rev_fields(wk, ws);
         return launch_walk<T, SB, TV, TC, NWS, REV>(p, k, v, fg, ws, wk, stream);
     }
     const int cps = state_chunks_per_segment(p, P);
@@ -466,7 +484,8 @@ hipError_t launch_state_cfg(const Problem& p, const T* k, const T* v, const floa
     hipError_t e = launch_walk<T, SB, TV, TC, NWS, REV>(p, k, v, fg, ws, pass1, stream);
     if (e != hipSuccess) return e;
     if ((e = launch_combine<REV>(p, fg, ws, P, cps, stream)) != hipSuccess) return e;
-    const StateWalk pass2{ws.seg_start, ws.c_final, P, P, cps, nwalk, soff, 0, 1, soff};
+    StateWalk pass2{ws.seg_start, ws.c_final, P, P, cps, nwalk, soff, 0, 1, soff};
+    set_rev_fields(pass2, ws);
     return launch_walk<T, SB, TV, TC, NWS, REV>(p, k, v, fg, ws, pass2, stream);
 }
 

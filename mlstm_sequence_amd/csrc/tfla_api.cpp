@@ -213,7 +213,16 @@ struct BwdWorkspace {
     float* xpart;     // [B,H,nc-1][nx]: partials of <D_k, C_k> across each chunk boundary
                       // (per-channel gate: [B,H,nc-1,d_qk][nx])
     double* head_part;  // [B,H]: per-(batch, head) part of the fixed decay's gradient
+    float* g_scaled;  // tfla_bwd_state: the final-state gradient times sqrt(d_qk) [B,H,d_qk,d_hv]
+    float* c_T;       // tfla_bwd_state: the recomputed final state [B,H,d_qk,d_hv]
     int np, nx;
+};
+
+// The state arguments of tfla_bwd_state (all NULL for tfla_bwd).
+struct BwdStateIO {
+    const float* c0 = nullptr;         // initial state C_0
+    const float* dc_final = nullptr;   // dL/dC_T
+    float* dc0 = nullptr;              // receives dL/dC_0
 };
 
 // the dq and dk products: contract d_hv, emit d_qk
@@ -225,16 +234,21 @@ tfla::Problem grad_qk_problem(const tfla::Problem& p)
     return pc;
 }
 
-size_t bwd_layout(const tfla::Problem& p, BwdWorkspace* ws, char* base)
+// with_states: the layout of tfla_bwd_state (a slot for C_0 among the
+// forward states, one for the final-state gradient among the reverse-walk
+// states, a coupling across the end of the sequence, C_T and the scaled
+// final-state gradient)
+size_t bwd_layout(const tfla::Problem& p, BwdWorkspace* ws, char* base, bool with_states = false)
 {
-    size_t off = tfla::workspace_layout(p, &ws->fwd, base);
+    size_t off = tfla::workspace_layout(p, &ws->fwd, base, true, with_states);
     const size_t bh = (size_t)p.B * p.H;
     auto take = [&](size_t bytes) -> float* {
         float* ptr = base ? reinterpret_cast<float*>(base + off) : nullptr;
         off += align256(bytes);
         return ptr;
     };
-    ws->dstates = p.nc > 1 ? take(bh * (p.nc - 1) * p.dhv * p.dqk * 4) : nullptr;
+    const size_t rslots = p.nc - 1 + (with_states ? 1 : 0);   // reverse-walk states
+    ws->dstates = rslots > 0 ? take(bh * rslots * p.dhv * p.dqk * 4) : nullptr;
     const bool sig = p.gate == tfla::kSig, gla = p.gate == tfla::kGla;
     ws->ar = sig ? take(bh * p.T * 4) : gla ? take(bh * p.T * p.dqk * 4) : nullptr;
     ws->lr = sig ? take(bh * p.T * 4) : nullptr;
@@ -243,8 +257,11 @@ size_t bwd_layout(const tfla::Problem& p, BwdWorkspace* ws, char* base)
     ws->dk_dots = take(bh * p.T * ws->np * 4);
     ws->nx = tfla::state_dot_parts(p);
     const size_t per_boundary = (size_t)ws->nx * (p.gate == tfla::kGla ? p.dqk : 1);
-    ws->xpart = p.nc > 1 ? take(bh * (p.nc - 1) * per_boundary * 4) : nullptr;
+    ws->xpart = rslots > 0 ? take(bh * rslots * per_boundary * 4) : nullptr;
     ws->head_part = p.gate == tfla::kScalar ? reinterpret_cast<double*>(take(bh * 8)) : nullptr;
+    const size_t sbytes = bh * p.dqk * p.dhv * 4;
+    ws->g_scaled = with_states ? take(sbytes) : nullptr;
+    ws->c_T = with_states ? take(sbytes) : nullptr;
     return off;
 }
 
@@ -262,15 +279,21 @@ int check_bwd_problem(int B, int H, int T, int d_qk, int d_hv, int L, int varian
 
 int run_bwd(const tfla::Problem& p, const void* q, const void* k, const void* v, const float* igate_pre,
             const float* fgate_pre, const void* dh, void* dq, void* dk, void* dv, float* dig, float* dfg,
-            const BwdWorkspace& ws, bool reuse_fwd, hipStream_t stream)
+            const BwdWorkspace& ws, bool reuse_fwd, const BwdStateIO& io, hipStream_t stream)
 {
     const float scale = 1.0f / sqrtf((float)p.dqk);
+    const bool has_c0 = io.c0 != nullptr, has_g = io.dc_final != nullptr;
+    const int nbound = p.nc - 1 + (has_g ? 1 : 0);   // chunk boundaries with a coupling
     hipError_t e;
     if (!reuse_fwd) {
         if ((e = tfla::launch_gates(p, igate_pre, fgate_pre, ws.fwd, stream)) != hipSuccess)
             return hip_fail(e, "gate kernel launch");
-        // forward states C_1..C_{nc-1}, [d_hv][d_qk] each
-        if ((e = tfla::launch_state(p, k, v, fgate_pre, ws.fwd, stream)) != hipSuccess)
+        // forward states C_1..C_{nc-1}, [d_hv][d_qk] each (preceded by C_0 when
+        // given), and C_T when a final-state gradient needs its coupling
+        tfla::Workspace fw = ws.fwd;
+        fw.c0 = io.c0;
+        fw.c_final = has_g ? ws.c_T : nullptr;
+        if ((e = tfla::launch_state(p, k, v, fgate_pre, fw, stream)) != hipSuccess)
             return hip_fail(e, "state kernel launch");
     }
     tfla::Workspace mirrored = ws.fwd;   // gate exponents of the mirrored chunks
@@ -280,17 +303,32 @@ int run_bwd(const tfla::Problem& p, const void* q, const void* k, const void* v,
         mirrored.a = ws.ar;
         mirrored.li = ws.lr;
     }
-    // reverse walk: D_0..D_{nc-2}, [d_hv][d_qk] each
+    // reverse walk: D_0..D_{nc-2}, [d_hv][d_qk] each, then D_{nc-1} = dC_T sqrt(d_qk)
+    // when given; dL/dC_0 = D_{-1} / sqrt(d_qk) on request
+    if (has_g && (e = tfla::launch_scale_copy(io.dc_final, ws.g_scaled, (size_t)p.B * p.H * p.dqk * p.dhv,
+                                              sqrtf((float)p.dqk), stream)) != hipSuccess)
+        return hip_fail(e, "final-state gradient copy");
     tfla::Workspace rev = ws.fwd;
     rev.states = ws.dstates;
+    rev.c0 = has_g ? ws.g_scaled : nullptr;
+    rev.c_final = io.dc0;
+    rev.end_scale = scale;
     rev.dot_partner = ws.fwd.states;
     rev.dots = ws.xpart;
+    rev.dot_slots = p.nc - 1 + (has_c0 ? 1 : 0);
+    rev.dot_off = has_c0 ? 1 : 0;
+    rev.dot_bound = nbound;
     if ((e = tfla::launch_state_rev(p, q, dh, fgate_pre, rev, stream)) != hipSuccess)
         return hip_fail(e, "reverse state kernel launch");
+    if (has_g && (e = tfla::launch_final_coupling(p, ws.g_scaled, ws.c_T, ws.xpart, ws.nx, nbound, stream)) !=
+                     hipSuccess)
+        return hip_fail(e, "final coupling kernel launch");
     mirrored.states = ws.dstates;
+    mirrored.c0 = has_g ? ws.g_scaled : nullptr;   // the last chunk reads the final-state gradient
     // dq = scale (e^{a_t} C_{k-1} dh_t + sum_{s<=t} w_ts (dh_t . v_s) k_s): contract d_hv, emit d_qk
     const tfla::Problem pc = grad_qk_problem(p);
     tfla::Workspace wq = ws.fwd;
+    wq.c0 = io.c0;   // the first chunk reads C_0 from the states
     wq.dot_partner = q;
     wq.dots = ws.dq_dots;
     if ((e = tfla::launch_intra_dq(pc, dh, v, k, fgate_pre, wq, dq, scale, stream)) != hipSuccess)
@@ -304,8 +342,8 @@ int run_bwd(const tfla::Problem& p, const void* q, const void* k, const void* v,
     // dv = scale (e^{a'_t} D_k^T k_t + sum_{s>=t} w_st (k_t . q_s) dh_s): mirrored, contract d_qk
     if ((e = tfla::launch_intra_dv(p, k, q, dh, fgate_pre, mirrored, dv, scale, stream)) != hipSuccess)
         return hip_fail(e, "dv kernel launch");
-    if ((e = tfla::launch_gate_grads(p, ws.xpart, ws.nx, ws.dq_dots, ws.dk_dots, ws.np, igate_pre, fgate_pre, dig,
-                                     dfg, ws.head_part, stream)) != hipSuccess)
+    if ((e = tfla::launch_gate_grads(p, ws.xpart, ws.nx, nbound, has_c0 || has_g, ws.dq_dots, ws.dk_dots, ws.np,
+                                     igate_pre, fgate_pre, dig, dfg, ws.head_part, stream)) != hipSuccess)
         return hip_fail(e, "gate gradient kernel launch");
     return TFLA_OK;
 }
@@ -344,6 +382,99 @@ int check_bwd(const void* q, const void* k, const void* v, const float* igate_pr
             if (overlaps(outs[i], outs[j])) return fail(TFLA_ERR_INVALID_ARG, "gradient outputs overlap");
     }
     return TFLA_OK;
+}
+
+// tfla_bwd_state's state buffers: fp32 [B,H,d_qk,d_hv], 16-byte aligned,
+// disjoint from every other tensor of the call; dc0 may be c0 or dc_final
+// itself (updated in place).
+int check_bwd_state_io(const tfla::Problem& p, const void* q, const void* k, const void* v, const float* igate_pre,
+                       const float* fgate_pre, const void* dh, const void* dq, const void* dk, const void* dv,
+                       const float* dig, const float* dfg, const BwdStateIO& io)
+{
+    for (const float* x : {io.c0, io.dc_final, (const float*)io.dc0})
+        if (x && !aligned(x, 16)) return fail(TFLA_ERR_INVALID_ARG, "c0, dc_final and dc0 must be 16-byte aligned");
+    const size_t esz = p.bf16 ? 2 : 4;
+    const size_t bht = (size_t)p.B * p.H * p.T;
+    const size_t sbytes = (size_t)p.B * p.H * p.dqk * p.dhv * 4;
+    Range others[11];
+    fwd_ranges(p, q, k, v, igate_pre, fgate_pre, dh, others);
+    others[6] = range_of(dq, bht * p.dqk * esz);
+    others[7] = range_of(dk, bht * p.dqk * esz);
+    others[8] = range_of(dv, bht * p.dhv * esz);
+    others[9] = range_of(dfg, gate_bytes(p));
+    others[10] = dig ? range_of(dig, bht * 4) : Range{0, 0};
+    const float* st[3] = {io.c0, io.dc_final, io.dc0};
+    for (int i = 0; i < 3; ++i) {
+        if (!st[i]) continue;
+        const Range r = range_of(st[i], sbytes);
+        for (const Range& o : others)
+            if (overlaps(r, o)) return fail(TFLA_ERR_INVALID_ARG, "c0, dc_final or dc0 overlaps another tensor");
+        for (int j = i + 1; j < 3; ++j) {
+            if (!st[j] || !overlaps(r, range_of(st[j], sbytes))) continue;
+            if (j == 2 && st[i] == st[j]) continue;   // dc0 in place of c0 or dc_final
+            return fail(TFLA_ERR_INVALID_ARG, "c0, dc_final and dc0 overlap (dc0 may only be one of them exactly)");
+        }
+    }
+    return TFLA_OK;
+}
+
+// tfla_bwd and tfla_bwd_state: validation, workspace, launches
+int bwd_entry(const void* q, const void* k, const void* v, const float* igate_pre, const float* fgate_pre,
+              const void* dh, void* dq, void* dk, void* dv, float* dig, float* dfg, int B, int H, int T, int d_qk,
+              int d_hv, int L, int variant, void* workspace, size_t workspace_bytes, void* stream,
+              const BwdStateIO* io)
+{
+    tfla::Problem p;
+    int rc = check_bwd(q, k, v, igate_pre, fgate_pre, dh, dq, dk, dv, dig, dfg, B, H, T, d_qk, d_hv, L, variant, &p);
+    if (rc) return rc;
+    const bool states = io != nullptr;
+    if (states && (rc = check_bwd_state_io(p, q, k, v, igate_pre, fgate_pre, dh, dq, dk, dv, dig, dfg, *io))) return rc;
+    BwdWorkspace ws;
+    const size_t need = bwd_layout(p, &ws, nullptr, states);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* base = workspace;
+    const bool reuse_fwd = (variant & TFLA_BWD_REUSE_FWD) != 0;
+    if (reuse_fwd && !workspace)
+        return fail(TFLA_ERR_INVALID_ARG, "TFLA_BWD_REUSE_FWD needs the forward pass's workspace");
+    if (reuse_fwd && states)
+        return fail(TFLA_ERR_INVALID_ARG, "TFLA_BWD_REUSE_FWD is for tfla_bwd only");
+    if (workspace) {
+        if (!aligned(workspace, 256)) return fail(TFLA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+        if (workspace_bytes < need)
+            return fail(TFLA_ERR_OUT_OF_MEMORY, "workspace of " + std::to_string(workspace_bytes) +
+                                                    " bytes is smaller than the " + std::to_string(need) + " needed");
+        const size_t esz = p.bf16 ? 2 : 4;
+        const size_t bht = (size_t)B * H * T;
+        Range tensors[14];
+        fwd_ranges(p, q, k, v, igate_pre, fgate_pre, dh, tensors);   // slot 3: dh, shaped like h
+        tensors[6] = range_of(dq, bht * d_qk * esz);
+        tensors[7] = range_of(dk, bht * d_qk * esz);
+        tensors[8] = range_of(dv, bht * d_hv * esz);
+        tensors[9] = range_of(dfg, gate_bytes(p));
+        tensors[10] = dig ? range_of(dig, bht * 4) : Range{0, 0};
+        const size_t sbytes = (size_t)B * H * d_qk * d_hv * 4;
+        tensors[11] = states && io->c0 ? range_of(io->c0, sbytes) : Range{0, 0};
+        tensors[12] = states && io->dc_final ? range_of(io->dc_final, sbytes) : Range{0, 0};
+        tensors[13] = states && io->dc0 ? range_of(io->dc0, sbytes) : Range{0, 0};
+        if ((rc = check_workspace_disjoint(workspace, need, tensors, 14))) return rc;
+    } else {
+        if (inject_alloc_fault())
+            return fail(TFLA_ERR_OUT_OF_MEMORY, "injected allocation failure (TFLA_FAULT=alloc)");
+        hipError_t e = hipMallocAsync(&base, need, s);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(TFLA_ERR_OUT_OF_MEMORY, std::string("workspace allocation of ") + std::to_string(need) +
+                                                    " bytes failed: " + hipGetErrorString(e));
+        }
+    }
+    bwd_layout(p, &ws, static_cast<char*>(base), states);
+    rc = run_bwd(p, q, k, v, igate_pre, fgate_pre, dh, dq, dk, dv, dig, dfg, ws, reuse_fwd,
+                 states ? *io : BwdStateIO{}, s);
+    if (!workspace && base) {
+        hipError_t e = hipFreeAsync(base, s);
+        if (e != hipSuccess && rc == TFLA_OK) rc = hip_fail(e, "workspace free");
+    }
+    return rc;
 }
 
 }  // namespace
@@ -581,48 +712,29 @@ int tfla_bwd(const void* q, const void* k, const void* v, const float* igate_pre
              const void* dh, void* dq, void* dk, void* dv, float* dig, float* dfg, int B, int H, int T, int d_qk,
              int d_hv, int L, int variant, void* workspace, size_t workspace_bytes, void* stream)
 {
+    return bwd_entry(q, k, v, igate_pre, fgate_pre, dh, dq, dk, dv, dig, dfg, B, H, T, d_qk, d_hv, L, variant,
+                     workspace, workspace_bytes, stream, nullptr);
+}
+
+size_t tfla_bwd_state_workspace_bytes(int B, int H, int T, int d_qk, int d_hv, int L, int variant)
+{
     tfla::Problem p;
-    int rc = check_bwd(q, k, v, igate_pre, fgate_pre, dh, dq, dk, dv, dig, dfg, B, H, T, d_qk, d_hv, L, variant, &p);
-    if (rc) return rc;
+    if (check_bwd_problem(B, H, T, d_qk, d_hv, L, variant, &p) != TFLA_OK) return 0;
     BwdWorkspace ws;
-    const size_t need = bwd_layout(p, &ws, nullptr);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    void* base = workspace;
-    const bool reuse_fwd = (variant & TFLA_BWD_REUSE_FWD) != 0;
-    if (reuse_fwd && !workspace)
-        return fail(TFLA_ERR_INVALID_ARG, "TFLA_BWD_REUSE_FWD needs the forward pass's workspace");
-    if (workspace) {
-        if (!aligned(workspace, 256)) return fail(TFLA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-        if (workspace_bytes < need)
-            return fail(TFLA_ERR_OUT_OF_MEMORY, "workspace of " + std::to_string(workspace_bytes) +
-                                                    " bytes is smaller than the " + std::to_string(need) + " needed");
-        const size_t esz = p.bf16 ? 2 : 4;
-        const size_t bht = (size_t)B * H * T;
-        Range tensors[11];
-        fwd_ranges(p, q, k, v, igate_pre, fgate_pre, dh, tensors);   // slot 3: dh, shaped like h
-        tensors[6] = range_of(dq, bht * d_qk * esz);
-        tensors[7] = range_of(dk, bht * d_qk * esz);
-        tensors[8] = range_of(dv, bht * d_hv * esz);
-        tensors[9] = range_of(dfg, gate_bytes(p));
-        tensors[10] = dig ? range_of(dig, bht * 4) : Range{0, 0};
-        if ((rc = check_workspace_disjoint(workspace, need, tensors, 11))) return rc;
-    } else {
-        if (inject_alloc_fault())
-            return fail(TFLA_ERR_OUT_OF_MEMORY, "injected allocation failure (TFLA_FAULT=alloc)");
-        hipError_t e = hipMallocAsync(&base, need, s);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return fail(TFLA_ERR_OUT_OF_MEMORY, std::string("workspace allocation of ") + std::to_string(need) +
-                                                    " bytes failed: " + hipGetErrorString(e));
-        }
-    }
-    bwd_layout(p, &ws, static_cast<char*>(base));
-    rc = run_bwd(p, q, k, v, igate_pre, fgate_pre, dh, dq, dk, dv, dig, dfg, ws, reuse_fwd, s);
-    if (!workspace && base) {
-        hipError_t e = hipFreeAsync(base, s);
-        if (e != hipSuccess && rc == TFLA_OK) rc = hip_fail(e, "workspace free");
-    }
-    return rc;
+    return bwd_layout(p, &ws, nullptr, true);
+}
+
+int tfla_bwd_state(const void* q, const void* k, const void* v, const float* igate_pre, const float* fgate_pre,
+                   const float* c0, const void* dh, const float* dc_final, void* dq, void* dk, void* dv, float* dig,
+                   float* dfg, float* dc0, int B, int H, int T, int d_qk, int d_hv, int L, int variant,
+                   void* workspace, size_t workspace_bytes, void* stream)
+{
+    BwdStateIO io;
+    io.c0 = c0;
+    io.dc_final = dc_final;
+    io.dc0 = dc0;
+    return bwd_entry(q, k, v, igate_pre, fgate_pre, dh, dq, dk, dv, dig, dfg, B, H, T, d_qk, d_hv, L, variant,
+                     workspace, workspace_bytes, stream, &io);
 }
 
 const char* tfla_error_string(int code)

@@ -57,6 +57,10 @@ def lib():
         L.tfla_bwd.restype = i
         L.tfla_bwd_workspace_bytes.argtypes = [i] * 7
         L.tfla_bwd_workspace_bytes.restype = sz
+        L.tfla_bwd_state.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp, vp, vp, vp, fp, fp, fp] + [i] * 7 + [vp, sz, vp]
+        L.tfla_bwd_state.restype = i
+        L.tfla_bwd_state_workspace_bytes.argtypes = [i] * 7
+        L.tfla_bwd_state_workspace_bytes.restype = sz
         L.tfla_dbg_gates.argtypes = [fp, fp, fp, fp, fp] + [i] * 6 + [vp]
         L.tfla_dbg_gates.restype = i
         L.tfla_dbg_states.argtypes = [vp, vp, fp, fp, fp] + [i] * 7 + [vp]
@@ -176,6 +180,19 @@ def tfla_bwd(q, k, v, igate_pre, fgate_pre, dh, dq, dk, dv, dig, dfg, B, H, T, d
                         _ptr(dk), _ptr(dv), _ptr(dig), _ptr(dfg), B, H, T, d_qk, d_hv, L, variant,
                         _ptr(workspace), workspace_bytes, _stream(stream))
     _check(rc, "tfla_bwd")
+
+
+def tfla_bwd_state_workspace_bytes(B, H, T, d_qk, d_hv, L, variant) -> int:
+    return lib().tfla_bwd_state_workspace_bytes(B, H, T, d_qk, d_hv, L, variant)
+
+
+def tfla_bwd_state(q, k, v, igate_pre, fgate_pre, c0, dh, dc_final, dq, dk, dv, dig, dfg, dc0, B, H, T, d_qk, d_hv,
+                   L, variant, workspace=None, workspace_bytes=0, stream=None):
+    """tfla_bwd_state(...): c0, dc_final, dc0 fp32 [B,H,d_qk,d_hv] or None."""
+    rc = lib().tfla_bwd_state(_ptr(q), _ptr(k), _ptr(v), _ptr(igate_pre), _ptr(fgate_pre), _ptr(c0), _ptr(dh),
+                              _ptr(dc_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dig), _ptr(dfg), _ptr(dc0),
+                              B, H, T, d_qk, d_hv, L, variant, _ptr(workspace), workspace_bytes, _stream(stream))
+    _check(rc, "tfla_bwd_state")
 
 
 def tfla_dbg_gates(igate_pre, fgate_pre, a_out, li_out, g_out, B, H, T, d_qk, L, variant, stream=None):

@@ -267,3 +267,34 @@ def test_workspace_must_not_overlap_a_tensor(L):
     assert bwd(ws=DQ, nws=bneed) == INVALID
     assert bwd(ws=DIG, nws=bneed) == INVALID
     assert bwd(ws=FG - 256 * 256, nws=bneed) == INVALID
+
+
+def bwd_state(c0=C0, dcf=CF, dc0=WS, variant=SIG | BF16, ws=None, nws=0, **kw):
+    a = dict(q=Q, k=K, v=V, ig=IG, fg=FG, dh=DH, dq=DQ, dk=DK, dv=DV, dig=DIG, dfg=DFG)
+    a.update(kw)
+    return tfla.lib().tfla_bwd_state(a["q"], a["k"], a["v"], a["ig"], a["fg"], c0, a["dh"], dcf, a["dq"], a["dk"],
+                                     a["dv"], a["dig"], a["dfg"], dc0, 2, 3, 300, 128, 256, 64, variant, ws, nws, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(c0=C0 + 8), INVALID), (dict(dc0=WS + 4), INVALID),            # misaligned state buffers
+    (dict(dc0=DQ), INVALID), (dict(c0=DH + 64), INVALID),               # overlap a tensor
+    (dict(dc0=C0 + 256), INVALID),                                      # partial overlap of c0
+    (dict(dcf=C0 + 16), INVALID),                                       # c0 and dc_final overlap
+    (dict(variant=SIG | BF16 | 0x200, ws=0x7000000000, nws=1 << 34), INVALID),  # no forward reuse here
+    (dict(dhv=0), INVALID),
+])
+def test_bwd_state_rejects_bad_arguments(L, kw, code):
+    if "dhv" in kw:
+        assert tfla.lib().tfla_bwd_state(Q, K, V, IG, FG, C0, DH, CF, DQ, DK, DV, DIG, DFG, WS, 2, 3, 300, 128, 0, 64,
+                                         SIG | BF16, None, 0, None) == code
+        return
+    assert bwd_state(**kw) == code
+    assert tfla.tfla_last_error()
+
+
+def test_bwd_state_workspace_bytes(L):
+    a = tfla.tfla_bwd_workspace_bytes(2, 3, 250, 128, 256, 64, SIG | BF16)
+    b = tfla.tfla_bwd_state_workspace_bytes(2, 3, 250, 128, 256, 64, SIG | BF16)
+    assert b > a > 0
+    assert tfla.tfla_bwd_state_workspace_bytes(2, 3, 250, 128, 192, 64, SIG | BF16) == 0
