@@ -196,6 +196,44 @@ def run_gpu_bwd(wl, L, steps, warmup, inputs_dev, dh):
     return ms, ms_reuse
 
 
+def run_gpu_decode(wl, steps_per_call, calls, warmup):
+    """tfla_fwd_recurrent from a carried state (decoding): microseconds per
+    call of `steps_per_call` steps over all B*H heads, and the HBM bytes the
+    step-by-step form must move (the fp32 state read and written once per
+    call, plus q, k, v, h and gates of the steps)."""
+    import torch
+    import workloads as W
+    from mlstm_sequence_amd import tfla
+
+    sub = wl.with_(T=steps_per_call)
+    inp = W.make_inputs(sub)
+    d = {n: (None if t is None else t.cuda()) for n, t in inp.items()}
+    gate = {0: tfla.MLSTM_SIG, 1: tfla.SCALAR_DECAY, 2: tfla.GLA_KEY}[wl.variant]
+    var = tfla.variant_of(gate, d["q"].dtype)
+    state = W.initial_state(wl.B, wl.H, wl.dqk, wl.dhv, seed=wl.seed + 2).cuda()
+    h = torch.empty_like(d["v"])
+    call = lambda: tfla.tfla_fwd_recurrent(d["q"], d["k"], d["v"], d["igate_pre"], d["fgate_pre"], state, h,
+                                           wl.B, wl.H, steps_per_call, wl.dqk, wl.dhv, var)
+    for _ in range(warmup):
+        call()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(calls):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / calls * 1e3
+    e = 2 if wl.dtype_name == "bf16" else 4
+    bh = wl.B * wl.H
+    gate_bytes = {0: 8, 1: 0, 2: 4 * wl.dqk}[wl.variant] * steps_per_call * bh
+    nbytes = bh * (2 * 4 * wl.dqk * wl.dhv + steps_per_call * ((2 * wl.dqk + 2 * wl.dhv) * e)) + gate_bytes
+    return {"steps_per_call": steps_per_call, "us_per_call": us, "tokens_per_s": wl.B * steps_per_call / (us * 1e-6),
+            "hbm_bytes_per_call": nbytes, "achieved_GBps": nbytes / (us * 1e-6) / 1e9,
+            "hbm_frac": nbytes / (us * 1e-6) / PEAK_HBM}
+
+
 # --------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(wl, target_s=15.0):
     """The oracle (plain C recurrence in double, OpenMP over heads) on all
@@ -386,6 +424,12 @@ def main():
         Lb = min(bwd, key=lambda L: bwd[L]["ms_per_step"])
         out["backward"] = dict(bwd[Lb], L=Lb, sweep={str(L): x for L, x in bwd.items()})
         del dh
+    # Decoding with the step-by-step form (context beside the metric): one
+    # step and 16 steps per call from a carried fp32 state, every head.
+    out["decode"] = [run_gpu_decode(wl, n, 50, 5) for n in (1, 16)]
+    for x in out["decode"]:
+        log(f"decode {x['steps_per_call']} step(s)/call: {x['us_per_call']:.1f} us, "
+            f"{x['achieved_GBps']:.0f} GB/s ({100 * x['hbm_frac']:.1f}% of HBM peak)")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(wl)
