@@ -211,6 +211,21 @@ __device__ __forceinline__ void store2(float* p, float x, float y)
     *reinterpret_cast<f32x2*>(p) = f32x2{x, y};
 }
 
+// store four consecutive elements (8-byte aligned for bf16, 16 for fp32)
+__device__ __forceinline__ void store4(bf16* p, float x, float y, float z, float w)
+{
+    bf16x4 t;
+    t[0] = to_bf16(x);
+    t[1] = to_bf16(y);
+    t[2] = to_bf16(z);
+    t[3] = to_bf16(w);
+    *reinterpret_cast<bf16x4*>(p) = t;
+}
+__device__ __forceinline__ void store4(float* p, float x, float y, float z, float w)
+{
+    *reinterpret_cast<f32x4*>(p) = f32x4{x, y, z, w};
+}
+
 // ---- scalar math -----------------------------------------------------------
 // 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

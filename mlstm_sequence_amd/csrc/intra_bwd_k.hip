@@ -11,4 +11,10 @@ hipError_t launch_intra_dk(const Problem& p, const void* q, const void* k, const
     return dispatch_type<kNatState | kMirror | kRowDots>(p, q, k, v, fgate_pre, ws, out, scale, stream);
 }
 
+hipError_t launch_intra_dk_p(const Problem& p, const void* q, const void* k, const void* v, const float* fgate_pre,
+                             const Workspace& ws, void* out, float scale, hipStream_t stream)
+{
+    return dispatch_type<kNatState | kMirror | kRowDots | kGivenP>(p, q, k, v, fgate_pre, ws, out, scale, stream);
+}
+
 }  // namespace tfla

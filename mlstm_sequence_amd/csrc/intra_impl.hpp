@@ -73,6 +73,7 @@ template <typename T, int DQK, int BV, int CW> struct IntraLds {
 // computes.  A C^T block and a K/V tile are never in flight together, so they
 // share the registers.
 template <typename T, int DQK, int BV, int CW, int NTH> struct Prefetch {
+    typedef typename Elem<T>::frag Frag;
     static constexpr int VEC = Elem<T>::vec;
     static constexpr int NC = BV * CW / 8 / NTH;          // C^T block: 8 floats per item
     static constexpr int NK = 64 * DQK / VEC / NTH;       // K tile: 16 bytes per item
@@ -83,6 +84,7 @@ template <typename T, int DQK, int BV, int CW, int NTH> struct Prefetch {
         struct {
             Vec16<T> k[NK];
             Vec16<T> v[NV];
+            Frag p[2][2];   // given-P mode: this wave's P fragments of the tile
         } kv;
     };
     float li, a;
@@ -104,12 +106,19 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
                                                            T* __restrict__ h, int H, int T_, int dhv, int L,
                                                            int nc, int c0, float scale,
                                                            const T* __restrict__ partner,
-                                                           float* __restrict__ dots)
+                                                           float* __restrict__ dots, T* __restrict__ pout,
+                                                           const T* __restrict__ pin)
 {
     constexpr bool NAT = (MODE & kNatState) != 0, REV = (MODE & kMirror) != 0, DOTS = (MODE & kRowDots) != 0;
     // per-channel gate: decay inside the contraction (forward, dv), or on the
     // output columns (dq, dk: the contracted index is the value channel)
     constexpr bool OUTDECAY = GATE == kGla && NAT, INDECAY = GATE == kGla && !NAT;
+    // P = the decayed, masked S of a chunk ([B*H][T][L], row = query step,
+    // column = key step - chunk start): written (EMITP) or read (GIVENP;
+    // mirrored: read transposed, row = the key's step, column = the query's)
+    // instead of computed; per-step gates only
+    constexpr bool EMITP = (MODE & kEmitP) != 0, GIVENP = (MODE & kGivenP) != 0;
+    static_assert(!(EMITP || GIVENP) || GATE != kGla, "shared P covers the per-step gates only");
     constexpr int NTH = 64 * NW;
     constexpr int BQ = 32 * NW;           // query rows per workgroup
     // C^T channels per stage: 128 (two stages at d_qk = 256) when the
@@ -225,19 +234,45 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
         }
     };
     auto fetch_kv = [&](int s0) {
+        if constexpr (!GIVENP) {
 #pragma unroll
-        for (int u = 0; u < PF::NK; ++u) {
-            const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
-            const int s = row(min(s0 + r, T_ - 1));
-            pf.kv.k[u].load(kb + (size_t)s * DQK + c);
+            for (int u = 0; u < PF::NK; ++u) {
+                const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
+                const int s = row(min(s0 + r, T_ - 1));
+                pf.kv.k[u].load(kb + (size_t)s * DQK + c);
+            }
         }
+        if constexpr (!EMITP) {
 #pragma unroll
-        for (int u = 0; u < PF::NV; ++u) {
-            const int idx = tid + NTH * u, r = idx / (BV / VEC), c = (idx % (BV / VEC)) * VEC;
-            const int s = row(min(s0 + r, T_ - 1));
-            pf.kv.v[u].load(vb + (size_t)s * dhv + v0 + c);
+            for (int u = 0; u < PF::NV; ++u) {
+                const int idx = tid + NTH * u, r = idx / (BV / VEC), c = (idx % (BV / VEC)) * VEC;
+                const int s = row(min(s0 + r, T_ - 1));
+                pf.kv.v[u].load(vb + (size_t)s * dhv + v0 + c);
+            }
         }
-        if (GATE == kSig && tid < 64) {
+        if constexpr (GIVENP && !REV) {
+            // this lane's P row, keys in the order the accumulator holds them
+            const T* pr = pin + (bh * (size_t)T_ + tqc) * L + (s0 - cs) + 4 * hh;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+                    pf.kv.p[mt][half] = load4x2(pr + 32 * mt + 16 * half, pr + 32 * mt + 16 * half + 8);
+        } else if constexpr (GIVENP) {
+            // mirrored: element (logical row r, logical key c) is P[row(c)][row(r) - cs];
+            // for one element index all lanes of a half read one P row
+            const T* pc = pin + bh * (size_t)T_ * L + (row(tqc) - cs);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int c = min(s0 + 32 * mt + 16 * half + 8 * (e >> 2) + 4 * hh + (e & 3), T_ - 1);
+                        frag_set(pf.kv.p[mt][half], e, to_float(pc[(size_t)row(c) * L]));
+                    }
+        }
+        if (GATE == kSig && !GIVENP && tid < 64) {
             const int s = min(s0 + tid, T_ - 1);
             pf.li = lb[s];
             if (!REV) pf.a = ab[s];
@@ -245,7 +280,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     };
     auto store_kv = [&](int s0, int ref_row) {
 #pragma unroll
-        for (int u = 0; u < PF::NK; ++u) {
+        for (int u = 0; u < (GIVENP ? 0 : PF::NK); ++u) {
             const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
             if (INDECAY) {
                 const int s = min(s0 + r, T_ - 1);
@@ -260,7 +295,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
             pf.kv.k[u].store(&sm.kv.ks[r][c]);
         }
 #pragma unroll
-        for (int u = 0; u < PF::NV; ++u) {
+        for (int u = 0; u < (EMITP ? 0 : PF::NV); ++u) {
             const int idx = tid + NTH * u, r = idx / (BV / VEC), c = (idx % (BV / VEC)) * VEC;
             if (OUTDECAY) {
                 // output-side decay: value row s scaled by e^{a_R - a_s} per
@@ -277,7 +312,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
             }
             pf.kv.v[u].store(&sm.kv.vs[r][c]);
         }
-        if (GATE == kSig && tid < 64) sm.bcol[tid] = (REV ? pf.li : pf.li - pf.a) * kLog2e;
+        if (GATE == kSig && !GIVENP && tid < 64) sm.bcol[tid] = (REV ? pf.li : pf.li - pf.a) * kLog2e;
     };
 
     f32x16 acc[NT];
@@ -289,7 +324,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     // states hold C before chunks 1..nc-1, preceded by C_0 when one is given
     // (c0 = 1); mirrored: the state of chunks kc+1.. in slot kc, the last
     // chunk's (a final-state gradient) in slot nc-1 when one is given (c0 = 1)
-    const bool inter = REV ? kc < nc - 1 + c0 : (kc > 0 || c0);
+    const bool inter = EMITP ? false : REV ? kc < nc - 1 + c0 : (kc > 0 || c0);
     if (inter) {
         const size_t slot = bh * (nc - 1 + c0) + (REV ? kc : kc - 1 + c0);
         const float* st = NAT ? states + slot * DQK * (size_t)dhv + v0
@@ -327,7 +362,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     }
 
     // ---------------- intra-chunk term, tiled along the chunk
-    if (!INDECAY && !inter) load_q(-1);
+    if (!INDECAY && !GIVENP && !inter) load_q(-1);
     // output-side decay: acc holds its partial sums in the frame of step
     // fref (true value = acc e^{a_t - a_fref}; fref < 0: the chunk start,
     // a = 0); the frame moves forward half by half, each move a factor <= 1
@@ -361,6 +396,12 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
         }
         __syncthreads();
         store_kv(s0, ref_row);
+        Frag pcur[2][2];   // given P: this tile's fragments, before the next fetch reuses pf
+        if constexpr (GIVENP) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+                for (int half = 0; half < 2; ++half) pcur[mt][half] = pf.kv.p[mt][half];
+        }
         __syncthreads();
         if (j + 1 < nkv) fetch_kv(s0 + 64);
 
@@ -370,6 +411,26 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
             if (slo > tlo + 31 || slo >= T_) continue;   // wholly above the diagonal, or past the end
             const bool diag = slo == tlo;
             if (OUTDECAY) move_frame(min(slo + 31, T_ - 1));
+            if constexpr (GIVENP) {
+                // P from memory; pairs above the diagonal or past the end may
+                // hold anything there and are selected to zero
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    Frag pfr = pcur[mt][half];
+                    if (diag || slo + 31 >= T_) {
+                        for (int e = 0; e < 8; ++e) {
+                            const int key = slo + 16 * half + 8 * (e >> 2) + 4 * hh + (e & 3);
+                            if (key > tlo + i32 || key >= T_) frag_set(pfr, e, 0.0f);
+                        }
+                    }
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        const Frag vf = frag_tr(sm.kv.vs, 32 * mt + 16 * half, 32 * nt, lane);
+                        acc[nt] = mma32(pfr, vf, acc[nt]);
+                    }
+                }
+                continue;
+            }
             // S^T (32 key steps x 32 query rows of this wave)
             f32x16 st;
             for (int r = 0; r < 16; ++r) st[r] = 0.0f;
@@ -390,6 +451,17 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
                 }
                 st[r] = (diag && sr > i32) ? 0.0f : p;
             }
+            if constexpr (EMITP) {
+                // P row t (this lane), keys slo + sr: four runs of 4 consecutive keys
+                const int t = tlo + i32;
+                if (t < T_) {
+                    T* prow = pout + (bh * (size_t)T_ + t) * L + (slo - cs) + 4 * hh;
+#pragma unroll
+                    for (int g4 = 0; g4 < 4; ++g4)
+                        store4(prow + 8 * g4, st[4 * g4], st[4 * g4 + 1], st[4 * g4 + 2], st[4 * g4 + 3]);
+                }
+                continue;
+            }
             // acc += P V: 16-step halves, in accumulator order
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
@@ -405,6 +477,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     }
 
     // ---------------- output
+    if constexpr (EMITP) return;
     if (OUTDECAY) {
         // out of the frame: e^{a_t - a_fref}, t within 31 steps before fref
 #pragma unroll
@@ -479,7 +552,7 @@ hipError_t launch_intra_t(const Problem& p, const void* q, const void* k, const 
     intra_kernel<T, GATE, DQK, BV, NW, MODE><<<blocks, 64 * NW, 0, stream>>>(
         static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), ws.a, ws.li, fg,
         ws.states, static_cast<T*>(h), p.H, p.T, p.dhv, p.L, p.nc, ws.c0 != nullptr, scale,
-        static_cast<const T*>(ws.dot_partner), ws.dots);
+        static_cast<const T*>(ws.dot_partner), ws.dots, static_cast<T*>(ws.p_out), static_cast<const T*>(ws.p_in));
     return hipGetLastError();
 }
 
@@ -519,9 +592,11 @@ template <typename T, int GATE, int DQK, int BV, int MODE>
 hipError_t dispatch_nw(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
                        const Workspace& ws, void* h, float scale, hipStream_t stream)
 {
-    // a workgroup's query rows never straddle a chunk
-    const int rows = intra_rows(p);
-    if constexpr (sizeof(T) == 2 && DQK <= 256) {
+    // a workgroup's query rows never straddle a chunk; writing P holds no
+    // accumulators, so 8 waves fit a 512-wide contraction there
+    const int rows = MODE == kEmitP ? intra_rows(Problem{p.B, p.H, p.T, 256, p.dhv, p.L, p.nc, p.gate, p.bf16})
+                                    : intra_rows(p);
+    if constexpr (sizeof(T) == 2 && (DQK <= 256 || MODE == kEmitP)) {
         if (rows == 256) return launch_intra_t<T, GATE, DQK, BV, 8, MODE>(p, q, k, v, fg, ws, h, scale, stream);
     }
     if (rows >= 128) return launch_intra_t<T, GATE, DQK, BV, 4, MODE>(p, q, k, v, fg, ws, h, scale, stream);
@@ -565,7 +640,9 @@ hipError_t dispatch_gate(const Problem& p, const void* q, const void* k, const v
     switch (p.gate) {
     case kSig: return dispatch_dqk<T, kSig, MODE>(p, q, k, v, fg, ws, h, scale, stream);
     case kScalar: return dispatch_dqk<T, kScalar, MODE>(p, q, k, v, fg, ws, h, scale, stream);
-    default: return dispatch_dqk<T, kGla, MODE>(p, q, k, v, fg, ws, h, scale, stream);
+    default:
+        if constexpr ((MODE & (kEmitP | kGivenP)) == 0) return dispatch_dqk<T, kGla, MODE>(p, q, k, v, fg, ws, h, scale, stream);
+        return hipErrorInvalidValue;
     }
 }
 

@@ -9,7 +9,7 @@ namespace tfla {
 enum GateKind { kSig = 0, kScalar = 1, kGla = 2 };
 
 // Operand modes of the intra-chunk kernel (bit set) for the gradient products.
-enum IntraMode { kNatState = 1, kMirror = 2, kRowDots = 4 };
+enum IntraMode { kNatState = 1, kMirror = 2, kRowDots = 4, kEmitP = 8, kGivenP = 16 };
 
 // Problem description shared by the launchers.  Sizes in elements.
 struct Problem {
@@ -43,6 +43,9 @@ struct Workspace {
     // boundaries per head in dots; factor on the end state written to c_final
     int dot_slots = 0, dot_off = 0, dot_bound = 0;
     float end_scale = 1.0f;
+    // intra-chunk kEmitP: P out ([B,H,T,L], I/O type); kGivenP: P read
+    void* p_out = nullptr;
+    const void* p_in = nullptr;
 };
 
 // Segmented state walk (few heads, long sequences): number of segments P
@@ -90,6 +93,14 @@ hipError_t launch_intra_dq(const Problem& p, const void* q, const void* k, const
                            const Workspace& ws, void* out, float scale, hipStream_t stream);
 hipError_t launch_intra_dk(const Problem& p, const void* q, const void* k, const void* v, const float* fgate_pre,
                            const Workspace& ws, void* out, float scale, hipStream_t stream);
+// The shared P of dq and dk (per-step gates): kEmitP over the dq operands,
+// then dq and dk with kGivenP reading it (dk transposed, in mirrored order).
+hipError_t launch_intra_p(const Problem& p, const void* q, const void* k, const float* fgate_pre,
+                          const Workspace& ws, hipStream_t stream);
+hipError_t launch_intra_dq_p(const Problem& p, const void* q, const void* k, const void* v, const float* fgate_pre,
+                             const Workspace& ws, void* out, float scale, hipStream_t stream);
+hipError_t launch_intra_dk_p(const Problem& p, const void* q, const void* k, const void* v, const float* fgate_pre,
+                             const Workspace& ws, void* out, float scale, hipStream_t stream);
 hipError_t launch_intra_dv(const Problem& p, const void* q, const void* k, const void* v, const float* fgate_pre,
                            const Workspace& ws, void* out, float scale, hipStream_t stream);
 

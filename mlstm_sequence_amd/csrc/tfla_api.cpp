@@ -213,6 +213,7 @@ struct BwdWorkspace {
     float* xpart;     // [B,H,nc-1][nx]: partials of <D_k, C_k> across each chunk boundary
                       // (per-channel gate: [B,H,nc-1,d_qk][nx])
     double* head_part;  // [B,H]: per-(batch, head) part of the fixed decay's gradient
+    void* pmat;       // per-step gates: the shared P of dq and dk [B,H,T,L], I/O type
     float* g_scaled;  // tfla_bwd_state: the final-state gradient times sqrt(d_qk) [B,H,d_qk,d_hv]
     float* c_T;       // tfla_bwd_state: the recomputed final state [B,H,d_qk,d_hv]
     int np, nx;
@@ -232,6 +233,16 @@ tfla::Problem grad_qk_problem(const tfla::Problem& p)
     pc.dqk = p.dhv;
     pc.dhv = p.dqk;
     return pc;
+}
+
+// dq and dk take a P computed once (per-step gates) where each would
+// otherwise recompute S = dh V^T for several value tiles of d_qk; with one
+// tile the separate P pass costs more than it saves (measured).
+bool shares_p(const tfla::Problem& p)
+{
+    if (p.gate == tfla::kGla) return false;
+    const tfla::Problem pc = grad_qk_problem(p);
+    return pc.dhv / tfla::intra_value_tile(pc) >= 2;
 }
 
 // with_states: the layout of tfla_bwd_state (a slot for C_0 among the
@@ -259,6 +270,8 @@ size_t bwd_layout(const tfla::Problem& p, BwdWorkspace* ws, char* base, bool wit
     const size_t per_boundary = (size_t)ws->nx * (p.gate == tfla::kGla ? p.dqk : 1);
     ws->xpart = rslots > 0 ? take(bh * rslots * per_boundary * 4) : nullptr;
     ws->head_part = p.gate == tfla::kScalar ? reinterpret_cast<double*>(take(bh * 8)) : nullptr;
+    const size_t pbytes = shares_p(p) ? bh * p.T * p.L * (p.bf16 ? 2 : 4) : 0;
+    ws->pmat = pbytes ? take(pbytes) : nullptr;
     const size_t sbytes = bh * p.dqk * p.dhv * 4;
     ws->g_scaled = with_states ? take(sbytes) : nullptr;
     ws->c_T = with_states ? take(sbytes) : nullptr;
@@ -327,18 +340,32 @@ int run_bwd(const tfla::Problem& p, const void* q, const void* k, const void* v,
     mirrored.c0 = has_g ? ws.g_scaled : nullptr;   // the last chunk reads the final-state gradient
     // dq = scale (e^{a_t} C_{k-1} dh_t + sum_{s<=t} w_ts (dh_t . v_s) k_s): contract d_hv, emit d_qk
     const tfla::Problem pc = grad_qk_problem(p);
+    // P_ts = w_ts (dh_t . v_s) once per chunk, shared by dq (P k) and dk (P^T q)
+    const bool shared_p = shares_p(p);
+    if (shared_p) {
+        tfla::Workspace wp = ws.fwd;
+        wp.p_out = ws.pmat;
+        tfla::Problem pp = pc;
+        pp.dhv = 64;   // one value tile: every query tile of the grid computes its P rows once
+        if ((e = tfla::launch_intra_p(pp, dh, v, fgate_pre, wp, stream)) != hipSuccess)
+            return hip_fail(e, "shared P kernel launch");
+    }
     tfla::Workspace wq = ws.fwd;
     wq.c0 = io.c0;   // the first chunk reads C_0 from the states
     wq.dot_partner = q;
     wq.dots = ws.dq_dots;
-    if ((e = tfla::launch_intra_dq(pc, dh, v, k, fgate_pre, wq, dq, scale, stream)) != hipSuccess)
-        return hip_fail(e, "dq kernel launch");
+    wq.p_in = ws.pmat;
+    e = shared_p ? tfla::launch_intra_dq_p(pc, dh, v, k, fgate_pre, wq, dq, scale, stream)
+                 : tfla::launch_intra_dq(pc, dh, v, k, fgate_pre, wq, dq, scale, stream);
+    if (e != hipSuccess) return hip_fail(e, "dq kernel launch");
     // dk = scale (e^{a'_t} D_k v_t + sum_{s>=t} w_st (v_t . dh_s) q_s): mirrored, contract d_hv
     tfla::Workspace wk = mirrored;
     wk.dot_partner = k;
     wk.dots = ws.dk_dots;
-    if ((e = tfla::launch_intra_dk(pc, v, dh, q, fgate_pre, wk, dk, scale, stream)) != hipSuccess)
-        return hip_fail(e, "dk kernel launch");
+    wk.p_in = ws.pmat;
+    e = shared_p ? tfla::launch_intra_dk_p(pc, v, dh, q, fgate_pre, wk, dk, scale, stream)
+                 : tfla::launch_intra_dk(pc, v, dh, q, fgate_pre, wk, dk, scale, stream);
+    if (e != hipSuccess) return hip_fail(e, "dk kernel launch");
     // dv = scale (e^{a'_t} D_k^T k_t + sum_{s>=t} w_st (k_t . q_s) dh_s): mirrored, contract d_qk
     if ((e = tfla::launch_intra_dv(p, k, q, dh, fgate_pre, mirrored, dv, scale, stream)) != hipSuccess)
         return hip_fail(e, "dv kernel launch");
