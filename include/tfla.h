@@ -18,9 +18,10 @@
  * The library evaluates it chunkwise (TFLA abstract: chunkwise-parallel
  * formulation with a second level of sequence tiling inside each chunk, so
  * the chunk size L is not bounded by on-chip memory): a gate prefix-sum
- * kernel, an inter-chunk state kernel that materialises the fp32 state at
- * every chunk boundary (the "ParallelChunk" form of the README), and an
- * intra-chunk kernel on bf16 matrix cores.
+ * kernel, an inter-chunk state kernel that walks the state in fp32 and
+ * materialises it at every chunk boundary (the "ParallelChunk" form of the
+ * README) in the I/O type, the operand type of the matrix-core products that
+ * read it, and an intra-chunk kernel on bf16 matrix cores.
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
@@ -181,8 +182,8 @@ int tfla_fwd_recurrent(const void* q, const void* k, const void* v,
  * pre-activations through their sigmoids (a log forget gate at its floor of
  * -100 passes no gradient).  The states C_k are recomputed
  * (nothing is kept from the forward call); the gradient into the state at
- * each chunk boundary is walked backwards over the chunks and materialised
- * in fp32 like C_k; dq, dk and dv are intra-chunk matrix-core products over
+ * each chunk boundary is walked backwards over the chunks in fp32 and
+ * materialised like C_k; dq, dk and dv are intra-chunk matrix-core products over
  * 64-step tiles as in the forward pass.
  *
  *   q, k, v, igate_pre, fgate_pre: as for tfla_fwd.
@@ -267,15 +268,16 @@ size_t tfla_bwd_state_workspace_bytes(int B, int H, int T, int d_qk, int d_hv, i
  * other kernels; this hook evaluates the same closed form.
  *
  * tfla_dbg_states -- gates plus the inter-chunk state kernel.  states_out
- * (device, fp32) receives the state after chunks 1..N_c-1 (N_c = ceil(T/L)),
- * each stored TRANSPOSED as [d_hv][d_qk]: layout [B,H,N_c-1,d_hv,d_qk].
+ * (device, the I/O type: bf16 with TFLA_IO_BF16, else fp32) receives the
+ * state after chunks 1..N_c-1 (N_c = ceil(T/L)), each rounded to that type
+ * (RNE) and stored TRANSPOSED as [d_hv][d_qk]: layout [B,H,N_c-1,d_hv,d_qk].
  * q is not needed; h is untouched.
  */
 int tfla_dbg_gates(const float* igate_pre, const float* fgate_pre,
                    float* a_out, float* li_out, float* g_out,
                    int B, int H, int T, int d_qk, int L, int variant, void* stream);
 int tfla_dbg_states(const void* k, const void* v,
-                    const float* igate_pre, const float* fgate_pre, float* states_out,
+                    const float* igate_pre, const float* fgate_pre, void* states_out,
                     int B, int H, int T, int d_qk, int d_hv, int L, int variant, void* stream);
 
 /* Static description of a status code. */

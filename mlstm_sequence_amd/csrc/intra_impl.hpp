@@ -75,12 +75,12 @@ template <typename T, int DQK, int BV, int CW> struct IntraLds {
 template <typename T, int DQK, int BV, int CW, int NTH> struct Prefetch {
     typedef typename Elem<T>::frag Frag;
     static constexpr int VEC = Elem<T>::vec;
-    static constexpr int NC = BV * CW / 8 / NTH;          // C^T block: 8 floats per item
+    static constexpr int NC = BV * CW / 8 / NTH;          // C^T block: 8 elements per item
     static constexpr int NK = 64 * DQK / VEC / NTH;       // K tile: 16 bytes per item
     static constexpr int NV = 64 * BV / VEC / NTH;        // V tile: 16 bytes per item
     static_assert(NC >= 1 && NK >= 1 && NV >= 1, "tile too small for the workgroup");
     union {
-        f32x4 c[NC][2];
+        Vec16<T> c[NC][8 / VEC];
         struct {
             Vec16<T> k[NK];
             Vec16<T> v[NV];
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
                                                            const T* __restrict__ v, const float* __restrict__ a,
                                                            const float* __restrict__ li,
                                                            const float* __restrict__ fg,
-                                                           const float* __restrict__ states,
+                                                           const T* __restrict__ states,
                                                            T* __restrict__ h, int H, int T_, int dhv, int L,
                                                            int nc, int c0, float scale,
                                                            const T* __restrict__ partner,
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     };
 
     // ---- stage loaders (global -> registers) and writers (registers -> LDS)
-    auto fetch_c = [&](const float* st, int cb) {
+    auto fetch_c = [&](const T* st, int cb) {
 #pragma unroll
         for (int u = 0; u < PF::NC; ++u) {
             const int idx = tid + NTH * u;
@@ -200,17 +200,14 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
                 // column vr of 8 contraction rows: each load is one row's
                 // run of consecutive columns across the lanes
                 const int vr = idx % BV, c8 = (idx / BV) * 8;
-                const float* src = st + (size_t)(cb + c8) * dhv + vr;
+                const T* src = st + (size_t)(cb + c8) * dhv + vr;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    pf.c[u][0][e] = src[(size_t)e * dhv];
-                    pf.c[u][1][e] = src[(size_t)(4 + e) * dhv];
-                }
+                for (int e = 0; e < 8; ++e) pf.c[u][e / VEC].v[e % VEC] = src[(size_t)e * dhv];
             } else {
                 const int vr = idx / (CW / 8), c8 = (idx % (CW / 8)) * 8;
-                const float* src = st + (size_t)vr * DQK + cb + c8;
-                pf.c[u][0] = *reinterpret_cast<const f32x4*>(src);
-                pf.c[u][1] = *reinterpret_cast<const f32x4*>(src + 4);
+                const T* src = st + (size_t)vr * DQK + cb + c8;
+#pragma unroll
+                for (int x = 0; x < 8 / VEC; ++x) pf.c[u][x].load(src + VEC * x);
             }
         }
     };
@@ -220,17 +217,8 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
             const int idx = tid + NTH * u;
             const int vr = NAT ? idx % BV : idx / (CW / 8);
             const int c8 = NAT ? (idx / BV) * 8 : (idx % (CW / 8)) * 8;
-            if constexpr (sizeof(T) == 2) {
-                Vec16<T> x;
-                for (int e = 0; e < 4; ++e) {
-                    x.set(e, pf.c[u][0][e]);
-                    x.set(4 + e, pf.c[u][1][e]);
-                }
-                x.store(&sm.cs[vr][c8]);
-            } else {
-                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(&sm.cs[vr][c8])) = pf.c[u][0];
-                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(&sm.cs[vr][c8 + 4])) = pf.c[u][1];
-            }
+#pragma unroll
+            for (int x = 0; x < 8 / VEC; ++x) pf.c[u][x].store(&sm.cs[vr][c8 + VEC * x]);
         }
     };
     auto fetch_kv = [&](int s0) {
@@ -327,8 +315,8 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     const bool inter = EMITP ? false : REV ? kc < nc - 1 + c0 : (kc > 0 || c0);
     if (inter) {
         const size_t slot = bh * (nc - 1 + c0) + (REV ? kc : kc - 1 + c0);
-        const float* st = NAT ? states + slot * DQK * (size_t)dhv + v0
-                              : states + (slot * dhv + v0) * DQK;
+        const T* st = NAT ? states + slot * DQK * (size_t)dhv + v0
+                          : states + (slot * dhv + v0) * DQK;
         fetch_c(st, 0);
         load_q(-1);
         for (int cb = 0; cb < DQK; cb += CW) {
@@ -551,7 +539,7 @@ hipError_t launch_intra_t(const Problem& p, const void* q, const void* k, const 
     const int blocks = p.B * p.H * nqt * (p.dhv / BV);
     intra_kernel<T, GATE, DQK, BV, NW, MODE><<<blocks, 64 * NW, 0, stream>>>(
         static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), ws.a, ws.li, fg,
-        ws.states, static_cast<T*>(h), p.H, p.T, p.dhv, p.L, p.nc, ws.c0 != nullptr, scale,
+        static_cast<const T*>(ws.states), static_cast<T*>(h), p.H, p.T, p.dhv, p.L, p.nc, ws.c0 != nullptr, scale,
         static_cast<const T*>(ws.dot_partner), ws.dots, static_cast<T*>(ws.p_out), static_cast<const T*>(ws.p_in));
     return hipGetLastError();
 }

@@ -24,7 +24,9 @@ struct Workspace {
     float* a;        // [B,H,T] (GLA: [B,H,T,dqk]) chunk-local log-forget sums; NULL for kScalar
     float* li;       // [B,H,T] log input gate; kSig only
     float* g;        // [B,H,nc] (GLA: [B,H,nc,dqk]); NULL for kScalar
-    float* states;   // [B,H,ns,dhv,dqk] fp32, transposed states before chunks
+    void* states;    // [B,H,ns,dhv,dqk] I/O type, transposed states before chunks
+                     // (walked in fp32; the intra-chunk kernel rounds them to
+                     // the I/O type for its matrix cores anyway)
                      // 1..nc-1 (ns = nc-1), or 0..nc-1 with an initial state (ns = nc)
     const float* c0 = nullptr;   // caller's initial state [B,H,dqk,dhv] (NULL: zero)
     float* c_final = nullptr;    // caller's final-state output [B,H,dqk,dhv] (NULL: none)
@@ -33,7 +35,7 @@ struct Workspace {
     // intra-chunk gradient modes with kRowDots: per output row and value
     // tile, the dot product of the fp32 output row with the same row of
     // `dot_partner` (an I/O-typed [B,H,T,out] tensor), into dots [B,H,T][out/BV].
-    // Reverse state walk: `dot_partner` = the forward states (fp32, the
+    // Reverse state walk: `dot_partner` = the forward states (the type and
     // layout of `states`), dots = per-wave partials of <D_m, C_m>
     // [B,H,nc-1][state_dot_parts(p)].
     const void* dot_partner = nullptr;

@@ -7,8 +7,10 @@
 //   C_k = diag(e^{g_k}) C_{k-1} + sum_{s in chunk k} w_s k_s v_s^T,
 //   w_s = e^{g_k - a_s + li_s}    (per key channel c for the GLA gate:
 //                                  e^{g_{k,c} - a_{s,c}})
-// from C_0 = 0 or a given initial state.  The state before chunk k (k >= 1,
-// and k = 0 when an initial state is given) is written in fp32, transposed
+// from C_0 = 0 or a given initial state, in fp32.  The state before chunk k
+// (k >= 1, and k = 0 when an initial state is given) is written in the I/O
+// type (the intra-chunk kernel's matrix-core operand type, to which it would
+// round an fp32 copy anyway: half the bytes for bf16), transposed
 // ([d_hv][d_qk]) so the intra-chunk kernel reads it as contiguous
 // matrix-core B operands.  On request the walk continues through the last
 // (possibly partial) chunk and writes the final state C_T in the caller's
@@ -112,9 +114,9 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
                                                     const float* __restrict__ li,
                                                     const float* __restrict__ g,
                                                     const float* __restrict__ fg,
-                                                    float* __restrict__ states, StateWalk wk, int H,
+                                                    T* __restrict__ states, StateWalk wk, int H,
                                                     int T_, int dqk, int dhv, int L, int nc,
-                                                    const float* __restrict__ cstates,
+                                                    const T* __restrict__ cstates,
                                                     float* __restrict__ xpart)
 {
     constexpr int NTH = 64 * NWS;
@@ -227,11 +229,11 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
     auto put_state = [&](const f32x16 (&acc)[MV][MC], int slot) {
 #pragma unroll
         for (int mv = 0; mv < MV; ++mv) {
-            float* dst = states + ((bh * ns + slot) * (size_t)dhv + v0 + vw + 32 * mv) * dqk + c0 + cw + i32;
+            T* dst = states + ((bh * ns + slot) * (size_t)dhv + v0 + vw + 32 * mv) * dqk + c0 + cw + i32;
 #pragma unroll
             for (int mc = 0; mc < MC; ++mc)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dst[(size_t)arow(r) * dqk + 32 * mc] = acc[mv][mc][r];
+                for (int r = 0; r < 16; ++r) dst[(size_t)arow(r) * dqk + 32 * mc] = from_float<T>(acc[mv][mc][r]);
         }
     };
 
@@ -289,13 +291,13 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
         if (dot_now) {
 #pragma unroll
             for (int mv = 0; mv < MV; ++mv) {
-                const float* src =
+                const T* src =
                     cstates + ((bh * wk.cp_slots + (nc - 2 - kc) + wk.cp_off) * (size_t)dhv + v0 + vw + 32 * mv) * dqk +
                     c0 + cw + i32;
 #pragma unroll
                 for (int mc = 0; mc < MC; ++mc)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) cpre[mv][mc][r] = src[(size_t)arow(r) * dqk + 32 * mc];
+                    for (int r = 0; r < 16; ++r) cpre[mv][mc][r] = to_float(src[(size_t)arow(r) * dqk + 32 * mc]);
             }
         }
         // acc (value rows vw.., key columns cw..) += V^T (w.K) over this block
@@ -418,18 +420,18 @@ hipError_t launch_walk(const Problem& p, const T* k, const T* v, const float* fg
     switch (p.gate) {
     case kSig:
         state_kernel<T, kSig, SB, TV, TC, NWS, REV><<<blocks, threads, 0, stream>>>(
-            k, v, ws.a, ws.li, ws.g, fg, ws.states, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc,
-            static_cast<const float*>(ws.dot_partner), ws.dots);
+            k, v, ws.a, ws.li, ws.g, fg, static_cast<T*>(ws.states), wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc,
+            static_cast<const T*>(ws.dot_partner), ws.dots);
         break;
     case kScalar:
         state_kernel<T, kScalar, SB, TV, TC, NWS, REV><<<blocks, threads, 0, stream>>>(
-            k, v, ws.a, ws.li, ws.g, fg, ws.states, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc,
-            static_cast<const float*>(ws.dot_partner), ws.dots);
+            k, v, ws.a, ws.li, ws.g, fg, static_cast<T*>(ws.states), wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc,
+            static_cast<const T*>(ws.dot_partner), ws.dots);
         break;
     default:
         state_kernel<T, kGla, SB, TV, TC, NWS, REV><<<blocks, threads, 0, stream>>>(
-            k, v, ws.a, ws.li, ws.g, fg, ws.states, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc,
-            static_cast<const float*>(ws.dot_partner), ws.dots);
+            k, v, ws.a, ws.li, ws.g, fg, static_cast<T*>(ws.states), wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc,
+            static_cast<const T*>(ws.dot_partner), ws.dots);
         break;
     }
     return hipGetLastError();

@@ -204,7 +204,7 @@ int run_path(const tfla::Problem& p, const void* q, const void* k, const void* v
 // mirrored gate exponents (mLSTMsig) and the per-step gate-gradient sums.
 struct BwdWorkspace {
     tfla::Workspace fwd;
-    float* dstates;   // [B,H,nc-1,d_hv,d_qk]
+    void* dstates;    // [B,H,nc-1,d_hv,d_qk], I/O type
     float* ar;        // [B,H,T] mLSTMsig, [B,H,T,d_qk] per-channel gate
     float* lr;        // [B,H,T] mLSTMsig
     float* dq_dots;   // [B,H,T][np]: q_t . dq_t per value tile of the dq kernel
@@ -259,7 +259,7 @@ size_t bwd_layout(const tfla::Problem& p, BwdWorkspace* ws, char* base, bool wit
         return ptr;
     };
     const size_t rslots = p.nc - 1 + (with_states ? 1 : 0);   // reverse-walk states
-    ws->dstates = rslots > 0 ? take(bh * rslots * p.dhv * p.dqk * 4) : nullptr;
+    ws->dstates = rslots > 0 ? take(bh * rslots * p.dhv * p.dqk * (p.bf16 ? 2 : 4)) : nullptr;
     const bool sig = p.gate == tfla::kSig, gla = p.gate == tfla::kGla;
     ws->ar = sig ? take(bh * p.T * 4) : gla ? take(bh * p.T * p.dqk * 4) : nullptr;
     ws->lr = sig ? take(bh * p.T * 4) : nullptr;
@@ -522,7 +522,7 @@ size_t workspace_layout(const Problem& p, Workspace* ws, char* base, bool with_s
     ws->li = p.gate == kSig ? take(bh * p.T * 4) : nullptr;
     ws->g = p.gate == kScalar ? nullptr : take(bh * p.nc * w * 4);
     const size_t slots = p.nc - 1 + (with_c0 ? 1 : 0);
-    ws->states = (with_states && slots > 0) ? take(bh * slots * p.dhv * p.dqk * 4) : nullptr;
+    ws->states = (with_states && slots > 0) ? take(bh * slots * p.dhv * p.dqk * (p.bf16 ? 2 : 4)) : nullptr;
     const int P = state_segments(p);
     ws->seg_end = P > 1 ? take(bh * P * p.dhv * p.dqk * 4) : nullptr;
     ws->seg_start = P > 1 ? take(bh * P * p.dhv * p.dqk * 4) : nullptr;
@@ -689,7 +689,7 @@ int tfla_dbg_gates(const float* igate_pre, const float* fgate_pre, float* a_out,
     return TFLA_OK;
 }
 
-int tfla_dbg_states(const void* k, const void* v, const float* igate_pre, const float* fgate_pre, float* states_out,
+int tfla_dbg_states(const void* k, const void* v, const float* igate_pre, const float* fgate_pre, void* states_out,
                     int B, int H, int T, int d_qk, int d_hv, int L, int variant, void* stream)
 {
     tfla::Problem p;

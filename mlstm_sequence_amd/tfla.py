@@ -63,7 +63,7 @@ def lib():
         L.tfla_bwd_state_workspace_bytes.restype = sz
         L.tfla_dbg_gates.argtypes = [fp, fp, fp, fp, fp] + [i] * 6 + [vp]
         L.tfla_dbg_gates.restype = i
-        L.tfla_dbg_states.argtypes = [vp, vp, fp, fp, fp] + [i] * 7 + [vp]
+        L.tfla_dbg_states.argtypes = [vp, vp, fp, fp, vp] + [i] * 7 + [vp]
         L.tfla_dbg_states.restype = i
         L.tfla_error_string.argtypes = [i]
         L.tfla_error_string.restype = ctypes.c_char_p

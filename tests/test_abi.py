@@ -86,9 +86,12 @@ def test_workspace_bytes(L):
     # T = 250, L = 64: four chunks, too few to split the state walk into segments
     B, H, T, dqk, dhv, Lc = 2, 3, 250, 128, 256, 64
     nc = -(-T // Lc)
-    sig = a256(B * H * T * 4) * 2 + a256(B * H * nc * 4) + a256(B * H * (nc - 1) * dhv * dqk * 4)
+    # the states are stored in the I/O type: 2 bytes per element for bf16, 4 for fp32
+    sig = a256(B * H * T * 4) * 2 + a256(B * H * nc * 4) + a256(B * H * (nc - 1) * dhv * dqk * 2)
     assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16) == sig
-    scal = a256(B * H * (nc - 1) * dhv * dqk * 4)
+    sig32 = a256(B * H * T * 4) * 2 + a256(B * H * nc * 4) + a256(B * H * (nc - 1) * dhv * dqk * 4)
+    assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG) == sig32
+    scal = a256(B * H * (nc - 1) * dhv * dqk * 2)
     assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SCALAR | BF16) == scal
     gla = a256(B * H * T * dqk * 4) + a256(B * H * nc * dqk * 4) + scal
     assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, GLA | BF16) == gla
@@ -104,7 +107,7 @@ def test_segmented_state_walk_workspace(L):
     base = tfla.tfla_workspace_bytes(B, H, 250, dqk, dhv, Lc, SIG | BF16)        # 4 chunks: no segments
     T = 64 * 40
     nc = 40
-    plain = (T * 4 * 2 + 256) + (nc * 4 + 256) + (nc - 1) * dhv * dqk * 4 * B * H
+    plain = (T * 4 * 2 + 256) + (nc * 4 + 256) + (nc - 1) * dhv * dqk * 2 * B * H
     seg = tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16)
     assert base > 0 and seg >= plain + 2 * B * H * 2 * dqk * dhv * 4
 
@@ -161,10 +164,10 @@ def test_state_workspace_bytes(L):
     B, H, T, dqk, dhv, Lc = 2, 3, 250, 128, 256, 64   # four chunks: no segmented state walk
     nc = -(-T // Lc)
     base = tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16)
-    sig = a256(B * H * T * 4) * 2 + a256(B * H * nc * 4) + a256(B * H * nc * dhv * dqk * 4)
+    sig = a256(B * H * T * 4) * 2 + a256(B * H * nc * 4) + a256(B * H * nc * dhv * dqk * 2)
     assert tfla.tfla_state_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16) == sig > base
-    # one chunk: the only state slot is the initial state's
-    assert tfla.tfla_state_workspace_bytes(B, H, 64, dqk, dhv, Lc, SCALAR | BF16) == a256(B * H * dhv * dqk * 4)
+    # one chunk: the only state slot is the initial state's (bf16 like the I/O)
+    assert tfla.tfla_state_workspace_bytes(B, H, 64, dqk, dhv, Lc, SCALAR | BF16) == a256(B * H * dhv * dqk * 2)
     assert tfla.tfla_state_workspace_bytes(B, H, T, 96, dhv, Lc, SIG) == 0
 
 
@@ -233,7 +236,7 @@ def test_bwd_workspace_bytes(L):
 
     B, H, T, dqk, dhv, Lc = 2, 3, 250, 128, 256, 64
     nc = -(-T // Lc)
-    states = a256(B * H * (nc - 1) * dhv * dqk * 4)
+    states = a256(B * H * (nc - 1) * dhv * dqk * 2)   # reverse-walk states, I/O type
     steps = a256(B * H * T * 4)
     # forward workspace, reverse-walk states, mirrored gates (2), the row
     # partials of q.dq and k.dk (one per 128-wide tile of d_qk here), and

@@ -56,7 +56,7 @@ def test_states(variant, dtype, dqk, dhv, T, L):
     wl, inp = case(variant, 1, 2, T, dqk, dhv, dtype, seed=dqk + T)
     _, st_ref = oracle_forward(inp, variant, L=L)
     nc = -(-T // L)
-    st = torch.full((1, 2, nc - 1, dhv, dqk), float("nan"), device="cuda")
+    st = torch.full((1, 2, nc - 1, dhv, dqk), float("nan"), device="cuda", dtype=dtype)   # I/O type
     ig = None if inp["igate_pre"] is None else inp["igate_pre"].cuda()
     tfla.tfla_dbg_states(inp["k"].cuda(), inp["v"].cuda(), ig, inp["fgate_pre"].cuda(), st, 1, 2, T, dqk, dhv, L,
                          tfla.variant_of(GATE[variant], dtype))

@@ -222,7 +222,7 @@ def test_segmented_state_walk(monkeypatch, segments, variant, dtype, B, H, T, dq
         _, st_ref = oracle.recurrent_fwd(W.as_f64(inp["q"]), W.as_f64(inp["k"]), W.as_f64(inp["v"]),
                                          W.as_f64(inp["igate_pre"]), W.as_f64(inp["fgate_pre"]), variant, L=L)
         nc = -(-T // L)
-        st = torch.full((B, H, nc - 1, dhv, dqk), float("nan"), device="cuda")
+        st = torch.full((B, H, nc - 1, dhv, dqk), float("nan"), device="cuda", dtype=dtype)
         d = to_dev(inp)
         tfla.tfla_dbg_states(d["k"], d["v"], d["igate_pre"], d["fgate_pre"], st, B, H, T, dqk, dhv, L,
                              tfla.variant_of(GATE[variant], dtype))
