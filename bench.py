@@ -57,7 +57,7 @@ def kernel_model(wl, L):
     T, dqk, dhv = wl.T, wl.dqk, wl.dhv
     steps_state = sum(n[:-1])           # steps whose chunk feeds a materialised state
     steps_inter = sum(n[1:])            # steps that read a state
-    st_bytes = 4 * dqk * dhv * (len(n) - 1)
+    st_bytes = e * dqk * dhv * (len(n) - 1)   # states are stored in the I/O type
     # per-step gate sums read by the consumers: a and li (mLSTMsig), a per
     # key channel (GLA), none for the closed-form fixed decay
     gstep = {0: 8, 1: 0, 2: 4 * dqk}[wl.variant]

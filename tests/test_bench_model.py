@@ -44,6 +44,6 @@ def test_intra_bytes_are_compulsory_io_plus_states():
     bh = wl.B * wl.H
     nc = wl.T // L
     io = bh * wl.T * (2 * wl.dqk + 2 * wl.dhv) * 2          # q, k, v in, h out (bf16)
-    states = bh * (nc - 1) * wl.dqk * wl.dhv * 4            # fp32 states read once
+    states = bh * (nc - 1) * wl.dqk * wl.dhv * 2            # states (stored bf16) read once
     gates = bh * wl.T * 8                                   # a and li
     assert m["intra"]["bytes"] == io + states + gates
