@@ -90,17 +90,18 @@ def backward_flops(wl, L):
 
 
 # --------------------------------------------------------------------------- GPU timing
-def run_gpu(wl, L, steps, warmup, inputs_dev, cold_calls=0):
+def run_gpu(wl, L, steps, warmup, inputs_dev, cold_calls=0, flags=0, keep_h=False):
+    """flags: extra variant bits (TFLA_STATES_FP32); keep_h: also return h."""
     import torch
     from mlstm_sequence_amd import tfla
 
     q, k, v = inputs_dev["q"], inputs_dev["k"], inputs_dev["v"]
     ig, fg = inputs_dev["igate_pre"], inputs_dev["fgate_pre"]
     gate = {0: tfla.MLSTM_SIG, 1: tfla.SCALAR_DECAY, 2: tfla.GLA_KEY}[wl.variant]
-    var = tfla.variant_of(gate, q.dtype)
+    var = tfla.variant_of(gate, q.dtype) | flags
     h = torch.empty((wl.B, wl.H, wl.T, wl.dhv), dtype=q.dtype, device=q.device)
-    ws = tfla.workspace_for(q, v, gate, L)
-    nbytes = ws.numel()
+    nbytes = tfla.tfla_workspace_bytes(wl.B, wl.H, wl.T, wl.dqk, wl.dhv, L, var)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream()
     args = (q, k, v, ig, fg, h, wl.B, wl.H, wl.T, wl.dqk, wl.dhv, L, var, ws, nbytes)
 
@@ -150,8 +151,8 @@ def run_gpu(wl, L, steps, warmup, inputs_dev, cold_calls=0):
         per["state"] += evs[1].elapsed_time(evs[2])
         per["intra"] += evs[2].elapsed_time(evs[3])
     per = {kname: t / steps for kname, t in per.items()}
-    del ws, h
-    return ms, wall / steps * 1e3, per, cold
+    del ws
+    return ms, wall / steps * 1e3, per, cold, (h if keep_h else None)
 
 
 def run_gpu_bwd(wl, L, steps, warmup, inputs_dev, dh):
@@ -345,7 +346,7 @@ def main():
 
     results = {}
     for L in sweep:
-        ms, wall_ms, per, cold = run_gpu(wl, L, args.steps, args.warmup, dev, cold_calls=10)
+        ms, wall_ms, per, cold, _ = run_gpu(wl, L, args.steps, args.warmup, dev, cold_calls=10)
         tps = wl.B * wl.T / (ms * 1e-3)
         fl = total_flops(wl, L)
         results[L] = {"ms": ms, "wall_ms": wall_ms, "per": per, "tokens_per_s": tps,
@@ -397,6 +398,18 @@ def main():
                   for L, x in results.items()},
         "cold_cache": r["cold"],
     }
+    # The same step with the chunk states materialised in fp32 instead of the
+    # I/O type (TFLA_STATES_FP32): identical h, twice the state bytes.
+    if wl.dtype_name == "bf16":
+        from mlstm_sequence_amd import tfla
+        _, _, _, _, h16 = run_gpu(wl, Lh, 2, 1, dev, keep_h=True)
+        ms32, _, per32, _, h32 = run_gpu(wl, Lh, args.steps, args.warmup, dev, flags=tfla.STATES_FP32, keep_h=True)
+        out["fp32_states"] = {"L": Lh, "ms_per_step": ms32, "tokens_per_s": wl.B * wl.T / (ms32 * 1e-3),
+                              "mfma_frac": total_flops(wl, Lh) / (ms32 * 1e-3) / PEAK_BF16, "kernels_ms": per32,
+                              "h_bitwise_equal": bool(torch.equal(h16, h32))}
+        del h16, h32
+        log(f"fp32 states, L={Lh}: {ms32:.3f} ms/step (state {per32['state']:.3f} ms, intra {per32['intra']:.3f} ms); "
+            f"h bitwise equal to the bf16-state step: {out['fp32_states']['h_bitwise_equal']}")
     # Chunk-size ablation (limit_chunk vs xl_chunk, TFLA abstract and summary):
     # at L = 64 every chunk is a single 64-step key/value tile, i.e. the chunk
     # is bounded by what one workgroup stages on chip; larger L tile the

@@ -50,8 +50,14 @@ enum tfla_variant {
     TFLA_SCALAR_DECAY = 1,  /* i = 1, f = sigmoid(fgate_pre[h]) fixed per head            */
     TFLA_GLA_KEY = 2,       /* i = 1, f_{t,c} = exp(logsigmoid(fgate_pre[t,c]) / 16)      */
     TFLA_IO_BF16 = 0x100,   /* q, k, v, h are bf16; without the flag they are fp32        */
-    TFLA_BWD_REUSE_FWD = 0x200  /* tfla_bwd only: reuse the forward pass's gate sums and
+    TFLA_BWD_REUSE_FWD = 0x200, /* tfla_bwd only: reuse the forward pass's gate sums and
                                    states left in the workspace (see tfla_bwd)              */
+    TFLA_STATES_FP32 = 0x400    /* forward calls, bf16 I/O: materialise the chunk states in
+                                   fp32 rather than bf16 (outputs are identical: the
+                                   intra-chunk products round the states to bf16 either way;
+                                   the state bytes double); no effect with fp32 I/O or on
+                                   tfla_fwd_recurrent; TFLA_ERR_UNSUPPORTED for the
+                                   backward calls                                           */
 };
 
 enum tfla_status {
@@ -199,7 +205,8 @@ int tfla_fwd_recurrent(const void* q, const void* k, const void* v,
  *   variant   any gate kind | TFLA_IO_BF16, as for tfla_fwd, optionally
  *             | TFLA_BWD_REUSE_FWD: the caller asserts that `workspace` (which
  *             must then be given) was last used by a completed tfla_fwd_ws
- *             call with the same inputs, shape, chunk size and variant, and
+ *             call with the same inputs, shape, chunk size and variant (so
+ *             without TFLA_STATES_FP32), and
  *             nothing has written its first tfla_workspace_bytes(...) bytes
  *             since; the gate prefix sums and the states C_k found there are
  *             used as they are, skipping their recomputation.  Results are
@@ -268,9 +275,10 @@ size_t tfla_bwd_state_workspace_bytes(int B, int H, int T, int d_qk, int d_hv, i
  * other kernels; this hook evaluates the same closed form.
  *
  * tfla_dbg_states -- gates plus the inter-chunk state kernel.  states_out
- * (device, the I/O type: bf16 with TFLA_IO_BF16, else fp32) receives the
- * state after chunks 1..N_c-1 (N_c = ceil(T/L)), each rounded to that type
- * (RNE) and stored TRANSPOSED as [d_hv][d_qk]: layout [B,H,N_c-1,d_hv,d_qk].
+ * (device, the I/O type: bf16 with TFLA_IO_BF16 unless TFLA_STATES_FP32 is
+ * set, else fp32) receives the state after chunks 1..N_c-1 (N_c = ceil(T/L)),
+ * each rounded to that type (RNE) and stored TRANSPOSED as [d_hv][d_qk]:
+ * layout [B,H,N_c-1,d_hv,d_qk].
  * q is not needed; h is untouched.
  */
 int tfla_dbg_gates(const float* igate_pre, const float* fgate_pre,

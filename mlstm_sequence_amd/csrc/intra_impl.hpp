@@ -49,6 +49,7 @@
 #pragma once
 
 #include <cstdlib>
+#include <type_traits>
 
 #include "gfx950.hpp"
 #include "kernels.hpp"
@@ -72,15 +73,17 @@ template <typename T, int DQK, int BV, int CW> struct IntraLds {
 // One stage's global loads, held in registers while the previous stage
 // computes.  A C^T block and a K/V tile are never in flight together, so they
 // share the registers.
-template <typename T, int DQK, int BV, int CW, int NTH> struct Prefetch {
+// S: the stored state type
+template <typename T, typename S, int DQK, int BV, int CW, int NTH> struct Prefetch {
     typedef typename Elem<T>::frag Frag;
     static constexpr int VEC = Elem<T>::vec;
+    static constexpr int SVEC = Elem<S>::vec;
     static constexpr int NC = BV * CW / 8 / NTH;          // C^T block: 8 elements per item
     static constexpr int NK = 64 * DQK / VEC / NTH;       // K tile: 16 bytes per item
     static constexpr int NV = 64 * BV / VEC / NTH;        // V tile: 16 bytes per item
     static_assert(NC >= 1 && NK >= 1 && NV >= 1, "tile too small for the workgroup");
     union {
-        Vec16<T> c[NC][8 / VEC];
+        Vec16<S> c[NC][8 / SVEC];
         struct {
             Vec16<T> k[NK];
             Vec16<T> v[NV];
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
                                                            const T* __restrict__ v, const float* __restrict__ a,
                                                            const float* __restrict__ li,
                                                            const float* __restrict__ fg,
-                                                           const T* __restrict__ states,
+                                                           const std::conditional_t<(MODE & kStateF32) != 0, float, T>* __restrict__ states,
                                                            T* __restrict__ h, int H, int T_, int dhv, int L,
                                                            int nc, int c0, float scale,
                                                            const T* __restrict__ partner,
@@ -129,7 +132,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     constexpr int VEC = Elem<T>::vec;
     typedef typename Elem<T>::frag Frag;
     typedef IntraLds<T, DQK, BV, CW> Lds;
-    typedef Prefetch<T, DQK, BV, CW, NTH> PF;
+    typedef std::conditional_t<(MODE & kStateF32) != 0, float, T> S;   // stored state type
+    constexpr int SVEC = Elem<S>::vec;
+    typedef Prefetch<T, S, DQK, BV, CW, NTH> PF;
     __shared__ Lds sm;
 
     const int nqt = (T_ + BQ - 1) / BQ;
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     };
 
     // ---- stage loaders (global -> registers) and writers (registers -> LDS)
-    auto fetch_c = [&](const T* st, int cb) {
+    auto fetch_c = [&](const S* st, int cb) {
 #pragma unroll
         for (int u = 0; u < PF::NC; ++u) {
             const int idx = tid + NTH * u;
@@ -200,14 +205,14 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
                 // column vr of 8 contraction rows: each load is one row's
                 // run of consecutive columns across the lanes
                 const int vr = idx % BV, c8 = (idx / BV) * 8;
-                const T* src = st + (size_t)(cb + c8) * dhv + vr;
+                const S* src = st + (size_t)(cb + c8) * dhv + vr;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pf.c[u][e / VEC].v[e % VEC] = src[(size_t)e * dhv];
+                for (int e = 0; e < 8; ++e) pf.c[u][e / SVEC].v[e % SVEC] = src[(size_t)e * dhv];
             } else {
                 const int vr = idx / (CW / 8), c8 = (idx % (CW / 8)) * 8;
-                const T* src = st + (size_t)vr * DQK + cb + c8;
+                const S* src = st + (size_t)vr * DQK + cb + c8;
 #pragma unroll
-                for (int x = 0; x < 8 / VEC; ++x) pf.c[u][x].load(src + VEC * x);
+                for (int x = 0; x < 8 / SVEC; ++x) pf.c[u][x].load(src + SVEC * x);
             }
         }
     };
@@ -217,8 +222,16 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
             const int idx = tid + NTH * u;
             const int vr = NAT ? idx % BV : idx / (CW / 8);
             const int c8 = NAT ? (idx / BV) * 8 : (idx % (CW / 8)) * 8;
+            if constexpr (std::is_same_v<S, T>) {
 #pragma unroll
-            for (int x = 0; x < 8 / VEC; ++x) pf.c[u][x].store(&sm.cs[vr][c8 + VEC * x]);
+                for (int x = 0; x < 8 / VEC; ++x) pf.c[u][x].store(&sm.cs[vr][c8 + VEC * x]);
+            } else {
+                // fp32 states, bf16 operands: RNE on the way into LDS
+                Vec16<T> y;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y.set(e, pf.c[u][e / SVEC].get(e % SVEC));
+                y.store(&sm.cs[vr][c8]);
+            }
         }
     };
     auto fetch_kv = [&](int s0) {
@@ -315,7 +328,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     const bool inter = EMITP ? false : REV ? kc < nc - 1 + c0 : (kc > 0 || c0);
     if (inter) {
         const size_t slot = bh * (nc - 1 + c0) + (REV ? kc : kc - 1 + c0);
-        const T* st = NAT ? states + slot * DQK * (size_t)dhv + v0
+        const S* st = NAT ? states + slot * DQK * (size_t)dhv + v0
                           : states + (slot * dhv + v0) * DQK;
         fetch_c(st, 0);
         load_q(-1);
@@ -539,7 +552,7 @@ hipError_t launch_intra_t(const Problem& p, const void* q, const void* k, const 
     const int blocks = p.B * p.H * nqt * (p.dhv / BV);
     intra_kernel<T, GATE, DQK, BV, NW, MODE><<<blocks, 64 * NW, 0, stream>>>(
         static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), ws.a, ws.li, fg,
-        static_cast<const T*>(ws.states), static_cast<T*>(h), p.H, p.T, p.dhv, p.L, p.nc, ws.c0 != nullptr, scale,
+        static_cast<const std::conditional_t<(MODE & kStateF32) != 0, float, T>*>(ws.states), static_cast<T*>(h), p.H, p.T, p.dhv, p.L, p.nc, ws.c0 != nullptr, scale,
         static_cast<const T*>(ws.dot_partner), ws.dots, static_cast<T*>(ws.p_out), static_cast<const T*>(ws.p_in));
     return hipGetLastError();
 }
@@ -582,7 +595,7 @@ hipError_t dispatch_nw(const Problem& p, const void* q, const void* k, const voi
 {
     // a workgroup's query rows never straddle a chunk; writing P holds no
     // accumulators, so 8 waves fit a 512-wide contraction there
-    const int rows = MODE == kEmitP ? intra_rows(Problem{p.B, p.H, p.T, 256, p.dhv, p.L, p.nc, p.gate, p.bf16})
+    const int rows = MODE == kEmitP ? intra_rows(Problem{p.B, p.H, p.T, 256, p.dhv, p.L, p.nc, p.gate, p.bf16, p.st32})
                                     : intra_rows(p);
     if constexpr (sizeof(T) == 2 && (DQK <= 256 || MODE == kEmitP)) {
         if (rows == 256) return launch_intra_t<T, GATE, DQK, BV, 8, MODE>(p, q, k, v, fg, ws, h, scale, stream);
@@ -614,7 +627,7 @@ hipError_t dispatch_dqk(const Problem& p, const void* q, const void* k, const vo
         if constexpr (sizeof(T) == 2) return dispatch_bv<T, GATE, 256, MODE>(p, q, k, v, fg, ws, h, scale, stream);
         return hipErrorInvalidValue;
     case 512:
-        if constexpr (sizeof(T) == 2 && MODE != 0)
+        if constexpr (sizeof(T) == 2 && MODE != 0 && MODE != kStateF32)
             return dispatch_bv<T, GATE, 512, MODE>(p, q, k, v, fg, ws, h, scale, stream);
         return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;

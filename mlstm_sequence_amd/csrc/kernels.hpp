@@ -8,8 +8,9 @@ namespace tfla {
 
 enum GateKind { kSig = 0, kScalar = 1, kGla = 2 };
 
-// Operand modes of the intra-chunk kernel (bit set) for the gradient products.
-enum IntraMode { kNatState = 1, kMirror = 2, kRowDots = 4, kEmitP = 8, kGivenP = 16 };
+// Operand modes of the intra-chunk kernel (bit set) for the gradient products;
+// kStateF32: the forward pass reading fp32 states with bf16 I/O.
+enum IntraMode { kNatState = 1, kMirror = 2, kRowDots = 4, kEmitP = 8, kGivenP = 16, kStateF32 = 32 };
 
 // Problem description shared by the launchers.  Sizes in elements.
 struct Problem {
@@ -17,6 +18,7 @@ struct Problem {
     int nc;          // number of chunks, ceil(T / L)
     int gate;        // GateKind
     bool bf16;       // element type of q, k, v, h
+    bool st32 = false;   // states materialised in fp32 (always for fp32 I/O)
 };
 
 // Workspace carve-up (device pointers into one allocation).
@@ -24,9 +26,10 @@ struct Workspace {
     float* a;        // [B,H,T] (GLA: [B,H,T,dqk]) chunk-local log-forget sums; NULL for kScalar
     float* li;       // [B,H,T] log input gate; kSig only
     float* g;        // [B,H,nc] (GLA: [B,H,nc,dqk]); NULL for kScalar
-    void* states;    // [B,H,ns,dhv,dqk] I/O type, transposed states before chunks
-                     // (walked in fp32; the intra-chunk kernel rounds them to
-                     // the I/O type for its matrix cores anyway)
+    void* states;    // [B,H,ns,dhv,dqk] I/O type (fp32 when Problem::st32),
+                     // transposed states before chunks (walked in fp32; the
+                     // intra-chunk kernel rounds them to the I/O type for its
+                     // matrix cores anyway)
                      // 1..nc-1 (ns = nc-1), or 0..nc-1 with an initial state (ns = nc)
     const float* c0 = nullptr;   // caller's initial state [B,H,dqk,dhv] (NULL: zero)
     float* c_final = nullptr;    // caller's final-state output [B,H,dqk,dhv] (NULL: none)

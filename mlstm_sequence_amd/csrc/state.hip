@@ -10,7 +10,8 @@
 // from C_0 = 0 or a given initial state, in fp32.  The state before chunk k
 // (k >= 1, and k = 0 when an initial state is given) is written in the I/O
 // type (the intra-chunk kernel's matrix-core operand type, to which it would
-// round an fp32 copy anyway: half the bytes for bf16), transposed
+// round an fp32 copy anyway: half the bytes for bf16; fp32 on request),
+// transposed
 // ([d_hv][d_qk]) so the intra-chunk kernel reads it as contiguous
 // matrix-core B operands.  On request the walk continues through the last
 // (possibly partial) chunk and writes the final state C_T in the caller's
@@ -108,15 +109,16 @@ template <typename T, int SB, int TV, int TC, int NTH> struct StatePrefetch {
     float g;                      // mLSTMsig: g of the block's chunk
 };
 
-template <typename T, int GATE, int SB, int TV, int TC, int NWS, bool REV>
+// S: the stored state type (T, or fp32 on request)
+template <typename T, int GATE, int SB, int TV, int TC, int NWS, bool REV, typename S>
 __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                     const float* __restrict__ a,
                                                     const float* __restrict__ li,
                                                     const float* __restrict__ g,
                                                     const float* __restrict__ fg,
-                                                    T* __restrict__ states, StateWalk wk, int H,
+                                                    S* __restrict__ states, StateWalk wk, int H,
                                                     int T_, int dqk, int dhv, int L, int nc,
-                                                    const T* __restrict__ cstates,
+                                                    const S* __restrict__ cstates,
                                                     float* __restrict__ xpart)
 {
     constexpr int NTH = 64 * NWS;
@@ -229,11 +231,11 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
     auto put_state = [&](const f32x16 (&acc)[MV][MC], int slot) {
 #pragma unroll
         for (int mv = 0; mv < MV; ++mv) {
-            T* dst = states + ((bh * ns + slot) * (size_t)dhv + v0 + vw + 32 * mv) * dqk + c0 + cw + i32;
+            S* dst = states + ((bh * ns + slot) * (size_t)dhv + v0 + vw + 32 * mv) * dqk + c0 + cw + i32;
 #pragma unroll
             for (int mc = 0; mc < MC; ++mc)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dst[(size_t)arow(r) * dqk + 32 * mc] = from_float<T>(acc[mv][mc][r]);
+                for (int r = 0; r < 16; ++r) dst[(size_t)arow(r) * dqk + 32 * mc] = from_float<S>(acc[mv][mc][r]);
         }
     };
 
@@ -291,7 +293,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
         if (dot_now) {
 #pragma unroll
             for (int mv = 0; mv < MV; ++mv) {
-                const T* src =
+                const S* src =
                     cstates + ((bh * wk.cp_slots + (nc - 2 - kc) + wk.cp_off) * (size_t)dhv + v0 + vw + 32 * mv) * dqk +
                     c0 + cw + i32;
 #pragma unroll
@@ -411,30 +413,40 @@ __global__ __launch_bounds__(256) void state_combine_kernel(const float* __restr
     }
 }
 
+template <typename T, int SB, int TV, int TC, int NWS, bool REV, typename S>
+hipError_t launch_walk_s(const Problem& p, const T* k, const T* v, const float* fg, const Workspace& ws,
+                         const StateWalk& wk, hipStream_t stream)
+{
+    const int blocks = p.B * p.H * (p.dhv / TV) * (p.dqk / TC) * wk.nseg;
+    const int threads = 64 * NWS;
+    S* st = static_cast<S*>(ws.states);
+    const S* cst = static_cast<const S*>(ws.dot_partner);
+    switch (p.gate) {
+    case kSig:
+        state_kernel<T, kSig, SB, TV, TC, NWS, REV, S><<<blocks, threads, 0, stream>>>(
+            k, v, ws.a, ws.li, ws.g, fg, st, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc, cst, ws.dots);
+        break;
+    case kScalar:
+        state_kernel<T, kScalar, SB, TV, TC, NWS, REV, S><<<blocks, threads, 0, stream>>>(
+            k, v, ws.a, ws.li, ws.g, fg, st, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc, cst, ws.dots);
+        break;
+    default:
+        state_kernel<T, kGla, SB, TV, TC, NWS, REV, S><<<blocks, threads, 0, stream>>>(
+            k, v, ws.a, ws.li, ws.g, fg, st, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc, cst, ws.dots);
+        break;
+    }
+    return hipGetLastError();
+}
+
+// states in the I/O type, or fp32 on request (forward walk, bf16 I/O)
 template <typename T, int SB, int TV, int TC, int NWS, bool REV>
 hipError_t launch_walk(const Problem& p, const T* k, const T* v, const float* fg, const Workspace& ws,
                        const StateWalk& wk, hipStream_t stream)
 {
-    const int blocks = p.B * p.H * (p.dhv / TV) * (p.dqk / TC) * wk.nseg;
-    const int threads = 64 * NWS;
-    switch (p.gate) {
-    case kSig:
-        state_kernel<T, kSig, SB, TV, TC, NWS, REV><<<blocks, threads, 0, stream>>>(
-            k, v, ws.a, ws.li, ws.g, fg, static_cast<T*>(ws.states), wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc,
-            static_cast<const T*>(ws.dot_partner), ws.dots);
-        break;
-    case kScalar:
-        state_kernel<T, kScalar, SB, TV, TC, NWS, REV><<<blocks, threads, 0, stream>>>(
-            k, v, ws.a, ws.li, ws.g, fg, static_cast<T*>(ws.states), wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc,
-            static_cast<const T*>(ws.dot_partner), ws.dots);
-        break;
-    default:
-        state_kernel<T, kGla, SB, TV, TC, NWS, REV><<<blocks, threads, 0, stream>>>(
-            k, v, ws.a, ws.li, ws.g, fg, static_cast<T*>(ws.states), wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc,
-            static_cast<const T*>(ws.dot_partner), ws.dots);
-        break;
+    if constexpr (!REV && sizeof(T) == 2) {
+        if (p.st32) return launch_walk_s<T, SB, TV, TC, NWS, REV, float>(p, k, v, fg, ws, wk, stream);
     }
-    return hipGetLastError();
+    return launch_walk_s<T, SB, TV, TC, NWS, REV, T>(p, k, v, fg, ws, wk, stream);
 }
 
 template <bool REV>

@@ -42,7 +42,7 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 int check_problem(int B, int H, int T, int d_qk, int d_hv, int L, int variant, tfla::Problem* p)
 {
     const int gate = variant & 0xff;
-    if ((variant & ~(0xff | TFLA_IO_BF16)) != 0 || gate > TFLA_GLA_KEY || gate < 0)
+    if ((variant & ~(0xff | TFLA_IO_BF16 | TFLA_STATES_FP32)) != 0 || gate > TFLA_GLA_KEY || gate < 0)
         return fail(TFLA_ERR_INVALID_ARG, "unknown variant " + std::to_string(variant));
     if (B < 1 || H < 1 || T < 1 || d_qk < 1 || d_hv < 1 || L < 1)
         return fail(TFLA_ERR_INVALID_ARG, "B, H, T, d_qk, d_hv and L must be >= 1");
@@ -70,6 +70,7 @@ int check_problem(int B, int H, int T, int d_qk, int d_hv, int L, int variant, t
     p->nc = (T + L - 1) / L;
     p->gate = gate;
     p->bf16 = bf16;
+    p->st32 = !bf16 || (variant & TFLA_STATES_FP32) != 0;
     return TFLA_OK;
 }
 
@@ -282,6 +283,8 @@ size_t bwd_layout(const tfla::Problem& p, BwdWorkspace* ws, char* base, bool wit
 // products contract) a power of two the intra kernel is instantiated for.
 int check_bwd_problem(int B, int H, int T, int d_qk, int d_hv, int L, int variant, tfla::Problem* p)
 {
+    if (variant & TFLA_STATES_FP32)
+        return fail(TFLA_ERR_UNSUPPORTED, "TFLA_STATES_FP32 is an option of the forward calls only");
     int rc = check_problem(B, H, T, d_qk, d_hv, L, variant & ~TFLA_BWD_REUSE_FWD, p);
     if (rc) return rc;
     if (!(d_hv == 64 || d_hv == 128 || (p->bf16 && (d_hv == 256 || d_hv == 512))))
@@ -522,7 +525,7 @@ size_t workspace_layout(const Problem& p, Workspace* ws, char* base, bool with_s
     ws->li = p.gate == kSig ? take(bh * p.T * 4) : nullptr;
     ws->g = p.gate == kScalar ? nullptr : take(bh * p.nc * w * 4);
     const size_t slots = p.nc - 1 + (with_c0 ? 1 : 0);
-    ws->states = (with_states && slots > 0) ? take(bh * slots * p.dhv * p.dqk * (p.bf16 ? 2 : 4)) : nullptr;
+    ws->states = (with_states && slots > 0) ? take(bh * slots * p.dhv * p.dqk * (p.st32 ? 4 : 2)) : nullptr;
     const int P = state_segments(p);
     ws->seg_end = P > 1 ? take(bh * P * p.dhv * p.dqk * 4) : nullptr;
     ws->seg_start = P > 1 ? take(bh * P * p.dhv * p.dqk * 4) : nullptr;

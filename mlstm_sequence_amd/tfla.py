@@ -17,6 +17,7 @@ SCALAR_DECAY = 1
 GLA_KEY = 2
 IO_BF16 = 0x100
 BWD_REUSE_FWD = 0x200
+STATES_FP32 = 0x400   # forward, bf16 I/O: materialise the chunk states in fp32
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_OUT_OF_MEMORY = 0, 1, 2, 3, 4
 

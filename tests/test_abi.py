@@ -96,6 +96,10 @@ def test_workspace_bytes(L):
     gla = a256(B * H * T * dqk * 4) + a256(B * H * nc * dqk * 4) + scal
     assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, GLA | BF16) == gla
     assert tfla.tfla_workspace_bytes(B, H, 64, dqk, dhv, Lc, SCALAR | BF16) == 0   # one chunk, no state
+    # TFLA_STATES_FP32 (0x400): fp32 states with bf16 I/O; no effect with fp32 I/O
+    assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16 | 0x400) == sig32
+    assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | 0x400) == sig32
+    assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16 | 0x800) == 0   # unknown flag
     assert tfla.tfla_workspace_bytes(B, H, T, 96, dhv, Lc, SIG) == 0
 
 
@@ -204,6 +208,7 @@ def bwd(q=Q, k=K, v=V, ig=IG, fg=FG, dh=DH, dq=DQ, dk=DK, dv=DV, dig=DIG, dfg=DF
     (dict(variant=SIG, dhv=256), UNSUPPORTED),                    # fp32 I/O: d_hv <= 128
     (dict(dqk=96), UNSUPPORTED), (dict(Lc=32), UNSUPPORTED),
     (dict(B=0), INVALID), (dict(variant=7), INVALID),
+    (dict(variant=SIG | BF16 | 0x400), UNSUPPORTED),               # TFLA_STATES_FP32: forward calls only
     (dict(dh=None), INVALID), (dict(dq=None), INVALID), (dict(dv=None), INVALID),
     (dict(dk=DK + 8), INVALID), (dict(dfg=None), INVALID), (dict(dfg=DFG + 2), INVALID),
     (dict(dig=None), INVALID),                                    # mLSTMsig needs dig
@@ -220,7 +225,7 @@ def test_bwd_rejects_bad_arguments(L, kw, code):
 def test_bwd_reuse_needs_the_forward_workspace(L):
     assert bwd(variant=SIG | BF16 | 0x200) == INVALID
     assert "workspace" in tfla.tfla_last_error()
-    assert bwd(variant=SIG | BF16 | 0x400) == INVALID          # unknown flag
+    assert bwd(variant=SIG | BF16 | 0x800) == INVALID          # unknown flag
     n = tfla.tfla_bwd_workspace_bytes(2, 3, 300, 128, 256, 64, SIG | BF16)
     assert n > 0 and tfla.tfla_bwd_workspace_bytes(2, 3, 300, 128, 256, 64, SIG | BF16 | 0x200) == n
 
@@ -254,6 +259,7 @@ def test_bwd_workspace_bytes(L):
            + Xg)
     assert tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, dhv, Lc, GLA | BF16) == gla
     assert tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, 192, Lc, SIG | BF16) == 0
+    assert tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16 | 0x400) == 0   # forward-only flag
 
 
 def test_workspace_must_not_overlap_a_tensor(L):
