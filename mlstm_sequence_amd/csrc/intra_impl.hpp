@@ -57,7 +57,9 @@
 namespace tfla {
 namespace {
 
-template <typename T, int DQK, int BV, int CW> struct IntraLds {
+// NATL: the state block is staged as stored, contraction-major (cst), and
+// read through transpose reads
+template <typename T, int DQK, int BV, int CW, bool NATL> struct IntraLds {
     static constexpr int kpad = 16 / sizeof(T);   // K / C^T rows: stride = 4 banks mod 32
     static constexpr int vpad = 64 / sizeof(T);   // V rows: stride = 16 banks mod 64 (transpose reads)
     union {
@@ -65,7 +67,8 @@ template <typename T, int DQK, int BV, int CW> struct IntraLds {
             T ks[64][DQK + kpad];   // K tile [step][channel]
             T vs[64][BV + vpad];    // V tile [step][value]
         } kv;
-        T cs[BV][CW + kpad];        // CW-channel block of C^T [value][channel]
+        T cs[NATL ? 1 : BV][CW + kpad];    // CW-channel block of C^T [value][channel]
+        T cst[NATL ? CW : 1][BV + vpad];   // the same block as [channel][value], rows permuted (see store_c)
     };
     float bcol[64];                 // mLSTMsig: (li_s - a_s) log2(e) per key step
 };
@@ -131,7 +134,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     constexpr int NT = BV / 32;           // 32-wide output column tiles
     constexpr int VEC = Elem<T>::vec;
     typedef typename Elem<T>::frag Frag;
-    typedef IntraLds<T, DQK, BV, CW> Lds;
+    typedef IntraLds<T, DQK, BV, CW, NAT> Lds;
     typedef std::conditional_t<(MODE & kStateF32) != 0, float, T> S;   // stored state type
     constexpr int SVEC = Elem<S>::vec;
     typedef Prefetch<T, S, DQK, BV, CW, NTH> PF;
@@ -202,12 +205,12 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
         for (int u = 0; u < PF::NC; ++u) {
             const int idx = tid + NTH * u;
             if constexpr (NAT) {
-                // column vr of 8 contraction rows: each load is one row's
-                // run of consecutive columns across the lanes
-                const int vr = idx % BV, c8 = (idx / BV) * 8;
-                const S* src = st + (size_t)(cb + c8) * dhv + vr;
+                // 8 consecutive output columns of contraction row c: the lanes
+                // read each row's run of columns with 16-byte loads
+                const int c = idx / (BV / 8), col8 = (idx % (BV / 8)) * 8;
+                const S* src = st + (size_t)(cb + c) * dhv + col8;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pf.c[u][e / SVEC].v[e % SVEC] = src[(size_t)e * dhv];
+                for (int x = 0; x < 8 / SVEC; ++x) pf.c[u][x].load(src + SVEC * x);
             } else {
                 const int vr = idx / (CW / 8), c8 = (idx % (CW / 8)) * 8;
                 const S* src = st + (size_t)vr * DQK + cb + c8;
@@ -220,8 +223,21 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
 #pragma unroll
         for (int u = 0; u < PF::NC; ++u) {
             const int idx = tid + NTH * u;
-            const int vr = NAT ? idx % BV : idx / (CW / 8);
-            const int c8 = NAT ? (idx / BV) * 8 : (idx % (CW / 8)) * 8;
+            if constexpr (NAT) {
+                // Transpose reads hand lane half hh the contraction rows
+                // 4hh..4hh+3 and 8+4hh..8+4hh+3 of each 16-row group, where
+                // the Q fragments hold channels 8hh..8hh+7 in order: storing
+                // contraction row c at row c with bits 2 and 3 swapped makes
+                // the two agree.
+                const int c = idx / (BV / 8), col8 = (idx % (BV / 8)) * 8;
+                const int r = (c & ~12) | ((c & 4) << 1) | ((c & 8) >> 1);
+                static_assert(std::is_same_v<S, T>, "gradient modes store states in the I/O type");
+#pragma unroll
+                for (int x = 0; x < 8 / VEC; ++x) pf.c[u][x].store(&sm.cst[r][col8 + VEC * x]);
+                continue;
+            }
+            const int vr = idx / (CW / 8);
+            const int c8 = (idx % (CW / 8)) * 8;
             if constexpr (std::is_same_v<S, T>) {
 #pragma unroll
                 for (int x = 0; x < 8 / VEC; ++x) pf.c[u][x].store(&sm.cs[vr][c8 + VEC * x]);
@@ -343,7 +359,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
             for (int kk = 0; kk < CW / 16; ++kk) {
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    const Frag bf = load8(&sm.cs[32 * nt + i32][16 * kk + 8 * hh]);
+                    Frag bf;
+                    if constexpr (NAT) bf = frag_tr(sm.cst, 16 * kk, 32 * nt, lane);
+                    else bf = load8(&sm.cs[32 * nt + i32][16 * kk + 8 * hh]);
                     acc[nt] = mma32(qf[cb / 16 + kk], bf, acc[nt]);
                 }
             }
