@@ -155,7 +155,11 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, hh = lane >> 5, i32 = lane & 31;
-    const int tq = t0 + 32 * w + i32;      // query step of this lane's fragment row
+    // this wave's 32-row block: with 8 waves, waves w and w + 4 share a SIMD,
+    // and block b meets b + 1 causal key halves, so the pairs take blocks
+    // {s, 7 - s} (9 halves per SIMD instead of 6..12)
+    const int wr = (NW == 8 && w >= 4) ? 11 - w : w;
+    const int tq = t0 + 32 * wr + i32;     // query step of this lane's fragment row
     // Rows at or past T are read clamped to row T-1 (branch-free loads): a
     // query row past the end only feeds its own output row, which is never
     // stored, and a key/value row past the end only meets query rows before
@@ -369,7 +373,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
         if (GATE != kGla) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int t = min(t0 + 32 * w + 8 * (r >> 2) + 4 * hh + (r & 3), T_ - 1);
+                const int t = min(t0 + 32 * wr + 8 * (r >> 2) + 4 * hh + (r & 3), T_ - 1);
                 const float e = (GATE == kSig) ? exp2_fast(ab[t] * kLog2e)
                                                : exp2_fast((float)(t - cs + (REV ? 0 : 1)) * lg2);
 #pragma unroll
@@ -399,7 +403,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
         fref = R;
     };
     const float at2 = (GATE == kSig) ? ab[tqc] * kLog2e : 0.0f;
-    const int tlo = t0 + 32 * w;                  // first query row of this wave
+    const int tlo = t0 + 32 * wr;                  // first query row of this wave
     const int nkv = (t0 - cs) / 64 + BQ / 64;     // key tiles up to the end of the query tile
     int q_ref = -2;                               // reference row the Q fragments are scaled for
 
@@ -501,7 +505,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
         // out of the frame: e^{a_t - a_fref}, t within 31 steps before fref
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int t = min(t0 + 32 * w + 8 * (r >> 2) + 4 * hh + (r & 3), T_ - 1);
+            const int t = min(t0 + 32 * wr + 8 * (r >> 2) + 4 * hh + (r & 3), T_ - 1);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const int col = v0 + 32 * nt + i32;
@@ -513,7 +517,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int t = t0 + 32 * w + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const int t = t0 + 32 * wr + 8 * (r >> 2) + 4 * hh + (r & 3);
         if (t >= T_) continue;
         T* dst = h + (bh * (size_t)T_ + row(t)) * dhv + v0 + i32;
 #pragma unroll
@@ -526,7 +530,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
         float* db = dots + bh * (size_t)T_ * dhv + v0 + i32;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int t = t0 + 32 * w + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const int t = t0 + 32 * wr + 8 * (r >> 2) + 4 * hh + (r & 3);
             if (t >= T_) continue;
             const size_t o = (size_t)row(t) * dhv;
 #pragma unroll
@@ -540,7 +544,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
         float sum[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int t = min(t0 + 32 * w + 8 * (r >> 2) + 4 * hh + (r & 3), T_ - 1);
+            const int t = min(t0 + 32 * wr + 8 * (r >> 2) + 4 * hh + (r & 3), T_ - 1);
             const T* pr = pb + (size_t)row(t) * dhv;
             float x = 0.0f;
 #pragma unroll
@@ -554,7 +558,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
         if (i32 == 0) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int t = t0 + 32 * w + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const int t = t0 + 32 * wr + 8 * (r >> 2) + 4 * hh + (r & 3);
                 if (t < T_) dots[(bh * (size_t)T_ + row(t)) * nvt + v0 / BV] = sum[r];
             }
         }
