@@ -4,7 +4,9 @@ This module is shared by the tests, the benchmark and the smoke check.  It
 holds no arithmetic of the method: it only draws random numbers with a seeded
 CPU ``torch.Generator`` and casts them (fp32 draws, cast round-to-nearest-even
 to bf16 for the bf16 workloads).  Both the GPU library and the CPU oracle
-receive the very same values.
+receive the very same values.  Inputs too large to draw on the host (the
+size-limit tests) are drawn the same way by a seeded generator on the GPU;
+the oracle then receives copies of the sampled heads.
 
 Draw order for every workload: q, k, v, then the input-gate pre-activation
 (mLSTMsig only), then the forget-gate pre-activation (per step, or per step
@@ -77,15 +79,15 @@ def scalar_decay_logits(H: int) -> torch.Tensor:
     return torch.tensor(vals, dtype=torch.float64).to(torch.float32)
 
 
-def make_inputs(w: Workload, seed: int | None = None) -> dict:
-    """Draws the inputs of ``w`` on the CPU.  Returns a dict with q, k, v
+def make_inputs(w: Workload, seed: int | None = None, device="cpu") -> dict:
+    """Draws the inputs of ``w`` on ``device`` (the CPU unless a test asks for the GPU).  Returns a dict with q, k, v
     (``w.dtype``), igate_pre (fp32 [B,H,T] or None), fgate_pre (fp32)."""
-    g = torch.Generator(device="cpu")
+    g = torch.Generator(device=device)
     g.manual_seed(w.seed if seed is None else seed)
     B, H, T = w.B, w.H, w.T
 
     def normal(shape, std=1.0, mean=0.0):
-        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        x = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
         if std != 1.0:
             x = x * torch.tensor(std, dtype=torch.float32)
         if mean != 0.0:
@@ -98,10 +100,10 @@ def make_inputs(w: Workload, seed: int | None = None) -> dict:
     if w.variant == MLSTM_SIG:
         ig = normal((B, H, T), 1.0, w.igate_mean)
         lo, hi = w.fgate_range
-        fg = torch.rand((B, H, T), generator=g, dtype=torch.float32) * (hi - lo) + lo
+        fg = torch.rand((B, H, T), generator=g, dtype=torch.float32, device=device) * (hi - lo) + lo
     elif w.variant == SCALAR:
         ig = None
-        fg = scalar_decay_logits(H)
+        fg = scalar_decay_logits(H).to(device)
     elif w.variant == GLA:
         ig = None
         fg = normal((B, H, T, w.dqk))
@@ -125,11 +127,11 @@ def initial_state(B: int, H: int, dqk: int, dhv: int, seed: int, std: float = 1.
     return torch.randn((B, H, dqk, dhv), generator=g, dtype=torch.float32) * std
 
 
-def upstream_grad(B: int, H: int, T: int, dhv: int, dtype: torch.dtype, seed: int) -> torch.Tensor:
+def upstream_grad(B: int, H: int, T: int, dhv: int, dtype: torch.dtype, seed: int, device="cpu") -> torch.Tensor:
     """A seeded gradient dL/dh [B,H,T,d_hv] ~ N(0, 1), cast to ``dtype``
     (the input of the backward pass)."""
-    g = torch.Generator().manual_seed(seed)
-    return torch.randn((B, H, T, dhv), generator=g, dtype=torch.float32).to(dtype).contiguous()
+    g = torch.Generator(device=device).manual_seed(seed)
+    return torch.randn((B, H, T, dhv), generator=g, dtype=torch.float32, device=device).to(dtype).contiguous()
 
 
 def head_slice(inputs: dict, variant: int, heads: list) -> dict:
