@@ -305,6 +305,8 @@ def main():
     ap.add_argument("--sweep", type=str, default=None, help="comma-separated chunk sizes to sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
+    ap.add_argument("--no-fp32-states", action="store_true",
+                    help="skip the timing with the states materialised in fp32 (TFLA_STATES_FP32)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (scales HBM byte counters)")
     args = ap.parse_args()
@@ -400,7 +402,7 @@ def main():
     }
     # The same step with the chunk states materialised in fp32 instead of the
     # I/O type (TFLA_STATES_FP32): identical h, twice the state bytes.
-    if wl.dtype_name == "bf16":
+    if wl.dtype_name == "bf16" and not args.no_fp32_states:
         from mlstm_sequence_amd import tfla
         _, _, _, _, h16 = run_gpu(wl, Lh, 2, 1, dev, keep_h=True)
         ms32, _, per32, _, h32 = run_gpu(wl, Lh, args.steps, args.warmup, dev, flags=tfla.STATES_FP32, keep_h=True)
