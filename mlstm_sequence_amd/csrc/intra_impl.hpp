@@ -58,8 +58,8 @@ namespace tfla {
 namespace {
 
 // NATL: the state block is staged as stored, contraction-major (cst), and
-// read through transpose reads
-template <typename T, int DQK, int BV, int CW, bool NATL> struct IntraLds {
+// read through transpose reads; NW waves stage their outputs in os
+template <typename T, int DQK, int BV, int CW, bool NATL, int NW> struct IntraLds {
     static constexpr int kpad = 16 / sizeof(T);   // K / C^T rows: stride = 4 banks mod 32
     static constexpr int vpad = 64 / sizeof(T);   // V rows: stride = 16 banks mod 64 (transpose reads)
     union {
@@ -69,6 +69,7 @@ template <typename T, int DQK, int BV, int CW, bool NATL> struct IntraLds {
         } kv;
         T cs[NATL ? 1 : BV][CW + kpad];    // CW-channel block of C^T [value][channel]
         T cst[NATL ? CW : 1][BV + vpad];   // the same block as [channel][value], rows permuted (see store_c)
+        T os[NW][32][64 + kpad];           // per wave: 32 output rows x 64 columns on their way out
     };
     float bcol[64];                 // mLSTMsig: (li_s - a_s) log2(e) per key step
 };
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     constexpr int NT = BV / 32;           // 32-wide output column tiles
     constexpr int VEC = Elem<T>::vec;
     typedef typename Elem<T>::frag Frag;
-    typedef IntraLds<T, DQK, BV, CW, NAT> Lds;
+    typedef IntraLds<T, DQK, BV, CW, NAT, NW> Lds;
     typedef std::conditional_t<(MODE & kStateF32) != 0, float, T> S;   // stored state type
     constexpr int SVEC = Elem<S>::vec;
     typedef Prefetch<T, S, DQK, BV, CW, NTH> PF;
@@ -515,13 +516,36 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
             }
         }
     }
+    // Out through LDS, 64 columns at a time: the wave writes its accumulators
+    // (lane = column) into its own 32 x 64 block, then every lane stores
+    // 16-byte runs of rows -- 32/VEC wide stores per lane instead of 64
+    // two-byte ones, which otherwise keep the memory pipeline busy after
+    // the last tile.
+    static_assert(NT % 2 == 0, "value tiles are multiples of 64 columns");
+    __syncthreads();   // every wave is done with the tiles the staging blocks overlay
+    T* const hrow = h + bh * (size_t)T_ * dhv + v0;   // this workgroup's output columns
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int t = t0 + 32 * wr + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (t >= T_) continue;
-        T* dst = h + (bh * (size_t)T_ + row(t)) * dhv + v0 + i32;
+    for (int ph = 0; ph < NT / 2; ++ph) {
+        auto os = sm.os[w];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) dst[32 * nt] = from_float<T>(acc[nt][r] * scale);
+        for (int r = 0; r < 16; ++r) {
+            const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
+            os[rr][i32] = from_float<T>(acc[2 * ph][r] * scale);
+            os[rr][32 + i32] = from_float<T>(acc[2 * ph + 1][r] * scale);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int qq = 0; qq < 32 / VEC; ++qq) {
+            const int c = lane + 64 * qq;                 // 16-byte piece of the 32 x 64 block
+            const int rr = c / (64 / VEC), col = (c % (64 / VEC)) * VEC;
+            const int t = t0 + 32 * wr + rr;
+            if (t < T_) {
+                Vec16<T> x;
+                x.load(&os[rr][col]);
+                x.store(hrow + (size_t)row(t) * dhv + 64 * ph + col);
+            }
+        }
+        if (ph + 1 < NT / 2) __syncthreads();   // this block is read before it is overwritten
     }
     if constexpr (DOTS && GATE == kGla) {
         // per-element products of the fp32 output with the partner, before
