@@ -228,14 +228,43 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
     // accumulator element r of lane (hh, i32) in tile (mv, mc): value row
     // vw + 32 mv + arow(r), key column cw + 32 mc + i32
     auto arow = [&](int r) { return 8 * (r >> 2) + 4 * hh + (r & 3); };
+    // The tile leaves through LDS (the block tiles' space, free between
+    // blocks): the waves write their accumulators (lane = key column), then
+    // every thread stores 16-byte runs of rows -- a few wide stores per lane
+    // instead of MV*MC*16 element stores.  Called by every thread.
+    constexpr int SP = 16 / sizeof(S);                 // row pad: 16 bytes
+    constexpr bool STAGE = sizeof(S) * TV * (TC + SP) <= sizeof(StateLds<T, SB, TV, TC>);
     auto put_state = [&](const f32x16 (&acc)[MV][MC], int slot) {
+        if constexpr (STAGE) {
+            S (*stg)[TC + SP] = reinterpret_cast<S (*)[TC + SP]>(&sm);
+            __syncthreads();   // every wave is done reading the block's tiles
 #pragma unroll
-        for (int mv = 0; mv < MV; ++mv) {
-            S* dst = states + ((bh * ns + slot) * (size_t)dhv + v0 + vw + 32 * mv) * dqk + c0 + cw + i32;
+            for (int mv = 0; mv < MV; ++mv)
 #pragma unroll
-            for (int mc = 0; mc < MC; ++mc)
+                for (int mc = 0; mc < MC; ++mc)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) dst[(size_t)arow(r) * dqk + 32 * mc] = from_float<S>(acc[mv][mc][r]);
+                    for (int r = 0; r < 16; ++r)
+                        stg[vw + 32 * mv + arow(r)][cw + 32 * mc + i32] = from_float<S>(acc[mv][mc][r]);
+            __syncthreads();
+            constexpr int EV = 16 / sizeof(S), PR = TC / EV;   // elements per piece, pieces per row
+            S* dst = states + ((bh * ns + slot) * (size_t)dhv + v0) * dqk + c0;
+#pragma unroll
+            for (int c = tid; c < TV * PR; c += NTH) {
+                const int rr = c / PR, col = (c % PR) * EV;
+                Vec16<S> x;
+                x.load(&stg[rr][col]);
+                x.store(dst + (size_t)rr * dqk + col);
+            }
+            // the next block's first barrier orders these reads before LDS is refilled
+        } else {
+#pragma unroll
+            for (int mv = 0; mv < MV; ++mv) {
+                S* dst = states + ((bh * ns + slot) * (size_t)dhv + v0 + vw + 32 * mv) * dqk + c0 + cw + i32;
+#pragma unroll
+                for (int mc = 0; mc < MC; ++mc)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dst[(size_t)arow(r) * dqk + 32 * mc] = from_float<S>(acc[mv][mc][r]);
+            }
         }
     };
 
