@@ -234,6 +234,10 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
     // instead of MV*MC*16 element stores.  Called by every thread.
     constexpr int SP = 16 / sizeof(S);                 // row pad: 16 bytes
     constexpr bool STAGE = sizeof(S) * TV * (TC + SP) <= sizeof(StateLds<T, SB, TV, TC>);
+    static_assert(STAGE || !REV, "the reverse walk's couplings go through the staging area");
+    // reverse walk: the forward state's tile in 16-byte pieces, CPN per thread
+    constexpr int CEV = 16 / sizeof(S), CPR = TC / CEV, CPN = TV * CPR / NTH;
+    static_assert(TV * CPR % NTH == 0, "tile pieces spread evenly over the threads");
     auto put_state = [&](const f32x16 (&acc)[MV][MC], int slot) {
         if constexpr (STAGE) {
             S (*stg)[TC + SP] = reinterpret_cast<S (*)[TC + SP]>(&sm);
@@ -317,18 +321,16 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
         }
         // the forward state of the boundary this block ends (reverse walk):
         // loaded now, used after the block's products
+        // (16-byte pieces of rows, as put_state stores them; they reach the
+        // accumulator layout through the staging area at the chunk end)
         const bool dot_now = REV && xpart && last && wk.write_states && kc < nc - 1;
-        float cpre[MV][MC][16];
+        Vec16<S> cvec[CPN];
         if (dot_now) {
+            const S* src = cstates + ((bh * wk.cp_slots + (nc - 2 - kc) + wk.cp_off) * (size_t)dhv + v0) * dqk + c0;
 #pragma unroll
-            for (int mv = 0; mv < MV; ++mv) {
-                const S* src =
-                    cstates + ((bh * wk.cp_slots + (nc - 2 - kc) + wk.cp_off) * (size_t)dhv + v0 + vw + 32 * mv) * dqk +
-                    c0 + cw + i32;
-#pragma unroll
-                for (int mc = 0; mc < MC; ++mc)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) cpre[mv][mc][r] = to_float(src[(size_t)arow(r) * dqk + 32 * mc]);
+            for (int j = 0; j < CPN; ++j) {
+                const int c = tid + NTH * j, rr = c / CPR, col = (c % CPR) * CEV;
+                cvec[j].load(src + (size_t)rr * dqk + col);
             }
         }
         // acc (value rows vw.., key columns cw..) += V^T (w.K) over this block
@@ -346,7 +348,25 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
         }
         if (last && wk.write_states && kc < nc - 1) {
             put_state(acc, REV ? nc - 2 - kc : kc + wk.soff);
+            float cpre[MV][MC][16];
             if (dot_now) {
+                if constexpr (REV) {
+                    S (*stg)[TC + SP] = reinterpret_cast<S (*)[TC + SP]>(&sm);
+                    __syncthreads();   // the state's pieces have been read out of the staging area
+#pragma unroll
+                    for (int j = 0; j < CPN; ++j) {
+                        const int c = tid + NTH * j, rr = c / CPR, col = (c % CPR) * CEV;
+                        cvec[j].store(&stg[rr][col]);
+                    }
+                    __syncthreads();
+#pragma unroll
+                    for (int mv = 0; mv < MV; ++mv)
+#pragma unroll
+                        for (int mc = 0; mc < MC; ++mc)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r)
+                                cpre[mv][mc][r] = to_float(stg[vw + 32 * mv + arow(r)][cw + 32 * mc + i32]);
+                }
                 // the coupling <D_m, C_m> across this chunk boundary: this
                 // wave's share, against the forward state stored in the
                 // same slot and layout
