@@ -522,6 +522,24 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     // two-byte ones, which otherwise keep the memory pipeline busy after
     // the last tile.
     static_assert(NT % 2 == 0, "value tiles are multiples of 64 columns");
+    // Row dots (per-step gates): the partner rows arrive as 16-byte pieces and
+    // reach the accumulator layout through the same blocks.
+    constexpr bool RDOTS = DOTS && GATE != kGla;
+    Vec16<T> ppc[RDOTS ? NT / 2 : 1][32 / VEC];
+    float sum[16];
+    if constexpr (RDOTS) {
+        const T* pb = partner + bh * (size_t)T_ * dhv + v0;
+#pragma unroll
+        for (int ph = 0; ph < NT / 2; ++ph)
+#pragma unroll
+            for (int qq = 0; qq < 32 / VEC; ++qq) {
+                const int c = lane + 64 * qq, rr = c / (64 / VEC), col = (c % (64 / VEC)) * VEC;
+                const int t = min(t0 + 32 * wr + rr, T_ - 1);
+                ppc[ph][qq].load(pb + (size_t)row(t) * dhv + 64 * ph + col);
+            }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum[r] = 0.0f;
+    }
     __syncthreads();   // every wave is done with the tiles the staging blocks overlay
     T* const hrow = h + bh * (size_t)T_ * dhv + v0;   // this workgroup's output columns
 #pragma unroll
@@ -545,6 +563,24 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
                 x.store(hrow + (size_t)row(t) * dhv + 64 * ph + col);
             }
         }
+        if constexpr (RDOTS) {
+            // row dot products of the fp32 output with the partner rows, before
+            // rounding: the gate gradients sum them over the sequence, where
+            // rounding first would not cancel
+            __syncthreads();   // the output pieces have been read
+#pragma unroll
+            for (int qq = 0; qq < 32 / VEC; ++qq) {
+                const int c = lane + 64 * qq, rr = c / (64 / VEC), col = (c % (64 / VEC)) * VEC;
+                ppc[ph][qq].store(&os[rr][col]);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
+                sum[r] += acc[2 * ph][r] * scale * to_float(os[rr][i32]);
+                sum[r] += acc[2 * ph + 1][r] * scale * to_float(os[rr][32 + i32]);
+            }
+        }
         if (ph + 1 < NT / 2) __syncthreads();   // this block is read before it is overwritten
     }
     if constexpr (DOTS && GATE == kGla) {
@@ -560,21 +596,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) db[o + 32 * nt] = acc[nt][r] * scale * to_float(pb[o + 32 * nt]);
         }
-    } else if constexpr (DOTS) {
-        // row dot products of the fp32 output with the partner rows, before
-        // rounding: the gate gradients sum them over the sequence, where
-        // rounding first would not cancel
-        const T* pb = partner + bh * (size_t)T_ * dhv + v0 + i32;
-        float sum[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int t = min(t0 + 32 * wr + 8 * (r >> 2) + 4 * hh + (r & 3), T_ - 1);
-            const T* pr = pb + (size_t)row(t) * dhv;
-            float x = 0.0f;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) x += acc[nt][r] * scale * to_float(pr[32 * nt]);
-            sum[r] = x;
-        }
+    } else if constexpr (RDOTS) {
 #pragma unroll
         for (int m = 1; m < 32; m <<= 1)
 #pragma unroll
