@@ -67,13 +67,16 @@ __global__ __launch_bounds__(256) void gates_mirror_gla_kernel(const float* __re
                                                               const float* __restrict__ g, float* __restrict__ ar,
                                                               int T_, int L, int nc, int dqk)
 {
+    // four consecutive channels per thread (d_qk is a multiple of 64)
     const size_t bh = blockIdx.y;
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t idx = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
     const int t = (int)(idx / dqk), c = (int)(idx % dqk);
     if (t >= T_) return;
     const int kc = t / L, cs = kc * L, len = min(L, T_ - cs);
     const int p = 2 * cs + len - 1 - t;
-    ar[(bh * T_ + t) * dqk + c] = g[(bh * nc + kc) * dqk + c] - a[(bh * T_ + p) * dqk + c];
+    const f32x4 gv = *reinterpret_cast<const f32x4*>(g + (bh * nc + kc) * dqk + c);
+    const f32x4 av = *reinterpret_cast<const f32x4*>(a + (bh * T_ + p) * dqk + c);
+    *reinterpret_cast<f32x4*>(ar + (bh * T_ + t) * dqk + c) = gv - av;
 }
 
 // r_t and k_t.dk_t from the per-tile partial dots of step t
@@ -161,12 +164,28 @@ __global__ __launch_bounds__(256) void grad_gla_kernel(const float* __restrict__
         for (int j = 0; j < nx; ++j) acc += xp[j];
         acc *= scale;
     }
-    for (int t = ce - 1; t >= cs; --t) {
-        const size_t o = (bh * T_ + t) * dqk + c;
-        acc += (double)dq_prod[o] - (double)dk_prod[o];
-        const float x = fg[o];
-        const bool floored = log_sigmoid(x) * (1.0f / 16.0f) < kLogForgetFloor;
-        dfg[o] = floored ? 0.0f : (float)(acc / (16.0 * (1.0 + exp((double)x))));
+    // the running sum in double; the factor d log f / dx = sigmoid(-x) / 16
+    // in fp32 (full relative precision); loads of U steps issued together
+    constexpr int U = 8;
+    for (int t1 = ce; t1 > cs; t1 -= U) {
+        float dqv[U], dkv[U], xv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t o = (bh * T_ + max(t1 - 1 - u, cs)) * dqk + c;
+            dqv[u] = dq_prod[o];
+            dkv[u] = dk_prod[o];
+            xv[u] = fg[o];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = t1 - 1 - u;
+            if (t < cs) break;
+            acc += (double)dqv[u] - (double)dkv[u];
+            const float x = xv[u];
+            const bool floored = log_sigmoid(x) * (1.0f / 16.0f) < kLogForgetFloor;
+            const float f = 1.0f / (16.0f * (1.0f + expf(x)));
+            dfg[(bh * T_ + t) * dqk + c] = floored ? 0.0f : (float)(acc * (double)f);
+        }
     }
 }
 
@@ -256,7 +275,7 @@ __global__ __launch_bounds__(256) void final_coupling_kernel(const float* __rest
 hipError_t launch_gates_mirror(const Problem& p, const Workspace& ws, float* ar, float* lr, hipStream_t stream)
 {
     if (p.gate == kGla) {
-        const dim3 grid((unsigned)(((size_t)p.T * p.dqk + 255) / 256), (unsigned)(p.B * p.H));
+        const dim3 grid((unsigned)(((size_t)p.T * p.dqk / 4 + 255) / 256), (unsigned)(p.B * p.H));
         gates_mirror_gla_kernel<<<grid, 256, 0, stream>>>(ws.a, ws.g, ar, p.T, p.L, p.nc, p.dqk);
     } else {
         const dim3 grid((unsigned)((p.T + 255) / 256), (unsigned)(p.B * p.H));
