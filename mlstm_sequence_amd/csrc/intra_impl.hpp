@@ -12,11 +12,13 @@
 // and loops over the 64-step key/value tiles up to its own rows, so the
 // chunk size L is bounded by nothing on chip.
 //
-// Workgroup = NW wavefronts (2, 4 or 8), wave w owning query rows
-// 32w..32w+31 (BQ = 32 NW, at most the chunk size);
+// Workgroup = NW wavefronts (2, 4 or 8), each owning 32 query rows (BQ =
+// 32 NW, at most the chunk size; with 8 waves the two waves of a SIMD take
+// row blocks s and 7 - s, which evens out the causal work);
 // all products are 32x32x16 matrix-core tiles:
 //   inter: acc = Q C_{k-1}[:, v-tile]; C^T is staged in LDS per CW-channel
-//          block (fp32 -> operand type, RNE); Q fragments stay in registers
+//          block (stored in the operand type by the state walk; fp32 states
+//          are rounded RNE on the way in); Q fragments stay in registers
 //          (A operand here, B operand of S^T below); rows scaled by e^{a_t}.
 //   intra: per key tile j: K_j and V_j staged row-major in LDS; per 32-step
 //          half: S^T = K Q^T, decay and causal mask in fp32 (a select, never
@@ -25,7 +27,8 @@
 //          order the accumulator holds it, and V_j is read in that order with
 //          LDS transpose reads.  Halves entirely above the diagonal are
 //          skipped per wave.
-//   out:   h = acc * scale, rounded to the I/O type.
+//   out:   h = acc * scale, rounded to the I/O type, through LDS (each wave
+//          stages 32 rows x 64 columns, then stores 16-byte runs of rows).
 // Every stage (a block of C^T, a K/V tile) is software-pipelined: its global
 // loads are issued into registers right after the previous stage reached
 // LDS, with consecutive lanes on consecutive 16-byte pieces of a row.
@@ -38,7 +41,7 @@
 // (the intra-chunk structure is shared; see tfla_bwd) through MODE bits:
 //   kNatState: the state block is stored contraction-major ([d_c][d_out],
 //              the natural layout of a state whose rows are contracted);
-//              it is read column-wise and staged out-major like C^T.
+//              it is staged as stored and read through transpose reads.
 //   kMirror:   the rows of every chunk are visited in reverse order (logical
 //              row cs + r is physical step cs + len - 1 - r), which turns the
 //              anti-causal sums of the backward pass into causal ones; the
@@ -46,6 +49,13 @@
 //              none for the last chunk), and the gate arrays are indexed by
 //              the logical row (a' = g - a + li for the query rows, and the
 //              key-side exponent li_s - a'_s = a_s - g stored pre-combined).
+//   kRowDots:  also the fp32 row dot products of the output with a partner
+//              tensor (per-step gates), or the per-element products (the
+//              per-channel gate), for the gate gradients.
+//   kEmitP / kGivenP: P (the decayed, masked S of a chunk, per-step gates)
+//              written once, or read instead of computed (dq reads it by
+//              rows, dk transposed in mirrored order).
+//   kStateF32: the forward pass reading fp32 states with bf16 I/O.
 #pragma once
 
 #include <cstdlib>
