@@ -532,12 +532,15 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     // two-byte ones, which otherwise keep the memory pipeline busy after
     // the last tile.
     static_assert(NT % 2 == 0, "value tiles are multiples of 64 columns");
-    // Row dots (per-step gates): the partner rows arrive as 16-byte pieces and
-    // reach the accumulator layout through the same blocks.
-    constexpr bool RDOTS = DOTS && GATE != kGla;
-    Vec16<T> ppc[RDOTS ? NT / 2 : 1][32 / VEC];
+    // Row dots (per-step gates) and per-element products (per-channel gate):
+    // the partner rows arrive as 16-byte pieces and reach the accumulator
+    // layout through the same blocks; the products leave through an fp32 view
+    // of the staging area where it fits.
+    constexpr bool RDOTS = DOTS && GATE != kGla, GDOTS = DOTS && GATE == kGla;
+    constexpr bool FSTAGE = GDOTS && sizeof(float) * NW * 32 * 68 <= sizeof(Lds) - sizeof(float) * 64;   // not into bcol
+    Vec16<T> ppc[DOTS ? NT / 2 : 1][32 / VEC];
     float sum[16];
-    if constexpr (RDOTS) {
+    if constexpr (DOTS) {
         const T* pb = partner + bh * (size_t)T_ * dhv + v0;
 #pragma unroll
         for (int ph = 0; ph < NT / 2; ++ph)
@@ -591,22 +594,56 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
                 sum[r] += acc[2 * ph + 1][r] * scale * to_float(os[rr][32 + i32]);
             }
         }
+        if constexpr (GDOTS) {
+            // per-element products of the fp32 output with the partner, before
+            // rounding (the per-channel gate gradient sums them per channel)
+            __syncthreads();   // the output pieces have been read
+#pragma unroll
+            for (int qq = 0; qq < 32 / VEC; ++qq) {
+                const int c = lane + 64 * qq, rr = c / (64 / VEC), col = (c % (64 / VEC)) * VEC;
+                ppc[ph][qq].store(&os[rr][col]);
+            }
+            __syncthreads();
+            float prod[2][16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
+                prod[0][r] = acc[2 * ph][r] * scale * to_float(os[rr][i32]);
+                prod[1][r] = acc[2 * ph + 1][r] * scale * to_float(os[rr][32 + i32]);
+            }
+            float* db = dots + bh * (size_t)T_ * dhv + v0 + 64 * ph;
+            if constexpr (FSTAGE) {
+                // this wave's 32 x 64 fp32 block (stride 68), then 16-byte runs of rows
+                __syncthreads();   // every wave has read its partner values
+                float (*fs)[68] = reinterpret_cast<float (*)[68]>(&sm) + 32 * w;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
+                    fs[rr][i32] = prod[0][r];
+                    fs[rr][32 + i32] = prod[1][r];
+                }
+                __syncthreads();
+#pragma unroll
+                for (int qq = 0; qq < 8; ++qq) {
+                    const int c = lane + 64 * qq, rr = c / 16, col = (c % 16) * 4;
+                    const int t = t0 + 32 * wr + rr;
+                    if (t < T_)
+                        *reinterpret_cast<f32x4*>(db + (size_t)row(t) * dhv + col) =
+                            *reinterpret_cast<const f32x4*>(&fs[rr][col]);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int t = t0 + 32 * wr + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    if (t >= T_) continue;
+                    db[(size_t)row(t) * dhv + i32] = prod[0][r];
+                    db[(size_t)row(t) * dhv + 32 + i32] = prod[1][r];
+                }
+            }
+        }
         if (ph + 1 < NT / 2) __syncthreads();   // this block is read before it is overwritten
     }
-    if constexpr (DOTS && GATE == kGla) {
-        // per-element products of the fp32 output with the partner, before
-        // rounding (the per-channel gate gradient sums them per channel)
-        const T* pb = partner + bh * (size_t)T_ * dhv + v0 + i32;
-        float* db = dots + bh * (size_t)T_ * dhv + v0 + i32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int t = t0 + 32 * wr + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (t >= T_) continue;
-            const size_t o = (size_t)row(t) * dhv;
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) db[o + 32 * nt] = acc[nt][r] * scale * to_float(pb[o + 32 * nt]);
-        }
-    } else if constexpr (RDOTS) {
+    if constexpr (RDOTS) {
 #pragma unroll
         for (int m = 1; m < 32; m <<= 1)
 #pragma unroll
