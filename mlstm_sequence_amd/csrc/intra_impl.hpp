@@ -140,9 +140,10 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     constexpr int BQ = 32 * NW;           // query rows per workgroup
     // C^T channels per stage: 128 (two stages at d_qk = 256) when the
     // registers allow, 64 for fp32 at four or more waves; two-wave
-    // workgroups hold a larger K/V prefetch, which 128-channel blocks of
-    // bf16 states fit inside
-    constexpr int CW = NW >= 4 ? ((sizeof(T) == 2 && DQK >= 128) ? 128 : 64) : (DQK >= 128 ? 128 : 64);
+    // workgroups and the 512-wide contraction at four waves hold a larger
+    // K/V prefetch, which 128- (256-) channel blocks of bf16 states fit inside
+    constexpr int CW = NW >= 4 ? ((sizeof(T) == 2 && DQK >= 128) ? (NW == 4 && DQK == 512 ? 256 : 128) : 64)
+                               : (DQK >= 128 ? 128 : 64);
     constexpr int KQ = DQK / 16;          // 16-channel contraction steps
     constexpr int NT = BV / 32;           // 32-wide output column tiles
     constexpr int VEC = Elem<T>::vec;
