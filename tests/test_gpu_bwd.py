@@ -87,6 +87,7 @@ BWD_CASES = [
     (GLA, F32, 1, 2, 200, 64, 128, 128),
     (GLA, BF, 2, 1, 700, 128, 512, 256),       # 512-wide contraction, long chunks
     (GLA, BF, 1, 1, 40, 64, 64, 64),           # one partial chunk
+    (GLA, BF, 1, 2, 600, 128, 256, 256),       # 8-wave dq, dk: products stored without the fp32 staging
 ]
 
 
