@@ -561,7 +561,11 @@ hipError_t launch_state_t(const Problem& p, const T* k, const T* v, const float*
     if (const char* e = std::getenv("TFLA_STATE_SB")) sb_cap = std::atoi(e);
     if constexpr (sizeof(T) == 2) {
         if (state_big_tiles(p)) {
-            if (p.L >= 256 && sb_cap >= 256)
+            // 256-step blocks fill the 160 KB of LDS (one workgroup per CU): only
+            // when the walk has no more workgroups than the device has CUs;
+            // otherwise 128-step blocks let two share a CU
+            const long wgs = (long)p.B * p.H * (p.dhv / 128) * (p.dqk / 128) * state_segments(p);
+            if (p.L >= 256 && sb_cap >= 256 && wgs <= 256)
                 return launch_state_cfg<T, 256, 128, 128, 8, REV>(p, k, v, fg, ws, stream);
             if (p.L >= 128 && sb_cap >= 128)
                 return launch_state_cfg<T, 128, 128, 128, 8, REV>(p, k, v, fg, ws, stream);
