@@ -30,12 +30,17 @@ __global__ __launch_bounds__(64) void gates_sig_kernel(const float* __restrict__
     const int E = L >> 6;                     // L is a multiple of 64, <= 1024
     const size_t base = bh * (size_t)T + t0;
 
-    float vals[16];
+    // both gates' loads go out together (one memory round trip)
+    float vals[16], livals[16];
     float run = 0.0f;
     for (int e = 0; e < E; ++e) {
-        const int p = lane * E + e;
+        const int p = min(lane * E + e, n - 1);
+        vals[e] = fg[base + p];
+        livals[e] = ig[base + p];
+    }
+    for (int e = 0; e < E; ++e) {
         float lf = 0.0f;
-        if (p < n) lf = fmaxf(log_sigmoid(fg[base + p]), kLogForgetFloor);
+        if (lane * E + e < n) lf = fmaxf(log_sigmoid(vals[e]), kLogForgetFloor);
         run += lf;
         vals[e] = run;
     }
@@ -50,7 +55,7 @@ __global__ __launch_bounds__(64) void gates_sig_kernel(const float* __restrict__
         const int p = lane * E + e;
         if (p < n) {
             a[base + p] = vals[e] + excl;
-            li[base + p] = log_sigmoid(ig[base + p]);
+            li[base + p] = log_sigmoid(livals[e]);
         }
     }
     const float total = __shfl(incl, 63, 64);
