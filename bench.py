@@ -90,6 +90,18 @@ def backward_flops(wl, L):
 
 
 # --------------------------------------------------------------------------- GPU timing
+def settle(call, seconds=0.05, batch=8):
+    """Untimed calls until `seconds` have passed: the device reaches its
+    steady clocks only after some tens of milliseconds of work, more than a
+    few warm-up steps give."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(batch):
+            call()
+        torch.cuda.synchronize()
+
+
 def run_gpu(wl, L, steps, warmup, inputs_dev, cold_calls=0, flags=0, keep_h=False):
     """flags: extra variant bits (TFLA_STATES_FP32); keep_h: also return h."""
     import torch
@@ -108,25 +120,40 @@ def run_gpu(wl, L, steps, warmup, inputs_dev, cold_calls=0, flags=0, keep_h=Fals
     for _ in range(warmup):
         tfla.tfla_fwd_ws(*args)
     torch.cuda.synchronize()
+    settle(lambda: tfla.tfla_fwd_ws(*args))
 
+    # Per-kernel durations: events recorded on the launch stream between the
+    # kernels (tfla_fwd_ws_marked).  The markers themselves add ~10 us per
+    # step, so this pass's step time is reported separately; it also brings
+    # the device to its steady state before the step time is taken.
     marks = []
     for _ in range(steps):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         for ev in evs:
             ev.record(stream)          # creates the event; the library re-records it
         marks.append(evs)
+    mstart = torch.cuda.Event(enable_timing=True)
+    mend = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    mstart.record(stream)
+    for i in range(steps):
+        tfla.tfla_fwd_ws_marked(*args, [ev.cuda_event for ev in marks[i]])
+    mend.record(stream)
+    torch.cuda.synchronize()
+    ms_marked = mstart.elapsed_time(mend) / steps
+
+    # The step time: the library call itself, no instrumentation between its
+    # kernels.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(steps):
-        tfla.tfla_fwd_ws_marked(*args, [ev.cuda_event for ev in marks[i]])
+        tfla.tfla_fwd_ws(*args)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
     ms = start.elapsed_time(end) / steps
     cold = None
     if cold_calls:
@@ -151,6 +178,7 @@ def run_gpu(wl, L, steps, warmup, inputs_dev, cold_calls=0, flags=0, keep_h=Fals
         per["state"] += evs[1].elapsed_time(evs[2])
         per["intra"] += evs[2].elapsed_time(evs[3])
     per = {kname: t / steps for kname, t in per.items()}
+    per["step_with_marks"] = ms_marked
     del ws
     return ms, wall / steps * 1e3, per, cold, (h if keep_h else None)
 
@@ -176,6 +204,8 @@ def run_gpu_bwd(wl, L, steps, warmup, inputs_dev, dh):
     def timed(call):
         for _ in range(warmup):
             call()
+        torch.cuda.synchronize()
+        settle(call, batch=2)
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -217,6 +247,8 @@ def run_gpu_decode(wl, steps_per_call, calls, warmup):
                                            wl.B, wl.H, steps_per_call, wl.dqk, wl.dhv, var)
     for _ in range(warmup):
         call()
+    torch.cuda.synchronize()
+    settle(call)
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
