@@ -14,7 +14,7 @@ ROOT = os.path.dirname(_HERE)
 CSRC = os.path.join(_HERE, "csrc")
 OBJDIR = os.path.join(ROOT, "_build", "libtfla")
 LIB = os.path.join(_HERE, "libtfla.so")
-SOURCES = ["tfla_api.cpp", "gates.hip", "state.hip", "intra.hip", "recurrent.hip", "grad.hip",
+SOURCES = ["tfla_api.cpp", "gates.hip", "state.hip", "intra.hip", "intra_sweep.hip", "recurrent.hip", "grad.hip",
            "intra_bwd_q.hip", "intra_bwd_k.hip", "intra_bwd_v.hip", "intra_bwd_p.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -1,0 +1,371 @@
+// intra_sweep.hip -- the forward pass's intra-chunk kernel for value widths
+// of two or more 128-column tiles (per-step gates, bf16 I/O, chunks of 256
+// steps).
+//
+// Per chunk it evaluates the same sum as the per-tile kernel (intra_impl.hpp)
+//   h_t = scale * ( e^{a_t} q_t^T C_{k-1} + sum_{cs <= s <= t} P_ts v_s ),
+//   P_ts = e^{a_t - a_s + li_s} (q_t . k_s)       (fixed decay: f^{t-s} (q_t . k_s))
+// but one workgroup owns a whole chunk of one head and every value column.
+// When value tiles belong to separate workgroups, each of them reads the
+// chunk's Q and K again and forms S = K Q^T again; on this chip the kernel's
+// time follows the bytes its CUs pull from L2, and Q and K are most of them.
+// Here:
+//   1. P once: K tiles staged in LDS, S^T = K Q^T on the matrix cores with
+//      the Q fragments in registers, decay and causal mask in fp32, and each
+//      wave's P rows parked in LDS as matrix-core A fragments -- written and
+//      read back by the lane that owns them, so no barrier guards them;
+//   2. per 128-wide value tile: acc = Q C_{k-1}^T[:, tile] (C^T blocks staged
+//      in LDS; rows scaled by e^{a_t}), acc += P V_tile (V tiles staged in
+//      LDS, read by transpose reads), h = scale * acc out through LDS.
+// Q and K cross from L2 once per chunk instead of once per value tile, and S
+// is formed once.  The products, their order and every rounding are those of
+// the per-tile kernel, so h is the same to the bit.  Every stage (K tile,
+// C^T block, V tile) is software-pipelined across the phase boundaries: its
+// global loads are issued into registers while the previous stage computes.
+//
+// Workgroup = NW = 8 waves, each owning 32 query rows; the two waves of a
+// SIMD take row blocks s and 7 - s, which evens out the causal work.
+#include <cstdlib>
+#include <type_traits>
+
+#include "gfx950.hpp"
+#include "kernels.hpp"
+
+namespace tfla {
+namespace {
+
+constexpr int kSweepBV = 128;   // value tile width
+
+template <int DQK> constexpr int sweep_cw() { return DQK >= 128 ? 128 : 64; }   // C^T channels per stage
+
+template <typename T, int DQK, int NW> struct SweepLds {
+    static constexpr int kpad = 16 / sizeof(T);   // K / C^T rows: stride = 4 banks mod 32
+    static constexpr int vpad = 64 / sizeof(T);   // V rows: stride = 16 banks mod 64 (transpose reads)
+    static constexpr int CW = sweep_cw<DQK>();
+    union {
+        T ks[64][DQK + kpad];             // K tile [step][channel]
+        T vs[64][kSweepBV + vpad];        // V tile [step][value]
+        T cs[kSweepBV][CW + kpad];        // C^T block [value][channel]
+        T os[NW][32][64 + kpad];          // per wave: 32 output rows x 64 columns on their way out
+    };
+    // P fragments: the wave with row block b owns the 32-key blocks m <= b
+    // of its rows, two 16-key halves each, one 16-byte fragment per lane:
+    // entry 2 (b(b+1)/2 + m) + half
+    bf16x8 p[NW * (NW + 1)][64];
+    float bcol[64];                       // mLSTMsig: (li_s - a_s) log2(e) per key step of the K tile
+};
+
+template <typename T, int GATE, int DQK, int NW, typename S>
+__global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __restrict__ q, const T* __restrict__ k,
+                                                                const T* __restrict__ v,
+                                                                const float* __restrict__ a,
+                                                                const float* __restrict__ li,
+                                                                const float* __restrict__ fg,
+                                                                const S* __restrict__ states, T* __restrict__ h,
+                                                                int H, int T_, int dhv, int nc, int c0, float scale)
+{
+    static_assert(GATE != kGla, "per-step gates only");
+    constexpr int NTH = 64 * NW, BQ = 32 * NW, BV = kSweepBV, NT = BV / 32, KQ = DQK / 16;
+    constexpr int CW = sweep_cw<DQK>(), NKV = BQ / 64;
+    constexpr int VEC = Elem<T>::vec, SVEC = Elem<S>::vec;
+    constexpr int NK = 64 * DQK / VEC / NTH;      // K tile: 16-byte items per thread
+    constexpr int NV = 64 * BV / VEC / NTH;       // V tile: 16-byte items per thread
+    constexpr int NC = BV * CW / 8 / NTH;         // C^T block: 8-element items per thread
+    static_assert(NK >= 1 && NV >= 1 && NC >= 1, "tile too small for the workgroup");
+    typedef typename Elem<T>::frag Frag;
+    __shared__ SweepLds<T, DQK, NW> sm;
+
+    const int blk = xcd_remap(blockIdx.x, gridDim.x);
+    const size_t bh = blk / nc;
+    const int kc = blk % nc, cs = kc * BQ;        // the query tile is the chunk
+    const int nvt = dhv / BV;
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, lane = tid & 63, hh = lane >> 5, i32 = lane & 31;
+    const int wr = (NW == 8 && w >= 4) ? 11 - w : w;
+    const int tlo = cs + 32 * wr;                 // first query row of this wave
+    // Rows at or past T are read clamped to row T-1: a query row past the
+    // end only feeds its own output row, which is never stored, and a key /
+    // value row past the end only meets query rows before it through the
+    // causal select (P = 0, times finite data).
+    const int tqc = min(tlo + i32, T_ - 1);
+
+    const T* qb = q + bh * (size_t)T_ * DQK;
+    const T* kb = k + bh * (size_t)T_ * DQK;
+    const T* vb = v + bh * (size_t)T_ * dhv;
+    const float* ab = (GATE == kSig) ? a + bh * (size_t)T_ : nullptr;
+    const float* lb = (GATE == kSig) ? li + bh * (size_t)T_ : nullptr;
+    float lg2 = 0.0f;   // log2 of the fixed decay
+    if (GATE == kScalar) lg2 = fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor) * kLog2e;
+
+    // states hold C before chunks 1..nc-1, preceded by C_0 when one is given
+    const bool inter = kc > 0 || c0;
+    const S* sb = inter ? states + (bh * (nc - 1 + c0) + (kc - 1 + c0)) * (size_t)dhv * DQK : states;
+
+    // ---- stage loaders (global -> registers) and writers (registers -> LDS)
+    Vec16<T> pk[NK], pv[NV];
+    Vec16<S> pc[NC][8 / SVEC];
+    float pli = 0.0f, pa = 0.0f;
+    auto fetch_k = [&](int s0) {
+#pragma unroll
+        for (int u = 0; u < NK; ++u) {
+            const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
+            pk[u].load(kb + (size_t)min(s0 + r, T_ - 1) * DQK + c);
+        }
+        if (GATE == kSig && tid < 64) {
+            const int s = min(s0 + tid, T_ - 1);
+            pli = lb[s];
+            pa = ab[s];
+        }
+    };
+    auto store_k = [&]() {
+#pragma unroll
+        for (int u = 0; u < NK; ++u) {
+            const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
+            pk[u].store(&sm.ks[r][c]);
+        }
+        if (GATE == kSig && tid < 64) sm.bcol[tid] = (pli - pa) * kLog2e;
+    };
+    auto fetch_c = [&](int v0, int cb) {
+#pragma unroll
+        for (int u = 0; u < NC; ++u) {
+            const int idx = tid + NTH * u, vr = idx / (CW / 8), c8 = (idx % (CW / 8)) * 8;
+            const S* src = sb + (size_t)(v0 + vr) * DQK + cb + c8;
+#pragma unroll
+            for (int x = 0; x < 8 / SVEC; ++x) pc[u][x].load(src + SVEC * x);
+        }
+    };
+    auto store_c = [&]() {
+#pragma unroll
+        for (int u = 0; u < NC; ++u) {
+            const int idx = tid + NTH * u, vr = idx / (CW / 8), c8 = (idx % (CW / 8)) * 8;
+            if constexpr (std::is_same_v<S, T>) {
+#pragma unroll
+                for (int x = 0; x < 8 / VEC; ++x) pc[u][x].store(&sm.cs[vr][c8 + VEC * x]);
+            } else {
+                // fp32 states, bf16 operands: RNE on the way into LDS
+                Vec16<T> y;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y.set(e, pc[u][e / SVEC].get(e % SVEC));
+                y.store(&sm.cs[vr][c8]);
+            }
+        }
+    };
+    auto fetch_v = [&](int v0, int s0) {
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int idx = tid + NTH * u, r = idx / (BV / VEC), c = (idx % (BV / VEC)) * VEC;
+            pv[u].load(vb + (size_t)min(s0 + r, T_ - 1) * dhv + v0 + c);
+        }
+    };
+    auto store_v = [&]() {
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int idx = tid + NTH * u, r = idx / (BV / VEC), c = (idx % (BV / VEC)) * VEC;
+            pv[u].store(&sm.vs[r][c]);
+        }
+    };
+    // the first stage of value tile nv
+    auto fetch_first = [&](int nv) {
+        if (inter) fetch_c(nv * BV, 0);
+        else fetch_v(nv * BV, cs);
+    };
+
+    // Q fragments (lane row tqc, channels 16 kq + 8 hh ..): the B operand of
+    // S^T = K Q^T and the A operand of Q C^T
+    Frag qf[KQ];
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq) qf[kq] = load8(qb + (size_t)tqc * DQK + 16 * kq + 8 * hh);
+
+    bf16x8 (*const pw)[64] = &sm.p[wr * (wr + 1)];   // this wave's P blocks
+
+    // ---------------- 1. P = decay o mask o S, once per chunk
+    const float at2 = (GATE == kSig) ? ab[tqc] * kLog2e : 0.0f;
+    fetch_k(cs);
+    for (int j = 0; j < NKV; ++j) {
+        const int s0 = cs + 64 * j;
+        __syncthreads();
+        store_k();
+        __syncthreads();
+        if (j + 1 < NKV) fetch_k(s0 + 64);
+        else fetch_first(0);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            const int slo = s0 + 32 * mt;
+            if (slo > tlo || slo >= T_) continue;   // wholly above the diagonal, or past the end
+            const bool diag = slo == tlo;
+            // S^T (32 key steps x 32 query rows of this wave)
+            f32x16 st;
+            for (int r = 0; r < 16; ++r) st[r] = 0.0f;
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) {
+                const Frag af = load8(&sm.ks[32 * mt + i32][16 * kq + 8 * hh]);
+                st = mma32(af, qf[kq], st);
+            }
+            // decay and causal mask: element r is key step slo + sr, query row tlo + i32
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int sr = 8 * (r >> 2) + 4 * hh + (r & 3);
+                float p = st[r];
+                if (GATE == kSig) p *= exp2_fast(at2 + sm.bcol[32 * mt + sr]);
+                else p *= exp2_fast((float)(tlo + i32 - slo - sr) * lg2);
+                st[r] = (diag && sr > i32) ? 0.0f : p;
+            }
+            // the accumulator, in its own order, is the A operand of P V
+            const int m = (slo - cs) / 32;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                Frag pfr;
+                for (int e = 0; e < 8; ++e) frag_set(pfr, e, st[8 * half + e]);
+                pw[2 * m + half][lane] = pfr;
+            }
+        }
+    }
+
+    // ---------------- 2. every value tile
+    T* const hbase = h + bh * (size_t)T_ * dhv;
+    for (int nv = 0; nv < nvt; ++nv) {
+        const int v0 = nv * BV;
+        f32x16 acc[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
+        if (inter) {
+            // e^{a_t} q_t^T C_{k-1}
+            for (int cb = 0; cb < DQK; cb += CW) {
+                __syncthreads();
+                store_c();
+                __syncthreads();
+                if (cb + CW < DQK) fetch_c(v0, cb + CW);
+                else fetch_v(v0, cs);
+#pragma unroll
+                for (int kk = 0; kk < CW / 16; ++kk) {
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        const Frag bf = load8(&sm.cs[32 * nt + i32][16 * kk + 8 * hh]);
+                        acc[nt] = mma32(qf[cb / 16 + kk], bf, acc[nt]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int t = min(tlo + 8 * (r >> 2) + 4 * hh + (r & 3), T_ - 1);
+                const float e = (GATE == kSig) ? exp2_fast(ab[t] * kLog2e) : exp2_fast((float)(t - cs + 1) * lg2);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= e;
+            }
+        }
+        // + P V, key tile by key tile
+        for (int j = 0; j < NKV; ++j) {
+            const int s0 = cs + 64 * j;
+            __syncthreads();
+            store_v();
+            __syncthreads();
+            if (j + 1 < NKV) fetch_v(v0, s0 + 64);
+            else if (nv + 1 < nvt) fetch_first(nv + 1);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const int slo = s0 + 32 * mt;
+                if (slo > tlo || slo >= T_) continue;   // the blocks step 1 skipped
+                const int m = (slo - cs) / 32;
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const Frag pfr = pw[2 * m + half][lane];
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        const Frag vf = frag_tr(sm.vs, 32 * mt + 16 * half, 32 * nt, lane);
+                        acc[nt] = mma32(pfr, vf, acc[nt]);
+                    }
+                }
+            }
+        }
+        // out through LDS, 64 columns at a time: the wave writes its
+        // accumulators (lane = column) into its own 32 x 64 block, then every
+        // lane stores 16-byte runs of rows
+        __syncthreads();   // every wave is done with the V tile the blocks overlay
+        T* const hrow = hbase + v0;
+#pragma unroll
+        for (int ph = 0; ph < NT / 2; ++ph) {
+            auto os = sm.os[w];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
+                os[rr][i32] = from_float<T>(acc[2 * ph][r] * scale);
+                os[rr][32 + i32] = from_float<T>(acc[2 * ph + 1][r] * scale);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int qq = 0; qq < 32 / VEC; ++qq) {
+                const int c = lane + 64 * qq;                 // 16-byte piece of the 32 x 64 block
+                const int rr = c / (64 / VEC), col = (c % (64 / VEC)) * VEC;
+                const int t = tlo + rr;
+                if (t < T_) {
+                    Vec16<T> x;
+                    x.load(&os[rr][col]);
+                    x.store(hrow + (size_t)t * dhv + 64 * ph + col);
+                }
+            }
+            // this block is read before it is overwritten (the next half, or
+            // the next value tile's first stage after its own barrier)
+            if (ph + 1 < NT / 2) __syncthreads();
+        }
+    }
+}
+
+template <typename S, int GATE, int DQK, int NW>
+hipError_t launch_sweep_t(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
+                          const Workspace& ws, void* h, hipStream_t stream)
+{
+    const float scale = 1.0f / sqrtf((float)p.dqk);
+    const long blocks = (long)p.B * p.H * p.nc;
+    intra_kernel_sweep<bf16, GATE, DQK, NW, S><<<(unsigned)blocks, 64 * NW, 0, stream>>>(
+        static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v), ws.a, ws.li, fg,
+        static_cast<const S*>(ws.states), static_cast<bf16*>(h), p.H, p.T, p.dhv, p.nc, ws.c0 != nullptr, scale);
+    return hipGetLastError();
+}
+
+template <typename S, int GATE, int NW>
+hipError_t sweep_dqk(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
+                     const Workspace& ws, void* h, hipStream_t stream)
+{
+    switch (p.dqk) {
+    case 64: return launch_sweep_t<S, GATE, 64, NW>(p, q, k, v, fg, ws, h, stream);
+    case 128: return launch_sweep_t<S, GATE, 128, NW>(p, q, k, v, fg, ws, h, stream);
+    case 256: return launch_sweep_t<S, GATE, 256, NW>(p, q, k, v, fg, ws, h, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename S>
+hipError_t sweep_gate(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
+                      const Workspace& ws, void* h, hipStream_t stream)
+{
+    if (p.gate == kSig) return sweep_dqk<S, kSig, 8>(p, q, k, v, fg, ws, h, stream);
+    return sweep_dqk<S, kScalar, 8>(p, q, k, v, fg, ws, h, stream);
+}
+
+}  // namespace
+
+// Applies to bf16 I/O, per-step gates, chunks of 256 steps, a contraction
+// of 64..256 channels and two or more 128-wide value tiles.  (Four-wave
+// workgroups for 128-step chunks would hold twice the K prefetch per
+// thread, which spills at a 256-wide contraction.)
+// TFLA_INTRA_SWEEP=0 turns it off (the per-tile kernel then runs; tuning
+// comparisons).
+bool intra_sweeps(const Problem& p)
+{
+    if (const char* e = std::getenv("TFLA_INTRA_SWEEP"))
+        if (std::atoi(e) == 0) return false;
+    return p.bf16 && p.gate != kGla && p.L == 256 &&
+           (p.dqk == 64 || p.dqk == 128 || p.dqk == 256) && p.dhv % kSweepBV == 0 && p.dhv / kSweepBV >= 2;
+}
+
+hipError_t launch_intra_sweep(const Problem& p, const void* q, const void* k, const void* v, const float* fgate_pre,
+                              const Workspace& ws, void* h, hipStream_t stream)
+{
+    if (!intra_sweeps(p)) return hipErrorInvalidValue;
+    if (p.st32) return sweep_gate<float>(p, q, k, v, fgate_pre, ws, h, stream);
+    return sweep_gate<bf16>(p, q, k, v, fgate_pre, ws, h, stream);
+}
+
+}  // namespace tfla

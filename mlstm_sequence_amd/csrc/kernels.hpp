@@ -90,6 +90,11 @@ hipError_t launch_recurrent(const Problem& p, const void* q, const void* k, cons
                             hipStream_t stream);
 hipError_t launch_intra(const Problem& p, const void* q, const void* k, const void* v,
                         const float* fgate_pre, const Workspace& ws, void* h, hipStream_t stream);
+// The forward intra-chunk kernel that forms a chunk's P once and sweeps
+// every value tile with it (launch_intra picks it where intra_sweeps holds).
+bool intra_sweeps(const Problem& p);
+hipError_t launch_intra_sweep(const Problem& p, const void* q, const void* k, const void* v,
+                              const float* fgate_pre, const Workspace& ws, void* h, hipStream_t stream);
 // The intra-chunk kernel in its gradient modes (dq: kNatState | kRowDots;
 // dk: kNatState | kMirror | kRowDots; dv: kMirror): p.dqk is the contracted width (64..512),
 // p.dhv the output width; ws.a / ws.li / ws.states as the mode reads them;

@@ -1,0 +1,100 @@
+"""The value-sweeping intra-chunk kernel of the forward pass (bf16 I/O,
+per-step gates, 256-step chunks, two or more 128-wide value tiles: one
+workgroup per chunk forms P once and sweeps every value tile) against the
+per-tile kernel it replaces there (TFLA_INTRA_SWEEP=0 selects that one).
+Both take the same products in the same order with the same roundings, so h
+must agree to the bit; both must match the oracle."""
+import os
+from contextlib import contextmanager
+
+import pytest
+import torch
+
+import workloads as W
+from gpu_helpers import GATE, TOL, case, gpu_forward, h_f64, oracle_forward, rel_err, to_dev
+from mlstm_sequence_amd import tfla
+
+pytestmark = pytest.mark.gpu
+
+SIG, SCAL = W.MLSTM_SIG, W.SCALAR
+BF = torch.bfloat16
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tfla.lib()
+
+
+@contextmanager
+def per_tile_kernel():
+    old = os.environ.get("TFLA_INTRA_SWEEP")
+    os.environ["TFLA_INTRA_SWEEP"] = "0"
+    try:
+        yield
+    finally:
+        if old is None:
+            del os.environ["TFLA_INTRA_SWEEP"]
+        else:
+            os.environ["TFLA_INTRA_SWEEP"] = old
+
+
+CASES = [
+    # variant, B, H, T, dqk, dhv
+    (SIG, 1, 2, 700, 256, 512),    # ragged last chunk
+    (SIG, 2, 1, 512, 256, 256),    # two full chunks
+    (SIG, 1, 2, 200, 256, 512),    # one partial chunk: no inter-chunk term
+    (SIG, 1, 1, 1, 256, 256),      # a single step
+    (SIG, 1, 2, 257, 128, 384),    # one step into the second chunk; three value tiles
+    (SIG, 1, 2, 900, 64, 256),
+    (SCAL, 2, 2, 600, 128, 256),
+    (SCAL, 1, 2, 1000, 256, 512),
+]
+
+
+@pytest.mark.parametrize("variant,B,H,T,dqk,dhv", CASES)
+def test_sweep_matches_per_tile_kernel_and_oracle(variant, B, H, T, dqk, dhv):
+    print(f"value sweep: variant {variant} B{B} H{H} T{T} {dqk}x{dhv} L256", flush=True)
+    wl, inp = case(variant, B, H, T, dqk, dhv, BF, seed=7 * T + dqk + dhv)
+    h_sweep = gpu_forward(inp, variant, 256)
+    with per_tile_kernel():
+        h_tile = gpu_forward(inp, variant, 256)
+    assert torch.equal(h_sweep, h_tile)
+    assert rel_err(h_f64(h_sweep), oracle_forward(inp, variant)) <= TOL[BF]
+
+
+@pytest.mark.parametrize("variant,flags", [(SIG, 0), (SCAL, 0), (SIG, tfla.STATES_FP32)])
+def test_sweep_with_initial_state(variant, flags):
+    B, H, T, dqk, dhv, L = 1, 2, 600, 256, 256, 256
+    print(f"value sweep with C_0: variant {variant} flags {flags:#x}", flush=True)
+    wl, inp = case(variant, B, H, T, dqk, dhv, BF, seed=91)
+    d = to_dev(inp)
+    c0 = W.initial_state(B, H, dqk, dhv, seed=3, std=1.5).cuda()
+    var = tfla.variant_of(GATE[variant], BF) | flags
+    outs = []
+    for sweep in (True, False):
+        h = torch.full((B, H, T, dhv), float("nan"), dtype=BF, device="cuda")
+        cf = torch.full((B, H, dqk, dhv), float("nan"), device="cuda")
+        if sweep:
+            tfla.tfla_fwd_state(d["q"], d["k"], d["v"], d["igate_pre"], d["fgate_pre"], c0, h, cf, B, H, T, dqk,
+                                dhv, L, var)
+        else:
+            with per_tile_kernel():
+                tfla.tfla_fwd_state(d["q"], d["k"], d["v"], d["igate_pre"], d["fgate_pre"], c0, h, cf, B, H, T,
+                                    dqk, dhv, L, var)
+        torch.cuda.synchronize()
+        outs.append(h)
+    assert torch.equal(outs[0], outs[1])
+    assert bool(torch.isfinite(outs[0]).all())
+
+
+def test_sweep_full_size_headline_workload():
+    """mLSTMsig B=4 H=8 T=8192 d_qk=256 d_hv=512 at L = 256: the launch the bench times."""
+    wl = W.WORKLOADS[3]
+    inp = W.make_inputs(wl, device="cuda")
+    h_sweep = gpu_forward(inp, wl.variant, 256)
+    with per_tile_kernel():
+        h_tile = gpu_forward(inp, wl.variant, 256)
+    assert bool(torch.isfinite(h_sweep).all())
+    assert torch.equal(h_sweep, h_tile)
