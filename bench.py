@@ -14,8 +14,8 @@ must move or compute, not what the kernels happen to execute):
          intra kernel : 2 d_qk d_hv per step of chunks 2..N_c  (q C_{k-1})
                         + n(n+1)(d_qk + d_hv) per chunk of n steps (causal QK^T and PV)
   bytes  gate kernel  : gate pre-activations in, a and li out (16 B per step) + g
-         state kernel : k, v of chunks 1..N_c-1 in, a and li in, fp32 states out
-         intra kernel : q, k, v in, h out, fp32 states in, a and li in
+         state kernel : k, v of chunks 1..N_c-1 in, a and li in, states out (I/O type)
+         intra kernel : q, k, v in, h out, states in (I/O type), a and li in
 The dominant kernel (longest average duration, measured with HIP events
 recorded around each launch on the stream it runs on) is reported against
 the HBM peak (8 TB/s) when its arithmetic intensity is below the bf16
@@ -318,7 +318,7 @@ def traffic_for(kernel, wl, L):
 
 
 def source_sha(kernel):
-    files = {"gates": ["gates.hip"], "state": ["state.hip"], "intra": ["intra.hip", "intra_impl.hpp"]}[kernel]
+    files = {"gates": ["gates.hip"], "state": ["state.hip"], "intra": ["intra.hip", "intra_impl.hpp", "intra_sweep.hip"]}[kernel]
     hs = hashlib.sha256()
     for f in files + ["gfx950.hpp"]:
         with open(os.path.join(ROOT, "mlstm_sequence_amd", "csrc", f), "rb") as fh:
