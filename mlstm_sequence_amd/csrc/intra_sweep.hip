@@ -55,7 +55,12 @@ template <typename T, int DQK, int NW> struct SweepLds {
     float bcol[64];                       // mLSTMsig: (li_s - a_s) log2(e) per key step of the K tile
 };
 
-template <typename T, int GATE, int DQK, int NW, typename S>
+// REV: the mirrored chunks of the backward pass's dv product (logical row
+// cs + r is physical step cs + len - 1 - r; the gate arrays are indexed by
+// the logical row, the key-side exponent stored pre-combined in li; the
+// chunk's own state is that of the chunks after it, slot kc, none for the
+// last chunk unless a final-state gradient sits there)
+template <typename T, int GATE, int DQK, int NW, typename S, bool REV>
 __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __restrict__ q, const T* __restrict__ k,
                                                                 const T* __restrict__ v,
                                                                 const float* __restrict__ a,
@@ -79,6 +84,9 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
     const size_t bh = blk / nc;
     const int kc = blk % nc, cs = kc * BQ;        // the query tile is the chunk
     const int nvt = dhv / BV;
+    const int clen = min(BQ, T_ - cs);            // steps in this chunk
+    // physical step of logical row t (t <= T-1)
+    auto row = [&](int t) { return REV ? 2 * cs + clen - 1 - t : t; };
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, lane = tid & 63, hh = lane >> 5, i32 = lane & 31;
@@ -99,8 +107,9 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
     if (GATE == kScalar) lg2 = fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor) * kLog2e;
 
     // states hold C before chunks 1..nc-1, preceded by C_0 when one is given
-    const bool inter = kc > 0 || c0;
-    const S* sb = inter ? states + (bh * (nc - 1 + c0) + (kc - 1 + c0)) * (size_t)dhv * DQK : states;
+    // (mirrored: the state of chunks kc+1.. in slot kc)
+    const bool inter = REV ? kc < nc - 1 + c0 : (kc > 0 || c0);
+    const S* sb = inter ? states + (bh * (nc - 1 + c0) + (REV ? kc : kc - 1 + c0)) * (size_t)dhv * DQK : states;
 
     // ---- stage loaders (global -> registers) and writers (registers -> LDS)
     Vec16<T> pk[NK], pv[NV];
@@ -110,12 +119,12 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
 #pragma unroll
         for (int u = 0; u < NK; ++u) {
             const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
-            pk[u].load(kb + (size_t)min(s0 + r, T_ - 1) * DQK + c);
+            pk[u].load(kb + (size_t)row(min(s0 + r, T_ - 1)) * DQK + c);
         }
         if (GATE == kSig && tid < 64) {
             const int s = min(s0 + tid, T_ - 1);
             pli = lb[s];
-            pa = ab[s];
+            if (!REV) pa = ab[s];
         }
     };
     auto store_k = [&]() {
@@ -124,7 +133,7 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
             const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
             pk[u].store(&sm.ks[r][c]);
         }
-        if (GATE == kSig && tid < 64) sm.bcol[tid] = (pli - pa) * kLog2e;
+        if (GATE == kSig && tid < 64) sm.bcol[tid] = (REV ? pli : pli - pa) * kLog2e;
     };
     auto fetch_c = [&](int v0, int cb) {
 #pragma unroll
@@ -155,7 +164,7 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int idx = tid + NTH * u, r = idx / (BV / VEC), c = (idx % (BV / VEC)) * VEC;
-            pv[u].load(vb + (size_t)min(s0 + r, T_ - 1) * dhv + v0 + c);
+            pv[u].load(vb + (size_t)row(min(s0 + r, T_ - 1)) * dhv + v0 + c);
         }
     };
     auto store_v = [&]() {
@@ -175,7 +184,7 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
     // S^T = K Q^T and the A operand of Q C^T
     Frag qf[KQ];
 #pragma unroll
-    for (int kq = 0; kq < KQ; ++kq) qf[kq] = load8(qb + (size_t)tqc * DQK + 16 * kq + 8 * hh);
+    for (int kq = 0; kq < KQ; ++kq) qf[kq] = load8(qb + (size_t)row(tqc) * DQK + 16 * kq + 8 * hh);
 
     bf16x8 (*const pw)[64] = &sm.p[wr * (wr + 1)];   // this wave's P blocks
 
@@ -250,7 +259,8 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int t = min(tlo + 8 * (r >> 2) + 4 * hh + (r & 3), T_ - 1);
-                const float e = (GATE == kSig) ? exp2_fast(ab[t] * kLog2e) : exp2_fast((float)(t - cs + 1) * lg2);
+                const float e = (GATE == kSig) ? exp2_fast(ab[t] * kLog2e)
+                                               : exp2_fast((float)(t - cs + (REV ? 0 : 1)) * lg2);
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= e;
             }
@@ -302,7 +312,7 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
                 if (t < T_) {
                     Vec16<T> x;
                     x.load(&os[rr][col]);
-                    x.store(hrow + (size_t)t * dhv + 64 * ph + col);
+                    x.store(hrow + (size_t)row(t) * dhv + 64 * ph + col);
                 }
             }
             // this block is read before it is overwritten (the next half, or
@@ -312,36 +322,36 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
     }
 }
 
-template <typename S, int GATE, int DQK, int NW>
+template <typename S, int GATE, int DQK, bool REV>
 hipError_t launch_sweep_t(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
-                          const Workspace& ws, void* h, hipStream_t stream)
+                          const Workspace& ws, void* h, float scale, hipStream_t stream)
 {
-    const float scale = 1.0f / sqrtf((float)p.dqk);
+    constexpr int NW = 8;
     const long blocks = (long)p.B * p.H * p.nc;
-    intra_kernel_sweep<bf16, GATE, DQK, NW, S><<<(unsigned)blocks, 64 * NW, 0, stream>>>(
+    intra_kernel_sweep<bf16, GATE, DQK, NW, S, REV><<<(unsigned)blocks, 64 * NW, 0, stream>>>(
         static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v), ws.a, ws.li, fg,
         static_cast<const S*>(ws.states), static_cast<bf16*>(h), p.H, p.T, p.dhv, p.nc, ws.c0 != nullptr, scale);
     return hipGetLastError();
 }
 
-template <typename S, int GATE, int NW>
+template <typename S, int GATE, bool REV>
 hipError_t sweep_dqk(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
-                     const Workspace& ws, void* h, hipStream_t stream)
+                     const Workspace& ws, void* h, float scale, hipStream_t stream)
 {
     switch (p.dqk) {
-    case 64: return launch_sweep_t<S, GATE, 64, NW>(p, q, k, v, fg, ws, h, stream);
-    case 128: return launch_sweep_t<S, GATE, 128, NW>(p, q, k, v, fg, ws, h, stream);
-    case 256: return launch_sweep_t<S, GATE, 256, NW>(p, q, k, v, fg, ws, h, stream);
+    case 64: return launch_sweep_t<S, GATE, 64, REV>(p, q, k, v, fg, ws, h, scale, stream);
+    case 128: return launch_sweep_t<S, GATE, 128, REV>(p, q, k, v, fg, ws, h, scale, stream);
+    case 256: return launch_sweep_t<S, GATE, 256, REV>(p, q, k, v, fg, ws, h, scale, stream);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <typename S>
+template <typename S, bool REV>
 hipError_t sweep_gate(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
-                      const Workspace& ws, void* h, hipStream_t stream)
+                      const Workspace& ws, void* h, float scale, hipStream_t stream)
 {
-    if (p.gate == kSig) return sweep_dqk<S, kSig, 8>(p, q, k, v, fg, ws, h, stream);
-    return sweep_dqk<S, kScalar, 8>(p, q, k, v, fg, ws, h, stream);
+    if (p.gate == kSig) return sweep_dqk<S, kSig, REV>(p, q, k, v, fg, ws, h, scale, stream);
+    return sweep_dqk<S, kScalar, REV>(p, q, k, v, fg, ws, h, scale, stream);
 }
 
 }  // namespace
@@ -364,8 +374,17 @@ hipError_t launch_intra_sweep(const Problem& p, const void* q, const void* k, co
                               const Workspace& ws, void* h, hipStream_t stream)
 {
     if (!intra_sweeps(p)) return hipErrorInvalidValue;
-    if (p.st32) return sweep_gate<float>(p, q, k, v, fgate_pre, ws, h, stream);
-    return sweep_gate<bf16>(p, q, k, v, fgate_pre, ws, h, stream);
+    const float scale = 1.0f / sqrtf((float)p.dqk);
+    if (p.st32) return sweep_gate<float, false>(p, q, k, v, fgate_pre, ws, h, scale, stream);
+    return sweep_gate<bf16, false>(p, q, k, v, fgate_pre, ws, h, scale, stream);
+}
+
+hipError_t launch_intra_sweep_dv(const Problem& p, const void* q, const void* k, const void* v,
+                                 const float* fgate_pre, const Workspace& ws, void* out, float scale,
+                                 hipStream_t stream)
+{
+    if (!intra_sweeps(p) || p.st32) return hipErrorInvalidValue;
+    return sweep_gate<bf16, true>(p, q, k, v, fgate_pre, ws, out, scale, stream);
 }
 
 }  // namespace tfla

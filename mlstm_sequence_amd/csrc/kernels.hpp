@@ -95,6 +95,10 @@ hipError_t launch_intra(const Problem& p, const void* q, const void* k, const vo
 bool intra_sweeps(const Problem& p);
 hipError_t launch_intra_sweep(const Problem& p, const void* q, const void* k, const void* v,
                               const float* fgate_pre, const Workspace& ws, void* h, hipStream_t stream);
+// The same kernel in the dv gradient mode (mirrored chunks; see launch_intra_dv).
+hipError_t launch_intra_sweep_dv(const Problem& p, const void* q, const void* k, const void* v,
+                                 const float* fgate_pre, const Workspace& ws, void* out, float scale,
+                                 hipStream_t stream);
 // The intra-chunk kernel in its gradient modes (dq: kNatState | kRowDots;
 // dk: kNatState | kMirror | kRowDots; dv: kMirror): p.dqk is the contracted width (64..512),
 // p.dhv the output width; ws.a / ws.li / ws.states as the mode reads them;

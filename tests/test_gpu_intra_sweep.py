@@ -98,3 +98,42 @@ def test_sweep_full_size_headline_workload():
         h_tile = gpu_forward(inp, wl.variant, 256)
     assert bool(torch.isfinite(h_sweep).all())
     assert torch.equal(h_sweep, h_tile)
+
+
+# ---- the dv product of the backward pass (mirrored chunks) -----------------
+from test_gpu_bwd import check as check_bwd, gpu_bwd, oracle_bwd          # noqa: E402
+from test_gpu_bwd_state import gpu_bwd_state, states                       # noqa: E402
+
+
+def same(a, b):
+    for x, y in zip(a, b):
+        assert (x is None) == (y is None)
+        if x is not None:
+            assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("variant,B,H,T,dqk,dhv", [
+    (SIG, 1, 2, 700, 256, 512), (SCAL, 2, 1, 600, 128, 256), (SIG, 1, 1, 200, 64, 256), (SIG, 1, 2, 512, 256, 256),
+])
+def test_dv_sweep_matches_per_tile_kernel_and_oracle(variant, B, H, T, dqk, dhv):
+    print(f"dv value sweep: variant {variant} B{B} H{H} T{T} {dqk}x{dhv} L256", flush=True)
+    wl, inp = case(variant, B, H, T, dqk, dhv, BF, seed=11 * T + dqk)
+    dh = W.upstream_grad(B, H, T, dhv, BF, seed=T + 7)
+    got = gpu_bwd(inp, dh, variant, 256, workspace=True)
+    with per_tile_kernel():
+        ref_tile = gpu_bwd(inp, dh, variant, 256, workspace=True)
+    same(got, ref_tile)
+    check_bwd(got, oracle_bwd(inp, dh, variant), BF, "sweep")
+
+
+@pytest.mark.parametrize("variant", [SIG, SCAL])
+def test_dv_sweep_with_initial_state_and_final_state_gradient(variant):
+    B, H, T, dqk, dhv = 1, 2, 600, 256, 256
+    print(f"dv value sweep with C_0 and dL/dC_T: variant {variant}", flush=True)
+    wl, inp = case(variant, B, H, T, dqk, dhv, BF, seed=123)
+    dh = W.upstream_grad(B, H, T, dhv, BF, seed=9)
+    c0, g = states(B, H, dqk, dhv, 77, True, True)
+    got = gpu_bwd_state(inp, dh, variant, 256, c0=c0, dcT=g)
+    with per_tile_kernel():
+        ref_tile = gpu_bwd_state(inp, dh, variant, 256, c0=c0, dcT=g)
+    same(got, ref_tile)
