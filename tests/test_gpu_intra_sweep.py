@@ -137,3 +137,24 @@ def test_dv_sweep_with_initial_state_and_final_state_gradient(variant):
     with per_tile_kernel():
         ref_tile = gpu_bwd_state(inp, dh, variant, 256, c0=c0, dcT=g)
     same(got, ref_tile)
+
+
+def test_sweep_more_than_2_31_elements():
+    """v and h hold 64 * 65536 * 512 = 2^31 elements; the last head sits past
+    every 32-bit offset (inputs drawn on the GPU by the seeded generators)."""
+    import numpy as np
+    B, H, T = 1, 64, 65536
+    wl = W.WORKLOADS[5].with_(B=B, H=H, T=T, dqk=256, dhv=512, seed=53)
+    print(f"value sweep, 2^31 elements: B{B} H{H} T{T} 256x512 L256", flush=True)
+    inp = W.make_inputs(wl, device="cuda")
+    assert inp["v"].numel() == 1 << 31
+    h = gpu_forward(inp, wl.variant, 256, workspace=True)
+    assert bool(torch.isfinite(h).all())
+    heads = [(0, H - 1)]
+    sl = {k: (None if t is None else t.cpu()) for k, t in W.head_slice(inp, wl.variant, heads).items()}
+    del inp
+    ref = oracle_forward(sl, wl.variant)
+    got = np.stack([h_f64(h[b, hh]) for b, hh in heads])
+    err = rel_err(got, ref)
+    print(f"rel err {err:.3e}", flush=True)
+    assert err <= TOL[BF]
