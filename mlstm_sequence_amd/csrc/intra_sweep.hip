@@ -82,7 +82,11 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
 
     const int blk = xcd_remap(blockIdx.x, gridDim.x);
     const size_t bh = blk / nc;
-    const int kc = blk % nc, cs = kc * BQ;        // the query tile is the chunk
+    // the query tile is the chunk; chunks are visited in the reverse of the
+    // order the state walk wrote their states (forward: the last chunk
+    // first), so the first workgroups find the states, K and V the walk
+    // touched last in the last-level cache
+    const int kc = REV ? blk % nc : nc - 1 - blk % nc, cs = kc * BQ;
     const int nvt = dhv / BV;
     const int clen = min(BQ, T_ - cs);            // steps in this chunk
     // physical step of logical row t (t <= T-1)
