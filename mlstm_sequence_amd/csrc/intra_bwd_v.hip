@@ -8,7 +8,7 @@ hipError_t launch_intra_dv(const Problem& p, const void* q, const void* k, const
                           const float* fgate_pre, const Workspace& ws, void* out, float scale,
                           hipStream_t stream)
 {
-    if (intra_sweeps(p)) return launch_intra_sweep_dv(p, q, k, v, fgate_pre, ws, out, scale, stream);
+    if (intra_sweeps_dv(p)) return launch_intra_sweep_dv(p, q, k, v, fgate_pre, ws, out, scale, stream);
     return dispatch_type<kMirror>(p, q, k, v, fgate_pre, ws, out, scale, stream);
 }
 

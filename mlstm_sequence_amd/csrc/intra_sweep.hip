@@ -1,6 +1,6 @@
 // intra_sweep.hip -- the forward pass's intra-chunk kernel for value widths
-// of two or more 128-column tiles (per-step gates, bf16 I/O, chunks of 256
-// steps).
+// of two or more 128-column tiles (bf16 I/O, chunks of 64 or 256 steps), and
+// the same computation over mirrored chunks for the dv product.
 //
 // Per chunk it evaluates the same sum as the per-tile kernel (intra_impl.hpp)
 //   h_t = scale * ( e^{a_t} q_t^T C_{k-1} + sum_{cs <= s <= t} P_ts v_s ),
@@ -23,8 +23,12 @@
 // C^T block, V tile) is software-pipelined across the phase boundaries: its
 // global loads are issued into registers while the previous stage computes.
 //
-// Workgroup = NW = 8 waves, each owning 32 query rows; the two waves of a
-// SIMD take row blocks s and 7 - s, which evens out the causal work.
+// Workgroup = NW waves (8 for 256-step chunks, 2 for 64), each owning 32
+// query rows; with 8 waves the two waves of a SIMD take row blocks s and
+// 7 - s, which evens out the causal work.  The per-channel gate uses the
+// per-tile kernel's reference-point factorisation: for each key tile, q is
+// scaled by e^{a_t - a_ref} and k by e^{a_ref - a_s} with a_ref at the
+// tile's middle step, and the inter-chunk term takes q o e^{a_t}.
 #include <cstdlib>
 #include <type_traits>
 
@@ -61,7 +65,7 @@ template <typename T, int DQK, int NW> struct SweepLds {
 // chunk's own state is that of the chunks after it, slot kc, none for the
 // last chunk unless a final-state gradient sits there)
 template <typename T, int GATE, int DQK, int NW, typename S, bool REV>
-__global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __restrict__ q, const T* __restrict__ k,
+__global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(const T* __restrict__ q, const T* __restrict__ k,
                                                                 const T* __restrict__ v,
                                                                 const float* __restrict__ a,
                                                                 const float* __restrict__ li,
@@ -69,7 +73,7 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
                                                                 const S* __restrict__ states, T* __restrict__ h,
                                                                 int H, int T_, int dhv, int nc, int c0, float scale)
 {
-    static_assert(GATE != kGla, "per-step gates only");
+    static_assert(GATE != kGla || !REV, "per-channel gate: forward pass only");
     constexpr int NTH = 64 * NW, BQ = 32 * NW, BV = kSweepBV, NT = BV / 32, KQ = DQK / 16;
     constexpr int CW = sweep_cw<DQK>(), NKV = BQ / 64;
     constexpr int VEC = Elem<T>::vec, SVEC = Elem<S>::vec;
@@ -105,7 +109,7 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
     const T* qb = q + bh * (size_t)T_ * DQK;
     const T* kb = k + bh * (size_t)T_ * DQK;
     const T* vb = v + bh * (size_t)T_ * dhv;
-    const float* ab = (GATE == kSig) ? a + bh * (size_t)T_ : nullptr;
+    const float* ab = (GATE == kSig) ? a + bh * (size_t)T_ : (GATE == kGla) ? a + bh * (size_t)T_ * DQK : nullptr;
     const float* lb = (GATE == kSig) ? li + bh * (size_t)T_ : nullptr;
     float lg2 = 0.0f;   // log2 of the fixed decay
     if (GATE == kScalar) lg2 = fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor) * kLog2e;
@@ -131,10 +135,23 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
             if (!REV) pa = ab[s];
         }
     };
-    auto store_k = [&]() {
+    // per-channel gate: k scaled by e^{a_ref - a_s} in fp32 (factor <= 1 for
+    // keys before the reference row) before its one rounding into LDS
+    auto store_k = [&](int s0, int ref_row) {
 #pragma unroll
         for (int u = 0; u < NK; ++u) {
             const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
+            if constexpr (GATE == kGla) {
+                const int s = min(s0 + r, T_ - 1);
+#pragma unroll
+                for (int e4 = 0; e4 < VEC / 4; ++e4) {
+                    const f32x4 er = *reinterpret_cast<const f32x4*>(ab + (size_t)ref_row * DQK + c + 4 * e4);
+                    const f32x4 es = *reinterpret_cast<const f32x4*>(ab + (size_t)s * DQK + c + 4 * e4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        pk[u].set(4 * e4 + e, pk[u].get(4 * e4 + e) * exp2_fast((er[e] - es[e]) * kLog2e));
+                }
+            }
             pk[u].store(&sm.ks[r][c]);
         }
         if (GATE == kSig && tid < 64) sm.bcol[tid] = (REV ? pli : pli - pa) * kLog2e;
@@ -185,10 +202,31 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
     };
 
     // Q fragments (lane row tqc, channels 16 kq + 8 hh ..): the B operand of
-    // S^T = K Q^T and the A operand of Q C^T
+    // S^T = K Q^T and the A operand of Q C^T.  Per-channel gate: q scaled by
+    // e^{a_t - a_ref} in fp32 (ref_row < 0: the chunk start, where a = 0) --
+    // the reference-point factorisation of the per-tile kernel
     Frag qf[KQ];
+    auto load_q = [&](int ref_row) {
 #pragma unroll
-    for (int kq = 0; kq < KQ; ++kq) qf[kq] = load8(qb + (size_t)row(tqc) * DQK + 16 * kq + 8 * hh);
+        for (int kq = 0; kq < KQ; ++kq) {
+            const int c = 16 * kq + 8 * hh;
+            if constexpr (GATE != kGla) {
+                qf[kq] = load8(qb + (size_t)row(tqc) * DQK + c);
+            } else {
+                const Frag raw = load8(qb + (size_t)tqc * DQK + c);
+                f32x4 ex[2];
+                ex[0] = *reinterpret_cast<const f32x4*>(ab + (size_t)tqc * DQK + c);
+                ex[1] = *reinterpret_cast<const f32x4*>(ab + (size_t)tqc * DQK + c + 4);
+                if (ref_row >= 0) {
+                    ex[0] -= *reinterpret_cast<const f32x4*>(ab + (size_t)ref_row * DQK + c);
+                    ex[1] -= *reinterpret_cast<const f32x4*>(ab + (size_t)ref_row * DQK + c + 4);
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) frag_set(qf[kq], e, frag_get(raw, e) * exp2_fast(ex[e >> 2][e & 3] * kLog2e));
+            }
+        }
+    };
+    if (GATE != kGla) load_q(-1);
 
     bf16x8 (*const pw)[64] = &sm.p[wr * (wr + 1)];   // this wave's P blocks
 
@@ -197,8 +235,13 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
     fetch_k(cs);
     for (int j = 0; j < NKV; ++j) {
         const int s0 = cs + 64 * j;
+        // per-channel gate: every key tile overlaps the query tile (the
+        // chunk), so its reference row is its middle step, and the Q
+        // fragments are rescaled to it
+        const int ref_row = (GATE == kGla) ? min(s0 + 31, T_ - 1) : -1;
+        if (GATE == kGla) load_q(ref_row);
         __syncthreads();
-        store_k();
+        store_k(s0, ref_row);
         __syncthreads();
         if (j + 1 < NKV) fetch_k(s0 + 64);
         else fetch_first(0);
@@ -221,7 +264,7 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
                 const int sr = 8 * (r >> 2) + 4 * hh + (r & 3);
                 float p = st[r];
                 if (GATE == kSig) p *= exp2_fast(at2 + sm.bcol[32 * mt + sr]);
-                else p *= exp2_fast((float)(tlo + i32 - slo - sr) * lg2);
+                else if (GATE == kScalar) p *= exp2_fast((float)(tlo + i32 - slo - sr) * lg2);
                 st[r] = (diag && sr > i32) ? 0.0f : p;
             }
             // the accumulator, in its own order, is the A operand of P V
@@ -234,6 +277,9 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
             }
         }
     }
+
+    // per-channel gate: the inter-chunk term takes q o e^{a_t}
+    if (GATE == kGla && inter) load_q(-1);
 
     // ---------------- 2. every value tile
     T* const hbase = h + bh * (size_t)T_ * dhv;
@@ -260,13 +306,15 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
                     }
                 }
             }
+            if (GATE != kGla) {   // per-channel gate: e^{a_t} already inside q
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int t = min(tlo + 8 * (r >> 2) + 4 * hh + (r & 3), T_ - 1);
-                const float e = (GATE == kSig) ? exp2_fast(ab[t] * kLog2e)
-                                               : exp2_fast((float)(t - cs + (REV ? 0 : 1)) * lg2);
+                for (int r = 0; r < 16; ++r) {
+                    const int t = min(tlo + 8 * (r >> 2) + 4 * hh + (r & 3), T_ - 1);
+                    const float e = (GATE == kSig) ? exp2_fast(ab[t] * kLog2e)
+                                                   : exp2_fast((float)(t - cs + (REV ? 0 : 1)) * lg2);
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= e;
+                    for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= e;
+                }
             }
         }
         // + P V, key tile by key tile
@@ -326,11 +374,10 @@ __global__ __launch_bounds__(64 * NW, 2) void intra_kernel_sweep(const T* __rest
     }
 }
 
-template <typename S, int GATE, int DQK, bool REV>
+template <typename S, int GATE, int DQK, int NW, bool REV>
 hipError_t launch_sweep_t(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
                           const Workspace& ws, void* h, float scale, hipStream_t stream)
 {
-    constexpr int NW = 8;
     const long blocks = (long)p.B * p.H * p.nc;
     intra_kernel_sweep<bf16, GATE, DQK, NW, S, REV><<<(unsigned)blocks, 64 * NW, 0, stream>>>(
         static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v), ws.a, ws.li, fg,
@@ -338,14 +385,26 @@ hipError_t launch_sweep_t(const Problem& p, const void* q, const void* k, const 
     return hipGetLastError();
 }
 
+// one wave per 32 steps of the chunk: 8 waves at L = 256, 2 at L = 64
+template <typename S, int GATE, int DQK, bool REV>
+hipError_t sweep_nw(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
+                    const Workspace& ws, void* h, float scale, hipStream_t stream)
+{
+    if (p.L == 64) return launch_sweep_t<S, GATE, DQK, 2, REV>(p, q, k, v, fg, ws, h, scale, stream);
+    // (the per-channel gate's per-tile Q rescaling does not fit 8 waves at d_qk = 256)
+    if constexpr (GATE != kGla || DQK <= 128)
+        return launch_sweep_t<S, GATE, DQK, 8, REV>(p, q, k, v, fg, ws, h, scale, stream);
+    return hipErrorInvalidValue;
+}
+
 template <typename S, int GATE, bool REV>
 hipError_t sweep_dqk(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
                      const Workspace& ws, void* h, float scale, hipStream_t stream)
 {
     switch (p.dqk) {
-    case 64: return launch_sweep_t<S, GATE, 64, REV>(p, q, k, v, fg, ws, h, scale, stream);
-    case 128: return launch_sweep_t<S, GATE, 128, REV>(p, q, k, v, fg, ws, h, scale, stream);
-    case 256: return launch_sweep_t<S, GATE, 256, REV>(p, q, k, v, fg, ws, h, scale, stream);
+    case 64: return sweep_nw<S, GATE, 64, REV>(p, q, k, v, fg, ws, h, scale, stream);
+    case 128: return sweep_nw<S, GATE, 128, REV>(p, q, k, v, fg, ws, h, scale, stream);
+    case 256: return sweep_nw<S, GATE, 256, REV>(p, q, k, v, fg, ws, h, scale, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -355,24 +414,31 @@ hipError_t sweep_gate(const Problem& p, const void* q, const void* k, const void
                       const Workspace& ws, void* h, float scale, hipStream_t stream)
 {
     if (p.gate == kSig) return sweep_dqk<S, kSig, REV>(p, q, k, v, fg, ws, h, scale, stream);
-    return sweep_dqk<S, kScalar, REV>(p, q, k, v, fg, ws, h, scale, stream);
+    if (p.gate == kScalar) return sweep_dqk<S, kScalar, REV>(p, q, k, v, fg, ws, h, scale, stream);
+    if constexpr (!REV) return sweep_dqk<S, kGla, false>(p, q, k, v, fg, ws, h, scale, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// Applies to bf16 I/O, per-step gates, chunks of 256 steps, a contraction
-// of 64..256 channels and two or more 128-wide value tiles.  (Four-wave
-// workgroups for 128-step chunks would hold twice the K prefetch per
-// thread, which spills at a 256-wide contraction.)
+// Applies to bf16 I/O, chunks of 64 or 256 steps (one wave per 32 steps),
+// a contraction of 64..256 channels and two or more 128-wide value tiles;
+// every gate in the forward pass (the per-channel gate at L = 256 only up to
+// d_qk = 128: its Q fragments, rescaled per key tile, spill at 8 waves and
+// d_qk = 256), the per-step gates in the dv product.
+// (Four-wave workgroups for 128-step chunks would hold twice the K prefetch
+// per thread of eight waves, which spills at a 256-wide contraction.)
 // TFLA_INTRA_SWEEP=0 turns it off (the per-tile kernel then runs; tuning
 // comparisons).
 bool intra_sweeps(const Problem& p)
 {
     if (const char* e = std::getenv("TFLA_INTRA_SWEEP"))
         if (std::atoi(e) == 0) return false;
-    return p.bf16 && p.gate != kGla && p.L == 256 &&
-           (p.dqk == 64 || p.dqk == 128 || p.dqk == 256) && p.dhv % kSweepBV == 0 && p.dhv / kSweepBV >= 2;
+    return p.bf16 && (p.L == 64 || p.L == 256) && (p.dqk == 64 || p.dqk == 128 || p.dqk == 256) &&
+           p.dhv % kSweepBV == 0 && p.dhv / kSweepBV >= 2 && !(p.gate == kGla && p.L == 256 && p.dqk == 256);
 }
+
+bool intra_sweeps_dv(const Problem& p) { return p.gate != kGla && intra_sweeps(p); }
 
 hipError_t launch_intra_sweep(const Problem& p, const void* q, const void* k, const void* v, const float* fgate_pre,
                               const Workspace& ws, void* h, hipStream_t stream)
@@ -387,7 +453,7 @@ hipError_t launch_intra_sweep_dv(const Problem& p, const void* q, const void* k,
                                  const float* fgate_pre, const Workspace& ws, void* out, float scale,
                                  hipStream_t stream)
 {
-    if (!intra_sweeps(p) || p.st32) return hipErrorInvalidValue;
+    if (!intra_sweeps_dv(p) || p.st32) return hipErrorInvalidValue;
     return sweep_gate<bf16, true>(p, q, k, v, fgate_pre, ws, out, scale, stream);
 }
 

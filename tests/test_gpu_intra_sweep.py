@@ -1,9 +1,10 @@
-"""The value-sweeping intra-chunk kernel of the forward pass (bf16 I/O,
-per-step gates, 256-step chunks, two or more 128-wide value tiles: one
-workgroup per chunk forms P once and sweeps every value tile) against the
-per-tile kernel it replaces there (TFLA_INTRA_SWEEP=0 selects that one).
-Both take the same products in the same order with the same roundings, so h
-must agree to the bit; both must match the oracle."""
+"""The value-sweeping intra-chunk kernel (bf16 I/O, 64- or 256-step chunks,
+two or more 128-wide value tiles: one workgroup per chunk forms P once and
+sweeps every value tile) against the per-tile kernel it replaces there
+(TFLA_INTRA_SWEEP=0 selects that one), in the forward pass (every gate) and
+in the backward pass's dv product (per-step gates).  Both take the same
+products in the same order with the same roundings, so h (and every
+gradient) must agree to the bit; both must match the oracle."""
 import os
 from contextlib import contextmanager
 
@@ -16,7 +17,7 @@ from mlstm_sequence_amd import tfla
 
 pytestmark = pytest.mark.gpu
 
-SIG, SCAL = W.MLSTM_SIG, W.SCALAR
+SIG, SCAL, GLA = W.MLSTM_SIG, W.SCALAR, W.GLA
 BF = torch.bfloat16
 
 
@@ -41,33 +42,42 @@ def per_tile_kernel():
 
 
 CASES = [
-    # variant, B, H, T, dqk, dhv
-    (SIG, 1, 2, 700, 256, 512),    # ragged last chunk
-    (SIG, 2, 1, 512, 256, 256),    # two full chunks
-    (SIG, 1, 2, 200, 256, 512),    # one partial chunk: no inter-chunk term
-    (SIG, 1, 1, 1, 256, 256),      # a single step
-    (SIG, 1, 2, 257, 128, 384),    # one step into the second chunk; three value tiles
-    (SIG, 1, 2, 900, 64, 256),
-    (SCAL, 2, 2, 600, 128, 256),
-    (SCAL, 1, 2, 1000, 256, 512),
+    # variant, B, H, T, dqk, dhv, L
+    (SIG, 1, 2, 700, 256, 512, 256),    # ragged last chunk
+    (SIG, 2, 1, 512, 256, 256, 256),    # two full chunks
+    (SIG, 1, 2, 200, 256, 512, 256),    # one partial chunk: no inter-chunk term
+    (SIG, 1, 1, 1, 256, 256, 256),      # a single step
+    (SIG, 1, 2, 257, 128, 384, 256),    # one step into the second chunk; three value tiles
+    (SIG, 1, 2, 900, 64, 256, 256),
+    (SCAL, 2, 2, 600, 128, 256, 256),
+    (SCAL, 1, 2, 1000, 256, 512, 256),
+    (SIG, 1, 2, 300, 256, 512, 64),     # two-wave workgroups
+    (SIG, 1, 1, 65, 128, 256, 64),
+    (SCAL, 2, 1, 200, 256, 256, 64),
+    (GLA, 1, 2, 300, 256, 512, 64),     # per-channel gate, the shape of its workload
+    (GLA, 1, 1, 1, 256, 256, 64),
+    (GLA, 2, 1, 130, 64, 384, 64),
+    (GLA, 1, 2, 600, 128, 256, 256),    # per-channel gate at 8 waves (d_qk <= 128)
+    (GLA, 1, 1, 300, 64, 512, 256),
 ]
 
 
-@pytest.mark.parametrize("variant,B,H,T,dqk,dhv", CASES)
-def test_sweep_matches_per_tile_kernel_and_oracle(variant, B, H, T, dqk, dhv):
-    print(f"value sweep: variant {variant} B{B} H{H} T{T} {dqk}x{dhv} L256", flush=True)
+@pytest.mark.parametrize("variant,B,H,T,dqk,dhv,L", CASES)
+def test_sweep_matches_per_tile_kernel_and_oracle(variant, B, H, T, dqk, dhv, L):
+    print(f"value sweep: variant {variant} B{B} H{H} T{T} {dqk}x{dhv} L{L}", flush=True)
     wl, inp = case(variant, B, H, T, dqk, dhv, BF, seed=7 * T + dqk + dhv)
-    h_sweep = gpu_forward(inp, variant, 256)
+    h_sweep = gpu_forward(inp, variant, L)
     with per_tile_kernel():
-        h_tile = gpu_forward(inp, variant, 256)
+        h_tile = gpu_forward(inp, variant, L)
     assert torch.equal(h_sweep, h_tile)
     assert rel_err(h_f64(h_sweep), oracle_forward(inp, variant)) <= TOL[BF]
 
 
-@pytest.mark.parametrize("variant,flags", [(SIG, 0), (SCAL, 0), (SIG, tfla.STATES_FP32)])
-def test_sweep_with_initial_state(variant, flags):
-    B, H, T, dqk, dhv, L = 1, 2, 600, 256, 256, 256
-    print(f"value sweep with C_0: variant {variant} flags {flags:#x}", flush=True)
+@pytest.mark.parametrize("variant,flags,L", [(SIG, 0, 256), (SCAL, 0, 256), (SIG, tfla.STATES_FP32, 256),
+                                             (SIG, 0, 64), (GLA, 0, 64), (GLA, tfla.STATES_FP32, 64)])
+def test_sweep_with_initial_state(variant, flags, L):
+    B, H, T, dqk, dhv = 1, 2, 600, 256, 256
+    print(f"value sweep with C_0: variant {variant} flags {flags:#x} L{L}", flush=True)
     wl, inp = case(variant, B, H, T, dqk, dhv, BF, seed=91)
     d = to_dev(inp)
     c0 = W.initial_state(B, H, dqk, dhv, seed=3, std=1.5).cuda()
@@ -89,13 +99,17 @@ def test_sweep_with_initial_state(variant, flags):
     assert bool(torch.isfinite(outs[0]).all())
 
 
-def test_sweep_full_size_headline_workload():
-    """mLSTMsig B=4 H=8 T=8192 d_qk=256 d_hv=512 at L = 256: the launch the bench times."""
-    wl = W.WORKLOADS[3]
+@pytest.mark.parametrize("cfg,L", [(3, 256), (3, 64), (4, 64)])
+def test_sweep_full_size(cfg, L):
+    """Workload 3 (mLSTMsig B=4 H=8 T=8192 d_qk=256 d_hv=512; L = 256 is the
+    launch the bench times) and workload 4 (per-channel gate B=8 H=4 T=2048
+    d_qk=256 d_hv=512, L = 64) at full size."""
+    wl = W.WORKLOADS[cfg]
+    print(f"value sweep full size: {wl.name} L{L}", flush=True)
     inp = W.make_inputs(wl, device="cuda")
-    h_sweep = gpu_forward(inp, wl.variant, 256)
+    h_sweep = gpu_forward(inp, wl.variant, L)
     with per_tile_kernel():
-        h_tile = gpu_forward(inp, wl.variant, 256)
+        h_tile = gpu_forward(inp, wl.variant, L)
     assert bool(torch.isfinite(h_sweep).all())
     assert torch.equal(h_sweep, h_tile)
 
@@ -112,16 +126,18 @@ def same(a, b):
             assert torch.equal(x, y)
 
 
-@pytest.mark.parametrize("variant,B,H,T,dqk,dhv", [
-    (SIG, 1, 2, 700, 256, 512), (SCAL, 2, 1, 600, 128, 256), (SIG, 1, 1, 200, 64, 256), (SIG, 1, 2, 512, 256, 256),
+@pytest.mark.parametrize("variant,B,H,T,dqk,dhv,L", [
+    (SIG, 1, 2, 700, 256, 512, 256), (SCAL, 2, 1, 600, 128, 256, 256), (SIG, 1, 1, 200, 64, 256, 256),
+    (SIG, 1, 2, 512, 256, 256, 256), (SIG, 1, 2, 300, 256, 512, 64), (SCAL, 1, 2, 150, 128, 256, 64),
+    (GLA, 1, 2, 300, 256, 512, 64),     # the per-channel gate keeps the per-tile dv kernel
 ])
-def test_dv_sweep_matches_per_tile_kernel_and_oracle(variant, B, H, T, dqk, dhv):
-    print(f"dv value sweep: variant {variant} B{B} H{H} T{T} {dqk}x{dhv} L256", flush=True)
+def test_dv_sweep_matches_per_tile_kernel_and_oracle(variant, B, H, T, dqk, dhv, L):
+    print(f"dv value sweep: variant {variant} B{B} H{H} T{T} {dqk}x{dhv} L{L}", flush=True)
     wl, inp = case(variant, B, H, T, dqk, dhv, BF, seed=11 * T + dqk)
     dh = W.upstream_grad(B, H, T, dhv, BF, seed=T + 7)
-    got = gpu_bwd(inp, dh, variant, 256, workspace=True)
+    got = gpu_bwd(inp, dh, variant, L, workspace=True)
     with per_tile_kernel():
-        ref_tile = gpu_bwd(inp, dh, variant, 256, workspace=True)
+        ref_tile = gpu_bwd(inp, dh, variant, L, workspace=True)
     same(got, ref_tile)
     check_bwd(got, oracle_bwd(inp, dh, variant), BF, "sweep")
 
