@@ -73,7 +73,6 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
                                                                 const S* __restrict__ states, T* __restrict__ h,
                                                                 int H, int T_, int dhv, int nc, int c0, float scale)
 {
-    static_assert(GATE != kGla || !REV, "per-channel gate: forward pass only");
     constexpr int NTH = 64 * NW, BQ = 32 * NW, BV = kSweepBV, NT = BV / 32, KQ = DQK / 16;
     constexpr int CW = sweep_cw<DQK>(), NKV = BQ / 64;
     constexpr int VEC = Elem<T>::vec, SVEC = Elem<S>::vec;
@@ -213,7 +212,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
             if constexpr (GATE != kGla) {
                 qf[kq] = load8(qb + (size_t)row(tqc) * DQK + c);
             } else {
-                const Frag raw = load8(qb + (size_t)tqc * DQK + c);
+                const Frag raw = load8(qb + (size_t)row(tqc) * DQK + c);
                 f32x4 ex[2];
                 ex[0] = *reinterpret_cast<const f32x4*>(ab + (size_t)tqc * DQK + c);
                 ex[1] = *reinterpret_cast<const f32x4*>(ab + (size_t)tqc * DQK + c + 4);
@@ -415,17 +414,16 @@ hipError_t sweep_gate(const Problem& p, const void* q, const void* k, const void
 {
     if (p.gate == kSig) return sweep_dqk<S, kSig, REV>(p, q, k, v, fg, ws, h, scale, stream);
     if (p.gate == kScalar) return sweep_dqk<S, kScalar, REV>(p, q, k, v, fg, ws, h, scale, stream);
-    if constexpr (!REV) return sweep_dqk<S, kGla, false>(p, q, k, v, fg, ws, h, scale, stream);
-    return hipErrorInvalidValue;
+    return sweep_dqk<S, kGla, REV>(p, q, k, v, fg, ws, h, scale, stream);
 }
 
 }  // namespace
 
 // Applies to bf16 I/O, chunks of 64 or 256 steps (one wave per 32 steps),
 // a contraction of 64..256 channels and two or more 128-wide value tiles;
-// every gate in the forward pass (the per-channel gate at L = 256 only up to
-// d_qk = 128: its Q fragments, rescaled per key tile, spill at 8 waves and
-// d_qk = 256), the per-step gates in the dv product.
+// every gate (the per-channel gate at L = 256 only up to d_qk = 128: its Q
+// fragments, rescaled per key tile, spill at 8 waves and d_qk = 256), in the
+// forward pass and in the dv product.
 // (Four-wave workgroups for 128-step chunks would hold twice the K prefetch
 // per thread of eight waves, which spills at a 256-wide contraction.)
 // TFLA_INTRA_SWEEP=0 turns it off (the per-tile kernel then runs; tuning
@@ -438,7 +436,7 @@ bool intra_sweeps(const Problem& p)
            p.dhv % kSweepBV == 0 && p.dhv / kSweepBV >= 2 && !(p.gate == kGla && p.L == 256 && p.dqk == 256);
 }
 
-bool intra_sweeps_dv(const Problem& p) { return p.gate != kGla && intra_sweeps(p); }
+bool intra_sweeps_dv(const Problem& p) { return intra_sweeps(p); }
 
 hipError_t launch_intra_sweep(const Problem& p, const void* q, const void* k, const void* v, const float* fgate_pre,
                               const Workspace& ws, void* h, hipStream_t stream)

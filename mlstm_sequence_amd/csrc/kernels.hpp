@@ -93,7 +93,7 @@ hipError_t launch_intra(const Problem& p, const void* q, const void* k, const vo
 // The forward intra-chunk kernel that forms a chunk's P once and sweeps
 // every value tile with it (launch_intra picks it where intra_sweeps holds).
 bool intra_sweeps(const Problem& p);
-bool intra_sweeps_dv(const Problem& p);   // the same for the dv product (per-step gates)
+bool intra_sweeps_dv(const Problem& p);   // the same for the dv product
 hipError_t launch_intra_sweep(const Problem& p, const void* q, const void* k, const void* v,
                               const float* fgate_pre, const Workspace& ws, void* h, hipStream_t stream);
 // The same kernel in the dv gradient mode (mirrored chunks; see launch_intra_dv).

@@ -2,7 +2,7 @@
 two or more 128-wide value tiles: one workgroup per chunk forms P once and
 sweeps every value tile) against the per-tile kernel it replaces there
 (TFLA_INTRA_SWEEP=0 selects that one), in the forward pass (every gate) and
-in the backward pass's dv product (per-step gates).  Both take the same
+in the backward pass's dv product.  Both take the same
 products in the same order with the same roundings, so h (and every
 gradient) must agree to the bit; both must match the oracle."""
 import os
@@ -129,7 +129,8 @@ def same(a, b):
 @pytest.mark.parametrize("variant,B,H,T,dqk,dhv,L", [
     (SIG, 1, 2, 700, 256, 512, 256), (SCAL, 2, 1, 600, 128, 256, 256), (SIG, 1, 1, 200, 64, 256, 256),
     (SIG, 1, 2, 512, 256, 256, 256), (SIG, 1, 2, 300, 256, 512, 64), (SCAL, 1, 2, 150, 128, 256, 64),
-    (GLA, 1, 2, 300, 256, 512, 64),     # the per-channel gate keeps the per-tile dv kernel
+    (GLA, 1, 2, 300, 256, 512, 64),     # per-channel gate (mirrored reference rows)
+    (GLA, 2, 1, 333, 128, 256, 64), (GLA, 1, 2, 600, 128, 256, 256),
 ])
 def test_dv_sweep_matches_per_tile_kernel_and_oracle(variant, B, H, T, dqk, dhv, L):
     print(f"dv value sweep: variant {variant} B{B} H{H} T{T} {dqk}x{dhv} L{L}", flush=True)
@@ -142,16 +143,16 @@ def test_dv_sweep_matches_per_tile_kernel_and_oracle(variant, B, H, T, dqk, dhv,
     check_bwd(got, oracle_bwd(inp, dh, variant), BF, "sweep")
 
 
-@pytest.mark.parametrize("variant", [SIG, SCAL])
-def test_dv_sweep_with_initial_state_and_final_state_gradient(variant):
+@pytest.mark.parametrize("variant,L", [(SIG, 256), (SCAL, 256), (SIG, 64), (GLA, 64)])
+def test_dv_sweep_with_initial_state_and_final_state_gradient(variant, L):
     B, H, T, dqk, dhv = 1, 2, 600, 256, 256
-    print(f"dv value sweep with C_0 and dL/dC_T: variant {variant}", flush=True)
+    print(f"dv value sweep with C_0 and dL/dC_T: variant {variant} L{L}", flush=True)
     wl, inp = case(variant, B, H, T, dqk, dhv, BF, seed=123)
     dh = W.upstream_grad(B, H, T, dhv, BF, seed=9)
     c0, g = states(B, H, dqk, dhv, 77, True, True)
-    got = gpu_bwd_state(inp, dh, variant, 256, c0=c0, dcT=g)
+    got = gpu_bwd_state(inp, dh, variant, L, c0=c0, dcT=g)
     with per_tile_kernel():
-        ref_tile = gpu_bwd_state(inp, dh, variant, 256, c0=c0, dcT=g)
+        ref_tile = gpu_bwd_state(inp, dh, variant, L, c0=c0, dcT=g)
     same(got, ref_tile)
 
 
