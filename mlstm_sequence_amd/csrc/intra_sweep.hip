@@ -1,5 +1,5 @@
 // intra_sweep.hip -- the forward pass's intra-chunk kernel for value widths
-// of two or more 128-column tiles (bf16 I/O, chunks of 64 or 256 steps), and
+// of two or more 128-column tiles (bf16 I/O, chunks of 64, 128 or 256 steps), and
 // the same computation over mirrored chunks for the dv product.
 //
 // Per chunk it evaluates the same sum as the per-tile kernel (intra_impl.hpp)
@@ -23,7 +23,7 @@
 // C^T block, V tile) is software-pipelined across the phase boundaries: its
 // global loads are issued into registers while the previous stage computes.
 //
-// Workgroup = NW waves (8 for 256-step chunks, 2 for 64), each owning 32
+// Workgroup = NW waves (8, 4 or 2 for 256-, 128- or 64-step chunks), each owning 32
 // query rows; with 8 waves the two waves of a SIMD take row blocks s and
 // 7 - s, which evens out the causal work.  The per-channel gate uses the
 // per-tile kernel's reference-point factorisation: for each key tile, q is
@@ -384,15 +384,19 @@ hipError_t launch_sweep_t(const Problem& p, const void* q, const void* k, const 
     return hipGetLastError();
 }
 
-// one wave per 32 steps of the chunk: 8 waves at L = 256, 2 at L = 64
+// one wave per 32 steps of the chunk: 8 waves at L = 256, 4 at 128, 2 at 64
+// (fewer than 8 at one wave per SIMD: their larger per-thread prefetch needs
+// the registers)
 template <typename S, int GATE, int DQK, bool REV>
 hipError_t sweep_nw(const Problem& p, const void* q, const void* k, const void* v, const float* fg,
                     const Workspace& ws, void* h, float scale, hipStream_t stream)
 {
     if (p.L == 64) return launch_sweep_t<S, GATE, DQK, 2, REV>(p, q, k, v, fg, ws, h, scale, stream);
-    // (the per-channel gate's per-tile Q rescaling does not fit 8 waves at d_qk = 256)
-    if constexpr (GATE != kGla || DQK <= 128)
+    // (the per-channel gate's per-tile Q rescaling does not fit 4 or 8 waves at d_qk = 256)
+    if constexpr (GATE != kGla || DQK <= 128) {
+        if (p.L == 128) return launch_sweep_t<S, GATE, DQK, 4, REV>(p, q, k, v, fg, ws, h, scale, stream);
         return launch_sweep_t<S, GATE, DQK, 8, REV>(p, q, k, v, fg, ws, h, scale, stream);
+    }
     return hipErrorInvalidValue;
 }
 
@@ -419,21 +423,19 @@ hipError_t sweep_gate(const Problem& p, const void* q, const void* k, const void
 
 }  // namespace
 
-// Applies to bf16 I/O, chunks of 64 or 256 steps (one wave per 32 steps),
-// a contraction of 64..256 channels and two or more 128-wide value tiles;
-// every gate (the per-channel gate at L = 256 only up to d_qk = 128: its Q
-// fragments, rescaled per key tile, spill at 8 waves and d_qk = 256), in the
-// forward pass and in the dv product.
-// (Four-wave workgroups for 128-step chunks would hold twice the K prefetch
-// per thread of eight waves, which spills at a 256-wide contraction.)
+// Applies to bf16 I/O, chunks of 64, 128 or 256 steps (one wave per 32
+// steps), a contraction of 64..256 channels and two or more 128-wide value
+// tiles; every gate (the per-channel gate at L >= 128 only up to d_qk = 128:
+// its Q fragments, rescaled per key tile, spill at 4 or 8 waves and d_qk =
+// 256), in the forward pass and in the dv product.
 // TFLA_INTRA_SWEEP=0 turns it off (the per-tile kernel then runs; tuning
 // comparisons).
 bool intra_sweeps(const Problem& p)
 {
     if (const char* e = std::getenv("TFLA_INTRA_SWEEP"))
         if (std::atoi(e) == 0) return false;
-    return p.bf16 && (p.L == 64 || p.L == 256) && (p.dqk == 64 || p.dqk == 128 || p.dqk == 256) &&
-           p.dhv % kSweepBV == 0 && p.dhv / kSweepBV >= 2 && !(p.gate == kGla && p.L == 256 && p.dqk == 256);
+    return p.bf16 && (p.L == 64 || p.L == 128 || p.L == 256) && (p.dqk == 64 || p.dqk == 128 || p.dqk == 256) &&
+           p.dhv % kSweepBV == 0 && p.dhv / kSweepBV >= 2 && !(p.gate == kGla && p.L >= 128 && p.dqk == 256);
 }
 
 bool intra_sweeps_dv(const Problem& p) { return intra_sweeps(p); }

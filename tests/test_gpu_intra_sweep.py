@@ -1,4 +1,4 @@
-"""The value-sweeping intra-chunk kernel (bf16 I/O, 64- or 256-step chunks,
+"""The value-sweeping intra-chunk kernel (bf16 I/O, 64-, 128- or 256-step chunks,
 two or more 128-wide value tiles: one workgroup per chunk forms P once and
 sweeps every value tile) against the per-tile kernel it replaces there
 (TFLA_INTRA_SWEEP=0 selects that one), in the forward pass (every gate) and
@@ -59,6 +59,9 @@ CASES = [
     (GLA, 2, 1, 130, 64, 384, 64),
     (GLA, 1, 2, 600, 128, 256, 256),    # per-channel gate at 8 waves (d_qk <= 128)
     (GLA, 1, 1, 300, 64, 512, 256),
+    (SIG, 1, 2, 500, 256, 512, 128),    # four-wave workgroups
+    (SCAL, 1, 2, 129, 128, 256, 128),
+    (GLA, 1, 2, 400, 128, 256, 128),
 ]
 
 
@@ -99,7 +102,7 @@ def test_sweep_with_initial_state(variant, flags, L):
     assert bool(torch.isfinite(outs[0]).all())
 
 
-@pytest.mark.parametrize("cfg,L", [(3, 256), (3, 64), (4, 64)])
+@pytest.mark.parametrize("cfg,L", [(3, 256), (3, 128), (3, 64), (4, 64)])
 def test_sweep_full_size(cfg, L):
     """Workload 3 (mLSTMsig B=4 H=8 T=8192 d_qk=256 d_hv=512; L = 256 is the
     launch the bench times) and workload 4 (per-channel gate B=8 H=4 T=2048
@@ -130,7 +133,8 @@ def same(a, b):
     (SIG, 1, 2, 700, 256, 512, 256), (SCAL, 2, 1, 600, 128, 256, 256), (SIG, 1, 1, 200, 64, 256, 256),
     (SIG, 1, 2, 512, 256, 256, 256), (SIG, 1, 2, 300, 256, 512, 64), (SCAL, 1, 2, 150, 128, 256, 64),
     (GLA, 1, 2, 300, 256, 512, 64),     # per-channel gate (mirrored reference rows)
-    (GLA, 2, 1, 333, 128, 256, 64), (GLA, 1, 2, 600, 128, 256, 256),
+    (GLA, 2, 1, 333, 128, 256, 64), (GLA, 1, 2, 600, 128, 256, 256), (SIG, 1, 2, 500, 256, 512, 128),
+    (GLA, 1, 1, 300, 128, 256, 128),
 ])
 def test_dv_sweep_matches_per_tile_kernel_and_oracle(variant, B, H, T, dqk, dhv, L):
     print(f"dv value sweep: variant {variant} B{B} H{H} T{T} {dqk}x{dhv} L{L}", flush=True)
