@@ -33,7 +33,9 @@
  *   - Arguments are validated before any HIP call; a rejected call has no
  *     side effect.  Every call returns a tfla_status; tfla_last_error()
  *     returns a thread-local message describing the last failure.
- *   - Calls are reentrant; the only mutable global state is that message.
+ *   - Calls are reentrant; the only mutable global state is that message
+ *     and the test overrides of tfla_dbg_set_knob (unset unless a test sets
+ *     them).  The library reads no environment variable.
  */
 #ifndef TFLA_H
 #define TFLA_H
@@ -287,6 +289,28 @@ int tfla_dbg_gates(const float* igate_pre, const float* fgate_pre,
 int tfla_dbg_states(const void* k, const void* v,
                     const float* igate_pre, const float* fgate_pre, void* states_out,
                     int B, int H, int T, int d_qk, int d_hv, int L, int variant, void* stream);
+
+/*
+ * tfla_dbg_set_knob -- test hook: process-wide overrides of choices the
+ * library otherwise makes from the problem shape, for tests that must reach
+ * a particular kernel at a small size and for tuning comparisons.  `value`
+ * < 0 restores the default.  Results stay correct under every setting
+ * (only the kernel choice or tiling changes), except TFLA_KNOB_FAULT_ALLOC,
+ * which makes the library's own workspace allocations fail.  Calls that
+ * run while a knob changes may see either setting.  Returns
+ * TFLA_ERR_INVALID_ARG for an unknown knob.
+ */
+enum tfla_knob {
+    TFLA_KNOB_INTRA_SWEEP = 0,     /* 0: the per-tile intra-chunk kernel where the value sweep
+                                      would run                                               */
+    TFLA_KNOB_INTRA_BV = 1,        /* 64: cap the per-tile kernel's value tile at 64 columns  */
+    TFLA_KNOB_INTRA_ROWS = 2,      /* 64, 128 or 256: cap its query rows per workgroup        */
+    TFLA_KNOB_STATE_SEGMENTS = 3,  /* n >= 1: the state walk's segment count                  */
+    TFLA_KNOB_STATE_SB = 4,        /* 64 or 128: cap the state walk's block of steps          */
+    TFLA_KNOB_FAULT_ALLOC = 5,     /* 1: the library's own workspace allocations fail         */
+    TFLA_KNOB_COUNT = 6
+};
+int tfla_dbg_set_knob(int knob, int value);
 
 /* Static description of a status code. */
 const char* tfla_error_string(int code);

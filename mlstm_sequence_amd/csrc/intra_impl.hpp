@@ -58,11 +58,11 @@
 //   kStateF32: the forward pass reading fp32 states with bf16 I/O.
 #pragma once
 
-#include <cstdlib>
 #include <type_traits>
 
 #include "gfx950.hpp"
 #include "kernels.hpp"
+#include "tfla.h"
 
 namespace tfla {
 namespace {
@@ -678,11 +678,10 @@ hipError_t launch_intra_t(const Problem& p, const void* q, const void* k, const 
 // Value-tile width: 128 when it divides d_hv (bf16 I/O), else 64 (fp32 I/O
 // always: its doubled fragments would not fit the register budget; nor
 // would a 512-wide contraction's at two waves, i.e. L = 64).
-// TFLA_INTRA_BV=64 forces 64 (tuning sweeps).
+// The intra-BV knob set to 64 forces 64 (tuning sweeps).
 inline int intra_bv(const Problem& p)
 {
-    if (const char* e = std::getenv("TFLA_INTRA_BV"))
-        if (std::atoi(e) == 64) return 64;
+    if (knob(TFLA_KNOB_INTRA_BV) == 64) return 64;
     if (p.dqk > 256 && p.L < 128) return 64;
     return (p.bf16 && p.dhv % 128 == 0) ? 128 : 64;
 }
@@ -693,15 +692,13 @@ inline int intra_bv(const Problem& p)
 // keeps 128: its 32 Q fragments need the whole register file, i.e. four
 // waves at one wave per SIMD (measured 14% faster over the backward pass
 // than eight spilling waves, and than 64-wide value tiles, which recompute
-// S = K Q^T for twice as many tiles).  TFLA_INTRA_ROWS=64|128|256 caps it
-// (tuning sweeps).
+// S = K Q^T for twice as many tiles).  The intra-rows knob (64, 128 or 256)
+// caps it (tuning sweeps).
 inline int intra_rows(const Problem& p)
 {
     int cap = p.bf16 ? (p.dqk > 256 ? 128 : 256) : 128;
-    if (const char* e = std::getenv("TFLA_INTRA_ROWS")) {
-        const int want = std::atoi(e);
-        if (want == 64 || want == 128 || want == 256) cap = want < cap ? want : cap;
-    }
+    const int want = knob(TFLA_KNOB_INTRA_ROWS);
+    if (want == 64 || want == 128 || want == 256) cap = want < cap ? want : cap;
     int rows = 64;
     while (rows * 2 <= cap && p.L % (rows * 2) == 0) rows *= 2;
     return rows;

@@ -29,11 +29,11 @@
 // per-tile kernel's reference-point factorisation: for each key tile, q is
 // scaled by e^{a_t - a_ref} and k by e^{a_ref - a_s} with a_ref at the
 // tile's middle step, and the inter-chunk term takes q o e^{a_t}.
-#include <cstdlib>
 #include <type_traits>
 
 #include "gfx950.hpp"
 #include "kernels.hpp"
+#include "tfla.h"
 
 namespace tfla {
 namespace {
@@ -428,12 +428,11 @@ hipError_t sweep_gate(const Problem& p, const void* q, const void* k, const void
 // tiles; every gate (the per-channel gate at L >= 128 only up to d_qk = 128:
 // its Q fragments, rescaled per key tile, spill at 4 or 8 waves and d_qk =
 // 256), in the forward pass and in the dv product.
-// TFLA_INTRA_SWEEP=0 turns it off (the per-tile kernel then runs; tuning
-// comparisons).
+// The intra-sweep knob set to 0 turns it off (the per-tile kernel then runs;
+// tests of bitwise agreement and tuning comparisons).
 bool intra_sweeps(const Problem& p)
 {
-    if (const char* e = std::getenv("TFLA_INTRA_SWEEP"))
-        if (std::atoi(e) == 0) return false;
+    if (knob(TFLA_KNOB_INTRA_SWEEP) == 0) return false;
     return p.bf16 && (p.L == 64 || p.L == 128 || p.L == 256) && (p.dqk == 64 || p.dqk == 128 || p.dqk == 256) &&
            p.dhv % kSweepBV == 0 && p.dhv / kSweepBV >= 2 && !(p.gate == kGla && p.L >= 128 && p.dqk == 256);
 }

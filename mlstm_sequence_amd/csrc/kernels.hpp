@@ -8,6 +8,11 @@ namespace tfla {
 
 enum GateKind { kSig = 0, kScalar = 1, kGla = 2 };
 
+// Test and tuning overrides set through tfla_dbg_set_knob (tfla.h knob
+// numbers); -1 when unset, which every reader takes as "the default".  The
+// library reads no environment variable.
+int knob(int which);
+
 // Operand modes of the intra-chunk kernel (bit set) for the gradient products;
 // kStateF32: the forward pass reading fp32 states with bf16 I/O.
 enum IntraMode { kNatState = 1, kMirror = 2, kRowDots = 4, kEmitP = 8, kGivenP = 16, kStateF32 = 32 };

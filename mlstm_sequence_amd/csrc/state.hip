@@ -54,10 +54,10 @@
 // one per key channel (the row dot of D_m and C_m in that channel),
 // [B*H][nc-1][d_qk][value tiles x 2].
 #include <algorithm>
-#include <cstdlib>
 
 #include "gfx950.hpp"
 #include "kernels.hpp"
+#include "tfla.h"
 
 namespace tfla {
 namespace {
@@ -557,8 +557,8 @@ hipError_t launch_state_t(const Problem& p, const T* k, const T* v, const float*
                           hipStream_t stream)
 {
     if (p.nc < 2 && !ws.c0 && !ws.c_final) return hipSuccess;
-    int sb_cap = 256;   // TFLA_STATE_SB=64|128 caps the block (tuning sweeps)
-    if (const char* e = std::getenv("TFLA_STATE_SB")) sb_cap = std::atoi(e);
+    int sb_cap = 256;   // the state-block knob (64 or 128) caps the block (tuning sweeps)
+    if (knob(TFLA_KNOB_STATE_SB) > 0) sb_cap = knob(TFLA_KNOB_STATE_SB);
     if constexpr (sizeof(T) == 2) {
         if (state_big_tiles(p)) {
             // 256-step blocks fill the 160 KB of LDS (one workgroup per CU): only
@@ -591,14 +591,14 @@ bool state_big_tiles(const Problem& p)
 
 // Segments of the chunk chain: enough workgroups for about two per CU of
 // a 256-CU device (512), each segment at least two chunks long; 1 when the
-// heads and tiles alone fill the device.  TFLA_STATE_SEGMENTS=n overrides
-// (tuning).
+// heads and tiles alone fill the device.  The state-segments knob overrides
+// it (tests reach the segmented walk at small sizes with it; tuning).
 int state_segments_for(const Problem& p, long heads_tiles)
 {
     const int nfeed = p.nc - 1;   // chunks that feed a stored state
     if (nfeed < 4) return 1;
     long P = 1;
-    if (const char* e = std::getenv("TFLA_STATE_SEGMENTS")) P = std::atol(e);
+    if (knob(TFLA_KNOB_STATE_SEGMENTS) > 0) P = knob(TFLA_KNOB_STATE_SEGMENTS);
     else if (heads_tiles < 256) P = (512 + heads_tiles - 1) / heads_tiles;
     P = std::min<long>(P, nfeed / 2);
     if (P < 2) return 1;

@@ -5,10 +5,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
-#include <cstring>
 #include <string>
 
 #include "kernels.hpp"
@@ -164,13 +163,12 @@ int check_state_io(const tfla::Problem& p, const void* q, const void* k, const v
     return TFLA_OK;
 }
 
-// Failure injection for tests of the error paths: TFLA_FAULT=alloc makes the
-// library's own workspace allocation fail before any launch.
-bool inject_alloc_fault()
-{
-    const char* f = std::getenv("TFLA_FAULT");
-    return f && std::strcmp(f, "alloc") == 0;
-}
+// Test and tuning overrides (tfla_dbg_set_knob): -1 = unset.
+std::atomic<int> g_knobs[TFLA_KNOB_COUNT] = {-1, -1, -1, -1, -1, -1};
+
+// Failure injection for tests of the error paths: the fault knob set to 1
+// makes the library's own workspace allocation fail before any launch.
+bool inject_alloc_fault() { return tfla::knob(TFLA_KNOB_FAULT_ALLOC) == 1; }
 
 int hip_fail(hipError_t e, const char* what)
 {
@@ -489,7 +487,7 @@ int bwd_entry(const void* q, const void* k, const void* v, const float* igate_pr
         if ((rc = check_workspace_disjoint(workspace, need, tensors, 14))) return rc;
     } else {
         if (inject_alloc_fault())
-            return fail(TFLA_ERR_OUT_OF_MEMORY, "injected allocation failure (TFLA_FAULT=alloc)");
+            return fail(TFLA_ERR_OUT_OF_MEMORY, "injected allocation failure (fault knob)");
         hipError_t e = hipMallocAsync(&base, need, s);
         if (e != hipSuccess) {
             (void)hipGetLastError();
@@ -510,6 +508,12 @@ int bwd_entry(const void* q, const void* k, const void* v, const float* igate_pr
 }  // namespace
 
 namespace tfla {
+
+int knob(int which)
+{
+    if (which < 0 || which >= TFLA_KNOB_COUNT) return -1;
+    return g_knobs[which].load(std::memory_order_relaxed);
+}
 
 size_t workspace_layout(const Problem& p, Workspace* ws, char* base, bool with_states, bool with_c0)
 {
@@ -581,7 +585,7 @@ int tfla_fwd(const void* q, const void* k, const void* v, const float* igate_pre
     if (rc) return rc;
     tfla::Workspace ws;
     const size_t need = tfla::workspace_layout(p, &ws, nullptr);
-    if (inject_alloc_fault()) return fail(TFLA_ERR_OUT_OF_MEMORY, "injected allocation failure (TFLA_FAULT=alloc)");
+    if (inject_alloc_fault()) return fail(TFLA_ERR_OUT_OF_MEMORY, "injected allocation failure (fault knob)");
     hipStream_t s = static_cast<hipStream_t>(stream);
     void* base = nullptr;
     if (need > 0) {
@@ -635,7 +639,7 @@ int tfla_fwd_state(const void* q, const void* k, const void* v, const float* iga
         if ((rc = check_workspace_disjoint(workspace, need, tensors, 8))) return rc;
     } else if (need > 0) {
         if (inject_alloc_fault())
-            return fail(TFLA_ERR_OUT_OF_MEMORY, "injected allocation failure (TFLA_FAULT=alloc)");
+            return fail(TFLA_ERR_OUT_OF_MEMORY, "injected allocation failure (fault knob)");
         hipError_t e = hipMallocAsync(&base, need, s);
         if (e != hipSuccess) {
             (void)hipGetLastError();
@@ -707,7 +711,7 @@ int tfla_dbg_states(const void* k, const void* v, const float* igate_pre, const 
     // gate sums in a private allocation; the states go straight to states_out
     tfla::Workspace ws;
     const size_t need = tfla::workspace_layout(p, &ws, nullptr, false);
-    if (inject_alloc_fault()) return fail(TFLA_ERR_OUT_OF_MEMORY, "injected allocation failure (TFLA_FAULT=alloc)");
+    if (inject_alloc_fault()) return fail(TFLA_ERR_OUT_OF_MEMORY, "injected allocation failure (fault knob)");
     hipStream_t s = static_cast<hipStream_t>(stream);
     void* base = nullptr;
     hipError_t e = hipSuccess;
@@ -765,6 +769,14 @@ int tfla_bwd_state(const void* q, const void* k, const void* v, const float* iga
     io.dc0 = dc0;
     return bwd_entry(q, k, v, igate_pre, fgate_pre, dh, dq, dk, dv, dig, dfg, B, H, T, d_qk, d_hv, L, variant,
                      workspace, workspace_bytes, stream, &io);
+}
+
+int tfla_dbg_set_knob(int which, int value)
+{
+    if (which < 0 || which >= TFLA_KNOB_COUNT)
+        return fail(TFLA_ERR_INVALID_ARG, "unknown knob " + std::to_string(which));
+    g_knobs[which].store(value < 0 ? -1 : value, std::memory_order_relaxed);
+    return TFLA_OK;
 }
 
 const char* tfla_error_string(int code)

@@ -221,24 +221,15 @@ int oracle_log_gates(const double* igate_pre, const double* fgate_pre,
  *            dL/dfgate_pre_t = (sum_c df_{t,c}) f_t (1 - f_t)
  *   kind 1:  dL/dfgate_pre[h] = sum over b, t, c of df_{t,c} f_h (1 - f_h)
  *   kind 2:  dL/dx_{t,c} = df_{t,c} f_{t,c} (1 - sigmoid(x_{t,c})) / 16
- * where a floored log forget gate (below -100) passes no gradient.  C_0 = 0.
+ * -- the plain derivative everywhere: no floor on the log forget gate (the
+ * GPU library's floor at -100 is a convention of that library, not of the
+ * function defined here).  C_0 = 0.
  * The forward sweep yields C_t and dq_t; the reverse sweep recomputes the
  * states of each 64-step block from a checkpoint taken in the forward sweep.
  *
  * Layouts as oracle_fwd; dh like h; dq, dk, dv like q, k, v; dig like
  * igate_pre (kind 0; may be NULL otherwise); dfg like fgate_pre.
  */
-static int forget_floored(int kind, const double* fgate_pre, size_t bh, int head, int T, int dqk, int t, int c)
-{
-    double x;
-    switch (kind) {
-    case KIND_MLSTM_SIG: x = log_sigmoid(fgate_pre[bh * (size_t)T + t]); break;
-    case KIND_SCALAR: x = log_sigmoid(fgate_pre[head]); break;
-    default: x = log_sigmoid(fgate_pre[(bh * (size_t)T + t) * dqk + c]) / 16.0; break;
-    }
-    return x < -100.0;
-}
-
 int oracle_bwd_state(const double* q, const double* k, const double* v,
                      const double* igate_pre, const double* fgate_pre, const double* c0,
                      const double* dh, const double* dcT,
@@ -348,17 +339,13 @@ int oracle_bwd_state(const double* q, const double* k, const double* v,
                     dig[(size_t)bh * T + t] = di * it * (1.0 - it);
                     double sdf = 0.0;
                     for (int c = 0; c < dqk; ++c) sdf += df[c];
-                    dfg[(size_t)bh * T + t] =
-                        forget_floored(kind, fgate_pre, (size_t)bh, head, T, dqk, t, 0) ? 0.0 : sdf * f[0] * (1.0 - f[0]);
+                    dfg[(size_t)bh * T + t] = sdf * f[0] * (1.0 - f[0]);
                 } else if (kind == KIND_SCALAR) {
-                    if (!forget_floored(kind, fgate_pre, (size_t)bh, head, T, dqk, t, 0))
-                        for (int c = 0; c < dqk; ++c) dscal[bh] += df[c] * f[c] * (1.0 - f[c]);
+                    for (int c = 0; c < dqk; ++c) dscal[bh] += df[c] * f[c] * (1.0 - f[c]);
                 } else {
                     for (int c = 0; c < dqk; ++c) {
                         const double x = fgate_pre[((size_t)bh * T + t) * dqk + c];
-                        dfg[((size_t)bh * T + t) * dqk + c] =
-                            forget_floored(kind, fgate_pre, (size_t)bh, head, T, dqk, t, c)
-                                ? 0.0 : df[c] * f[c] * (1.0 - sigmoid(x)) / 16.0;
+                        dfg[((size_t)bh * T + t) * dqk + c] = df[c] * f[c] * (1.0 - sigmoid(x)) / 16.0;
                     }
                 }
             }

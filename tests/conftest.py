@@ -21,3 +21,19 @@ def _oracle_built():
         from oracle.build import build
         build()
     yield
+
+
+@pytest.fixture
+def set_knob():
+    """set_knob(which, value): a library test override (tfla_dbg_set_knob)
+    for this test only; every knob it touched is cleared afterwards."""
+    from mlstm_sequence_amd import tfla
+    touched = []
+
+    def _set(which, value):
+        tfla.tfla_dbg_set_knob(which, int(value))
+        touched.append(which)
+
+    yield _set
+    for which in touched:
+        tfla.tfla_dbg_set_knob(which, -1)

@@ -72,8 +72,8 @@ def test_rejects_bad_arguments(L, kw, code):
     assert tfla.tfla_last_error()
 
 
-def test_injected_allocation_failure(L, monkeypatch):
-    monkeypatch.setenv("TFLA_FAULT", "alloc")
+def test_injected_allocation_failure(L, set_knob):
+    set_knob(tfla.KNOB_FAULT_ALLOC, 1)
     assert fwd() == OOM
     assert "injected" in tfla.tfla_last_error()
     assert L.tfla_dbg_states(K, V, IG, FG, WS, 2, 3, 300, 128, 256, 64, SIG | BF16, None) == OOM
@@ -155,8 +155,8 @@ def test_fwd_state_rejects_bad_arguments(L, kw, code):
     assert tfla.tfla_last_error()
 
 
-def test_fwd_state_allocation_failure(L, monkeypatch):
-    monkeypatch.setenv("TFLA_FAULT", "alloc")
+def test_fwd_state_allocation_failure(L, set_knob):
+    set_knob(tfla.KNOB_FAULT_ALLOC, 1)
     assert fwd_state(ws=None, nws=0) == OOM
     assert "injected" in tfla.tfla_last_error()
 
@@ -230,8 +230,8 @@ def test_bwd_reuse_needs_the_forward_workspace(L):
     assert n > 0 and tfla.tfla_bwd_workspace_bytes(2, 3, 300, 128, 256, 64, SIG | BF16 | 0x200) == n
 
 
-def test_bwd_injected_allocation_failure(L, monkeypatch):
-    monkeypatch.setenv("TFLA_FAULT", "alloc")
+def test_bwd_injected_allocation_failure(L, set_knob):
+    set_knob(tfla.KNOB_FAULT_ALLOC, 1)
     assert bwd() == OOM
 
 
@@ -307,3 +307,82 @@ def test_bwd_state_workspace_bytes(L):
     b = tfla.tfla_bwd_state_workspace_bytes(2, 3, 250, 128, 256, 64, SIG | BF16)
     assert b > a > 0
     assert tfla.tfla_bwd_state_workspace_bytes(2, 3, 250, 128, 192, 64, SIG | BF16) == 0
+
+
+# ---- the binding checks tensors before a pointer reaches the library --------
+def _cpu_case(gate=SIG, dtype=None, B=1, H=2, T=40, dqk=64, dhv=128):
+    import torch
+    dtype = dtype or torch.bfloat16
+    q = torch.zeros(B, H, T, dqk, dtype=dtype)
+    k = torch.zeros(B, H, T, dqk, dtype=dtype)
+    v = torch.zeros(B, H, T, dhv, dtype=dtype)
+    if gate == SIG:
+        ig, fg = torch.zeros(B, H, T), torch.zeros(B, H, T)
+    elif gate == SCALAR:
+        ig, fg = None, torch.zeros(H)
+    else:
+        ig, fg = None, torch.zeros(B, H, T, dqk)
+    return q, k, v, ig, fg
+
+
+def _malformed():
+    """(description, mutate(case) -> case, expected exception)"""
+    import torch
+    return [
+        ("k transposed view", lambda c: (c[0], c[1].transpose(2, 3).contiguous().transpose(2, 3), *c[2:]), ValueError),
+        ("v non-contiguous", lambda c: (c[0], c[1], torch.zeros(1, 2, 128, 40, dtype=c[2].dtype).transpose(2, 3),
+                                         *c[3:]), ValueError),
+        ("v of another dtype", lambda c: (c[0], c[1], c[2].float(), *c[3:]), TypeError),
+        ("bf16 gate", lambda c: (*c[:3], c[3].to(torch.bfloat16), c[4]), TypeError),
+        ("fgate of the wrong rank", lambda c: (*c[:4], c[4][..., None].expand(1, 2, 40, 64).contiguous()), ValueError),
+        ("k of another length", lambda c: (c[0], c[1][:, :, :39].contiguous(), *c[2:]), ValueError),
+        ("missing input gate", lambda c: (*c[:3], None, c[4]), ValueError),
+    ]
+
+
+@pytest.mark.parametrize("idx", range(7))
+def test_binding_rejects_malformed_tensors(L, idx):
+    name, mutate, exc = _malformed()[idx]
+    q, k, v, ig, fg = mutate(_cpu_case())
+    with pytest.raises(exc):
+        tfla.forward(q, k, v, ig, fg, tfla.MLSTM_SIG, 64)
+    import torch
+    dh = torch.zeros(1, 2, 40, 128, dtype=torch.bfloat16)
+    with pytest.raises(exc):
+        tfla.backward(q, k, v, ig, fg, dh, tfla.MLSTM_SIG, 64)
+
+
+def test_binding_rejects_gla_gate_shapes_and_cpu_tensors(L):
+    import torch
+    q, k, v, ig, fg = _cpu_case(GLA)
+    with pytest.raises(ValueError):            # [B,H,T] is the per-step shape, not the per-channel one
+        tfla.forward(q, k, v, None, fg[..., 0].contiguous(), tfla.GLA_KEY, 64)
+    with pytest.raises(ValueError):            # an input gate where the variant has none
+        tfla.forward(q, k, v, torch.zeros(1, 2, 40), fg, tfla.GLA_KEY, 64)
+    q, k, v, ig, fg = _cpu_case(SCALAR)
+    with pytest.raises(ValueError):            # fixed decay takes one logit per head
+        tfla.forward(q, k, v, None, torch.zeros(1, 2, 40), tfla.SCALAR_DECAY, 64)
+    with pytest.raises(ValueError, match="GPU memory"):   # well formed, but host tensors
+        tfla.forward(q, k, v, None, fg, tfla.SCALAR_DECAY, 64)
+    st = torch.zeros(1, 2, 64, 128)
+    with pytest.raises(ValueError):            # state of the wrong orientation
+        tfla.tfla_fwd_recurrent(q, k, v, None, fg, st.transpose(2, 3).contiguous(), torch.zeros_like(v),
+                                1, 2, 40, 64, 128, SCALAR | BF16)
+    with pytest.raises(ValueError):            # workspace smaller than the byte count passed
+        tfla.tfla_fwd_ws(q, k, v, None, fg, torch.zeros_like(v), 1, 2, 40, 64, 128, 64, SCALAR | BF16,
+                         torch.zeros(16, dtype=torch.uint8), 1024)
+
+
+def test_knobs_are_set_and_cleared_through_the_hook(L, set_knob):
+    assert L.tfla_dbg_set_knob(99, 1) == INVALID
+    assert "knob" in tfla.tfla_last_error()
+    assert L.tfla_dbg_set_knob(-1, 1) == INVALID
+    # the segment knob changes the workspace the segmented walk needs
+    B, H, T, dqk, dhv, Lc = 1, 2, 64 * 11 + 29, 64, 128, 64
+    base = tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16)
+    set_knob(tfla.KNOB_STATE_SEGMENTS, 2)            # by default this shape takes 4 segments
+    assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16) < base
+    set_knob(tfla.KNOB_STATE_SEGMENTS, 1)            # no segmented walk at all
+    assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16) < base
+    tfla.tfla_dbg_set_knob(tfla.KNOB_STATE_SEGMENTS, -1)
+    assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16) == base

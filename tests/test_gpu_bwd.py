@@ -6,7 +6,6 @@ pre-activations; tolerance max|d|/max|ref| <= 1e-4 (fp32 I/O) and <= 2e-2
 (bf16 I/O) on every gradient, the bar of the forward pass.  bf16 inputs and
 dh are exact in the oracle's float64.
 """
-import os
 
 import numpy as np
 import pytest
@@ -102,10 +101,10 @@ def test_backward_matches_oracle(variant, dtype, B, H, T, dqk, dhv, L):
 
 @pytest.mark.parametrize("segments", ["1", "2", "5"])
 @pytest.mark.parametrize("variant", [SIG, SCAL, GLA])
-def test_backward_segmented_walk(variant, segments, monkeypatch):
+def test_backward_segmented_walk(variant, segments, set_knob):
     """Forced segment counts of both state walks (the reverse walk's first
     segment holds the partial last chunk)."""
-    monkeypatch.setenv("TFLA_STATE_SEGMENTS", segments)
+    set_knob(tfla.KNOB_STATE_SEGMENTS, segments)
     B, H, T, dqk, dhv, L = 1, 2, 64 * 11 + 29, 64, 128, 64
     wl, inp = case(variant, B, H, T, dqk, dhv, BF, seed=77 + variant)
     dh = W.upstream_grad(B, H, T, dhv, BF, seed=78)
@@ -169,12 +168,12 @@ def test_backward_rejects_odd_widths():
 @pytest.mark.parametrize("variant,dtype,T,L,segments", [
     (SIG, BF, 1100, 128, None), (SCAL, F32, 333, 64, None), (GLA, BF, 530, 64, None), (SIG, BF, 64 * 11 + 29, 64, "3"),
 ])
-def test_backward_reusing_forward_workspace(variant, dtype, T, L, segments, monkeypatch):
+def test_backward_reusing_forward_workspace(variant, dtype, T, L, segments, set_knob):
     """tfla_fwd_ws leaves its gate sums and states in the workspace; tfla_bwd
     with TFLA_BWD_REUSE_FWD on that workspace skips recomputing them and
     returns bitwise the gradients of the recomputing call."""
     if segments:
-        monkeypatch.setenv("TFLA_STATE_SEGMENTS", segments)
+        set_knob(tfla.KNOB_STATE_SEGMENTS, segments)
     B, H, dqk, dhv = 1, 2, 64, 128
     wl, inp = case(variant, B, H, T, dqk, dhv, dtype, seed=T + variant)
     dh = W.upstream_grad(B, H, T, dhv, dtype, seed=T + 1)

@@ -99,8 +99,8 @@ def test_state_backward_matches_oracle(variant, dtype, B, H, T, dqk, dhv, L, wit
 
 @pytest.mark.parametrize("segments", ["2", "5"])
 @pytest.mark.parametrize("variant", [SIG, SCAL, GLA])
-def test_state_backward_segmented_walks(variant, segments, monkeypatch):
-    monkeypatch.setenv("TFLA_STATE_SEGMENTS", segments)
+def test_state_backward_segmented_walks(variant, segments, set_knob):
+    set_knob(tfla.KNOB_STATE_SEGMENTS, segments)
     B, H, T, dqk, dhv, L = 1, 2, 64 * 11 + 29, 64, 128, 64
     wl, inp = case(variant, B, H, T, dqk, dhv, BF, seed=31 + variant)
     dh = W.upstream_grad(B, H, T, dhv, BF, seed=32)

@@ -14,7 +14,9 @@ pytestmark = pytest.mark.gpu
 
 SAMPLES = {1: [(0, 0)], 2: [(0, 0), (3, 17), (7, 31)], 3: [(0, 0), (3, 7)], 4: [(0, 0), (7, 3)],
            5: [(0, 0), (0, 7)]}
-CASES = [(c, L) for c in sorted(W.WORKLOADS) for L in W.WORKLOADS[c].chunk_sizes]
+# every listed chunk size, plus the longer chunks the benchmark's sweep
+# reports for the T = 8192 mLSTMsig workload (d_qk = 256, d_hv = 512)
+CASES = sorted([(c, L) for c in W.WORKLOADS for L in W.WORKLOADS[c].chunk_sizes] + [(3, 512), (3, 1024)])
 
 _cache = {}
 

@@ -1,12 +1,10 @@
 """The value-sweeping intra-chunk kernel (bf16 I/O, 64-, 128- or 256-step chunks,
 two or more 128-wide value tiles: one workgroup per chunk forms P once and
 sweeps every value tile) against the per-tile kernel it replaces there
-(TFLA_INTRA_SWEEP=0 selects that one), in the forward pass (every gate) and
+(the intra-sweep test override selects that one), in the forward pass (every gate) and
 in the backward pass's dv product.  Both take the same
 products in the same order with the same roundings, so h (and every
 gradient) must agree to the bit; both must match the oracle."""
-import os
-from contextlib import contextmanager
 
 import pytest
 import torch
@@ -28,17 +26,9 @@ def _gpu():
     tfla.lib()
 
 
-@contextmanager
 def per_tile_kernel():
-    old = os.environ.get("TFLA_INTRA_SWEEP")
-    os.environ["TFLA_INTRA_SWEEP"] = "0"
-    try:
-        yield
-    finally:
-        if old is None:
-            del os.environ["TFLA_INTRA_SWEEP"]
-        else:
-            os.environ["TFLA_INTRA_SWEEP"] = old
+    """The per-tile kernel where the value sweep would run (test override)."""
+    return tfla.knob(tfla.KNOB_INTRA_SWEEP, 0)
 
 
 CASES = [

@@ -206,11 +206,11 @@ def test_long_context_split_in_two():
     (GLA, BF, 1, 2, 900, 128, 128, 64, True),
     (SIG, F32, 1, 2, 1111, 64, 128, 64, True),
 ])
-def test_segmented_state_walk(monkeypatch, segments, variant, dtype, B, H, T, dqk, dhv, L, with_c0):
+def test_segmented_state_walk(set_knob, segments, variant, dtype, B, H, T, dqk, dhv, L, with_c0):
     """The chunk chain cut into segments (end states from zero, a combine
     pass, a second walk from the true start states) gives the oracle's
     outputs, final state and chunk-boundary states."""
-    monkeypatch.setenv("TFLA_STATE_SEGMENTS", segments)
+    set_knob(tfla.KNOB_STATE_SEGMENTS, segments)
     wl, inp = case(variant, B, H, T, dqk, dhv, dtype, seed=int(segments) * 100 + T)
     c0 = W.initial_state(B, H, dqk, dhv, seed=int(segments), std=1.5) if with_c0 else None
     print(f"segments {segments}: {variant} {dtype} B{B} H{H} T{T} {dqk}x{dhv} L{L} c0={with_c0}", flush=True)

@@ -332,18 +332,18 @@ def _closed_form_torch(q, k, v, ig, fg, kind):
     import torch
     B, H, T, dqk = q.shape
     if kind == MLSTM_SIG:
-        lf = torch.clamp(torch.nn.functional.logsigmoid(fg), min=-100.0)        # [B,H,T]
+        lf = torch.nn.functional.logsigmoid(fg)                                  # [B,H,T]
         li = torch.nn.functional.logsigmoid(ig)
         cum = torch.cumsum(lf, dim=-1)
         logd = cum[..., :, None] - cum[..., None, :] + li[..., None, :]          # [B,H,t,s]
         s = q @ k.transpose(-1, -2)
     elif kind == SCALAR:
-        lf = torch.clamp(torch.nn.functional.logsigmoid(fg), min=-100.0)        # [H]
+        lf = torch.nn.functional.logsigmoid(fg)                                  # [H]
         t = torch.arange(T, dtype=torch.float64)
         logd = (t[:, None] - t[None, :])[None, None] * lf[None, :, None, None]
         s = q @ k.transpose(-1, -2)
     else:
-        lf = torch.clamp(torch.nn.functional.logsigmoid(fg) / 16.0, min=-100.0)  # [B,H,T,c]
+        lf = torch.nn.functional.logsigmoid(fg) / 16.0                           # [B,H,T,c]
         cum = torch.cumsum(lf, dim=2)
         # per channel decay inside q.k; mask before exponentiating (no inf * 0)
         diff = cum[:, :, :, None, :] - cum[:, :, None, :, :]                     # [B,H,t,s,c]
@@ -370,6 +370,99 @@ def test_backward_matches_autograd_of_closed_form(kind):
         if tt[name] is None:
             continue
         assert rel_err(g, tt[name].grad.numpy()) <= 1e-10, name
+
+
+def _forget_grad_by_pairs(q, k, v, ig, fg, dh, kind):
+    """dL/dfgate_pre by brute force over the step pairs a forget gate couples.
+    h_t = sum_{s<=t} D_ts i_s (q_t . k_s) v_s / sqrt(d) with
+    D_ts = prod_{r=s+1..t} f_r, so dD_ts/dlog f_j = D_ts exactly when
+    s < j <= t: dL/dlog f_j = sum_{t>=j} sum_{s<j} D_ts i_s (q_t . k_s)
+    (dh_t . v_s) / sqrt(d) (per key channel c for the per-channel gate,
+    with q_t,c k_s,c in place of q_t . k_s).  Every term is formed as a
+    product of positive decays, so gradients of size e^-250 keep their
+    relative precision.  Then through the gate functions."""
+    B, H, T, dqk = q.shape
+    sig = lambda x: 0.5 * (1.0 + np.tanh(0.5 * x))                 # no overflow at |x| = 2000
+    logsig = lambda x: np.minimum(x, 0.0) - np.log1p(np.exp(-np.abs(x)))
+    out = np.zeros(fg.shape)
+    for b in range(B):
+        for hd in range(H):
+            if kind == MLSTM_SIG:
+                lf = logsig(fg[b, hd])[:, None] * np.ones((1, dqk))
+                i = sig(ig[b, hd])
+            elif kind == SCALAR:
+                lf = np.full((T, dqk), logsig(fg[hd]))
+                i = np.ones(T)
+            else:
+                lf = logsig(fg[b, hd]) / 16.0
+                i = np.ones(T)
+            g = np.zeros((T, dqk))
+            for j in range(T):
+                for t in range(j, T):
+                    for s_ in range(j):
+                        D = np.exp(np.sum(lf[s_ + 1:t + 1], axis=0))          # [dqk]
+                        g[j] += D * i[s_] * q[b, hd, t] * k[b, hd, s_] * np.dot(dh[b, hd, t], v[b, hd, s_])
+            g /= math.sqrt(dqk)
+            if kind == MLSTM_SIG:
+                out[b, hd] = g.sum(axis=1) * sig(-fg[b, hd])
+            elif kind == SCALAR:
+                out[hd] += g.sum() * sig(-fg[hd])
+            else:
+                out[b, hd] = g * sig(-fg[b, hd]) / 16.0
+    return out
+
+
+@pytest.mark.parametrize("kind", [MLSTM_SIG, SCALAR, GLA])
+def test_backward_is_the_plain_derivative_for_vanishing_forget_gates(kind):
+    """Forget gates far below e^-100 (a log forget gate of -250, or -125 per
+    key channel): the gradient of their pre-activation is the plain
+    derivative -- tiny but not zero -- element by element against the
+    brute-force pair sum (a floor on the log gate would zero exactly these
+    entries); the other gradients against float64 autograd of the
+    quadratic closed form."""
+    import torch
+    B, H, T, dqk, dhv = 1, 2, 9, 3, 4
+    q, k, v, ig, fg, dh = _all_inputs(kind, B, H, T, dqk, dhv, seed=55 + kind)
+    if kind == MLSTM_SIG:
+        fg[0, 0, [2, 5]] = -250.0
+        extreme = np.zeros(fg.shape, bool)
+        extreme[0, 0, [2, 5]] = True
+    elif kind == SCALAR:
+        fg[1] = -250.0
+        extreme = np.array([False, True])
+    else:
+        fg[0, 1, 4, :2] = -2000.0          # log f = logsigmoid(-2000) / 16 = -125
+        extreme = np.zeros(fg.shape, bool)
+        extreme[0, 1, 4, :2] = True
+    got = oracle.recurrent_bwd(q, k, v, ig, fg, dh, kind)
+    ref = _forget_grad_by_pairs(q, k, v, ig, fg, dh, kind)
+    assert rel_err(got[4], ref) <= 1e-10
+    assert np.all(ref[extreme] != 0.0) and np.all(np.abs(ref[extreme]) < 1e-50)
+    np.testing.assert_allclose(got[4][extreme], ref[extreme], rtol=1e-9, atol=0.0)
+    tt = {n: (None if a is None else torch.tensor(a, dtype=torch.float64, requires_grad=True))
+          for n, a in zip(["q", "k", "v", "ig"], [q, k, v, ig])}
+    h = _closed_form_torch(tt["q"], tt["k"], tt["v"], tt["ig"], torch.tensor(fg), kind)
+    (h * torch.tensor(dh)).sum().backward()
+    for name, g in zip(["q", "k", "v", "ig"], got):
+        if tt[name] is not None:
+            assert rel_err(g, tt[name].grad.numpy()) <= 1e-10, name
+
+
+def test_backward_of_a_zero_forget_gate():
+    """f = sigmoid(-inf) = 0: dh/dfgate_pre = f (1 - f) dL/df = 0 at that
+    step exactly, and the other gradients are finite and match the reverse
+    sum identity dL/dlog f_t = sum_{t' >= t} (q.dq - k.dk) times (1 - f)."""
+    B, H, T, dqk, dhv = 1, 1, 12, 3, 2
+    q, k, v, ig, fg, dh = _all_inputs(MLSTM_SIG, B, H, T, dqk, dhv, seed=57)
+    fg[0, 0, 6] = -np.inf
+    dq, dk, dv, dig, dfg = oracle.recurrent_bwd(q, k, v, ig, fg, dh, MLSTM_SIG)
+    assert dfg[0, 0, 6] == 0.0
+    for g in (dq, dk, dv, dig, dfg):
+        assert np.all(np.isfinite(g))
+    r = np.sum(q * dq - k * dk, axis=-1)
+    dlogf = np.flip(np.cumsum(np.flip(r, -1), -1), -1)
+    f = 1.0 / (1.0 + np.exp(-fg))
+    assert rel_err(dlogf * (1.0 - f), dfg) <= 1e-10
 
 
 @pytest.mark.parametrize("kind", [MLSTM_SIG, GLA])
