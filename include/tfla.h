@@ -126,6 +126,25 @@ int tfla_fwd_ws_marked(const void* q, const void* k, const void* v,
                        void* workspace, size_t workspace_bytes, void* const* marks, void* stream);
 
 /*
+ * tfla_fwd_noalloc -- tfla_fwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): it calls no hipMalloc / hipFree or other allocating
+ * routine.  Its workspace is a static device array inside the library of
+ * tfla_fwd_noalloc_max_workspace() bytes (64 MiB), one per GPU, held until
+ * the process ends; its address is looked up once per device on the first
+ * call there.  Problems whose tfla_workspace_bytes(...) exceed it return
+ * TFLA_ERR_OUT_OF_MEMORY (use tfla_fwd_ws).  Every call on one GPU shares
+ * that GPU's array: calls whose kernels overlap in time on one GPU (other
+ * streams, other threads) race on it and must be serialised by the caller,
+ * e.g. by issuing them on one stream.  Arguments, layouts and results are
+ * those of tfla_fwd.
+ */
+int tfla_fwd_noalloc(const void* q, const void* k, const void* v,
+                     const float* igate_pre, const float* fgate_pre, void* h,
+                     int B, int H, int T, int d_qk, int d_hv, int L, int variant, void* stream);
+size_t tfla_fwd_noalloc_max_workspace(void);
+
+/*
  * tfla_fwd_state -- the forward pass from a given initial state, returning
  * the final state (chunked prefill; splitting a long sequence into calls;
  * the sequence-sharded evaluation of several devices).  The recurrence is

@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <string>
 
 #include "kernels.hpp"
@@ -161,6 +162,41 @@ int check_state_io(const tfla::Problem& p, const void* q, const void* k, const v
     if (c0 && c_final && c0 != c_final && overlaps(range_of(c0, sbytes), range_of(c_final, sbytes)))
         return fail(TFLA_ERR_INVALID_ARG, "c_final overlaps c0 without being the same buffer");
     return TFLA_OK;
+}
+
+// ---- the allocation-free entry point's scratch ------------------------------
+// tfla_fwd_noalloc keeps its workspace in this file-scope device array (one
+// copy per GPU, held until the process ends).  Host code never uses the
+// array's name as an address: on each device the address comes from
+// hipGetSymbolAddress once, with that device current, and is cached here.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the current device; NULL after a failure (message
+// in *err).
+void* scratch_on_current_device(std::string* err)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        *err = std::string("no usable current device: ") + hipGetErrorString(e);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            *err = std::string("hipGetSymbolAddress(scratch) failed: ") + hipGetErrorString(e);
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
 }
 
 // Test and tuning overrides (tfla_dbg_set_knob): -1 = unset.
@@ -604,6 +640,34 @@ int tfla_fwd(const void* q, const void* k, const void* v, const float* igate_pre
     }
     return rc;
 }
+
+int tfla_fwd_noalloc(const void* q, const void* k, const void* v, const float* igate_pre, const float* fgate_pre,
+                     void* h, int B, int H, int T, int d_qk, int d_hv, int L, int variant, void* stream)
+{
+    tfla::Problem p;
+    int rc = check_fwd(q, k, v, igate_pre, fgate_pre, h, B, H, T, d_qk, d_hv, L, variant, &p);
+    if (rc) return rc;
+    tfla::Workspace ws;
+    const size_t need = tfla::workspace_layout(p, &ws, nullptr);
+    if (need > kScratchBytes)
+        return fail(TFLA_ERR_OUT_OF_MEMORY, "tfla_fwd_noalloc: the problem needs " + std::to_string(need) +
+                                                " bytes of workspace; its static scratch holds " +
+                                                std::to_string(kScratchBytes) + " (use tfla_fwd or tfla_fwd_ws)");
+    std::string err;
+    void* base = scratch_on_current_device(&err);
+    if (!base) return fail(TFLA_ERR_HIP, "tfla_fwd_noalloc: " + err);
+    // the scratch is device memory of this library; no tensor can overlap it
+    // unless a caller passed a pointer into it
+    Range tensors[6];
+    fwd_ranges(p, q, k, v, igate_pre, fgate_pre, h, tensors);
+    if ((rc = check_workspace_disjoint(base, need, tensors, 6))) return rc;
+    // every workspace byte the kernels read is written earlier in the same
+    // call (gate sums, states, segment states), so nothing needs clearing
+    tfla::workspace_layout(p, &ws, static_cast<char*>(base));
+    return run_path(p, q, k, v, igate_pre, fgate_pre, h, ws, static_cast<hipStream_t>(stream));
+}
+
+size_t tfla_fwd_noalloc_max_workspace(void) { return kScratchBytes; }
 
 size_t tfla_state_workspace_bytes(int B, int H, int T, int d_qk, int d_hv, int L, int variant)
 {

@@ -49,6 +49,10 @@ def lib():
         L.tfla_fwd_ws.restype = i
         L.tfla_fwd_ws_marked.argtypes = [vp, vp, vp, fp, fp, vp] + [i] * 7 + [vp, sz, vp, vp]
         L.tfla_fwd_ws_marked.restype = i
+        L.tfla_fwd_noalloc.argtypes = [vp, vp, vp, fp, fp, vp] + [i] * 7 + [vp]
+        L.tfla_fwd_noalloc.restype = i
+        L.tfla_fwd_noalloc_max_workspace.argtypes = []
+        L.tfla_fwd_noalloc_max_workspace.restype = sz
         L.tfla_workspace_bytes.argtypes = [i] * 7
         L.tfla_workspace_bytes.restype = sz
         L.tfla_fwd_state.argtypes = [vp, vp, vp, fp, fp, fp, vp, fp] + [i] * 7 + [vp, sz, vp]
@@ -250,6 +254,19 @@ def tfla_fwd(q, k, v, igate_pre, fgate_pre, h, B, H, T, d_qk, d_hv, L, variant, 
     rc = lib().tfla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(igate_pre), _ptr(fgate_pre), _ptr(h),
                         B, H, T, d_qk, d_hv, L, variant, _stream(stream))
     _check(rc, "tfla_fwd")
+
+
+def tfla_fwd_noalloc(q, k, v, igate_pre, fgate_pre, h, B, H, T, d_qk, d_hv, L, variant, stream=None):
+    """tfla_fwd_noalloc(...): tfla_fwd with the library's static scratch as
+    workspace (no allocation; see include/tfla.h for its size limit)."""
+    _check_fwd(q, k, v, igate_pre, fgate_pre, h, B, H, T, d_qk, d_hv, variant)
+    rc = lib().tfla_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(igate_pre), _ptr(fgate_pre), _ptr(h),
+                                B, H, T, d_qk, d_hv, L, variant, _stream(stream))
+    _check(rc, "tfla_fwd_noalloc")
+
+
+def tfla_fwd_noalloc_max_workspace() -> int:
+    return lib().tfla_fwd_noalloc_max_workspace()
 
 
 def tfla_fwd_ws(q, k, v, igate_pre, fgate_pre, h, B, H, T, d_qk, d_hv, L, variant, workspace,

@@ -386,3 +386,13 @@ def test_knobs_are_set_and_cleared_through_the_hook(L, set_knob):
     assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16) < base
     tfla.tfla_dbg_set_knob(tfla.KNOB_STATE_SEGMENTS, -1)
     assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16) == base
+
+
+def test_noalloc_rejects_oversized_problems_before_any_hip_call(L):
+    var = SIG | BF16
+    need = tfla.tfla_workspace_bytes(4, 8, 8192, 256, 512, 64, var)
+    assert need > L.tfla_fwd_noalloc_max_workspace() == 64 << 20
+    rc = L.tfla_fwd_noalloc(Q, K, V, IG, FG, H_, 4, 8, 8192, 256, 512, 64, var, None)
+    assert rc == OOM
+    assert "scratch" in tfla.tfla_last_error()
+    assert L.tfla_fwd_noalloc(Q, K, V, IG, FG, H_, 4, 8, 8192, 96, 512, 64, var, None) == UNSUPPORTED
