@@ -29,6 +29,11 @@ tiny inputs.  Gate variants (``kind``):
   decay, README model table).
 * 2 ``GLA``: i = 1, f_{t,c} = exp(logsigmoid(x_{t,c}) / 16) per key channel
   (data-dependent gates, GLA abstract).
+
+mLSTMexp (exponential input gate with normaliser and max state, the variant
+mLSTMsig simplifies: TFLA research-map summary, Approach) has its own
+recurrent oracle :func:`recurrent_fwd_exp`, pinned by
+:func:`closed_form_fwd_exp` and :func:`chunkwise_fwd_exp`.
 """
 from __future__ import annotations
 
@@ -61,6 +66,8 @@ def _load():
         lib.oracle_bwd_state.restype = ctypes.c_int
         lib.oracle_log_gates.argtypes = [dp] * 5 + [ctypes.c_int] * 6
         lib.oracle_log_gates.restype = ctypes.c_int
+        lib.oracle_fwd_exp.argtypes = [dp] * 6 + [ctypes.c_int] * 5
+        lib.oracle_fwd_exp.restype = ctypes.c_int
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
         lib.oracle_sigmoid.argtypes = [ctypes.c_double]
@@ -111,6 +118,100 @@ def recurrent_fwd(q, k, v, igate_pre, fgate_pre, kind, L=None):
     if rc != 0:
         raise ValueError("oracle_fwd rejected its arguments")
     return (h, states) if L is not None else h
+
+
+def recurrent_fwd_exp(q, k, v, igate_pre, fgate_pre):
+    """mLSTMexp oracle (``oracle_fwd_exp`` in oracle.c): exponential input
+    gate exp(igate_pre), forget gate sigmoid(fgate_pre), normaliser state and
+    max state, stepped in double.  Returns h [B,H,T,dhv] float64."""
+    q, k, v, ig, fg = map(_f64, (q, k, v, igate_pre, fgate_pre))
+    B, H, T, dqk = q.shape
+    dhv = v.shape[-1]
+    h = np.empty((B, H, T, dhv), dtype=np.float64)
+    rc = _load().oracle_fwd_exp(_ptr(q), _ptr(k), _ptr(v), _ptr(ig), _ptr(fg), _ptr(h), B, H, T, dqk, dhv)
+    if rc != 0:
+        raise ValueError("oracle_fwd_exp rejected its arguments")
+    return h
+
+
+def closed_form_fwd_exp(q, k, v, igate_pre, fgate_pre):
+    """mLSTMexp by its plain definition, brute force in numpy float64 (no
+    max state; overflows once exp(igate_pre) does):
+        num_t = sum_{s<=t} (prod_{r=s+1..t} f_r) e^{igate_pre_s} (q_t . k_s) v_s / sqrt(d)
+        den_t = the same sum without v_s
+        h_t   = num_t / max(|den_t|, 1)"""
+    q, k, v, ig, fg = map(_f64, (q, k, v, igate_pre, fgate_pre))
+    B, H, T, dqk = q.shape
+    f = 1.0 / (1.0 + np.exp(-fg))
+    i = np.exp(ig)
+    h = np.zeros(v.shape)
+    for b in range(B):
+        for hd in range(H):
+            for t in range(T):
+                num = np.zeros(v.shape[-1])
+                den = 0.0
+                for s_ in range(t + 1):
+                    w = np.prod(f[b, hd, s_ + 1:t + 1]) * i[b, hd, s_] * np.dot(q[b, hd, t], k[b, hd, s_])
+                    num += w * v[b, hd, s_]
+                    den += w
+                num /= np.sqrt(dqk)
+                den /= np.sqrt(dqk)
+                h[b, hd, t] = num / max(abs(den), 1.0)
+    return h
+
+
+def chunkwise_fwd_exp(q, k, v, igate_pre, fgate_pre, L):
+    """mLSTMexp in chunkwise-parallel form, numpy float64, any chunk size L
+    (ragged last chunk included), each chunk stabilised by its own running
+    maximum: per chunk, the carried states (C, n) and their log scale m enter
+    every row with weight e^{a_t + m}, the rows' own pairs with
+    e^{a_t - a_s + igate_pre_s}; every term is taken relative to the row's
+    largest log weight before exponentiating, and the carried states are
+    renormalised to the largest log weight reaching the chunk's end."""
+    q, k, v, ig, fg = map(_f64, (q, k, v, igate_pre, fgate_pre))
+    B, H, T, dqk = q.shape
+    dhv = v.shape[-1]
+    lf = np.minimum(fg, 0.0) - np.log1p(np.exp(-np.abs(fg)))
+    h = np.zeros((B, H, T, dhv))
+    sc = 1.0 / np.sqrt(dqk)
+    for b in range(B):
+        for hd in range(H):
+            C = np.zeros((dqk, dhv))
+            n = np.zeros(dqk)
+            m = -np.inf                                   # log scale of (C, n)
+            for t0 in range(0, T, L):
+                t1 = min(t0 + L, T)
+                a = np.cumsum(lf[b, hd, t0:t1])           # chunk-local log decay
+                for t in range(t0, t1):
+                    r = t - t0
+                    logw = a[r] - a[:r + 1] + ig[b, hd, t0:t + 1]      # the chunk's pairs s <= t
+                    top = max(a[r] + m, np.max(logw))
+                    if top == -np.inf:
+                        continue                            # nothing has entered: h_t = 0
+                    w = np.exp(logw - top)
+                    qk = k[b, hd, t0:t + 1] @ q[b, hd, t]
+                    num = (w * qk) @ v[b, hd, t0:t + 1]
+                    den = np.dot(w, qk)
+                    if m != -np.inf:
+                        ci = np.exp(a[r] + m - top)
+                        num = num + ci * (q[b, hd, t] @ C)
+                        den = den + ci * np.dot(q[b, hd, t], n)
+                    h[b, hd, t] = num * sc / max(abs(den) * sc, np.exp(-top))
+                # carry to the chunk end
+                g = a[-1]
+                logw = g - a + ig[b, hd, t0:t1]
+                top = max(g + m, np.max(logw))
+                if top == -np.inf:
+                    C[:] = 0.0
+                    n[:] = 0.0
+                    m = -np.inf
+                    continue
+                w = np.exp(logw - top)
+                cc = np.exp(g + m - top) if m != -np.inf else 0.0
+                C = cc * C + (k[b, hd, t0:t1] * w[:, None]).T @ v[b, hd, t0:t1]
+                n = cc * n + w @ k[b, hd, t0:t1]
+                m = top
+    return h
 
 
 def recurrent_fwd_state(q, k, v, igate_pre, fgate_pre, kind, c0=None):

@@ -378,6 +378,94 @@ int oracle_bwd(const double* q, const double* k, const double* v,
                             B, H, T, dqk, dhv, kind);
 }
 
+/*
+ * mLSTMexp forward (the mLSTM with an exponential input gate, a normaliser
+ * state and a max state, which the TFLA research-map summary, Approach,
+ * names as what mLSTMsig removes; the pages print no equations, so this is
+ * the plainest reading of those words, with the forget gate of mLSTMsig):
+ *
+ *   i_t = exp(igate_pre_t),  f_t = sigmoid(fgate_pre_t)
+ *   C_t = f_t C_{t-1} + i_t k_t v_t^T,   n_t = f_t n_{t-1} + i_t k_t    (C_0 = 0, n_0 = 0)
+ *   h_t = (C_t^T q_t / sqrt(d_qk)) / max(|n_t . q_t| / sqrt(d_qk), 1)
+ *
+ * evaluated step by step with the max state m_t = max(log f_t + m_{t-1},
+ * igate_pre_t) (m_0 = -inf) carried beside the stabilised states
+ * Cs = C e^{-m}, ns = n e^{-m}:
+ *
+ *   Cs_t = e^{log f_t + m_{t-1} - m_t} Cs_{t-1} + e^{igate_pre_t - m_t} k_t v_t^T   (ns_t likewise)
+ *   h_t  = (Cs_t^T q_t / sqrt(d)) / max(|ns_t . q_t| / sqrt(d), e^{-m_t})
+ *
+ * which is the same h (numerator and denominator both scaled by e^{-m_t})
+ * without the overflow of e^{igate_pre}.  While no input has entered
+ * (m_t = -inf: every input gate so far 0, or erased by a forget gate of 0)
+ * the states are 0 and h_t = 0.  Layouts as oracle_fwd; igate_pre [B,H,T].
+ */
+int oracle_fwd_exp(const double* q, const double* k, const double* v,
+                   const double* igate_pre, const double* fgate_pre, double* h,
+                   int B, int H, int T, int dqk, int dhv)
+{
+    if (!q || !k || !v || !igate_pre || !fgate_pre || !h) return -1;
+    if (B < 0 || H < 0 || T < 0 || dqk < 1 || dhv < 1) return -1;
+    const long nbh = (long)B * H;
+    const double scale = 1.0 / sqrt((double)dqk);
+    int bad = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < nbh; ++bh) {
+        double* C = (double*)calloc((size_t)dqk * dhv, sizeof(double));
+        double* n = (double*)calloc((size_t)dqk, sizeof(double));
+        if (!C || !n) {
+            free(C);
+            free(n);
+#pragma omp atomic write
+            bad = 1;
+            continue;
+        }
+        double m = -INFINITY;
+        for (int t = 0; t < T; ++t) {
+            const double* qt = q + ((size_t)bh * T + t) * dqk;
+            const double* kt = k + ((size_t)bh * T + t) * dqk;
+            const double* vt = v + ((size_t)bh * T + t) * dhv;
+            double* ht = h + ((size_t)bh * T + t) * dhv;
+            const double lf = log_sigmoid(fgate_pre[(size_t)bh * T + t]);
+            const double li = igate_pre[(size_t)bh * T + t];
+            const double carried = lf + m;                 /* -inf when nothing is carried */
+            const double m_new = carried > li ? carried : li;
+            if (m_new == -INFINITY) {
+                /* no input has entered: C_t = 0, n_t = 0, h_t = 0 */
+                memset(C, 0, (size_t)dqk * dhv * sizeof(double));
+                memset(n, 0, (size_t)dqk * sizeof(double));
+                for (int j = 0; j < dhv; ++j) ht[j] = 0.0;
+                m = m_new;
+                continue;
+            }
+            const double fs = carried == -INFINITY ? 0.0 : exp(carried - m_new);
+            const double is = li == -INFINITY ? 0.0 : exp(li - m_new);
+            for (int c = 0; c < dqk; ++c) {
+                double* row = C + (size_t)c * dhv;
+                const double ik = is * kt[c];
+                for (int j = 0; j < dhv; ++j) row[j] = fs * row[j] + ik * vt[j];
+                n[c] = fs * n[c] + ik;
+            }
+            double den = 0.0;
+            for (int c = 0; c < dqk; ++c) den += n[c] * qt[c];
+            den = fabs(den) * scale;
+            const double lower = exp(-m_new);
+            const double div = den > lower ? den : lower;
+            for (int j = 0; j < dhv; ++j) ht[j] = 0.0;
+            for (int c = 0; c < dqk; ++c) {
+                const double* row = C + (size_t)c * dhv;
+                for (int j = 0; j < dhv; ++j) ht[j] += row[j] * qt[c];
+            }
+            for (int j = 0; j < dhv; ++j) ht[j] = ht[j] * scale / div;
+            m = m_new;
+        }
+        free(C);
+        free(n);
+    }
+    return bad ? -1 : 0;
+}
+
 /* the scalar gate functions, exported so tests can pin them */
 double oracle_sigmoid(double x) { return sigmoid(x); }
 double oracle_log_sigmoid(double x) { return log_sigmoid(x); }
