@@ -51,6 +51,9 @@ enum tfla_variant {
     TFLA_MLSTM_SIG = 0,     /* i = sigmoid(igate_pre[t]), f = sigmoid(fgate_pre[t])       */
     TFLA_SCALAR_DECAY = 1,  /* i = 1, f = sigmoid(fgate_pre[h]) fixed per head            */
     TFLA_GLA_KEY = 2,       /* i = 1, f_{t,c} = exp(logsigmoid(fgate_pre[t,c]) / 16)      */
+    TFLA_MLSTM_EXP = 3,     /* mLSTMexp: i = exp(igate_pre[t]), f = sigmoid(fgate_pre[t]),
+                               normaliser and max state (tfla_fwd, _ws, _ws_marked and
+                               _noalloc only; see tfla_fwd)                                 */
     TFLA_IO_BF16 = 0x100,   /* q, k, v, h are bf16; without the flag they are fp32        */
     TFLA_BWD_REUSE_FWD = 0x200, /* tfla_bwd only: reuse the forward pass's gate sums and
                                    states left in the workspace (see tfla_bwd)              */
@@ -76,10 +79,11 @@ enum tfla_status {
  *   q          [B,H,T,d_qk]  bf16 or fp32 (see TFLA_IO_BF16)
  *   k          [B,H,T,d_qk]
  *   v          [B,H,T,d_hv]
- *   igate_pre  fp32 [B,H,T] input-gate pre-activations for TFLA_MLSTM_SIG;
- *              must be NULL for the other variants (their input gate is 1).
+ *   igate_pre  fp32 [B,H,T] input-gate pre-activations for TFLA_MLSTM_SIG and
+ *              TFLA_MLSTM_EXP; must be NULL for the other variants (their
+ *              input gate is 1).
  *   fgate_pre  fp32 forget-gate pre-activations:
- *                TFLA_MLSTM_SIG    [B,H,T]
+ *                TFLA_MLSTM_SIG, TFLA_MLSTM_EXP [B,H,T]
  *                TFLA_SCALAR_DECAY [H]      (logit of the per-head decay;
  *                                            +inf means no decay)
  *                TFLA_GLA_KEY      [B,H,T,d_qk]
@@ -94,6 +98,17 @@ enum tfla_status {
  * Gate pre-activations may be +-inf (a gate of exactly 1 or 0).  The log
  * forget gate is floored at -100 (a forget gate below e^-100 acts as
  * e^-100), which keeps log-decay differences finite.
+ *
+ * TFLA_MLSTM_EXP -- the mLSTM with an exponential input gate, a normaliser
+ * state n and a max state m (what mLSTMsig simplifies: "Tiled Flash Linear
+ * Attention ..." research-map summary, Approach):
+ *     C_t = f_t C_{t-1} + i_t k_t v_t^T,   n_t = f_t n_{t-1} + i_t k_t,
+ *     h_t = (C_t^T q_t / sqrt(d_qk)) / max(|n_t . q_t| / sqrt(d_qk), 1),
+ * i_t = exp(igate_pre_t), f_t = sigmoid(fgate_pre_t), evaluated with the max
+ * state so that exp(igate_pre) never overflows.  igate_pre must not be
+ * +inf; it is floored at -100 (an input gate below e^-100 acts as e^-100).
+ * Forward only: the state-I/O, step-by-step and backward entry points and
+ * the test hooks return TFLA_ERR_UNSUPPORTED for it.
  *
  * Scratch: allocates its workspace (tfla_workspace_bytes) stream-ordered
  * with hipMallocAsync and frees it with hipFreeAsync on `stream`.

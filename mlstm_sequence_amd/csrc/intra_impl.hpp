@@ -124,7 +124,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
                                                            int nc, int c0, float scale,
                                                            const T* __restrict__ partner,
                                                            float* __restrict__ dots, T* __restrict__ pout,
-                                                           const T* __restrict__ pin)
+                                                           const T* __restrict__ pin,
+                                                           const float* __restrict__ lbp,
+                                                           const float* __restrict__ nst)
 {
     constexpr bool NAT = (MODE & kNatState) != 0, REV = (MODE & kMirror) != 0, DOTS = (MODE & kRowDots) != 0;
     // per-channel gate: decay inside the contraction (forward, dv), or on the
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     const T* vb = v + bh * (size_t)T_ * dhv;
     const int gw = OUTDECAY ? dhv : DQK;   // per-channel gate row width
     const float* ab = (GATE == kGla) ? a + bh * (size_t)T_ * gw : a + bh * (size_t)T_;
-    const float* lb = (GATE == kSig) ? li + bh * (size_t)T_ : nullptr;
+    const float* lb = per_step_li(GATE) ? li + bh * (size_t)T_ : nullptr;
     float lg2 = 0.0f;   // log2 of the fixed decay
     if (GATE == kScalar) lg2 = fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor) * kLog2e;
 
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
                         frag_set(pf.kv.p[mt][half], e, to_float(pc[(size_t)row(c) * L]));
                     }
         }
-        if (GATE == kSig && !GIVENP && tid < 64) {
+        if (per_step_li(GATE) && !GIVENP && tid < 64) {
             const int s = min(s0 + tid, T_ - 1);
             pf.li = lb[s];
             if (!REV) pf.a = ab[s];
@@ -347,7 +349,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
             }
             pf.kv.v[u].store(&sm.kv.vs[r][c]);
         }
-        if (GATE == kSig && !GIVENP && tid < 64) sm.bcol[tid] = (REV ? pf.li : pf.li - pf.a) * kLog2e;
+        if (per_step_li(GATE) && !GIVENP && tid < 64) sm.bcol[tid] = (REV ? pf.li : pf.li - pf.a) * kLog2e;
     };
 
     f32x16 acc[NT];
@@ -388,8 +390,8 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int t = min(t0 + 32 * wr + 8 * (r >> 2) + 4 * hh + (r & 3), T_ - 1);
-                const float e = (GATE == kSig) ? exp2_fast(ab[t] * kLog2e)
-                                               : exp2_fast((float)(t - cs + (REV ? 0 : 1)) * lg2);
+                const float e = per_step_li(GATE) ? exp2_fast(ab[t] * kLog2e)
+                                                  : exp2_fast((float)(t - cs + (REV ? 0 : 1)) * lg2);
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= e;
             }
@@ -416,7 +418,8 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
         }
         fref = R;
     };
-    const float at2 = (GATE == kSig) ? ab[tqc] * kLog2e : 0.0f;
+    const float at2 = per_step_li(GATE) ? ab[tqc] * kLog2e : 0.0f;
+    float rsum = 0.0f;   // mLSTMexp: this lane's part of the row sum of P (the normaliser)
     const int tlo = t0 + 32 * wr;                  // first query row of this wave
     const int nkv = (t0 - cs) / 64 + BQ / 64;     // key tiles up to the end of the query tile
     int q_ref = -2;                               // reference row the Q fragments are scaled for
@@ -481,12 +484,16 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
             for (int r = 0; r < 16; ++r) {
                 const int sr = 8 * (r >> 2) + 4 * hh + (r & 3);
                 float p = st[r];
-                if (GATE == kSig) {
+                if (per_step_li(GATE)) {
                     p *= exp2_fast(at2 + sm.bcol[32 * mt + sr]);
                 } else if (GATE == kScalar) {
                     p *= exp2_fast((float)(tlo + i32 - slo - sr) * lg2);
                 }
                 st[r] = (diag && sr > i32) ? 0.0f : p;
+            }
+            if constexpr (GATE == kExp) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) rsum += st[r];
             }
             if constexpr (EMITP) {
                 // P row t (this lane), keys slo + sr: four runs of 4 consecutive keys
@@ -515,6 +522,31 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
 
     // ---------------- output
     if constexpr (EMITP) return;
+    // mLSTMexp: each row's factor scale / max(|scale den_t|, e^{lb_t}) with
+    // den_t = sum_s P_ts + e^{a'_t} q_t . n_{k-1} (the stabilised normaliser),
+    // formed in this lane (row tlo + i32) and handed to the accumulator
+    // layout (row_fac) where rows run along the registers
+    float fac = scale;
+    if constexpr (GATE == kExp) {
+        rsum += __shfl_xor(rsum, 32, 64);
+        float qn = 0.0f;
+        if (inter) {
+            const float* nb = nst + (bh * (nc - 1) + kc - 1) * (size_t)DQK;
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) {
+                const int c = 16 * kq + 8 * hh;
+                f32x4 nv[2];
+                load_gates8(nb + c, nv);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qn += frag_get(qf[kq], e) * nv[e >> 2][e & 3];
+            }
+            qn += __shfl_xor(qn, 32, 64);
+        }
+        const float den = rsum + exp2_fast(at2) * qn;
+        fac = scale / fmaxf(fabsf(den * scale), exp2_fast(lbp[bh * (size_t)T_ + tqc] * kLog2e));
+    }
+    // the factor of accumulator row rr (held by lane rr in the S^T layout)
+    auto row_fac = [&](int rr) { return GATE == kExp ? __shfl(fac, rr, 64) : scale; };
     if (OUTDECAY) {
         // out of the frame: e^{a_t - a_fref}, t within 31 steps before fref
 #pragma unroll
@@ -564,8 +596,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
-            os[rr][i32] = from_float<T>(acc[2 * ph][r] * scale);
-            os[rr][32 + i32] = from_float<T>(acc[2 * ph + 1][r] * scale);
+            const float fr = row_fac(rr);
+            os[rr][i32] = from_float<T>(acc[2 * ph][r] * fr);
+            os[rr][32 + i32] = from_float<T>(acc[2 * ph + 1][r] * fr);
         }
         __syncthreads();
 #pragma unroll
@@ -671,7 +704,8 @@ hipError_t launch_intra_t(const Problem& p, const void* q, const void* k, const 
     intra_kernel<T, GATE, DQK, BV, NW, MODE><<<blocks, 64 * NW, 0, stream>>>(
         static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), ws.a, ws.li, fg,
         static_cast<const std::conditional_t<(MODE & kStateF32) != 0, float, T>*>(ws.states), static_cast<T*>(h), p.H, p.T, p.dhv, p.L, p.nc, ws.c0 != nullptr, scale,
-        static_cast<const T*>(ws.dot_partner), ws.dots, static_cast<T*>(ws.p_out), static_cast<const T*>(ws.p_in));
+        static_cast<const T*>(ws.dot_partner), ws.dots, static_cast<T*>(ws.p_out), static_cast<const T*>(ws.p_in),
+        ws.lb, ws.nst);
     return hipGetLastError();
 }
 
@@ -756,6 +790,10 @@ hipError_t dispatch_gate(const Problem& p, const void* q, const void* k, const v
     switch (p.gate) {
     case kSig: return dispatch_dqk<T, kSig, MODE>(p, q, k, v, fg, ws, h, scale, stream);
     case kScalar: return dispatch_dqk<T, kScalar, MODE>(p, q, k, v, fg, ws, h, scale, stream);
+    case kExp:
+        // mLSTMexp has a forward pass only
+        if constexpr (MODE == 0 || MODE == kStateF32) return dispatch_dqk<T, kExp, MODE>(p, q, k, v, fg, ws, h, scale, stream);
+        return hipErrorInvalidValue;
     default:
         if constexpr ((MODE & (kEmitP | kGivenP)) == 0) return dispatch_dqk<T, kGla, MODE>(p, q, k, v, fg, ws, h, scale, stream);
         return hipErrorInvalidValue;

@@ -71,7 +71,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
                                                                 const float* __restrict__ li,
                                                                 const float* __restrict__ fg,
                                                                 const S* __restrict__ states, T* __restrict__ h,
-                                                                int H, int T_, int dhv, int nc, int c0, float scale)
+                                                                int H, int T_, int dhv, int nc, int c0, float scale,
+                                                                const float* __restrict__ lbp,
+                                                                const float* __restrict__ nst)
 {
     constexpr int NTH = 64 * NW, BQ = 32 * NW, BV = kSweepBV, NT = BV / 32, KQ = DQK / 16;
     constexpr int CW = sweep_cw<DQK>(), NKV = BQ / 64;
@@ -108,8 +110,8 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
     const T* qb = q + bh * (size_t)T_ * DQK;
     const T* kb = k + bh * (size_t)T_ * DQK;
     const T* vb = v + bh * (size_t)T_ * dhv;
-    const float* ab = (GATE == kSig) ? a + bh * (size_t)T_ : (GATE == kGla) ? a + bh * (size_t)T_ * DQK : nullptr;
-    const float* lb = (GATE == kSig) ? li + bh * (size_t)T_ : nullptr;
+    const float* ab = per_step_li(GATE) ? a + bh * (size_t)T_ : (GATE == kGla) ? a + bh * (size_t)T_ * DQK : nullptr;
+    const float* lb = per_step_li(GATE) ? li + bh * (size_t)T_ : nullptr;
     float lg2 = 0.0f;   // log2 of the fixed decay
     if (GATE == kScalar) lg2 = fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor) * kLog2e;
 
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
             const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
             pk[u].load(kb + (size_t)row(min(s0 + r, T_ - 1)) * DQK + c);
         }
-        if (GATE == kSig && tid < 64) {
+        if (per_step_li(GATE) && tid < 64) {
             const int s = min(s0 + tid, T_ - 1);
             pli = lb[s];
             if (!REV) pa = ab[s];
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
             }
             pk[u].store(&sm.ks[r][c]);
         }
-        if (GATE == kSig && tid < 64) sm.bcol[tid] = (REV ? pli : pli - pa) * kLog2e;
+        if (per_step_li(GATE) && tid < 64) sm.bcol[tid] = (REV ? pli : pli - pa) * kLog2e;
     };
     auto fetch_c = [&](int v0, int cb) {
 #pragma unroll
@@ -230,7 +232,8 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
     bf16x8 (*const pw)[64] = &sm.p[wr * (wr + 1)];   // this wave's P blocks
 
     // ---------------- 1. P = decay o mask o S, once per chunk
-    const float at2 = (GATE == kSig) ? ab[tqc] * kLog2e : 0.0f;
+    const float at2 = per_step_li(GATE) ? ab[tqc] * kLog2e : 0.0f;
+    float rsum = 0.0f;   // mLSTMexp: this lane's part of the row sum of P (the normaliser)
     fetch_k(cs);
     for (int j = 0; j < NKV; ++j) {
         const int s0 = cs + 64 * j;
@@ -262,9 +265,13 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
             for (int r = 0; r < 16; ++r) {
                 const int sr = 8 * (r >> 2) + 4 * hh + (r & 3);
                 float p = st[r];
-                if (GATE == kSig) p *= exp2_fast(at2 + sm.bcol[32 * mt + sr]);
+                if (per_step_li(GATE)) p *= exp2_fast(at2 + sm.bcol[32 * mt + sr]);
                 else if (GATE == kScalar) p *= exp2_fast((float)(tlo + i32 - slo - sr) * lg2);
                 st[r] = (diag && sr > i32) ? 0.0f : p;
+            }
+            if constexpr (GATE == kExp) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) rsum += st[r];
             }
             // the accumulator, in its own order, is the A operand of P V
             const int m = (slo - cs) / 32;
@@ -279,6 +286,33 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
 
     // per-channel gate: the inter-chunk term takes q o e^{a_t}
     if (GATE == kGla && inter) load_q(-1);
+
+    // mLSTMexp: each row's factor scale / max(|scale den_t|, e^{lb_t}) with
+    // den_t = sum_s P_ts + e^{a'_t} q_t . n_{k-1} (the stabilised normaliser),
+    // formed in this lane (row tlo + i32) and handed to the accumulator
+    // layout (row_fac) where rows run along the registers
+    float fac = scale;
+    if constexpr (GATE == kExp) {
+        rsum += __shfl_xor(rsum, 32, 64);
+        float qn = 0.0f;
+        if (inter) {
+            const float* nb = nst + (bh * (nc - 1) + kc - 1) * (size_t)DQK;
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) {
+                const int c = 16 * kq + 8 * hh;
+                f32x4 nv[2];
+                nv[0] = *reinterpret_cast<const f32x4*>(nb + c);
+                nv[1] = *reinterpret_cast<const f32x4*>(nb + c + 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qn += frag_get(qf[kq], e) * nv[e >> 2][e & 3];
+            }
+            qn += __shfl_xor(qn, 32, 64);
+        }
+        const float den = rsum + exp2_fast(at2) * qn;
+        fac = scale / fmaxf(fabsf(den * scale), exp2_fast(lbp[bh * (size_t)T_ + tqc] * kLog2e));
+    }
+    // the factor of accumulator row rr (held by lane rr in the S^T layout)
+    auto row_fac = [&](int rr) { return GATE == kExp ? __shfl(fac, rr, 64) : scale; };
 
     // ---------------- 2. every value tile
     T* const hbase = h + bh * (size_t)T_ * dhv;
@@ -309,7 +343,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int t = min(tlo + 8 * (r >> 2) + 4 * hh + (r & 3), T_ - 1);
-                    const float e = (GATE == kSig) ? exp2_fast(ab[t] * kLog2e)
+                    const float e = per_step_li(GATE) ? exp2_fast(ab[t] * kLog2e)
                                                    : exp2_fast((float)(t - cs + (REV ? 0 : 1)) * lg2);
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= e;
@@ -351,8 +385,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
-                os[rr][i32] = from_float<T>(acc[2 * ph][r] * scale);
-                os[rr][32 + i32] = from_float<T>(acc[2 * ph + 1][r] * scale);
+                const float fr = row_fac(rr);
+                os[rr][i32] = from_float<T>(acc[2 * ph][r] * fr);
+                os[rr][32 + i32] = from_float<T>(acc[2 * ph + 1][r] * fr);
             }
             __syncthreads();
 #pragma unroll
@@ -380,7 +415,8 @@ hipError_t launch_sweep_t(const Problem& p, const void* q, const void* k, const 
     const long blocks = (long)p.B * p.H * p.nc;
     intra_kernel_sweep<bf16, GATE, DQK, NW, S, REV><<<(unsigned)blocks, 64 * NW, 0, stream>>>(
         static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v), ws.a, ws.li, fg,
-        static_cast<const S*>(ws.states), static_cast<bf16*>(h), p.H, p.T, p.dhv, p.nc, ws.c0 != nullptr, scale);
+        static_cast<const S*>(ws.states), static_cast<bf16*>(h), p.H, p.T, p.dhv, p.nc, ws.c0 != nullptr, scale,
+        ws.lb, ws.nst);
     return hipGetLastError();
 }
 
@@ -418,6 +454,10 @@ hipError_t sweep_gate(const Problem& p, const void* q, const void* k, const void
 {
     if (p.gate == kSig) return sweep_dqk<S, kSig, REV>(p, q, k, v, fg, ws, h, scale, stream);
     if (p.gate == kScalar) return sweep_dqk<S, kScalar, REV>(p, q, k, v, fg, ws, h, scale, stream);
+    if (p.gate == kExp) {
+        if constexpr (!REV) return sweep_dqk<S, kExp, REV>(p, q, k, v, fg, ws, h, scale, stream);
+        return hipErrorInvalidValue;
+    }
     return sweep_dqk<S, kGla, REV>(p, q, k, v, fg, ws, h, scale, stream);
 }
 

@@ -6,7 +6,11 @@
 
 namespace tfla {
 
-enum GateKind { kSig = 0, kScalar = 1, kGla = 2 };
+enum GateKind { kSig = 0, kScalar = 1, kGla = 2, kExp = 3 };
+
+// mLSTMsig and mLSTMexp share the per-step exponents of the chunkwise form
+// (mLSTMexp's are stabilised by its max state; see gates_exp.hip)
+constexpr bool per_step_li(int gate) { return gate == kSig || gate == kExp; }
 
 // Test and tuning overrides set through tfla_dbg_set_knob (tfla.h knob
 // numbers); -1 when unset, which every reader takes as "the default".  The
@@ -36,6 +40,13 @@ struct Workspace {
                      // intra-chunk kernel rounds them to the I/O type for its
                      // matrix cores anyway)
                      // 1..nc-1 (ns = nc-1), or 0..nc-1 with an initial state (ns = nc)
+    // mLSTMexp (kExp): a, li and g hold its stabilised exponents (the
+    // mLSTMsig kernels then form the stabilised numerator), plus
+    float* lb = nullptr;      // [B,H,T] log of the lower bound of the normaliser, -(a_t + M_t)
+    float* nst = nullptr;     // [B,H,nc-1,dqk] stabilised normaliser state before chunks 1..nc-1
+    float* npart = nullptr;   // [B,H,nc,dqk] each chunk's own normaliser contribution
+    float* mprev = nullptr;   // [B,H,nc] max state entering each chunk
+    float* uk = nullptr;      // [B,H,nc] chunk maximum of igate_pre - a
     const float* c0 = nullptr;   // caller's initial state [B,H,dqk,dhv] (NULL: zero)
     float* c_final = nullptr;    // caller's final-state output [B,H,dqk,dhv] (NULL: none)
     float* seg_end = nullptr;    // segmented state walk: end states [B*H][P][dqk][dhv]
@@ -79,6 +90,11 @@ size_t workspace_layout(const Problem& p, Workspace* ws, char* base, bool with_s
 
 hipError_t launch_gates(const Problem& p, const float* igate_pre, const float* fgate_pre,
                         const Workspace& ws, hipStream_t stream);
+// mLSTMexp's gate work (gates_exp.hip): fills ws.a, ws.li, ws.g with its
+// stabilised exponents and ws.lb, ws.nst (ws.npart, ws.mprev, ws.uk as
+// scratch); k is read for the normaliser.
+hipError_t launch_gates_exp(const Problem& p, const void* k, const float* igate_pre, const float* fgate_pre,
+                            const Workspace& ws, hipStream_t stream);
 hipError_t launch_gates_closed_form(const Problem& p, const float* fgate_pre, float* a, float* li,
                                     float* g, hipStream_t stream);
 hipError_t launch_state(const Problem& p, const void* k, const void* v, const float* fgate_pre,

@@ -628,9 +628,12 @@ int state_chunks_per_segment(const Problem& p, int P)
     return (nfeed + P - 1) / P;
 }
 
-hipError_t launch_state(const Problem& p, const void* k, const void* v, const float* fgate_pre,
+hipError_t launch_state(const Problem& pin, const void* k, const void* v, const float* fgate_pre,
                         const Workspace& ws, hipStream_t stream)
 {
+    // mLSTMexp: the mLSTMsig walk over its stabilised exponents (gates_exp.hip)
+    Problem p = pin;
+    if (p.gate == kExp) p.gate = kSig;
     if (p.bf16)
         return launch_state_t<bf16, false>(p, static_cast<const bf16*>(k), static_cast<const bf16*>(v), fgate_pre,
                                            ws, stream);

@@ -42,7 +42,7 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 int check_problem(int B, int H, int T, int d_qk, int d_hv, int L, int variant, tfla::Problem* p)
 {
     const int gate = variant & 0xff;
-    if ((variant & ~(0xff | TFLA_IO_BF16 | TFLA_STATES_FP32)) != 0 || gate > TFLA_GLA_KEY || gate < 0)
+    if ((variant & ~(0xff | TFLA_IO_BF16 | TFLA_STATES_FP32)) != 0 || gate > TFLA_MLSTM_EXP || gate < 0)
         return fail(TFLA_ERR_INVALID_ARG, "unknown variant " + std::to_string(variant));
     if (B < 1 || H < 1 || T < 1 || d_qk < 1 || d_hv < 1 || L < 1)
         return fail(TFLA_ERR_INVALID_ARG, "B, H, T, d_qk, d_hv and L must be >= 1");
@@ -78,8 +78,8 @@ int check_gates(const tfla::Problem& p, const float* igate_pre, const float* fga
 {
     if (!fgate_pre) return fail(TFLA_ERR_INVALID_ARG, "fgate_pre is NULL");
     if (!aligned(fgate_pre, 4)) return fail(TFLA_ERR_INVALID_ARG, "fgate_pre is not 4-byte aligned");
-    if (p.gate == tfla::kSig) {
-        if (!igate_pre) return fail(TFLA_ERR_INVALID_ARG, "igate_pre is NULL but the variant is mLSTMsig");
+    if (tfla::per_step_li(p.gate)) {
+        if (!igate_pre) return fail(TFLA_ERR_INVALID_ARG, "igate_pre is NULL but the variant has an input gate");
         if (!aligned(igate_pre, 4)) return fail(TFLA_ERR_INVALID_ARG, "igate_pre is not 4-byte aligned");
     } else if (igate_pre) {
         return fail(TFLA_ERR_INVALID_ARG, "igate_pre must be NULL for this variant (input gate is 1)");
@@ -90,7 +90,7 @@ int check_gates(const tfla::Problem& p, const float* igate_pre, const float* fga
 size_t gate_bytes(const tfla::Problem& p)
 {
     const size_t bh = (size_t)p.B * p.H;
-    if (p.gate == tfla::kSig) return bh * p.T * 4;
+    if (tfla::per_step_li(p.gate)) return bh * p.T * 4;
     if (p.gate == tfla::kScalar) return (size_t)p.H * 4;
     return bh * p.T * p.dqk * 4;
 }
@@ -224,7 +224,8 @@ int run_path(const tfla::Problem& p, const void* q, const void* k, const void* v
 {
     int rc = mark(marks, 0, stream);
     if (rc) return rc;
-    hipError_t e = tfla::launch_gates(p, igate_pre, fgate_pre, ws, stream);
+    hipError_t e = p.gate == tfla::kExp ? tfla::launch_gates_exp(p, k, igate_pre, fgate_pre, ws, stream)
+                                        : tfla::launch_gates(p, igate_pre, fgate_pre, ws, stream);
     if (e != hipSuccess) return hip_fail(e, "gate kernel launch");
     if ((rc = mark(marks, 1, stream))) return rc;
     e = tfla::launch_state(p, k, v, fgate_pre, ws, stream);
@@ -321,6 +322,7 @@ int check_bwd_problem(int B, int H, int T, int d_qk, int d_hv, int L, int varian
         return fail(TFLA_ERR_UNSUPPORTED, "TFLA_STATES_FP32 is an option of the forward calls only");
     int rc = check_problem(B, H, T, d_qk, d_hv, L, variant & ~TFLA_BWD_REUSE_FWD, p);
     if (rc) return rc;
+    if (p->gate == tfla::kExp) return fail(TFLA_ERR_UNSUPPORTED, "mLSTMexp has a forward pass only (no backward)");
     if (!(d_hv == 64 || d_hv == 128 || (p->bf16 && (d_hv == 256 || d_hv == 512))))
         return fail(TFLA_ERR_UNSUPPORTED, "backward: d_hv must be 64, 128, 256 or 512 (fp32 I/O: 64 or 128), got " +
                                               std::to_string(d_hv));
@@ -562,8 +564,15 @@ size_t workspace_layout(const Problem& p, Workspace* ws, char* base, bool with_s
         return ptr;
     };
     ws->a = p.gate == kScalar ? nullptr : take(bh * p.T * w * 4);
-    ws->li = p.gate == kSig ? take(bh * p.T * 4) : nullptr;
+    ws->li = per_step_li(p.gate) ? take(bh * p.T * 4) : nullptr;
     ws->g = p.gate == kScalar ? nullptr : take(bh * p.nc * w * 4);
+    if (p.gate == kExp) {
+        ws->lb = take(bh * p.T * 4);
+        ws->npart = take(bh * p.nc * p.dqk * 4);
+        ws->nst = p.nc > 1 ? take(bh * (p.nc - 1) * p.dqk * 4) : nullptr;
+        ws->mprev = take(bh * p.nc * 4);
+        ws->uk = take(bh * p.nc * 4);
+    }
     const size_t slots = p.nc - 1 + (with_c0 ? 1 : 0);
     ws->states = (with_states && slots > 0) ? take(bh * slots * p.dhv * p.dqk * (p.st32 ? 4 : 2)) : nullptr;
     const int P = state_segments(p);
@@ -673,6 +682,7 @@ size_t tfla_state_workspace_bytes(int B, int H, int T, int d_qk, int d_hv, int L
 {
     tfla::Problem p;
     if (check_problem(B, H, T, d_qk, d_hv, L, variant, &p) != TFLA_OK) return 0;
+    if (p.gate == tfla::kExp) return 0;
     tfla::Workspace ws;
     return tfla::workspace_layout(p, &ws, nullptr, true, true);
 }
@@ -685,6 +695,8 @@ int tfla_fwd_state(const void* q, const void* k, const void* v, const float* iga
     int rc = check_fwd(q, k, v, igate_pre, fgate_pre, h, B, H, T, d_qk, d_hv, L, variant, &p);
     if (rc) return rc;
     if ((rc = check_state_io(p, q, k, v, igate_pre, fgate_pre, h, c0, c_final))) return rc;
+    if (p.gate == tfla::kExp)
+        return fail(TFLA_ERR_UNSUPPORTED, "mLSTMexp has no state input or output (use tfla_fwd)");
     tfla::Workspace ws;
     const bool with_c0 = c0 != nullptr;
     const size_t need = tfla::workspace_layout(p, &ws, nullptr, true, with_c0);
@@ -729,6 +741,7 @@ int tfla_fwd_recurrent(const void* q, const void* k, const void* v, const float*
     // the chunk size plays no part here; any valid one passes the shared checks
     int rc = check_fwd(q, k, v, igate_pre, fgate_pre, h, B, H, T, d_qk, d_hv, 64, variant, &p);
     if (rc) return rc;
+    if (p.gate == tfla::kExp) return fail(TFLA_ERR_UNSUPPORTED, "mLSTMexp has no step-by-step form here");
     if (!state) return fail(TFLA_ERR_INVALID_ARG, "state must not be NULL");
     if ((rc = check_state_io(p, q, k, v, igate_pre, fgate_pre, h, state, nullptr))) return rc;
     hipError_t e = tfla::launch_recurrent(p, q, k, v, igate_pre, fgate_pre, state, h, static_cast<hipStream_t>(stream));
@@ -741,6 +754,7 @@ int tfla_dbg_gates(const float* igate_pre, const float* fgate_pre, float* a_out,
     tfla::Problem p;
     int rc = check_problem(B, H, T, d_qk, 64, L, variant, &p);
     if (rc) return rc;
+    if (p.gate == tfla::kExp) return fail(TFLA_ERR_UNSUPPORTED, "tfla_dbg_gates: not for mLSTMexp");
     rc = check_gates(p, igate_pre, fgate_pre);
     if (rc) return rc;
     if (!a_out || !li_out || !g_out) return fail(TFLA_ERR_INVALID_ARG, "a_out, li_out and g_out must not be NULL");
@@ -766,6 +780,7 @@ int tfla_dbg_states(const void* k, const void* v, const float* igate_pre, const 
     tfla::Problem p;
     int rc = check_problem(B, H, T, d_qk, d_hv, L, variant, &p);
     if (rc) return rc;
+    if (p.gate == tfla::kExp) return fail(TFLA_ERR_UNSUPPORTED, "tfla_dbg_states: not for mLSTMexp");
     rc = check_gates(p, igate_pre, fgate_pre);
     if (rc) return rc;
     if (!k || !v || !aligned(k, 16) || !aligned(v, 16))

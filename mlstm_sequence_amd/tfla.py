@@ -15,6 +15,7 @@ import torch  # loaded first: libtfla then shares torch's HIP runtime (same SONA
 MLSTM_SIG = 0
 SCALAR_DECAY = 1
 GLA_KEY = 2
+MLSTM_EXP = 3   # mLSTMexp: exponential input gate, normaliser and max state (forward only)
 IO_BF16 = 0x100
 BWD_REUSE_FWD = 0x200
 STATES_FP32 = 0x400   # forward, bf16 I/O: materialise the chunk states in fp32
@@ -178,7 +179,7 @@ def _check_device(dev):
 
 def _check_gates(igate_pre, fgate_pre, B, H, T, d_qk, variant, dev, ig_name="igate_pre", fg_name="fgate_pre"):
     gate = variant & 0xFF
-    if gate == MLSTM_SIG:
+    if gate in (MLSTM_SIG, MLSTM_EXP):
         if igate_pre is None:
             raise ValueError(f"{ig_name} is required for mLSTMsig")
         dev = _expect(igate_pre, ig_name, (B, H, T), torch.float32, dev)

@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "tfla.h")
 tfla = pytest.importorskip("mlstm_sequence_amd.tfla")
 
 BF16 = 0x100
-SIG, SCALAR, GLA = 0, 1, 2
+SIG, SCALAR, GLA, EXP = 0, 1, 2, 3
 INVALID, UNSUPPORTED, OOM = 1, 2, 4
 
 # 16-byte aligned fake device addresses: validation never dereferences them
@@ -55,11 +55,12 @@ def fwd(q=Q, k=K, v=V, ig=IG, fg=FG, h=H_, B=2, H=3, T=300, dqk=128, dhv=256, Lc
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(variant=3), INVALID), (dict(variant=0x200), INVALID), (dict(variant=-1), INVALID),
+    (dict(variant=4), INVALID), (dict(variant=0x200), INVALID), (dict(variant=-1), INVALID),
     (dict(B=0), INVALID), (dict(T=0), INVALID), (dict(H=-2), INVALID),
     (dict(q=None), INVALID), (dict(h=None), INVALID), (dict(fg=None), INVALID),
     (dict(q=Q + 8), INVALID), (dict(h=H_ + 2), INVALID), (dict(fg=FG + 2), INVALID),
     (dict(ig=None), INVALID),                                   # mLSTMsig needs an input gate
+    (dict(ig=None, variant=EXP | BF16), INVALID),               # ... and so does mLSTMexp
     (dict(variant=SCALAR | BF16), INVALID),                     # ... the others must not have one
     (dict(h=Q + 64), INVALID), (dict(h=V - 32), INVALID),       # output overlaps an input
     (dict(dqk=96), UNSUPPORTED), (dict(dqk=512), UNSUPPORTED), (dict(dhv=100), UNSUPPORTED),
@@ -396,3 +397,26 @@ def test_noalloc_rejects_oversized_problems_before_any_hip_call(L):
     assert rc == OOM
     assert "scratch" in tfla.tfla_last_error()
     assert L.tfla_fwd_noalloc(Q, K, V, IG, FG, H_, 4, 8, 8192, 96, 512, 64, var, None) == UNSUPPORTED
+
+
+
+def test_mlstm_exp_is_forward_only(L):
+    """mLSTMexp has tfla_fwd / _ws / _noalloc only: the state-I/O, step-by-step
+    and backward entry points and the test hooks reject it before any HIP
+    call; its forward workspace holds the stabilised exponents, the lower
+    bounds, the max-state chain and the normaliser states."""
+    var = EXP | BF16
+    B, H, T, dqk, dhv, Lc = 2, 3, 300, 128, 256, 64
+    assert L.tfla_fwd_state(Q, K, V, IG, FG, None, H_, None, B, H, T, dqk, dhv, Lc, var, None, 0, None) == UNSUPPORTED
+    assert "mLSTMexp" in tfla.tfla_last_error()
+    assert L.tfla_fwd_recurrent(Q, K, V, IG, FG, C0, H_, B, H, T, dqk, dhv, var, None) == UNSUPPORTED
+    assert L.tfla_bwd(Q, K, V, IG, FG, H_, WS, C0, CF, IG, FG, B, H, T, dqk, dhv, Lc, var, None, 0, None) == UNSUPPORTED
+    assert tfla.tfla_bwd_workspace_bytes(B, H, T, dqk, dhv, Lc, var) == 0
+    assert tfla.tfla_state_workspace_bytes(B, H, T, dqk, dhv, Lc, var) == 0
+    assert L.tfla_dbg_gates(IG, FG, WS, C0, CF, B, H, T, dqk, Lc, var, None) == UNSUPPORTED
+    assert L.tfla_dbg_states(K, V, IG, FG, WS, B, H, T, dqk, dhv, Lc, var, None) == UNSUPPORTED
+    a256 = lambda n: (n + 255) // 256 * 256
+    nc = -(-T // Lc)
+    sig = tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16)
+    extra = a256(B * H * T * 4) + a256(B * H * nc * dqk * 4) + a256(B * H * (nc - 1) * dqk * 4) + 2 * a256(B * H * nc * 4)
+    assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, var) == sig + extra
