@@ -60,15 +60,23 @@ def kernel_model(wl, L):
     st_bytes = e * dqk * dhv * (len(n) - 1)   # states are stored in the I/O type
     # per-step gate sums read by the consumers: a and li (mLSTMsig), a per
     # key channel (GLA), none for the closed-form fixed decay
-    gstep = {0: 8, 1: 0, 2: 4 * dqk}[wl.variant]
-    gchunk = {0: 4, 1: 0, 2: 4 * dqk}[wl.variant] * len(n)
-    gin = {0: 8, 1: 0, 2: 4 * dqk}[wl.variant] * T
+    gstep = {0: 8, 1: 0, 2: 4 * dqk, 3: 8}[wl.variant]
+    gchunk = {0: 4, 1: 0, 2: 4 * dqk, 3: 4}[wl.variant] * len(n)
+    gin = {0: 8, 1: 0, 2: 4 * dqk, 3: 8}[wl.variant] * T
     gates = {"flops": 0, "bytes": bh * (gin + gstep * T + gchunk)}
+    if wl.variant == 3:
+        # mLSTMexp's four gate launches: a and the prefix maxima written, read
+        # back with igate_pre and rewritten with the lower bound (+ 8 + 12 + 12
+        # B per step), k read once for the normaliser contributions, which are
+        # written, read and turned into normaliser states (3 x 4 d_qk B per chunk)
+        gates["bytes"] += bh * (T * (32 + dqk * e) + 3 * 4 * dqk * len(n))
     state = {"flops": bh * 2 * dqk * dhv * steps_state,
              "bytes": bh * ((dqk + dhv) * e * steps_state + gstep * steps_state + gchunk + st_bytes)}
     intra_f = 2 * dqk * dhv * steps_inter + sum(m * (m + 1) * (dqk + dhv) for m in n)
+    # mLSTMexp also reads its lower bound per step and the normaliser state per chunk
+    exp_extra = (4 * T + 4 * dqk * (len(n) - 1)) if wl.variant == 3 else 0
     intra = {"flops": bh * intra_f,
-             "bytes": bh * ((2 * dqk + dhv) * e * T + dhv * e * T + st_bytes + gstep * T)}
+             "bytes": bh * ((2 * dqk + dhv) * e * T + dhv * e * T + st_bytes + gstep * T + exp_extra)}
     return {"gates": gates, "state": state, "intra": intra}
 
 
@@ -109,7 +117,7 @@ def run_gpu(wl, L, steps, warmup, inputs_dev, cold_calls=0, flags=0, keep_h=Fals
 
     q, k, v = inputs_dev["q"], inputs_dev["k"], inputs_dev["v"]
     ig, fg = inputs_dev["igate_pre"], inputs_dev["fgate_pre"]
-    gate = {0: tfla.MLSTM_SIG, 1: tfla.SCALAR_DECAY, 2: tfla.GLA_KEY}[wl.variant]
+    gate = {0: tfla.MLSTM_SIG, 1: tfla.SCALAR_DECAY, 2: tfla.GLA_KEY, 3: tfla.MLSTM_EXP}[wl.variant]
     var = tfla.variant_of(gate, q.dtype) | flags
     h = torch.empty((wl.B, wl.H, wl.T, wl.dhv), dtype=q.dtype, device=q.device)
     nbytes = tfla.tfla_workspace_bytes(wl.B, wl.H, wl.T, wl.dqk, wl.dhv, L, var)
@@ -191,7 +199,7 @@ def run_gpu_bwd(wl, L, steps, warmup, inputs_dev, dh):
 
     q, k, v = inputs_dev["q"], inputs_dev["k"], inputs_dev["v"]
     ig, fg = inputs_dev["igate_pre"], inputs_dev["fgate_pre"]
-    gate = {0: tfla.MLSTM_SIG, 1: tfla.SCALAR_DECAY, 2: tfla.GLA_KEY}[wl.variant]
+    gate = {0: tfla.MLSTM_SIG, 1: tfla.SCALAR_DECAY, 2: tfla.GLA_KEY, 3: tfla.MLSTM_EXP}[wl.variant]
     var = tfla.variant_of(gate, q.dtype)
     nws = tfla.tfla_bwd_workspace_bytes(wl.B, wl.H, wl.T, wl.dqk, wl.dhv, L, var)
     ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=q.device)
@@ -239,7 +247,7 @@ def run_gpu_decode(wl, steps_per_call, calls, warmup):
     sub = wl.with_(T=steps_per_call)
     inp = W.make_inputs(sub)
     d = {n: (None if t is None else t.cuda()) for n, t in inp.items()}
-    gate = {0: tfla.MLSTM_SIG, 1: tfla.SCALAR_DECAY, 2: tfla.GLA_KEY}[wl.variant]
+    gate = {0: tfla.MLSTM_SIG, 1: tfla.SCALAR_DECAY, 2: tfla.GLA_KEY, 3: tfla.MLSTM_EXP}[wl.variant]
     var = tfla.variant_of(gate, d["q"].dtype)
     state = W.initial_state(wl.B, wl.H, wl.dqk, wl.dhv, seed=wl.seed + 2).cuda()
     h = torch.empty_like(d["v"])
@@ -265,6 +273,69 @@ def run_gpu_decode(wl, steps_per_call, calls, warmup):
     return {"steps_per_call": steps_per_call, "us_per_call": us, "tokens_per_s": wl.B * steps_per_call / (us * 1e-6),
             "hbm_bytes_per_call": nbytes, "achieved_GBps": nbytes / (us * 1e-6) / 1e9,
             "hbm_frac": nbytes / (us * 1e-6) / PEAK_HBM}
+
+
+def roofline_for(wl, L, per):
+    """The dominant kernel's (longest average duration) algorithmic bytes or
+    flops per launch over its measured duration, against the HBM peak when
+    its arithmetic intensity is below the bf16 matrix-core ridge, else
+    against the matrix-core peak of the I/O type."""
+    model = kernel_model(wl, L)
+    dom = max(("gates", "state", "intra"), key=lambda k: per[k])
+    dm = model[dom]
+    dt = per[dom] * 1e-3
+    peak_f = PEAK_BF16 if wl.dtype_name == "bf16" else PEAK_FP32
+    if dm["flops"] / peak_f > dm["bytes"] / PEAK_HBM:
+        roof = {"bound": "mfma", "achieved": dm["flops"] / dt / 1e12, "peak": peak_f / 1e12, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": dm["bytes"] / dt / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_for(dom, wl, L)
+    roof.update({"kernel": dom, "ms_per_launch": per[dom], "algorithmic_bytes": dm["bytes"],
+                 "algorithmic_flops": dm["flops"]})
+    return roof
+
+
+def gpu_clocks():
+    """Current shader and memory clocks of GPU 0 as rocm-smi reports them
+    (None where the tool is missing or prints nothing parseable)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        data = json.loads(r.stdout)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    card = next((v for k, v in data.items() if k.startswith("card")), None)
+    if not isinstance(card, dict):
+        return None
+    pick = lambda key: next((v for k, v in card.items() if key in k.lower()), None)
+    return {"sclk": pick("sclk"), "mclk": pick("mclk"), "fclk": pick("fclk")}
+
+
+def hbm_probe(nbytes=4 << 30, reps=10):
+    """The HBM rates plain streaming kernels reach on this device (torch's own
+    element-wise copy and sum-reduction kernels over a buffer 16x the 256 MB
+    last-level cache): the practical ceiling of an HBM-bound kernel, beside
+    the 8 TB/s of the specification."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    res = {"buffer_bytes": nbytes, "reps": reps}
+    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes), ("read", lambda: src.sum(), nbytes)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        rate = moved / (ms * 1e-3)
+        res[name] = {"ms": ms, "bytes": moved, "GBps": rate / 1e9, "frac_of_8TBps": rate / PEAK_HBM}
+    del src, dst
+    return res
 
 
 # --------------------------------------------------------------------------- CPU baseline
@@ -341,6 +412,10 @@ def main():
                     help="skip the timing with the states materialised in fp32 (TFLA_STATES_FP32)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (scales HBM byte counters)")
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="only measure the HBM rate of plain streaming kernels (copy, read) and print it")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other workloads' lines (default workload only)")
     args = ap.parse_args()
 
     if args.copy_calibration:
@@ -352,6 +427,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "dispatches": 3}), flush=True)
+        return
+
+    if args.hbm_probe:
+        print(json.dumps({"hbm_probe": hbm_probe()}), flush=True)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -378,6 +457,7 @@ def main():
     dev = {n: (None if t is None else t.cuda()) for n, t in inputs.items()}
     torch.cuda.synchronize()
 
+    clocks_before = gpu_clocks()
     results = {}
     for L in sweep:
         ms, wall_ms, per, cold, _ = run_gpu(wl, L, args.steps, args.warmup, dev, cold_calls=10)
@@ -393,21 +473,8 @@ def main():
     else:
         Lh = max((L for L in listed if L in results), key=lambda L: results[L]["tokens_per_s"])
     r = results[Lh]
-    model = kernel_model(wl, Lh)
-    dom = max(("gates", "state", "intra"), key=lambda k: r["per"][k])
-    dm = model[dom]
-    dt = r["per"][dom] * 1e-3
-    peak_f = PEAK_BF16 if wl.dtype_name == "bf16" else PEAK_FP32
-    mfma_bound = dm["flops"] / peak_f > dm["bytes"] / PEAK_HBM
-    if mfma_bound:
-        roof = {"bound": "mfma", "achieved": dm["flops"] / dt / 1e12, "peak": peak_f / 1e12, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": dm["bytes"] / dt / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    tr = traffic_for(dom, wl, Lh)
-    roof["traffic"] = tr
-    roof.update({"kernel": dom, "ms_per_launch": r["per"][dom], "algorithmic_bytes": dm["bytes"],
-                 "algorithmic_flops": dm["flops"]})
+    roof = roofline_for(wl, Lh, r["per"])
+    clocks_after = gpu_clocks()
 
     out = {
         "metric": METRIC,
@@ -431,7 +498,38 @@ def main():
                            "mfma_frac": x["mfma_frac"], "kernels_ms": x["per"], "cold_cache": x["cold"]}
                   for L, x in results.items()},
         "cold_cache": r["cold"],
+        "gpu_clocks": {"before_sweep": clocks_before, "after_sweep": clocks_after},
     }
+    # mLSTMexp on the same inputs and launch (TFLA research-map summary, Key
+    # results: the mLSTMsig forward kernel is over 30% faster than
+    # mLSTMexp's on H100): the same state walk and intra-chunk products plus
+    # its max-state chain, normaliser and bound
+    if wl.variant == W.MLSTM_SIG and wl.dtype_name == "bf16":
+        wle = wl.with_(variant=W.MLSTM_EXP, name=wl.name.replace("mlstm_sig", "mlstm_exp"))
+        mse, _, pere, _, _ = run_gpu(wle, Lh, args.steps, args.warmup, dev)
+        out["mlstm_exp"] = {"L": Lh, "ms_per_step": mse, "tokens_per_s": wl.B * wl.T / (mse * 1e-3),
+                            "kernels_ms": pere, "mlstm_sig_ms_per_step": r["ms"],
+                            "sig_faster_by": mse / r["ms"] - 1.0}
+        log(f"mLSTMexp, L={Lh}: {mse:.3f} ms/step (gates {pere['gates']:.3f}, state {pere['state']:.3f}, "
+            f"intra {pere['intra']:.3f} ms); mLSTMsig faster by {100 * (mse / r['ms'] - 1):.1f}%")
+    # every other workload at its listed chunk sizes (parity cases of the
+    # tests; reported so each config has a driver-run record)
+    if args.config == 3 and not args.no_workloads:
+        others = {}
+        for c in (1, 2, 4, 5):
+            wlc = W.WORKLOADS[c]
+            devc = {n: (None if t is None else t.cuda()) for n, t in W.make_inputs(wlc).items()}
+            for L in wlc.chunk_sizes:
+                msc, _, perc, _, _ = run_gpu(wlc, L, args.steps, args.warmup, devc)
+                others[f"{wlc.name}:L{L}"] = {
+                    "config": c, "L": L, "B": wlc.B, "H": wlc.H, "T": wlc.T, "d_qk": wlc.dqk, "d_hv": wlc.dhv,
+                    "io": wlc.dtype_name, "ms_per_step": msc, "tokens_per_s": wlc.B * wlc.T / (msc * 1e-3),
+                    "mfma_frac": total_flops(wlc, L) / (msc * 1e-3) / PEAK_BF16, "kernels_ms": perc,
+                    "roofline": roofline_for(wlc, L, perc)}
+                log(f"{wlc.name} L={L}: {msc:.3f} ms/step, {wlc.B * wlc.T / (msc * 1e-3):.4g} tokens/s "
+                    f"(gates {perc['gates']:.3f}, state {perc['state']:.3f}, intra {perc['intra']:.3f} ms)")
+            del devc
+        out["workloads"] = others
     # The same step with the chunk states materialised in fp32 instead of the
     # I/O type (TFLA_STATES_FP32): identical h, twice the state bytes.
     if wl.dtype_name == "bf16" and not args.no_fp32_states:

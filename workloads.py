@@ -9,7 +9,7 @@ size-limit tests) are drawn the same way by a seeded generator on the GPU;
 the oracle then receives copies of the sampled heads.
 
 Draw order for every workload: q, k, v, then the input-gate pre-activation
-(mLSTMsig only), then the forget-gate pre-activation (per step, or per step
+(mLSTMsig and mLSTMexp), then the forget-gate pre-activation (per step, or per step
 and key channel for the per-channel gate).  The per-head scalar decay needs no
 draw: gamma_h = 1 - 2^-(5 + h/4) (the decay schedule of the RetNet-style
 multi-scale retention the flash-linear-attention README benchmarks), passed as
@@ -23,8 +23,8 @@ from dataclasses import dataclass, field, replace
 import numpy as np
 import torch
 
-MLSTM_SIG, SCALAR, GLA = 0, 1, 2
-VARIANT_NAMES = {MLSTM_SIG: "mlstm_sig", SCALAR: "scalar_decay", GLA: "gla_key"}
+MLSTM_SIG, SCALAR, GLA, MLSTM_EXP = 0, 1, 2, 3
+VARIANT_NAMES = {MLSTM_SIG: "mlstm_sig", SCALAR: "scalar_decay", GLA: "gla_key", MLSTM_EXP: "mlstm_exp"}
 
 
 @dataclass(frozen=True)
@@ -97,7 +97,7 @@ def make_inputs(w: Workload, seed: int | None = None, device="cpu") -> dict:
     q = normal((B, H, T, w.dqk), w.qkv_std).to(w.dtype)
     k = normal((B, H, T, w.dqk), w.qkv_std).to(w.dtype)
     v = normal((B, H, T, w.dhv), w.qkv_std).to(w.dtype)
-    if w.variant == MLSTM_SIG:
+    if w.variant in (MLSTM_SIG, MLSTM_EXP):
         ig = normal((B, H, T), 1.0, w.igate_mean)
         lo, hi = w.fgate_range
         fg = torch.rand((B, H, T), generator=g, dtype=torch.float32, device=device) * (hi - lo) + lo
