@@ -91,8 +91,8 @@ enum tfla_status {
  *              overwritten; must not overlap any input.
  *   B, H, T    >= 1.  T need not be a multiple of L (the last chunk may be
  *              partial).
- *   d_qk       64, 128 or 256          (fp32 I/O: 64 or 128)
- *   d_hv       a multiple of 64, <= 512 (fp32 I/O: <= 256)
+ *   d_qk       64, 128 or 256
+ *   d_hv       a multiple of 64, <= 512
  *   L          chunk size: 64, 128, 256, 512 or 1024
  *
  * Gate pre-activations may be +-inf (a gate of exactly 1 or 0).  The log
@@ -247,8 +247,8 @@ int tfla_fwd_recurrent(const void* q, const void* k, const void* v,
  *             since; the gate prefix sums and the states C_k found there are
  *             used as they are, skipping their recomputation.  Results are
  *             then bitwise those without the flag.
- *   d_qk      as for tfla_fwd; d_hv 64, 128, 256 or 512 (fp32 I/O: 64 or
- *             128), since the dq and dk products contract over it.
+ *   d_qk      as for tfla_fwd; d_hv 64, 128, 256 or 512, since the dq and
+ *             dk products contract over it.
  *   workspace caller-owned device workspace of at least
  *             tfla_bwd_workspace_bytes(...) bytes, 256-byte aligned and
  *             disjoint from every tensor argument, or NULL to let the call

@@ -773,10 +773,13 @@ hipError_t dispatch_dqk(const Problem& p, const void* q, const void* k, const vo
     case 64: return dispatch_bv<T, GATE, 64, MODE>(p, q, k, v, fg, ws, h, scale, stream);
     case 128: return dispatch_bv<T, GATE, 128, MODE>(p, q, k, v, fg, ws, h, scale, stream);
     case 256:
-        if constexpr (sizeof(T) == 2) return dispatch_bv<T, GATE, 256, MODE>(p, q, k, v, fg, ws, h, scale, stream);
-        return hipErrorInvalidValue;
+        // (fp32 I/O: 64-wide value tiles keep the 256-channel Q fragments
+        // within the registers of four waves)
+        return dispatch_bv<T, GATE, 256, MODE>(p, q, k, v, fg, ws, h, scale, stream);
     case 512:
-        if constexpr (sizeof(T) == 2 && MODE != 0 && MODE != kStateF32)
+        // (fp32 I/O: the 512 fp32 channels of the Q fragments fit four waves
+        // only where P is given; the backward pass shares P there)
+        if constexpr (MODE != 0 && MODE != kStateF32)
             return dispatch_bv<T, GATE, 512, MODE>(p, q, k, v, fg, ws, h, scale, stream);
         return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;

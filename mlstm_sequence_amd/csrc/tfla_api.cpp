@@ -47,12 +47,10 @@ int check_problem(int B, int H, int T, int d_qk, int d_hv, int L, int variant, t
     if (B < 1 || H < 1 || T < 1 || d_qk < 1 || d_hv < 1 || L < 1)
         return fail(TFLA_ERR_INVALID_ARG, "B, H, T, d_qk, d_hv and L must be >= 1");
     const bool bf16 = (variant & TFLA_IO_BF16) != 0;
-    if (!(d_qk == 64 || d_qk == 128 || (d_qk == 256 && bf16)))
-        return fail(TFLA_ERR_UNSUPPORTED, "d_qk must be 64, 128 or 256 (fp32 I/O: 64 or 128), got " +
-                                              std::to_string(d_qk));
-    if (d_hv % 64 != 0 || d_hv > (bf16 ? 512 : 256))
-        return fail(TFLA_ERR_UNSUPPORTED, "d_hv must be a multiple of 64 up to 512 (fp32 I/O: 256), got " +
-                                              std::to_string(d_hv));
+    if (!(d_qk == 64 || d_qk == 128 || d_qk == 256))
+        return fail(TFLA_ERR_UNSUPPORTED, "d_qk must be 64, 128 or 256, got " + std::to_string(d_qk));
+    if (d_hv % 64 != 0 || d_hv > 512)
+        return fail(TFLA_ERR_UNSUPPORTED, "d_hv must be a multiple of 64 up to 512, got " + std::to_string(d_hv));
     if (!(L == 64 || L == 128 || L == 256 || L == 512 || L == 1024))
         return fail(TFLA_ERR_UNSUPPORTED, "chunk size L must be 64, 128, 256, 512 or 1024, got " +
                                               std::to_string(L));
@@ -277,6 +275,10 @@ tfla::Problem grad_qk_problem(const tfla::Problem& p)
 bool shares_p(const tfla::Problem& p)
 {
     if (p.gate == tfla::kGla) return false;
+    // fp32 I/O, 256- or 512-wide contraction: the P pass holds no
+    // accumulators, and dq / dk given P hold no Q fragments, where forming
+    // P inside them would spill hundreds of registers
+    if (!p.bf16 && p.dhv >= 256) return true;
     const tfla::Problem pc = grad_qk_problem(p);
     return pc.dhv / tfla::intra_value_tile(pc) >= 2;
 }
@@ -323,9 +325,8 @@ int check_bwd_problem(int B, int H, int T, int d_qk, int d_hv, int L, int varian
     int rc = check_problem(B, H, T, d_qk, d_hv, L, variant & ~TFLA_BWD_REUSE_FWD, p);
     if (rc) return rc;
     if (p->gate == tfla::kExp) return fail(TFLA_ERR_UNSUPPORTED, "mLSTMexp has a forward pass only (no backward)");
-    if (!(d_hv == 64 || d_hv == 128 || (p->bf16 && (d_hv == 256 || d_hv == 512))))
-        return fail(TFLA_ERR_UNSUPPORTED, "backward: d_hv must be 64, 128, 256 or 512 (fp32 I/O: 64 or 128), got " +
-                                              std::to_string(d_hv));
+    if (!(d_hv == 64 || d_hv == 128 || d_hv == 256 || d_hv == 512))
+        return fail(TFLA_ERR_UNSUPPORTED, "backward: d_hv must be 64, 128, 256 or 512, got " + std::to_string(d_hv));
     return TFLA_OK;
 }
 

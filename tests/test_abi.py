@@ -65,8 +65,8 @@ def fwd(q=Q, k=K, v=V, ig=IG, fg=FG, h=H_, B=2, H=3, T=300, dqk=128, dhv=256, Lc
     (dict(h=Q + 64), INVALID), (dict(h=V - 32), INVALID),       # output overlaps an input
     (dict(dqk=96), UNSUPPORTED), (dict(dqk=512), UNSUPPORTED), (dict(dhv=100), UNSUPPORTED),
     (dict(dhv=576), UNSUPPORTED), (dict(Lc=32), UNSUPPORTED), (dict(Lc=96), UNSUPPORTED),
-    (dict(Lc=2048), UNSUPPORTED), (dict(variant=SIG, dqk=256), UNSUPPORTED),
-    (dict(variant=SIG, dhv=320), UNSUPPORTED), (dict(B=300, H=300), UNSUPPORTED),
+    (dict(Lc=2048), UNSUPPORTED), (dict(variant=SIG, dqk=512), UNSUPPORTED),
+    (dict(variant=SIG, dhv=576), UNSUPPORTED), (dict(B=300, H=300), UNSUPPORTED),
 ])
 def test_rejects_bad_arguments(L, kw, code):
     assert fwd(**kw) == code
@@ -186,7 +186,7 @@ def rec(state=C0, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(state=None), INVALID), (dict(state=C0 + 4), INVALID), (dict(state=H_), INVALID),
     (dict(state=V + 256), INVALID), (dict(T=0), INVALID), (dict(ig=None), INVALID),
-    (dict(dhv=100), UNSUPPORTED), (dict(dqk=256, variant=SIG), UNSUPPORTED),
+    (dict(dhv=100), UNSUPPORTED), (dict(dqk=512, variant=SIG), UNSUPPORTED),
 ])
 def test_recurrent_rejects_bad_arguments(L, kw, code):
     assert rec(**kw) == code
@@ -206,7 +206,7 @@ def bwd(q=Q, k=K, v=V, ig=IG, fg=FG, dh=DH, dq=DQ, dk=DK, dv=DV, dig=DIG, dfg=DF
 @pytest.mark.parametrize("kw,code", [
     (dict(variant=GLA | BF16), INVALID),                          # per-channel gate: no input gate
     (dict(dhv=192), UNSUPPORTED), (dict(dhv=320), UNSUPPORTED),   # d_hv is contracted: powers of two
-    (dict(variant=SIG, dhv=256), UNSUPPORTED),                    # fp32 I/O: d_hv <= 128
+    (dict(variant=SIG, dhv=384), UNSUPPORTED),                    # fp32 I/O too
     (dict(dqk=96), UNSUPPORTED), (dict(Lc=32), UNSUPPORTED),
     (dict(B=0), INVALID), (dict(variant=7), INVALID),
     (dict(variant=SIG | BF16 | 0x400), UNSUPPORTED),               # TFLA_STATES_FP32: forward calls only
