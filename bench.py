@@ -313,15 +313,20 @@ def gpu_clocks():
 
 
 def hbm_probe(nbytes=4 << 30, reps=10):
-    """The HBM rates plain streaming kernels reach on this device (torch's own
-    element-wise copy and sum-reduction kernels over a buffer 16x the 256 MB
-    last-level cache): the practical ceiling of an HBM-bound kernel, beside
-    the 8 TB/s of the specification."""
+    """The HBM rates plain streaming kernels reach on this device over a
+    buffer 16x the 256 MB last-level cache: the library's streaming probe
+    (tfla_dbg_stream: 16-byte loads, a given number in flight per thread,
+    a given number of 256-thread workgroups; the best of a small sweep) and
+    torch's own element-wise copy and sum reduction for comparison.  The
+    practical ceiling of an HBM-bound kernel, beside the 8 TB/s of the
+    specification."""
     import torch
+    from mlstm_sequence_amd import tfla
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
     res = {"buffer_bytes": nbytes, "reps": reps}
-    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes), ("read", lambda: src.sum(), nbytes)):
+
+    def timed(fn):
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
@@ -331,9 +336,28 @@ def hbm_probe(nbytes=4 << 30, reps=10):
             fn()
         e1.record()
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+        return e0.elapsed_time(e1) / reps
+
+    def entry(ms, moved, **kw):
         rate = moved / (ms * 1e-3)
-        res[name] = {"ms": ms, "bytes": moved, "GBps": rate / 1e9, "frac_of_8TBps": rate / PEAK_HBM}
+        return dict(kw, ms=ms, bytes=moved, GBps=rate / 1e9, frac_of_8TBps=rate / PEAK_HBM)
+
+    half = nbytes // 2
+    sweep = []
+    for loads in (4, 8, 16):
+        for wgs in (256, 512, 1024, 2048):
+            ms = timed(lambda: tfla.tfla_dbg_stream(0, src, dst, nbytes, loads, wgs))
+            sweep.append(entry(ms, nbytes, kind="read", loads_per_thread=loads, workgroups=wgs))
+    for loads in (1, 4, 8):
+        for wgs in (256, 1024):
+            # the first half of src copied to the first half of dst
+            ms = timed(lambda: tfla.tfla_dbg_stream(1, src, dst, half, loads, wgs))
+            sweep.append(entry(ms, 2 * half, kind="copy", loads_per_thread=loads, workgroups=wgs))
+    res["probe_sweep"] = sweep
+    res["probe_read_best"] = max((x for x in sweep if x["kind"] == "read"), key=lambda x: x["GBps"])
+    res["probe_copy_best"] = max((x for x in sweep if x["kind"] == "copy"), key=lambda x: x["GBps"])
+    res["torch_copy"] = entry(timed(lambda: dst.copy_(src)), 2 * nbytes)
+    res["torch_read"] = entry(timed(lambda: src.sum()), nbytes)
     del src, dst
     return res
 

@@ -325,6 +325,22 @@ int tfla_dbg_states(const void* k, const void* v,
                     int B, int H, int T, int d_qk, int d_hv, int L, int variant, void* stream);
 
 /*
+ * tfla_dbg_stream -- measurement aid, not part of the computation: a plain
+ * streaming kernel that measures the HBM rate a kernel on this device
+ * reaches.  mode 0 reads `bytes` of `src` (device) and folds them into one
+ * register per lane (`dst`: device scratch of at least 4 KB, written only
+ * in a case that does not occur); mode 1 copies `bytes` from `src` to `dst`
+ * (device, not overlapping).  `loads_per_thread` (1, 2, 4, 8 or 16)
+ * independent 16-byte loads per thread per round, `workgroups` (>= 1)
+ * workgroups of 256 threads striding over the buffer; both set the bytes a
+ * CU keeps in flight.  `bytes` a multiple of 16, pointers 16-byte aligned.
+ * Asynchronous on `stream`.  Returns TFLA_ERR_INVALID_ARG for arguments out
+ * of these ranges.
+ */
+int tfla_dbg_stream(int mode, const void* src, void* dst, size_t bytes, int loads_per_thread, int workgroups,
+                    void* stream);
+
+/*
  * tfla_dbg_set_knob -- test hook: process-wide overrides of choices the
  * library otherwise makes from the problem shape, for tests that must reach
  * a particular kernel at a small size and for tuning comparisons.  `value`
@@ -342,7 +358,10 @@ enum tfla_knob {
     TFLA_KNOB_STATE_SEGMENTS = 3,  /* n >= 1: the state walk's segment count                  */
     TFLA_KNOB_STATE_SB = 4,        /* 64 or 128: cap the state walk's block of steps          */
     TFLA_KNOB_FAULT_ALLOC = 5,     /* 1: the library's own workspace allocations fail         */
-    TFLA_KNOB_COUNT = 6
+    TFLA_KNOB_STATE_REWALK = 6,    /* 1: the forward segmented state walk walks every segment
+                                      again from its true start instead of fixing up the
+                                      states it stored (the fixed decay always does)          */
+    TFLA_KNOB_COUNT = 7
 };
 int tfla_dbg_set_knob(int knob, int value);
 

@@ -62,36 +62,62 @@ __global__ __launch_bounds__(64) void gates_sig_kernel(const float* __restrict__
     if (lane == 0) g[bh * nc + kc] = total;
 }
 
-// Per-key-channel gate: one thread per (chunk, head, channel), serial over
-// the chunk's steps; consecutive threads read consecutive channels.  The
-// loads of 16 steps are issued together (the running sum is the only serial
-// dependence), so the loop is not one memory latency per step.
+// Per-key-channel gate, one 256-thread workgroup per (chunk, head).  A
+// thread owns 4 consecutive channels (one 16-byte piece of a step's row) and
+// 16 consecutive steps: its 16 loads go out together (a wavefront's lanes
+// cover whole 1 KB rows of 256 channels), it forms log f for its 64 values
+// and their running sums over its steps, and the segment totals of the
+// threads before it on the same channels (through LDS) give the chunk-local
+// prefix.  256 threads cover 64 steps at d_qk = 256 (128 at 128, 256 at 64);
+// longer chunks take several passes, carrying the running total per channel.
+// log f on the transcendental unit (log_sigmoid_fast): with the library
+// calls the 64 evaluations per thread, not the loads, set the kernel's time.
 __global__ __launch_bounds__(256) void gates_gla_kernel(const float* __restrict__ x,
                                                         float* __restrict__ a, float* __restrict__ g,
                                                         int T, int dqk, int L, int nc)
 {
-    constexpr int U = 16;
+    constexpr int E = 16;                        // steps per thread
+    __shared__ f32x4 tot[256];                   // [segment][channel group] totals of a pass
+    __shared__ f32x4 carry[64];                  // running total per channel group
     const int kc = blockIdx.x;
     const size_t bh = blockIdx.y;
-    const int c = threadIdx.x;
-    if (c >= dqk) return;
+    const int tid = threadIdx.x;
+    const int ncg = dqk / 4;                     // channel groups (16-byte pieces per row)
+    const int nseg = 256 / ncg;                  // step segments per pass
+    const int cg = tid % ncg, seg = tid / ncg;
     const int t0 = kc * L;
     const int n = min(L, T - t0);
-    const size_t base = (bh * (size_t)T + t0) * dqk + c;
-    float run = 0.0f;
-    for (int p0 = 0; p0 < n; p0 += U) {
-        float xv[U];
+    const f32x4* xb = reinterpret_cast<const f32x4*>(x + (bh * (size_t)T + t0) * dqk) + cg;
+    f32x4* ab = reinterpret_cast<f32x4*>(a + (bh * (size_t)T + t0) * dqk) + cg;
+    if (tid < ncg) carry[tid] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int p0 = 0; p0 < n; p0 += nseg * E) {
+        const int s0 = p0 + seg * E;             // this thread's first step
+        f32x4 v[E];
 #pragma unroll
-        for (int u = 0; u < U; ++u) xv[u] = x[base + (size_t)min(p0 + u, n - 1) * dqk];
+        for (int e = 0; e < E; ++e) v[e] = xb[(size_t)min(s0 + e, n - 1) * ncg];
+        f32x4 run = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (p0 + u < n) {
-                run += fmaxf(log_sigmoid(xv[u]) * (1.0f / 16.0f), kLogForgetFloor);
-                a[base + (size_t)(p0 + u) * dqk] = run;
-            }
+        for (int e = 0; e < E; ++e) {
+            f32x4 lf;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                lf[c] = s0 + e < n ? fmaxf(log_sigmoid_fast(v[e][c]) * (1.0f / 16.0f), kLogForgetFloor) : 0.0f;
+            run += lf;
+            v[e] = run;
         }
+        tot[tid] = run;
+        __syncthreads();
+        // the totals of the earlier segments of this pass, and the carry
+        f32x4 off = carry[cg];
+        for (int j = 0; j < seg; ++j) off += tot[j * ncg + cg];
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (s0 + e < n) ab[(size_t)(s0 + e) * ncg] = v[e] + off;
+        __syncthreads();                         // every thread has read carry and tot
+        if (seg == nseg - 1) carry[cg] = off + run;
+        __syncthreads();
     }
-    g[(bh * nc + kc) * dqk + c] = run;
+    if (tid < ncg) reinterpret_cast<f32x4*>(g + (bh * nc + kc) * (size_t)dqk)[tid] = carry[tid];
 }
 
 // Fixed per-head decay: a_t = (t - t0 + 1) log(gamma_h) in closed form.

@@ -236,6 +236,23 @@ __device__ __forceinline__ float log_sigmoid(float x)
     return fminf(x, 0.0f) - log1pf(expf(-fabsf(x)));
 }
 
+// The same on the transcendental unit, for kernels that evaluate it per
+// element of large tensors: y = e^{-|x|} = 2^{-|x| log2 e} (v_exp_f32), and
+// log1p(y) by D. Goldberg, "What every computer scientist should know about
+// floating-point arithmetic" (1991), Theorem 4: with u = 1 + y rounded,
+// log1p(y) = y if u = 1, else ln(u) y / (u - 1) -- the rounding of u cancels
+// between ln(u) and u - 1, so small y keep their relative accuracy.  ln(u) =
+// log2(u) ln 2 (v_log_f32), 1 / (u - 1) by v_rcp_f32.  A few ulp against
+// the library calls.
+__device__ __forceinline__ float log_sigmoid_fast(float x)
+{
+    constexpr float kLn2 = 0.6931471805599453f;
+    const float y = exp2_fast(-fabsf(x) * kLog2e);
+    const float u = 1.0f + y;
+    const float l1p = u == 1.0f ? y : __builtin_amdgcn_logf(u) * kLn2 * (y * __builtin_amdgcn_rcpf(u - 1.0f));
+    return fminf(x, 0.0f) - l1p;
+}
+
 // Block index remap so that consecutive logical tiles land on one XCD:
 // the dispatcher places workgroup b on XCD b % 8, so logical tile
 // (b % 8) * (n / 8) + b / 8 keeps neighbours (which share K/V rows and

@@ -115,6 +115,12 @@ hipError_t launch_intra(const Problem& p, const void* q, const void* k, const vo
 // every value tile with it (launch_intra picks it where intra_sweeps holds).
 bool intra_sweeps(const Problem& p);
 bool intra_sweeps_dv(const Problem& p);   // the same for the dv product
+
+// plain streaming kernels (probe.hip): mode 0 reads `bytes` of src, mode 1
+// copies them to dst; `loads` 16-byte loads per thread per round (1, 2, 4, 8
+// or 16), `blocks` workgroups of 256 threads
+hipError_t launch_stream_probe(int mode, const void* src, void* dst, size_t bytes, int loads, int blocks,
+                               hipStream_t stream);
 hipError_t launch_intra_sweep(const Problem& p, const void* q, const void* k, const void* v,
                               const float* fgate_pre, const Workspace& ws, void* h, hipStream_t stream);
 // The same kernel in the dv gradient mode (mirrored chunks; see launch_intra_dv).

@@ -31,16 +31,34 @@
 //
 // Few heads and long sequences leave most CUs idle on that serial walk.
 // Then the chunk chain is cut into P segments (sequence parallelism on one
-// device, the same decomposition that shards a sequence over devices):
-//   pass 1: every segment but the last walks its chunks from zero and
-//           writes its end state E_p;
-//   combine: S_0 = C_0, S_{p+1} = diag(e^{G_p}) S_p + E_p, G_p the segment's
-//           summed log forget gate (per key channel for the GLA gate);
-//   pass 2: every segment walks its chunks again from its true start S_p
-//           and writes the states (and C_T).
-// It costs one more read of k and v; the serial part left is P steps of a
-// d_qk x d_hv elementwise update.
-//
+// device, the same decomposition that shards a sequence over devices).
+// Forward:
+//   walk:    every segment walks its chunks once, from zero (segment 0 from
+//            C_0), stores the states it reaches and its end state E_p;
+//   combine: S_0 = 0, S_{p+1} = diag(e^{G_p}) S_p + E_p, G_p the segment's
+//            summed log forget gate (per key channel for the per-channel
+//            gate): the true start state of every segment;
+//   fix-up:  the state a segment p >= 1 stored after its chunk k becomes
+//            state + diag(e^{G_{p,k}}) S_p, G_{p,k} the log forget gate
+//            summed from the segment's start through chunk k (and C_T
+//            likewise from the last segment's end state).
+// K and V cross from memory once; the fix-up reads and writes the stored
+// states once more, which for bf16 states is a quarter of the bytes of K and
+// V per chunk at d_qk = d_hv.  The serial part left is P steps of a
+// d_qk x d_hv elementwise update.  (The stored states are rounded to the
+// state type before the fix-up adds the start state: one more rounding than
+// a walk from the true start.  The gate gradient of the fixed decay, one
+// number per head summed over the couplings of every chunk boundary, feels
+// it -- about 2.5x its error at two segments -- so that gate keeps the
+// two-pass form below; the per-step and per-channel gate gradients do not
+// change.  The forward walk and the backward pass's recomputation of it
+// take the same form, so reusing a forward workspace stays bitwise.)
+// Reverse (the backward pass's walk), and the forward walk of the fixed
+// decay: pass 1 walks every segment but the last from zero for its end
+// state, the combine as above (from C_0, or from the final state gradient),
+// and pass 2 walks every segment again from its true start and stores the
+// states (and couplings).
+
 // Reverse walk (REV, for the backward pass): the gradient that flows into
 // the state from the chunks after chunk j,
 //   D_{j-1} = diag(e^{g_j}) D_j + sum_{t in chunk j} e^{a_t} q_t dh_t^T,
@@ -81,6 +99,9 @@ struct StateWalk {
     // the factor on the end state it writes
     int cp_slots = 0, cp_off = 0, nbound = 0;
     float end_scale = 1.0f;
+    // init holds one state per head, read by segment 0 only (the others
+    // start from zero)
+    int init_first = 0;
 };
 
 // Tile of C^T per workgroup: TV value rows x TC key columns; NWS wavefronts
@@ -277,10 +298,11 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
         return (size_t)(c0 + cw + 32 * mc + i32) * dhv + v0 + vw + 32 * mv + arow(r);
     };
     f32x16 acc[MV][MC];
-    if (wk.init) {
+    if (wk.init && (!wk.init_first || seg == 0)) {
         // the segment's initial state in [d_qk][d_hv]: read once; segment 0
         // stores the caller's C_0 transposed as the state before chunk 0
-        const float* src = wk.init + (bh * wk.nseg_buf + seg) * (size_t)dqk * dhv;
+        const float* src = wk.init_first ? wk.init + bh * (size_t)dqk * dhv
+                                         : wk.init + (bh * wk.nseg_buf + seg) * (size_t)dqk * dhv;
 #pragma unroll
         for (int mv = 0; mv < MV; ++mv)
             for (int mc = 0; mc < MC; ++mc)
@@ -462,6 +484,103 @@ __global__ __launch_bounds__(256) void state_combine_kernel(const float* __restr
     }
 }
 
+// Fix-up of the forward segmented walk: one workgroup per 64 x 64 tile of
+// the state ([d_qk] x [d_hv]), head and segment p >= 1.  The segment's start
+// state tile S_p (fp32 [d_qk][d_hv]) is staged in LDS; for each chunk k of
+// the segment the stored state (transposed, [d_hv][d_qk], type S) gains
+// e^{G_{p,k}} S_p, G_{p,k} the gate summed from the segment's first chunk
+// through k in the order the combine kernel sums it; the last segment's end
+// state gives C_T the same way.  Thread (v, 16-channel run) for the stored
+// states, (c, 16-value run) for C_T.
+template <int GATE, typename S>
+__global__ __launch_bounds__(256) void state_fixup_kernel(S* __restrict__ states, const float* __restrict__ segs,
+                                                          const float* __restrict__ ends, float* __restrict__ cT,
+                                                          const float* __restrict__ g, const float* __restrict__ fg,
+                                                          int H, int T_, int dqk, int dhv, int L, int nc, int P,
+                                                          int cps, int nwalk, int soff)
+{
+    __shared__ float ss[64][65];                 // S_p tile [channel][value]
+    const int ntv = dhv / 64;
+    const int c0 = (blockIdx.x / ntv) * 64, v0 = (blockIdx.x % ntv) * 64;
+    const size_t bh = blockIdx.y;
+    const int p = blockIdx.z + 1;
+    const int tid = threadIdx.x;
+    const size_t n = (size_t)dqk * dhv;
+    const float* sp = segs + (bh * P + p) * n;
+    for (int i = tid; i < 64 * 64; i += 256) ss[i / 64][i % 64] = sp[(size_t)(c0 + i / 64) * dhv + v0 + i % 64];
+    __syncthreads();
+    float lgam = 0.0f;
+    if (GATE == kScalar) lgam = fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor);
+    // log forget gate of chunk kc (per head, or per key channel c)
+    auto gate = [&](int kc, int c) {
+        if (GATE == kSig) return g[bh * nc + kc];
+        if (GATE == kScalar) return (float)min(L, T_ - kc * L) * lgam;
+        return g[(bh * nc + kc) * (size_t)dqk + c];
+    };
+    const int kbeg = p * cps, kend = p == P - 1 ? nwalk : min(kbeg + cps, nwalk);
+    const int ns = nc - 1 + soff;                // stored states per head
+    {
+        // stored states: row v of the tile, channels cr .. cr+15
+        const int v = tid / 4, cr = (tid % 4) * 16;
+        float G[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) G[j] = 0.0f;
+        for (int kc = kbeg; kc < kend && kc < nc - 1; ++kc) {
+            S* row = states + ((bh * ns + kc + soff) * (size_t)dhv + v0 + v) * dqk + c0 + cr;
+            constexpr int VEC = Elem<S>::vec;
+            Vec16<S> x[16 / VEC];
+#pragma unroll
+            for (int q = 0; q < 16 / VEC; ++q) x[q].load(row + VEC * q);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                G[j] += gate(kc, c0 + cr + j);
+                const float d = exp2_fast(G[j] * kLog2e);
+                x[j / VEC].set(j % VEC, x[j / VEC].get(j % VEC) + d * ss[cr + j][v]);
+            }
+#pragma unroll
+            for (int q = 0; q < 16 / VEC; ++q) x[q].store(row + VEC * q);
+        }
+    }
+    if (cT && p == P - 1) {
+        // C_T = E_{P-1} + e^{G} S_{P-1}: row c of the tile, values vr .. vr+15
+        const int c = tid / 4, vr = (tid % 4) * 16;
+        float G = 0.0f;
+        for (int kc = kbeg; kc < kend; ++kc) G += gate(kc, c0 + c);
+        const float d = exp2_fast(G * kLog2e);
+        const float* e = ends + (bh * P + p) * n + (size_t)(c0 + c) * dhv + v0 + vr;
+        float* o = cT + bh * n + (size_t)(c0 + c) * dhv + v0 + vr;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f32x4 x = *reinterpret_cast<const f32x4*>(e + 4 * q);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] += d * ss[c][vr + 4 * q + j];
+            *reinterpret_cast<f32x4*>(o + 4 * q) = x;
+        }
+    }
+}
+
+template <int GATE, typename S>
+hipError_t launch_fixup_s(const Problem& p, const Workspace& ws, const float* fg, int P, int cps, int nwalk, int soff,
+                          hipStream_t stream)
+{
+    const dim3 grid((unsigned)((p.dqk / 64) * (p.dhv / 64)), (unsigned)(p.B * p.H), (unsigned)(P - 1));
+    state_fixup_kernel<GATE, S><<<grid, 256, 0, stream>>>(static_cast<S*>(ws.states), ws.seg_start, ws.seg_end,
+                                                          ws.c_final, ws.g, fg, p.H, p.T, p.dqk, p.dhv, p.L, p.nc,
+                                                          P, cps, nwalk, soff);
+    return hipGetLastError();
+}
+
+template <typename S>
+hipError_t launch_fixup(const Problem& p, const Workspace& ws, const float* fg, int P, int cps, int nwalk, int soff,
+                        hipStream_t stream)
+{
+    switch (p.gate) {
+    case kSig: return launch_fixup_s<kSig, S>(p, ws, fg, P, cps, nwalk, soff, stream);
+    case kScalar: return launch_fixup_s<kScalar, S>(p, ws, fg, P, cps, nwalk, soff, stream);
+    default: return launch_fixup_s<kGla, S>(p, ws, fg, P, cps, nwalk, soff, stream);
+    }
+}
+
 template <typename T, int SB, int TV, int TC, int NWS, bool REV, typename S>
 hipError_t launch_walk_s(const Problem& p, const T* k, const T* v, const float* fg, const Workspace& ws,
                          const StateWalk& wk, hipStream_t stream)
@@ -499,21 +618,21 @@ hipError_t launch_walk(const Problem& p, const T* k, const T* v, const float* fg
 }
 
 template <bool REV>
-hipError_t launch_combine(const Problem& p, const float* fg, const Workspace& ws, int P, int cps,
+hipError_t launch_combine(const Problem& p, const float* fg, const Workspace& ws, const float* c0, int P, int cps,
                           hipStream_t stream)
 {
     const dim3 cgrid((unsigned)((p.dqk * p.dhv + 255) / 256), (unsigned)(p.B * p.H));
     switch (p.gate) {
     case kSig:
-        state_combine_kernel<kSig, REV><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, ws.c0, ws.g, fg, p.H,
+        state_combine_kernel<kSig, REV><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, c0, ws.g, fg, p.H,
                                                                    p.T, p.dqk, p.dhv, p.L, p.nc, P, cps);
         break;
     case kScalar:
-        state_combine_kernel<kScalar, REV><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, ws.c0, ws.g, fg,
+        state_combine_kernel<kScalar, REV><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, c0, ws.g, fg,
                                                                       p.H, p.T, p.dqk, p.dhv, p.L, p.nc, P, cps);
         break;
     default:
-        state_combine_kernel<kGla, REV><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, ws.c0, ws.g, fg,
+        state_combine_kernel<kGla, REV><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, c0, ws.g, fg,
                                                                      p.H, p.T, p.dqk, p.dhv, p.L, p.nc, P, cps);
         break;
     }
@@ -543,10 +662,23 @@ hipError_t launch_state_cfg(const Problem& p, const T* k, const T* v, const floa
         return launch_walk<T, SB, TV, TC, NWS, REV>(p, k, v, fg, ws, wk, stream);
     }
     const int cps = state_chunks_per_segment(p, P);
+    // (the fixed decay walks twice: its gate gradient, one number per head,
+    // sums the couplings of every boundary and feels the fix-up's rounding)
+    if (!REV && p.gate != kScalar && knob(TFLA_KNOB_STATE_REWALK) != 1) {
+        // one walk of every segment (segment 0 from C_0) storing the states
+        // it reaches and every end state, the combine from S_0 = 0, the fix-up
+        StateWalk walk{ws.c0, ws.seg_end, P, P, cps, nwalk, soff, 1, 1, soff};
+        walk.init_first = 1;
+        hipError_t e = launch_walk<T, SB, TV, TC, NWS, REV>(p, k, v, fg, ws, walk, stream);
+        if (e != hipSuccess) return e;
+        if ((e = launch_combine<REV>(p, fg, ws, nullptr, P, cps, stream)) != hipSuccess) return e;
+        if (sizeof(T) == 2 && p.st32) return launch_fixup<float>(p, ws, fg, P, cps, nwalk, soff, stream);
+        return launch_fixup<T>(p, ws, fg, P, cps, nwalk, soff, stream);
+    }
     const StateWalk pass1{nullptr, ws.seg_end, P, P - 1, cps, p.nc - 1, 0, 1, 0, soff};
     hipError_t e = launch_walk<T, SB, TV, TC, NWS, REV>(p, k, v, fg, ws, pass1, stream);
     if (e != hipSuccess) return e;
-    if ((e = launch_combine<REV>(p, fg, ws, P, cps, stream)) != hipSuccess) return e;
+    if ((e = launch_combine<REV>(p, fg, ws, ws.c0, P, cps, stream)) != hipSuccess) return e;
     StateWalk pass2{ws.seg_start, ws.c_final, P, P, cps, nwalk, soff, 0, 1, soff};
     set_rev_fields(pass2, ws);
     return launch_walk<T, SB, TV, TC, NWS, REV>(p, k, v, fg, ws, pass2, stream);

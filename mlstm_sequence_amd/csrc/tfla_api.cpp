@@ -76,6 +76,9 @@ int check_gates(const tfla::Problem& p, const float* igate_pre, const float* fga
 {
     if (!fgate_pre) return fail(TFLA_ERR_INVALID_ARG, "fgate_pre is NULL");
     if (!aligned(fgate_pre, 4)) return fail(TFLA_ERR_INVALID_ARG, "fgate_pre is not 4-byte aligned");
+    // the per-channel gate kernel reads rows of fgate_pre in 16-byte pieces
+    if (p.gate == tfla::kGla && !aligned(fgate_pre, 16))
+        return fail(TFLA_ERR_INVALID_ARG, "fgate_pre (per-channel gate) is not 16-byte aligned");
     if (tfla::per_step_li(p.gate)) {
         if (!igate_pre) return fail(TFLA_ERR_INVALID_ARG, "igate_pre is NULL but the variant has an input gate");
         if (!aligned(igate_pre, 4)) return fail(TFLA_ERR_INVALID_ARG, "igate_pre is not 4-byte aligned");
@@ -198,7 +201,7 @@ void* scratch_on_current_device(std::string* err)
 }
 
 // Test and tuning overrides (tfla_dbg_set_knob): -1 = unset.
-std::atomic<int> g_knobs[TFLA_KNOB_COUNT] = {-1, -1, -1, -1, -1, -1};
+std::atomic<int> g_knobs[TFLA_KNOB_COUNT] = {-1, -1, -1, -1, -1, -1, -1};
 
 // Failure injection for tests of the error paths: the fault knob set to 1
 // makes the library's own workspace allocation fail before any launch.
@@ -773,6 +776,20 @@ int tfla_dbg_gates(const float* igate_pre, const float* fgate_pre, float* a_out,
     }
     if (e != hipSuccess) return hip_fail(e, "gate kernel launch");
     return TFLA_OK;
+}
+
+int tfla_dbg_stream(int mode, const void* src, void* dst, size_t bytes, int loads_per_thread, int workgroups,
+                    void* stream)
+{
+    if (mode != 0 && mode != 1) return fail(TFLA_ERR_INVALID_ARG, "tfla_dbg_stream: mode must be 0 (read) or 1 (copy)");
+    if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16) || bytes % 16 != 0)
+        return fail(TFLA_ERR_INVALID_ARG, "tfla_dbg_stream: 16-byte aligned buffers and a multiple of 16 bytes");
+    const int l = loads_per_thread;
+    if (!(l == 1 || l == 2 || l == 4 || l == 8 || l == 16) || workgroups < 1)
+        return fail(TFLA_ERR_INVALID_ARG, "tfla_dbg_stream: loads_per_thread 1, 2, 4, 8 or 16; workgroups >= 1");
+    const hipError_t e = tfla::launch_stream_probe(mode, src, dst, bytes, l, workgroups,
+                                                   static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TFLA_OK : hip_fail(e, "stream probe launch");
 }
 
 int tfla_dbg_states(const void* k, const void* v, const float* igate_pre, const float* fgate_pre, void* states_out,

@@ -23,7 +23,8 @@ STATES_FP32 = 0x400   # forward, bf16 I/O: materialise the chunk states in fp32
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_HIP, ERR_OUT_OF_MEMORY = 0, 1, 2, 3, 4
 
 # test overrides (tfla_dbg_set_knob)
-KNOB_INTRA_SWEEP, KNOB_INTRA_BV, KNOB_INTRA_ROWS, KNOB_STATE_SEGMENTS, KNOB_STATE_SB, KNOB_FAULT_ALLOC = range(6)
+(KNOB_INTRA_SWEEP, KNOB_INTRA_BV, KNOB_INTRA_ROWS, KNOB_STATE_SEGMENTS, KNOB_STATE_SB, KNOB_FAULT_ALLOC,
+ KNOB_STATE_REWALK) = range(7)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtfla.so")
@@ -74,6 +75,8 @@ def lib():
         L.tfla_dbg_gates.restype = i
         L.tfla_dbg_states.argtypes = [vp, vp, fp, fp, vp] + [i] * 7 + [vp]
         L.tfla_dbg_states.restype = i
+        L.tfla_dbg_stream.argtypes = [i, vp, vp, sz, i, i, vp]
+        L.tfla_dbg_stream.restype = i
         L.tfla_dbg_set_knob.argtypes = [i, i]
         L.tfla_dbg_set_knob.restype = i
         L.tfla_error_string.argtypes = [i]
@@ -366,6 +369,20 @@ def tfla_dbg_gates(igate_pre, fgate_pre, a_out, li_out, g_out, B, H, T, d_qk, L,
     rc = lib().tfla_dbg_gates(_ptr(igate_pre), _ptr(fgate_pre), _ptr(a_out), _ptr(li_out), _ptr(g_out),
                               B, H, T, d_qk, L, variant, _stream(stream))
     _check(rc, "tfla_dbg_gates")
+
+
+def tfla_dbg_stream(mode, src, dst, nbytes, loads_per_thread, workgroups, stream=None):
+    """Streaming probe (measurement aid): mode 0 reads ``nbytes`` of ``src``,
+    mode 1 copies them to ``dst``; both CUDA tensors of at least ``nbytes``
+    (``dst`` at least 4 KB in mode 0)."""
+    for t, name in ((src, "src"), (dst, "dst")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{name} must be a CUDA tensor")
+    need = (nbytes, max(4096, nbytes if mode == 1 else 0))
+    if src.numel() * src.element_size() < need[0] or dst.numel() * dst.element_size() < need[1]:
+        raise ValueError("tfla_dbg_stream: buffers smaller than the bytes asked for")
+    rc = lib().tfla_dbg_stream(mode, _ptr(src), _ptr(dst), nbytes, loads_per_thread, workgroups, _stream(stream))
+    _check(rc, "tfla_dbg_stream")
 
 
 def tfla_dbg_states(k, v, igate_pre, fgate_pre, states_out, B, H, T, d_qk, d_hv, L, variant, stream=None):

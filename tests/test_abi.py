@@ -59,6 +59,7 @@ def fwd(q=Q, k=K, v=V, ig=IG, fg=FG, h=H_, B=2, H=3, T=300, dqk=128, dhv=256, Lc
     (dict(B=0), INVALID), (dict(T=0), INVALID), (dict(H=-2), INVALID),
     (dict(q=None), INVALID), (dict(h=None), INVALID), (dict(fg=None), INVALID),
     (dict(q=Q + 8), INVALID), (dict(h=H_ + 2), INVALID), (dict(fg=FG + 2), INVALID),
+    (dict(variant=GLA | BF16, ig=None, fg=FG + 4), INVALID),   # per-channel gate rows: 16-byte aligned
     (dict(ig=None), INVALID),                                   # mLSTMsig needs an input gate
     (dict(ig=None, variant=EXP | BF16), INVALID),               # ... and so does mLSTMexp
     (dict(variant=SCALAR | BF16), INVALID),                     # ... the others must not have one
@@ -420,3 +421,15 @@ def test_mlstm_exp_is_forward_only(L):
     sig = tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG | BF16)
     extra = a256(B * H * T * 4) + a256(B * H * nc * dqk * 4) + a256(B * H * (nc - 1) * dqk * 4) + 2 * a256(B * H * nc * 4)
     assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, var) == sig + extra
+
+
+def test_stream_probe_rejects_bad_arguments(L):
+    """The streaming probe (a measurement aid) checks its arguments before
+    any HIP call."""
+    assert L.tfla_dbg_stream(2, Q, K, 1 << 20, 4, 256, None) == INVALID      # no such mode
+    assert L.tfla_dbg_stream(0, Q, K, 1 << 20, 3, 256, None) == INVALID      # 3 loads per thread
+    assert L.tfla_dbg_stream(0, Q, K, 1 << 20, 4, 0, None) == INVALID        # no workgroups
+    assert L.tfla_dbg_stream(1, Q, K, 1000, 4, 256, None) == INVALID         # not a multiple of 16
+    assert L.tfla_dbg_stream(0, Q + 8, K, 1 << 20, 4, 256, None) == INVALID  # misaligned
+    assert L.tfla_dbg_stream(0, None, K, 1 << 20, 4, 256, None) == INVALID
+    assert "tfla_dbg_stream" in tfla.tfla_last_error()

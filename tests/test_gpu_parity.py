@@ -46,6 +46,25 @@ def test_gate_prefix_sums(variant, T, L):
     assert rel_err(li.cpu().numpy(), li_ref) <= 1e-6
 
 
+@pytest.mark.parametrize("dqk", [64, 128, 256])
+@pytest.mark.parametrize("T,L", [(1, 64), (97, 64), (700, 128), (900, 256), (1500, 512), (2100, 1024)])
+def test_per_channel_gate_prefix_sums(dqk, T, L):
+    """The per-channel gate kernel (16 steps x 4 channels per thread, segment
+    totals through LDS, a carry across passes when the chunk is longer than
+    one pass) at every d_qk and chunk size, ragged last chunks included."""
+    print(f"per-channel gate sums: d_qk {dqk} T {T} L {L}", flush=True)
+    wl, inp = case(GLA, 1, 2, T, dqk, 64, BF, seed=T + dqk + L)
+    a_ref, _, g_ref = oracle.log_gates(None, W.as_f64(inp["fgate_pre"]), GLA, 1, 2, T, dqk, L)
+    nc = -(-T // L)
+    a = torch.full((1, 2, T * dqk), float("nan"), device="cuda")
+    li = torch.full((1, 2, T), float("nan"), device="cuda")
+    g = torch.full((1, 2, nc * dqk), float("nan"), device="cuda")
+    tfla.tfla_dbg_gates(None, inp["fgate_pre"].cuda(), a, li, g, 1, 2, T, dqk, L, tfla.variant_of(tfla.GLA_KEY, BF))
+    torch.cuda.synchronize()
+    assert rel_err(a.cpu().numpy().reshape(a_ref.shape), a_ref) <= 1e-5
+    assert rel_err(g.cpu().numpy().reshape(g_ref.shape), g_ref) <= 1e-5
+
+
 # ---------------------------------------------------------------- state kernel
 @pytest.mark.parametrize("variant,dtype,dqk,dhv,T,L", [
     (SIG, F32, 64, 64, 256, 64), (SIG, BF, 256, 512, 700, 128), (SIG, BF, 128, 192, 640, 64),

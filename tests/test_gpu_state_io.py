@@ -228,3 +228,40 @@ def test_segmented_state_walk(set_knob, segments, variant, dtype, B, H, T, dqk, 
                              tfla.variant_of(GATE[variant], dtype))
         torch.cuda.synchronize()
         assert rel_err(st.cpu().double().numpy().swapaxes(-1, -2), st_ref[:, :, :nc - 1]) <= STOL[dtype]
+
+
+@pytest.mark.parametrize("variant,dtype,dqk,dhv,L,with_c0", [
+    (SIG, BF, 128, 128, 64, True), (SCAL, BF, 128, 256, 64, False), (GLA, BF, 64, 128, 128, True),
+    (SIG, F32, 64, 128, 64, True), (SIG, BF, 256, 512, 256, True),
+])
+@pytest.mark.parametrize("segments", ["2", "5"])
+def test_segmented_walk_fixup_against_second_walk(set_knob, variant, dtype, dqk, dhv, L, with_c0, segments):
+    """The forward segmented walk fixes up the states it stored (the start
+    state of each segment, decayed, added in place); the two-pass form walks
+    every segment again from its true start.  Both give the oracle's h and
+    C_T, and the stored states of the two agree to within the one extra
+    rounding of the fix-up (two roundings to the state type instead of one).
+    The fixed decay walks twice either way."""
+    set_knob(tfla.KNOB_STATE_SEGMENTS, segments)
+    B, H, T = 1, 2, 64 * 23 + 17
+    wl, inp = case(variant, B, H, T, dqk, dhv, dtype, seed=int(segments) * 7 + dqk + L)
+    c0 = W.initial_state(B, H, dqk, dhv, seed=5, std=1.5) if with_c0 else None
+    print(f"fix-up vs second walk: {variant} {dtype} {dqk}x{dhv} L{L} c0={with_c0} P={segments}", flush=True)
+    h_ref, c_ref = oracle_state(inp, variant, c0)
+    outs = {}
+    for rewalk in (0, 1):
+        with tfla.knob(tfla.KNOB_STATE_REWALK, rewalk):
+            h, cf = run_state(to_dev(inp), variant, L, c0=c0)
+            assert rel_err(h_f64(h), h_ref) <= TOL[dtype]
+            assert rel_err(cf.cpu().double().numpy(), c_ref) <= STOL[dtype]
+            if not with_c0:
+                nc = -(-T // L)
+                st = torch.full((B, H, nc - 1, dhv, dqk), float("nan"), device="cuda", dtype=dtype)
+                d = to_dev(inp)
+                tfla.tfla_dbg_states(d["k"], d["v"], d["igate_pre"], d["fgate_pre"], st, B, H, T, dqk, dhv, L,
+                                     tfla.variant_of(GATE[variant], dtype))
+                torch.cuda.synchronize()
+                outs[rewalk] = st.double().cpu().numpy()
+    if outs:
+        unit = 2.0 ** -8 if dtype == BF else 2.0 ** -23   # the state type's relative spacing
+        assert rel_err(outs[0], outs[1]) <= 2 * unit
