@@ -434,7 +434,12 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
     }
 }
 
-// combine pass: start states of the segments from their end states
+// combine pass: start states of the segments from their end states.  A
+// thread owns 4 consecutive elements of one row (16-byte pieces; one key
+// channel, so one gate for the per-channel gate too) and walks the segments
+// in order; the end states of 16 segments are loaded together, and the
+// gates summed over a segment's chunks are the same for the whole head
+// (scalar loads) except for the per-channel gate.
 template <int GATE, bool REV>
 __global__ __launch_bounds__(256) void state_combine_kernel(const float* __restrict__ E, float* __restrict__ S,
                                                             const float* __restrict__ c0,
@@ -442,25 +447,26 @@ __global__ __launch_bounds__(256) void state_combine_kernel(const float* __restr
                                                             const float* __restrict__ fg, int H, int T_, int dqk,
                                                             int dhv, int L, int nc, int P, int cps)
 {
+    constexpr int U = 16;   // segments whose loads are issued together
     const size_t n = (size_t)dqk * dhv;
     const size_t bh = blockIdx.y;
-    const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (e >= n) return;
     const int c = (int)(e / dhv);
     float lgam = 0.0f;
     if (GATE == kScalar) lgam = fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor);
-    float st = c0 ? c0[bh * n + e] : 0.0f;
-    S[(bh * P) * n + e] = st;
-    constexpr int U = 8;   // segments whose loads are issued together
+    f32x4 st = c0 ? *reinterpret_cast<const f32x4*>(c0 + bh * n + e) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    *reinterpret_cast<f32x4*>(S + (bh * P) * n + e) = st;
     for (int p0 = 0; p0 + 1 < P; p0 += U) {
-        float ev[U], gv[U];
+        f32x4 ev[U];
+        float gv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int p = p0 + u;
-            ev[u] = 0.0f;
+            ev[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             gv[u] = 0.0f;
             if (p + 1 < P) {
-                ev[u] = E[(bh * P + p) * n + e];
+                ev[u] = *reinterpret_cast<const f32x4*>(E + (bh * P + p) * n + e);
                 if (GATE == kScalar) {
                     // the reverse walk's first segment holds the partial last chunk
                     const int steps = REV && p == 0 ? (cps - 1) * L + (T_ - (nc - 1) * L) : cps * L;
@@ -477,8 +483,10 @@ __global__ __launch_bounds__(256) void state_combine_kernel(const float* __restr
         for (int u = 0; u < U; ++u) {
             const int p = p0 + u;
             if (p + 1 < P) {
-                st = exp2_fast(gv[u] * kLog2e) * st + ev[u];
-                S[(bh * P + p + 1) * n + e] = st;
+                const float d = exp2_fast(gv[u] * kLog2e);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) st[j] = d * st[j] + ev[u][j];
+                *reinterpret_cast<f32x4*>(S + (bh * P + p + 1) * n + e) = st;
             }
         }
     }
@@ -507,7 +515,11 @@ __global__ __launch_bounds__(256) void state_fixup_kernel(S* __restrict__ states
     const int tid = threadIdx.x;
     const size_t n = (size_t)dqk * dhv;
     const float* sp = segs + (bh * P + p) * n;
-    for (int i = tid; i < 64 * 64; i += 256) ss[i / 64][i % 64] = sp[(size_t)(c0 + i / 64) * dhv + v0 + i % 64];
+    for (int i = tid; i < 64 * 16; i += 256) {   // 16-byte pieces of the tile's rows
+        const f32x4 x = *reinterpret_cast<const f32x4*>(sp + (size_t)(c0 + i / 16) * dhv + v0 + 4 * (i % 16));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ss[i / 16][4 * (i % 16) + j] = x[j];
+    }
     __syncthreads();
     float lgam = 0.0f;
     if (GATE == kScalar) lgam = fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor);
@@ -520,25 +532,47 @@ __global__ __launch_bounds__(256) void state_fixup_kernel(S* __restrict__ states
     const int kbeg = p * cps, kend = p == P - 1 ? nwalk : min(kbeg + cps, nwalk);
     const int ns = nc - 1 + soff;                // stored states per head
     {
-        // stored states: row v of the tile, channels cr .. cr+15
+        // stored states: row v of the tile, channels cr .. cr+15; the rows of
+        // CG chunks are loaded together
+        constexpr int VEC = Elem<S>::vec, NQ = 16 / VEC, CG = 4;
         const int v = tid / 4, cr = (tid % 4) * 16;
         float G[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) G[j] = 0.0f;
-        for (int kc = kbeg; kc < kend && kc < nc - 1; ++kc) {
-            S* row = states + ((bh * ns + kc + soff) * (size_t)dhv + v0 + v) * dqk + c0 + cr;
-            constexpr int VEC = Elem<S>::vec;
-            Vec16<S> x[16 / VEC];
+        const int klast = min(kend, nc - 1);     // chunks with a stored state
+        for (int k0 = kbeg; k0 < klast; k0 += CG) {
+            Vec16<S> x[CG][NQ];
 #pragma unroll
-            for (int q = 0; q < 16 / VEC; ++q) x[q].load(row + VEC * q);
+            for (int u = 0; u < CG; ++u) {
+                const int kc = min(k0 + u, klast - 1);
+                const S* row = states + ((bh * ns + kc + soff) * (size_t)dhv + v0 + v) * dqk + c0 + cr;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                G[j] += gate(kc, c0 + cr + j);
-                const float d = exp2_fast(G[j] * kLog2e);
-                x[j / VEC].set(j % VEC, x[j / VEC].get(j % VEC) + d * ss[cr + j][v]);
+                for (int q = 0; q < NQ; ++q) x[u][q].load(row + VEC * q);
             }
 #pragma unroll
-            for (int q = 0; q < 16 / VEC; ++q) x[q].store(row + VEC * q);
+            for (int u = 0; u < CG; ++u) {
+                const int kc = k0 + u;
+                if (kc >= klast) break;
+                float d[16];
+                if (GATE == kGla) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        G[j] += gate(kc, c0 + cr + j);
+                        d[j] = exp2_fast(G[j] * kLog2e);
+                    }
+                } else {
+                    G[0] += gate(kc, 0);
+                    const float dd = exp2_fast(G[0] * kLog2e);
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) d[j] = dd;
+                }
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    x[u][j / VEC].set(j % VEC, x[u][j / VEC].get(j % VEC) + d[j] * ss[cr + j][v]);
+                S* row = states + ((bh * ns + kc + soff) * (size_t)dhv + v0 + v) * dqk + c0 + cr;
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) x[u][q].store(row + VEC * q);
+            }
         }
     }
     if (cT && p == P - 1) {
@@ -621,7 +655,7 @@ template <bool REV>
 hipError_t launch_combine(const Problem& p, const float* fg, const Workspace& ws, const float* c0, int P, int cps,
                           hipStream_t stream)
 {
-    const dim3 cgrid((unsigned)((p.dqk * p.dhv + 255) / 256), (unsigned)(p.B * p.H));
+    const dim3 cgrid((unsigned)((p.dqk * p.dhv / 4 + 255) / 256), (unsigned)(p.B * p.H));
     switch (p.gate) {
     case kSig:
         state_combine_kernel<kSig, REV><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, c0, ws.g, fg, p.H,
@@ -721,17 +755,20 @@ bool state_big_tiles(const Problem& p)
     return heads_tiles >= 256 || state_segments_for(p, heads_tiles) > 1;
 }
 
-// Segments of the chunk chain: enough workgroups for about two per CU of
-// a 256-CU device (512), each segment at least two chunks long; 1 when the
-// heads and tiles alone fill the device.  The state-segments knob overrides
-// it (tests reach the segmented walk at small sizes with it; tuning).
+// Segments of the chunk chain: enough workgroups for about one per CU of a
+// 256-CU device, each segment at least two chunks long; 1 when the heads
+// and tiles alone fill the device.  (One per CU rather than two: the walk
+// then takes 256-step blocks, and the combine and the fix-up move half the
+// bytes -- 0.261 ms against 0.273 ms per forward at 64 segments on the
+// T = 65536, 8-head workload.)  The state-segments knob overrides it (tests
+// reach the segmented walk at small sizes with it; tuning).
 int state_segments_for(const Problem& p, long heads_tiles)
 {
     const int nfeed = p.nc - 1;   // chunks that feed a stored state
     if (nfeed < 4) return 1;
     long P = 1;
     if (knob(TFLA_KNOB_STATE_SEGMENTS) > 0) P = knob(TFLA_KNOB_STATE_SEGMENTS);
-    else if (heads_tiles < 256) P = (512 + heads_tiles - 1) / heads_tiles;
+    else if (heads_tiles < 256) P = (256 + heads_tiles - 1) / heads_tiles;
     P = std::min<long>(P, nfeed / 2);
     if (P < 2) return 1;
     const int cps = (int)((nfeed + P - 1) / P);
