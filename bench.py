@@ -421,6 +421,131 @@ def source_sha(kernel):
     return hs.hexdigest()[:16]
 
 
+# --------------------------------------------------------------------------- HBM byte counters
+def counter_run(wl, L, calls):
+    """Only `calls` forward calls at chunk size L, nothing else of this
+    library on the device (the target of the rocprofv3 --pmc passes that
+    count HBM bytes per phase)."""
+    import torch
+    from mlstm_sequence_amd import tfla
+    import workloads as W
+
+    dev = {n: (None if t is None else t.cuda()) for n, t in W.make_inputs(wl).items()}
+    gate = {0: tfla.MLSTM_SIG, 1: tfla.SCALAR_DECAY, 2: tfla.GLA_KEY, 3: tfla.MLSTM_EXP}[wl.variant]
+    var = tfla.variant_of(gate, dev["q"].dtype)
+    h = torch.empty((wl.B, wl.H, wl.T, wl.dhv), dtype=dev["q"].dtype, device="cuda")
+    nbytes = tfla.tfla_workspace_bytes(wl.B, wl.H, wl.T, wl.dqk, wl.dhv, L, var)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+    for i in range(calls):
+        tfla.tfla_fwd_ws(dev["q"], dev["k"], dev["v"], dev["igate_pre"], dev["fgate_pre"], h,
+                         wl.B, wl.H, wl.T, wl.dqk, wl.dhv, L, var, ws, nbytes)
+        torch.cuda.synchronize()
+        log(f"counter run: call {i + 1} of {calls} done")
+    print(json.dumps({"workload": wl.name, "L": L, "calls": calls}), flush=True)
+
+
+COPY_CAL_BYTES = 1 << 30
+
+
+def copy_calibration():
+    """A plain copy of COPY_CAL_BYTES with the streaming probe's copy kernel,
+    three times: what FETCH_SIZE and WRITE_SIZE read for bytes known to
+    move (the scale of the counters)."""
+    import torch
+    from mlstm_sequence_amd import tfla
+    src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        tfla.tfla_dbg_stream(1, src, dst, COPY_CAL_BYTES, 4, 1024)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_CAL_BYTES, "dispatches": 3}), flush=True)
+
+
+def _phase_of(kernel_name):
+    """Phase of one of this library's forward kernels from its demangled
+    name: gates, state, intra, the calibration copy, or None."""
+    import re
+    m = re.search(r"tfla::(?:\(anonymous namespace\)::)?(\w+)", kernel_name)
+    if m:
+        base = m.group(1)
+    else:
+        # template instances keep their mangled name: length-prefixed identifier
+        m = re.search(r"_ZN4tfla12_GLOBAL__N_1(\d+)", kernel_name)
+        if not m:
+            return None
+        base = kernel_name[m.end():m.end() + int(m.group(1))]
+    if base.startswith("gates_"):
+        return "gates"
+    if base in ("state_kernel", "state_combine_kernel", "state_fixup_kernel"):
+        return "state"
+    if base.startswith("intra_kernel"):
+        return "intra"
+    if base == "probe_copy_kernel":
+        return "copy"
+    return None
+
+
+def _counter_sums(csv_path, counter):
+    """Sum of one counter per phase over the run, and dispatches per phase."""
+    import csv
+    sums, counts = {}, {}
+    with open(csv_path, newline="") as fh:
+        for row in csv.DictReader(fh):
+            if row["Counter_Name"] != counter:
+                continue
+            ph = _phase_of(row["Kernel_Name"])
+            if ph is None:
+                continue
+            sums[ph] = sums.get(ph, 0.0) + float(row["Counter_Value"])
+            counts[ph] = counts.get(ph, 0) + 1
+    return sums, counts
+
+
+def write_traffic(run_dir, wl, L):
+    """HBM bytes per forward launch of each phase from four rocprofv3 --pmc
+    runs under run_dir: fetch/ and write/ (FETCH_SIZE, WRITE_SIZE of
+    --counter-run), copy_fetch/ and copy_write/ (the same counters of
+    --copy-calibration).  Each counter is scaled by bytes moved over what
+    it reads for the calibration copy; the per-launch figures go into
+    profiles/traffic.json with the hash of each kernel's source, and a
+    markdown table is printed."""
+    csvp = lambda sub: os.path.join(run_dir, sub, "run_counter_collection.csv")
+    cf, nf = _counter_sums(csvp("copy_fetch"), "FETCH_SIZE")
+    cw, nw = _counter_sums(csvp("copy_write"), "WRITE_SIZE")
+    # a copy moves the bytes once in each direction; counters in KiB
+    fetch_scale = COPY_CAL_BYTES / (cf["copy"] / nf["copy"] * 1024)
+    write_scale = COPY_CAL_BYTES / (cw["copy"] / nw["copy"] * 1024)
+    fs, fn = _counter_sums(csvp("fetch"), "FETCH_SIZE")
+    ws_, wn = _counter_sums(csvp("write"), "WRITE_SIZE")
+    calls = fn["intra"]
+    if wn.get("intra") != calls:
+        raise SystemExit(f"fetch and write runs differ in forward calls ({calls} vs {wn.get('intra')})")
+    model = kernel_model(wl, L)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    print(f"Calibration: a {COPY_CAL_BYTES >> 20} MiB copy reads FETCH_SIZE = {cf['copy'] / nf['copy']:.0f} KiB "
+          f"and WRITE_SIZE = {cw['copy'] / nw['copy']:.0f} KiB per dispatch: fetch scale {fetch_scale:.3f}, "
+          f"write scale {write_scale:.3f}; {calls} forward calls.\n")
+    print("| phase | dispatches per call | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB "
+          "| total MB | algorithmic MB | total / algorithmic |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for ph in ("gates", "state", "intra"):
+        if ph not in fs:
+            continue
+        fk, wk = fs[ph] / calls, ws_.get(ph, 0.0) / calls
+        fb, wb = fk * 1024 * fetch_scale, wk * 1024 * write_scale
+        alg = model[ph]["bytes"]
+        rec[f"{ph}:{wl.name}:L{L}"] = {
+            "bytes_per_launch": fb + wb, "fetch_bytes": fb, "write_bytes": wb, "fetch_kib_counter": fk,
+            "write_kib_counter": wk, "fetch_scale": fetch_scale, "write_scale": write_scale,
+            "algorithmic_bytes": alg, "calls": calls, "src_sha": source_sha(ph)}
+        print(f"| {ph} | {fn[ph] // calls} | {fk:.0f} | {wk:.0f} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | "
+              f"{(fb + wb) / 1e6:.1f} | {alg / 1e6:.1f} | {(fb + wb) / alg:.3f} |")
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+
+
 # --------------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -436,6 +561,11 @@ def main():
                     help="skip the timing with the states materialised in fp32 (TFLA_STATES_FP32)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (scales HBM byte counters)")
+    ap.add_argument("--counter-run", action="store_true",
+                    help="only warmup + steps forward calls at --L (target of the HBM byte counter runs)")
+    ap.add_argument("--traffic-from", type=str, default=None, metavar="DIR",
+                    help="no GPU: turn the FETCH_SIZE/WRITE_SIZE runs under DIR into per-launch HBM bytes "
+                         "of --config at --L (profiles/traffic.json) and print them")
     ap.add_argument("--hbm-probe", action="store_true",
                     help="only measure the HBM rate of plain streaming kernels (copy, read) and print it")
     ap.add_argument("--no-workloads", action="store_true",
@@ -443,14 +573,17 @@ def main():
     args = ap.parse_args()
 
     if args.copy_calibration:
-        import torch
-        n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": n, "dispatches": 3}), flush=True)
+        copy_calibration()
+        return
+    if args.traffic_from or args.counter_run:
+        import workloads as W
+        wl = W.WORKLOADS[args.config]
+        if args.L is None:
+            raise SystemExit("--counter-run and --traffic-from need --L")
+        if args.traffic_from:
+            write_traffic(args.traffic_from, wl, args.L)
+        else:
+            counter_run(wl, args.L, args.warmup + args.steps)
         return
 
     if args.hbm_probe:
