@@ -435,47 +435,103 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
 }
 
 // combine pass: start states of the segments from their end states.  A
-// thread owns 4 consecutive elements of one row (16-byte pieces; one key
-// channel, so one gate for the per-channel gate too) and walks the segments
-// in order; the end states of 16 segments are loaded together, and the
-// gates summed over a segment's chunks are the same for the whole head
-// (scalar loads) except for the per-channel gate.
-template <int GATE, bool REV>
+// thread owns VE consecutive elements of one row (4-, 8- or 16-byte pieces;
+// one key channel, so one gate for the per-channel gate too) and walks the
+// segments in order; the end states of 16 segments are loaded together, and
+// the gates summed over a segment's chunks are the same for the whole head
+// (scalar loads) except for the per-channel gate.  VE is as large as keeps
+// 512 or more workgroups: the pass moves few bytes per head and is bound by
+// the rate each CU loads at, so it wants every CU busy.
+template <int VE>
+struct CombineVec {
+    float x[VE];
+    __device__ __forceinline__ void load(const float* p)
+    {
+        if constexpr (VE == 4) {
+            const f32x4 t = *reinterpret_cast<const f32x4*>(p);
+            for (int j = 0; j < 4; ++j) x[j] = t[j];
+        } else if constexpr (VE == 2) {
+            const float2 t = *reinterpret_cast<const float2*>(p);
+            x[0] = t.x;
+            x[1] = t.y;
+        } else {
+            x[0] = *p;
+        }
+    }
+    __device__ __forceinline__ void store(float* p) const
+    {
+        if constexpr (VE == 4) *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+        else if constexpr (VE == 2) *reinterpret_cast<float2*>(p) = float2{x[0], x[1]};
+        else *p = x[0];
+    }
+};
+
+template <int GATE, bool REV, int VE>
 __global__ __launch_bounds__(256) void state_combine_kernel(const float* __restrict__ E, float* __restrict__ S,
                                                             const float* __restrict__ c0,
                                                             const float* __restrict__ g,
                                                             const float* __restrict__ fg, int H, int T_, int dqk,
                                                             int dhv, int L, int nc, int P, int cps)
 {
-    constexpr int U = 16;   // segments whose loads are issued together
+    // segments whose loads are issued together (U x the workgroup's key
+    // channels <= 256: up to 5 channels at 4-byte pieces, 16 at 16-byte ones)
+    constexpr int U = VE == 1 ? 32 : 16;
+    // a batch's segment gate sums, per key channel of the workgroup for the
+    // per-channel gate: [segment of the batch][channel]; formed by one thread
+    // each (its chunks' loads go out together) instead of by every thread
+    // one dependent load at a time
+    __shared__ float gs[256];
     const size_t n = (size_t)dqk * dhv;
     const size_t bh = blockIdx.y;
-    const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (e >= n) return;
-    const int c = (int)(e / dhv);
+    const size_t eb = (size_t)blockIdx.x * 256 * VE;   // the workgroup's first element
+    const size_t e = eb + (size_t)threadIdx.x * VE;
+    const bool live = e < n;
+    const int c = (int)(min(e, n - 1) / dhv);
+    const int clo = (int)(eb / dhv);
+    const int nch = GATE == kGla ? (int)((min(eb + 256 * VE, n) - 1) / dhv) - clo + 1 : 1;   // <= 16
     float lgam = 0.0f;
     if (GATE == kScalar) lgam = fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor);
-    f32x4 st = c0 ? *reinterpret_cast<const f32x4*>(c0 + bh * n + e) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    *reinterpret_cast<f32x4*>(S + (bh * P) * n + e) = st;
+    CombineVec<VE> st;
+    if (c0 && live) st.load(c0 + bh * n + e);
+    else
+        for (int j = 0; j < VE; ++j) st.x[j] = 0.0f;
+    if (live) st.store(S + (bh * P) * n + e);
     for (int p0 = 0; p0 + 1 < P; p0 += U) {
-        f32x4 ev[U];
+        // the batch's end states first: their loads are in flight while the
+        // gate sums are formed
+        CombineVec<VE> ev[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            for (int j = 0; j < VE; ++j) ev[u].x[j] = 0.0f;
+            if (p0 + u + 1 < P && live) ev[u].load(E + (bh * P + p0 + u) * n + e);
+        }
+        if (GATE != kScalar) {
+            const int t = threadIdx.x, p = p0 + t / nch;
+            if (t < U * nch && p + 1 < P) {
+                // summed from the segment's first chunk on (the fix-up sums
+                // the same terms in the same order)
+                float sum = 0.0f;
+#pragma unroll 8
+                for (int kw = p * cps; kw < (p + 1) * cps; ++kw) {
+                    const int kc = REV ? nc - 1 - kw : kw;
+                    sum += GATE == kSig ? g[bh * nc + kc] : g[(bh * nc + kc) * dqk + clo + t % nch];
+                }
+                gs[t] = sum;
+            }
+            __syncthreads();
+        }
         float gv[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int p = p0 + u;
-            ev[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             gv[u] = 0.0f;
             if (p + 1 < P) {
-                ev[u] = *reinterpret_cast<const f32x4*>(E + (bh * P + p) * n + e);
                 if (GATE == kScalar) {
                     // the reverse walk's first segment holds the partial last chunk
                     const int steps = REV && p == 0 ? (cps - 1) * L + (T_ - (nc - 1) * L) : cps * L;
                     gv[u] = (float)steps * lgam;
                 } else {
-                    for (int kw = p * cps; kw < (p + 1) * cps; ++kw) {
-                        const int kc = REV ? nc - 1 - kw : kw;
-                        gv[u] += GATE == kSig ? g[bh * nc + kc] : g[(bh * nc + kc) * dqk + c];
-                    }
+                    gv[u] = gs[u * nch + (GATE == kGla ? c - clo : 0)];
                 }
             }
         }
@@ -485,10 +541,11 @@ __global__ __launch_bounds__(256) void state_combine_kernel(const float* __restr
             if (p + 1 < P) {
                 const float d = exp2_fast(gv[u] * kLog2e);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) st[j] = d * st[j] + ev[u][j];
-                *reinterpret_cast<f32x4*>(S + (bh * P + p + 1) * n + e) = st;
+                for (int j = 0; j < VE; ++j) st.x[j] = d * st.x[j] + ev[u].x[j];
+                if (live) st.store(S + (bh * P + p + 1) * n + e);
             }
         }
+        if (GATE != kScalar) __syncthreads();   // gs is read before the next batch refills it
     }
 }
 
@@ -651,26 +708,37 @@ hipError_t launch_walk(const Problem& p, const T* k, const T* v, const float* fg
     return launch_walk_s<T, SB, TV, TC, NWS, REV, T>(p, k, v, fg, ws, wk, stream);
 }
 
+template <int GATE, bool REV, int VE>
+hipError_t launch_combine_ve(const Problem& p, const float* fg, const Workspace& ws, const float* c0, int P, int cps,
+                             hipStream_t stream)
+{
+    const dim3 cgrid((unsigned)((p.dqk * p.dhv / VE + 255) / 256), (unsigned)(p.B * p.H));
+    state_combine_kernel<GATE, REV, VE><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, c0, ws.g, fg, p.H, p.T,
+                                                                   p.dqk, p.dhv, p.L, p.nc, P, cps);
+    return hipGetLastError();
+}
+
+template <int GATE, bool REV>
+hipError_t launch_combine_g(const Problem& p, const float* fg, const Workspace& ws, const float* c0, int P, int cps,
+                            hipStream_t stream)
+{
+    // d_qk d_hv is a multiple of 4096 (both multiples of 64)
+    const long per_head4 = (long)p.dqk * p.dhv / 4 / 256;
+    const long heads = (long)p.B * p.H;
+    if (per_head4 * heads >= 512) return launch_combine_ve<GATE, REV, 4>(p, fg, ws, c0, P, cps, stream);
+    if (2 * per_head4 * heads >= 512) return launch_combine_ve<GATE, REV, 2>(p, fg, ws, c0, P, cps, stream);
+    return launch_combine_ve<GATE, REV, 1>(p, fg, ws, c0, P, cps, stream);
+}
+
 template <bool REV>
 hipError_t launch_combine(const Problem& p, const float* fg, const Workspace& ws, const float* c0, int P, int cps,
                           hipStream_t stream)
 {
-    const dim3 cgrid((unsigned)((p.dqk * p.dhv / 4 + 255) / 256), (unsigned)(p.B * p.H));
     switch (p.gate) {
-    case kSig:
-        state_combine_kernel<kSig, REV><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, c0, ws.g, fg, p.H,
-                                                                   p.T, p.dqk, p.dhv, p.L, p.nc, P, cps);
-        break;
-    case kScalar:
-        state_combine_kernel<kScalar, REV><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, c0, ws.g, fg,
-                                                                      p.H, p.T, p.dqk, p.dhv, p.L, p.nc, P, cps);
-        break;
-    default:
-        state_combine_kernel<kGla, REV><<<cgrid, 256, 0, stream>>>(ws.seg_end, ws.seg_start, c0, ws.g, fg,
-                                                                     p.H, p.T, p.dqk, p.dhv, p.L, p.nc, P, cps);
-        break;
+    case kSig: return launch_combine_g<kSig, REV>(p, fg, ws, c0, P, cps, stream);
+    case kScalar: return launch_combine_g<kScalar, REV>(p, fg, ws, c0, P, cps, stream);
+    default: return launch_combine_g<kGla, REV>(p, fg, ws, c0, P, cps, stream);
     }
-    return hipGetLastError();
 }
 
 // the reverse walk's coupling partner and end-state factor, from the workspace
