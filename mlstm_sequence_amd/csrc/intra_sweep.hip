@@ -42,7 +42,11 @@ constexpr int kSweepBV = 128;   // value tile width
 
 template <int DQK> constexpr int sweep_cw() { return DQK >= 128 ? 128 : 64; }   // C^T channels per stage
 
-template <typename T, int DQK, int NW> struct SweepLds {
+// QI: the per-channel gate's inter-chunk Q fragments (q o e^{a_t}) are
+// parked in LDS when the P phase first loads q, instead of being loaded and
+// rescaled again after it (by then the chunk's q and gate rows have left L2:
+// a quarter more bytes per launch); only where it fits beside the P blocks
+template <typename T, int DQK, int NW, bool QI> struct SweepLds {
     static constexpr int kpad = 16 / sizeof(T);   // K / C^T rows: stride = 4 banks mod 32
     static constexpr int vpad = 64 / sizeof(T);   // V rows: stride = 16 banks mod 64 (transpose reads)
     static constexpr int CW = sweep_cw<DQK>();
@@ -57,6 +61,8 @@ template <typename T, int DQK, int NW> struct SweepLds {
     // entry 2 (b(b+1)/2 + m) + half
     bf16x8 p[NW * (NW + 1)][64];
     float bcol[64];                       // mLSTMsig: (li_s - a_s) log2(e) per key step of the K tile
+    // per wave and channel block: lane-owned Q fragments, read back by the lane that wrote them
+    bf16x8 qi[QI ? NW * (DQK / 16) : 1][QI ? 64 : 1];
 };
 
 // REV: the mirrored chunks of the backward pass's dv product (logical row
@@ -83,7 +89,8 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
     constexpr int NC = BV * CW / 8 / NTH;         // C^T block: 8-element items per thread
     static_assert(NK >= 1 && NV >= 1 && NC >= 1, "tile too small for the workgroup");
     typedef typename Elem<T>::frag Frag;
-    __shared__ SweepLds<T, DQK, NW> sm;
+    constexpr bool QI = GATE == kGla && NW <= 4 && std::is_same_v<T, bf16>;
+    __shared__ SweepLds<T, DQK, NW, QI> sm;
 
     const int blk = xcd_remap(blockIdx.x, gridDim.x);
     const size_t bh = blk / nc;
@@ -207,7 +214,8 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
     // e^{a_t - a_ref} in fp32 (ref_row < 0: the chunk start, where a = 0) --
     // the reference-point factorisation of the per-tile kernel
     Frag qf[KQ];
-    auto load_q = [&](int ref_row) {
+    // park: also form q o e^{a_t} (what ref_row < 0 gives) and keep it in LDS
+    auto load_q = [&](int ref_row, bool park = false) {
 #pragma unroll
         for (int kq = 0; kq < KQ; ++kq) {
             const int c = 16 * kq + 8 * hh;
@@ -218,6 +226,14 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
                 f32x4 ex[2];
                 ex[0] = *reinterpret_cast<const f32x4*>(ab + (size_t)tqc * DQK + c);
                 ex[1] = *reinterpret_cast<const f32x4*>(ab + (size_t)tqc * DQK + c + 4);
+                if constexpr (QI) {
+                    if (park) {
+                        Frag qi;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) frag_set(qi, e, frag_get(raw, e) * exp2_fast(ex[e >> 2][e & 3] * kLog2e));
+                        sm.qi[w * KQ + kq][lane] = qi;
+                    }
+                }
                 if (ref_row >= 0) {
                     ex[0] -= *reinterpret_cast<const f32x4*>(ab + (size_t)ref_row * DQK + c);
                     ex[1] -= *reinterpret_cast<const f32x4*>(ab + (size_t)ref_row * DQK + c + 4);
@@ -241,7 +257,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
         // chunk), so its reference row is its middle step, and the Q
         // fragments are rescaled to it
         const int ref_row = (GATE == kGla) ? min(s0 + 31, T_ - 1) : -1;
-        if (GATE == kGla) load_q(ref_row);
+        if (GATE == kGla) load_q(ref_row, QI && j == 0 && inter);
         __syncthreads();
         store_k(s0, ref_row);
         __syncthreads();
@@ -285,7 +301,14 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
     }
 
     // per-channel gate: the inter-chunk term takes q o e^{a_t}
-    if (GATE == kGla && inter) load_q(-1);
+    if (GATE == kGla && inter) {
+        if constexpr (QI) {
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) qf[kq] = sm.qi[w * KQ + kq][lane];
+        } else {
+            load_q(-1);
+        }
+    }
 
     // mLSTMexp: each row's factor scale / max(|scale den_t|, e^{lb_t}) with
     // den_t = sum_s P_ts + e^{a'_t} q_t . n_{k-1} (the stabilised normaliser),
