@@ -317,18 +317,24 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
                 for (int r = 0; r < 16; ++r) acc[mv][mc][r] = 0.0f;
     }
 
-    // one block: stage it, launch the next block's loads into the freed
-    // registers, multiply, and write the state at a chunk end
-    PF pf;
-    if (b0 < bend) fetch(pf, b0);
-    for (int b = b0; b < bend; ++b) {
+    // one block: stage it, launch the loads of the block DEPTH places on
+    // into the freed registers, multiply, and write the state at a chunk end.
+    // The forward walk keeps two blocks' loads in flight (two register sets,
+    // used in turn): the loads of block b+1 are still arriving while block b
+    // is staged and the loads of b+2 go out, so the CU's memory requests do
+    // not drain at every block boundary.  For 128-step blocks: the 256-step
+    // ones and the reverse walk's couplings need those registers, and the
+    // 64-step blocks ran slower with it (T = 8192 workload, L = 64: state
+    // walk 0.316 against 0.303 ms; L = 128: 0.228 against 0.240 ms).
+    constexpr int DEPTH = !REV && SB == 128 ? 2 : 1;
+    auto block = [&](PF& pf, int b) {
         const int kc = b / bpc;               // walk position; chunk(kc) is the chunk
         const bool first = (b % bpc) == 0, last = (b % bpc) == bpc - 1 || b == bend - 1;
         __syncthreads();
         store(pf, b);
         const float gk = pf.g;                // g of this block's chunk, before the next fetch overwrites it
         __syncthreads();
-        if (b + 1 < bend) fetch(pf, b + 1);
+        if (b + DEPTH < bend) fetch(pf, b + DEPTH);
         if (first) {
             // decay of the carried state across chunk kc (column c of C^T = row c of C)
 #pragma unroll
@@ -430,6 +436,19 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
             for (int mv = 0; mv < MV; ++mv)
                 for (int mc = 0; mc < MC; ++mc)
                     for (int r = 0; r < 16; ++r) dst[nat(mv, mc, r)] = acc[mv][mc][r] * wk.end_scale;
+        }
+    };
+    if constexpr (DEPTH == 1) {
+        PF pf;
+        if (b0 < bend) fetch(pf, b0);
+        for (int b = b0; b < bend; ++b) block(pf, b);
+    } else {
+        PF pfa, pfb;
+        if (b0 < bend) fetch(pfa, b0);
+        if (b0 + 1 < bend) fetch(pfb, b0 + 1);
+        for (int b = b0; b < bend; b += 2) {
+            block(pfa, b);
+            if (b + 1 < bend) block(pfb, b + 1);
         }
     }
 }
@@ -795,11 +814,14 @@ hipError_t launch_state_t(const Problem& p, const T* k, const T* v, const float*
     if (knob(TFLA_KNOB_STATE_SB) > 0) sb_cap = knob(TFLA_KNOB_STATE_SB);
     if constexpr (sizeof(T) == 2) {
         if (state_big_tiles(p)) {
-            // 256-step blocks fill the 160 KB of LDS (one workgroup per CU): only
-            // when the walk has no more workgroups than the device has CUs;
-            // otherwise 128-step blocks let two share a CU
+            // reverse walk: 256-step blocks fill the 160 KB of LDS (one
+            // workgroup per CU), only when the walk has no more workgroups than
+            // the device has CUs; otherwise 128-step blocks let two share a CU.
+            // The forward walk takes 128-step blocks with two blocks' loads in
+            // flight (T = 8192, L = 256: 0.190-0.203 against 0.199-0.207 ms
+            // with 256-step blocks and one, on two devices)
             const long wgs = (long)p.B * p.H * (p.dhv / 128) * (p.dqk / 128) * state_segments(p);
-            if (p.L >= 256 && sb_cap >= 256 && wgs <= 256)
+            if (REV && p.L >= 256 && sb_cap >= 256 && wgs <= 256)
                 return launch_state_cfg<T, 256, 128, 128, 8, REV>(p, k, v, fg, ws, stream);
             if (p.L >= 128 && sb_cap >= 128)
                 return launch_state_cfg<T, 128, 128, 128, 8, REV>(p, k, v, fg, ws, stream);
@@ -825,10 +847,9 @@ bool state_big_tiles(const Problem& p)
 
 // Segments of the chunk chain: enough workgroups for about one per CU of a
 // 256-CU device, each segment at least two chunks long; 1 when the heads
-// and tiles alone fill the device.  (One per CU rather than two: the walk
-// then takes 256-step blocks, and the combine and the fix-up move half the
-// bytes -- 0.261 ms against 0.273 ms per forward at 64 segments on the
-// T = 65536, 8-head workload.)  The state-segments knob overrides it (tests
+// and tiles alone fill the device.  (One per CU rather than two: the
+// combine and the fix-up move half the bytes -- 0.261 ms against 0.273 ms
+// per forward at 64 segments on the T = 65536, 8-head workload.)  The state-segments knob overrides it (tests
 // reach the segmented walk at small sizes with it; tuning).
 int state_segments_for(const Problem& p, long heads_tiles)
 {
