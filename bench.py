@@ -300,6 +300,11 @@ def gpu_clocks():
     """Current shader and memory clocks of GPU 0 as rocm-smi reports them
     (None where the tool is missing or prints nothing parseable)."""
     import subprocess
+    # Under rocprofv3 (ROCPROF_* set) a child process loads the profiler's
+    # tool library, which opens the device before rocm-smi's launcher
+    # re-executes itself: no clock record in profiled runs.
+    if any(k.startswith("ROCPROF_") for k in os.environ):
+        return None
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
         data = json.loads(r.stdout)
