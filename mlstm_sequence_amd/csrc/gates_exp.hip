@@ -20,9 +20,9 @@
 //   n_k   = e^{g'_k} n_{k-1} + sum_{s in k} e^{g'_k - a'_s + li'_s} k_s
 // the stabilised normaliser before each chunk (the state walk's weights,
 // same fp32 expression).  Four launches: chunk-local sums and maxima, the
-// max-state chain over chunks (one wavefront per head, serial in the
-// chunks), the per-step exponents with each chunk's normaliser
-// contribution, and the normaliser chain.
+// max-state chain over chunks (one wavefront per head, runs of chunks per
+// lane joined by a scan), the per-step exponents with each chunk's
+// normaliser contribution, and the normaliser chain (runs per wavefront).
 //
 // The input-gate pre-activation is floored at -100 (an input gate below
 // e^-100 acts as e^-100), which keeps every maximum finite; the log forget
@@ -109,28 +109,56 @@ __device__ __forceinline__ float readlane_f(float x, int j)
 
 // The max-state chain, one wavefront per head: m_k = g_k + max(m_{k-1}, U_k)
 // with m before chunk 0 taken as U_0; writes the state entering each chunk.
-// Serial in the chunks (a few instructions each); the loads of 64 chunks go
-// out together.
+// Each step is the map x -> max(x + A, B) with A = g_k, B = g_k + U_k, and
+// two such maps compose into one of the same form (A_i + A_j,
+// max(B_i + A_j, B_j)), so lane j composes the maps of its run of
+// consecutive chunks, a shuffle scan over the lanes gives the state
+// entering each run, and each lane then steps through its run writing the
+// states.  Inside a run each link is the fp32 recurrence the state walk
+// implies (its decay g' is formed from the stored m); where a run starts,
+// the entering m comes from the composed maps, whose sums of g are
+// associated differently: it can differ from a serial walk's by a few ulp,
+// which scales the carried state by e^delta against the stabiliser the
+// next chunk assumes, |delta| of that size (the normaliser and numerator
+// carry the same factor).
 __global__ __launch_bounds__(64) void gates_exp_chain_kernel(const float* __restrict__ g,
                                                              const float* __restrict__ uk,
                                                              float* __restrict__ mprev, int nc)
 {
     const size_t bh = blockIdx.x;
     const int lane = threadIdx.x;
-    float m = 0.0f;
-    for (int k0 = 0; k0 < nc; k0 += 64) {
-        const int k = k0 + lane;
-        const float gk = k < nc ? g[bh * nc + k] : 0.0f;
-        const float uv = k < nc ? uk[bh * nc + k] : 0.0f;
-        const int cnt = min(64, nc - k0);
-        float mine = 0.0f;
-        for (int j = 0; j < cnt; ++j) {
-            const float gj = readlane_f(gk, j), uj = readlane_f(uv, j);
-            if (k0 + j == 0) m = uj;
-            if (lane == j) mine = m;
-            m = gj + fmaxf(m, uj);
+    const int run = (nc + 63) / 64;
+    const int k0 = min(lane * run, nc), k1 = min(k0 + run, nc);
+    const float* gb = g + bh * nc;
+    const float* ub = uk + bh * nc;
+    const float ninf = -__builtin_inff();
+    // this lane's composed map (identity: A = 0, B = -inf)
+    float A = 0.0f, B = ninf;
+    for (int k = k0; k < k1; ++k) {
+        const float gk = gb[k];
+        B = fmaxf(B + gk, ub[k] + gk);
+        A += gk;
+    }
+    // exclusive scan of the maps over the lanes (earlier runs first)
+    float eA = A, eB = B;
+    for (int off = 1; off < 64; off <<= 1) {
+        const float pA = __shfl_up(eA, off, 64), pB = __shfl_up(eB, off, 64);
+        if (lane >= off) {
+            eB = fmaxf(pB + eA, eB);
+            eA = pA + eA;
         }
-        if (k < nc) mprev[bh * nc + k] = mine;
+    }
+    // inclusive -> exclusive: the maps of the runs before this lane's
+    float xA = __shfl_up(eA, 1, 64), xB = __shfl_up(eB, 1, 64);
+    if (lane == 0) {
+        xA = 0.0f;
+        xB = ninf;
+    }
+    const float m0 = ub[0];
+    float m = fmaxf(m0 + xA, xB);
+    for (int k = k0; k < k1; ++k) {
+        mprev[bh * nc + k] = m;
+        m = gb[k] + fmaxf(m, ub[k]);
     }
 }
 
@@ -196,34 +224,44 @@ __global__ __launch_bounds__(256) void gates_exp_final_kernel(const float* __res
     }
 }
 
-// The normaliser chain, one thread per (head, key channel):
-// n_k = e^{g'_k} n_{k-1} + npart_k, stored for chunks 0..nc-2 (the state
-// before chunk k+1), in the state walk's order of operations.
-__global__ __launch_bounds__(256) void gates_exp_norm_kernel(const float* __restrict__ g,
-                                                             const float* __restrict__ npart,
-                                                             float* __restrict__ nst, int dqk, int nc, long nthreads)
+// The normaliser chain n_k = e^{g'_k} n_{k-1} + npart_k, stored for chunks
+// 0..nc-2 (the state before chunk k+1).  A workgroup owns 64 key channels
+// of one head (a lane each) and cuts the chain into 16 runs (a wave each):
+// every wave composes its run's maps x -> d x + p from zero, the carry into
+// each run comes from composing the earlier runs' maps through LDS, and each
+// wave then steps through its run from that carry in the state walk's order
+// of operations (the first run exactly as a serial walk).
+__global__ __launch_bounds__(1024) void gates_exp_norm_kernel(const float* __restrict__ g,
+                                                              const float* __restrict__ npart,
+                                                              float* __restrict__ nst, int dqk, int nc)
 {
-    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= nthreads) return;
-    const size_t bh = idx / dqk;
-    const int c = (int)(idx % dqk);
-    constexpr int U = 8;   // chunks whose loads go out together
+    constexpr int W = 16;
+    __shared__ float sd[W][64], sp[W][64];
+    const size_t bh = blockIdx.y;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int c = blockIdx.x * 64 + lane;
+    const bool live = c < dqk;
+    const int nch = nc - 1;                      // states stored
+    const int run = (nch + W - 1) / W;
+    const int k0 = min(w * run, nch), k1 = min(k0 + run, nch);
+    const float* gb = g + bh * nc;
+    const float* pb = npart + bh * nc * (size_t)dqk + (live ? c : 0);
+    float D = 1.0f, P = 0.0f;
+    for (int k = k0; k < k1; ++k) {
+        const float d = exp2_fast(gb[k] * kLog2e);
+        P = d * P + pb[(size_t)k * dqk];
+        D *= d;
+    }
+    sd[w][lane] = D;
+    sp[w][lane] = P;
+    __syncthreads();
     float nv = 0.0f;
-    for (int k0 = 0; k0 < nc - 1; k0 += U) {
-        float gv[U], pv[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int kk = min(k0 + u, nc - 2);
-            gv[u] = g[bh * nc + kk];
-            pv[u] = npart[(bh * nc + kk) * dqk + c];
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (k0 + u < nc - 1) {
-                nv = exp2_fast(gv[u] * kLog2e) * nv + pv[u];
-                nst[(bh * (nc - 1) + k0 + u) * dqk + c] = nv;
-            }
-        }
+    for (int j = 0; j < w; ++j) nv = sd[j][lane] * nv + sp[j][lane];
+    if (!live) return;
+    float* ob = nst + bh * (size_t)nch * dqk + c;
+    for (int k = k0; k < k1; ++k) {
+        nv = exp2_fast(gb[k] * kLog2e) * nv + pb[(size_t)k * dqk];
+        ob[(size_t)k * dqk] = nv;
     }
 }
 
@@ -244,9 +282,8 @@ hipError_t launch_gates_exp(const Problem& p, const void* k, const float* igate_
                                                                 ws.li, ws.lb, ws.g, ws.mprev, ws.uk, ws.npart, p.T,
                                                                 p.dqk, p.L, p.nc);
     if (p.nc > 1) {
-        const long n = (long)p.B * p.H * p.dqk;
-        gates_exp_norm_kernel<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(ws.g, ws.npart, ws.nst, p.dqk, p.nc,
-                                                                             n);
+        const dim3 ngrid((unsigned)((p.dqk + 63) / 64), (unsigned)(p.B * p.H));
+        gates_exp_norm_kernel<<<ngrid, 1024, 0, stream>>>(ws.g, ws.npart, ws.nst, p.dqk, p.nc);
     }
     return hipGetLastError();
 }
