@@ -113,6 +113,23 @@ def test_backward_segmented_walk(variant, segments, set_knob):
     check(got, oracle_bwd(inp, dh, variant), BF, f"P={segments}")
 
 
+@pytest.mark.parametrize("variant,B,H,dqk,dhv,segments", [
+    (SIG, 1, 4, 256, 512, "3"),     # combine in 16-byte pieces, both walks
+    (SCAL, 1, 2, 256, 512, "5"),    # 8-byte pieces
+    (GLA, 4, 8, 256, 64, "3"),      # 16-byte pieces, 16 key channels per workgroup
+])
+def test_backward_segmented_walk_wide_combine(variant, B, H, dqk, dhv, segments, set_knob):
+    """Forced segments at shapes whose combine passes (the forward walk's
+    and the reverse walk's) take 8- or 16-byte pieces per thread."""
+    set_knob(tfla.KNOB_STATE_SEGMENTS, segments)
+    T, L = 64 * 13 + 5, 64
+    wl, inp = case(variant, B, H, T, dqk, dhv, BF, seed=91 + variant + H)
+    dh = W.upstream_grad(B, H, T, dhv, BF, seed=92)
+    print(f"bwd wide combine: variant={variant} B{B} H{H} {dqk}x{dhv} segments={segments}", flush=True)
+    got = gpu_bwd(inp, dh, variant, L, workspace=True)
+    check(got, oracle_bwd(inp, dh, variant), BF, f"P={segments}")
+
+
 def test_backward_chunk_size_invariance():
     """The gradients do not depend on the chunk size beyond rounding."""
     B, H, T, dqk, dhv = 1, 2, 1100, 128, 256

@@ -230,6 +230,41 @@ def test_segmented_state_walk(set_knob, segments, variant, dtype, B, H, T, dqk, 
         assert rel_err(st.cpu().double().numpy().swapaxes(-1, -2), st_ref[:, :, :nc - 1]) <= STOL[dtype]
 
 
+# The combine pass takes 4-, 8- or 16-byte pieces per thread, as many as
+# keep 512 or more workgroups (d_qk d_hv / (4 x 256) per head, times the
+# heads): these shapes reach 8 and 16 bytes, and the per-channel gate with 4
+# and 16 key channels per workgroup (d_hv = 128 and 64).
+@pytest.mark.parametrize("variant,B,H,T,dqk,dhv,L,with_c0,segments", [
+    (SIG, 1, 2, 1100, 256, 512, 64, True, "3"),     # 8-byte pieces
+    (SIG, 1, 4, 1100, 256, 512, 64, False, "7"),    # 16-byte pieces
+    (SCAL, 1, 4, 1100, 256, 512, 128, True, "3"),   # 16-byte pieces, the two-pass form
+    (GLA, 2, 8, 700, 128, 128, 64, True, "3"),      # 8-byte pieces, 4 channels per workgroup
+    (GLA, 4, 8, 700, 256, 64, 64, False, "5"),      # 16-byte pieces, 16 channels per workgroup
+])
+def test_segmented_walk_wide_combine(set_knob, variant, B, H, T, dqk, dhv, L, with_c0, segments):
+    """The segmented walk at shapes whose combine pass takes wider pieces
+    per thread: the oracle's outputs, final state and (without C_0) the
+    chunk-boundary states."""
+    set_knob(tfla.KNOB_STATE_SEGMENTS, segments)
+    wl, inp = case(variant, B, H, T, dqk, dhv, BF, seed=int(segments) * 31 + dqk + H)
+    c0 = W.initial_state(B, H, dqk, dhv, seed=3, std=1.5) if with_c0 else None
+    print(f"wide combine: {variant} B{B} H{H} T{T} {dqk}x{dhv} L{L} c0={with_c0} P={segments}", flush=True)
+    h, cf = run_state(to_dev(inp), variant, L, c0=c0)
+    h_ref, c_ref = oracle_state(inp, variant, c0)
+    assert rel_err(h_f64(h), h_ref) <= TOL[BF]
+    assert rel_err(cf.cpu().double().numpy(), c_ref) <= STOL[BF]
+    if not with_c0:
+        _, st_ref = oracle.recurrent_fwd(W.as_f64(inp["q"]), W.as_f64(inp["k"]), W.as_f64(inp["v"]),
+                                         W.as_f64(inp["igate_pre"]), W.as_f64(inp["fgate_pre"]), variant, L=L)
+        nc = -(-T // L)
+        st = torch.full((B, H, nc - 1, dhv, dqk), float("nan"), device="cuda", dtype=BF)
+        d = to_dev(inp)
+        tfla.tfla_dbg_states(d["k"], d["v"], d["igate_pre"], d["fgate_pre"], st, B, H, T, dqk, dhv, L,
+                             tfla.variant_of(GATE[variant], BF))
+        torch.cuda.synchronize()
+        assert rel_err(st.cpu().double().numpy().swapaxes(-1, -2), st_ref[:, :, :nc - 1]) <= STOL[BF]
+
+
 @pytest.mark.parametrize("variant,dtype,dqk,dhv,L,with_c0", [
     (SIG, BF, 128, 128, 64, True), (SCAL, BF, 128, 256, 64, False), (GLA, BF, 64, 128, 128, True),
     (SIG, F32, 64, 128, 64, True), (SIG, BF, 256, 512, 256, True),
