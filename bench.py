@@ -506,7 +506,7 @@ def _counter_sums(csv_path, counter):
     return sums, counts
 
 
-def write_traffic(run_dir, wl, L):
+def write_traffic(run_dir, wl, L, out_path=None):
     """HBM bytes per forward launch of each phase from four rocprofv3 --pmc
     runs under run_dir: fetch/ and write/ (FETCH_SIZE, WRITE_SIZE of
     --counter-run), copy_fetch/ and copy_write/ (the same counters of
@@ -526,7 +526,7 @@ def write_traffic(run_dir, wl, L):
     if wn.get("intra") != calls:
         raise SystemExit(f"fetch and write runs differ in forward calls ({calls} vs {wn.get('intra')})")
     model = kernel_model(wl, L)
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = out_path or os.path.join(ROOT, "profiles", "traffic.json")
     rec = json.load(open(path)) if os.path.exists(path) else {}
     print(f"Calibration: a {COPY_CAL_BYTES >> 20} MiB copy reads FETCH_SIZE = {cf['copy'] / nf['copy']:.0f} KiB "
           f"and WRITE_SIZE = {cw['copy'] / nw['copy']:.0f} KiB per dispatch: fetch scale {fetch_scale:.3f}, "
