@@ -306,7 +306,8 @@ def gpu_clocks():
     if any(k.startswith("ROCPROF_") for k in os.environ):
         return None
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True, text=True,
+                           timeout=20)
         data = json.loads(r.stdout)
     except (OSError, ValueError, subprocess.SubprocessError):
         return None
@@ -314,7 +315,7 @@ def gpu_clocks():
     if not isinstance(card, dict):
         return None
     pick = lambda key: next((v for k, v in card.items() if key in k.lower()), None)
-    return {"sclk": pick("sclk"), "mclk": pick("mclk"), "fclk": pick("fclk")}
+    return {"sclk": pick("sclk"), "mclk": pick("mclk"), "fclk": pick("fclk"), "power_w": pick("power")}
 
 
 def hbm_probe(nbytes=4 << 30, reps=10):
@@ -365,6 +366,57 @@ def hbm_probe(nbytes=4 << 30, reps=10):
     res["torch_read"] = entry(timed(lambda: src.sum()), nbytes)
     del src, dst
     return res
+
+
+def mfma_probe(iters=2000, reps=5):
+    """The rate the matrix cores reach on back-to-back 32x32x16 bf16
+    instructions with register operands (tfla_dbg_mfma: four accumulator
+    chains per wavefront, 256-thread workgroups; the best of a few grid
+    sizes), beside the specification's 2.5 PFLOP/s dense bf16."""
+    import torch
+    from mlstm_sequence_amd import tfla
+    sink = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    sweep = []
+    for wgs in (256, 512, 1024, 2048):
+        for _ in range(2):
+            tfla.tfla_dbg_mfma(iters, wgs, sink)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            tfla.tfla_dbg_mfma(iters, wgs, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        flops = wgs * 4 * 4 * iters * 32768
+        sweep.append({"workgroups": wgs, "iters": iters, "ms": ms, "flops": flops,
+                      "TFLOPs": flops / (ms * 1e-3) / 1e12, "frac_of_2.5PF": flops / (ms * 1e-3) / PEAK_BF16})
+    best = max(sweep, key=lambda x: x["TFLOPs"])
+    return {"sweep": sweep, "best": best}
+
+
+def measured_peaks():
+    """Short probes for the bench line: the matrix cores' bf16 rate and the
+    HBM read rate of the streaming probe (8 loads per thread, one
+    workgroup per CU, 2 GiB)."""
+    import torch
+    from mlstm_sequence_amd import tfla
+    m = mfma_probe(iters=1000, reps=3)["best"]
+    n = 2 << 30
+    src = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    sink = torch.empty(1024, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        tfla.tfla_dbg_stream(0, src, sink, n, 8, 256)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        tfla.tfla_dbg_stream(0, src, sink, n, 8, 256)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = n / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e9
+    del src
+    return {"mfma_bf16_tflops": m["TFLOPs"], "mfma_workgroups": m["workgroups"], "hbm_read_gbps": gbps}
 
 
 # --------------------------------------------------------------------------- CPU baseline
@@ -573,6 +625,8 @@ def main():
                          "of --config at --L (profiles/traffic.json) and print them")
     ap.add_argument("--hbm-probe", action="store_true",
                     help="only measure the HBM rate of plain streaming kernels (copy, read) and print it")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only measure the bf16 matrix-core rate of back-to-back instructions and print it")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the other workloads' lines (default workload only)")
     args = ap.parse_args()
@@ -593,6 +647,9 @@ def main():
 
     if args.hbm_probe:
         print(json.dumps({"hbm_probe": hbm_probe()}), flush=True)
+        return
+    if args.mfma_probe:
+        print(json.dumps({"mfma_probe": mfma_probe()}), flush=True)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -662,6 +719,15 @@ def main():
         "cold_cache": r["cold"],
         "gpu_clocks": {"before_sweep": clocks_before, "after_sweep": clocks_after},
     }
+    # the matrix-core and HBM rates plain probe kernels reach on this device,
+    # and the headline against them (beside the specification's peaks)
+    mp = measured_peaks()
+    mp["step_mfma_frac_of_measured"] = r["mfma_frac"] * PEAK_BF16 / (mp["mfma_bf16_tflops"] * 1e12)
+    if roof["unit"] == "GB/s":
+        mp["roofline_achieved_frac_of_measured_read"] = roof["achieved"] / mp["hbm_read_gbps"]
+    out["measured_peaks"] = mp
+    log(f"measured peaks: {mp['mfma_bf16_tflops']:.0f} TFLOP/s bf16 matrix cores, {mp['hbm_read_gbps']:.0f} GB/s "
+        f"HBM read; step at {100 * mp['step_mfma_frac_of_measured']:.1f}% of the measured matrix-core rate")
     # mLSTMexp on the same inputs and launch (TFLA research-map summary, Key
     # results: the mLSTMsig forward kernel is over 30% faster than
     # mLSTMexp's on H100): the same state walk and intra-chunk products plus

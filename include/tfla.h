@@ -341,6 +341,18 @@ int tfla_dbg_stream(int mode, const void* src, void* dst, size_t bytes, int load
                     void* stream);
 
 /*
+ * tfla_dbg_mfma -- measurement aid, not part of the computation: the rate
+ * the matrix cores reach on back-to-back 32x32x16 bf16 instructions with
+ * register operands.  `workgroups` (>= 1) workgroups of 256 threads, each
+ * wavefront running 4 independent accumulator chains of `iters` (>= 1)
+ * instructions: 4 * iters * 32768 flops per wavefront, 4 wavefronts per
+ * workgroup.  `sink`: device scratch of at least 1 KB, written only in a
+ * case that does not occur.  Asynchronous on `stream`.  Returns
+ * TFLA_ERR_INVALID_ARG for arguments out of these ranges.
+ */
+int tfla_dbg_mfma(int iters, int workgroups, void* sink, void* stream);
+
+/*
  * tfla_dbg_set_knob -- test hook: process-wide overrides of choices the
  * library otherwise makes from the problem shape, for tests that must reach
  * a particular kernel at a small size and for tuning comparisons.  `value`

@@ -121,6 +121,8 @@ bool intra_sweeps_dv(const Problem& p);   // the same for the dv product
 // or 16), `blocks` workgroups of 256 threads
 hipError_t launch_stream_probe(int mode, const void* src, void* dst, size_t bytes, int loads, int blocks,
                                hipStream_t stream);
+// back-to-back bf16 matrix instructions (4 x 32768 flops per wavefront per iteration)
+hipError_t launch_mfma_probe(int iters, int blocks, float* sink, hipStream_t stream);
 hipError_t launch_intra_sweep(const Problem& p, const void* q, const void* k, const void* v,
                               const float* fgate_pre, const Workspace& ws, void* h, hipStream_t stream);
 // The same kernel in the dv gradient mode (mirrored chunks; see launch_intra_dv).

@@ -1,10 +1,12 @@
-// probe.hip -- plain streaming kernels that measure the HBM rate a kernel on
-// this device can reach (the practical ceiling beside the specification's
-// 8 TB/s): a read of a buffer folded into one register per lane, and a
-// copy.  Each thread issues U independent 16-byte loads per round, lanes of
-// a wavefront on consecutive 16-byte pieces; the grid strides over the
-// buffer.  The rate depends on the bytes a CU keeps in flight (loads per
-// thread times waves per CU), which the caller sets with U and the grid.
+// probe.hip -- plain kernels that measure what a kernel on this device can
+// reach, beside the specification's figures.  Streaming: a read of a buffer
+// folded into one register per lane, and a copy.  Each thread issues U
+// independent 16-byte loads per round, lanes of a wavefront on consecutive
+// 16-byte pieces; the grid strides over the buffer.  The rate depends on the
+// bytes a CU keeps in flight (loads per thread times waves per CU), which the
+// caller sets with U and the grid.  Matrix cores: back-to-back 32x32x16 bf16
+// matrix instructions on register operands, four independent accumulator
+// chains per wavefront, no memory traffic.
 #include "gfx950.hpp"
 #include "kernels.hpp"
 
@@ -63,7 +65,37 @@ hipError_t probe_launch(int mode, const u32x4* src, u32x4* dst, size_t n, int bl
     return hipGetLastError();
 }
 
+// 4 chains x iters matrix instructions per wavefront (32768 flops each);
+// the operands depend on the lane so that nothing folds, and the sums are
+// stored only in a case that does not occur
+__global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* __restrict__ sink)
+{
+    constexpr int CH = 4;
+    bf16x8 a, b;
+    for (int e = 0; e < 8; ++e) {
+        a[e] = to_bf16(1.0f + 0.001f * (float)((threadIdx.x + e) & 7));
+        b[e] = to_bf16(0.5f - 0.001f * (float)((threadIdx.x * 3 + e) & 7));
+    }
+    f32x16 acc[CH];
+    for (int c = 0; c < CH; ++c)
+        for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) acc[c] = mma32(a, b, acc[c]);
+    }
+    float sum = 0.0f;
+    for (int c = 0; c < CH; ++c)
+        for (int r = 0; r < 16; ++r) sum += acc[c][r];
+    if (sum == -1.0f) sink[threadIdx.x] = sum;
+}
+
 }  // namespace
+
+hipError_t launch_mfma_probe(int iters, int blocks, float* sink, hipStream_t stream)
+{
+    probe_mfma_kernel<<<blocks, 256, 0, stream>>>(iters, sink);
+    return hipGetLastError();
+}
 
 hipError_t launch_stream_probe(int mode, const void* src, void* dst, size_t bytes, int loads, int blocks,
                                hipStream_t stream)

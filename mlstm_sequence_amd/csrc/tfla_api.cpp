@@ -792,6 +792,15 @@ int tfla_dbg_stream(int mode, const void* src, void* dst, size_t bytes, int load
     return e == hipSuccess ? TFLA_OK : hip_fail(e, "stream probe launch");
 }
 
+int tfla_dbg_mfma(int iters, int workgroups, void* sink, void* stream)
+{
+    if (iters < 1 || workgroups < 1 || !sink || !aligned(sink, 16))
+        return fail(TFLA_ERR_INVALID_ARG, "tfla_dbg_mfma: iters >= 1, workgroups >= 1, a 16-byte aligned sink");
+    const hipError_t e = tfla::launch_mfma_probe(iters, workgroups, static_cast<float*>(sink),
+                                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TFLA_OK : hip_fail(e, "matrix-core probe launch");
+}
+
 int tfla_dbg_states(const void* k, const void* v, const float* igate_pre, const float* fgate_pre, void* states_out,
                     int B, int H, int T, int d_qk, int d_hv, int L, int variant, void* stream)
 {

@@ -77,6 +77,8 @@ def lib():
         L.tfla_dbg_states.restype = i
         L.tfla_dbg_stream.argtypes = [i, vp, vp, sz, i, i, vp]
         L.tfla_dbg_stream.restype = i
+        L.tfla_dbg_mfma.argtypes = [i, i, vp, vp]
+        L.tfla_dbg_mfma.restype = i
         L.tfla_dbg_set_knob.argtypes = [i, i]
         L.tfla_dbg_set_knob.restype = i
         L.tfla_error_string.argtypes = [i]
@@ -383,6 +385,17 @@ def tfla_dbg_stream(mode, src, dst, nbytes, loads_per_thread, workgroups, stream
         raise ValueError("tfla_dbg_stream: buffers smaller than the bytes asked for")
     rc = lib().tfla_dbg_stream(mode, _ptr(src), _ptr(dst), nbytes, loads_per_thread, workgroups, _stream(stream))
     _check(rc, "tfla_dbg_stream")
+
+
+def tfla_dbg_mfma(iters, workgroups, sink, stream=None):
+    """Matrix-core probe (measurement aid): 4 * iters * 32768 flops per
+    wavefront, 4 wavefronts per workgroup; ``sink`` a CUDA tensor of at
+    least 1 KB."""
+    if not isinstance(sink, torch.Tensor) or not sink.is_cuda:
+        raise TypeError("sink must be a CUDA tensor")
+    if sink.numel() * sink.element_size() < 1024:
+        raise ValueError("tfla_dbg_mfma: sink smaller than 1 KB")
+    _check(lib().tfla_dbg_mfma(iters, workgroups, _ptr(sink), _stream(stream)), "tfla_dbg_mfma")
 
 
 def tfla_dbg_states(k, v, igate_pre, fgate_pre, states_out, B, H, T, d_qk, d_hv, L, variant, stream=None):

@@ -433,3 +433,13 @@ def test_stream_probe_rejects_bad_arguments(L):
     assert L.tfla_dbg_stream(0, Q + 8, K, 1 << 20, 4, 256, None) == INVALID  # misaligned
     assert L.tfla_dbg_stream(0, None, K, 1 << 20, 4, 256, None) == INVALID
     assert "tfla_dbg_stream" in tfla.tfla_last_error()
+
+
+def test_mfma_probe_rejects_bad_arguments(L):
+    """The matrix-core probe (a measurement aid) checks its arguments before
+    any HIP call."""
+    assert L.tfla_dbg_mfma(0, 256, Q, None) == INVALID        # no iterations
+    assert L.tfla_dbg_mfma(100, 0, Q, None) == INVALID        # no workgroups
+    assert L.tfla_dbg_mfma(100, 256, None, None) == INVALID   # no sink
+    assert L.tfla_dbg_mfma(100, 256, Q + 8, None) == INVALID  # misaligned sink
+    assert "tfla_dbg_mfma" in tfla.tfla_last_error()
