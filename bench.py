@@ -297,8 +297,9 @@ def roofline_for(wl, L, per):
 
 
 def gpu_clocks():
-    """Current shader and memory clocks of GPU 0 as rocm-smi reports them
-    (None where the tool is missing or prints nothing parseable)."""
+    """Current shader and memory clocks of GPU 0 as rocm-smi reports them,
+    and its power where it reports one (None where the tool is missing or
+    prints nothing parseable)."""
     import subprocess
     # Under rocprofv3 (ROCPROF_* set) a child process loads the profiler's
     # tool library, which opens the device before rocm-smi's launcher
