@@ -19,10 +19,13 @@
 //   lb_t  = -(a_t + M_t)          (h_t = num_t / max(|den_t|, e^{lb_t}))
 //   n_k   = e^{g'_k} n_{k-1} + sum_{s in k} e^{g'_k - a'_s + li'_s} k_s
 // the stabilised normaliser before each chunk (the state walk's weights,
-// same fp32 expression).  Four launches: chunk-local sums and maxima, the
+// same fp32 expression).  Launches: chunk-local sums and maxima, the
 // max-state chain over chunks (one wavefront per head, runs of chunks per
-// lane joined by a scan), the per-step exponents with each chunk's
-// normaliser contribution, and the normaliser chain (runs per wavefront).
+// lane joined by a scan), the per-step exponents.  The normaliser states
+// come from the state walk itself when it is not segmented (it forms
+// sum_s w_s k_s from the w.K it stages); a segmented walk takes them from
+// here: each chunk's normaliser contribution (k read once) and the
+// normaliser chain (runs per wavefront).
 //
 // The input-gate pre-activation is floored at -100 (an input gate below
 // e^-100 acts as e^-100), which keeps every maximum finite; the log forget
@@ -164,9 +167,10 @@ __global__ __launch_bounds__(64) void gates_exp_chain_kernel(const float* __rest
 
 // Per (chunk, head), 256 threads: the stabilised exponents a', li', lb, g'
 // (a and li overwritten in place: each step is read and written by one
-// thread), then the chunk's normaliser contribution sum_s w_s k_s with the
-// state walk's weight w_s = e^{g' - a'_s + li'_s}: threads own 16-byte
-// column groups of K at interleaved steps, summed over the steps through LDS.
+// thread), then (npart not NULL: a segmented state walk) the chunk's
+// normaliser contribution sum_s w_s k_s with the state walk's weight
+// w_s = e^{g' - a'_s + li'_s}: threads own 16-byte column groups of K at
+// interleaved steps, summed over the steps through LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void gates_exp_final_kernel(const float* __restrict__ ig,
                                                               const T* __restrict__ k, float* __restrict__ a,
@@ -197,9 +201,10 @@ __global__ __launch_bounds__(256) void gates_exp_final_kernel(const float* __res
         a[base + p] = ar;
         li[base + p] = lip;
         lb[base + p] = -(araw + M);
-        wsh[p] = exp2_fast((gp - ar + lip) * kLog2e);
+        if (npart) wsh[p] = exp2_fast((gp - ar + lip) * kLog2e);
     }
     if (tid == 0) g[bh * nc + kc] = gp;
+    if (!npart) return;   // the state walk forms the normaliser states itself
     __syncthreads();
     const int NG = dqk / VEC, NP = NTH / NG;   // column groups, step phases
     const int cg = tid % NG, sp = tid / NG;
@@ -271,17 +276,21 @@ hipError_t launch_gates_exp(const Problem& p, const void* k, const float* igate_
                             const Workspace& ws, hipStream_t stream)
 {
     const dim3 grid(p.nc, p.B * p.H);
+    // an unsegmented state walk forms the normaliser states beside the
+    // numerator states (from the w.K it stages), so k is not read here
+    const bool walk_n = exp_walk_normaliser(p);
+    float* npart = walk_n ? nullptr : ws.npart;
     gates_exp_local_kernel<<<grid, 64, 0, stream>>>(igate_pre, fgate_pre, ws.a, ws.li, ws.g, ws.uk, p.T, p.L, p.nc);
     gates_exp_chain_kernel<<<p.B * p.H, 64, 0, stream>>>(ws.g, ws.uk, ws.mprev, p.nc);
     if (p.bf16)
         gates_exp_final_kernel<bf16><<<grid, 256, 0, stream>>>(igate_pre, static_cast<const bf16*>(k), ws.a, ws.li,
-                                                               ws.lb, ws.g, ws.mprev, ws.uk, ws.npart, p.T, p.dqk,
+                                                               ws.lb, ws.g, ws.mprev, ws.uk, npart, p.T, p.dqk,
                                                                p.L, p.nc);
     else
         gates_exp_final_kernel<float><<<grid, 256, 0, stream>>>(igate_pre, static_cast<const float*>(k), ws.a,
-                                                                ws.li, ws.lb, ws.g, ws.mprev, ws.uk, ws.npart, p.T,
+                                                                ws.li, ws.lb, ws.g, ws.mprev, ws.uk, npart, p.T,
                                                                 p.dqk, p.L, p.nc);
-    if (p.nc > 1) {
+    if (p.nc > 1 && !walk_n) {
         const dim3 ngrid((unsigned)((p.dqk + 63) / 64), (unsigned)(p.B * p.H));
         gates_exp_norm_kernel<<<ngrid, 1024, 0, stream>>>(ws.g, ws.npart, ws.nst, p.dqk, p.nc);
     }

@@ -28,6 +28,7 @@ struct Problem {
     int gate;        // GateKind
     bool bf16;       // element type of q, k, v, h
     bool st32 = false;   // states materialised in fp32 (always for fp32 I/O)
+    bool walk_norm = false;   // mLSTMexp: the state walk also forms the normaliser states
 };
 
 // Workspace carve-up (device pointers into one allocation).
@@ -73,6 +74,9 @@ struct Workspace {
 // (1: unsegmented), chunks per segment, and whether 128x128 state tiles
 // are used.  Functions of the problem shape only.
 int state_segments(const Problem& p);
+// mLSTMexp: the (unsegmented) state walk forms the normaliser states beside
+// the numerator states, so the gate kernels leave them out
+bool exp_walk_normaliser(const Problem& p);
 int state_segments_for(const Problem& p, long heads_tiles);
 int state_chunks_per_segment(const Problem& p, int P);
 // Value-tile width of the intra-chunk kernel for an output width p.dhv

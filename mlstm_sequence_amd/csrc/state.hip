@@ -102,6 +102,9 @@ struct StateWalk {
     // init holds one state per head, read by segment 0 only (the others
     // start from zero)
     int init_first = 0;
+    // mLSTMexp, forward walk: the stabilised normaliser state after each
+    // chunk k < nc-1, [B*H][nc-1][d_qk], formed beside C (NULL: not)
+    float* nst = nullptr;
 };
 
 // Tile of C^T per workgroup: TV value rows x TC key columns; NWS wavefronts
@@ -130,8 +133,9 @@ template <typename T, int SB, int TV, int TC, int NTH> struct StatePrefetch {
     float g;                      // mLSTMsig: g of the block's chunk
 };
 
-// S: the stored state type (T, or fp32 on request)
-template <typename T, int GATE, int SB, int TV, int TC, int NWS, bool REV, typename S>
+// S: the stored state type (T, or fp32 on request); NORM: mLSTMexp's
+// forward walk, which also forms the normaliser states (wk.nst)
+template <typename T, int GATE, int SB, int TV, int TC, int NWS, bool REV, typename S, bool NORM = false>
 __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                     const float* __restrict__ a,
                                                     const float* __restrict__ li,
@@ -212,9 +216,26 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
             }
         }
     };
+    // mLSTMexp: n_k = e^{g_k} n_{k-1} + sum_{s in k} w_s k_s with the walk's
+    // weights, from the fp32 products w.K before their rounding into LDS:
+    // each thread of a first-value-tile workgroup sums its K items (one
+    // group of VEC key channels, every NTH-th item) per chunk, decayed like
+    // the state; the chunk end adds the threads' sums up per key column.
+    static_assert(!NORM || (!REV && GATE == kSig), "the normaliser rides on the forward mLSTMsig walk");
+    static_assert(64 % (TC / VEC) == 0, "a thread's K items share one channel group, the lane's");
+    static_assert(NTH * VEC * sizeof(float) <= sizeof(StateLds<T, SB, TV, TC>), "the sums fit the staging area");
+    const bool norm = NORM && v0 == 0;
+    float nrm[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) nrm[e] = 0.0f;
     auto store = [&](PF& pf, int b) {
         const int cs = chunk(b / bpc) * L;
         const int len = min(L, T_ - cs);     // steps in this chunk
+        if (norm && b % bpc == 0) {
+            const float d = exp2_fast(pf.g * kLog2e);   // the state's decay across this chunk
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) nrm[e] *= d;
+        }
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
             const int idx = tid + NTH * u, r = idx / (TV / VEC), c = (idx % (TV / VEC)) * VEC;
@@ -241,6 +262,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
                 else if (GATE == kGla) x *= exp2_fast((pf.gg[u][e / 4][e % 4] - pf.ga[u][e / 4][e % 4]) * kLog2e);
                 else x *= ws;
                 kw.set(e, live ? x : 0.0f);
+                if (norm) nrm[e] += live ? x : 0.0f;
             }
             kw.store(&sm.ks[r][c]);
         }
@@ -376,6 +398,36 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
         }
         if (last && wk.write_states && kc < nc - 1) {
             put_state(acc, REV ? nc - 2 - kc : kc + wk.soff);
+            if (norm) {
+                // n after this chunk: the threads' partial sums of each key
+                // column, added within each wavefront (lanes l, l + NG, ...
+                // hold channel group l % NG) and then over the wavefronts
+                // through LDS (the staging area is free once every thread
+                // has stored its state pieces)
+                constexpr int NG = TC / VEC;
+                float part[VEC];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    float x = nrm[e];
+#pragma unroll
+                    for (int off = NG; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+                    part[e] = x;
+                }
+                float* red = reinterpret_cast<float*>(&sm);
+                __syncthreads();
+                if (lane < NG) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) red[(w * NG + lane) * VEC + e] = part[e];
+                }
+                __syncthreads();
+                if (tid < TC) {
+                    float sum = 0.0f;
+#pragma unroll
+                    for (int j = 0; j < NWS; ++j) sum += red[(j * NG + tid / VEC) * VEC + tid % VEC];
+                    wk.nst[(bh * (nc - 1) + kc) * (size_t)dqk + c0 + tid] = sum;
+                }
+                // the next block's first barrier orders these reads before LDS is refilled
+            }
             float cpre[MV][MC][16];
             if (dot_now) {
                 if constexpr (REV) {
@@ -701,6 +753,13 @@ hipError_t launch_walk_s(const Problem& p, const T* k, const T* v, const float* 
     const S* cst = static_cast<const S*>(ws.dot_partner);
     switch (p.gate) {
     case kSig:
+        if constexpr (!REV) {
+            if (wk.nst) {
+                state_kernel<T, kSig, SB, TV, TC, NWS, REV, S, true><<<blocks, threads, 0, stream>>>(
+                    k, v, ws.a, ws.li, ws.g, fg, st, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc, cst, ws.dots);
+                break;
+            }
+        }
         state_kernel<T, kSig, SB, TV, TC, NWS, REV, S><<<blocks, threads, 0, stream>>>(
             k, v, ws.a, ws.li, ws.g, fg, st, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc, cst, ws.dots);
         break;
@@ -780,6 +839,7 @@ hipError_t launch_state_cfg(const Problem& p, const T* k, const T* v, const floa
     if (P <= 1) {
         StateWalk wk{ws.c0, ws.c_final, 1, 1, nwalk > 0 ? nwalk : 1, nwalk, soff, 0, 1, soff};
         set_rev_fields(wk, ws);
+        if (!REV && p.walk_norm) wk.nst = ws.nst;
         return launch_walk<T, SB, TV, TC, NWS, REV>(p, k, v, fg, ws, wk, stream);
     }
     const int cps = state_chunks_per_segment(p, P);
@@ -821,8 +881,10 @@ hipError_t launch_state_t(const Problem& p, const T* k, const T* v, const float*
             // flight (T = 8192, L = 256: 0.190-0.203 against 0.199-0.207 ms
             // with 256-step blocks and one, on two devices)
             const long wgs = (long)p.B * p.H * (p.dhv / 128) * (p.dqk / 128) * state_segments(p);
-            if (REV && p.L >= 256 && sb_cap >= 256 && wgs <= 256)
-                return launch_state_cfg<T, 256, 128, 128, 8, REV>(p, k, v, fg, ws, stream);
+            if constexpr (REV) {
+                if (p.L >= 256 && sb_cap >= 256 && wgs <= 256)
+                    return launch_state_cfg<T, 256, 128, 128, 8, REV>(p, k, v, fg, ws, stream);
+            }
             if (p.L >= 128 && sb_cap >= 128)
                 return launch_state_cfg<T, 128, 128, 128, 8, REV>(p, k, v, fg, ws, stream);
             return launch_state_cfg<T, 64, 128, 128, 8, REV>(p, k, v, fg, ws, stream);
@@ -880,6 +942,8 @@ int state_segments(const Problem& p)
     return state_segments_for(p, (long)p.B * p.H * (p.dhv / 64) * (p.dqk / 64));
 }
 
+bool exp_walk_normaliser(const Problem& p) { return p.gate == kExp && state_segments(p) <= 1; }
+
 int state_chunks_per_segment(const Problem& p, int P)
 {
     const int nfeed = p.nc - 1;
@@ -891,7 +955,10 @@ hipError_t launch_state(const Problem& pin, const void* k, const void* v, const 
 {
     // mLSTMexp: the mLSTMsig walk over its stabilised exponents (gates_exp.hip)
     Problem p = pin;
-    if (p.gate == kExp) p.gate = kSig;
+    if (p.gate == kExp) {
+        p.gate = kSig;
+        p.walk_norm = exp_walk_normaliser(pin);
+    }
     if (p.bf16)
         return launch_state_t<bf16, false>(p, static_cast<const bf16*>(k), static_cast<const bf16*>(v), fgate_pre,
                                            ws, stream);
