@@ -62,39 +62,44 @@ __global__ __launch_bounds__(64) void gates_sig_kernel(const float* __restrict__
     if (lane == 0) g[bh * nc + kc] = total;
 }
 
-// Per-key-channel gate, one 256-thread workgroup per (chunk, head).  A
-// thread owns 4 consecutive channels (one 16-byte piece of a step's row) and
-// 16 consecutive steps: its 16 loads go out together (a wavefront's lanes
-// cover whole 1 KB rows of 256 channels), it forms log f for its 64 values
-// and their running sums over its steps, and the segment totals of the
-// threads before it on the same channels (through LDS) give the chunk-local
-// prefix.  256 threads cover 64 steps at d_qk = 256 (128 at 128, 256 at 64);
-// longer chunks take several passes, carrying the running total per channel.
-// log f on the transcendental unit (log_sigmoid_fast): with the library
-// calls the 64 evaluations per thread, not the loads, set the kernel's time.
+// Per-key-channel gate, one 256-thread workgroup per (chunk, head, run of
+// CW key channels).  A thread owns 4 consecutive channels (one 16-byte piece
+// of a step's row) and E consecutive steps: its E loads go out together (a
+// wavefront's lanes cover whole rows of the workgroup's channels), it forms
+// log f for its 4E values and their running sums over its steps, and the
+// segment totals of the threads before it on the same channels (through
+// LDS) give the chunk-local prefix.  256 threads cover 1024 E / CW steps per
+// pass (64 at d_qk = 256 with 128-channel runs and E = 8; 128 at 128, 256 at
+// 64 with E = 16); longer chunks take several passes, carrying the running
+// total per channel.  log f on the transcendental unit (log_sigmoid_fast):
+// with the library calls the evaluations per thread, not the loads, set the
+// kernel's time.  Two workgroups per chunk at d_qk = 256 (half the loads in
+// flight per thread, twice the workgroups) measured faster than one.
+template <int E>
 __global__ __launch_bounds__(256) void gates_gla_kernel(const float* __restrict__ x,
                                                         float* __restrict__ a, float* __restrict__ g,
-                                                        int T, int dqk, int L, int nc)
+                                                        int T, int dqk, int cw, int L, int nc)
 {
-    constexpr int E = 16;                        // steps per thread
     __shared__ f32x4 tot[256];                   // [segment][channel group] totals of a pass
     __shared__ f32x4 carry[64];                  // running total per channel group
-    const int kc = blockIdx.x;
+    const int runs = dqk / cw;
+    const int kc = blockIdx.x / runs, c0 = (blockIdx.x % runs) * cw;
     const size_t bh = blockIdx.y;
     const int tid = threadIdx.x;
-    const int ncg = dqk / 4;                     // channel groups (16-byte pieces per row)
+    const int ncg = cw / 4;                      // channel groups (16-byte pieces per row)
     const int nseg = 256 / ncg;                  // step segments per pass
     const int cg = tid % ncg, seg = tid / ncg;
     const int t0 = kc * L;
     const int n = min(L, T - t0);
-    const f32x4* xb = reinterpret_cast<const f32x4*>(x + (bh * (size_t)T + t0) * dqk) + cg;
-    f32x4* ab = reinterpret_cast<f32x4*>(a + (bh * (size_t)T + t0) * dqk) + cg;
+    const size_t rs = dqk / 4;                   // row stride in 16-byte pieces
+    const f32x4* xb = reinterpret_cast<const f32x4*>(x + (bh * (size_t)T + t0) * dqk + c0) + cg;
+    f32x4* ab = reinterpret_cast<f32x4*>(a + (bh * (size_t)T + t0) * dqk + c0) + cg;
     if (tid < ncg) carry[tid] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int p0 = 0; p0 < n; p0 += nseg * E) {
         const int s0 = p0 + seg * E;             // this thread's first step
         f32x4 v[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) v[e] = xb[(size_t)min(s0 + e, n - 1) * ncg];
+        for (int e = 0; e < E; ++e) v[e] = xb[(size_t)min(s0 + e, n - 1) * rs];
         f32x4 run = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -112,12 +117,12 @@ __global__ __launch_bounds__(256) void gates_gla_kernel(const float* __restrict_
         for (int j = 0; j < seg; ++j) off += tot[j * ncg + cg];
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            if (s0 + e < n) ab[(size_t)(s0 + e) * ncg] = v[e] + off;
+            if (s0 + e < n) ab[(size_t)(s0 + e) * rs] = v[e] + off;
         __syncthreads();                         // every thread has read carry and tot
         if (seg == nseg - 1) carry[cg] = off + run;
         __syncthreads();
     }
-    if (tid < ncg) reinterpret_cast<f32x4*>(g + (bh * nc + kc) * (size_t)dqk)[tid] = carry[tid];
+    if (tid < ncg) reinterpret_cast<f32x4*>(g + (bh * nc + kc) * (size_t)dqk + c0)[tid] = carry[tid];
 }
 
 // Fixed per-head decay: a_t = (t - t0 + 1) log(gamma_h) in closed form.
@@ -146,7 +151,12 @@ hipError_t launch_gates(const Problem& p, const float* igate_pre, const float* f
     if (p.gate == kSig) {
         gates_sig_kernel<<<grid, 64, 0, stream>>>(igate_pre, fgate_pre, ws.a, ws.li, ws.g, p.T, p.L, p.nc);
     } else if (p.gate == kGla) {
-        gates_gla_kernel<<<grid, 256, 0, stream>>>(fgate_pre, ws.a, ws.g, p.T, p.dqk, p.L, p.nc);
+        if (p.dqk == 256) {
+            const dim3 g2(p.nc * 2, p.B * p.H);
+            gates_gla_kernel<8><<<g2, 256, 0, stream>>>(fgate_pre, ws.a, ws.g, p.T, p.dqk, 128, p.L, p.nc);
+        } else {
+            gates_gla_kernel<16><<<grid, 256, 0, stream>>>(fgate_pre, ws.a, ws.g, p.T, p.dqk, p.dqk, p.L, p.nc);
+        }
     } else {
         return hipSuccess;   // closed form, evaluated inside the consumers
     }
