@@ -36,6 +36,9 @@ struct Workspace {
     float* a;        // [B,H,T] (GLA: [B,H,T,dqk]) chunk-local log-forget sums; NULL for kScalar
     float* li;       // [B,H,T] log input gate; kSig only
     float* g;        // [B,H,nc] (GLA: [B,H,nc,dqk]); NULL for kScalar
+    // per-channel gate: k_t o e^{g_k - a_t} in the I/O type, the forward state
+    // walk's weighted keys, formed by the gate kernel (NULL: the walk weights K)
+    void* kw = nullptr;
     void* states;    // [B,H,ns,dhv,dqk] I/O type (fp32 when Problem::st32),
                      // transposed states before chunks (walked in fp32; the
                      // intra-chunk kernel rounds them to the I/O type for its
@@ -92,7 +95,8 @@ int state_dot_parts(const Problem& p);
 size_t workspace_layout(const Problem& p, Workspace* ws, char* base, bool with_states = true,
                         bool with_c0 = false);
 
-hipError_t launch_gates(const Problem& p, const float* igate_pre, const float* fgate_pre,
+// k: the keys, for the per-channel gate's weighted keys (ws.kw); may be NULL
+hipError_t launch_gates(const Problem& p, const void* k, const float* igate_pre, const float* fgate_pre,
                         const Workspace& ws, hipStream_t stream);
 // mLSTMexp's gate work (gates_exp.hip): fills ws.a, ws.li, ws.g with its
 // stabilised exponents and ws.lb, ws.nst (ws.npart, ws.mprev, ws.uk as

@@ -134,8 +134,11 @@ template <typename T, int SB, int TV, int TC, int NTH> struct StatePrefetch {
 };
 
 // S: the stored state type (T, or fp32 on request); NORM: mLSTMexp's
-// forward walk, which also forms the normaliser states (wk.nst)
-template <typename T, int GATE, int SB, int TV, int TC, int NWS, bool REV, typename S, bool NORM = false>
+// forward walk, which also forms the normaliser states (wk.nst); PREW: the
+// per-channel gate's forward walk reading keys the gate kernel has already
+// weighted (k points at them; no gate rows are read)
+template <typename T, int GATE, int SB, int TV, int TC, int NWS, bool REV, typename S, bool NORM = false,
+          bool PREW = false>
 __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k, const T* __restrict__ v,
                                                     const float* __restrict__ a,
                                                     const float* __restrict__ li,
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
                 pf.a[u] = a[bh * T_ + s];
                 if (!REV) pf.li[u] = li[bh * T_ + s];
             }
-            if (GATE == kGla) {
+            if (GATE == kGla && !PREW) {
                 const float* ar = a + (bh * T_ + s) * (size_t)dqk + c0 + c;
                 const float* gr = g + (bh * nc + kc) * (size_t)dqk + c0 + c;
                 for (int e4 = 0; e4 < VEC / 4; ++e4) {
@@ -222,6 +225,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
     // group of VEC key channels, every NTH-th item) per chunk, decayed like
     // the state; the chunk end adds the threads' sums up per key column.
     static_assert(!NORM || (!REV && GATE == kSig), "the normaliser rides on the forward mLSTMsig walk");
+    static_assert(!PREW || (!REV && GATE == kGla), "weighted keys: the per-channel gate's forward walk");
     static_assert(64 % (TC / VEC) == 0, "a thread's K items share one channel group, the lane's");
     static_assert(NTH * VEC * sizeof(float) <= sizeof(StateLds<T, SB, TV, TC>), "the sums fit the staging area");
     const bool norm = NORM && v0 == 0;
@@ -259,8 +263,8 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
             for (int e = 0; e < VEC; ++e) {
                 float x = pf.k[u].get(e);
                 if (GATE == kGla && REV) x *= exp2_fast(pf.ga[u][e / 4][e % 4] * kLog2e);
-                else if (GATE == kGla) x *= exp2_fast((pf.gg[u][e / 4][e % 4] - pf.ga[u][e / 4][e % 4]) * kLog2e);
-                else x *= ws;
+                else if (GATE == kGla && !PREW) x *= exp2_fast((pf.gg[u][e / 4][e % 4] - pf.ga[u][e / 4][e % 4]) * kLog2e);
+                else if (GATE != kGla) x *= ws;
                 kw.set(e, live ? x : 0.0f);
                 if (norm) nrm[e] += live ? x : 0.0f;
             }
@@ -768,6 +772,14 @@ hipError_t launch_walk_s(const Problem& p, const T* k, const T* v, const float* 
             k, v, ws.a, ws.li, ws.g, fg, st, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc, cst, ws.dots);
         break;
     default:
+        if constexpr (!REV) {
+            if (ws.kw) {   // keys weighted by the gate kernel
+                state_kernel<T, kGla, SB, TV, TC, NWS, REV, S, false, true><<<blocks, threads, 0, stream>>>(
+                    static_cast<const T*>(ws.kw), v, ws.a, ws.li, ws.g, fg, st, wk, p.H, p.T, p.dqk, p.dhv, p.L,
+                    p.nc, cst, ws.dots);
+                break;
+            }
+        }
         state_kernel<T, kGla, SB, TV, TC, NWS, REV, S><<<blocks, threads, 0, stream>>>(
             k, v, ws.a, ws.li, ws.g, fg, st, wk, p.H, p.T, p.dqk, p.dhv, p.L, p.nc, cst, ws.dots);
         break;

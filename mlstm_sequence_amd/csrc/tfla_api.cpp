@@ -226,7 +226,7 @@ int run_path(const tfla::Problem& p, const void* q, const void* k, const void* v
     int rc = mark(marks, 0, stream);
     if (rc) return rc;
     hipError_t e = p.gate == tfla::kExp ? tfla::launch_gates_exp(p, k, igate_pre, fgate_pre, ws, stream)
-                                        : tfla::launch_gates(p, igate_pre, fgate_pre, ws, stream);
+                                        : tfla::launch_gates(p, k, igate_pre, fgate_pre, ws, stream);
     if (e != hipSuccess) return hip_fail(e, "gate kernel launch");
     if ((rc = mark(marks, 1, stream))) return rc;
     e = tfla::launch_state(p, k, v, fgate_pre, ws, stream);
@@ -342,7 +342,7 @@ int run_bwd(const tfla::Problem& p, const void* q, const void* k, const void* v,
     const int nbound = p.nc - 1 + (has_g ? 1 : 0);   // chunk boundaries with a coupling
     hipError_t e;
     if (!reuse_fwd) {
-        if ((e = tfla::launch_gates(p, igate_pre, fgate_pre, ws.fwd, stream)) != hipSuccess)
+        if ((e = tfla::launch_gates(p, k, igate_pre, fgate_pre, ws.fwd, stream)) != hipSuccess)
             return hip_fail(e, "gate kernel launch");
         // forward states C_1..C_{nc-1}, [d_hv][d_qk] each (preceded by C_0 when
         // given), and C_T when a final-state gradient needs its coupling
@@ -570,6 +570,7 @@ size_t workspace_layout(const Problem& p, Workspace* ws, char* base, bool with_s
     ws->a = p.gate == kScalar ? nullptr : take(bh * p.T * w * 4);
     ws->li = per_step_li(p.gate) ? take(bh * p.T * 4) : nullptr;
     ws->g = p.gate == kScalar ? nullptr : take(bh * p.nc * w * 4);
+    ws->kw = p.gate == kGla ? take(bh * p.T * p.dqk * (p.bf16 ? 2 : 4)) : nullptr;
     if (p.gate == kExp) {
         ws->lb = take(bh * p.T * 4);
         ws->npart = take(bh * p.nc * p.dqk * 4);
@@ -772,7 +773,7 @@ int tfla_dbg_gates(const float* igate_pre, const float* fgate_pre, float* a_out,
             e = hipMemsetAsync(li_out, 0, (size_t)B * H * T * 4, s);
             if (e != hipSuccess) return hip_fail(e, "li_out clear");
         }
-        e = tfla::launch_gates(p, igate_pre, fgate_pre, ws, s);
+        e = tfla::launch_gates(p, nullptr, igate_pre, fgate_pre, ws, s);
     }
     if (e != hipSuccess) return hip_fail(e, "gate kernel launch");
     return TFLA_OK;
@@ -830,7 +831,7 @@ int tfla_dbg_states(const void* k, const void* v, const float* igate_pre, const 
     }
     tfla::workspace_layout(p, &ws, static_cast<char*>(base), false);
     ws.states = states_out;
-    e = tfla::launch_gates(p, igate_pre, fgate_pre, ws, s);
+    e = tfla::launch_gates(p, k, igate_pre, fgate_pre, ws, s);
     if (e == hipSuccess) e = tfla::launch_state(p, k, v, fgate_pre, ws, s);
     rc = e == hipSuccess ? TFLA_OK : hip_fail(e, "gate/state kernel launch");
     if (base) {

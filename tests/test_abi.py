@@ -95,7 +95,8 @@ def test_workspace_bytes(L):
     assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SIG) == sig32
     scal = a256(B * H * (nc - 1) * dhv * dqk * 2)
     assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, SCALAR | BF16) == scal
-    gla = a256(B * H * T * dqk * 4) + a256(B * H * nc * dqk * 4) + scal
+    # per-channel gate: a and g per key channel, and the walk's weighted keys in the I/O type
+    gla = a256(B * H * T * dqk * 4) + a256(B * H * nc * dqk * 4) + a256(B * H * T * dqk * 2) + scal
     assert tfla.tfla_workspace_bytes(B, H, T, dqk, dhv, Lc, GLA | BF16) == gla
     assert tfla.tfla_workspace_bytes(B, H, 64, dqk, dhv, Lc, SCALAR | BF16) == 0   # one chunk, no state
     # TFLA_STATES_FP32 (0x400): fp32 states with bf16 I/O; no effect with fp32 I/O
