@@ -76,9 +76,12 @@ __global__ __launch_bounds__(64) void gates_sig_kernel(const float* __restrict__
 // kernel's time.  Two workgroups per chunk at d_qk = 256 (half the loads in
 // flight per thread, twice the workgroups) measured faster than one.
 // With kw: the forward state walk's weighted keys k_t o e^{g_k - a_t} as
-// well, in the I/O type (the walk's own fp32 expression and rounding, so the
-// walk reads them instead of K and the gate rows and its states do not
-// change); the gate rows come back from memory, where this thread put them.
+// well, in the I/O type (the walk's own fp32 expression from the stored a
+// and g, and its rounding, so the walk reads them instead of K and the gate
+// rows and its states do not change).  A chunk of one pass forms them in
+// the pass, once the segment totals give the chunk's total; longer chunks
+// read their gate rows back after the passes (each thread the ones it
+// wrote).
 __device__ __forceinline__ f32x4 load4(const bf16* p)
 {
     const bf16x4 t = *reinterpret_cast<const bf16x4*>(p);
