@@ -14,7 +14,9 @@ must move or compute, not what the kernels happen to execute):
          intra kernel : 2 d_qk d_hv per step of chunks 2..N_c  (q C_{k-1})
                         + n(n+1)(d_qk + d_hv) per chunk of n steps (causal QK^T and PV)
   bytes  gate kernel  : gate pre-activations in, a and li out (16 B per step) + g
+                        (per-channel gate: also k in and the weighted keys out)
          state kernel : k, v of chunks 1..N_c-1 in, a and li in, states out (I/O type)
+                        (per-channel gate: the weighted keys instead of k and a)
          intra kernel : q, k, v in, h out, states in (I/O type), a and li in
 The dominant kernel (longest average duration, measured with HIP events
 recorded around each launch on the stream it runs on) is reported against
@@ -64,20 +66,45 @@ def kernel_model(wl, L):
     gchunk = {0: 4, 1: 0, 2: 4 * dqk, 3: 4}[wl.variant] * len(n)
     gin = {0: 8, 1: 0, 2: 4 * dqk, 3: 8}[wl.variant] * T
     gates = {"flops": 0, "bytes": bh * (gin + gstep * T + gchunk)}
+    # the state walk's per-step gate reads: the per-channel gate's walk reads
+    # the keys the gate kernel has weighted (k read and kw written there,
+    # 2 d_qk e B per step) instead of K and the gate rows
+    gwalk = gstep
+    if wl.variant == 2:
+        gates["bytes"] += bh * T * 2 * dqk * e
+        gwalk = 0
+    nst_bytes = 0
     if wl.variant == 3:
-        # mLSTMexp's four gate launches: a and the prefix maxima written, read
-        # back with igate_pre and rewritten with the lower bound (+ 8 + 12 + 12
-        # B per step), k read once for the normaliser contributions, which are
-        # written, read and turned into normaliser states (3 x 4 d_qk B per chunk)
-        gates["bytes"] += bh * (T * (32 + dqk * e) + 3 * 4 * dqk * len(n))
+        # mLSTMexp's gate launches: a and the prefix maxima written, read back
+        # with igate_pre and rewritten with the lower bound (+ 8 + 12 + 12 B per
+        # step); the normaliser states are formed by the walk (4 d_qk B per
+        # stored state) unless it is segmented, when k is read once more for
+        # the normaliser contributions, which are written, read and turned
+        # into normaliser states (3 x 4 d_qk B per chunk)
+        gates["bytes"] += bh * T * 32
+        if state_walk_segmented(wl, L):
+            gates["bytes"] += bh * (T * dqk * e + 3 * 4 * dqk * len(n))
+        else:
+            nst_bytes = 4 * dqk * (len(n) - 1)
     state = {"flops": bh * 2 * dqk * dhv * steps_state,
-             "bytes": bh * ((dqk + dhv) * e * steps_state + gstep * steps_state + gchunk + st_bytes)}
+             "bytes": bh * ((dqk + dhv) * e * steps_state + gwalk * steps_state + gchunk + st_bytes + nst_bytes)}
     intra_f = 2 * dqk * dhv * steps_inter + sum(m * (m + 1) * (dqk + dhv) for m in n)
     # mLSTMexp also reads its lower bound per step and the normaliser state per chunk
     exp_extra = (4 * T + 4 * dqk * (len(n) - 1)) if wl.variant == 3 else 0
     intra = {"flops": bh * intra_f,
              "bytes": bh * ((2 * dqk + dhv) * e * T + dhv * e * T + st_bytes + gstep * T + exp_extra)}
     return {"gates": gates, "state": state, "intra": intra}
+
+
+def state_walk_segmented(wl, L):
+    """Whether the library cuts the state walk into segments (few heads
+    and tiles for the 256 CUs, at least four chunks feeding a state)."""
+    nfeed = -(-wl.T // L) - 1
+    if nfeed < 4:
+        return False
+    t = 128 if (wl.dtype_name == "bf16" and wl.dqk % 128 == 0 and wl.dhv % 128 == 0) else 64
+    heads_tiles = wl.B * wl.H * (wl.dhv // t) * (wl.dqk // t)
+    return heads_tiles < 256 and min(-(-256 // heads_tiles), nfeed // 2) >= 2
 
 
 def total_flops(wl, L):
