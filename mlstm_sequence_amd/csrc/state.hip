@@ -27,7 +27,10 @@
 // reads.  The block loop is software-pipelined: the next block's loads are
 // issued into registers right after the current block reached LDS.  Blocks
 // are as long as the chunk allows (up to 256 steps on 128x128 tiles).
-// States leave as 128-byte rows.
+// States leave as 128-byte rows.  For the per-channel gate the forward walk
+// reads keys the gate kernel has already weighted (the same fp32 expression
+// and rounding it would apply), not K and the fp32 gate rows; for mLSTMexp
+// it also sums w.K per key channel into the normaliser states.
 //
 // Few heads and long sequences leave most CUs idle on that serial walk.
 // Then the chunk chain is cut into P segments (sequence parallelism on one
