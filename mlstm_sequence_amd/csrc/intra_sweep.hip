@@ -46,21 +46,23 @@ template <int DQK> constexpr int sweep_cw() { return DQK >= 128 ? 128 : 64; }   
 // parked in LDS when the P phase first loads q, instead of being loaded and
 // rescaled again after it (by then the chunk's q and gate rows have left L2:
 // a quarter more bytes per launch); only where it fits beside the P blocks
-template <typename T, int DQK, int NW, bool QI> struct SweepLds {
+// DB: two stage buffers, used in turn (see the kernel's stage order)
+template <typename T, int DQK, int NW, bool QI, bool DB> struct SweepLds {
     static constexpr int kpad = 16 / sizeof(T);   // K / C^T rows: stride = 4 banks mod 32
     static constexpr int vpad = 64 / sizeof(T);   // V rows: stride = 16 banks mod 64 (transpose reads)
     static constexpr int CW = sweep_cw<DQK>();
-    union {
+    union Stage {
         T ks[64][DQK + kpad];             // K tile [step][channel]
         T vs[64][kSweepBV + vpad];        // V tile [step][value]
         T cs[kSweepBV][CW + kpad];        // C^T block [value][channel]
         T os[NW][32][64 + kpad];          // per wave: 32 output rows x 64 columns on their way out
     };
+    Stage st[DB ? 2 : 1];
     // P fragments: the wave with row block b owns the 32-key blocks m <= b
     // of its rows, two 16-key halves each, one 16-byte fragment per lane:
     // entry 2 (b(b+1)/2 + m) + half
     bf16x8 p[NW * (NW + 1)][64];
-    float bcol[64];                       // mLSTMsig: (li_s - a_s) log2(e) per key step of the K tile
+    float bcol[DB ? 2 : 1][64];           // mLSTMsig: (li_s - a_s) log2(e) per key step of the K tile
     // per wave and channel block: lane-owned Q fragments, read back by the lane that wrote them
     bf16x8 qi[QI ? NW * (DQK / 16) : 1][QI ? 64 : 1];
 };
@@ -90,7 +92,20 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
     static_assert(NK >= 1 && NV >= 1 && NC >= 1, "tile too small for the workgroup");
     typedef typename Elem<T>::frag Frag;
     constexpr bool QI = GATE == kGla && NW <= 4 && std::is_same_v<T, bf16>;
-    __shared__ SweepLds<T, DQK, NW, QI> sm;
+    // DB (eight waves, an even number of C^T blocks): stage i is written into
+    // buffer i mod 2 while the waves may still read stage i - 1 from the other,
+    // so one barrier per stage (after the write) suffices.  Every stage count
+    // per phase is even (K tiles, C^T blocks, V tiles), so a stage's buffer is
+    // its index in its phase mod 2 and the last V tile of a value tile sits in
+    // buffer 1, where the output blocks then go while the next stage is
+    // written into buffer 0.  EARLY: the loads of stage i + 1 leave before that
+    // barrier rather than after it (mLSTMexp only: for the other gates it
+    // costs spilled registers and measured slower)
+    constexpr bool DB = NW == 8 && (DQK / CW) % 2 == 0;
+    constexpr bool EARLY = DB && GATE == kExp;
+    __shared__ SweepLds<T, DQK, NW, QI, DB> sm;
+    static_assert(sizeof(sm) <= 160 * 1024, "LDS");
+    static_assert(!DB || (NKV % 2 == 0), "stage parity");
 
     const int blk = xcd_remap(blockIdx.x, gridDim.x);
     const size_t bh = blk / nc;
@@ -145,7 +160,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
     };
     // per-channel gate: k scaled by e^{a_ref - a_s} in fp32 (factor <= 1 for
     // keys before the reference row) before its one rounding into LDS
-    auto store_k = [&](int s0, int ref_row) {
+    auto store_k = [&](int s0, int ref_row, int b) {
 #pragma unroll
         for (int u = 0; u < NK; ++u) {
             const int idx = tid + NTH * u, r = idx / (DQK / VEC), c = (idx % (DQK / VEC)) * VEC;
@@ -160,9 +175,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
                         pk[u].set(4 * e4 + e, pk[u].get(4 * e4 + e) * exp2_fast((er[e] - es[e]) * kLog2e));
                 }
             }
-            pk[u].store(&sm.ks[r][c]);
+            pk[u].store(&sm.st[b].ks[r][c]);
         }
-        if (per_step_li(GATE) && tid < 64) sm.bcol[tid] = (REV ? pli : pli - pa) * kLog2e;
+        if (per_step_li(GATE) && tid < 64) sm.bcol[b][tid] = (REV ? pli : pli - pa) * kLog2e;
     };
     auto fetch_c = [&](int v0, int cb) {
 #pragma unroll
@@ -173,19 +188,19 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
             for (int x = 0; x < 8 / SVEC; ++x) pc[u][x].load(src + SVEC * x);
         }
     };
-    auto store_c = [&]() {
+    auto store_c = [&](int b) {
 #pragma unroll
         for (int u = 0; u < NC; ++u) {
             const int idx = tid + NTH * u, vr = idx / (CW / 8), c8 = (idx % (CW / 8)) * 8;
             if constexpr (std::is_same_v<S, T>) {
 #pragma unroll
-                for (int x = 0; x < 8 / VEC; ++x) pc[u][x].store(&sm.cs[vr][c8 + VEC * x]);
+                for (int x = 0; x < 8 / VEC; ++x) pc[u][x].store(&sm.st[b].cs[vr][c8 + VEC * x]);
             } else {
                 // fp32 states, bf16 operands: RNE on the way into LDS
                 Vec16<T> y;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) y.set(e, pc[u][e / SVEC].get(e % SVEC));
-                y.store(&sm.cs[vr][c8]);
+                y.store(&sm.st[b].cs[vr][c8]);
             }
         }
     };
@@ -196,11 +211,11 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
             pv[u].load(vb + (size_t)row(min(s0 + r, T_ - 1)) * dhv + v0 + c);
         }
     };
-    auto store_v = [&]() {
+    auto store_v = [&](int b) {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int idx = tid + NTH * u, r = idx / (BV / VEC), c = (idx % (BV / VEC)) * VEC;
-            pv[u].store(&sm.vs[r][c]);
+            pv[u].store(&sm.st[b].vs[r][c]);
         }
     };
     // the first stage of value tile nv
@@ -258,11 +273,16 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
         // fragments are rescaled to it
         const int ref_row = (GATE == kGla) ? min(s0 + 31, T_ - 1) : -1;
         if (GATE == kGla) load_q(ref_row, QI && j == 0 && inter);
+        const int b = DB ? j & 1 : 0;
+        auto next = [&]() {
+            if (j + 1 < NKV) fetch_k(s0 + 64);
+            else fetch_first(0);
+        };
+        if constexpr (!DB) __syncthreads();
+        store_k(s0, ref_row, b);
+        if constexpr (EARLY) next();
         __syncthreads();
-        store_k(s0, ref_row);
-        __syncthreads();
-        if (j + 1 < NKV) fetch_k(s0 + 64);
-        else fetch_first(0);
+        if constexpr (!EARLY) next();
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             const int slo = s0 + 32 * mt;
@@ -273,7 +293,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
             for (int r = 0; r < 16; ++r) st[r] = 0.0f;
 #pragma unroll
             for (int kq = 0; kq < KQ; ++kq) {
-                const Frag af = load8(&sm.ks[32 * mt + i32][16 * kq + 8 * hh]);
+                const Frag af = load8(&sm.st[b].ks[32 * mt + i32][16 * kq + 8 * hh]);
                 st = mma32(af, qf[kq], st);
             }
             // decay and causal mask: element r is key step slo + sr, query row tlo + i32
@@ -281,7 +301,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
             for (int r = 0; r < 16; ++r) {
                 const int sr = 8 * (r >> 2) + 4 * hh + (r & 3);
                 float p = st[r];
-                if (per_step_li(GATE)) p *= exp2_fast(at2 + sm.bcol[32 * mt + sr]);
+                if (per_step_li(GATE)) p *= exp2_fast(at2 + sm.bcol[b][32 * mt + sr]);
                 else if (GATE == kScalar) p *= exp2_fast((float)(tlo + i32 - slo - sr) * lg2);
                 st[r] = (diag && sr > i32) ? 0.0f : p;
             }
@@ -348,16 +368,21 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
         if (inter) {
             // e^{a_t} q_t^T C_{k-1}
             for (int cb = 0; cb < DQK; cb += CW) {
+                const int b = DB ? (cb / CW) & 1 : 0;
+                auto next = [&]() {
+                    if (cb + CW < DQK) fetch_c(v0, cb + CW);
+                    else fetch_v(v0, cs);
+                };
+                if constexpr (!DB) __syncthreads();
+                store_c(b);
+                if constexpr (EARLY) next();
                 __syncthreads();
-                store_c();
-                __syncthreads();
-                if (cb + CW < DQK) fetch_c(v0, cb + CW);
-                else fetch_v(v0, cs);
+                if constexpr (!EARLY) next();
 #pragma unroll
                 for (int kk = 0; kk < CW / 16; ++kk) {
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) {
-                        const Frag bf = load8(&sm.cs[32 * nt + i32][16 * kk + 8 * hh]);
+                        const Frag bf = load8(&sm.st[b].cs[32 * nt + i32][16 * kk + 8 * hh]);
                         acc[nt] = mma32(qf[cb / 16 + kk], bf, acc[nt]);
                     }
                 }
@@ -376,11 +401,16 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
         // + P V, key tile by key tile
         for (int j = 0; j < NKV; ++j) {
             const int s0 = cs + 64 * j;
+            const int b = DB ? j & 1 : 0;
+            auto next = [&]() {
+                if (j + 1 < NKV) fetch_v(v0, s0 + 64);
+                else if (nv + 1 < nvt) fetch_first(nv + 1);
+            };
+            if constexpr (!DB) __syncthreads();
+            store_v(b);
+            if constexpr (EARLY) next();
             __syncthreads();
-            store_v();
-            __syncthreads();
-            if (j + 1 < NKV) fetch_v(v0, s0 + 64);
-            else if (nv + 1 < nvt) fetch_first(nv + 1);
+            if constexpr (!EARLY) next();
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 const int slo = s0 + 32 * mt;
@@ -391,7 +421,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
                     const Frag pfr = pw[2 * m + half][lane];
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) {
-                        const Frag vf = frag_tr(sm.vs, 32 * mt + 16 * half, 32 * nt, lane);
+                        const Frag vf = frag_tr(sm.st[b].vs, 32 * mt + 16 * half, 32 * nt, lane);
                         acc[nt] = mma32(pfr, vf, acc[nt]);
                     }
                 }
@@ -404,7 +434,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
         T* const hrow = hbase + v0;
 #pragma unroll
         for (int ph = 0; ph < NT / 2; ++ph) {
-            auto os = sm.os[w];
+            auto os = sm.st[DB ? (NKV - 1) & 1 : 0].os[w];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -425,7 +455,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
                 }
             }
             // this block is read before it is overwritten (the next half, or
-            // the next value tile's first stage after its own barrier)
+            // the next value tile's first stage after its own barrier; with
+            // two buffers that stage goes to the other one, and the stage
+            // after it waits for the first one's barrier)
             if (ph + 1 < NT / 2) __syncthreads();
         }
     }
