@@ -423,6 +423,48 @@ def mfma_probe(iters=2000, reps=5):
     return {"sweep": sweep, "best": best}
 
 
+LDS_PROBE_MODES = {0: "16-byte row reads", 1: "transpose reads", 2: "16-byte row reads, each feeding one 32x32x16",
+                   3: "transpose reads, each feeding one 32x32x16", 4: "32x32x16 on a register operand"}
+
+
+def lds_probe(iters=4000, reps=3):
+    """How fast a CU serves the intra-chunk kernels' LDS operand reads, alone
+    and each feeding one 32x32x16 bf16 instruction (tfla_dbg_lds: one
+    workgroup per CU, 256 workgroups; cycles from the shader clock inside
+    each workgroup, median over workgroups, best of `reps` launches).  At
+    2.5 PFLOP/s a CU completes one such instruction per SIMD every 32 cycles,
+    and an instruction whose A operand comes from LDS takes 1 KB of it: 128
+    bytes per cycle per CU at full rate."""
+    import torch
+    from mlstm_sequence_amd import tfla
+    n = 256
+    clocks = torch.zeros(2 * n, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    out = []
+    for waves in (4, 8):
+        for mode in range(5):
+            best = None
+            for _ in range(reps + 1):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                tfla.tfla_dbg_lds(mode, waves, iters, n, clocks, sink)
+                e1.record()
+                torch.cuda.synchronize()
+                c = clocks.view(n, 2).cpu()
+                cyc = sorted((c[:, 1] - c[:, 0]).tolist())
+                r = (cyc[n // 2], cyc[0], cyc[-1], e0.elapsed_time(e1))
+                if best is None or r[0] < best[0]:
+                    best = r
+            med, lo, hi, ms = best
+            lds_bytes = waves * iters * 8 * 1024 if mode < 4 else 0
+            mfma = waves * iters * 8 if mode >= 2 else 0
+            out.append({"mode": mode, "what": LDS_PROBE_MODES[mode], "waves": waves, "iters": iters,
+                        "cycles_median": med, "cycles_min": lo, "cycles_max": hi, "launch_ms": ms,
+                        "lds_bytes_per_cycle_per_cu": lds_bytes / med,
+                        "mfma_busy": mfma * 32 / (med * 4)})
+    return out
+
+
 def measured_peaks():
     """Short probes for the bench line: the matrix cores' bf16 rate and the
     HBM read rate of the streaming probe (8 loads per thread, one
@@ -653,6 +695,8 @@ def main():
                          "of --config at --L (profiles/traffic.json) and print them")
     ap.add_argument("--hbm-probe", action="store_true",
                     help="only measure the HBM rate of plain streaming kernels (copy, read) and print it")
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="LDS operand-read rates alone and feeding the matrix cores (tfla_dbg_lds), then exit")
     ap.add_argument("--mfma-probe", action="store_true",
                     help="only measure the bf16 matrix-core rate of back-to-back instructions and print it")
     ap.add_argument("--no-workloads", action="store_true",
@@ -675,6 +719,10 @@ def main():
 
     if args.hbm_probe:
         print(json.dumps({"hbm_probe": hbm_probe()}), flush=True)
+        return
+    if args.lds_probe:
+        for r in lds_probe():
+            print(json.dumps({"lds_probe": r}), flush=True)
         return
     if args.mfma_probe:
         print(json.dumps({"mfma_probe": mfma_probe()}), flush=True)

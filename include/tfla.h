@@ -353,6 +353,24 @@ int tfla_dbg_stream(int mode, const void* src, void* dst, size_t bytes, int load
 int tfla_dbg_mfma(int iters, int workgroups, void* sink, void* stream);
 
 /*
+ * tfla_dbg_lds -- measurement aid, not part of the computation: the rate at
+ * which a CU serves the LDS operand reads of the intra-chunk kernels, alone
+ * and each feeding one 32x32x16 bf16 matrix instruction.  `workgroups` (>= 1)
+ * workgroups of `waves` (4 or 8) wavefronts, each holding 96 KB of LDS (one
+ * per CU); every wavefront runs `iters` (>= 1) iterations of 8 fragment reads
+ * of 1 KB (64 lanes x 16 bytes): mode 0 16-byte row reads of a 64 x 264 bf16
+ * tile, mode 1 transpose reads (ds_read_b64_tr_b16) of a 64 x 160 tile, modes
+ * 2 and 3 the same with each fragment the A operand of one matrix
+ * instruction (4 independent accumulator chains), mode 4 the 8 instructions
+ * alone on a register operand.  `clocks` (device, 2 * workgroups uint64):
+ * the shader clock of each workgroup before and after its loop, both after a
+ * barrier.  `sink`: device scratch of at least 2 KB, written only in a case
+ * that does not occur.  Asynchronous on `stream`.  Returns
+ * TFLA_ERR_INVALID_ARG for arguments out of these ranges.
+ */
+int tfla_dbg_lds(int mode, int waves, int iters, int workgroups, void* clocks, void* sink, void* stream);
+
+/*
  * tfla_dbg_set_knob -- test hook: process-wide overrides of choices the
  * library otherwise makes from the problem shape, for tests that must reach
  * a particular kernel at a small size and for tuning comparisons.  `value`

@@ -131,6 +131,8 @@ hipError_t launch_stream_probe(int mode, const void* src, void* dst, size_t byte
                                hipStream_t stream);
 // back-to-back bf16 matrix instructions (4 x 32768 flops per wavefront per iteration)
 hipError_t launch_mfma_probe(int iters, int blocks, float* sink, hipStream_t stream);
+hipError_t launch_lds_probe(int mode, int waves, int iters, int blocks, unsigned long long* out, float* sink,
+                            hipStream_t stream);
 hipError_t launch_intra_sweep(const Problem& p, const void* q, const void* k, const void* v,
                               const float* fgate_pre, const Workspace& ws, void* h, hipStream_t stream);
 // The same kernel in the dv gradient mode (mirrored chunks; see launch_intra_dv).

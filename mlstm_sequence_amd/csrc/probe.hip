@@ -6,7 +6,10 @@
 // bytes a CU keeps in flight (loads per thread times waves per CU), which the
 // caller sets with U and the grid.  Matrix cores: back-to-back 32x32x16 bf16
 // matrix instructions on register operands, four independent accumulator
-// chains per wavefront, no memory traffic.
+// chains per wavefront, no memory traffic.  LDS: the operand reads of the
+// intra-chunk kernels (16-byte rows of a padded K tile, transpose reads of a
+// padded V tile), alone or each feeding one 32x32x16 instruction, timed in
+// shader-clock cycles inside one workgroup per CU.
 #include "gfx950.hpp"
 #include "kernels.hpp"
 
@@ -89,7 +92,74 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* __res
     if (sum == -1.0f) sink[threadIdx.x] = sum;
 }
 
+// LDS operand reads as the intra-chunk kernels issue them.  96 KB of LDS per
+// workgroup (one workgroup per CU); rows 0..63 of a K tile with 264-element
+// rows and of a V tile with 160-element rows (the kernels' padding).  Per
+// iteration each wavefront reads 8 fragments of 1 KB: MODE 0 16-byte rows of
+// the K tile, MODE 1 transpose reads of the V tile; MODE 2 and 3 the same,
+// each fragment the A operand of one 32x32x16 instruction (4 accumulator
+// chains); MODE 4 the instructions alone on a register operand.  Thread 0
+// stores the shader clock before and after the loop, both taken after a
+// barrier: out[2 b], out[2 b + 1].
+template <int MODE>
+__global__ __launch_bounds__(512) void probe_lds_kernel(int iters, unsigned long long* __restrict__ out,
+                                                        float* __restrict__ sink)
+{
+    constexpr int N = 96 * 1024 / 2;
+    __shared__ __attribute__((aligned(16))) bf16 lds[N];
+    for (int i = threadIdx.x; i < N; i += blockDim.x) lds[i] = to_bf16(0.001f * (float)(i & 15));
+    const bf16 (*ks)[264] = reinterpret_cast<const bf16 (*)[264]>(lds);
+    const bf16 (*vs)[160] = reinterpret_cast<const bf16 (*)[160]>(lds + 64 * 264);
+    const int lane = threadIdx.x & 63, i32 = lane & 31, hh = lane >> 5;
+    f32x16 acc[4];
+    for (int c = 0; c < 4; ++c)
+        for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    __syncthreads();
+    // the register operand comes from LDS too, so that every mode holds the 96 KB
+    const bf16x8 qf = load8(&lds[(lane * 8) & (N - 1)]);
+    const unsigned long long t0 = clock64();
+    for (int it = 0; it < iters; ++it) {
+        asm volatile("" ::: "memory");   // the reads stay inside the loop
+        const int mt = it & 1;
+#pragma unroll
+        for (int kq = 0; kq < 8; ++kq) {
+            bf16x8 f;
+            if constexpr (MODE == 0 || MODE == 2) f = load8(&ks[32 * mt + i32][16 * kq + 8 * hh]);
+            else if constexpr (MODE == 1 || MODE == 3) f = frag_tr(vs, 16 * (kq & 3), 32 * (kq >> 2) + 64 * mt, lane);
+            else f = qf;
+            if constexpr (MODE >= 2) acc[kq & 3] = mma32(f, qf, acc[kq & 3]);
+            else x ^= __builtin_bit_cast(u32x4, f);
+        }
+    }
+    __syncthreads();
+    const unsigned long long t1 = clock64();
+    if (threadIdx.x == 0) {
+        out[2 * blockIdx.x] = t0;
+        out[2 * blockIdx.x + 1] = t1;
+    }
+    float sum = 0.0f;
+    for (int c = 0; c < 4; ++c)
+        for (int r = 0; r < 16; ++r) sum += acc[c][r];
+    if (sum == -1.0f || (x.x ^ x.y ^ x.z ^ x.w) == 0x9e3779b9u) sink[threadIdx.x] = sum;
+}
+
 }  // namespace
+
+hipError_t launch_lds_probe(int mode, int waves, int iters, int blocks, unsigned long long* out, float* sink,
+                            hipStream_t stream)
+{
+    const int nt = 64 * waves;
+    switch (mode) {
+    case 0: probe_lds_kernel<0><<<blocks, nt, 0, stream>>>(iters, out, sink); break;
+    case 1: probe_lds_kernel<1><<<blocks, nt, 0, stream>>>(iters, out, sink); break;
+    case 2: probe_lds_kernel<2><<<blocks, nt, 0, stream>>>(iters, out, sink); break;
+    case 3: probe_lds_kernel<3><<<blocks, nt, 0, stream>>>(iters, out, sink); break;
+    case 4: probe_lds_kernel<4><<<blocks, nt, 0, stream>>>(iters, out, sink); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_mfma_probe(int iters, int blocks, float* sink, hipStream_t stream)
 {

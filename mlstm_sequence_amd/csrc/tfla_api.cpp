@@ -802,6 +802,19 @@ int tfla_dbg_mfma(int iters, int workgroups, void* sink, void* stream)
     return e == hipSuccess ? TFLA_OK : hip_fail(e, "matrix-core probe launch");
 }
 
+int tfla_dbg_lds(int mode, int waves, int iters, int workgroups, void* clocks, void* sink, void* stream)
+{
+    if (mode < 0 || mode > 4 || (waves != 4 && waves != 8) || iters < 1 || workgroups < 1 || !clocks ||
+        !aligned(clocks, 8) || !sink || !aligned(sink, 16))
+        return fail(TFLA_ERR_INVALID_ARG,
+                    "tfla_dbg_lds: mode 0..4, waves 4 or 8, iters >= 1, workgroups >= 1, 8-byte aligned clocks, "
+                    "a 16-byte aligned sink");
+    const hipError_t e = tfla::launch_lds_probe(mode, waves, iters, workgroups,
+                                                static_cast<unsigned long long*>(clocks), static_cast<float*>(sink),
+                                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TFLA_OK : hip_fail(e, "LDS probe launch");
+}
+
 int tfla_dbg_states(const void* k, const void* v, const float* igate_pre, const float* fgate_pre, void* states_out,
                     int B, int H, int T, int d_qk, int d_hv, int L, int variant, void* stream)
 {

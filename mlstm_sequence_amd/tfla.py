@@ -79,6 +79,8 @@ def lib():
         L.tfla_dbg_stream.restype = i
         L.tfla_dbg_mfma.argtypes = [i, i, vp, vp]
         L.tfla_dbg_mfma.restype = i
+        L.tfla_dbg_lds.argtypes = [i, i, i, i, vp, vp, vp]
+        L.tfla_dbg_lds.restype = i
         L.tfla_dbg_set_knob.argtypes = [i, i]
         L.tfla_dbg_set_knob.restype = i
         L.tfla_error_string.argtypes = [i]
@@ -396,6 +398,21 @@ def tfla_dbg_mfma(iters, workgroups, sink, stream=None):
     if sink.numel() * sink.element_size() < 1024:
         raise ValueError("tfla_dbg_mfma: sink smaller than 1 KB")
     _check(lib().tfla_dbg_mfma(iters, workgroups, _ptr(sink), _stream(stream)), "tfla_dbg_mfma")
+
+
+def tfla_dbg_lds(mode, waves, iters, workgroups, clocks, sink, stream=None):
+    """LDS probe (measurement aid): ``clocks`` an int64 CUDA tensor of at
+    least 2 * workgroups elements (shader clock before / after each
+    workgroup's loop), ``sink`` a CUDA tensor of at least 2 KB."""
+    for name, t in (("clocks", clocks), ("sink", sink)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{name} must be a CUDA tensor")
+    if clocks.dtype != torch.int64 or clocks.numel() < 2 * workgroups:
+        raise ValueError("tfla_dbg_lds: clocks must be int64 with 2 * workgroups elements")
+    if sink.numel() * sink.element_size() < 2048:
+        raise ValueError("tfla_dbg_lds: sink smaller than 2 KB")
+    _check(lib().tfla_dbg_lds(mode, waves, iters, workgroups, _ptr(clocks), _ptr(sink), _stream(stream)),
+           "tfla_dbg_lds")
 
 
 def tfla_dbg_states(k, v, igate_pre, fgate_pre, states_out, B, H, T, d_qk, d_hv, L, variant, stream=None):

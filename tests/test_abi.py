@@ -444,3 +444,16 @@ def test_mfma_probe_rejects_bad_arguments(L):
     assert L.tfla_dbg_mfma(100, 256, None, None) == INVALID   # no sink
     assert L.tfla_dbg_mfma(100, 256, Q + 8, None) == INVALID  # misaligned sink
     assert "tfla_dbg_mfma" in tfla.tfla_last_error()
+
+
+def test_lds_probe_rejects_bad_arguments(L):
+    """The LDS probe (a measurement aid) checks its arguments before any HIP
+    call."""
+    assert L.tfla_dbg_lds(5, 8, 100, 256, Q, K, None) == INVALID       # no such mode
+    assert L.tfla_dbg_lds(0, 6, 100, 256, Q, K, None) == INVALID       # 6 waves
+    assert L.tfla_dbg_lds(0, 8, 0, 256, Q, K, None) == INVALID         # no iterations
+    assert L.tfla_dbg_lds(0, 8, 100, 0, Q, K, None) == INVALID         # no workgroups
+    assert L.tfla_dbg_lds(0, 8, 100, 256, None, K, None) == INVALID    # no clock buffer
+    assert L.tfla_dbg_lds(0, 8, 100, 256, Q + 4, K, None) == INVALID   # misaligned clock buffer
+    assert L.tfla_dbg_lds(0, 8, 100, 256, Q, K + 8, None) == INVALID   # misaligned sink
+    assert "tfla_dbg_lds" in tfla.tfla_last_error()
