@@ -75,6 +75,7 @@
 // one per key channel (the row dot of D_m and C_m in that channel),
 // [B*H][nc-1][d_qk][value tiles x 2].
 #include <algorithm>
+#include <type_traits>
 
 #include "gfx950.hpp"
 #include "kernels.hpp"
@@ -134,6 +135,7 @@ template <typename T, int SB, int TV, int TC, int NTH> struct StatePrefetch {
     f32x4 ga[NK][VEC / 4];        // per-channel gate: a of the K item's columns
     f32x4 gg[NK][VEC / 4];        // per-channel gate: g of the K item's columns
     float g;                      // mLSTMsig: g of the block's chunk
+    float gd[4];                  // per-channel gate: g of the block's chunk at the lane's key columns
 };
 
 // S: the stored state type (T, or fp32 on request); NORM: mLSTMexp's
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
     constexpr int VEC = Elem<T>::vec;
     constexpr int WC = NWS / 2;                        // waves along the key columns
     constexpr int MV = TV / 64, MC = TC / WC / 32;     // 32x32 accumulators per wave along value / key
-    static_assert(MC >= 1, "tile too narrow for the waves");
+    static_assert(MC >= 1 && MC <= 4, "tile too narrow for the waves");
 
     const int ntv = dhv / TV, ntk = dqk / TC;
     const int blk = xcd_remap(blockIdx.x, gridDim.x);
@@ -197,6 +199,10 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
         const int kc = chunk(b / bpc);
         const int s0 = kc * L + (b % bpc) * SB;
         if (GATE == kSig) pf.g = g[bh * nc + kc];
+        if (GATE == kGla) {
+#pragma unroll
+            for (int mc = 0; mc < MC; ++mc) pf.gd[mc] = g[(bh * nc + kc) * dqk + c0 + cw + 32 * mc + i32];
+        }
         // rows past the end (partial last chunk) are read clamped and weighted 0
 #pragma unroll
         for (int u = 0; u < PF::NV; ++u) {
@@ -354,16 +360,24 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
     // not drain at every block boundary.  For 128-step blocks: the 256-step
     // ones and the reverse walk's couplings need those registers, and the
     // 64-step blocks ran slower with it (T = 8192 workload, L = 64: state
-    // walk 0.316 against 0.303 ms; L = 128: 0.228 against 0.240 ms).
-    constexpr int DEPTH = !REV && SB == 128 ? 2 : 1;
-    auto block = [&](PF& pf, int b) {
+    // walk 0.316 against 0.303 ms; L = 128: 0.228 against 0.240 ms) --
+    // except the per-channel gate's walk over pre-weighted keys, whose
+    // 64-step blocks are whole chunks (below).
+    // ahead (std::true_type): the block DEPTH places on exists, so its
+    // fetch and the walk's last-block work need no run-time test.
+    constexpr int DEPTH = !REV && (SB == 128 || PREW) ? 2 : 1;
+    auto block = [&](PF& pf, int b, auto ahead) {
         const int kc = b / bpc;               // walk position; chunk(kc) is the chunk
         const bool first = (b % bpc) == 0, last = (b % bpc) == bpc - 1 || b == bend - 1;
         __syncthreads();
         store(pf, b);
         const float gk = pf.g;                // g of this block's chunk, before the next fetch overwrites it
+        float gdk[MC];                        // likewise the per-channel gate's g at this lane's key columns
+#pragma unroll
+        for (int mc = 0; mc < MC; ++mc) gdk[mc] = pf.gd[mc];
         __syncthreads();
-        if (b + DEPTH < bend) fetch(pf, b + DEPTH);
+        if constexpr (decltype(ahead)::value) fetch(pf, b + DEPTH);
+        else if (b + DEPTH < bend) fetch(pf, b + DEPTH);
         if (first) {
             // decay of the carried state across chunk kc (column c of C^T = row c of C)
 #pragma unroll
@@ -371,7 +385,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
                 float e;
                 if (GATE == kSig) e = exp2_fast(gk * kLog2e);
                 else if (GATE == kScalar) e = exp2_fast((float)min(L, T_ - chunk(kc) * L) * lg2);
-                else e = exp2_fast(g[(bh * nc + chunk(kc)) * dqk + c0 + cw + 32 * mc + i32] * kLog2e);
+                else e = exp2_fast(gdk[mc] * kLog2e);
 #pragma unroll
                 for (int mv = 0; mv < MV; ++mv) acc[mv][mc] *= e;
             }
@@ -486,7 +500,7 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
                 }
             }
         }
-        if (b == bend - 1 && wk.end && (wk.end_all || seg == wk.nseg - 1)) {
+        if (!decltype(ahead)::value && b == bend - 1 && wk.end && (wk.end_all || seg == wk.nseg - 1)) {
             // the state after the walk, in [d_qk][d_hv]; each workgroup writes
             // only the tile it read from its initial state, so the caller's C_0
             // and C_T may be the same buffer
@@ -497,18 +511,45 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
                     for (int r = 0; r < 16; ++r) dst[nat(mv, mc, r)] = acc[mv][mc][r] * wk.end_scale;
         }
     };
+    const std::true_type ahead;
+    const std::false_type check;
+    // The memory-counter waits the compiler places before a block's staging
+    // follow every path into it: a path on which the other register set was
+    // not fetched (a conditional fetch, a skipped block) makes it wait for
+    // every load in flight, the other set's too.  The per-channel gate's walk
+    // (a state store after every 64-step block) therefore runs a steady loop
+    // in which both sets are always fetched, and the last blocks after it;
+    // its decay reads g from the prefetched set, not with a load of its own
+    // whose wait would drain the other set's loads and the state stores
+    // (T = 2048 per-channel workload: walk 0.101 -> 0.075 ms).  On the
+    // mLSTMsig walk the same steady loop measured slower (T = 8192, L = 256:
+    // 0.202 -> 0.211 ms), so it keeps the plain loop.
     if constexpr (DEPTH == 1) {
         PF pf;
         if (b0 < bend) fetch(pf, b0);
-        for (int b = b0; b < bend; ++b) block(pf, b);
-    } else {
+        for (int b = b0; b < bend; ++b) block(pf, b, check);
+    } else if constexpr (!PREW) {
         PF pfa, pfb;
         if (b0 < bend) fetch(pfa, b0);
         if (b0 + 1 < bend) fetch(pfb, b0 + 1);
         for (int b = b0; b < bend; b += 2) {
-            block(pfa, b);
-            if (b + 1 < bend) block(pfb, b + 1);
+            block(pfa, b, check);
+            if (b + 1 < bend) block(pfb, b + 1, check);
         }
+    } else {
+        PF pfa, pfb;
+        if (b0 < bend) {
+            fetch(pfa, b0);
+            fetch(pfb, min(b0 + 1, bend - 1));
+        }
+        int b = b0;
+        for (; b + 3 < bend; b += 2) {
+            block(pfa, b, ahead);
+            block(pfb, b + 1, ahead);
+        }
+        if (b < bend) block(pfa, b, check);
+        if (b + 1 < bend) block(pfb, b + 1, check);
+        if (b + 2 < bend) block(pfa, b + 2, check);
     }
 }
 
