@@ -188,6 +188,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
     const int gw = OUTDECAY ? dhv : DQK;   // per-channel gate row width
     const float* ab = (GATE == kGla) ? a + bh * (size_t)T_ * gw : a + bh * (size_t)T_;
     const float* lb = per_step_li(GATE) ? li + bh * (size_t)T_ : nullptr;
+    const float at2 = per_step_li(GATE) ? ab[tqc] * kLog2e : 0.0f;   // a of this lane's row, log2 units
     float lg2 = 0.0f;   // log2 of the fixed decay
     if (GATE == kScalar) lg2 = fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor) * kLog2e;
 
@@ -387,10 +388,12 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
             }
         }
         if (GATE != kGla) {
+            // a_t of accumulator row rr from lane rr (its own row's at2)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int t = min(t0 + 32 * wr + 8 * (r >> 2) + 4 * hh + (r & 3), T_ - 1);
-                const float e = per_step_li(GATE) ? exp2_fast(ab[t] * kLog2e)
+                const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
+                const int t = min(t0 + 32 * wr + rr, T_ - 1);
+                const float e = per_step_li(GATE) ? exp2_fast(__shfl(at2, rr, 64))
                                                   : exp2_fast((float)(t - cs + (REV ? 0 : 1)) * lg2);
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= e;
@@ -418,7 +421,6 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
         }
         fref = R;
     };
-    const float at2 = per_step_li(GATE) ? ab[tqc] * kLog2e : 0.0f;
     float rsum = 0.0f;   // mLSTMexp: this lane's part of the row sum of P (the normaliser)
     const int tlo = t0 + 32 * wr;                  // first query row of this wave
     const int nkv = (t0 - cs) / 64 + BQ / 64;     // key tiles up to the end of the query tile

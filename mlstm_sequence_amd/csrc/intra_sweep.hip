@@ -283,6 +283,10 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
         if constexpr (EARLY) next();
         __syncthreads();
         if constexpr (!EARLY) next();
+        // the next stage's loads leave here, before this stage's matrix
+        // work: at 256 registers the compiler otherwise sinks them below it
+        // (to shorten their registers' lives), and they then arrive late
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
             const int slo = s0 + 32 * mt;
@@ -378,6 +382,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
                 if constexpr (EARLY) next();
                 __syncthreads();
                 if constexpr (!EARLY) next();
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int kk = 0; kk < CW / 16; ++kk) {
 #pragma unroll
@@ -388,10 +393,14 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
                 }
             }
             if (GATE != kGla) {   // per-channel gate: e^{a_t} already inside q
+                // a_t of accumulator row rr comes from lane rr, which holds
+                // it for its own row (at2), not from a load of its own: a
+                // load here would wait behind the V tile's loads in flight
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int t = min(tlo + 8 * (r >> 2) + 4 * hh + (r & 3), T_ - 1);
-                    const float e = per_step_li(GATE) ? exp2_fast(ab[t] * kLog2e)
+                    const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
+                    const int t = min(tlo + rr, T_ - 1);
+                    const float e = per_step_li(GATE) ? exp2_fast(__shfl(at2, rr, 64))
                                                    : exp2_fast((float)(t - cs + (REV ? 0 : 1)) * lg2);
 #pragma unroll
                     for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= e;
@@ -411,6 +420,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
             if constexpr (EARLY) next();
             __syncthreads();
             if constexpr (!EARLY) next();
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 const int slo = s0 + 32 * mt;
