@@ -139,8 +139,8 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
 
     // states hold C before chunks 1..nc-1, preceded by C_0 when one is given
     // (mirrored: the state of chunks kc+1.. in slot kc)
-    const bool inter = REV ? kc < nc - 1 + c0 : (kc > 0 || c0);
-    const S* sb = inter ? states + (bh * (nc - 1 + c0) + (REV ? kc : kc - 1 + c0)) * (size_t)dhv * DQK : states;
+    const bool inter_rt = REV ? kc < nc - 1 + c0 : (kc > 0 || c0);
+    const S* sb = inter_rt ? states + (bh * (nc - 1 + c0) + (REV ? kc : kc - 1 + c0)) * (size_t)dhv * DQK : states;
 
     // ---- stage loaders (global -> registers) and writers (registers -> LDS)
     Vec16<T> pk[NK], pv[NV];
@@ -218,11 +218,6 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
             pv[u].store(&sm.st[b].vs[r][c]);
         }
     };
-    // the first stage of value tile nv
-    auto fetch_first = [&](int nv) {
-        if (inter) fetch_c(nv * BV, 0);
-        else fetch_v(nv * BV, cs);
-    };
 
     // Q fragments (lane row tqc, channels 16 kq + 8 hh ..): the B operand of
     // S^T = K Q^T and the A operand of Q C^T.  Per-channel gate: q scaled by
@@ -260,216 +255,243 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
     };
     if (GATE != kGla) load_q(-1);
 
-    bf16x8 (*const pw)[64] = &sm.p[wr * (wr + 1)];   // this wave's P blocks
-
-    // ---------------- 1. P = decay o mask o S, once per chunk
-    const float at2 = per_step_li(GATE) ? ab[tqc] * kLog2e : 0.0f;
-    float rsum = 0.0f;   // mLSTMexp: this lane's part of the row sum of P (the normaliser)
-    fetch_k(cs);
-    for (int j = 0; j < NKV; ++j) {
-        const int s0 = cs + 64 * j;
-        // per-channel gate: every key tile overlaps the query tile (the
-        // chunk), so its reference row is its middle step, and the Q
-        // fragments are rescaled to it
-        const int ref_row = (GATE == kGla) ? min(s0 + 31, T_ - 1) : -1;
-        if (GATE == kGla) load_q(ref_row, QI && j == 0 && inter);
-        const int b = DB ? j & 1 : 0;
-        auto next = [&]() {
-            if (j + 1 < NKV) fetch_k(s0 + 64);
-            else fetch_first(0);
+    // Chunks with and without an inter-chunk term run separate copies of
+    // the rest: with the choice known at compile time, the loads that start
+    // the next value tile go straight into the registers of their stage (a
+    // run-time choice between the C^T and the V stage merged the two register
+    // sets after the branch, and the copies waited for the loads at once)
+    auto body = [&](auto inter_c) {
+        // 0 or 1: the choice, known at compile time; 2: taken at run time
+        constexpr int IM = decltype(inter_c)::value;
+        const bool inter = IM == 2 ? inter_rt : IM == 1;
+        // the first stage of value tile nv
+        auto fetch_first = [&](int nv) {
+            if constexpr (IM == 2) {
+                if (inter) fetch_c(nv * BV, 0);
+                else fetch_v(nv * BV, cs);
+            } else if constexpr (IM == 1) {
+                fetch_c(nv * BV, 0);
+            } else {
+                fetch_v(nv * BV, cs);
+            }
         };
-        if constexpr (!DB) __syncthreads();
-        store_k(s0, ref_row, b);
-        if constexpr (EARLY) next();
-        __syncthreads();
-        if constexpr (!EARLY) next();
-        // the next stage's loads leave here, before this stage's matrix
-        // work: at 256 registers the compiler otherwise sinks them below it
-        // (to shorten their registers' lives), and they then arrive late
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-            const int slo = s0 + 32 * mt;
-            if (slo > tlo || slo >= T_) continue;   // wholly above the diagonal, or past the end
-            const bool diag = slo == tlo;
-            // S^T (32 key steps x 32 query rows of this wave)
-            f32x16 st;
-            for (int r = 0; r < 16; ++r) st[r] = 0.0f;
-#pragma unroll
-            for (int kq = 0; kq < KQ; ++kq) {
-                const Frag af = load8(&sm.st[b].ks[32 * mt + i32][16 * kq + 8 * hh]);
-                st = mma32(af, qf[kq], st);
-            }
-            // decay and causal mask: element r is key step slo + sr, query row tlo + i32
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int sr = 8 * (r >> 2) + 4 * hh + (r & 3);
-                float p = st[r];
-                if (per_step_li(GATE)) p *= exp2_fast(at2 + sm.bcol[b][32 * mt + sr]);
-                else if (GATE == kScalar) p *= exp2_fast((float)(tlo + i32 - slo - sr) * lg2);
-                st[r] = (diag && sr > i32) ? 0.0f : p;
-            }
-            if constexpr (GATE == kExp) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) rsum += st[r];
-            }
-            // the accumulator, in its own order, is the A operand of P V
-            const int m = (slo - cs) / 32;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                Frag pfr;
-                for (int e = 0; e < 8; ++e) frag_set(pfr, e, st[8 * half + e]);
-                pw[2 * m + half][lane] = pfr;
+        bf16x8 (*const pw)[64] = &sm.p[wr * (wr + 1)];   // this wave's P blocks
+
+        // ---------------- 1. P = decay o mask o S, once per chunk
+        const float at2 = per_step_li(GATE) ? ab[tqc] * kLog2e : 0.0f;
+        float rsum = 0.0f;   // mLSTMexp: this lane's part of the row sum of P (the normaliser)
+        fetch_k(cs);
+        for (int j = 0; j < NKV; ++j) {
+            const int s0 = cs + 64 * j;
+            // per-channel gate: every key tile overlaps the query tile (the
+            // chunk), so its reference row is its middle step, and the Q
+            // fragments are rescaled to it
+            const int ref_row = (GATE == kGla) ? min(s0 + 31, T_ - 1) : -1;
+            if (GATE == kGla) load_q(ref_row, QI && j == 0 && inter);
+            const int b = DB ? j & 1 : 0;
+            auto next = [&]() {
+                if (j + 1 < NKV) fetch_k(s0 + 64);
+                else fetch_first(0);
+            };
+            if constexpr (!DB) __syncthreads();
+            store_k(s0, ref_row, b);
+            if constexpr (EARLY) next();
+            __syncthreads();
+            if constexpr (!EARLY) next();
+            // the next stage's loads leave here, before this stage's matrix
+            // work: at 256 registers the compiler otherwise sinks them below it
+            // (to shorten their registers' lives), and they then arrive late
+            __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const int slo = s0 + 32 * mt;
+                if (slo > tlo || slo >= T_) continue;   // wholly above the diagonal, or past the end
+                const bool diag = slo == tlo;
+                // S^T (32 key steps x 32 query rows of this wave)
+                f32x16 st;
+                for (int r = 0; r < 16; ++r) st[r] = 0.0f;
+    #pragma unroll
+                for (int kq = 0; kq < KQ; ++kq) {
+                    const Frag af = load8(&sm.st[b].ks[32 * mt + i32][16 * kq + 8 * hh]);
+                    st = mma32(af, qf[kq], st);
+                }
+                // decay and causal mask: element r is key step slo + sr, query row tlo + i32
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int sr = 8 * (r >> 2) + 4 * hh + (r & 3);
+                    float p = st[r];
+                    if (per_step_li(GATE)) p *= exp2_fast(at2 + sm.bcol[b][32 * mt + sr]);
+                    else if (GATE == kScalar) p *= exp2_fast((float)(tlo + i32 - slo - sr) * lg2);
+                    st[r] = (diag && sr > i32) ? 0.0f : p;
+                }
+                if constexpr (GATE == kExp) {
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) rsum += st[r];
+                }
+                // the accumulator, in its own order, is the A operand of P V
+                const int m = (slo - cs) / 32;
+    #pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    Frag pfr;
+                    for (int e = 0; e < 8; ++e) frag_set(pfr, e, st[8 * half + e]);
+                    pw[2 * m + half][lane] = pfr;
+                }
             }
         }
-    }
 
-    // per-channel gate: the inter-chunk term takes q o e^{a_t}
-    if (GATE == kGla && inter) {
-        if constexpr (QI) {
-#pragma unroll
-            for (int kq = 0; kq < KQ; ++kq) qf[kq] = sm.qi[w * KQ + kq][lane];
-        } else {
-            load_q(-1);
-        }
-    }
-
-    // mLSTMexp: each row's factor scale / max(|scale den_t|, e^{lb_t}) with
-    // den_t = sum_s P_ts + e^{a'_t} q_t . n_{k-1} (the stabilised normaliser),
-    // formed in this lane (row tlo + i32) and handed to the accumulator
-    // layout (row_fac) where rows run along the registers
-    float fac = scale;
-    if constexpr (GATE == kExp) {
-        rsum += __shfl_xor(rsum, 32, 64);
-        float qn = 0.0f;
-        if (inter) {
-            const float* nb = nst + (bh * (nc - 1) + kc - 1) * (size_t)DQK;
-#pragma unroll
-            for (int kq = 0; kq < KQ; ++kq) {
-                const int c = 16 * kq + 8 * hh;
-                f32x4 nv[2];
-                nv[0] = *reinterpret_cast<const f32x4*>(nb + c);
-                nv[1] = *reinterpret_cast<const f32x4*>(nb + c + 4);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qn += frag_get(qf[kq], e) * nv[e >> 2][e & 3];
+        // per-channel gate: the inter-chunk term takes q o e^{a_t}
+        if (GATE == kGla && inter) {
+            if constexpr (QI) {
+    #pragma unroll
+                for (int kq = 0; kq < KQ; ++kq) qf[kq] = sm.qi[w * KQ + kq][lane];
+            } else {
+                load_q(-1);
             }
-            qn += __shfl_xor(qn, 32, 64);
         }
-        const float den = rsum + exp2_fast(at2) * qn;
-        fac = scale / fmaxf(fabsf(den * scale), exp2_fast(lbp[bh * (size_t)T_ + tqc] * kLog2e));
-    }
-    // the factor of accumulator row rr (held by lane rr in the S^T layout)
-    auto row_fac = [&](int rr) { return GATE == kExp ? __shfl(fac, rr, 64) : scale; };
 
-    // ---------------- 2. every value tile
-    T* const hbase = h + bh * (size_t)T_ * dhv;
-    for (int nv = 0; nv < nvt; ++nv) {
-        const int v0 = nv * BV;
-        f32x16 acc[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-            for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
-        if (inter) {
-            // e^{a_t} q_t^T C_{k-1}
-            for (int cb = 0; cb < DQK; cb += CW) {
-                const int b = DB ? (cb / CW) & 1 : 0;
+        // mLSTMexp: each row's factor scale / max(|scale den_t|, e^{lb_t}) with
+        // den_t = sum_s P_ts + e^{a'_t} q_t . n_{k-1} (the stabilised normaliser),
+        // formed in this lane (row tlo + i32) and handed to the accumulator
+        // layout (row_fac) where rows run along the registers
+        float fac = scale;
+        if constexpr (GATE == kExp) {
+            rsum += __shfl_xor(rsum, 32, 64);
+            float qn = 0.0f;
+            if (inter) {
+                const float* nb = nst + (bh * (nc - 1) + kc - 1) * (size_t)DQK;
+    #pragma unroll
+                for (int kq = 0; kq < KQ; ++kq) {
+                    const int c = 16 * kq + 8 * hh;
+                    f32x4 nv[2];
+                    nv[0] = *reinterpret_cast<const f32x4*>(nb + c);
+                    nv[1] = *reinterpret_cast<const f32x4*>(nb + c + 4);
+    #pragma unroll
+                    for (int e = 0; e < 8; ++e) qn += frag_get(qf[kq], e) * nv[e >> 2][e & 3];
+                }
+                qn += __shfl_xor(qn, 32, 64);
+            }
+            const float den = rsum + exp2_fast(at2) * qn;
+            fac = scale / fmaxf(fabsf(den * scale), exp2_fast(lbp[bh * (size_t)T_ + tqc] * kLog2e));
+        }
+        // the factor of accumulator row rr (held by lane rr in the S^T layout)
+        auto row_fac = [&](int rr) { return GATE == kExp ? __shfl(fac, rr, 64) : scale; };
+
+        // ---------------- 2. every value tile
+        T* const hbase = h + bh * (size_t)T_ * dhv;
+        for (int nv = 0; nv < nvt; ++nv) {
+            const int v0 = nv * BV;
+            f32x16 acc[NT];
+    #pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
+            if (inter) {
+                // e^{a_t} q_t^T C_{k-1}
+                for (int cb = 0; cb < DQK; cb += CW) {
+                    const int b = DB ? (cb / CW) & 1 : 0;
+                    auto next = [&]() {
+                        if (cb + CW < DQK) fetch_c(v0, cb + CW);
+                        else fetch_v(v0, cs);
+                    };
+                    if constexpr (!DB) __syncthreads();
+                    store_c(b);
+                    if constexpr (EARLY) next();
+                    __syncthreads();
+                    if constexpr (!EARLY) next();
+                    __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+                    for (int kk = 0; kk < CW / 16; ++kk) {
+    #pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) {
+                            const Frag bf = load8(&sm.st[b].cs[32 * nt + i32][16 * kk + 8 * hh]);
+                            acc[nt] = mma32(qf[cb / 16 + kk], bf, acc[nt]);
+                        }
+                    }
+                }
+                if (GATE != kGla) {   // per-channel gate: e^{a_t} already inside q
+                    // a_t of accumulator row rr comes from lane rr, which holds
+                    // it for its own row (at2), not from a load of its own: a
+                    // load here would wait behind the V tile's loads in flight
+    #pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
+                        const int t = min(tlo + rr, T_ - 1);
+                        const float e = per_step_li(GATE) ? exp2_fast(__shfl(at2, rr, 64))
+                                                       : exp2_fast((float)(t - cs + (REV ? 0 : 1)) * lg2);
+    #pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= e;
+                    }
+                }
+            }
+            // + P V, key tile by key tile
+            for (int j = 0; j < NKV; ++j) {
+                const int s0 = cs + 64 * j;
+                const int b = DB ? j & 1 : 0;
                 auto next = [&]() {
-                    if (cb + CW < DQK) fetch_c(v0, cb + CW);
-                    else fetch_v(v0, cs);
+                    if (j + 1 < NKV) fetch_v(v0, s0 + 64);
+                    else if (nv + 1 < nvt) fetch_first(nv + 1);
                 };
                 if constexpr (!DB) __syncthreads();
-                store_c(b);
+                store_v(b);
                 if constexpr (EARLY) next();
                 __syncthreads();
                 if constexpr (!EARLY) next();
                 __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int kk = 0; kk < CW / 16; ++kk) {
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        const Frag bf = load8(&sm.st[b].cs[32 * nt + i32][16 * kk + 8 * hh]);
-                        acc[nt] = mma32(qf[cb / 16 + kk], bf, acc[nt]);
+    #pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    const int slo = s0 + 32 * mt;
+                    if (slo > tlo || slo >= T_) continue;   // the blocks step 1 skipped
+                    const int m = (slo - cs) / 32;
+    #pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        const Frag pfr = pw[2 * m + half][lane];
+    #pragma unroll
+                        for (int nt = 0; nt < NT; ++nt) {
+                            const Frag vf = frag_tr(sm.st[b].vs, 32 * mt + 16 * half, 32 * nt, lane);
+                            acc[nt] = mma32(pfr, vf, acc[nt]);
+                        }
                     }
                 }
             }
-            if (GATE != kGla) {   // per-channel gate: e^{a_t} already inside q
-                // a_t of accumulator row rr comes from lane rr, which holds
-                // it for its own row (at2), not from a load of its own: a
-                // load here would wait behind the V tile's loads in flight
-#pragma unroll
+            // out through LDS, 64 columns at a time: the wave writes its
+            // accumulators (lane = column) into its own 32 x 64 block, then every
+            // lane stores 16-byte runs of rows
+            __syncthreads();   // every wave is done with the V tile the blocks overlay
+            T* const hrow = hbase + v0;
+    #pragma unroll
+            for (int ph = 0; ph < NT / 2; ++ph) {
+                auto os = sm.st[DB ? (NKV - 1) & 1 : 0].os[w];
+    #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
-                    const int t = min(tlo + rr, T_ - 1);
-                    const float e = per_step_li(GATE) ? exp2_fast(__shfl(at2, rr, 64))
-                                                   : exp2_fast((float)(t - cs + (REV ? 0 : 1)) * lg2);
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= e;
+                    const float fr = row_fac(rr);
+                    os[rr][i32] = from_float<T>(acc[2 * ph][r] * fr);
+                    os[rr][32 + i32] = from_float<T>(acc[2 * ph + 1][r] * fr);
                 }
-            }
-        }
-        // + P V, key tile by key tile
-        for (int j = 0; j < NKV; ++j) {
-            const int s0 = cs + 64 * j;
-            const int b = DB ? j & 1 : 0;
-            auto next = [&]() {
-                if (j + 1 < NKV) fetch_v(v0, s0 + 64);
-                else if (nv + 1 < nvt) fetch_first(nv + 1);
-            };
-            if constexpr (!DB) __syncthreads();
-            store_v(b);
-            if constexpr (EARLY) next();
-            __syncthreads();
-            if constexpr (!EARLY) next();
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const int slo = s0 + 32 * mt;
-                if (slo > tlo || slo >= T_) continue;   // the blocks step 1 skipped
-                const int m = (slo - cs) / 32;
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const Frag pfr = pw[2 * m + half][lane];
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        const Frag vf = frag_tr(sm.st[b].vs, 32 * mt + 16 * half, 32 * nt, lane);
-                        acc[nt] = mma32(pfr, vf, acc[nt]);
+                __syncthreads();
+    #pragma unroll
+                for (int qq = 0; qq < 32 / VEC; ++qq) {
+                    const int c = lane + 64 * qq;                 // 16-byte piece of the 32 x 64 block
+                    const int rr = c / (64 / VEC), col = (c % (64 / VEC)) * VEC;
+                    const int t = tlo + rr;
+                    if (t < T_) {
+                        Vec16<T> x;
+                        x.load(&os[rr][col]);
+                        x.store(hrow + (size_t)row(t) * dhv + 64 * ph + col);
                     }
                 }
+                // this block is read before it is overwritten (the next half, or
+                // the next value tile's first stage after its own barrier; with
+                // two buffers that stage goes to the other one, and the stage
+                // after it waits for the first one's barrier)
+                if (ph + 1 < NT / 2) __syncthreads();
             }
         }
-        // out through LDS, 64 columns at a time: the wave writes its
-        // accumulators (lane = column) into its own 32 x 64 block, then every
-        // lane stores 16-byte runs of rows
-        __syncthreads();   // every wave is done with the V tile the blocks overlay
-        T* const hrow = hbase + v0;
-#pragma unroll
-        for (int ph = 0; ph < NT / 2; ++ph) {
-            auto os = sm.st[DB ? (NKV - 1) & 1 : 0].os[w];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
-                const float fr = row_fac(rr);
-                os[rr][i32] = from_float<T>(acc[2 * ph][r] * fr);
-                os[rr][32 + i32] = from_float<T>(acc[2 * ph + 1][r] * fr);
-            }
-            __syncthreads();
-#pragma unroll
-            for (int qq = 0; qq < 32 / VEC; ++qq) {
-                const int c = lane + 64 * qq;                 // 16-byte piece of the 32 x 64 block
-                const int rr = c / (64 / VEC), col = (c % (64 / VEC)) * VEC;
-                const int t = tlo + rr;
-                if (t < T_) {
-                    Vec16<T> x;
-                    x.load(&os[rr][col]);
-                    x.store(hrow + (size_t)row(t) * dhv + 64 * ph + col);
-                }
-            }
-            // this block is read before it is overwritten (the next half, or
-            // the next value tile's first stage after its own barrier; with
-            // two buffers that stage goes to the other one, and the stage
-            // after it waits for the first one's barrier)
-            if (ph + 1 < NT / 2) __syncthreads();
-        }
+    };
+    if constexpr (GATE == kGla) {
+        body(std::integral_constant<int, 2>{});   // (two copies of the per-channel gate's body spill)
+    } else {
+        if (inter_rt) body(std::integral_constant<int, 1>{});
+        else body(std::integral_constant<int, 0>{});
     }
 }
 
