@@ -302,7 +302,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
             // work: at 256 registers the compiler otherwise sinks them below it
             // (to shorten their registers' lives), and they then arrive late
             __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
+#pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 const int slo = s0 + 32 * mt;
                 if (slo > tlo || slo >= T_) continue;   // wholly above the diagonal, or past the end
@@ -310,13 +310,13 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
                 // S^T (32 key steps x 32 query rows of this wave)
                 f32x16 st;
                 for (int r = 0; r < 16; ++r) st[r] = 0.0f;
-    #pragma unroll
+#pragma unroll
                 for (int kq = 0; kq < KQ; ++kq) {
                     const Frag af = load8(&sm.st[b].ks[32 * mt + i32][16 * kq + 8 * hh]);
                     st = mma32(af, qf[kq], st);
                 }
                 // decay and causal mask: element r is key step slo + sr, query row tlo + i32
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int sr = 8 * (r >> 2) + 4 * hh + (r & 3);
                     float p = st[r];
@@ -325,12 +325,12 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
                     st[r] = (diag && sr > i32) ? 0.0f : p;
                 }
                 if constexpr (GATE == kExp) {
-    #pragma unroll
+#pragma unroll
                     for (int r = 0; r < 16; ++r) rsum += st[r];
                 }
                 // the accumulator, in its own order, is the A operand of P V
                 const int m = (slo - cs) / 32;
-    #pragma unroll
+#pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     Frag pfr;
                     for (int e = 0; e < 8; ++e) frag_set(pfr, e, st[8 * half + e]);
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
         // per-channel gate: the inter-chunk term takes q o e^{a_t}
         if (GATE == kGla && inter) {
             if constexpr (QI) {
-    #pragma unroll
+#pragma unroll
                 for (int kq = 0; kq < KQ; ++kq) qf[kq] = sm.qi[w * KQ + kq][lane];
             } else {
                 load_q(-1);
@@ -359,13 +359,13 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
             float qn = 0.0f;
             if (inter) {
                 const float* nb = nst + (bh * (nc - 1) + kc - 1) * (size_t)DQK;
-    #pragma unroll
+#pragma unroll
                 for (int kq = 0; kq < KQ; ++kq) {
                     const int c = 16 * kq + 8 * hh;
                     f32x4 nv[2];
                     nv[0] = *reinterpret_cast<const f32x4*>(nb + c);
                     nv[1] = *reinterpret_cast<const f32x4*>(nb + c + 4);
-    #pragma unroll
+#pragma unroll
                     for (int e = 0; e < 8; ++e) qn += frag_get(qf[kq], e) * nv[e >> 2][e & 3];
                 }
                 qn += __shfl_xor(qn, 32, 64);
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
         for (int nv = 0; nv < nvt; ++nv) {
             const int v0 = nv * BV;
             f32x16 acc[NT];
-    #pragma unroll
+#pragma unroll
             for (int nt = 0; nt < NT; ++nt)
                 for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
             if (inter) {
@@ -398,9 +398,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
                     __syncthreads();
                     if constexpr (!EARLY) next();
                     __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
+#pragma unroll
                     for (int kk = 0; kk < CW / 16; ++kk) {
-    #pragma unroll
+#pragma unroll
                         for (int nt = 0; nt < NT; ++nt) {
                             const Frag bf = load8(&sm.st[b].cs[32 * nt + i32][16 * kk + 8 * hh]);
                             acc[nt] = mma32(qf[cb / 16 + kk], bf, acc[nt]);
@@ -411,13 +411,13 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
                     // a_t of accumulator row rr comes from lane rr, which holds
                     // it for its own row (at2), not from a load of its own: a
                     // load here would wait behind the V tile's loads in flight
-    #pragma unroll
+#pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
                         const int t = min(tlo + rr, T_ - 1);
                         const float e = per_step_li(GATE) ? exp2_fast(__shfl(at2, rr, 64))
                                                        : exp2_fast((float)(t - cs + (REV ? 0 : 1)) * lg2);
-    #pragma unroll
+#pragma unroll
                         for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= e;
                     }
                 }
@@ -436,15 +436,15 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
                 __syncthreads();
                 if constexpr (!EARLY) next();
                 __builtin_amdgcn_sched_barrier(0);
-    #pragma unroll
+#pragma unroll
                 for (int mt = 0; mt < 2; ++mt) {
                     const int slo = s0 + 32 * mt;
                     if (slo > tlo || slo >= T_) continue;   // the blocks step 1 skipped
                     const int m = (slo - cs) / 32;
-    #pragma unroll
+#pragma unroll
                     for (int half = 0; half < 2; ++half) {
                         const Frag pfr = pw[2 * m + half][lane];
-    #pragma unroll
+#pragma unroll
                         for (int nt = 0; nt < NT; ++nt) {
                             const Frag vf = frag_tr(sm.st[b].vs, 32 * mt + 16 * half, 32 * nt, lane);
                             acc[nt] = mma32(pfr, vf, acc[nt]);
@@ -457,10 +457,10 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
             // lane stores 16-byte runs of rows
             __syncthreads();   // every wave is done with the V tile the blocks overlay
             T* const hrow = hbase + v0;
-    #pragma unroll
+#pragma unroll
             for (int ph = 0; ph < NT / 2; ++ph) {
                 auto os = sm.st[DB ? (NKV - 1) & 1 : 0].os[w];
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
                     const float fr = row_fac(rr);
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
                     os[rr][32 + i32] = from_float<T>(acc[2 * ph + 1][r] * fr);
                 }
                 __syncthreads();
-    #pragma unroll
+#pragma unroll
                 for (int qq = 0; qq < 32 / VEC; ++qq) {
                     const int c = lane + 64 * qq;                 // 16-byte piece of the 32 x 64 block
                     const int rr = c / (64 / VEC), col = (c % (64 / VEC)) * VEC;
