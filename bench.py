@@ -695,6 +695,10 @@ def main():
                          "of --config at --L (profiles/traffic.json) and print them")
     ap.add_argument("--hbm-probe", action="store_true",
                     help="only measure the HBM rate of plain streaming kernels (copy, read) and print it")
+    ap.add_argument("--probe-mib", type=str, default="4096",
+                    help="--hbm-probe buffer sizes in MiB, comma-separated (sizes within the 256 MB "
+                         "last-level cache show what it serves)")
+    ap.add_argument("--probe-reps", type=int, default=10, help="--hbm-probe timed calls per point")
     ap.add_argument("--lds-probe", action="store_true",
                     help="LDS operand-read rates alone and feeding the matrix cores (tfla_dbg_lds), then exit")
     ap.add_argument("--mfma-probe", action="store_true",
@@ -718,7 +722,12 @@ def main():
         return
 
     if args.hbm_probe:
-        print(json.dumps({"hbm_probe": hbm_probe()}), flush=True)
+        for mib in (int(x) for x in args.probe_mib.split(",")):
+            r = hbm_probe(nbytes=mib << 20, reps=args.probe_reps)
+            rb, cb = r["probe_read_best"], r["probe_copy_best"]
+            log(f"{mib} MiB: read {rb['GBps']:.0f} GB/s ({rb['loads_per_thread']} loads per thread, "
+                f"{rb['workgroups']} workgroups), copy {cb['GBps']:.0f} GB/s")
+            print(json.dumps({"hbm_probe": r}), flush=True)
         return
     if args.lds_probe:
         for r in lds_probe():
