@@ -188,6 +188,8 @@ template <> struct Vec16<bf16> {
     __device__ __forceinline__ void set(int e, float x) { v[e] = to_bf16(x); }
     __device__ __forceinline__ void zero() { for (int e = 0; e < 8; ++e) v[e] = (bf16)0.0f; }
     __device__ __forceinline__ void store(bf16* p) const { *reinterpret_cast<bf16x8*>(p) = v; }
+    // non-temporal: for results this launch and the next do not read again
+    __device__ __forceinline__ void store_nt(bf16* p) const { __builtin_nontemporal_store(v, reinterpret_cast<bf16x8*>(p)); }
 };
 template <> struct Vec16<float> {
     f32x4 v;
@@ -196,6 +198,7 @@ template <> struct Vec16<float> {
     __device__ __forceinline__ void set(int e, float x) { v[e] = x; }
     __device__ __forceinline__ void zero() { v = f32x4{0.f, 0.f, 0.f, 0.f}; }
     __device__ __forceinline__ void store(float* p) const { *reinterpret_cast<f32x4*>(p) = v; }
+    __device__ __forceinline__ void store_nt(float* p) const { __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p)); }
 };
 
 // store two consecutive elements (x at p[0], y at p[1])

@@ -618,7 +618,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 4 && DQK <= 256 ? 2 : 1) void intra_
             if (t < T_) {
                 Vec16<T> x;
                 x.load(&os[rr][col]);
-                x.store(hrow + (size_t)row(t) * dhv + 64 * ph + col);
+                x.store_nt(hrow + (size_t)row(t) * dhv + 64 * ph + col);   // (not read again by the library)
             }
         }
         if constexpr (RDOTS) {

@@ -477,7 +477,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
                     if (t < T_) {
                         Vec16<T> x;
                         x.load(&os[rr][col]);
-                        x.store(hrow + (size_t)row(t) * dhv + 64 * ph + col);
+                        x.store_nt(hrow + (size_t)row(t) * dhv + 64 * ph + col);   // (the library does not read h)
                     }
                 }
                 // this block is read before it is overwritten (the next half, or
