@@ -294,14 +294,15 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
     // reverse walk: the forward state's tile in 16-byte pieces, CPN per thread
     constexpr int CEV = 16 / sizeof(S), CPR = TC / CEV, CPN = TV * CPR / NTH;
     static_assert(TV * CPR % NTH == 0, "tile pieces spread evenly over the threads");
-    // An unsegmented forward walk's states are read again only by the intra
-    // kernel, after the walk: they leave with non-temporal stores, so the
-    // caches do not hold them dirty into that kernel (T = 8192 workload, L =
-    // 256: step 0.434 -> 0.431 ms; per-channel gate 0.253 -> 0.250 ms).  A
-    // segmented walk's fix-up reads its states back at once and keeps the
-    // plain stores.  The empty asm statements keep the compiler from merging
-    // the two stores into one, which would drop the non-temporal hint.
-    const bool nt_states = !REV && wk.nseg == 1;
+    // An unsegmented walk's states are read again only by the intra kernels,
+    // after the walk: they leave with non-temporal stores, so the caches do
+    // not hold them dirty into those kernels (T = 8192 workload, L = 256:
+    // forward step 0.434 -> 0.431 ms, backward 1.500 -> 1.491 ms; per-channel
+    // gate forward 0.253 -> 0.250 ms).  A segmented walk's fix-up reads its
+    // states back at once and keeps the plain stores.  The empty asm
+    // statements keep the compiler from merging the two stores into one,
+    // which would drop the non-temporal hint.
+    const bool nt_states = wk.nseg == 1;
     auto put_state = [&](const f32x16 (&acc)[MV][MC], int slot) {
         if constexpr (STAGE) {
             S (*stg)[TC + SP] = reinterpret_cast<S (*)[TC + SP]>(&sm);
