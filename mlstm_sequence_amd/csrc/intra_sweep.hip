@@ -47,13 +47,13 @@ template <int DQK> constexpr int sweep_cw() { return DQK >= 128 ? 128 : 64; }   
 // rescaled again after it (by then the chunk's q and gate rows have left L2:
 // a quarter more bytes per launch); only where it fits beside the P blocks
 // DB: two stage buffers, used in turn (see the kernel's stage order)
-template <typename T, int DQK, int NW, bool QI, bool DB> struct SweepLds {
+template <typename T, int DQK, int NW, bool QI, bool DB, int VS> struct SweepLds {
     static constexpr int kpad = 16 / sizeof(T);   // K / C^T rows: stride = 4 banks mod 32
     static constexpr int vpad = 64 / sizeof(T);   // V rows: stride = 16 banks mod 64 (transpose reads)
     static constexpr int CW = sweep_cw<DQK>();
     union Stage {
         T ks[64][DQK + kpad];             // K tile [step][channel]
-        T vs[64][kSweepBV + vpad];        // V tile [step][value]
+        T vs[VS][kSweepBV + vpad];        // V tile [step][value]
         T cs[kSweepBV][CW + kpad];        // C^T block [value][channel]
         T os[NW][32][64 + kpad];          // per wave: 32 output rows x 64 columns on their way out
     };
@@ -85,9 +85,14 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
 {
     constexpr int NTH = 64 * NW, BQ = 32 * NW, BV = kSweepBV, NT = BV / 32, KQ = DQK / 16;
     constexpr int CW = sweep_cw<DQK>(), NKV = BQ / 64;
+    // V tiles of VS steps: 128 in the forward pass at eight waves (two V
+    // stages per value tile instead of four: T = 8192 workload, L = 256,
+    // intra 0.218 -> 0.215 ms), else 64 (the mirrored dv product measured
+    // 3% slower with 128)
+    constexpr int VS = NW == 8 && !REV ? 128 : 64, NVS = BQ / VS;
     constexpr int VEC = Elem<T>::vec, SVEC = Elem<S>::vec;
     constexpr int NK = 64 * DQK / VEC / NTH;      // K tile: 16-byte items per thread
-    constexpr int NV = 64 * BV / VEC / NTH;       // V tile: 16-byte items per thread
+    constexpr int NV = VS * BV / VEC / NTH;       // V tile: 16-byte items per thread
     constexpr int NC = BV * CW / 8 / NTH;         // C^T block: 8-element items per thread
     static_assert(NK >= 1 && NV >= 1 && NC >= 1, "tile too small for the workgroup");
     typedef typename Elem<T>::frag Frag;
@@ -104,9 +109,9 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
     // it spilled registers for every gate but mLSTMexp)
     constexpr bool DB = NW == 8 && (DQK / CW) % 2 == 0;
     constexpr bool EARLY = DB;
-    __shared__ SweepLds<T, DQK, NW, QI, DB> sm;
+    __shared__ SweepLds<T, DQK, NW, QI, DB, VS> sm;
     static_assert(sizeof(sm) <= 160 * 1024, "LDS");
-    static_assert(!DB || (NKV % 2 == 0), "stage parity");
+    static_assert(!DB || (NKV % 2 == 0 && NVS % 2 == 0), "stage parity");
 
     const int blk = xcd_remap(blockIdx.x, gridDim.x);
     const size_t bh = blk / nc;
@@ -424,11 +429,11 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
                 }
             }
             // + P V, key tile by key tile
-            for (int j = 0; j < NKV; ++j) {
-                const int s0 = cs + 64 * j;
+            for (int j = 0; j < NVS; ++j) {
+                const int s0 = cs + VS * j;
                 const int b = DB ? j & 1 : 0;
                 auto next = [&]() {
-                    if (j + 1 < NKV) fetch_v(v0, s0 + 64);
+                    if (j + 1 < NVS) fetch_v(v0, s0 + VS);
                     else if (nv + 1 < nvt) fetch_first(nv + 1);
                 };
                 if constexpr (!DB) __syncthreads();
@@ -438,7 +443,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
                 if constexpr (!EARLY) next();
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
+                for (int mt = 0; mt < VS / 32; ++mt) {
                     const int slo = s0 + 32 * mt;
                     if (slo > tlo || slo >= T_) continue;   // the blocks step 1 skipped
                     const int m = (slo - cs) / 32;
@@ -460,7 +465,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void intra_kernel_sweep(c
             T* const hrow = hbase + v0;
 #pragma unroll
             for (int ph = 0; ph < NT / 2; ++ph) {
-                auto os = sm.st[DB ? (NKV - 1) & 1 : 0].os[w];
+                auto os = sm.st[DB ? (NVS - 1) & 1 : 0].os[w];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
