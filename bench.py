@@ -27,7 +27,9 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import glob
 import json
+import re
 import os
 import sys
 import time
@@ -137,8 +139,10 @@ def settle(call, seconds=0.05, batch=8):
         torch.cuda.synchronize()
 
 
-def run_gpu(wl, L, steps, warmup, inputs_dev, cold_calls=0, flags=0, keep_h=False):
-    """flags: extra variant bits (TFLA_STATES_FP32); keep_h: also return h."""
+def run_gpu(wl, L, steps, warmup, inputs_dev, cold_calls=0, flags=0, keep_h=False, clocks=None):
+    """flags: extra variant bits (TFLA_STATES_FP32); keep_h: also return h;
+    clocks: a dict that receives the clock levels read while 300 more calls
+    run (after the timed pass)."""
     import torch
     from mlstm_sequence_amd import tfla
 
@@ -190,6 +194,18 @@ def run_gpu(wl, L, steps, warmup, inputs_dev, cold_calls=0, flags=0, keep_h=Fals
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(end) / steps
+    if clocks is not None:
+        # shader clock levels sampled every ~5 ms while 300 more calls run
+        for _ in range(300):
+            tfla.tfla_fwd_ws(*args)
+        samples = []
+        for _ in range(16):
+            samples.append(sysfs_clocks())
+            time.sleep(0.005)
+        torch.cuda.synchronize()
+        sc = sorted(int(re.sub(r"\D", "", x["sclk"])) for x in samples if x and x.get("sclk"))
+        clocks["under_load"] = {"sclk_mhz_samples": sc, "mclk": (samples[0] or {}).get("mclk"),
+                                "calls": 300, "ms_per_call": ms} if sc else None
     cold = None
     if cold_calls:
         # cold caches: a 1 GiB write between calls evicts the 8 x 4 MB L2 and
@@ -336,14 +352,35 @@ def gpu_clocks():
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True, text=True,
                            timeout=20)
-        data = json.loads(r.stdout)
+        # (a warning about low-power states can precede the JSON on stdout)
+        data = json.loads(r.stdout[r.stdout.index("{"):])
     except (OSError, ValueError, subprocess.SubprocessError):
         return None
     card = next((v for k, v in data.items() if k.startswith("card")), None)
     if not isinstance(card, dict):
         return None
     pick = lambda key: next((v for k, v in card.items() if key in k.lower()), None)
-    return {"sclk": pick("sclk"), "mclk": pick("mclk"), "fclk": pick("fclk"), "power_w": pick("power")}
+    return {"sclk": pick("sclk clock speed"), "mclk": pick("mclk clock speed"), "fclk": pick("fclk clock speed"),
+            "power_w": pick("power")}
+
+
+def sysfs_clocks():
+    """The current DPM level of the shader, memory and fabric clocks of the
+    first card, read from sysfs (a file read: usable while kernels run and
+    under the profiler); None where the files are missing."""
+    out = {}
+    for name in ("sclk", "mclk", "fclk"):
+        for path in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{name}")):
+            try:
+                with open(path) as fh:
+                    lines = fh.read().splitlines()
+            except OSError:
+                continue
+            cur = next((ln for ln in lines if ln.strip().endswith("*")), None)
+            if cur:
+                out[name] = cur.split(":", 1)[1].replace("*", "").strip()
+                break
+    return out or None
 
 
 def hbm_probe(nbytes=4 << 30, reps=10):
@@ -394,6 +431,40 @@ def hbm_probe(nbytes=4 << 30, reps=10):
     res["torch_read"] = entry(timed(lambda: src.sum()), nbytes)
     del src, dst
     return res
+
+
+def clock_ramp(wl, L, chunks=40, per_chunk=60):
+    """The step time and the shader clock level under sustained load: after
+    a short warm-up and 0.5 s idle, `chunks` x `per_chunk` forward calls back
+    to back, HIP events between the chunks and the sysfs clock level read
+    after each chunk is enqueued."""
+    import torch
+    from mlstm_sequence_amd import tfla
+    import workloads as W
+    d = {n: (None if t is None else t.cuda()) for n, t in W.make_inputs(wl).items()}
+    gate = {0: tfla.MLSTM_SIG, 1: tfla.SCALAR_DECAY, 2: tfla.GLA_KEY, 3: tfla.MLSTM_EXP}[wl.variant]
+    var = tfla.variant_of(gate, d["q"].dtype)
+    h = torch.empty((wl.B, wl.H, wl.T, wl.dhv), dtype=d["q"].dtype, device="cuda")
+    nb = tfla.tfla_workspace_bytes(wl.B, wl.H, wl.T, wl.dqk, wl.dhv, L, var)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+    args = (d["q"], d["k"], d["v"], d["igate_pre"], d["fgate_pre"], h, wl.B, wl.H, wl.T, wl.dqk, wl.dhv, L, var,
+            ws, nb)
+    for _ in range(5):
+        tfla.tfla_fwd_ws(*args)
+    torch.cuda.synchronize()
+    time.sleep(0.5)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(chunks + 1)]
+    evs[0].record()
+    t0 = time.perf_counter()
+    samples = []
+    for c in range(chunks):
+        for _ in range(per_chunk):
+            tfla.tfla_fwd_ws(*args)
+        evs[c + 1].record()
+        samples.append(((time.perf_counter() - t0) * 1e3, sysfs_clocks()))
+    torch.cuda.synchronize()
+    return [{"chunk": c, "ms_per_call": evs[c].elapsed_time(evs[c + 1]) / per_chunk,
+             "host_ms_at_enqueue": round(samples[c][0], 1), "clocks": samples[c][1]} for c in range(chunks)]
 
 
 def mfma_probe(iters=2000, reps=5):
@@ -699,6 +770,9 @@ def main():
                     help="--hbm-probe buffer sizes in MiB, comma-separated (sizes within the 256 MB "
                          "last-level cache show what it serves)")
     ap.add_argument("--probe-reps", type=int, default=10, help="--hbm-probe timed calls per point")
+    ap.add_argument("--clock-ramp", action="store_true",
+                    help="step time and shader clock level through ~1 s of back-to-back calls of --config at "
+                         "--L (default 256), then exit")
     ap.add_argument("--lds-probe", action="store_true",
                     help="LDS operand-read rates alone and feeding the matrix cores (tfla_dbg_lds), then exit")
     ap.add_argument("--mfma-probe", action="store_true",
@@ -721,6 +795,13 @@ def main():
             counter_run(wl, args.L, args.warmup + args.steps)
         return
 
+    if args.clock_ramp:
+        import workloads as W
+        for x in clock_ramp(W.WORKLOADS[args.config], args.L or 256):
+            log(f"chunk {x['chunk']:2d}: {x['ms_per_call']:.4f} ms/call, enqueued by {x['host_ms_at_enqueue']} ms, "
+                f"clocks {x['clocks']}")
+            print(json.dumps(x), flush=True)
+        return
     if args.hbm_probe:
         for mib in (int(x) for x in args.probe_mib.split(",")):
             r = hbm_probe(nbytes=mib << 20, reps=args.probe_reps)
@@ -763,8 +844,10 @@ def main():
 
     clocks_before = gpu_clocks()
     results = {}
+    clocks_load = {}
     for L in sweep:
-        ms, wall_ms, per, cold, _ = run_gpu(wl, L, args.steps, args.warmup, dev, cold_calls=10)
+        ms, wall_ms, per, cold, _ = run_gpu(wl, L, args.steps, args.warmup, dev, cold_calls=10,
+                                            clocks=clocks_load.setdefault(L, {}))
         tps = wl.B * wl.T / (ms * 1e-3)
         fl = total_flops(wl, L)
         results[L] = {"ms": ms, "wall_ms": wall_ms, "per": per, "tokens_per_s": tps,
@@ -802,7 +885,8 @@ def main():
                            "mfma_frac": x["mfma_frac"], "kernels_ms": x["per"], "cold_cache": x["cold"]}
                   for L, x in results.items()},
         "cold_cache": r["cold"],
-        "gpu_clocks": {"before_sweep": clocks_before, "after_sweep": clocks_after},
+        "gpu_clocks": {"before_sweep": clocks_before, "after_sweep": clocks_after,
+                       "under_load": clocks_load.get(Lh, {}).get("under_load")},
     }
     # the matrix-core and HBM rates plain probe kernels reach on this device,
     # and the headline against them (beside the specification's peaks)
