@@ -419,18 +419,29 @@ __global__ __launch_bounds__(64 * NWS) void state_kernel(const T* __restrict__ k
                 cvec[j].load(src + (size_t)rr * dqk + col);
             }
         }
-        // acc (value rows vw.., key columns cw..) += V^T (w.K) over this block
+        // acc (value rows vw.., key columns cw..) += V^T (w.K) over this block.
+        // The operands of the next 16 steps are read from LDS (into the other
+        // of two fragment sets) before this step's products are issued, so
+        // the reads' latency overlaps the matrix work instead of preceding it
+        // (T = 8192 workload, L = 256: walk 0.205 -> 0.199 ms)
+        {
+            typename Elem<T>::frag af[2][MV], bf[2][MC];
+            auto frags = [&](int set, int kb16) {
 #pragma unroll
-        for (int kb16 = 0; kb16 < SB; kb16 += 16) {
-            typename Elem<T>::frag af[MV], bf[MC];
+                for (int mv = 0; mv < MV; ++mv) af[set][mv] = frag_tr(sm.vs, kb16, vw + 32 * mv, lane);
 #pragma unroll
-            for (int mv = 0; mv < MV; ++mv) af[mv] = frag_tr(sm.vs, kb16, vw + 32 * mv, lane);
+                for (int mc = 0; mc < MC; ++mc) bf[set][mc] = frag_tr(sm.ks, kb16, cw + 32 * mc, lane);
+            };
+            frags(0, 0);
 #pragma unroll
-            for (int mc = 0; mc < MC; ++mc) bf[mc] = frag_tr(sm.ks, kb16, cw + 32 * mc, lane);
+            for (int kb16 = 0; kb16 < SB; kb16 += 16) {
+                const int cur = (kb16 / 16) & 1;
+                if (kb16 + 16 < SB) frags(cur ^ 1, kb16 + 16);
 #pragma unroll
-            for (int mv = 0; mv < MV; ++mv)
+                for (int mv = 0; mv < MV; ++mv)
 #pragma unroll
-                for (int mc = 0; mc < MC; ++mc) acc[mv][mc] = mma32(af[mv], bf[mc], acc[mv][mc]);
+                    for (int mc = 0; mc < MC; ++mc) acc[mv][mc] = mma32(af[cur][mv], bf[cur][mc], acc[mv][mc]);
+            }
         }
         if (last && wk.write_states && kc < nc - 1) {
             put_state(acc, REV ? nc - 2 - kc : kc + wk.soff);
