@@ -5,13 +5,17 @@
 //
 //   C_t = diag(f_t) C_{t-1} + i_t k_t v_t^T,   h_t = C_t^T q_t / sqrt(d_qk)
 //
-// One workgroup (4 wavefronts) owns all d_qk rows x 64 value columns of one
+// One workgroup (4 wavefronts) owns all d_qk rows x 32 value columns of one
 // head's state and keeps them in fp32 registers for the whole call: lane j
-// holds value column v0 + j, wave w holds key rows w R .. w R + R - 1
-// (R = d_qk / 4).  Steps run in batches of kSteps: the batch's q and k (as
-// fp32), gates and v columns are staged in LDS once, every step updates the
-// thread's state rows and forms its partial dot product with q, and the four
-// waves' partials meet in LDS and are summed in a fixed order, so results
+// holds value column v0 + (j mod 32), and the half-wave j / 32 of wave w
+// holds key rows p R .. p R + R - 1 with p = 2 w + j / 32 (R = d_qk / 8).
+// Each half-wave reads and writes 128 contiguous bytes of a state row, and
+// the 32-column split gives twice the workgroups of a 64-column one (the
+// step is bound by moving the state, and more workgroups keep more of it in
+// flight).  Steps run in batches of kSteps: the batch's q and k (as fp32),
+// gates and v columns are staged in LDS once, every step updates the
+// thread's state rows and forms its partial dot product with q, and the
+// eight row parts meet in LDS and are summed in a fixed order, so results
 // are deterministic.  The state is read once at the start and written back
 // once at the end, by the same thread, so it is updated in place.
 #include "gfx950.hpp"
@@ -28,23 +32,23 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const T* __restrict__ q,
                                                         const float* __restrict__ fg, float* __restrict__ state,
                                                         T* __restrict__ h, int H, int T_, int dhv, float scale)
 {
-    constexpr int S = kSteps, R = DQK / 4;
+    constexpr int S = kSteps, R = DQK / 8;
     constexpr int GW = GATE == kGla ? DQK : 1;
     __shared__ float qs[S][DQK], ks[S][DQK];
     __shared__ float fs[S][GW];          // per-channel forget gates (GLA)
-    __shared__ float vs[S][64];
+    __shared__ float vs[S][32];
     __shared__ float gi[S], gf[S];       // mLSTMsig input / forget gate of each step
-    __shared__ float part[S][4][64];     // per-wave partial outputs
+    __shared__ float part[S][8][32];     // partial outputs of the eight row parts
 
-    const int nvt = dhv / 64;
+    const int nvt = dhv / 32;
     const size_t bh = blockIdx.x / nvt;
-    const int v0 = (blockIdx.x % nvt) * 64;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int v0 = (blockIdx.x % nvt) * 32;
+    const int tid = threadIdx.x, col = tid & 31, part_id = tid >> 5;   // part_id = 2 w + half-wave
 
-    float* cb = state + bh * (size_t)DQK * dhv + v0 + lane;   // column v0 + lane of C [d_qk][d_hv]
+    float* cb = state + bh * (size_t)DQK * dhv + v0 + col;   // column v0 + col of C [d_qk][d_hv]
     float c[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) c[r] = cb[(size_t)(w * R + r) * dhv];
+    for (int r = 0; r < R; ++r) c[r] = cb[(size_t)(part_id * R + r) * dhv];
 
     float gam = 1.0f;   // fixed decay
     if (GATE == kScalar) gam = exp2_fast(fmaxf(log_sigmoid(fg[bh % H]), kLogForgetFloor) * kLog2e);
@@ -61,8 +65,8 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const T* __restrict__ q,
                 fs[s][cc % GW] =
                     exp2_fast(fmaxf(log_sigmoid(fg[row * DQK + cc]) * (1.0f / 16.0f), kLogForgetFloor) * kLog2e);
         }
-        for (int idx = tid; idx < S * 64; idx += 256) {
-            const int s = idx / 64, j = idx % 64;
+        for (int idx = tid; idx < S * 32; idx += 256) {
+            const int s = idx / 32, j = idx % 32;
             const size_t row = bh * T_ + min(t0 + s, T_ - 1);
             vs[s][j] = to_float(v[row * dhv + v0 + j]);
         }
@@ -73,7 +77,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const T* __restrict__ q,
         }
         __syncthreads();
         for (int s = 0; s < n; ++s) {
-            float f = gam, iv = vs[s][lane];
+            float f = gam, iv = vs[s][col];
             if (GATE == kSig) {
                 f = gf[s];
                 iv *= gi[s];
@@ -81,29 +85,30 @@ __global__ __launch_bounds__(256) void recurrent_kernel(const T* __restrict__ q,
             float o = 0.0f;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const int cc = w * R + r;
+                const int cc = part_id * R + r;
                 const float fc = GATE == kGla ? fs[s][cc % GW] : f;
                 c[r] = fc * c[r] + ks[s][cc] * iv;
                 o += c[r] * qs[s][cc];
             }
-            part[s][w][lane] = o;
+            part[s][part_id][col] = o;
         }
         __syncthreads();
-        for (int idx = tid; idx < n * 64; idx += 256) {
-            const int s = idx / 64, j = idx % 64;
-            const float o = (part[s][0][j] + part[s][1][j]) + (part[s][2][j] + part[s][3][j]);
+        for (int idx = tid; idx < n * 32; idx += 256) {
+            const int s = idx / 32, j = idx % 32;
+            const float o = ((part[s][0][j] + part[s][1][j]) + (part[s][2][j] + part[s][3][j])) +
+                            ((part[s][4][j] + part[s][5][j]) + (part[s][6][j] + part[s][7][j]));
             h[(bh * T_ + t0 + s) * dhv + v0 + j] = from_float<T>(o * scale);
         }
     }
 #pragma unroll
-    for (int r = 0; r < R; ++r) cb[(size_t)(w * R + r) * dhv] = c[r];
+    for (int r = 0; r < R; ++r) cb[(size_t)(part_id * R + r) * dhv] = c[r];
 }
 
 template <typename T, int GATE>
 hipError_t launch_t(const Problem& p, const void* q, const void* k, const void* v, const float* ig,
                     const float* fg, float* state, void* h, hipStream_t stream)
 {
-    const int blocks = p.B * p.H * (p.dhv / 64);
+    const int blocks = p.B * p.H * (p.dhv / 32);
     const float scale = 1.0f / sqrtf((float)p.dqk);
     const T* qt = static_cast<const T*>(q);
     const T* kt = static_cast<const T*>(k);
